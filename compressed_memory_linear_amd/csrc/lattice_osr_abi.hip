@@ -1,0 +1,176 @@
+// lattice_osr_abi.hip -- the C ABI of liblattice_osr.so (include/lattice_osr.h):
+// host-side argument checks, workspace sizing and dispatch to the kernels.
+// Every check runs before any HIP call; no C++ exception crosses the ABI.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/lattice_osr.h"
+#include "osr_launch.h"
+
+namespace {
+
+bool pow2_dim(int x) { return x == 16 || x == 32 || x == 64 || x == 128; }
+bool pow2_chunk(int c) { return c >= 1 && c <= 128 && (c & (c - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, size_t bytes) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Validate a descriptor; returns 0 or a negative status.
+int check_desc(const lattice_osr_desc* d) {
+    if (!d) return LATTICE_OSR_ERR_NULL;
+    if (d->B <= 0 || d->T <= 0 || d->H <= 0 || d->m <= 0 || d->d <= 0) return LATTICE_OSR_ERR_SHAPE;
+    if (static_cast<int64_t>(d->B) * d->H > INT_MAX) return LATTICE_OSR_ERR_SHAPE;
+    if (static_cast<int64_t>(d->B) * d->T * d->H > (INT64_C(1) << 40)) return LATTICE_OSR_ERR_SHAPE;
+    if (!pow2_dim(d->m) || !pow2_dim(d->d)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->in_dtype != LATTICE_OSR_F32 && d->in_dtype != LATTICE_OSR_BF16) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->y_dtype != LATTICE_OSR_F32 && d->y_dtype != LATTICE_OSR_BF16) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->mode != LATTICE_OSR_MODE_DEC && d->mode != LATTICE_OSR_MODE_SIM) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->gamma_per_slot != 0 && d->gamma_per_slot != 1) return LATTICE_OSR_ERR_UNSUPPORTED;
+    return LATTICE_OSR_OK;
+}
+
+// Which implementation runs a chunked call.
+enum class Path { TokenLoop, Mfma };
+
+Path chunk_path(const lattice_osr_desc* d, int C) {
+    if (C > 1 && d->in_dtype == LATTICE_OSR_BF16 && osr::mfma_supported(d->m, d->d, C))
+        return Path::Mfma;
+    return Path::TokenLoop;
+}
+
+size_t workspace_needed(const lattice_osr_desc* d, int C) {
+    if (chunk_path(d, C) == Path::Mfma) return osr::mfma_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C);
+    return 0;
+}
+
+// Pointer, alias and workspace checks common to all entry points.
+int check_buffers(const lattice_osr_desc* d, const void* q, const void* k, const void* v,
+                  const void* gamma, const void* mu, const float* sin, const float* sout,
+                  const void* y, const void* ws, size_t ws_bytes, size_t ws_needed) {
+    if (!q || !k || !v || !gamma || !mu || !sin || !sout || !y) return LATTICE_OSR_ERR_NULL;
+    if (ws_needed > 0 && !ws) return LATTICE_OSR_ERR_NULL;
+    if (ws_bytes < ws_needed) return LATTICE_OSR_ERR_WORKSPACE;
+
+    const size_t ein = d->in_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const size_t ey = d->y_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const size_t tok = static_cast<size_t>(d->B) * d->T * d->H;
+    const size_t st = static_cast<size_t>(d->B) * d->H * d->m * d->d * sizeof(float);
+    const Range rq = range_of(q, tok * d->m * ein), rk = range_of(k, tok * d->m * ein);
+    const Range rv = range_of(v, tok * d->d * ein), rmu = range_of(mu, tok * ein);
+    const Range rg = range_of(gamma, tok * (d->gamma_per_slot ? d->m : 1) * ein);
+    const Range rin = range_of(sin, st), rout = range_of(sout, st);
+    const Range ry = range_of(y, tok * d->d * ey);
+    const Range rw = range_of(ws, ws_needed);
+
+    if (rin.lo != rout.lo && overlap(rin, rout)) return LATTICE_OSR_ERR_ALIAS;
+    const Range others[] = {rq, rk, rv, rg, rmu, rin, rout, rw};
+    for (const Range& r : others)
+        if (overlap(ry, r)) return LATTICE_OSR_ERR_ALIAS;
+    const Range outs_vs_in[] = {rq, rk, rv, rg, rmu};
+    for (const Range& r : outs_vs_in)
+        if (overlap(rout, r) || overlap(rw, r)) return LATTICE_OSR_ERR_ALIAS;
+    if (overlap(rw, rin) || overlap(rw, rout)) return LATTICE_OSR_ERR_ALIAS;
+    return LATTICE_OSR_OK;
+}
+
+osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const void* k,
+                        const void* v, const void* gamma, const void* mu, const float* sin,
+                        float* sout, void* y, void* ws) {
+    osr::Params p;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.gamma = gamma;
+    p.mu = mu;
+    p.state_in = sin;
+    p.state_out = sout;
+    p.y = y;
+    p.zbuf = static_cast<float*>(ws);
+    p.B = d->B;
+    p.T = d->T;
+    p.H = d->H;
+    p.chunk = C;
+    p.gamma_per_slot = d->gamma_per_slot;
+    p.mode = d->mode;
+    p.y_bf16 = d->y_dtype == LATTICE_OSR_BF16 ? 1 : 0;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lattice_osr_abi_version(void) { return LATTICE_OSR_ABI_VERSION; }
+
+const char* lattice_osr_status_string(int status) {
+    switch (status) {
+        case LATTICE_OSR_OK: return "ok";
+        case LATTICE_OSR_ERR_NULL: return "null pointer argument";
+        case LATTICE_OSR_ERR_SHAPE: return "bad shape (non-positive dimension, T % chunk_size != 0, or T != 1 for decode)";
+        case LATTICE_OSR_ERR_UNSUPPORTED: return "unsupported configuration (m, d, chunk size, dtype, mode or gamma layout)";
+        case LATTICE_OSR_ERR_WORKSPACE: return "workspace too small";
+        case LATTICE_OSR_ERR_LAUNCH: return "kernel launch failed";
+        case LATTICE_OSR_ERR_ALIAS: return "forbidden overlap between arguments";
+        default: return "unknown status";
+    }
+}
+
+size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc, int32_t chunk_size) {
+    if (check_desc(desc) != LATTICE_OSR_OK || !pow2_chunk(chunk_size) || desc->T % chunk_size != 0)
+        return static_cast<size_t>(-1);
+    return workspace_needed(desc, chunk_size);
+}
+
+int lattice_osr_fwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, const void* q,
+                            const void* k, const void* v, const void* gamma, const void* mu,
+                            const float* state_in, float* state_out, void* y, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (chunk_size <= 0 || desc->T % chunk_size != 0) return LATTICE_OSR_ERR_SHAPE;
+    if (!pow2_chunk(chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    const size_t need = workspace_needed(desc, chunk_size);
+    rc = check_buffers(desc, q, k, v, gamma, mu, state_in, state_out, y, workspace, workspace_bytes, need);
+    if (rc) return rc;
+    const osr::Params p = make_params(desc, chunk_size, q, k, v, gamma, mu, state_in, state_out, y, workspace);
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (chunk_path(desc, chunk_size) == Path::Mfma) return osr::launch_mfma_chunked(desc->m, desc->d, p, st);
+    return osr::launch_valu(false, desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, st);
+}
+
+int lattice_osr_fwd_recurrent(const lattice_osr_desc* desc, const void* q, const void* k,
+                              const void* v, const void* gamma, const void* mu,
+                              const float* state_in, float* state_out, void* y, void* workspace,
+                              size_t workspace_bytes, void* hip_stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    rc = check_buffers(desc, q, k, v, gamma, mu, state_in, state_out, y, workspace, workspace_bytes, 0);
+    if (rc) return rc;
+    const osr::Params p = make_params(desc, 1, q, k, v, gamma, mu, state_in, state_out, y, workspace);
+    return osr::launch_valu(false, desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16,
+                            static_cast<hipStream_t>(hip_stream));
+}
+
+int lattice_osr_decode_step(const lattice_osr_desc* desc, const void* q, const void* k,
+                            const void* v, const void* gamma, const void* mu,
+                            const float* state_in, float* state_out, void* y, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (desc->T != 1) return LATTICE_OSR_ERR_SHAPE;
+    rc = check_buffers(desc, q, k, v, gamma, mu, state_in, state_out, y, workspace, workspace_bytes, 0);
+    if (rc) return rc;
+    const osr::Params p = make_params(desc, 1, q, k, v, gamma, mu, state_in, state_out, y, workspace);
+    return osr::launch_valu(true, desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16,
+                            static_cast<hipStream_t>(hip_stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,139 @@
+// osr_device.h -- device-side helpers shared by the OSR kernels (gfx950).
+//
+// Element conversion, input loads, wave64 reductions and the kernel parameter
+// block.  Nothing here is specific to one kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace osr {
+
+// Kernel parameter block.  Pointers are device pointers; layouts as in
+// include/lattice_osr.h ([B,T,H,m] / [B,T,H,d] / [B,T,H] / [B,H,m,d]).
+struct Params {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* gamma;
+    const void* mu;
+    const float* state_in;
+    float* state_out;
+    void* y;
+    float* zbuf;       // chunk-start states [B,H,NC,m,d] (split chunk path only)
+    int B, T, H;
+    int chunk;         // C
+    int gamma_per_slot;
+    int mode;          // 0 = decoding objective, 1 = similarity objective
+    int y_bf16;        // 1: y is bf16, 0: y is fp32
+};
+
+// ---------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 bits (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    __bf16 h = static_cast<__bf16>(x);
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// Element loaders: TIn is float (fp32 inputs) or uint16_t (bf16 bit patterns).
+template <typename TIn>
+__device__ __forceinline__ float ld(const TIn* p, int64_t i);
+
+template <>
+__device__ __forceinline__ float ld<float>(const float* p, int64_t i) {
+    return p[i];
+}
+template <>
+__device__ __forceinline__ float ld<uint16_t>(const uint16_t* p, int64_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+
+// Four consecutive elements (i must be a multiple of 4).
+template <typename TIn>
+__device__ __forceinline__ float4 ld4(const TIn* p, int64_t i);
+
+template <>
+__device__ __forceinline__ float4 ld4<float>(const float* p, int64_t i) {
+    return *reinterpret_cast<const float4*>(p + i);
+}
+template <>
+__device__ __forceinline__ float4 ld4<uint16_t>(const uint16_t* p, int64_t i) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+    return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                       __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+}
+
+// Store four consecutive y values as fp32 or bf16.
+__device__ __forceinline__ void st_y4(void* y, int64_t i, float4 val, int y_bf16) {
+    if (y_bf16) {
+        uint2 u;
+        u.x = static_cast<uint32_t>(f32_to_bf16_bits(val.x)) |
+              (static_cast<uint32_t>(f32_to_bf16_bits(val.y)) << 16);
+        u.y = static_cast<uint32_t>(f32_to_bf16_bits(val.z)) |
+              (static_cast<uint32_t>(f32_to_bf16_bits(val.w)) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + i) = u;
+    } else {
+        *reinterpret_cast<float4*>(static_cast<float*>(y) + i) = val;
+    }
+}
+
+__device__ __forceinline__ void st_y1(void* y, int64_t i, float val, int y_bf16) {
+    if (y_bf16)
+        static_cast<uint16_t*>(y)[i] = f32_to_bf16_bits(val);
+    else
+        static_cast<float*>(y)[i] = val;
+}
+
+// Streaming (non-temporal) 16-byte loads/stores of fp32 state rows.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 ld_nt4(const float* p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_nt4(float* p, float4 a) {
+    f32x4_t v = {a.x, a.y, a.z, a.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+
+// -------------------------------------------------------------- float4 ----
+__device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); }
+__device__ __forceinline__ float4 operator+(float4 a, float4 b) {
+    return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float4 operator-(float4 a, float4 b) {
+    return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+}
+__device__ __forceinline__ float4 operator*(float s, float4 a) {
+    return make_float4(s * a.x, s * a.y, s * a.z, s * a.w);
+}
+__device__ __forceinline__ float4 fma4(float s, float4 a, float4 c) {
+    return make_float4(fmaf(s, a.x, c.x), fmaf(s, a.y, c.y), fmaf(s, a.z, c.z), fmaf(s, a.w, c.w));
+}
+__device__ __forceinline__ float dot4(float4 a, float4 b) {
+    return fmaf(a.x, b.x, fmaf(a.y, b.y, fmaf(a.z, b.z, a.w * b.w)));
+}
+
+// ---------------------------------------------------------- reductions ----
+// Sum over groups of G consecutive lanes of a wave64 (G a power of two <= 64);
+// every lane of the group receives the sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int off = G / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Sum over lanes that share (lane % S), S a power of two < 64: butterfly over
+// the lane bits >= log2(S).  Every lane receives the sum of its class.
+template <int S>
+__device__ __forceinline__ float strided_sum(float x) {
+#pragma unroll
+    for (int off = S; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+}  // namespace osr

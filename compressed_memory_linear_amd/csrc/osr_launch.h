@@ -1,0 +1,24 @@
+// osr_launch.h -- host-side launchers of the OSR kernels (internal to the
+// library; the public interface is include/lattice_osr.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "osr_device.h"
+
+namespace osr {
+
+// VALU kernels.  decode: one exact step per (b,h) (T must be 1).
+// Otherwise the token-by-token forward with chunk size p.chunk (1 = exact).
+// Returns 0, -3 (unsupported m/d) or -5 (launch error).
+int launch_valu(bool decode, int m, int d, const Params& p, bool in_bf16, hipStream_t st);
+
+// MFMA chunk path (bf16 inputs): whether (m, d, C) has a built variant, the
+// workspace it needs, and the launch of the inter-chunk state-passing kernel
+// followed by the intra-chunk read-out kernel.
+bool mfma_supported(int m, int d, int C);
+size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C);
+int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st);
+
+}  // namespace osr

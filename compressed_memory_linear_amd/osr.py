@@ -1,0 +1,192 @@
+"""Python binding of liblattice_osr.so (include/lattice_osr.h).
+
+Argument marshalling only: every step of the recurrence runs in the library's
+HIP kernels.  Tensors are PyTorch device tensors (PyTorch provides device
+memory and the stream); the functions keep the C entry points' names.
+
+If the library has not been built (``python -m compressed_memory_linear_amd.build``)
+the first call raises; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblattice_osr.so")
+
+F32, BF16 = 0, 1
+MODE_DEC, MODE_SIM = 0, 1
+
+OK = 0
+ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS = -1, -2, -3, -4, -5, -6
+
+EXPORTED = ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step",
+            "lattice_osr_workspace_bytes", "lattice_osr_status_string", "lattice_osr_abi_version")
+
+
+class lattice_osr_desc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "T", "H", "m", "d", "gamma_per_slot", "in_dtype", "y_dtype", "mode")]
+
+
+class OSRError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library():
+    """Load liblattice_osr.so (raises if it was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m compressed_memory_linear_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, dp = ctypes.c_void_p, ctypes.POINTER(lattice_osr_desc)
+        fwd = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        lib.lattice_osr_fwd_chunked.argtypes = [dp, ctypes.c_int32] + fwd[1:]
+        lib.lattice_osr_fwd_recurrent.argtypes = fwd
+        lib.lattice_osr_decode_step.argtypes = fwd
+        for f in ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step"):
+            getattr(lib, f).restype = ctypes.c_int
+        lib.lattice_osr_workspace_bytes.argtypes = [dp, ctypes.c_int32]
+        lib.lattice_osr_workspace_bytes.restype = ctypes.c_size_t
+        lib.lattice_osr_status_string.argtypes = [ctypes.c_int]
+        lib.lattice_osr_status_string.restype = ctypes.c_char_p
+        lib.lattice_osr_abi_version.argtypes = []
+        lib.lattice_osr_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def lattice_osr_abi_version() -> int:
+    return int(load_library().lattice_osr_abi_version())
+
+
+def status_string(status: int) -> str:
+    return load_library().lattice_osr_status_string(int(status)).decode()
+
+
+lattice_osr_status_string = status_string
+
+
+def make_desc(B, T, H, m, d, gamma_per_slot=1, in_dtype=BF16, y_dtype=F32, mode=MODE_DEC):
+    return lattice_osr_desc(B, T, H, m, d, gamma_per_slot, in_dtype, y_dtype, mode)
+
+
+def lattice_osr_workspace_bytes(desc: lattice_osr_desc, chunk_size: int) -> int:
+    n = int(load_library().lattice_osr_workspace_bytes(ctypes.byref(desc), int(chunk_size)))
+    if n == ctypes.c_size_t(-1).value:
+        raise OSRError(ERR_SHAPE, "lattice_osr_workspace_bytes")
+    return n
+
+
+# ------------------------------------------------------------ marshalling --
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode) -> lattice_osr_desc:
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q/k/gamma are [B,T,H,m], v is [B,T,H,d]")
+    B, T, H, m = q.shape
+    d = v.shape[-1]
+    if q.dtype not in _DT:
+        raise ValueError("inputs must be float32 or bfloat16")
+    for t in (q, k, v, gamma, mu):
+        if t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q, k, v, gamma, mu must share dtype/device and be contiguous")
+    if state_in.dtype != torch.float32 or not state_in.is_contiguous():
+        raise ValueError("state must be contiguous float32 [B,H,m,d]")
+    per_slot = 1 if gamma.dim() == 4 else 0
+    return make_desc(B, T, H, m, d, per_slot, _DT[q.dtype], _DT[y_dtype], mode)
+
+
+def _outputs(desc, q, state_in, state_out, y, y_dtype):
+    if y is None:
+        y = torch.empty((desc.B, desc.T, desc.H, desc.d), dtype=y_dtype, device=q.device)
+    if state_out is None:
+        state_out = torch.empty_like(state_in)
+    return state_out, y
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def lattice_osr_fwd_chunked(q, k, v, gamma, mu, state_in, chunk_size: int, *, mode: int = MODE_DEC,
+                            y_dtype=torch.float32, state_out=None, y=None, workspace=None,
+                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunk-wise OSR forward.  Returns (y [B,T,H,d], state_out [B,H,m,d])."""
+    lib = load_library()
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode)
+    state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
+    need = lattice_osr_workspace_bytes(desc, chunk_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.lattice_osr_fwd_chunked(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y),
+                                     _ptr(workspace), wbytes, _stream(stream))
+    if rc != OK:
+        raise OSRError(rc, "lattice_osr_fwd_chunked")
+    return y, state_out
+
+
+def lattice_osr_fwd_recurrent(q, k, v, gamma, mu, state_in, *, mode: int = MODE_DEC,
+                              y_dtype=torch.float32, state_out=None, y=None,
+                              stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Exact token-by-token OSR forward.  Returns (y, state_out)."""
+    lib = load_library()
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode)
+    state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
+    rc = lib.lattice_osr_fwd_recurrent(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                       _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y), None, 0,
+                                       _stream(stream))
+    if rc != OK:
+        raise OSRError(rc, "lattice_osr_fwd_recurrent")
+    return y, state_out
+
+
+def lattice_osr_decode_step(q, k, v, gamma, mu, state_in, *, mode: int = MODE_DEC,
+                            y_dtype=torch.float32, state_out=None, y=None,
+                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One exact decode step (T = 1); state_out may be state_in (in place)."""
+    lib = load_library()
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode)
+    state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
+    rc = lib.lattice_osr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                     _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y), None, 0,
+                                     _stream(stream))
+    if rc != OK:
+        raise OSRError(rc, "lattice_osr_decode_step")
+    return y, state_out
+
+
+# ------------------------------------------------------------ host inputs --
+def to_device(inp, device="cuda") -> dict:
+    """Move an OSRInputs batch (numpy, storage form) to device tensors.
+
+    bf16 bit patterns become torch.bfloat16 tensors with the same bits.
+    """
+    out = {}
+    for name in ("q", "k", "v", "gamma", "mu"):
+        a = getattr(inp, name)
+        t = torch.from_numpy(a.copy())
+        if a.dtype.itemsize == 2:
+            t = t.view(torch.bfloat16)
+        out[name] = t.to(device)
+    out["state"] = torch.from_numpy(inp.state.copy()).to(device)
+    return out

@@ -1,0 +1,142 @@
+/*
+ * lattice_osr.h -- C ABI of the MI355X (gfx950) Orthogonal State Recurrence
+ * (OSR) library, liblattice_osr.so.
+ *
+ * The operation is the state update and read-out of the Lattice compression
+ * layer ("Lattice: Learning to Efficiently Compress the Memory", Karami,
+ * Pascanu, Mirrokni, arXiv 2504.05646).  A state of m slots, each a vector of
+ * length d, is updated per token t by writing into every slot only the part of
+ * the token's vector h_t that is orthogonal to that slot (eq. OSR), scaled by
+ * the per-slot writing intensity gamma_t * k_t, after decaying the slot by the
+ * forget gate mu_t (eq. dacay_recurrence); each slot is then projected back
+ * onto the unit sphere (eq. normalized_recurrence).  The output is the
+ * read-out y_t = S_t q_t of the updated state (general form of the layer).
+ *   decoding objective:   h_t = phi(S) k_t - v_t   (eq. decoding_recurrence)
+ *   similarity objective: h_t = -v_t               (eq. similarity_recurrence)
+ * Chunked evaluation takes the update's projections at the chunk-start state
+ * (section "Parallel and Hardware Efficient Form", eq. recurrence_linear2);
+ * with chunk size 1 it is the exact recurrence.
+ *
+ * Layouts (all contiguous, row-major, as in the implementation appendix):
+ *   q, k        [B, T, H, m]     in_dtype
+ *   gamma       [B, T, H, m]     in_dtype   (gamma_per_slot = 1)
+ *               [B, T, H]        in_dtype   (gamma_per_slot = 0)
+ *   v           [B, T, H, d]     in_dtype
+ *   mu          [B, T, H]        in_dtype
+ *   y           [B, T, H, d]     y_dtype
+ *   state_in/out[B, H, m, d]     float32, row i = slot s_i
+ * Slots of state_in must be non-zero; every slot is projected onto the unit
+ * sphere at each chunk start and once more on the returned state.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller, including
+ * the workspace.  The library never allocates, frees or retains device memory
+ * and keeps no mutable global state; calls on distinct streams may run
+ * concurrently.  state_out may alias state_in exactly (in-place update); any
+ * partial overlap between state_in and state_out, or any overlap of y with
+ * another argument, is rejected.
+ *
+ * Errors: every entry point returns LATTICE_OSR_OK (0) or a negative status.
+ * All argument checks run on the host before any HIP call; on error nothing
+ * is enqueued.  LATTICE_OSR_ERR_LAUNCH reports hipGetLastError() after the
+ * launch.  Non-finite input values are not detected; they propagate.
+ *
+ * Asynchrony: work is enqueued on `hip_stream` (a hipStream_t; NULL = the
+ * default stream).  No call synchronises.  Inputs must stay valid and
+ * unmodified until the stream reaches the end of the enqueued work.
+ */
+#ifndef LATTICE_OSR_H
+#define LATTICE_OSR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LATTICE_OSR_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define LATTICE_OSR_API __attribute__((visibility("default")))
+#else
+#define LATTICE_OSR_API
+#endif
+
+/* Element types of the token inputs (in_dtype) and of y (y_dtype). */
+#define LATTICE_OSR_F32 0
+#define LATTICE_OSR_BF16 1
+
+/* Objective that defines h_t. */
+#define LATTICE_OSR_MODE_DEC 0 /* decoding (l2 reconstruction): h = phi(S)k - v */
+#define LATTICE_OSR_MODE_SIM 1 /* dot-product similarity:       h = -v        */
+
+/* Status codes. */
+#define LATTICE_OSR_OK 0
+#define LATTICE_OSR_ERR_NULL (-1)        /* a required pointer is NULL              */
+#define LATTICE_OSR_ERR_SHAPE (-2)       /* non-positive dims, T % C != 0, T != 1 for decode */
+#define LATTICE_OSR_ERR_UNSUPPORTED (-3) /* m, d not in {16,32,64,128}; C not a power of two <= 128; bad enum */
+#define LATTICE_OSR_ERR_WORKSPACE (-4)   /* workspace smaller than lattice_osr_workspace_bytes() */
+#define LATTICE_OSR_ERR_LAUNCH (-5)      /* the HIP launch reported an error        */
+#define LATTICE_OSR_ERR_ALIAS (-6)       /* forbidden overlap between arguments      */
+
+typedef struct {
+    int32_t B;              /* batch (decode: number of sequences)               */
+    int32_t T;              /* tokens per sequence                               */
+    int32_t H;              /* heads                                             */
+    int32_t m;              /* slots per head: 16, 32, 64 or 128                 */
+    int32_t d;              /* slot / value width: 16, 32, 64 or 128             */
+    int32_t gamma_per_slot; /* 1: gamma is [B,T,H,m]; 0: gamma is [B,T,H]        */
+    int32_t in_dtype;       /* LATTICE_OSR_F32 or LATTICE_OSR_BF16               */
+    int32_t y_dtype;        /* LATTICE_OSR_F32 or LATTICE_OSR_BF16               */
+    int32_t mode;           /* LATTICE_OSR_MODE_DEC or LATTICE_OSR_MODE_SIM      */
+} lattice_osr_desc;
+
+/*
+ * Chunk-wise forward (training / prefill).  Each chunk of C = chunk_size
+ * tokens takes its projections, gates and (decoding objective) h_t from the
+ * chunk-start state (eq. recurrence_linear2, the gated-linear-attention form
+ * of the section "Parallel and Hardware Efficient Form"); C = 1 is the exact
+ * recurrence.  Requires T % chunk_size == 0 and chunk_size a power of two in
+ * [1, 128].  workspace must hold lattice_osr_workspace_bytes(desc, chunk_size)
+ * bytes (it may be NULL when that is 0); its contents on entry are ignored.
+ */
+LATTICE_OSR_API int lattice_osr_fwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size,
+                            const void* q, const void* k, const void* v, const void* gamma,
+                            const void* mu, const float* state_in, float* state_out, void* y,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Exact recurrent forward: the recurrence of eq. recurrence_detailed applied
+ * token by token (chunk size 1), the state held on chip across tokens.
+ * Needs no workspace (workspace may be NULL, workspace_bytes 0).
+ */
+LATTICE_OSR_API int lattice_osr_fwd_recurrent(const lattice_osr_desc* desc, const void* q, const void* k,
+                              const void* v, const void* gamma, const void* mu,
+                              const float* state_in, float* state_out, void* y,
+                              void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * One exact decode step for B sequences x H heads (desc->T must be 1): read
+ * each state once, apply one update, write it once, emit y.  In place
+ * (state_out == state_in) is allowed.  Needs no workspace.
+ */
+LATTICE_OSR_API int lattice_osr_decode_step(const lattice_osr_desc* desc, const void* q, const void* k,
+                            const void* v, const void* gamma, const void* mu,
+                            const float* state_in, float* state_out, void* y,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes lattice_osr_fwd_chunked needs for this shape (0 if none);
+ * (size_t)-1 if the arguments are invalid. */
+LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc, int32_t chunk_size);
+
+/* Static text for a status code (never NULL). */
+LATTICE_OSR_API const char* lattice_osr_status_string(int status);
+
+/* LATTICE_OSR_ABI_VERSION of the loaded library. */
+LATTICE_OSR_API int lattice_osr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATTICE_OSR_H */

@@ -1,0 +1,137 @@
+"""Host-only checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point that include/lattice_osr.h
+declares, and reject bad arguments with the documented status codes before
+any HIP call is made (so these run on a machine without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from compressed_memory_linear_amd import osr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lattice_osr.h")
+
+# Fake device addresses: only compared and range-checked on the host, never
+# dereferenced, because every case below fails validation first.
+BASE = 1 << 40
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LATTICE_OSR_API\s+[\w\s\*]+?\b(lattice_osr_\w+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported():
+    declared = _declared_functions()
+    assert set(declared) == set(osr.EXPORTED)
+    lib = osr.load_library()
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert osr.lattice_osr_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = osr.status_string(code)
+        assert s and s != "unknown status"
+    assert osr.status_string(-99) == "unknown status"
+
+
+def _ptrs(desc, gap=1 << 32):
+    """Disjoint fake buffers for q, k, v, gamma, mu, state_in, state_out, y."""
+    return [BASE + i * gap for i in range(8)]
+
+
+def _call(fn, desc, ptrs, chunk=None, ws=None, ws_bytes=0):
+    lib = osr.load_library()
+    args = [ctypes.byref(desc)]
+    if chunk is not None:
+        args.append(chunk)
+    args += ptrs + [ws, ws_bytes, None]
+    return getattr(lib, fn)(*args)
+
+
+FWD = ["lattice_osr_fwd_recurrent", "lattice_osr_decode_step"]
+
+
+@pytest.mark.parametrize("fn", FWD + ["lattice_osr_fwd_chunked"])
+def test_null_pointers(fn):
+    d = osr.make_desc(1, 1, 1, 16, 16)
+    chunk = 1 if fn == "lattice_osr_fwd_chunked" else None
+    lib = osr.load_library()
+    assert getattr(lib, fn)(None, *([chunk] if chunk else []), *_ptrs(d), None, 0, None) == osr.ERR_NULL
+    for i in range(8):
+        p = _ptrs(d)
+        p[i] = None
+        assert _call(fn, d, p, chunk) == osr.ERR_NULL, i
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", 0, osr.ERR_SHAPE), ("T", 0, osr.ERR_SHAPE), ("H", -1, osr.ERR_SHAPE),
+    ("m", 0, osr.ERR_SHAPE), ("m", 48, osr.ERR_UNSUPPORTED), ("d", 256, osr.ERR_UNSUPPORTED),
+    ("in_dtype", 2, osr.ERR_UNSUPPORTED), ("y_dtype", 7, osr.ERR_UNSUPPORTED),
+    ("mode", 2, osr.ERR_UNSUPPORTED), ("gamma_per_slot", 2, osr.ERR_UNSUPPORTED),
+])
+def test_bad_descriptor(field, value, status):
+    d = osr.make_desc(2, 8, 2, 32, 32)
+    setattr(d, field, value)
+    for fn in FWD:
+        if fn == "lattice_osr_decode_step" and field != "T":
+            d.T = 1
+        assert _call(fn, d, _ptrs(d)) == status, fn
+        d.T = 8 if field != "T" else value
+    assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), 4) == status
+
+
+def test_chunk_size_rules():
+    d = osr.make_desc(1, 48, 1, 32, 32)
+    assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), 32) == osr.ERR_SHAPE      # ragged tail
+    assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), 0) == osr.ERR_SHAPE
+    assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), 3) == osr.ERR_UNSUPPORTED  # 48 % 3 == 0
+    assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), 6) == osr.ERR_UNSUPPORTED
+    d2 = osr.make_desc(1, 512, 1, 32, 32)
+    assert _call("lattice_osr_fwd_chunked", d2, _ptrs(d2), 256) == osr.ERR_UNSUPPORTED
+    with pytest.raises(osr.OSRError):
+        osr.lattice_osr_workspace_bytes(d, 32)
+
+
+def test_decode_requires_single_token():
+    d = osr.make_desc(4, 2, 2, 32, 32)
+    assert _call("lattice_osr_decode_step", d, _ptrs(d)) == osr.ERR_SHAPE
+
+
+def test_aliasing_rules():
+    d = osr.make_desc(1, 1, 1, 16, 16, in_dtype=osr.F32)
+    state_bytes = 16 * 16 * 4
+    p = _ptrs(d)
+    # partial overlap of state_out with state_in
+    p[6] = p[5] + 64
+    assert _call("lattice_osr_decode_step", d, p) == osr.ERR_ALIAS
+    # y overlapping an input
+    p = _ptrs(d)
+    p[7] = p[2]
+    assert _call("lattice_osr_decode_step", d, p) == osr.ERR_ALIAS
+    # y overlapping the state
+    p = _ptrs(d)
+    p[7] = p[5] + state_bytes - 4
+    assert _call("lattice_osr_decode_step", d, p) == osr.ERR_ALIAS
+    # state_out overlapping an input
+    p = _ptrs(d)
+    p[6] = p[0]
+    assert _call("lattice_osr_fwd_recurrent", d, p) == osr.ERR_ALIAS
+
+
+def test_workspace_too_small_is_rejected():
+    for (m, dd, C) in ((64, 64, 64), (32, 32, 16), (64, 128, 64), (128, 128, 128)):
+        d = osr.make_desc(2, 4 * C, 2, m, dd)
+        need = osr.lattice_osr_workspace_bytes(d, C)
+        if need == 0:
+            continue
+        assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), C, None, 0) == osr.ERR_NULL
+        assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), C, BASE * 4, need - 1) == osr.ERR_WORKSPACE
+        # workspace overlapping an input
+        assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), C, _ptrs(d)[0], need) == osr.ERR_ALIAS
