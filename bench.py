@@ -1,0 +1,242 @@
+"""Benchmark of the OSR forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one chunk-wise OSR forward over the headline workload (B=4, H=8,
+T=2048, m=d=64, chunk 64, bf16 inputs, fp32 state and y) with every input
+already resident in HBM; the whole step runs in the library's HIP kernels,
+called through the C ABI.  The metric is head-tokens per second (B*H*T per
+step).  Printed: one JSON line with the headline value, the roofline of the
+chunk path measured live with HIP events on the launch stream, the fp64 CPU
+oracle timed on this host, and secondary lines for the decode, recurrent and
+other chunked workloads.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
+FP32_VALU_PEAK_TFLOPS = 157.3
+
+HEADLINE = "chunked_b4h8_t2048_m64d64_c64"
+
+
+def algorithmic_bytes(w: dict, y_bytes: int = 4) -> float:
+    """Compulsory HBM bytes of one forward: every input read once, y written
+    once, the fp32 state read once and written once per (b,h)."""
+    e = 2 if w["in_dtype"] == "bf16" else 4
+    tok = w["B"] * w["H"] * w["T"]
+    per_tok = e * (3 * w["m"] + w["d"] + 1) + y_bytes * w["d"]
+    return float(tok * per_tok + 2 * 4 * w["B"] * w["H"] * w["m"] * w["d"])
+
+
+def algorithmic_flops(w: dict, chunk: int) -> float:
+    """Algorithmic flops of one forward (multiply-add = 2), decoding objective:
+    chunk C > 1: 8md + (C+1)(m+d) + 4md/C + 16m + 3d per head-token;
+    C = 1 (recurrent, decode): 12md + 16m + 3d per head-token."""
+    m, d = w["m"], w["d"]
+    if chunk > 1:
+        f = 8 * m * d + (chunk + 1) * (m + d) + 4 * m * d / chunk + 16 * m + 3 * d
+    else:
+        f = 12 * m * d + 16 * m + 3 * d
+    return float(f * w["B"] * w["H"] * w["T"])
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "compressed_memory_linear_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+class Case:
+    """Device-resident inputs and outputs for one entry point on one workload."""
+
+    def __init__(self, name: str, entry: str, chunk: int, y_dtype=None):
+        import torch
+        from compressed_memory_linear_amd import osr, synth
+        self.name, self.entry, self.chunk = name, entry, chunk
+        self.w = dict(synth.WORKLOADS[name])
+        inp = synth.workload_inputs(name)
+        self.inp = inp
+        t = osr.to_device(inp)
+        self.t = t
+        self.y_dtype = y_dtype or torch.float32
+        self.y = torch.empty((inp.B, inp.T, inp.H, inp.d), dtype=self.y_dtype, device="cuda")
+        self.state_in = t["state"]
+        self.state_out = torch.empty_like(t["state"])
+        self.ws = None
+        if entry == "chunked":
+            desc = osr.make_desc(inp.B, inp.T, inp.H, inp.m, inp.d, 1,
+                                 osr.BF16 if inp.in_dtype == "bf16" else osr.F32, osr.F32)
+            need = osr.lattice_osr_workspace_bytes(desc, chunk)
+            if need:
+                self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+
+    def step(self):
+        from compressed_memory_linear_amd import osr
+        t = self.t
+        args = (t["q"], t["k"], t["v"], t["gamma"], t["mu"], self.state_in)
+        if self.entry == "chunked":
+            osr.lattice_osr_fwd_chunked(*args, self.chunk, y_dtype=self.y_dtype, state_out=self.state_out,
+                                        y=self.y, workspace=self.ws)
+        elif self.entry == "recurrent":
+            osr.lattice_osr_fwd_recurrent(*args, y_dtype=self.y_dtype, state_out=self.state_out, y=self.y)
+        else:
+            # decode keeps stepping the same state in place, as a decoder would
+            osr.lattice_osr_decode_step(*args, y_dtype=self.y_dtype, state_out=self.state_in, y=self.y)
+
+    @property
+    def head_tokens(self) -> int:
+        return self.inp.B * self.inp.H * self.inp.T
+
+
+def time_case(case: Case, steps: int, warmup: int):
+    """Average ms per step, timed with HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        case.step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        case.step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(name: str, chunk: int, budget_s: float = 10.0) -> dict:
+    """The fp64 oracle on this host, over the whole workload, repeated until
+    about budget_s seconds have passed (at least once)."""
+    import oracle
+    from compressed_memory_linear_amd import synth
+    inp = synth.workload_inputs(name)
+    args = inp.values_f64()
+    reps, total, threads = 0, 0.0, 0
+    while reps == 0 or (total < budget_s and reps < 50):
+        t0 = time.perf_counter()
+        _, _, threads = oracle.osr_forward(*args, chunk_size=chunk, return_threads=True)
+        total += time.perf_counter() - t0
+        reps += 1
+    return {"value": inp.head_tokens * reps / total, "unit": "head-tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"whole workload {name} (B*H*T = {inp.head_tokens} head-tokens), "
+                      f"{reps} repetition(s), {total:.2f} s, fp64 C with {threads} threads over (b,h)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--only", default=None, help="time a single workload/entry (profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the OSR path shards over "
+                                   "(batch, head) with no communication, and multi-GPU runs are "
+                                   "not part of it; use --gpus 1"}))
+        return 2
+
+    import torch
+    from compressed_memory_linear_amd import osr
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    osr.load_library()
+
+    if args.only:
+        name, entry, chunk = args.only.split(":")
+        case = Case(name, entry, int(chunk))
+        ms = time_case(case, args.steps, args.warmup)
+        print(json.dumps({"only": args.only, "ms_per_step": ms,
+                          "head_tokens_per_s": case.head_tokens / (ms * 1e-3)}), flush=True)
+        return 0
+
+    head = Case(HEADLINE, "chunked", 64)
+    ms = time_case(head, args.steps, args.warmup)
+    value = head.head_tokens / (ms * 1e-3)
+    abytes = algorithmic_bytes(head.w)
+    achieved = abytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "tokens/s for OSR fwd (BxHxT, m, d) + % of MFMA/HBM roofline",
+        "value": value,
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16-in/f32",
+        "data": "synthetic",
+        "config": {"workload": HEADLINE, "B": 4, "H": 8, "T": 2048, "m": 64, "d": 64, "chunk": 64,
+                   "inputs": "bf16", "state": "f32", "y": "f32", "objective": "decoding"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(f"chunked:{HEADLINE}"),
+                     "algorithmic_bytes_per_launch": abytes,
+                     "algorithmic_flops_per_launch": algorithmic_flops(head.w, 64),
+                     "mfma_frac_algorithmic": algorithmic_flops(head.w, 64) / (ms * 1e-3) / 1e12
+                                              / BF16_MFMA_PEAK_TFLOPS,
+                     "measured": "HIP events on the launch stream around the timed steps"},
+    }
+    del head
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = []
+        for name, entry, chunk, steps in (("decode_s256h32_m128d128", "decode", 1, 50),
+                                          ("chunked_b8h16_t4096_m64d128_c64", "chunked", 64, 3),
+                                          ("chunked_b1h16_t65536_m128d128_c128", "chunked", 128, 2),
+                                          (HEADLINE, "recurrent", 1, 2)):
+            c = Case(name, entry, chunk)
+            t_ms = time_case(c, steps, 1)
+            ab = algorithmic_bytes(c.w)
+            sec.append({"workload": name, "entry": entry, "chunk": chunk, "ms_per_step": t_ms,
+                        "head_tokens_per_s": c.head_tokens / (t_ms * 1e-3),
+                        "hbm_gbs_algorithmic": ab / (t_ms * 1e-3) / 1e9,
+                        "hbm_frac": ab / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "tflops_algorithmic": algorithmic_flops(c.w, chunk) / (t_ms * 1e-3) / 1e12})
+            del c
+            torch.cuda.empty_cache()
+        out["secondary"] = sec
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(HEADLINE, 64)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,10 +1,79 @@
-// osr_mfma.hip -- MFMA chunk path (placeholder until the kernels land).
+// osr_mfma.hip -- selection of the MFMA chunk schedule (bf16 inputs, C >= 16).
+//
+// Two schedules evaluate the same per-chunk arithmetic (osr_mfma_kernels.h):
+//   split: the inter-chunk state-passing kernel (one workgroup per (b,h),
+//          sequential over chunks) stores each chunk-start state in the
+//          workspace; the intra-chunk kernel then forms every read-out with
+//          one workgroup per (chunk, b, h), in parallel over the sequence.
+//   fused: one workgroup per (b,h) does both; no workspace.
+// split wins when B*H alone cannot fill the 256 compute units.
+#include <stdlib.h>
+#include <string.h>
+
 #include "osr_launch.h"
+#include "osr_mfma_kernels.h"
 
 namespace osr {
+namespace mfma {
+template <int M>
+int launch_m(int d, int c0, bool split, const Params& p, hipStream_t st);
+extern template int launch_m<16>(int, int, bool, const Params&, hipStream_t);
+extern template int launch_m<32>(int, int, bool, const Params&, hipStream_t);
+extern template int launch_m<64>(int, int, bool, const Params&, hipStream_t);
+extern template int launch_m<128>(int, int, bool, const Params&, hipStream_t);
 
-bool mfma_supported(int, int, int) { return false; }
-size_t mfma_workspace_bytes(int, int, int, int, int, int) { return 0; }
-int launch_mfma_chunked(int, int, const Params&, hipStream_t) { return -3; }
+template <int M, int D>
+constexpr int pick_c0_md(int C) {
+    return (C >= 32 && fits<M, D, 32>()) ? 32 : 16;
+}
+template <int M>
+int pick_c0_m(int d, int C) {
+    switch (d) {
+        case 16: return pick_c0_md<M, 16>(C);
+        case 32: return pick_c0_md<M, 32>(C);
+        case 64: return pick_c0_md<M, 64>(C);
+        default: return pick_c0_md<M, 128>(C);
+    }
+}
+int pick_c0(int m, int d, int C) {
+    switch (m) {
+        case 16: return pick_c0_m<16>(d, C);
+        case 32: return pick_c0_m<32>(d, C);
+        case 64: return pick_c0_m<64>(d, C);
+        default: return pick_c0_m<128>(d, C);
+    }
+}
+
+// Schedule choice.  LATTICE_OSR_CHUNK_SCHEDULE=split|fused overrides the
+// default (split when there are fewer (b,h) sequences than compute units).
+bool use_split(int B, int H) {
+    const char* e = getenv("LATTICE_OSR_CHUNK_SCHEDULE");
+    if (e && strcmp(e, "split") == 0) return true;
+    if (e && strcmp(e, "fused") == 0) return false;
+    return static_cast<int64_t>(B) * H < 256;
+}
+}  // namespace mfma
+
+bool mfma_supported(int m, int d, int C) {
+    const bool dims = (m == 16 || m == 32 || m == 64 || m == 128) && (d == 16 || d == 32 || d == 64 || d == 128);
+    return dims && C >= 16 && C <= 128 && (C & (C - 1)) == 0;
+}
+
+size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C) {
+    if (!mfma::use_split(B, H)) return 0;
+    return static_cast<size_t>(B) * H * (T / C) * m * d * sizeof(float);
+}
+
+int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st) {
+    const int c0 = mfma::pick_c0(m, d, p.chunk);
+    const bool split = mfma::use_split(p.B, p.H);
+    switch (m) {
+        case 16: return mfma::launch_m<16>(d, c0, split, p, st);
+        case 32: return mfma::launch_m<32>(d, c0, split, p, st);
+        case 64: return mfma::launch_m<64>(d, c0, split, p, st);
+        case 128: return mfma::launch_m<128>(d, c0, split, p, st);
+        default: return -3;
+    }
+}
 
 }  // namespace osr

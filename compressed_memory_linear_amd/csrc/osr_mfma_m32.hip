@@ -1,0 +1,8 @@
+// osr_mfma_m32.hip -- MFMA chunk kernels instantiated for m = 32 slots.
+#include "osr_mfma_inst.h"
+
+namespace osr {
+namespace mfma {
+template int launch_m<32>(int d, int c0, bool split, const Params& p, hipStream_t st);
+}  // namespace mfma
+}  // namespace osr

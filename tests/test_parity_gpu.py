@@ -237,3 +237,30 @@ def test_deterministic(entry, C):
     y1, S1 = _run(entry, inp, C)
     y2, S2 = _run(entry, inp, C)
     assert torch.equal(y1, y2) and torch.equal(S1, S2)
+
+
+# ----------------------------------------------------- MFMA chunk schedules --
+MFMA_CASES = [(16, 16, 16), (32, 32, 32), (64, 64, 64), (64, 128, 64), (128, 64, 32), (128, 128, 128),
+              (32, 128, 16), (128, 32, 64)]
+
+
+@pytest.mark.parametrize("schedule", ["split", "fused"])
+@pytest.mark.parametrize("m,d,C", MFMA_CASES)
+def test_mfma_schedules(monkeypatch, schedule, m, d, C):
+    _say(f"mfma schedule={schedule} m={m} d={d} C={C}")
+    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", schedule)
+    inp = synth.make_inputs(2, 4 * C, 3, m, d, seed=100 + m + 3 * d + C, in_dtype=synth.BF16)
+    y, S = _run("chunked", inp, C)
+    _check(inp, y, S, C, osr.MODE_DEC)
+
+
+@pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM])
+def test_mfma_split_and_fused_agree(monkeypatch, mode):
+    _say(f"mfma split vs fused mode={mode}")
+    inp = synth.make_inputs(2, 256, 2, 64, 64, seed=77, in_dtype=synth.BF16)
+    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "split")
+    ys, Ss = _run("chunked", inp, 64, mode=mode)
+    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "fused")
+    yf, Sf = _run("chunked", inp, 64, mode=mode)
+    assert (ys - yf).abs().max().item() <= 1e-5 * ys.abs().max().item()
+    assert (Ss - Sf).abs().max().item() <= 1e-5
