@@ -127,6 +127,16 @@ __device__ __forceinline__ float group_sum(float x) {
     return x;
 }
 
+// Sum over each row of 16 lanes (lanes 16r .. 16r+15) with DPP row
+// rotations; every lane of the row receives the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));  // row_ror:2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));  // row_ror:1
+    return x;
+}
+
 // Sum over lanes that share (lane % S), S a power of two < 64: butterfly over
 // the lane bits >= log2(S).  Every lane receives the sum of its class.
 template <int S>

@@ -16,33 +16,11 @@
 namespace osr {
 namespace mfma {
 template <int M>
-int launch_m(int d, int c0, bool split, const Params& p, hipStream_t st);
-extern template int launch_m<16>(int, int, bool, const Params&, hipStream_t);
-extern template int launch_m<32>(int, int, bool, const Params&, hipStream_t);
-extern template int launch_m<64>(int, int, bool, const Params&, hipStream_t);
-extern template int launch_m<128>(int, int, bool, const Params&, hipStream_t);
-
-template <int M, int D>
-constexpr int pick_c0_md(int C) {
-    return (C >= 32 && fits<M, D, 32>()) ? 32 : 16;
-}
-template <int M>
-int pick_c0_m(int d, int C) {
-    switch (d) {
-        case 16: return pick_c0_md<M, 16>(C);
-        case 32: return pick_c0_md<M, 32>(C);
-        case 64: return pick_c0_md<M, 64>(C);
-        default: return pick_c0_md<M, 128>(C);
-    }
-}
-int pick_c0(int m, int d, int C) {
-    switch (m) {
-        case 16: return pick_c0_m<16>(d, C);
-        case 32: return pick_c0_m<32>(d, C);
-        case 64: return pick_c0_m<64>(d, C);
-        default: return pick_c0_m<128>(d, C);
-    }
-}
+int launch_m(int d, bool split, const Params& p, hipStream_t st);
+extern template int launch_m<16>(int, bool, const Params&, hipStream_t);
+extern template int launch_m<32>(int, bool, const Params&, hipStream_t);
+extern template int launch_m<64>(int, bool, const Params&, hipStream_t);
+extern template int launch_m<128>(int, bool, const Params&, hipStream_t);
 
 // Schedule choice.  LATTICE_OSR_CHUNK_SCHEDULE=split|fused overrides the
 // default (split when there are fewer (b,h) sequences than compute units).
@@ -65,13 +43,12 @@ size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C) {
 }
 
 int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st) {
-    const int c0 = mfma::pick_c0(m, d, p.chunk);
     const bool split = mfma::use_split(p.B, p.H);
     switch (m) {
-        case 16: return mfma::launch_m<16>(d, c0, split, p, st);
-        case 32: return mfma::launch_m<32>(d, c0, split, p, st);
-        case 64: return mfma::launch_m<64>(d, c0, split, p, st);
-        case 128: return mfma::launch_m<128>(d, c0, split, p, st);
+        case 16: return mfma::launch_m<16>(d, split, p, st);
+        case 32: return mfma::launch_m<32>(d, split, p, st);
+        case 64: return mfma::launch_m<64>(d, split, p, st);
+        case 128: return mfma::launch_m<128>(d, split, p, st);
         default: return -3;
     }
 }

@@ -9,37 +9,75 @@
 namespace osr {
 namespace mfma {
 
-template <int M, int D, int C0>
-static int launch_mdc(bool split, const Params& p, hipStream_t st) {
-    if constexpr (!fits<M, D, C0>()) {
+// Sub-block length C0 (<= C).  Longer sub-blocks mean fewer barriers per
+// chunk but more live registers (gates, H fragments and the prefetched
+// inputs grow with C0); the table keeps every kernel within the register file
+// (no spills) where possible, and the read-out kernels at <= 32 because their
+// causal block grows as C0^2.
+template <int M, int D, bool WITH_Y>
+constexpr int pick_c0(int C) {
+    int c0;
+    if (WITH_Y)
+        c0 = D == 128 ? 16 : 32;
+    else
+        c0 = M * D <= 64 * 32 ? 64 : (M == 128 && D == 128 ? 16 : 32);
+    while (c0 > 16 && (c0 > C || !(WITH_Y ? fits<M, D, 32, true>() : fits<M, D, 32, false>()))) c0 /= 2;
+    return c0;
+}
+
+template <int M, int D, int C0, bool WITH_Y, bool WRITE_Z>
+static int launch_loop(const Params& p, hipStream_t st) {
+    if constexpr (!fits<M, D, C0, WITH_Y>()) {
         return -3;
     } else {
-        using G = Cfg<M, D, C0>;
         const unsigned BH = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H);
-        if (split) {
-            const unsigned NC = static_cast<unsigned>(p.T / p.chunk);
-            hipLaunchKernelGGL((osr_chunk_loop_kernel<M, D, C0, false, true>), dim3(BH), dim3(G::NT), 0, st, p);
-            if (hipGetLastError() != hipSuccess) return -5;
-            hipLaunchKernelGGL((osr_intra_chunk_kernel<M, D, C0>), dim3(BH * NC), dim3(G::NT), 0, st, p);
-        } else {
-            hipLaunchKernelGGL((osr_chunk_loop_kernel<M, D, C0, true, false>), dim3(BH), dim3(G::NT), 0, st, p);
-        }
+        hipLaunchKernelGGL((osr_chunk_loop_kernel<M, D, C0, WITH_Y, WRITE_Z>), dim3(BH), dim3(4 * D), 0, st, p);
+        return hipGetLastError() == hipSuccess ? 0 : -5;
+    }
+}
+
+template <int M, int D, int C0>
+static int launch_intra(const Params& p, hipStream_t st) {
+    if constexpr (!fits<M, D, C0, true>()) {
+        return -3;
+    } else {
+        const int BH = p.B * p.H, NC = p.T / p.chunk;
+        // Enough workgroups for every CU at the occupancy LDS allows; each
+        // takes cpw consecutive chunks (a power of two dividing NC).
+        const int per_cu = (160 * 1024) / Cfg<M, D, C0, true>::BYTES;
+        const int64_t target = 256LL * (per_cu > 0 ? per_cu : 1);
+        int cpw = 1;
+        while (cpw * 2 <= NC && NC % (cpw * 2) == 0 && static_cast<int64_t>(BH) * NC / (cpw * 2) >= target) cpw *= 2;
+        const unsigned grid = static_cast<unsigned>(BH) * static_cast<unsigned>(NC / cpw);
+        hipLaunchKernelGGL((osr_intra_chunk_kernel<M, D, C0>), dim3(grid), dim3(4 * D), 0, st, p, cpw);
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }
 }
 
 template <int M, int D>
-static int launch_md(int c0, bool split, const Params& p, hipStream_t st) {
-    return c0 == 32 ? launch_mdc<M, D, 32>(split, p, st) : launch_mdc<M, D, 16>(split, p, st);
+static int launch_md(bool split, const Params& p, hipStream_t st) {
+    const int C = p.chunk;
+    if (split) {
+        int rc;
+        switch (pick_c0<M, D, false>(C)) {
+            case 64: rc = launch_loop<M, D, 64, false, true>(p, st); break;
+            case 32: rc = launch_loop<M, D, 32, false, true>(p, st); break;
+            default: rc = launch_loop<M, D, 16, false, true>(p, st); break;
+        }
+        if (rc) return rc;
+        return pick_c0<M, D, true>(C) == 32 ? launch_intra<M, D, 32>(p, st) : launch_intra<M, D, 16>(p, st);
+    }
+    return pick_c0<M, D, true>(C) == 32 ? launch_loop<M, D, 32, true, false>(p, st)
+                                        : launch_loop<M, D, 16, true, false>(p, st);
 }
 
 template <int M>
-int launch_m(int d, int c0, bool split, const Params& p, hipStream_t st) {
+int launch_m(int d, bool split, const Params& p, hipStream_t st) {
     switch (d) {
-        case 16: return launch_md<M, 16>(c0, split, p, st);
-        case 32: return launch_md<M, 32>(c0, split, p, st);
-        case 64: return launch_md<M, 64>(c0, split, p, st);
-        case 128: return launch_md<M, 128>(c0, split, p, st);
+        case 16: return launch_md<M, 16>(split, p, st);
+        case 32: return launch_md<M, 32>(split, p, st);
+        case 64: return launch_md<M, 64>(split, p, st);
+        case 128: return launch_md<M, 128>(split, p, st);
         default: return -3;
     }
 }

@@ -12,8 +12,8 @@
 //   s_i   <- g_{t,i} s_i + kappa_{t,i} h_t,   y_t = sum_i q_{t,i} s_i
 // which is a gated linear attention with keys kappa, values h, queries q and
 // a per-key rank-one gate g.  The gated recurrence is evaluated in closed form
-// over sub-blocks of C0 tokens (C0 = 16 or 32): with A the running product of
-// g inside the sub-block and R the running state at its start,
+// over sub-blocks of C0 tokens: with A the running product of g inside the
+// sub-block and R the running state at its start,
 //   Y   = (Q (.) A) R + tril[(Q (.) A)(kappa (/) A)^T] H
 //   R  <- diag(A_end) R + W^T H,   W_t = kappa_t (.) prod_{l > t} g_l.
 // Z and R are fp32; every product whose operand derives from the state runs
@@ -25,8 +25,11 @@
 // v_mfma_f32_16x16x16_bf16 an accumulator tile (lane l holds rows
 // 4(l/16)+r of column l%16) is directly a B operand whose k index is the
 // tile's row, so R feeds the read-out and H feeds the causal product and the
-// state update without a transpose.  Contractions over d (c = H Z^T) and all
-// A operands go through LDS.
+// state update without a transpose.  The contraction over d (c = H Z^T) goes
+// through LDS; the wave that owns slot block mb computes c for all tokens of
+// the sub-block and forms the gates and their running/suffix products in
+// registers (lane shuffles), so a sub-block needs two workgroup barriers.
+// Inputs of sub-block s+1 are loaded into registers while s computes.
 #pragma once
 
 #include "osr_device.h"
@@ -55,6 +58,7 @@ __device__ __forceinline__ short bf16_bits(float x) {
 __device__ __forceinline__ float bf16_val(short b) {
     return __uint_as_float(static_cast<uint32_t>(static_cast<uint16_t>(b)) << 16);
 }
+__device__ __forceinline__ float bf16u(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi).
 __device__ __forceinline__ void split1(float x, short& hi, short& lo) {
@@ -71,333 +75,389 @@ __device__ __forceinline__ void split4(f32x4 x, s16x4& hi, s16x4& lo) {
     }
 }
 
-template <int M, int D, int C0>
+template <int M, int D, int C0, bool WITH_Y>
 struct Cfg {
     static constexpr int NW = D / 16;   // waves; wave w owns d-block w
     static constexpr int NT = 64 * NW;
     static constexpr int MT = M / 16;   // slot tiles
     static constexpr int TB = C0 / 16;  // token tiles per sub-block
+    static constexpr int MPW = (MT + NW - 1) / NW;  // slot tiles per wave in the gate phase
     static constexpr int PAD = 8;       // bf16 elements of row padding
     static constexpr int ZS_LD = D + PAD;
     static constexpr int KS_LD = M + PAD;
     static constexpr int HS_LD = D + PAD;
     static constexpr int QA_LD = M + PAD;
     static constexpr int WT_LD = C0 + PAD;
-    // Scalar (gate) phase: each slot column is split into NSEG token segments
-    // of L tokens; SPT slots per thread when there are fewer threads than slots.
-    static constexpr int SPT = M > NT ? M / NT : 1;
-    static constexpr int NSEG0 = NT > M ? NT / M : 1;
-    static constexpr int NSEG = NSEG0 < C0 ? NSEG0 : C0;
-    static constexpr int L = C0 / NSEG;
-    static constexpr int SCAL_THREADS = (M < NT ? M : NT) * NSEG;
+    static constexpr int VS_LD = D + PAD;
+    static constexpr int GS_LD = M;                        // gamma / q tiles (unpadded)
+    // 16-byte pieces of the staged tiles, and pieces per thread.
+    static constexpr int KPC = C0 * M / 8, KPT = (KPC + NT - 1) / NT;
+    static constexpr int VPC = C0 * D / 8, VPT = (VPC + NT - 1) / NT;
+    // One staging buffer (bf16): K [C0][KS_LD], V [C0][VS_LD], gamma [C0][M]
+    // (or [C0] per token), q [C0][M] (read-out only), mu [C0].
+    static constexpr int SO_K = 0;
+    static constexpr int SO_V = SO_K + C0 * KS_LD;
+    static constexpr int SO_G = SO_V + C0 * VS_LD;
+    static constexpr int SO_Q = SO_G + C0 * GS_LD;
+    static constexpr int SO_MU = SO_Q + (WITH_Y ? C0 * GS_LD : 0);
+    static constexpr int SO_GT = SO_MU + C0;               // per-token gamma [C0]
+    static constexpr int STAGE = SO_GT + C0;               // elements per buffer
 
     // LDS layout (bytes).
-    static constexpr int O_ZH = 0;
-    static constexpr int O_ZL = O_ZH + M * ZS_LD * 2;
-    static constexpr int O_KS = O_ZL + M * ZS_LD * 2;
-    static constexpr int O_HH = O_KS + C0 * KS_LD * 2;
-    static constexpr int O_HL = O_HH + C0 * HS_LD * 2;
-    static constexpr int O_CS = O_HL + C0 * HS_LD * 2;
-    static constexpr int O_HP = O_CS + C0 * M * 4;           // hh partials [NW][C0]
-    static constexpr int O_QH = O_HP + NW * C0 * 4;
-    static constexpr int O_QL = O_QH + C0 * QA_LD * 2;
-    static constexpr int O_KH = O_QL + C0 * QA_LD * 2;
-    static constexpr int O_KL = O_KH + C0 * QA_LD * 2;
-    static constexpr int O_WH = O_KL + C0 * QA_LD * 2;
-    static constexpr int O_WL = O_WH + M * WT_LD * 2;
-    static constexpr int O_AE = O_WL + M * WT_LD * 2;        // A_end [M]
-    static constexpr int O_SG = O_AE + M * 4;                // segment products [NSEG][M]
-    static constexpr int O_NP = O_SG + NSEG * M * 4;         // norm partials [NW][M]
-    static constexpr int BYTES = O_NP + NW * M * 4;
+    static constexpr int O_ZH = 0;                                  // Z hi  [M][ZS_LD]
+    static constexpr int O_ZL = O_ZH + M * ZS_LD * 2;               // Z lo
+    static constexpr int O_KS = O_ZL + M * ZS_LD * 2;               // staging [2][STAGE]
+    static constexpr int O_HH = O_KS + 2 * STAGE * 2;               // H hi  [C0][HS_LD]
+    static constexpr int O_HL = O_HH + C0 * HS_LD * 2;              // H lo
+    static constexpr int O_HP = O_HL + C0 * HS_LD * 2;              // |h|^2 partials [NW][C0]
+    static constexpr int O_WH = O_HP + NW * C0 * 4;                 // W^T hi [M][WT_LD]
+    static constexpr int O_WL = O_WH + M * WT_LD * 2;               // W^T lo
+    static constexpr int O_AE = O_WL + M * WT_LD * 2;               // A_end [M]
+    static constexpr int O_NP = O_AE + M * 4;                       // norm partials [NW][M]
+    static constexpr int O_QH = O_NP + NW * M * 4;                  // Q.A hi [C0][QA_LD]
+    static constexpr int O_QL = O_QH + (WITH_Y ? C0 * QA_LD * 2 : 0);
+    static constexpr int O_KH = O_QL + (WITH_Y ? C0 * QA_LD * 2 : 0);  // kappa/A hi
+    static constexpr int O_KL = O_KH + (WITH_Y ? C0 * QA_LD * 2 : 0);
+    static constexpr int BYTES = O_KL + (WITH_Y ? C0 * QA_LD * 2 : 0);
 
     static_assert(M % 16 == 0 && D % 16 == 0 && C0 % 16 == 0, "tile multiples");
     static_assert(NW >= 1 && NT <= 1024, "waves");
-    static_assert(L * NSEG == C0, "segments divide the sub-block");
-    static_assert(SPT * NT >= M || M <= NT, "slots covered");
 };
 
-// LDS fits in one workgroup (160 KiB on gfx950).
-template <int M, int D, int C0>
+template <int M, int D, int C0, bool WITH_Y>
 constexpr bool fits() {
-    return Cfg<M, D, C0>::BYTES <= 160 * 1024;
+    return Cfg<M, D, C0, WITH_Y>::BYTES <= 160 * 1024;
+}
+
+// Inputs of the next sub-block, loaded into registers as 16-byte pieces while
+// the current sub-block computes and written to its LDS staging buffer only
+// after the current sub-block's gate phase (so the loads have a whole phase
+// of work to land behind).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <class G>
+struct Pre {
+    u32x4 k[G::KPT], g[G::KPT], q[G::KPT], v[G::VPT];
+    uint16_t mu, gt;  // per-token scalars: thread tau < C0 holds token tau
+};
+
+// Every load below is unconditional (indices are clamped; a per-token gamma
+// reads a valid dummy tile from k) so none sits behind a branch, which would
+// make the compiler wait for it at the join.
+template <class G, bool WITH_Y>
+__device__ __forceinline__ void prefetch(Pre<G>& pf, const Params& p, int b, int hd, int t0) {
+    constexpr int M = G::MT * 16, D = G::NW * 16, C0 = G::TB * 16;
+    const int tid = threadIdx.x;
+    const uint16_t* kg = static_cast<const uint16_t*>(p.k);
+    const uint16_t* vg = static_cast<const uint16_t*>(p.v);
+    const uint16_t* gg = static_cast<const uint16_t*>(p.gamma);
+    const uint16_t* gtile = p.gamma_per_slot ? gg : kg;
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q);
+    const uint16_t* mug = static_cast<const uint16_t*>(p.mu);
+    const int64_t row0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;  // token t0
+    const int64_t rs = p.H;                                               // token stride in rows
+#pragma unroll
+    for (int j = 0; j < G::KPT; ++j) {
+        int e = tid + j * G::NT;
+        if (G::KPC % G::NT != 0) e = e < G::KPC ? e : G::KPC - 1;
+        const int64_t off = (row0 + (e / (M / 8)) * rs) * M + (e % (M / 8)) * 8;
+        pf.k[j] = *reinterpret_cast<const u32x4*>(kg + off);
+        pf.g[j] = *reinterpret_cast<const u32x4*>(gtile + off);
+        if constexpr (WITH_Y) pf.q[j] = *reinterpret_cast<const u32x4*>(qg + off);
+    }
+#pragma unroll
+    for (int j = 0; j < G::VPT; ++j) {
+        int e = tid + j * G::NT;
+        if (G::VPC % G::NT != 0) e = e < G::VPC ? e : G::VPC - 1;
+        pf.v[j] = *reinterpret_cast<const u32x4*>(vg + (row0 + (e / (D / 8)) * rs) * D + (e % (D / 8)) * 8);
+    }
+    const int64_t n = row0 + (tid % C0) * rs;
+    pf.mu = mug[n];
+    pf.gt = gg[p.gamma_per_slot ? n * M : n];
+}
+
+template <class G, bool WITH_Y>
+__device__ __forceinline__ void commit(const Pre<G>& pf, short* st) {
+    constexpr int M = G::MT * 16, D = G::NW * 16, C0 = G::TB * 16;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < G::KPT; ++j) {
+        const int e = tid + j * G::NT;
+        if (G::KPC % G::NT == 0 || e < G::KPC) {
+            const int tau = e / (M / 8), i0 = (e % (M / 8)) * 8;
+            *reinterpret_cast<u32x4*>(st + G::SO_K + tau * G::KS_LD + i0) = pf.k[j];
+            *reinterpret_cast<u32x4*>(st + G::SO_G + tau * G::GS_LD + i0) = pf.g[j];
+            if constexpr (WITH_Y) *reinterpret_cast<u32x4*>(st + G::SO_Q + tau * G::GS_LD + i0) = pf.q[j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < G::VPT; ++j) {
+        const int e = tid + j * G::NT;
+        if (G::VPC % G::NT == 0 || e < G::VPC) {
+            const int tau = e / (D / 8), c0 = (e % (D / 8)) * 8;
+            *reinterpret_cast<u32x4*>(st + G::SO_V + tau * G::VS_LD + c0) = pf.v[j];
+        }
+    }
+    if (tid < C0) {
+        st[G::SO_MU + tid] = static_cast<short>(pf.mu);
+        st[G::SO_GT + tid] = static_cast<short>(pf.gt);
+    }
+}
+
+// Products of x over the four 16-lane groups of a wave, per lane column:
+// excl_lo = prod over lower groups, excl_hi = prod over higher groups,
+// total = prod over all four.
+__device__ __forceinline__ void group_scan(float x, int lg, float& excl_lo, float& excl_hi, float& total) {
+    float inc = x;
+    float t = __shfl_up(inc, 16, 64);
+    if (lg >= 1) inc *= t;
+    t = __shfl_up(inc, 32, 64);
+    if (lg >= 2) inc *= t;
+    // inc = prod_{g' <= lg}
+    t = __shfl_up(inc, 16, 64);
+    excl_lo = lg >= 1 ? t : 1.f;
+    const int lane = threadIdx.x & 63;
+    total = __shfl(inc, (lane & 15) + 48, 64);
+    float sinc = x;
+    t = __shfl_down(sinc, 16, 64);
+    if (lg <= 2) sinc *= t;
+    t = __shfl_down(sinc, 32, 64);
+    if (lg <= 1) sinc *= t;
+    // sinc = prod_{g' >= lg}
+    t = __shfl_down(sinc, 16, 64);
+    excl_hi = lg <= 2 ? t : 1.f;
 }
 
 // --------------------------------------------------------------------------
-// One chunk for one (b, h).  acc_R holds the chunk-start state (projected by
-// the caller); on return it holds the pre-projection state at the chunk end.
-// WITH_Y: also form and store the read-outs y.
-// need_state: also apply the update after the last sub-block.
+// One sub-block of C0 tokens starting at token t0 (inside a chunk whose
+// chunk-start state Z is in zfh/zfl and in LDS).  acc_R: running state.
+// st: this sub-block's staged inputs (visible); nxt: the next sub-block's
+// inputs (in flight), written to st_next here.
 template <int M, int D, int C0, bool WITH_Y>
-__device__ __forceinline__ void osr_chunk(const Params& p, char* smem, f32x4 (&acc_R)[M / 16],
-                                          int b, int hd, int t_chunk0, int C, bool need_state) {
-    using G = Cfg<M, D, C0>;
+__device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 (&acc_R)[M / 16],
+                                             const s16x4 (&zfh)[M / 16], const s16x4 (&zfl)[M / 16],
+                                             bool r_is_z, const short* st,
+                                             const Pre<Cfg<M, D, C0, WITH_Y>>& nxt, short* st_next,
+                                             bool has_next, bool need_state, int b, int hd, int t0) {
+    using G = Cfg<M, D, C0, WITH_Y>;
     constexpr int MT = G::MT, TB = G::TB;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int lg = lane >> 4, lc = lane & 15;   // lane group (row quad) and column
-    const int dcol = 16 * w + lc;               // this lane's state/H/Y column
+    const int lg = lane >> 4, lc = lane & 15;
+    const int dcol = 16 * w + lc;
+    const short* ks = st + G::SO_K;
+    const short* vs = st + G::SO_V;
+    const short* gs = st + G::SO_G;
+    const short* qs = st + G::SO_Q;
+    const short* mus = st + G::SO_MU;
+    const short* gts = st + G::SO_GT;
+    const bool gslot = p.gamma_per_slot != 0;
 
     short* zh = reinterpret_cast<short*>(smem + G::O_ZH);
     short* zl = reinterpret_cast<short*>(smem + G::O_ZL);
-    short* ks = reinterpret_cast<short*>(smem + G::O_KS);
     short* hsh = reinterpret_cast<short*>(smem + G::O_HH);
     short* hsl = reinterpret_cast<short*>(smem + G::O_HL);
-    float* cs = reinterpret_cast<float*>(smem + G::O_CS);
     float* hp = reinterpret_cast<float*>(smem + G::O_HP);
+    short* wth = reinterpret_cast<short*>(smem + G::O_WH);
+    short* wtl = reinterpret_cast<short*>(smem + G::O_WL);
+    float* aend = reinterpret_cast<float*>(smem + G::O_AE);
     short* qah = reinterpret_cast<short*>(smem + G::O_QH);
     short* qal = reinterpret_cast<short*>(smem + G::O_QL);
     short* kah = reinterpret_cast<short*>(smem + G::O_KH);
     short* kal = reinterpret_cast<short*>(smem + G::O_KL);
-    short* wth = reinterpret_cast<short*>(smem + G::O_WH);
-    short* wtl = reinterpret_cast<short*>(smem + G::O_WL);
-    float* aend = reinterpret_cast<float*>(smem + G::O_AE);
-    float* segp = reinterpret_cast<float*>(smem + G::O_SG);
 
-    const uint16_t* qg = static_cast<const uint16_t*>(p.q);
-    const uint16_t* kg = static_cast<const uint16_t*>(p.k);
-    const uint16_t* vg = static_cast<const uint16_t*>(p.v);
-    const uint16_t* gg = static_cast<const uint16_t*>(p.gamma);
-    const uint16_t* mug = static_cast<const uint16_t*>(p.mu);
-    auto bth = [&](int t) { return (static_cast<int64_t>(b) * p.T + t) * p.H + hd; };
-
-    // Z as B operands (k = slot) for H = K Z, and row-major in LDS for c = H Z^T.
-    s16x4 zfh[MT], zfl[MT];
+    // ---- H = K Z - V for this wave's columns; |h|^2 partials; H to LDS ----
+    f32x4 accH[TB];
+    s16x4 hfh[TB], hfl[TB];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-        split4(acc_R[mt], zfh[mt], zfl[mt]);
+    for (int tb = 0; tb < TB; ++tb) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        if (p.mode == 0) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const s16x4 kf = *reinterpret_cast<const s16x4*>(ks + (16 * tb + lc) * G::KS_LD + 16 * mt + 4 * lg);
+                a = mma(kf, zfl[mt], a);
+                a = mma(kf, zfh[mt], a);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a[r] -= bf16_val(vs[(16 * tb + 4 * lg + r) * G::VS_LD + dcol]);
+        accH[tb] = a;
+        split4(a, hfh[tb], hfl[tb]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mt + 4 * lg + r;
-            zh[row * G::ZS_LD + dcol] = zfh[mt][r];
-            zl[row * G::ZS_LD + dcol] = zfl[mt][r];
+            const int row = 16 * tb + 4 * lg + r;
+            hsh[row * G::HS_LD + dcol] = hfh[tb][r];
+            hsl[row * G::HS_LD + dcol] = hfl[tb][r];
+            const float sq = row16_sum(a[r] * a[r]);
+            if (lc == 0) hp[w * C0 + row] = sq;
         }
     }
+    __syncthreads();  // (A) H, |h|^2 partials visible
 
-    for (int u = 0; u < C; u += C0) {
-        const int t0 = t_chunk0 + u;
-        // ---- stage K of the sub-block (exact bf16) -------------------------
-        for (int e = tid; e < C0 * M / 8; e += G::NT) {
-            const int tau = e / (M / 8), i0 = (e % (M / 8)) * 8;
-            const uint4 val = *reinterpret_cast<const uint4*>(kg + bth(t0 + tau) * M + i0);
-            *reinterpret_cast<uint4*>(ks + tau * G::KS_LD + i0) = val;
-        }
-        __syncthreads();  // ks, and (first sub-block) zh/zl, visible
-
-        // ---- H = K Z - V for this wave's columns ---------------------------
-        f32x4 accH[TB];
+    // ---- c = H Z^T for this wave's slot tiles; gates in registers --------
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-            if (p.mode == 0) {
+    for (int mi = 0; mi < G::MPW; ++mi) {
+        const int mb = w + mi * G::NW;
+        if (mb < MT) {
+            const int i = 16 * mb + lc;  // this lane's slot
+            float gt[TB][4], kp[TB][4], tot[TB], ex_lo[TB], ex_hi[TB];
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    const s16x4 kf = *reinterpret_cast<const s16x4*>(
-                        ks + (16 * tb + lc) * G::KS_LD + 16 * mt + 4 * lg);
-                    a = mma(kf, zfl[mt], a);
-                    a = mma(kf, zfh[mt], a);
+            for (int tb = 0; tb < TB; ++tb) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kd = 0; kd < D / 16; ++kd) {
+                    const int ao = (16 * tb + lc) * G::HS_LD + 16 * kd + 4 * lg;
+                    const int bo = (16 * mb + lc) * G::ZS_LD + 16 * kd + 4 * lg;
+                    c = mma3(*reinterpret_cast<const s16x4*>(hsh + ao), *reinterpret_cast<const s16x4*>(hsl + ao),
+                             *reinterpret_cast<const s16x4*>(zh + bo), *reinterpret_cast<const s16x4*>(zl + bo), c);
                 }
-            }
+                float prod = 1.f;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                a[r] -= bf16_bits_to_f32(vg[bth(t0 + 16 * tb + 4 * lg + r) * D + dcol]);
-            accH[tb] = a;
-        }
-        // |h_t|^2 partial over this wave's columns; H row-major (hi/lo) to LDS.
-        s16x4 hfh[TB], hfl[TB];
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            split4(accH[tb], hfh[tb], hfl[tb]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * tb + 4 * lg + r;
-                hsh[row * G::HS_LD + dcol] = hfh[tb][r];
-                hsl[row * G::HS_LD + dcol] = hfl[tb][r];
-                float sq = accH[tb][r] * accH[tb][r];
-                sq = group_sum<16>(sq);
-                if (lc == 0) hp[w * C0 + row] = sq;
-            }
-        }
-        __syncthreads();  // H and |h|^2 partials visible
-
-        // ---- c = H Z^T (contraction over all d), tiles spread over waves ---
-        for (int ti = w; ti < TB * MT; ti += G::NW) {
-            const int tb = ti / MT, mb = ti % MT;
-            f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kd = 0; kd < D / 16; ++kd) {
-                const int ao = (16 * tb + lc) * G::HS_LD + 16 * kd + 4 * lg;
-                const int bo = (16 * mb + lc) * G::ZS_LD + 16 * kd + 4 * lg;
-                a = mma3(*reinterpret_cast<const s16x4*>(hsh + ao), *reinterpret_cast<const s16x4*>(hsl + ao),
-                         *reinterpret_cast<const s16x4*>(zh + bo), *reinterpret_cast<const s16x4*>(zl + bo), a);
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) cs[(16 * tb + 4 * lg + r) * M + 16 * mb + lc] = a[r];
-        }
-        __syncthreads();  // c visible
-
-        // ---- gates: beta, g, kappa; running products along the sub-block ---
-        // Pass 1: per (slot, token segment) the gates and the segment product.
-        const bool sact = tid < G::SCAL_THREADS;
-        float gt[G::SPT][G::L], kp[G::SPT][G::L];
-        if (sact) {
-#pragma unroll
-            for (int sp = 0; sp < G::SPT; ++sp) {
-                const int i = (G::SPT > 1) ? tid + sp * G::NT : tid % M;
-                const int seg = (G::SPT > 1) ? 0 : tid / M;
-                float run = 1.f;
-#pragma unroll
-                for (int j = 0; j < G::L; ++j) {
-                    const int tau = seg * G::L + j;
-                    const int64_t n = bth(t0 + tau);
+                for (int r = 0; r < 4; ++r) {
+                    const int tau = 16 * tb + 4 * lg + r;
                     float hh = 0.f;
 #pragma unroll
                     for (int ww = 0; ww < G::NW; ++ww) hh += hp[ww * C0 + tau];
-                    const float c = cs[tau * M + i];
                     const float k = bf16_val(ks[tau * G::KS_LD + i]);
-                    const float gam = bf16_bits_to_f32(p.gamma_per_slot ? gg[n * M + i] : gg[n]);
-                    const float mu = bf16_bits_to_f32(mug[n]);
-                    const float a = gam * k;
-                    const float wv = fmaxf(fmaf(-c, c, hh), 0.f);
+                    const float mu = bf16_val(mus[tau]);
+                    const float a = bf16_val(gslot ? gs[tau * G::GS_LD + i] : gts[tau]) * k;
+                    const float wv = fmaxf(fmaf(-c[r], c[r], hh), 0.f);
                     const float beta = rsqrtf(fmaf(mu, mu, a * a * wv));
-                    gt[sp][j] = beta * fmaf(a, c, mu);
-                    kp[sp][j] = -beta * a;
-                    run *= gt[sp][j];
+                    gt[tb][r] = beta * fmaf(a, c[r], mu);
+                    kp[tb][r] = -beta * a;
+                    prod *= gt[tb][r];
                 }
-                segp[seg * M + i] = run;
+                group_scan(prod, lg, ex_lo[tb], ex_hi[tb], tot[tb]);
             }
-        }
-        __syncthreads();  // segment products visible
-        // Pass 2: running products A, suffix products, and the operands
-        // Q (.) A, kappa (/) A (read-out) and W^T (state update).
-        if (sact) {
+            // Running (A) and suffix (prod_{l > t}) products over the sub-block.
+            float fwd = 1.f;
 #pragma unroll
-            for (int sp = 0; sp < G::SPT; ++sp) {
-                const int i = (G::SPT > 1) ? tid + sp * G::NT : tid % M;
-                const int seg = (G::SPT > 1) ? 0 : tid / M;
-                float before = 1.f, after = 1.f;
+            for (int tb = 0; tb < TB; ++tb) {
+                float bwd = 1.f;
 #pragma unroll
-                for (int s2 = 0; s2 < G::NSEG; ++s2) {
-                    const float v = segp[s2 * M + i];
-                    if (s2 < seg) before *= v;
-                    if (s2 > seg) after *= v;
+                for (int tb2 = tb + 1; tb2 < TB; ++tb2) bwd *= tot[tb2];
+                float A = fwd * ex_lo[tb];
+                float suf[4];
+                float s = bwd * ex_hi[tb];
+#pragma unroll
+                for (int r = 3; r >= 0; --r) {
+                    suf[r] = s;
+                    s *= gt[tb][r];
                 }
-                float suf[G::L];
-                float sacc = after;
+                s16x4 wh4, wl4;
 #pragma unroll
-                for (int j = G::L - 1; j >= 0; --j) {
-                    suf[j] = sacc;
-                    sacc *= gt[sp][j];
-                }
-                if (seg == 0) aend[i] = sacc;  // product over the whole sub-block
-                float A = before;
-#pragma unroll
-                for (int j = 0; j < G::L; ++j) {
-                    const int tau = seg * G::L + j;
-                    A *= gt[sp][j];
+                for (int r = 0; r < 4; ++r) {
+                    const int tau = 16 * tb + 4 * lg + r;
+                    A *= gt[tb][r];
                     short hi, lo;
-                    split1(kp[sp][j] * suf[j], hi, lo);
-                    wth[i * G::WT_LD + tau] = hi;
-                    wtl[i * G::WT_LD + tau] = lo;
+                    split1(kp[tb][r] * suf[r], hi, lo);
+                    wh4[r] = hi;
+                    wl4[r] = lo;
                     if constexpr (WITH_Y) {
-                        const float q = bf16_bits_to_f32(qg[bth(t0 + tau) * M + i]);
-                        split1(q * A, hi, lo);
+                        split1(bf16_val(qs[tau * G::GS_LD + i]) * A, hi, lo);
                         qah[tau * G::QA_LD + i] = hi;
                         qal[tau * G::QA_LD + i] = lo;
-                        split1(kp[sp][j] / A, hi, lo);
+                        split1(kp[tb][r] / A, hi, lo);
                         kah[tau * G::QA_LD + i] = hi;
                         kal[tau * G::QA_LD + i] = lo;
                     }
                 }
+                *reinterpret_cast<s16x4*>(wth + i * G::WT_LD + 16 * tb + 4 * lg) = wh4;
+                *reinterpret_cast<s16x4*>(wtl + i * G::WT_LD + 16 * tb + 4 * lg) = wl4;
+                fwd *= tot[tb];
+            }
+            if (lg == 0) aend[i] = fwd;
+        }
+    }
+    if (has_next) commit<G, WITH_Y>(nxt, st_next);
+    __syncthreads();  // (B) W^T, A_end, Q.A, kappa/A and the next staged inputs visible
+
+    // ---- read-out: Y = (Q.A) R + tril(P) H, P^T = (kappa/A)(Q.A)^T ---
+    if constexpr (WITH_Y) {
+        s16x4 rfh[MT], rfl[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if (r_is_z) {
+                rfh[mt] = zfh[mt];
+                rfl[mt] = zfl[mt];
+            } else {
+                split4(acc_R[mt], rfh[mt], rfl[mt]);
             }
         }
-        __syncthreads();  // W^T, A_end (and Q.A, kappa/A) visible
-
-        // ---- read-out: Y = (Q.A) R + tril(P) H, P^T = (kappa/A)(Q.A)^T ---
-        if constexpr (WITH_Y) {
-            s16x4 rfh[MT], rfl[MT];
+        const int64_t row0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                if (u == 0) {
-                    rfh[mt] = zfh[mt];
-                    rfl[mt] = zfl[mt];
-                } else {
-                    split4(acc_R[mt], rfh[mt], rfl[mt]);
-                }
+                const int ao = (16 * tb + lc) * G::QA_LD + 16 * mt + 4 * lg;
+                y = mma3(*reinterpret_cast<const s16x4*>(qah + ao), *reinterpret_cast<const s16x4*>(qal + ao),
+                         rfh[mt], rfl[mt], y);
             }
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            for (int jb = 0; jb <= tb; ++jb) {
+                f32x4 pt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int mt = 0; mt < MT; ++mt) {
-                    const int ao = (16 * tb + lc) * G::QA_LD + 16 * mt + 4 * lg;
-                    y = mma3(*reinterpret_cast<const s16x4*>(qah + ao), *reinterpret_cast<const s16x4*>(qal + ao),
-                             rfh[mt], rfl[mt], y);
+                    const int ao = (16 * jb + lc) * G::QA_LD + 16 * mt + 4 * lg;
+                    const int bo = (16 * tb + lc) * G::QA_LD + 16 * mt + 4 * lg;
+                    pt = mma3(*reinterpret_cast<const s16x4*>(kah + ao), *reinterpret_cast<const s16x4*>(kal + ao),
+                              *reinterpret_cast<const s16x4*>(qah + bo), *reinterpret_cast<const s16x4*>(qal + bo), pt);
                 }
+                if (jb == tb) {
 #pragma unroll
-                for (int jb = 0; jb <= tb; ++jb) {
-                    f32x4 pt = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        const int ao = (16 * jb + lc) * G::QA_LD + 16 * mt + 4 * lg;
-                        const int bo = (16 * tb + lc) * G::QA_LD + 16 * mt + 4 * lg;
-                        pt = mma3(*reinterpret_cast<const s16x4*>(kah + ao), *reinterpret_cast<const s16x4*>(kal + ao),
-                                  *reinterpret_cast<const s16x4*>(qah + bo), *reinterpret_cast<const s16x4*>(qal + bo), pt);
-                    }
-                    if (jb == tb) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (4 * lg + r > lc) pt[r] = 0.f;  // causal: j <= tau
-                    }
-                    s16x4 ph, pl;
-                    split4(pt, ph, pl);
-                    y = mma3(ph, pl, hfh[jb], hfl[jb], y);
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * lg + r > lc) pt[r] = 0.f;  // causal: j <= tau
                 }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    st_y1(p.y, bth(t0 + 16 * tb + 4 * lg + r) * D + dcol, y[r], p.y_bf16);
+                s16x4 ph, pl;
+                split4(pt, ph, pl);
+                y = mma3(ph, pl, hfh[jb], hfl[jb], y);
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                st_y1(p.y, (row0 + static_cast<int64_t>(16 * tb + 4 * lg + r) * p.H) * D + dcol, y[r], p.y_bf16);
         }
+    }
 
-        // ---- state update: R <- diag(A_end) R + W^T H ----------------------
-        if (need_state || u + C0 < C) {
+    // ---- state update: R <- diag(A_end) R + W^T H ----------------------
+    if (need_state) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                f32x4 a = acc_R[mt];
+        for (int mt = 0; mt < MT; ++mt) {
+            f32x4 a = acc_R[mt];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) a[r] *= aend[16 * mt + 4 * lg + r];
+            for (int r = 0; r < 4; ++r) a[r] *= aend[16 * mt + 4 * lg + r];
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    const int ao = (16 * mt + lc) * G::WT_LD + 16 * tb + 4 * lg;
-                    a = mma3(*reinterpret_cast<const s16x4*>(wth + ao), *reinterpret_cast<const s16x4*>(wtl + ao),
-                             hfh[tb], hfl[tb], a);
-                }
-                acc_R[mt] = a;
+            for (int tb = 0; tb < TB; ++tb) {
+                const int ao = (16 * mt + lc) * G::WT_LD + 16 * tb + 4 * lg;
+                a = mma3(*reinterpret_cast<const s16x4*>(wth + ao), *reinterpret_cast<const s16x4*>(wtl + ao),
+                         hfh[tb], hfl[tb], a);
             }
+            acc_R[mt] = a;
         }
     }
 }
 
 // Project every slot (row) of the accumulator-held state onto the unit
 // sphere: sums of squares over each wave's 16 columns, then across waves.
-template <int M, int D, int C0>
+template <int M, int D, class G>
 __device__ __forceinline__ void project_state(f32x4 (&acc)[M / 16], char* smem) {
-    using G = Cfg<M, D, C0>;
     float* np = reinterpret_cast<float*>(smem + G::O_NP);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
 #pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
+    for (int mt = 0; mt < M / 16; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float s = group_sum<16>(acc[mt][r] * acc[mt][r]);
+            const float s = row16_sum(acc[mt][r] * acc[mt][r]);
             if (lc == 0) np[w * M + 16 * mt + 4 * lg + r] = s;
         }
     __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < G::MT; ++mt)
+    for (int mt = 0; mt < M / 16; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float n2 = 0.f;
 #pragma unroll
-            for (int ww = 0; ww < G::NW; ++ww) n2 += np[ww * M + 16 * mt + 4 * lg + r];
+            for (int ww = 0; ww < D / 16; ++ww) n2 += np[ww * M + 16 * mt + 4 * lg + r];
             acc[mt][r] *= rsqrtf(n2);
         }
     __syncthreads();
@@ -421,40 +481,92 @@ __device__ __forceinline__ void store_rows(const f32x4 (&acc)[M / 16], float* ds
         for (int r = 0; r < 4; ++r) dst[(16 * mt + 4 * lg + r) * D + 16 * w + lc] = acc[mt][r];
 }
 
+// Chunk-start state Z (in acc) -> B-operand fragments and the row-major LDS
+// copy used by c = H Z^T.  The caller guarantees no wave still reads zh/zl.
+template <int M, int D, class G>
+__device__ __forceinline__ void stage_z(const f32x4 (&acc)[M / 16], s16x4 (&zfh)[M / 16], s16x4 (&zfl)[M / 16],
+                                        char* smem) {
+    short* zh = reinterpret_cast<short*>(smem + G::O_ZH);
+    short* zl = reinterpret_cast<short*>(smem + G::O_ZL);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
+#pragma unroll
+    for (int mt = 0; mt < M / 16; ++mt) {
+        split4(acc[mt], zfh[mt], zfl[mt]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * lg + r;
+            zh[row * G::ZS_LD + 16 * w + lc] = zfh[mt][r];
+            zl[row * G::ZS_LD + 16 * w + lc] = zfl[mt][r];
+        }
+    }
+}
+
 // Sequential chunk loop for one (b, h) per workgroup.
 //   WITH_Y = false, WRITE_Z = true : inter-chunk state-passing kernel; stores
 //       every chunk-start state to p.zbuf for the intra-chunk kernel.
 //   WITH_Y = true,  WRITE_Z = false: fused forward (state passing + read-out).
 template <int M, int D, int C0, bool WITH_Y, bool WRITE_Z>
 __global__ __launch_bounds__(4 * D) void osr_chunk_loop_kernel(Params p) {
-    using G = Cfg<M, D, C0>;
+    using G = Cfg<M, D, C0, WITH_Y>;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
+    short* stage = reinterpret_cast<short*>(smem + G::O_KS);
     const int bh = blockIdx.x, b = bh / p.H, hd = bh % p.H;
-    const int C = p.chunk, NC = p.T / C;
+    const int C = p.chunk, NC = p.T / C, NS = p.T / C0, SPC = C / C0;
     f32x4 acc[G::MT];
+    s16x4 zfh[G::MT], zfl[G::MT];
+    Pre<G> nxt;
     load_rows<M, D>(acc, p.state_in + static_cast<int64_t>(bh) * M * D);
-    for (int ch = 0; ch < NC; ++ch) {
-        project_state<M, D, C0>(acc, smem);
-        if constexpr (WRITE_Z)
-            store_rows<M, D>(acc, p.zbuf + (static_cast<int64_t>(bh) * NC + ch) * M * D);
-        osr_chunk<M, D, C0, WITH_Y>(p, smem, acc, b, hd, ch * C, C, true);
+    prefetch<G, WITH_Y>(nxt, p, b, hd, 0);
+    commit<G, WITH_Y>(nxt, stage);
+    for (int s = 0; s < NS; ++s) {
+        const int t0 = s * C0;
+        if (s % SPC == 0) {
+            project_state<M, D, G>(acc, smem);  // its barriers also publish the first staged inputs
+            if constexpr (WRITE_Z)
+                store_rows<M, D>(acc, p.zbuf + (static_cast<int64_t>(bh) * NC + s / SPC) * M * D);
+            stage_z<M, D, G>(acc, zfh, zfl, smem);
+        }
+        // Unconditional (the last sub-block re-reads its own tile) so the
+        // prefetch registers are never a conditionally written aggregate.
+        const bool has_next = s + 1 < NS;
+        prefetch<G, WITH_Y>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
+        osr_subblock<M, D, C0, WITH_Y>(p, smem, acc, zfh, zfl, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
+                                       stage + ((s + 1) & 1) * G::STAGE, has_next, true, b, hd, t0);
     }
-    project_state<M, D, C0>(acc, smem);
+    project_state<M, D, G>(acc, smem);
     store_rows<M, D>(acc, p.state_out + static_cast<int64_t>(bh) * M * D);
 }
 
-// Intra-chunk read-out: one workgroup per (chunk, b, h), starting from the
-// chunk-start state the state-passing kernel stored.
+// Intra-chunk read-out: each workgroup takes cpw consecutive chunks of one
+// (b, h), each starting from the chunk-start state the state-passing kernel
+// stored.
 template <int M, int D, int C0>
-__global__ __launch_bounds__(4 * D) void osr_intra_chunk_kernel(Params p) {
-    using G = Cfg<M, D, C0>;
+__global__ __launch_bounds__(4 * D) void osr_intra_chunk_kernel(Params p, int cpw) {
+    using G = Cfg<M, D, C0, true>;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
-    const int BH = p.B * p.H, C = p.chunk, NC = p.T / C;
-    const int ch = blockIdx.x / BH, bh = blockIdx.x % BH;
+    short* stage = reinterpret_cast<short*>(smem + G::O_KS);
+    const int C = p.chunk, NC = p.T / C, SPC = C / C0;
+    const int groups = NC / cpw;
+    const int bh = blockIdx.x / groups, grp = blockIdx.x % groups;
     const int b = bh / p.H, hd = bh % p.H;
+    const int ch0 = grp * cpw, NS = cpw * SPC;
     f32x4 acc[G::MT];
-    load_rows<M, D>(acc, p.zbuf + (static_cast<int64_t>(bh) * NC + ch) * M * D);
-    osr_chunk<M, D, C0, true>(p, smem, acc, b, hd, ch * C, C, false);
+    s16x4 zfh[G::MT], zfl[G::MT];
+    Pre<G> nxt;
+    prefetch<G, true>(nxt, p, b, hd, ch0 * C);
+    commit<G, true>(nxt, stage);
+    for (int s = 0; s < NS; ++s) {
+        const int ch = ch0 + s / SPC, t0 = ch0 * C + s * C0;
+        if (s % SPC == 0) {
+            load_rows<M, D>(acc, p.zbuf + (static_cast<int64_t>(bh) * NC + ch) * M * D);
+            __syncthreads();  // previous chunk's readers of Z are done; first staged inputs visible
+            stage_z<M, D, G>(acc, zfh, zfl, smem);
+        }
+        const bool has_next = s + 1 < NS;
+        prefetch<G, true>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
+        osr_subblock<M, D, C0, true>(p, smem, acc, zfh, zfl, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
+                                     stage + ((s + 1) & 1) * G::STAGE, has_next, (s + 1) % SPC != 0, b, hd, t0);
+    }
 }
 
 }  // namespace mfma
