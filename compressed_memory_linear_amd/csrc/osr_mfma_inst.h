@@ -15,13 +15,17 @@ namespace mfma {
 // (no spills) where possible, and the read-out kernels at <= 32 because their
 // causal block grows as C0^2.
 template <int M, int D, bool WITH_Y>
+constexpr bool fits_c0(int c0) {
+    return c0 == 64 ? fits<M, D, 64, WITH_Y>() : c0 == 32 ? fits<M, D, 32, WITH_Y>() : fits<M, D, 16, WITH_Y>();
+}
+template <int M, int D, bool WITH_Y>
 constexpr int pick_c0(int C) {
     int c0;
     if (WITH_Y)
         c0 = D == 128 ? 16 : 32;
     else
         c0 = M * D <= 64 * 32 ? 64 : (M == 128 && D == 128 ? 16 : 32);
-    while (c0 > 16 && (c0 > C || !(WITH_Y ? fits<M, D, 32, true>() : fits<M, D, 32, false>()))) c0 /= 2;
+    while (c0 > 16 && (c0 > C || !fits_c0<M, D, WITH_Y>(c0))) c0 /= 2;
     return c0;
 }
 

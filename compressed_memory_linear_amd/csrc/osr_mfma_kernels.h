@@ -52,6 +52,19 @@ __device__ __forceinline__ f32x4 mma3(s16x4 ah, s16x4 al, s16x4 bh, s16x4 bl, f3
     return mma(ah, bh, c);
 }
 
+// v_mfma_f32_16x16x32_bf16: twice the k of the 16x16x16 form at the same
+// issue cost.  Lane l holds A[l%16][8(l/16)+j] and B[8(l/16)+j][l%16].
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mma32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma32x3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+    c = mma32(al, bh, c);
+    c = mma32(ah, bl, c);
+    return mma32(ah, bh, c);
+}
+__device__ __forceinline__ bf16x8 ld8(const short* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
 __device__ __forceinline__ short bf16_bits(float x) {
     return __builtin_bit_cast(short, static_cast<__bf16>(x));
 }
@@ -88,7 +101,12 @@ struct Cfg {
     static constexpr int HS_LD = D + PAD;
     static constexpr int QA_LD = M + PAD;
     static constexpr int WT_LD = C0 + PAD;
+    static constexpr int HT_LD = C0 + PAD;
     static constexpr int VS_LD = D + PAD;
+    // Which contractions run as 16x16x32 (their k extent is a multiple of 32).
+    static constexpr bool K32_M = M % 32 == 0;   // H = K Z (k = slot)
+    static constexpr bool K32_D = D % 32 == 0;   // c = H Z^T (k = column)
+    static constexpr bool K32_C = C0 % 32 == 0;  // R += W^T H (k = token)
     static constexpr int GS_LD = M;                        // gamma / q tiles (unpadded)
     // 16-byte pieces of the staged tiles, and pieces per thread.
     static constexpr int KPC = C0 * M / 8, KPT = (KPC + NT - 1) / NT;
@@ -110,7 +128,9 @@ struct Cfg {
     static constexpr int O_HH = O_KS + 2 * STAGE * 2;               // H hi  [C0][HS_LD]
     static constexpr int O_HL = O_HH + C0 * HS_LD * 2;              // H lo
     static constexpr int O_HP = O_HL + C0 * HS_LD * 2;              // |h|^2 partials [NW][C0]
-    static constexpr int O_WH = O_HP + NW * C0 * 4;                 // W^T hi [M][WT_LD]
+    static constexpr int O_TH = O_HP + NW * C0 * 4;                 // H^T hi [D][HT_LD]
+    static constexpr int O_TL = O_TH + (K32_C ? D * HT_LD * 2 : 0); // H^T lo
+    static constexpr int O_WH = O_TL + (K32_C ? D * HT_LD * 2 : 0); // W^T hi [M][WT_LD]
     static constexpr int O_WL = O_WH + M * WT_LD * 2;               // W^T lo
     static constexpr int O_AE = O_WL + M * WT_LD * 2;               // A_end [M]
     static constexpr int O_NP = O_AE + M * 4;                       // norm partials [NW][M]
@@ -236,6 +256,7 @@ __device__ __forceinline__ void group_scan(float x, int lg, float& excl_lo, floa
 template <int M, int D, int C0, bool WITH_Y>
 __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 (&acc_R)[M / 16],
                                              const s16x4 (&zfh)[M / 16], const s16x4 (&zfl)[M / 16],
+                                             const bf16x8 (&z8h)[(M + 31) / 32], const bf16x8 (&z8l)[(M + 31) / 32],
                                              bool r_is_z, const short* st,
                                              const Pre<Cfg<M, D, C0, WITH_Y>>& nxt, short* st_next,
                                              bool has_next, bool need_state, int b, int hd, int t0) {
@@ -257,6 +278,8 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
     short* hsh = reinterpret_cast<short*>(smem + G::O_HH);
     short* hsl = reinterpret_cast<short*>(smem + G::O_HL);
     float* hp = reinterpret_cast<float*>(smem + G::O_HP);
+    short* hth = reinterpret_cast<short*>(smem + G::O_TH);
+    short* htl = reinterpret_cast<short*>(smem + G::O_TL);
     short* wth = reinterpret_cast<short*>(smem + G::O_WH);
     short* wtl = reinterpret_cast<short*>(smem + G::O_WL);
     float* aend = reinterpret_cast<float*>(smem + G::O_AE);
@@ -272,24 +295,50 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
     for (int tb = 0; tb < TB; ++tb) {
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
         if (p.mode == 0) {
+            if constexpr (G::K32_M) {
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const s16x4 kf = *reinterpret_cast<const s16x4*>(ks + (16 * tb + lc) * G::KS_LD + 16 * mt + 4 * lg);
-                a = mma(kf, zfl[mt], a);
-                a = mma(kf, zfh[mt], a);
+                for (int km = 0; km < M / 32; ++km) {
+                    const bf16x8 kf = ld8(ks + (16 * tb + lc) * G::KS_LD + 32 * km + 8 * lg);
+                    a = mma32(kf, z8l[km], a);
+                    a = mma32(kf, z8h[km], a);
+                }
+            } else {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) {
+                    const s16x4 kf = *reinterpret_cast<const s16x4*>(ks + (16 * tb + lc) * G::KS_LD + 16 * mt + 4 * lg);
+                    a = mma(kf, zfl[mt], a);
+                    a = mma(kf, zfh[mt], a);
+                }
             }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) a[r] -= bf16_val(vs[(16 * tb + 4 * lg + r) * G::VS_LD + dcol]);
         accH[tb] = a;
         split4(a, hfh[tb], hfl[tb]);
+        if constexpr (G::K32_C) {
+            *reinterpret_cast<s16x4*>(hth + dcol * G::HT_LD + 16 * tb + 4 * lg) = hfh[tb];
+            *reinterpret_cast<s16x4*>(htl + dcol * G::HT_LD + 16 * tb + 4 * lg) = hfl[tb];
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 16 * tb + 4 * lg + r;
             hsh[row * G::HS_LD + dcol] = hfh[tb][r];
             hsl[row * G::HS_LD + dcol] = hfl[tb][r];
-            const float sq = row16_sum(a[r] * a[r]);
-            if (lc == 0) hp[w * C0 + row] = sq;
+        }
+    }
+    // |h_t|^2 partial sums over this wave's 16 columns: all reductions first,
+    // then one guarded block of stores.
+    {
+        float sq[TB][4];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sq[tb][r] = row16_sum(accH[tb][r] * accH[tb][r]);
+        if (lc == 0) {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hp[w * C0 + 16 * tb + 4 * lg + r] = sq[tb][r];
         }
     }
     __syncthreads();  // (A) H, |h|^2 partials visible
@@ -304,12 +353,21 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (G::K32_D) {
 #pragma unroll
-                for (int kd = 0; kd < D / 16; ++kd) {
-                    const int ao = (16 * tb + lc) * G::HS_LD + 16 * kd + 4 * lg;
-                    const int bo = (16 * mb + lc) * G::ZS_LD + 16 * kd + 4 * lg;
-                    c = mma3(*reinterpret_cast<const s16x4*>(hsh + ao), *reinterpret_cast<const s16x4*>(hsl + ao),
-                             *reinterpret_cast<const s16x4*>(zh + bo), *reinterpret_cast<const s16x4*>(zl + bo), c);
+                    for (int kd = 0; kd < D / 32; ++kd) {
+                        const int ao = (16 * tb + lc) * G::HS_LD + 32 * kd + 8 * lg;
+                        const int bo = (16 * mb + lc) * G::ZS_LD + 32 * kd + 8 * lg;
+                        c = mma32x3(ld8(hsh + ao), ld8(hsl + ao), ld8(zh + bo), ld8(zl + bo), c);
+                    }
+                } else {
+#pragma unroll
+                    for (int kd = 0; kd < D / 16; ++kd) {
+                        const int ao = (16 * tb + lc) * G::HS_LD + 16 * kd + 4 * lg;
+                        const int bo = (16 * mb + lc) * G::ZS_LD + 16 * kd + 4 * lg;
+                        c = mma3(*reinterpret_cast<const s16x4*>(hsh + ao), *reinterpret_cast<const s16x4*>(hsl + ao),
+                                 *reinterpret_cast<const s16x4*>(zh + bo), *reinterpret_cast<const s16x4*>(zl + bo), c);
+                    }
                 }
                 float prod = 1.f;
 #pragma unroll
@@ -322,7 +380,7 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
                     const float mu = bf16_val(mus[tau]);
                     const float a = bf16_val(gslot ? gs[tau * G::GS_LD + i] : gts[tau]) * k;
                     const float wv = fmaxf(fmaf(-c[r], c[r], hh), 0.f);
-                    const float beta = rsqrtf(fmaf(mu, mu, a * a * wv));
+                    const float beta = __builtin_amdgcn_rsqf(fmaf(mu, mu, a * a * wv));
                     gt[tb][r] = beta * fmaf(a, c[r], mu);
                     kp[tb][r] = -beta * a;
                     prod *= gt[tb][r];
@@ -426,11 +484,20 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
             f32x4 a = acc_R[mt];
 #pragma unroll
             for (int r = 0; r < 4; ++r) a[r] *= aend[16 * mt + 4 * lg + r];
+            if constexpr (G::K32_C) {
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const int ao = (16 * mt + lc) * G::WT_LD + 16 * tb + 4 * lg;
-                a = mma3(*reinterpret_cast<const s16x4*>(wth + ao), *reinterpret_cast<const s16x4*>(wtl + ao),
-                         hfh[tb], hfl[tb], a);
+                for (int kt = 0; kt < C0 / 32; ++kt) {
+                    const int ao = (16 * mt + lc) * G::WT_LD + 32 * kt + 8 * lg;
+                    const int bo = dcol * G::HT_LD + 32 * kt + 8 * lg;
+                    a = mma32x3(ld8(wth + ao), ld8(wtl + ao), ld8(hth + bo), ld8(htl + bo), a);
+                }
+            } else {
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int ao = (16 * mt + lc) * G::WT_LD + 16 * tb + 4 * lg;
+                    a = mma3(*reinterpret_cast<const s16x4*>(wth + ao), *reinterpret_cast<const s16x4*>(wtl + ao),
+                             hfh[tb], hfl[tb], a);
+                }
             }
             acc_R[mt] = a;
         }
@@ -443,13 +510,19 @@ template <int M, int D, class G>
 __device__ __forceinline__ void project_state(f32x4 (&acc)[M / 16], char* smem) {
     float* np = reinterpret_cast<float*>(smem + G::O_NP);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
+    // All row sums first (independent DPP chains the compiler can interleave),
+    // then a single guarded block of stores.
+    float ss[M / 16][4];
 #pragma unroll
     for (int mt = 0; mt < M / 16; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float s = row16_sum(acc[mt][r] * acc[mt][r]);
-            if (lc == 0) np[w * M + 16 * mt + 4 * lg + r] = s;
-        }
+        for (int r = 0; r < 4; ++r) ss[mt][r] = row16_sum(acc[mt][r] * acc[mt][r]);
+    if (lc == 0) {
+#pragma unroll
+        for (int mt = 0; mt < M / 16; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) np[w * M + 16 * mt + 4 * lg + r] = ss[mt][r];
+    }
     __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < M / 16; ++mt)
@@ -458,7 +531,7 @@ __device__ __forceinline__ void project_state(f32x4 (&acc)[M / 16], char* smem) 
             float n2 = 0.f;
 #pragma unroll
             for (int ww = 0; ww < D / 16; ++ww) n2 += np[ww * M + 16 * mt + 4 * lg + r];
-            acc[mt][r] *= rsqrtf(n2);
+            acc[mt][r] *= __builtin_amdgcn_rsqf(n2);
         }
     __syncthreads();
 }
@@ -485,7 +558,7 @@ __device__ __forceinline__ void store_rows(const f32x4 (&acc)[M / 16], float* ds
 // copy used by c = H Z^T.  The caller guarantees no wave still reads zh/zl.
 template <int M, int D, class G>
 __device__ __forceinline__ void stage_z(const f32x4 (&acc)[M / 16], s16x4 (&zfh)[M / 16], s16x4 (&zfl)[M / 16],
-                                        char* smem) {
+                                        bf16x8 (&z8h)[(M + 31) / 32], bf16x8 (&z8l)[(M + 31) / 32], char* smem) {
     short* zh = reinterpret_cast<short*>(smem + G::O_ZH);
     short* zl = reinterpret_cast<short*>(smem + G::O_ZL);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
@@ -498,6 +571,19 @@ __device__ __forceinline__ void stage_z(const f32x4 (&acc)[M / 16], s16x4 (&zfh)
             zh[row * G::ZS_LD + 16 * w + lc] = zfh[mt][r];
             zl[row * G::ZS_LD + 16 * w + lc] = zfl[mt][r];
         }
+    }
+    if constexpr (G::K32_M) {
+        // B operands of H = K Z with k = slot: 8 consecutive slots of this
+        // lane's column.  The column belongs to this wave, so its own LDS
+        // writes above are all it reads (no barrier needed).
+#pragma unroll
+        for (int km = 0; km < M / 32; ++km)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int row = 32 * km + 8 * lg + j;
+                z8h[km][j] = __builtin_bit_cast(__bf16, zh[row * G::ZS_LD + 16 * w + lc]);
+                z8l[km][j] = __builtin_bit_cast(__bf16, zl[row * G::ZS_LD + 16 * w + lc]);
+            }
     }
 }
 
@@ -514,23 +600,27 @@ __global__ __launch_bounds__(4 * D) void osr_chunk_loop_kernel(Params p) {
     const int C = p.chunk, NC = p.T / C, NS = p.T / C0, SPC = C / C0;
     f32x4 acc[G::MT];
     s16x4 zfh[G::MT], zfl[G::MT];
+    bf16x8 z8h[(M + 31) / 32], z8l[(M + 31) / 32];
     Pre<G> nxt;
     load_rows<M, D>(acc, p.state_in + static_cast<int64_t>(bh) * M * D);
     prefetch<G, WITH_Y>(nxt, p, b, hd, 0);
     commit<G, WITH_Y>(nxt, stage);
     for (int s = 0; s < NS; ++s) {
         const int t0 = s * C0;
-        if (s % SPC == 0) {
-            project_state<M, D, G>(acc, smem);  // its barriers also publish the first staged inputs
-            if constexpr (WRITE_Z)
-                store_rows<M, D>(acc, p.zbuf + (static_cast<int64_t>(bh) * NC + s / SPC) * M * D);
-            stage_z<M, D, G>(acc, zfh, zfl, smem);
-        }
         // Unconditional (the last sub-block re-reads its own tile) so the
         // prefetch registers are never a conditionally written aggregate.
+        // Issued before the chunk-start stores below: the memory counter
+        // retires in order, so loads issued after those stores would make
+        // the commit wait for the stores as well.
         const bool has_next = s + 1 < NS;
+        if (s % SPC == 0) project_state<M, D, G>(acc, smem);  // its barriers also publish the first staged inputs
         prefetch<G, WITH_Y>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
-        osr_subblock<M, D, C0, WITH_Y>(p, smem, acc, zfh, zfl, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
+        if (s % SPC == 0) {
+            if constexpr (WRITE_Z)
+                store_rows<M, D>(acc, p.zbuf + (static_cast<int64_t>(bh) * NC + s / SPC) * M * D);
+            stage_z<M, D, G>(acc, zfh, zfl, z8h, z8l, smem);
+        }
+        osr_subblock<M, D, C0, WITH_Y>(p, smem, acc, zfh, zfl, z8h, z8l, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
                                        stage + ((s + 1) & 1) * G::STAGE, has_next, true, b, hd, t0);
     }
     project_state<M, D, G>(acc, smem);
@@ -552,6 +642,7 @@ __global__ __launch_bounds__(4 * D) void osr_intra_chunk_kernel(Params p, int cp
     const int ch0 = grp * cpw, NS = cpw * SPC;
     f32x4 acc[G::MT];
     s16x4 zfh[G::MT], zfl[G::MT];
+    bf16x8 z8h[(M + 31) / 32], z8l[(M + 31) / 32];
     Pre<G> nxt;
     prefetch<G, true>(nxt, p, b, hd, ch0 * C);
     commit<G, true>(nxt, stage);
@@ -560,11 +651,11 @@ __global__ __launch_bounds__(4 * D) void osr_intra_chunk_kernel(Params p, int cp
         if (s % SPC == 0) {
             load_rows<M, D>(acc, p.zbuf + (static_cast<int64_t>(bh) * NC + ch) * M * D);
             __syncthreads();  // previous chunk's readers of Z are done; first staged inputs visible
-            stage_z<M, D, G>(acc, zfh, zfl, smem);
+            stage_z<M, D, G>(acc, zfh, zfl, z8h, z8l, smem);
         }
         const bool has_next = s + 1 < NS;
         prefetch<G, true>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
-        osr_subblock<M, D, C0, true>(p, smem, acc, zfh, zfl, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
+        osr_subblock<M, D, C0, true>(p, smem, acc, zfh, zfl, z8h, z8l, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
                                      stage + ((s + 1) & 1) * G::STAGE, has_next, (s + 1) % SPC != 0, b, hd, t0);
     }
 }
