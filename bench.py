@@ -174,6 +174,16 @@ def main() -> int:
         return 1
     osr.load_library()
 
+    if args.only == "copy":
+        # Plain device-to-device copy of 256 MiB: the reference for scaling the
+        # FETCH_SIZE / WRITE_SIZE counters (it moves exactly 256 MiB each way).
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"only": "copy", "bytes_each_way": 256 << 20, "launches": args.warmup + args.steps}))
+        return 0
     if args.only:
         name, entry, chunk = args.only.split(":")
         case = Case(name, entry, int(chunk))
