@@ -58,6 +58,15 @@ int check_buffers(const lattice_osr_desc* d, const void* q, const void* k, const
     if (!q || !k || !v || !gamma || !mu || !sin || !sout || !y) return LATTICE_OSR_ERR_NULL;
     if (ws_needed > 0 && !ws) return LATTICE_OSR_ERR_NULL;
     if (ws_bytes < ws_needed) return LATTICE_OSR_ERR_WORKSPACE;
+    // The kernels move the per-slot and per-column tensors in 16-byte pieces;
+    // mu and a per-token gamma are read element by element.
+    const size_t ein_align = d->in_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const void* vec[] = {q, k, v, d->gamma_per_slot ? gamma : nullptr, sin, sout, y, ws};
+    for (const void* ptr : vec)
+        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return LATTICE_OSR_ERR_ALIGN;
+    const void* elem[] = {mu, gamma};
+    for (const void* ptr : elem)
+        if (reinterpret_cast<uintptr_t>(ptr) % ein_align != 0) return LATTICE_OSR_ERR_ALIGN;
 
     const size_t ein = d->in_dtype == LATTICE_OSR_BF16 ? 2 : 4;
     const size_t ey = d->y_dtype == LATTICE_OSR_BF16 ? 2 : 4;
@@ -119,6 +128,7 @@ const char* lattice_osr_status_string(int status) {
         case LATTICE_OSR_ERR_WORKSPACE: return "workspace too small";
         case LATTICE_OSR_ERR_LAUNCH: return "kernel launch failed";
         case LATTICE_OSR_ERR_ALIAS: return "forbidden overlap between arguments";
+        case LATTICE_OSR_ERR_ALIGN: return "misaligned pointer argument";
         default: return "unknown status";
     }
 }

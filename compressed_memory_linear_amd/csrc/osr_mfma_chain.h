@@ -1,0 +1,460 @@
+// osr_mfma_chain.h -- inter-chunk state passing of the chunk-wise OSR forward
+// on gfx950 matrix cores.
+//
+// Method: "Lattice: Learning to Efficiently Compress the Memory" (arXiv
+// 2504.05646), section "Parallel and Hardware Efficient Form", eq.
+// recurrence_linear2: inside a chunk every projection, gate and h_t is taken at
+// the unit-projected chunk-start state Z, so the chunk-end state is
+//   R_end = diag(A_C) Z + sum_t diag(kappa_t (.) prod_{l > t} g_l) 1 h_t^T
+// with H = K Z - V (decoding) or -V (similarity), c = H Z^T,
+// a = gamma (.) k, w = max(|h|^2 - c^2, 0), beta = (mu^2 + a^2 w)^(-1/2)
+// (appendix "Computing beta"), g = beta (mu + a c), kappa = -beta a.  This
+// kernel only carries that state from chunk to chunk (one workgroup per
+// (b, h), sequential over chunks) and stores every chunk-start state Z for the
+// read-out kernel, which then runs in parallel over chunks.
+//
+// Work layout (transposed relative to the read-out kernels): one workgroup of
+// m/16 waves; wave w owns the slot rows [16w, 16w + 16) of the state for all d
+// columns, held as MFMA accumulator tiles of R^T (lane (lg, lc) of tile j
+// holds R[16w + lc][16j + 4lg + r]).  With that ownership
+//   * the per-slot projection onto the unit sphere is wave-local;
+//   * the tiles of Z^T are, as they stand, B operands of c = H Z^T for the
+//     wave's own slots, whose gates the same wave forms;
+//   * the gated suffix products W (tokens x slots) come out of the gate phase
+//     already in the B-operand layout of the update R^T += H^T W, and A_end is
+//     a per-lane scalar;
+// so a sub-block needs one workgroup barrier after H is written (plus one at
+// its start that publishes Z, the staged inputs and frees the H buffers).
+// H = K Z - V contracts over slots, which span all waves: Z^T goes through
+// LDS once per chunk and the H tiles are shared through LDS in both the
+// token-major (for c) and the column-major (for the update) layout.
+//
+// 16x16x32 operands built from accumulator tiles use a permuted k order: two
+// D-layout tiles t0, t1 (lane (lg, lc) holds rows 4lg..4lg+3 of column lc)
+// concatenated form a B operand whose k index 8lg + j stands for row
+// 16(j/4) + 4lg + j%4 of the 32-row block; the matching A operand is read from
+// LDS as two 8-byte pieces at columns 4lg and 16 + 4lg of the block.  Any
+// bijection of k leaves the contraction unchanged.
+#pragma once
+
+#include "osr_mfma_kernels.h"
+
+namespace osr {
+namespace mfma {
+
+template <int M, int D, int C0>
+struct ChainCfg {
+    static constexpr int M_ = M, D_ = D, C0_ = C0;
+    static constexpr int NW = M / 16;  // wave w owns slots [16w, 16w + 16)
+    static constexpr int NT = 64 * NW;
+    static constexpr int DB = D / 16;   // column tiles
+    static constexpr int TB = C0 / 16;  // token tiles per sub-block
+    // H = K Z - V work split: TG waves take distinct token tiles, and the WS
+    // waves that share a token tile split its column tiles; WSE of those have
+    // work (WSE partial |h|^2 sums per token).
+    static constexpr int TG = TB < NW ? TB : NW;
+    static constexpr int WS = NW / TG;
+    static constexpr int WSE = WS < DB ? WS : DB;
+    static constexpr int TPW = TB / TG;   // token tiles per wave
+    static constexpr int DPW = DB / WSE;  // column tiles per wave
+    static constexpr int PAD = 8;         // bf16 elements of row padding
+    static constexpr int ZT_LD = M + PAD;
+    static constexpr int KS_LD = M + PAD;
+    static constexpr int VS_LD = D + PAD;
+    static constexpr int HS_LD = D + PAD;
+    static constexpr int HT_LD = C0 + PAD;
+    static constexpr int GS_LD = M;
+    static constexpr bool K32_M = M % 32 == 0;   // H = K Z     (k = slot)
+    static constexpr bool K32_D = D % 32 == 0;   // c = H Z^T   (k = column)
+    static constexpr bool K32_C = C0 % 32 == 0;  // R^T += H^T W (k = token)
+    // Staged inputs, as in the read-out kernels (no q).
+    static constexpr int KPC = C0 * M / 8, KPT = (KPC + NT - 1) / NT;
+    static constexpr int VPC = C0 * D / 8, VPT = (VPC + NT - 1) / NT;
+    static constexpr int SO_K = 0;
+    static constexpr int SO_V = SO_K + C0 * KS_LD;
+    static constexpr int SO_G = SO_V + C0 * VS_LD;
+    static constexpr int SO_Q = SO_G + C0 * GS_LD;
+    static constexpr int SO_MU = SO_Q;
+    static constexpr int SO_GT = SO_MU + C0;
+    static constexpr int STAGE = SO_GT + C0;
+    // LDS layout (bytes).
+    static constexpr int O_ZTH = 0;                          // Z^T hi [D][ZT_LD]
+    static constexpr int O_ZTL = O_ZTH + D * ZT_LD * 2;      // Z^T lo
+    static constexpr int O_KS = O_ZTL + D * ZT_LD * 2;       // staging [2][STAGE]
+    static constexpr int O_HH = O_KS + 2 * STAGE * 2;        // H hi   [C0][HS_LD]
+    static constexpr int O_HL = O_HH + C0 * HS_LD * 2;       // H lo
+    static constexpr int O_TH = O_HL + C0 * HS_LD * 2;       // H^T hi [D][HT_LD]
+    static constexpr int O_TL = O_TH + D * HT_LD * 2;        // H^T lo
+    static constexpr int O_HP = O_TL + D * HT_LD * 2;        // |h|^2 partials [C0][WSE]
+    static constexpr int BYTES = O_HP + C0 * WSE * 4;
+
+    static_assert(M % 16 == 0 && D % 16 == 0 && C0 % 16 == 0, "tile multiples");
+    static_assert(NT <= 1024, "waves");
+};
+
+template <int M, int D, int C0>
+constexpr bool chain_fits() {
+    return ChainCfg<M, D, C0>::BYTES <= 160 * 1024;
+}
+
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Two D-layout tiles -> one permuted 32-k operand.
+__device__ __forceinline__ bf16x8 cat8(s16x4 a, s16x4 b) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// The matching operand read from LDS: p points at column 4lg of a 32-column block.
+__device__ __forceinline__ bf16x8 ld8p(const short* p) {
+    return cat8(*reinterpret_cast<const s16x4*>(p), *reinterpret_cast<const s16x4*>(p + 16));
+}
+__device__ __forceinline__ s16x4 ld4s(const short* p) { return *reinterpret_cast<const s16x4*>(p); }
+
+// Reductions over the four 16-lane rows of a wave, per lane column, with the
+// gfx950 row swaps: permlane16_swap(x, x) gives every row the value of the
+// even and of the odd row of its pair (rows 0/1, 2/3); permlane32_swap(y, y)
+// gives the values of rows 0/1 and of rows 2/3 when y is uniform per pair.
+__device__ __forceinline__ void pair_rows(float x, float& even, float& odd) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    even = __uint_as_float(r[0]);
+    odd = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void half_rows(float y, float& lo, float& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+    float e, o, lo, hi;
+    pair_rows(x, e, o);
+    half_rows(e + o, lo, hi);
+    return lo + hi;
+}
+// Products over the rows of x per lane column: below = rows < lg, above =
+// rows > lg, total = all four.
+__device__ __forceinline__ void rows4_prod_scan(float x, int lg, float& below, float& above, float& total) {
+    float e, o, lo, hi;
+    pair_rows(x, e, o);
+    half_rows(e * o, lo, hi);
+    total = lo * hi;
+    below = ((lg & 1) ? e : 1.f) * ((lg & 2) ? lo : 1.f);
+    above = ((lg & 1) ? 1.f : o) * ((lg & 2) ? 1.f : hi);
+}
+
+// Unit-sphere projection of the wave's slot rows (eq. normalized_recurrence):
+// lane (lg, lc) holds 4 columns of slot lc per tile; the row sum adds the
+// four lane rows.
+template <int DB>
+__device__ __forceinline__ float row_inv_norm(const f32x4 (&acc)[DB]) {
+    float n2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < DB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) n2 = fmaf(acc[j][r], acc[j][r], n2);
+    return __builtin_amdgcn_rsqf(rows4_sum(n2));
+}
+
+template <int M, int D, int C0, bool WRITE_Z>
+__global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
+    using G = ChainCfg<M, D, C0>;
+    constexpr int DB = G::DB, TB = G::TB;
+    __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
+    short* stage = reinterpret_cast<short*>(smem + G::O_KS);
+    short* zth = reinterpret_cast<short*>(smem + G::O_ZTH);
+    short* ztl = reinterpret_cast<short*>(smem + G::O_ZTL);
+    short* hsh = reinterpret_cast<short*>(smem + G::O_HH);
+    short* hsl = reinterpret_cast<short*>(smem + G::O_HL);
+    short* hth = reinterpret_cast<short*>(smem + G::O_TH);
+    short* htl = reinterpret_cast<short*>(smem + G::O_TL);
+    float* hp = reinterpret_cast<float*>(smem + G::O_HP);
+
+    const int bh = blockIdx.x, b = bh / p.H, hd = bh % p.H;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lg = lane >> 4, lc = lane & 15;
+    const int slot = 16 * w + lc;
+    const int C = p.chunk, NC = p.T / C, NS = p.T / C0, SPC = C / C0;
+    const bool gslot = p.gamma_per_slot != 0;
+    // H = K Z - V assignment of this wave.
+    const int g1_tb0 = w % G::TG, g1_grp = w / G::TG;
+    const bool g1_active = g1_grp < G::WSE;
+
+    f32x4 acc[DB];             // R^T tiles: acc[j][r] = R[slot][16j + 4lg + r]
+    s16x4 zfh[DB], zfl[DB];    // split Z^T tiles: B operands of c = H Z^T
+    Pre<G> nxt;
+
+    {
+        const float* src = p.state_in + static_cast<int64_t>(bh) * M * D + static_cast<int64_t>(slot) * D + 4 * lg;
+#pragma unroll
+        for (int j = 0; j < DB; ++j) acc[j] = *reinterpret_cast<const f32x4*>(src + 16 * j);
+    }
+    prefetch<G, false>(nxt, p, b, hd, 0);
+    commit<G, false>(nxt, stage);
+
+    for (int s = 0; s < NS; ++s) {
+        const int t0 = s * C0;
+        const bool chunk_start = s % SPC == 0;
+        const bool has_next = s + 1 < NS;
+        const short* st = stage + (s & 1) * G::STAGE;
+        const short* ks = st + G::SO_K;
+        const short* vs = st + G::SO_V;
+        const short* gs = st + G::SO_G;
+        const short* mus = st + G::SO_MU;
+        const short* gts = st + G::SO_GT;
+
+        if (chunk_start) {
+            const float inv = row_inv_norm<DB>(acc);
+#pragma unroll
+            for (int j = 0; j < DB; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[j][r] *= inv;
+        }
+        // Loads of the next sub-block, issued before the chunk-start stores
+        // below (the memory counter retires in order).  Unconditional: the
+        // last sub-block re-reads its own tile.
+        prefetch<G, false>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
+        if (chunk_start) {
+            if constexpr (WRITE_Z) {
+                float* dst = p.zbuf + (static_cast<int64_t>(bh) * NC + s / SPC) * M * D +
+                             static_cast<int64_t>(slot) * D + 4 * lg;
+#pragma unroll
+                for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
+            }
+            // Z^T to LDS (read by every wave's H = K Z); the split tiles stay
+            // in registers.  No wave reads Z^T between the last sub-block's
+            // barrier (A) and the barrier (S) below.
+#pragma unroll
+            for (int j = 0; j < DB; ++j) {
+                split4(acc[j], zfh[j], zfl[j]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int col = 16 * j + 4 * lg + r;
+                    zth[col * G::ZT_LD + slot] = zfh[j][r];
+                    ztl[col * G::ZT_LD + slot] = zfl[j][r];
+                }
+            }
+        }
+        __syncthreads();  // (S) Z^T and this sub-block's staged inputs visible; H buffers free
+
+        // ---- H = K Z - V (token tiles x column tiles of this wave) -------
+        // Operands first, then the MFMAs of all tiles interleaved (independent
+        // accumulators), then the epilogue.
+        if (g1_active) {
+            constexpr int TPW = G::TPW, DPW = G::DPW;
+            f32x4 ha[TPW][DPW];
+#pragma unroll
+            for (int ti = 0; ti < TPW; ++ti)
+#pragma unroll
+                for (int dj = 0; dj < DPW; ++dj) ha[ti][dj] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (p.mode == 0) {
+                if constexpr (G::K32_M) {
+                    constexpr int KM = M / 32;
+                    bf16x8 kf[TPW][KM];
+#pragma unroll
+                    for (int ti = 0; ti < TPW; ++ti)
+#pragma unroll
+                        for (int km = 0; km < KM; ++km)
+                            kf[ti][km] = ld8(ks + (16 * (g1_tb0 + G::TG * ti) + lc) * G::KS_LD + 32 * km + 8 * lg);
+#pragma unroll
+                    for (int km = 0; km < KM; ++km) {
+                        bf16x8 zh8[DPW], zl8[DPW];
+#pragma unroll
+                        for (int dj = 0; dj < DPW; ++dj) {
+                            const int zo = (16 * (g1_grp + G::WSE * dj) + lc) * G::ZT_LD + 32 * km + 8 * lg;
+                            zh8[dj] = ld8(zth + zo);
+                            zl8[dj] = ld8(ztl + zo);
+                        }
+#pragma unroll
+                        for (int ti = 0; ti < TPW; ++ti)
+#pragma unroll
+                            for (int dj = 0; dj < DPW; ++dj) ha[ti][dj] = mma32(kf[ti][km], zl8[dj], ha[ti][dj]);
+#pragma unroll
+                        for (int ti = 0; ti < TPW; ++ti)
+#pragma unroll
+                            for (int dj = 0; dj < DPW; ++dj) ha[ti][dj] = mma32(kf[ti][km], zh8[dj], ha[ti][dj]);
+                    }
+                } else {
+                    s16x4 kf[TPW];
+#pragma unroll
+                    for (int ti = 0; ti < TPW; ++ti)
+                        kf[ti] = ld4s(ks + (16 * (g1_tb0 + G::TG * ti) + lc) * G::KS_LD + 4 * lg);
+#pragma unroll
+                    for (int dj = 0; dj < DPW; ++dj) {
+                        const int zo = (16 * (g1_grp + G::WSE * dj) + lc) * G::ZT_LD + 4 * lg;
+                        const s16x4 zh4 = ld4s(zth + zo), zl4 = ld4s(ztl + zo);
+#pragma unroll
+                        for (int ti = 0; ti < TPW; ++ti) {
+                            ha[ti][dj] = mma(kf[ti], zl4, ha[ti][dj]);
+                            ha[ti][dj] = mma(kf[ti], zh4, ha[ti][dj]);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int ti = 0; ti < TPW; ++ti) {
+                const int tb = g1_tb0 + G::TG * ti;
+                float sq[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int dj = 0; dj < DPW; ++dj) {
+                    const int dcol = 16 * (g1_grp + G::WSE * dj) + lc;
+                    f32x4 a = ha[ti][dj];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a[r] -= bf16_val(vs[(16 * tb + 4 * lg + r) * G::VS_LD + dcol]);
+                    s16x4 hh4, hl4;
+                    split4(a, hh4, hl4);
+                    *reinterpret_cast<s16x4*>(hth + dcol * G::HT_LD + 16 * tb + 4 * lg) = hh4;
+                    *reinterpret_cast<s16x4*>(htl + dcol * G::HT_LD + 16 * tb + 4 * lg) = hl4;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * tb + 4 * lg + r;
+                        hsh[row * G::HS_LD + dcol] = hh4[r];
+                        hsl[row * G::HS_LD + dcol] = hl4[r];
+                        sq[r] = fmaf(a[r], a[r], sq[r]);
+                    }
+                }
+                // |h_t|^2 over this wave's columns: reductions first, one
+                // guarded block of stores.
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sq[r] = row16_sum(sq[r]);
+                if (lc == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) hp[(16 * tb + 4 * lg + r) * G::WSE + g1_grp] = sq[r];
+                }
+            }
+        }
+        __syncthreads();  // (A) H, H^T and |h|^2 partials visible
+
+        // ---- c = H Z^T for this wave's slots; gates ------------------------
+        // Gate inputs of this wave's slots are read before the products.
+        float hh[TB][4], av[TB][4], muv[TB][4];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            if constexpr (G::WSE == 1) {
+                const f32x4 h4 = *reinterpret_cast<const f32x4*>(hp + 16 * tb + 4 * lg);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) hh[tb][r] = h4[r];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float* q4 = hp + (16 * tb + 4 * lg + r) * G::WSE;
+                    float x = 0.f;
+#pragma unroll
+                    for (int g = 0; g < G::WSE; ++g) x += q4[g];
+                    hh[tb][r] = x;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tau = 16 * tb + 4 * lg + r;
+                const float k = bf16_val(ks[tau * G::KS_LD + slot]);
+                av[tb][r] = bf16_val(gslot ? gs[tau * G::GS_LD + slot] : gts[tau]) * k;
+                muv[tb][r] = bf16_val(mus[tau]);
+            }
+        }
+        f32x4 cc[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) cc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (G::K32_D) {
+#pragma unroll
+            for (int kd = 0; kd < D / 32; ++kd) {
+                bf16x8 ah[TB], al[TB];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int ao = (16 * tb + lc) * G::HS_LD + 32 * kd + 4 * lg;
+                    ah[tb] = ld8p(hsh + ao);
+                    al[tb] = ld8p(hsl + ao);
+                }
+                const bf16x8 bh = cat8(zfh[2 * kd], zfh[2 * kd + 1]), bl = cat8(zfl[2 * kd], zfl[2 * kd + 1]);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) cc[tb] = mma32(al[tb], bh, cc[tb]);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) cc[tb] = mma32(ah[tb], bl, cc[tb]);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) cc[tb] = mma32(ah[tb], bh, cc[tb]);
+            }
+        } else {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int ao = (16 * tb + lc) * G::HS_LD + 4 * lg;
+                cc[tb] = mma3(ld4s(hsh + ao), ld4s(hsl + ao), zfh[0], zfl[0], cc[tb]);
+            }
+        }
+        float gt[TB][4], kp[TB][4], tot[TB], ex_lo[TB], ex_hi[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            float prod = 1.f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float a = av[tb][r], mu = muv[tb][r], cr = cc[tb][r];
+                const float wv = fmaxf(fmaf(-cr, cr, hh[tb][r]), 0.f);
+                const float beta = __builtin_amdgcn_rsqf(fmaf(mu, mu, a * a * wv));
+                gt[tb][r] = beta * fmaf(a, cr, mu);
+                kp[tb][r] = -beta * a;
+                prod *= gt[tb][r];
+            }
+            rows4_prod_scan(prod, lg, ex_lo[tb], ex_hi[tb], tot[tb]);
+        }
+        // W_t = kappa_t (.) prod_{l > t} g_l inside the sub-block, split into
+        // B operands of the update (k = token); A_end = prod of all g.
+        s16x4 wh4[TB], wl4[TB];
+        float aend = 1.f;
+#pragma unroll
+        for (int tb = TB - 1; tb >= 0; --tb) {
+            float s_ = aend * ex_hi[tb];
+#pragma unroll
+            for (int r = 3; r >= 0; --r) {
+                short hi, lo;
+                split1(kp[tb][r] * s_, hi, lo);
+                wh4[tb][r] = hi;
+                wl4[tb][r] = lo;
+                s_ *= gt[tb][r];
+            }
+            aend *= tot[tb];
+        }
+
+        // ---- R^T <- R^T diag(A_end) + H^T W ---------------------------------
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[db][r] *= aend;
+        if constexpr (G::K32_C) {
+#pragma unroll
+            for (int kt = 0; kt < C0 / 32; ++kt) {
+                bf16x8 th[DB], tl[DB];
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int ao = (16 * db + lc) * G::HT_LD + 32 * kt + 4 * lg;
+                    th[db] = ld8p(hth + ao);
+                    tl[db] = ld8p(htl + ao);
+                }
+                const bf16x8 bh = cat8(wh4[2 * kt], wh4[2 * kt + 1]), bl = cat8(wl4[2 * kt], wl4[2 * kt + 1]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] = mma32(tl[db], bh, acc[db]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] = mma32(th[db], bl, acc[db]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] = mma32(th[db], bh, acc[db]);
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int ao = (16 * db + lc) * G::HT_LD + 4 * lg;
+                acc[db] = mma3(ld4s(hth + ao), ld4s(htl + ao), wh4[0], wl4[0], acc[db]);
+            }
+        }
+        // Next sub-block's inputs into the other staging buffer (its last
+        // readers, the previous sub-block's gates, finished before (S)).
+        if (has_next) commit<G, false>(nxt, stage + ((s + 1) & 1) * G::STAGE);
+    }
+
+    const float inv = row_inv_norm<DB>(acc);
+    float* dst = p.state_out + static_cast<int64_t>(bh) * M * D + static_cast<int64_t>(slot) * D + 4 * lg;
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+        f32x4 z = acc[j];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[r] *= inv;
+        *reinterpret_cast<f32x4*>(dst + 16 * j) = z;
+    }
+}
+
+}  // namespace mfma
+}  // namespace osr

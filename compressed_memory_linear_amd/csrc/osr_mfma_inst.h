@@ -4,29 +4,51 @@
 #pragma once
 
 #include "osr_launch.h"
+#include "osr_mfma_chain.h"
 #include "osr_mfma_kernels.h"
 
 namespace osr {
 namespace mfma {
 
-// Sub-block length C0 (<= C).  Longer sub-blocks mean fewer barriers per
-// chunk but more live registers (gates, H fragments and the prefetched
-// inputs grow with C0); the table keeps every kernel within the register file
-// (no spills) where possible, and the read-out kernels at <= 32 because their
-// causal block grows as C0^2.
+// Sub-block length C0 (<= C) of the read-out kernels.  Longer sub-blocks
+// mean fewer barriers per chunk but more live registers (gates, H fragments
+// and the prefetched inputs grow with C0); the read-out kernels stay at <= 32
+// because their causal block grows as C0^2, and at 16 for d = 128 to stay
+// within the register file.
 template <int M, int D, bool WITH_Y>
 constexpr bool fits_c0(int c0) {
     return c0 == 64 ? fits<M, D, 64, WITH_Y>() : c0 == 32 ? fits<M, D, 32, WITH_Y>() : fits<M, D, 16, WITH_Y>();
 }
-template <int M, int D, bool WITH_Y>
-constexpr int pick_c0(int C) {
-    int c0;
-    if (WITH_Y)
-        c0 = D == 128 ? 16 : 32;
-    else
-        c0 = M * D <= 64 * 32 ? 64 : (M == 128 && D == 128 ? 16 : 32);
-    while (c0 > 16 && (c0 > C || !fits_c0<M, D, WITH_Y>(c0))) c0 /= 2;
+template <int M, int D>
+constexpr int pick_c0_readout(int C) {
+    int c0 = D == 128 ? 16 : 32;
+    while (c0 > 16 && (c0 > C || !fits_c0<M, D, true>(c0))) c0 /= 2;
     return c0;
+}
+// The state-passing kernel takes whole chunks where LDS and the register
+// file allow (one sub-block per chunk: two barriers per chunk); 64-token
+// sub-blocks spill when one lane row holds d = 128 columns of state with
+// fewer than 4 waves, or with 8 waves (2 per SIMD) from d = 64 up.
+template <int M, int D>
+constexpr bool chain_fits_c0(int c0) {
+    return c0 == 64 ? chain_fits<M, D, 64>() : c0 == 32 ? chain_fits<M, D, 32>() : chain_fits<M, D, 16>();
+}
+template <int M, int D>
+constexpr int pick_c0_chain(int C) {
+    int c0 = (D == 128 && M <= 64) || (M == 128 && D >= 64) ? 32 : 64;
+    while (c0 > 16 && (c0 > C || !chain_fits_c0<M, D>(c0))) c0 /= 2;
+    return c0;
+}
+
+template <int M, int D, int C0>
+static int launch_chain(const Params& p, hipStream_t st) {
+    if constexpr (!chain_fits<M, D, C0>()) {
+        return -3;
+    } else {
+        const unsigned BH = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H);
+        hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true>), dim3(BH), dim3(4 * M), 0, st, p);
+        return hipGetLastError() == hipSuccess ? 0 : -5;
+    }
 }
 
 template <int M, int D, int C0, bool WITH_Y, bool WRITE_Z>
@@ -61,18 +83,18 @@ static int launch_intra(const Params& p, hipStream_t st) {
 template <int M, int D>
 static int launch_md(bool split, const Params& p, hipStream_t st) {
     const int C = p.chunk;
+    const int c0 = pick_c0_readout<M, D>(C);
     if (split) {
         int rc;
-        switch (pick_c0<M, D, false>(C)) {
-            case 64: rc = launch_loop<M, D, 64, false, true>(p, st); break;
-            case 32: rc = launch_loop<M, D, 32, false, true>(p, st); break;
-            default: rc = launch_loop<M, D, 16, false, true>(p, st); break;
+        switch (pick_c0_chain<M, D>(C)) {
+            case 64: rc = launch_chain<M, D, 64>(p, st); break;
+            case 32: rc = launch_chain<M, D, 32>(p, st); break;
+            default: rc = launch_chain<M, D, 16>(p, st); break;
         }
         if (rc) return rc;
-        return pick_c0<M, D, true>(C) == 32 ? launch_intra<M, D, 32>(p, st) : launch_intra<M, D, 16>(p, st);
+        return c0 == 32 ? launch_intra<M, D, 32>(p, st) : launch_intra<M, D, 16>(p, st);
     }
-    return pick_c0<M, D, true>(C) == 32 ? launch_loop<M, D, 32, true, false>(p, st)
-                                        : launch_loop<M, D, 16, true, false>(p, st);
+    return c0 == 32 ? launch_loop<M, D, 32, true, false>(p, st) : launch_loop<M, D, 16, true, false>(p, st);
 }
 
 template <int M>

@@ -90,6 +90,7 @@ __device__ __forceinline__ void split4(f32x4 x, s16x4& hi, s16x4& lo) {
 
 template <int M, int D, int C0, bool WITH_Y>
 struct Cfg {
+    static constexpr int M_ = M, D_ = D, C0_ = C0;
     static constexpr int NW = D / 16;   // waves; wave w owns d-block w
     static constexpr int NT = 64 * NW;
     static constexpr int MT = M / 16;   // slot tiles
@@ -166,7 +167,7 @@ struct Pre {
 // make the compiler wait for it at the join.
 template <class G, bool WITH_Y>
 __device__ __forceinline__ void prefetch(Pre<G>& pf, const Params& p, int b, int hd, int t0) {
-    constexpr int M = G::MT * 16, D = G::NW * 16, C0 = G::TB * 16;
+    constexpr int M = G::M_, D = G::D_, C0 = G::C0_;
     const int tid = threadIdx.x;
     const uint16_t* kg = static_cast<const uint16_t*>(p.k);
     const uint16_t* vg = static_cast<const uint16_t*>(p.v);
@@ -198,7 +199,7 @@ __device__ __forceinline__ void prefetch(Pre<G>& pf, const Params& p, int b, int
 
 template <class G, bool WITH_Y>
 __device__ __forceinline__ void commit(const Pre<G>& pf, short* st) {
-    constexpr int M = G::MT * 16, D = G::NW * 16, C0 = G::TB * 16;
+    constexpr int M = G::M_, D = G::D_, C0 = G::C0_;
     const int tid = threadIdx.x;
 #pragma unroll
     for (int j = 0; j < G::KPT; ++j) {

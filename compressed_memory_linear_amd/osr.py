@@ -21,7 +21,7 @@ F32, BF16 = 0, 1
 MODE_DEC, MODE_SIM = 0, 1
 
 OK = 0
-ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS = -1, -2, -3, -4, -5, -6
+ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_ALIGN = -1, -2, -3, -4, -5, -6, -7
 
 EXPORTED = ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step",
             "lattice_osr_workspace_bytes", "lattice_osr_status_string", "lattice_osr_abi_version")

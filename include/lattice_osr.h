@@ -25,6 +25,9 @@
  *   mu          [B, T, H]        in_dtype
  *   y           [B, T, H, d]     y_dtype
  *   state_in/out[B, H, m, d]     float32, row i = slot s_i
+ * Alignment: q, k, v, a per-slot gamma, state_in, state_out, y and the
+ * workspace must be 16-byte aligned; mu and a per-token gamma need only
+ * element alignment (any token slice of a contiguous tensor qualifies).
  * Slots of state_in must be non-zero; every slot is projected onto the unit
  * sphere at each chunk start and once more on the returned state.
  *
@@ -78,6 +81,7 @@ extern "C" {
 #define LATTICE_OSR_ERR_WORKSPACE (-4)   /* workspace smaller than lattice_osr_workspace_bytes() */
 #define LATTICE_OSR_ERR_LAUNCH (-5)      /* the HIP launch reported an error        */
 #define LATTICE_OSR_ERR_ALIAS (-6)       /* forbidden overlap between arguments      */
+#define LATTICE_OSR_ERR_ALIGN (-7)       /* a pointer is misaligned (see Alignment)  */
 
 typedef struct {
     int32_t B;              /* batch (decode: number of sequences)               */

@@ -35,7 +35,7 @@ def test_header_declarations_are_exported():
 
 def test_abi_version_and_status_strings():
     assert osr.lattice_osr_abi_version() == 1
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = osr.status_string(code)
         assert s and s != "unknown status"
     assert osr.status_string(-99) == "unknown status"
@@ -117,12 +117,40 @@ def test_aliasing_rules():
     assert _call("lattice_osr_decode_step", d, p) == osr.ERR_ALIAS
     # y overlapping the state
     p = _ptrs(d)
-    p[7] = p[5] + state_bytes - 4
+    p[7] = p[5] + state_bytes - 16
     assert _call("lattice_osr_decode_step", d, p) == osr.ERR_ALIAS
     # state_out overlapping an input
     p = _ptrs(d)
     p[6] = p[0]
     assert _call("lattice_osr_fwd_recurrent", d, p) == osr.ERR_ALIAS
+
+
+@pytest.mark.parametrize("fn", FWD + ["lattice_osr_fwd_chunked"])
+def test_misaligned_pointers_are_rejected(fn):
+    """q, k, v, per-slot gamma, the states and y need 16-byte alignment; mu
+    and a per-token gamma only element alignment."""
+    chunk = 1 if fn == "lattice_osr_fwd_chunked" else None
+    for gps in (1, 0):
+        d = osr.make_desc(1, 1, 1, 16, 16, gamma_per_slot=gps)
+        for i in range(8):
+            if i == 4 or (i == 3 and not gps):
+                continue  # element-aligned offsets are accepted (never launched here)
+            for off in (2, 4, 8):
+                p = _ptrs(d)
+                p[i] += off
+                assert _call(fn, d, p, chunk) == osr.ERR_ALIGN, (gps, i, off)
+        # mu / per-token gamma at an odd byte offset are rejected
+        for i in ([4] if gps else [3, 4]):
+            p = _ptrs(d)
+            p[i] += 1
+            assert _call(fn, d, p, chunk) == osr.ERR_ALIGN, (gps, i)
+
+
+def test_misaligned_workspace_is_rejected():
+    d = osr.make_desc(2, 256, 2, 64, 64)
+    need = osr.lattice_osr_workspace_bytes(d, 64)
+    if need:
+        assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), 64, BASE * 4 + 8, need) == osr.ERR_ALIGN
 
 
 def test_workspace_too_small_is_rejected():
