@@ -31,11 +31,20 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+# Extra flags per source-file prefix.  The state-passing kernel keeps its MFMA
+# accumulators in VGPRs: its state tiles are rescaled, split and stored by
+# VALU code every chunk, which otherwise costs a copy out of (and back into)
+# the accumulation registers each time.  The read-out kernels need the
+# accumulation registers for capacity, so they keep the compiler's choice.
+FLAGS_BY_PREFIX = {
+    "osr_chain_": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    extra = [f for pre, fl in FLAGS_BY_PREFIX.items() if os.path.basename(src).startswith(pre) for f in fl]
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

@@ -1,0 +1,8 @@
+// osr_chain_m128.hip -- state-passing chunk kernel instantiated for m = 128 slots.
+#include "osr_chain_inst.h"
+
+namespace osr {
+namespace mfma {
+template int launch_chain_m<128>(int d, const Params& p, hipStream_t st);
+}  // namespace mfma
+}  // namespace osr

@@ -57,12 +57,16 @@ struct ChainCfg {
     static constexpr int WSE = WS < DB ? WS : DB;
     static constexpr int TPW = TB / TG;   // token tiles per wave
     static constexpr int DPW = DB / WSE;  // column tiles per wave
-    static constexpr int PAD = 8;         // bf16 elements of row padding
-    static constexpr int ZT_LD = M + PAD;
-    static constexpr int KS_LD = M + PAD;
-    static constexpr int VS_LD = D + PAD;
-    static constexpr int HS_LD = D + PAD;
-    static constexpr int HT_LD = C0 + PAD;
+    // Row strides (bf16 elements).  Buffers read as 16-byte MFMA operands
+    // (rows lc = 0..15) pad by 8: a stride of 4 (mod 8) words puts the 8 lanes
+    // of a 128-byte read phase on distinct bank quads.  The H buffers, read as
+    // 8-byte operands and written as scattered 2-byte rows 4lg + r, pad by 4:
+    // a stride of 2 (mod 4) words makes both conflict-free.
+    static constexpr int ZT_LD = M + 8;
+    static constexpr int KS_LD = M + 8;
+    static constexpr int VS_LD = D + 8;
+    static constexpr int HS_LD = D + 4;
+    static constexpr int HT_LD = C0 + 4;
     static constexpr int GS_LD = M;
     static constexpr bool K32_M = M % 32 == 0;   // H = K Z     (k = slot)
     static constexpr bool K32_D = D % 32 == 0;   // c = H Z^T   (k = column)
@@ -74,9 +78,8 @@ struct ChainCfg {
     static constexpr int SO_V = SO_K + C0 * KS_LD;
     static constexpr int SO_G = SO_V + C0 * VS_LD;
     static constexpr int SO_Q = SO_G + C0 * GS_LD;
-    static constexpr int SO_MU = SO_Q;
-    static constexpr int SO_GT = SO_MU + C0;
-    static constexpr int STAGE = SO_GT + C0;
+    static constexpr int SO_MU = SO_Q;           // mu [C0] fp32
+    static constexpr int STAGE = SO_MU + 2 * C0;
     // LDS layout (bytes).
     static constexpr int O_ZTH = 0;                          // Z^T hi [D][ZT_LD]
     static constexpr int O_ZTL = O_ZTH + D * ZT_LD * 2;      // Z^T lo
@@ -172,7 +175,6 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
     const int lg = lane >> 4, lc = lane & 15;
     const int slot = 16 * w + lc;
     const int C = p.chunk, NC = p.T / C, NS = p.T / C0, SPC = C / C0;
-    const bool gslot = p.gamma_per_slot != 0;
     // H = K Z - V assignment of this wave.
     const int g1_tb0 = w % G::TG, g1_grp = w / G::TG;
     const bool g1_active = g1_grp < G::WSE;
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
         for (int j = 0; j < DB; ++j) acc[j] = *reinterpret_cast<const f32x4*>(src + 16 * j);
     }
     prefetch<G, false>(nxt, p, b, hd, 0);
-    commit<G, false>(nxt, stage);
+    commit<G, false>(nxt, stage, p.gamma_per_slot != 0);
 
     for (int s = 0; s < NS; ++s) {
         const int t0 = s * C0;
@@ -197,8 +199,7 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
         const short* ks = st + G::SO_K;
         const short* vs = st + G::SO_V;
         const short* gs = st + G::SO_G;
-        const short* mus = st + G::SO_MU;
-        const short* gts = st + G::SO_GT;
+        const float* mus = reinterpret_cast<const float*>(st + G::SO_MU);
 
         if (chunk_start) {
             const float inv = row_inv_norm<DB>(acc);
@@ -239,11 +240,16 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
         // accumulators), then the epilogue.
         if (g1_active) {
             constexpr int TPW = G::TPW, DPW = G::DPW;
+            // Accumulators start at -V.
             f32x4 ha[TPW][DPW];
 #pragma unroll
             for (int ti = 0; ti < TPW; ++ti)
 #pragma unroll
-                for (int dj = 0; dj < DPW; ++dj) ha[ti][dj] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int dj = 0; dj < DPW; ++dj) {
+                    const int tb = g1_tb0 + G::TG * ti, dcol = 16 * (g1_grp + G::WSE * dj) + lc;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) ha[ti][dj][r] = -bf16_val(vs[(16 * tb + 4 * lg + r) * G::VS_LD + dcol]);
+                }
             if (p.mode == 0) {
                 if constexpr (G::K32_M) {
                     constexpr int KM = M / 32;
@@ -295,9 +301,7 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
 #pragma unroll
                 for (int dj = 0; dj < DPW; ++dj) {
                     const int dcol = 16 * (g1_grp + G::WSE * dj) + lc;
-                    f32x4 a = ha[ti][dj];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) a[r] -= bf16_val(vs[(16 * tb + 4 * lg + r) * G::VS_LD + dcol]);
+                    const f32x4 a = ha[ti][dj];
                     s16x4 hh4, hl4;
                     split4(a, hh4, hl4);
                     *reinterpret_cast<s16x4*>(hth + dcol * G::HT_LD + 16 * tb + 4 * lg) = hh4;
@@ -341,12 +345,13 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
                     hh[tb][r] = x;
                 }
             }
+            const f32x4 mu4 = *reinterpret_cast<const f32x4*>(mus + 16 * tb + 4 * lg);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tau = 16 * tb + 4 * lg + r;
                 const float k = bf16_val(ks[tau * G::KS_LD + slot]);
-                av[tb][r] = bf16_val(gslot ? gs[tau * G::GS_LD + slot] : gts[tau]) * k;
-                muv[tb][r] = bf16_val(mus[tau]);
+                av[tb][r] = bf16_val(gs[tau * G::GS_LD + slot]) * k;
+                muv[tb][r] = mu4[r];
             }
         }
         f32x4 cc[TB];
@@ -399,14 +404,13 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
 #pragma unroll
         for (int tb = TB - 1; tb >= 0; --tb) {
             float s_ = aend * ex_hi[tb];
+            f32x4 wv;
 #pragma unroll
             for (int r = 3; r >= 0; --r) {
-                short hi, lo;
-                split1(kp[tb][r] * s_, hi, lo);
-                wh4[tb][r] = hi;
-                wl4[tb][r] = lo;
+                wv[r] = kp[tb][r] * s_;
                 s_ *= gt[tb][r];
             }
+            split4(wv, wh4[tb], wl4[tb]);
             aend *= tot[tb];
         }
 
@@ -442,7 +446,7 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
         }
         // Next sub-block's inputs into the other staging buffer (its last
         // readers, the previous sub-block's gates, finished before (S)).
-        if (has_next) commit<G, false>(nxt, stage + ((s + 1) & 1) * G::STAGE);
+        if (has_next) commit<G, false>(nxt, stage + ((s + 1) & 1) * G::STAGE, p.gamma_per_slot != 0);
     }
 
     const float inv = row_inv_norm<DB>(acc);

@@ -4,7 +4,6 @@
 #pragma once
 
 #include "osr_launch.h"
-#include "osr_mfma_chain.h"
 #include "osr_mfma_kernels.h"
 
 namespace osr {
@@ -25,31 +24,10 @@ constexpr int pick_c0_readout(int C) {
     while (c0 > 16 && (c0 > C || !fits_c0<M, D, true>(c0))) c0 /= 2;
     return c0;
 }
-// The state-passing kernel takes whole chunks where LDS and the register
-// file allow (one sub-block per chunk: two barriers per chunk); 64-token
-// sub-blocks spill when one lane row holds d = 128 columns of state with
-// fewer than 4 waves, or with 8 waves (2 per SIMD) from d = 64 up.
-template <int M, int D>
-constexpr bool chain_fits_c0(int c0) {
-    return c0 == 64 ? chain_fits<M, D, 64>() : c0 == 32 ? chain_fits<M, D, 32>() : chain_fits<M, D, 16>();
-}
-template <int M, int D>
-constexpr int pick_c0_chain(int C) {
-    int c0 = (D == 128 && M <= 64) || (M == 128 && D >= 64) ? 32 : 64;
-    while (c0 > 16 && (c0 > C || !chain_fits_c0<M, D>(c0))) c0 /= 2;
-    return c0;
-}
-
-template <int M, int D, int C0>
-static int launch_chain(const Params& p, hipStream_t st) {
-    if constexpr (!chain_fits<M, D, C0>()) {
-        return -3;
-    } else {
-        const unsigned BH = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H);
-        hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true>), dim3(BH), dim3(4 * M), 0, st, p);
-        return hipGetLastError() == hipSuccess ? 0 : -5;
-    }
-}
+// State-passing kernel, instantiated in osr_chain_m*.hip (built with MFMA
+// results in VGPRs).
+template <int M>
+int launch_chain_m(int d, const Params& p, hipStream_t st);
 
 template <int M, int D, int C0, bool WITH_Y, bool WRITE_Z>
 static int launch_loop(const Params& p, hipStream_t st) {
@@ -85,12 +63,7 @@ static int launch_md(bool split, const Params& p, hipStream_t st) {
     const int C = p.chunk;
     const int c0 = pick_c0_readout<M, D>(C);
     if (split) {
-        int rc;
-        switch (pick_c0_chain<M, D>(C)) {
-            case 64: rc = launch_chain<M, D, 64>(p, st); break;
-            case 32: rc = launch_chain<M, D, 32>(p, st); break;
-            default: rc = launch_chain<M, D, 16>(p, st); break;
-        }
+        const int rc = launch_chain_m<M>(D, p, st);
         if (rc) return rc;
         return c0 == 32 ? launch_intra<M, D, 32>(p, st) : launch_intra<M, D, 16>(p, st);
     }

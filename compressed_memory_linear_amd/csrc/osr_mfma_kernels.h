@@ -73,19 +73,25 @@ __device__ __forceinline__ float bf16_val(short b) {
 }
 __device__ __forceinline__ float bf16u(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// x = hi + lo with hi = bf16(x), lo = bf16(x - hi).
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi) (round to nearest even).
 __device__ __forceinline__ void split1(float x, short& hi, short& lo) {
     hi = bf16_bits(x);
     lo = bf16_bits(x - bf16_val(hi));
 }
+// Four values at a time: packed conversions of pairs; the hi part of each
+// pair comes back as fp32 with a shift (low half) or a mask (high half).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ unsigned cvt2_bf16(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
 __device__ __forceinline__ void split4(f32x4 x, s16x4& hi, s16x4& lo) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        short h, l;
-        split1(x[j], h, l);
-        hi[j] = h;
-        lo[j] = l;
-    }
+    const unsigned h01 = cvt2_bf16(x[0], x[1]), h23 = cvt2_bf16(x[2], x[3]);
+    const float r0 = x[0] - __uint_as_float(h01 << 16), r1 = x[1] - __uint_as_float(h01 & 0xffff0000u);
+    const float r2 = x[2] - __uint_as_float(h23 << 16), r3 = x[3] - __uint_as_float(h23 & 0xffff0000u);
+    hi = __builtin_bit_cast(s16x4, u32x2{h01, h23});
+    lo = __builtin_bit_cast(s16x4, u32x2{cvt2_bf16(r0, r1), cvt2_bf16(r2, r3)});
 }
 
 template <int M, int D, int C0, bool WITH_Y>
@@ -112,15 +118,15 @@ struct Cfg {
     // 16-byte pieces of the staged tiles, and pieces per thread.
     static constexpr int KPC = C0 * M / 8, KPT = (KPC + NT - 1) / NT;
     static constexpr int VPC = C0 * D / 8, VPT = (VPC + NT - 1) / NT;
-    // One staging buffer (bf16): K [C0][KS_LD], V [C0][VS_LD], gamma [C0][M]
-    // (or [C0] per token), q [C0][M] (read-out only), mu [C0].
+    // One staging buffer: K [C0][KS_LD], V [C0][VS_LD], gamma [C0][M] (a
+    // per-token gamma broadcast over the slots), q [C0][M] (read-out only) in
+    // bf16; mu [C0] in fp32.
     static constexpr int SO_K = 0;
     static constexpr int SO_V = SO_K + C0 * KS_LD;
     static constexpr int SO_G = SO_V + C0 * VS_LD;
     static constexpr int SO_Q = SO_G + C0 * GS_LD;
-    static constexpr int SO_MU = SO_Q + (WITH_Y ? C0 * GS_LD : 0);
-    static constexpr int SO_GT = SO_MU + C0;               // per-token gamma [C0]
-    static constexpr int STAGE = SO_GT + C0;               // elements per buffer
+    static constexpr int SO_MU = SO_Q + (WITH_Y ? C0 * GS_LD : 0);  // mu [C0] fp32
+    static constexpr int STAGE = SO_MU + 2 * C0;           // bf16 elements per buffer
 
     // LDS layout (bytes).
     static constexpr int O_ZH = 0;                                  // Z hi  [M][ZS_LD]
@@ -159,20 +165,25 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 template <class G>
 struct Pre {
     u32x4 k[G::KPT], g[G::KPT], q[G::KPT], v[G::VPT];
-    uint16_t mu, gt;  // per-token scalars: thread tau < C0 holds token tau
+    uint16_t gtok[G::KPT];  // per-token gamma of each piece's token
+    uint16_t mu;            // thread tau < C0 holds token tau
 };
 
-// Every load below is unconditional (indices are clamped; a per-token gamma
-// reads a valid dummy tile from k) so none sits behind a branch, which would
-// make the compiler wait for it at the join.
+// Every load below is unconditional (indices are clamped) so none sits behind
+// a branch, which would make the compiler wait for it at the join.  A
+// per-token gamma is broadcast over the 8 slots of each piece at commit, so the
+// staged gamma tile is always [C0][M]: both the tile load (a valid dummy tile,
+// k, for a per-token gamma) and the scalar load (the first slot's gamma for a
+// per-slot gamma) are issued, and commit picks one.
 template <class G, bool WITH_Y>
 __device__ __forceinline__ void prefetch(Pre<G>& pf, const Params& p, int b, int hd, int t0) {
     constexpr int M = G::M_, D = G::D_, C0 = G::C0_;
     const int tid = threadIdx.x;
+    const bool gslot = p.gamma_per_slot != 0;
     const uint16_t* kg = static_cast<const uint16_t*>(p.k);
     const uint16_t* vg = static_cast<const uint16_t*>(p.v);
     const uint16_t* gg = static_cast<const uint16_t*>(p.gamma);
-    const uint16_t* gtile = p.gamma_per_slot ? gg : kg;
+    const uint16_t* gtile = gslot ? gg : kg;
     const uint16_t* qg = static_cast<const uint16_t*>(p.q);
     const uint16_t* mug = static_cast<const uint16_t*>(p.mu);
     const int64_t row0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;  // token t0
@@ -181,9 +192,11 @@ __device__ __forceinline__ void prefetch(Pre<G>& pf, const Params& p, int b, int
     for (int j = 0; j < G::KPT; ++j) {
         int e = tid + j * G::NT;
         if (G::KPC % G::NT != 0) e = e < G::KPC ? e : G::KPC - 1;
-        const int64_t off = (row0 + (e / (M / 8)) * rs) * M + (e % (M / 8)) * 8;
+        const int64_t row = row0 + (e / (M / 8)) * rs;
+        const int64_t off = row * M + (e % (M / 8)) * 8;
         pf.k[j] = *reinterpret_cast<const u32x4*>(kg + off);
         pf.g[j] = *reinterpret_cast<const u32x4*>(gtile + off);
+        pf.gtok[j] = gg[gslot ? row * M : row];
         if constexpr (WITH_Y) pf.q[j] = *reinterpret_cast<const u32x4*>(qg + off);
     }
 #pragma unroll
@@ -192,13 +205,11 @@ __device__ __forceinline__ void prefetch(Pre<G>& pf, const Params& p, int b, int
         if (G::VPC % G::NT != 0) e = e < G::VPC ? e : G::VPC - 1;
         pf.v[j] = *reinterpret_cast<const u32x4*>(vg + (row0 + (e / (D / 8)) * rs) * D + (e % (D / 8)) * 8);
     }
-    const int64_t n = row0 + (tid % C0) * rs;
-    pf.mu = mug[n];
-    pf.gt = gg[p.gamma_per_slot ? n * M : n];
+    pf.mu = mug[row0 + (tid % C0) * rs];
 }
 
 template <class G, bool WITH_Y>
-__device__ __forceinline__ void commit(const Pre<G>& pf, short* st) {
+__device__ __forceinline__ void commit(const Pre<G>& pf, short* st, bool gslot) {
     constexpr int M = G::M_, D = G::D_, C0 = G::C0_;
     const int tid = threadIdx.x;
 #pragma unroll
@@ -207,7 +218,8 @@ __device__ __forceinline__ void commit(const Pre<G>& pf, short* st) {
         if (G::KPC % G::NT == 0 || e < G::KPC) {
             const int tau = e / (M / 8), i0 = (e % (M / 8)) * 8;
             *reinterpret_cast<u32x4*>(st + G::SO_K + tau * G::KS_LD + i0) = pf.k[j];
-            *reinterpret_cast<u32x4*>(st + G::SO_G + tau * G::GS_LD + i0) = pf.g[j];
+            const unsigned g2 = static_cast<unsigned>(pf.gtok[j]) * 0x10001u;
+            *reinterpret_cast<u32x4*>(st + G::SO_G + tau * G::GS_LD + i0) = gslot ? pf.g[j] : u32x4{g2, g2, g2, g2};
             if constexpr (WITH_Y) *reinterpret_cast<u32x4*>(st + G::SO_Q + tau * G::GS_LD + i0) = pf.q[j];
         }
     }
@@ -219,10 +231,7 @@ __device__ __forceinline__ void commit(const Pre<G>& pf, short* st) {
             *reinterpret_cast<u32x4*>(st + G::SO_V + tau * G::VS_LD + c0) = pf.v[j];
         }
     }
-    if (tid < C0) {
-        st[G::SO_MU + tid] = static_cast<short>(pf.mu);
-        st[G::SO_GT + tid] = static_cast<short>(pf.gt);
-    }
+    if (tid < C0) reinterpret_cast<float*>(st + G::SO_MU)[tid] = bf16u(pf.mu);
 }
 
 // Products of x over the four 16-lane groups of a wave, per lane column:
@@ -270,9 +279,7 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
     const short* vs = st + G::SO_V;
     const short* gs = st + G::SO_G;
     const short* qs = st + G::SO_Q;
-    const short* mus = st + G::SO_MU;
-    const short* gts = st + G::SO_GT;
-    const bool gslot = p.gamma_per_slot != 0;
+    const float* mus = reinterpret_cast<const float*>(st + G::SO_MU);
 
     short* zh = reinterpret_cast<short*>(smem + G::O_ZH);
     short* zl = reinterpret_cast<short*>(smem + G::O_ZL);
@@ -378,8 +385,8 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
 #pragma unroll
                     for (int ww = 0; ww < G::NW; ++ww) hh += hp[ww * C0 + tau];
                     const float k = bf16_val(ks[tau * G::KS_LD + i]);
-                    const float mu = bf16_val(mus[tau]);
-                    const float a = bf16_val(gslot ? gs[tau * G::GS_LD + i] : gts[tau]) * k;
+                    const float mu = mus[tau];
+                    const float a = bf16_val(gs[tau * G::GS_LD + i]) * k;
                     const float wv = fmaxf(fmaf(-c[r], c[r], hh), 0.f);
                     const float beta = __builtin_amdgcn_rsqf(fmaf(mu, mu, a * a * wv));
                     gt[tb][r] = beta * fmaf(a, c[r], mu);
@@ -404,14 +411,12 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
                     s *= gt[tb][r];
                 }
                 s16x4 wh4, wl4;
+                split4(f32x4{kp[tb][0] * suf[0], kp[tb][1] * suf[1], kp[tb][2] * suf[2], kp[tb][3] * suf[3]}, wh4, wl4);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int tau = 16 * tb + 4 * lg + r;
                     A *= gt[tb][r];
                     short hi, lo;
-                    split1(kp[tb][r] * suf[r], hi, lo);
-                    wh4[r] = hi;
-                    wl4[r] = lo;
                     if constexpr (WITH_Y) {
                         split1(bf16_val(qs[tau * G::GS_LD + i]) * A, hi, lo);
                         qah[tau * G::QA_LD + i] = hi;
@@ -428,7 +433,7 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
             if (lg == 0) aend[i] = fwd;
         }
     }
-    if (has_next) commit<G, WITH_Y>(nxt, st_next);
+    if (has_next) commit<G, WITH_Y>(nxt, st_next, p.gamma_per_slot != 0);
     __syncthreads();  // (B) W^T, A_end, Q.A, kappa/A and the next staged inputs visible
 
     // ---- read-out: Y = (Q.A) R + tril(P) H, P^T = (kappa/A)(Q.A)^T ---
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(4 * D) void osr_chunk_loop_kernel(Params p) {
     Pre<G> nxt;
     load_rows<M, D>(acc, p.state_in + static_cast<int64_t>(bh) * M * D);
     prefetch<G, WITH_Y>(nxt, p, b, hd, 0);
-    commit<G, WITH_Y>(nxt, stage);
+    commit<G, WITH_Y>(nxt, stage, p.gamma_per_slot != 0);
     for (int s = 0; s < NS; ++s) {
         const int t0 = s * C0;
         // Unconditional (the last sub-block re-reads its own tile) so the
@@ -646,7 +651,7 @@ __global__ __launch_bounds__(4 * D) void osr_intra_chunk_kernel(Params p, int cp
     bf16x8 z8h[(M + 31) / 32], z8l[(M + 31) / 32];
     Pre<G> nxt;
     prefetch<G, true>(nxt, p, b, hd, ch0 * C);
-    commit<G, true>(nxt, stage);
+    commit<G, true>(nxt, stage, p.gamma_per_slot != 0);
     for (int s = 0; s < NS; ++s) {
         const int ch = ch0 + s / SPC, t0 = ch0 * C + s * C0;
         if (s % SPC == 0) {
