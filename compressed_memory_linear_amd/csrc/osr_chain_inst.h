@@ -29,7 +29,10 @@ static int launch_chain(const Params& p, hipStream_t st) {
         return -3;
     } else {
         const unsigned BH = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H);
-        hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true>), dim3(BH), dim3(4 * M), 0, st, p);
+        if (p.chunk == C0)
+            hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true>), dim3(BH), dim3(4 * M), 0, st, p);
+        else
+            hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false>), dim3(BH), dim3(4 * M), 0, st, p);
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }
 }

@@ -39,7 +39,9 @@ bool mfma_supported(int m, int d, int C) {
 
 size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C) {
     if (!mfma::use_split(B, H)) return 0;
-    return static_cast<size_t>(B) * H * (T / C) * m * d * sizeof(float);
+    // per (b,h,chunk): Z [m][d], g and kappa [m][C], h [d][C], fp32
+    const size_t per_chunk = static_cast<size_t>(m) * d + 2 * static_cast<size_t>(m) * C + static_cast<size_t>(d) * C;
+    return static_cast<size_t>(B) * H * (T / C) * per_chunk * sizeof(float);
 }
 
 int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st) {

@@ -9,9 +9,10 @@
 // with H = K Z - V (decoding) or -V (similarity), c = H Z^T,
 // a = gamma (.) k, w = max(|h|^2 - c^2, 0), beta = (mu^2 + a^2 w)^(-1/2)
 // (appendix "Computing beta"), g = beta (mu + a c), kappa = -beta a.  This
-// kernel only carries that state from chunk to chunk (one workgroup per
-// (b, h), sequential over chunks) and stores every chunk-start state Z for the
-// read-out kernel, which then runs in parallel over chunks.
+// kernel carries that state from chunk to chunk (one workgroup per (b, h),
+// sequential over chunks) and stores, per chunk, Z, the gates g and kappa and
+// the vectors h_t, from which the read-out kernel forms every y_t in parallel
+// over chunks.
 //
 // Work layout (transposed relative to the read-out kernels): one workgroup of
 // m/16 waves; wave w owns the slot rows [16w, 16w + 16) of the state for all d
@@ -100,49 +101,6 @@ constexpr bool chain_fits() {
     return ChainCfg<M, D, C0>::BYTES <= 160 * 1024;
 }
 
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-
-// Two D-layout tiles -> one permuted 32-k operand.
-__device__ __forceinline__ bf16x8 cat8(s16x4 a, s16x4 b) {
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-// The matching operand read from LDS: p points at column 4lg of a 32-column block.
-__device__ __forceinline__ bf16x8 ld8p(const short* p) {
-    return cat8(*reinterpret_cast<const s16x4*>(p), *reinterpret_cast<const s16x4*>(p + 16));
-}
-__device__ __forceinline__ s16x4 ld4s(const short* p) { return *reinterpret_cast<const s16x4*>(p); }
-
-// Reductions over the four 16-lane rows of a wave, per lane column, with the
-// gfx950 row swaps: permlane16_swap(x, x) gives every row the value of the
-// even and of the odd row of its pair (rows 0/1, 2/3); permlane32_swap(y, y)
-// gives the values of rows 0/1 and of rows 2/3 when y is uniform per pair.
-__device__ __forceinline__ void pair_rows(float x, float& even, float& odd) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    even = __uint_as_float(r[0]);
-    odd = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ void half_rows(float y, float& lo, float& hi) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
-    lo = __uint_as_float(r[0]);
-    hi = __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float rows4_sum(float x) {
-    float e, o, lo, hi;
-    pair_rows(x, e, o);
-    half_rows(e + o, lo, hi);
-    return lo + hi;
-}
-// Products over the rows of x per lane column: below = rows < lg, above =
-// rows > lg, total = all four.
-__device__ __forceinline__ void rows4_prod_scan(float x, int lg, float& below, float& above, float& total) {
-    float e, o, lo, hi;
-    pair_rows(x, e, o);
-    half_rows(e * o, lo, hi);
-    total = lo * hi;
-    below = ((lg & 1) ? e : 1.f) * ((lg & 2) ? lo : 1.f);
-    above = ((lg & 1) ? 1.f : o) * ((lg & 2) ? 1.f : hi);
-}
-
 // Unit-sphere projection of the wave's slot rows (eq. normalized_recurrence):
 // lane (lg, lc) holds 4 columns of slot lc per tile; the row sum adds the
 // four lane rows.
@@ -156,7 +114,9 @@ __device__ __forceinline__ float row_inv_norm(const f32x4 (&acc)[DB]) {
     return __builtin_amdgcn_rsqf(rows4_sum(n2));
 }
 
-template <int M, int D, int C0, bool WRITE_Z>
+// ONE: one sub-block per chunk (C0 = C), known at compile time so the
+// chunk-start work is straight-line code.
+template <int M, int D, int C0, bool WRITE_Z, bool ONE>
 __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
     using G = ChainCfg<M, D, C0>;
     constexpr int DB = G::DB, TB = G::TB;
@@ -174,7 +134,7 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lg = lane >> 4, lc = lane & 15;
     const int slot = 16 * w + lc;
-    const int C = p.chunk, NC = p.T / C, NS = p.T / C0, SPC = C / C0;
+    const int C = p.chunk, NS = p.T / C0, SPC = C / C0;
     // H = K Z - V assignment of this wave.
     const int g1_tb0 = w % G::TG, g1_grp = w / G::TG;
     const bool g1_active = g1_grp < G::WSE;
@@ -193,13 +153,17 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
 
     for (int s = 0; s < NS; ++s) {
         const int t0 = s * C0;
-        const bool chunk_start = s % SPC == 0;
+        const bool chunk_start = ONE || s % SPC == 0;
+        const int chunk = ONE ? s : s / SPC;
         const bool has_next = s + 1 < NS;
         const short* st = stage + (s & 1) * G::STAGE;
         const short* ks = st + G::SO_K;
         const short* vs = st + G::SO_V;
         const short* gs = st + G::SO_G;
         const float* mus = reinterpret_cast<const float*>(st + G::SO_MU);
+        // this sub-block's part of the chunk's workspace (read-out inputs)
+        const Workspace ws = workspace_at<M, D>(p, bh, chunk);
+        const int tc0 = ONE ? 0 : (s % SPC) * C0;
 
         if (chunk_start) {
             const float inv = row_inv_norm<DB>(acc);
@@ -214,8 +178,7 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
         prefetch<G, false>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
         if (chunk_start) {
             if constexpr (WRITE_Z) {
-                float* dst = p.zbuf + (static_cast<int64_t>(bh) * NC + s / SPC) * M * D +
-                             static_cast<int64_t>(slot) * D + 4 * lg;
+                float* dst = ws.z + static_cast<int64_t>(slot) * D + 4 * lg;
 #pragma unroll
                 for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
             }
@@ -302,6 +265,8 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
                 for (int dj = 0; dj < DPW; ++dj) {
                     const int dcol = 16 * (g1_grp + G::WSE * dj) + lc;
                     const f32x4 a = ha[ti][dj];
+                    if constexpr (WRITE_Z)
+                        *reinterpret_cast<f32x4*>(ws.h + static_cast<int64_t>(dcol) * C + tc0 + 16 * tb + 4 * lg) = a;
                     s16x4 hh4, hl4;
                     split4(a, hh4, hl4);
                     *reinterpret_cast<s16x4*>(hth + dcol * G::HT_LD + 16 * tb + 4 * lg) = hh4;
@@ -325,6 +290,7 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
             }
         }
         __syncthreads();  // (A) H, H^T and |h|^2 partials visible
+
 
         // ---- c = H Z^T for this wave's slots; gates ------------------------
         // Gate inputs of this wave's slots are read before the products.
@@ -396,6 +362,11 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
                 prod *= gt[tb][r];
             }
             rows4_prod_scan(prod, lg, ex_lo[tb], ex_hi[tb], tot[tb]);
+            if constexpr (WRITE_Z) {
+                const int64_t o = static_cast<int64_t>(slot) * C + tc0 + 16 * tb + 4 * lg;
+                *reinterpret_cast<f32x4*>(ws.g + o) = f32x4{gt[tb][0], gt[tb][1], gt[tb][2], gt[tb][3]};
+                *reinterpret_cast<f32x4*>(ws.k + o) = f32x4{kp[tb][0], kp[tb][1], kp[tb][2], kp[tb][3]};
+            }
         }
         // W_t = kappa_t (.) prod_{l > t} g_l inside the sub-block, split into
         // B operands of the update (k = token); A_end = prod of all g.
@@ -444,8 +415,12 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
                 acc[db] = mma3(ld4s(hth + ao), ld4s(htl + ao), wh4[0], wl4[0], acc[db]);
             }
         }
+
         // Next sub-block's inputs into the other staging buffer (its last
         // readers, the previous sub-block's gates, finished before (S)).
+        // The memory counter retires loads and stores in order; the loads
+        // were issued before this sub-block's workspace stores, so the wait
+        // for them here leaves those stores in flight.
         if (has_next) commit<G, false>(nxt, stage + ((s + 1) & 1) * G::STAGE, p.gamma_per_slot != 0);
     }
 

@@ -5,6 +5,7 @@
 
 #include "osr_launch.h"
 #include "osr_mfma_kernels.h"
+#include "osr_mfma_readout.h"
 
 namespace osr {
 namespace mfma {
@@ -18,6 +19,14 @@ template <int M, int D, bool WITH_Y>
 constexpr bool fits_c0(int c0) {
     return c0 == 64 ? fits<M, D, 64, WITH_Y>() : c0 == 32 ? fits<M, D, 32, WITH_Y>() : fits<M, D, 16, WITH_Y>();
 }
+// Sub-block of the split schedule's read-out kernel: 32 tokens (the running
+// gate products stay within a short window), 16 where C is 16 and for
+// m = 128 with one wave (d = 16), which would spill at 32.
+template <int M, int D>
+constexpr int pick_c0_split_readout(int C) {
+    return C >= 32 && readout_fits<M, D, 32>() && !(M == 128 && D == 16) ? 32 : 16;
+}
+// Sub-block of the fused kernel.
 template <int M, int D>
 constexpr int pick_c0_readout(int C) {
     int c0 = D == 128 ? 16 : 32;
@@ -41,19 +50,18 @@ static int launch_loop(const Params& p, hipStream_t st) {
 }
 
 template <int M, int D, int C0>
-static int launch_intra(const Params& p, hipStream_t st) {
-    if constexpr (!fits<M, D, C0, true>()) {
+static int launch_readout(const Params& p, hipStream_t st) {
+    if constexpr (!readout_fits<M, D, C0>()) {
         return -3;
     } else {
         const int BH = p.B * p.H, NC = p.T / p.chunk;
-        // Enough workgroups for every CU at the occupancy LDS allows; each
-        // takes cpw consecutive chunks (a power of two dividing NC).
-        const int per_cu = (160 * 1024) / Cfg<M, D, C0, true>::BYTES;
-        const int64_t target = 256LL * (per_cu > 0 ? per_cu : 1);
+        // At least 1024 workgroups (4 per CU); each takes cpw consecutive
+        // chunks (a power of two dividing NC), which keeps the register
+        // prefetch running across chunk boundaries.
         int cpw = 1;
-        while (cpw * 2 <= NC && NC % (cpw * 2) == 0 && static_cast<int64_t>(BH) * NC / (cpw * 2) >= target) cpw *= 2;
+        while (cpw * 2 <= NC && NC % (cpw * 2) == 0 && static_cast<int64_t>(BH) * NC / (cpw * 2) >= 1024) cpw *= 2;
         const unsigned grid = static_cast<unsigned>(BH) * static_cast<unsigned>(NC / cpw);
-        hipLaunchKernelGGL((osr_intra_chunk_kernel<M, D, C0>), dim3(grid), dim3(4 * D), 0, st, p, cpw);
+        hipLaunchKernelGGL((osr_readout_kernel<M, D, C0>), dim3(grid), dim3(4 * D), 0, st, p, cpw);
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }
 }
@@ -65,7 +73,7 @@ static int launch_md(bool split, const Params& p, hipStream_t st) {
     if (split) {
         const int rc = launch_chain_m<M>(D, p, st);
         if (rc) return rc;
-        return c0 == 32 ? launch_intra<M, D, 32>(p, st) : launch_intra<M, D, 16>(p, st);
+        return pick_c0_split_readout<M, D>(C) == 32 ? launch_readout<M, D, 32>(p, st) : launch_readout<M, D, 16>(p, st);
     }
     return c0 == 32 ? launch_loop<M, D, 32, true, false>(p, st) : launch_loop<M, D, 16, true, false>(p, st);
 }

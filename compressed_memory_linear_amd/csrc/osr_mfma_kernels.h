@@ -94,6 +94,75 @@ __device__ __forceinline__ void split4(f32x4 x, s16x4& hi, s16x4& lo) {
     lo = __builtin_bit_cast(s16x4, u32x2{cvt2_bf16(r0, r1), cvt2_bf16(r2, r3)});
 }
 
+// 16x16x32 operands built from accumulator tiles use a permuted k order: two
+// D-layout tiles t0, t1 (lane (lg, lc) holds rows 4lg..4lg+3 of column lc)
+// concatenated form an operand whose k index 8lg + j stands for row
+// 16(j/4) + 4lg + j%4 of the 32-row block; the matching operand is read from
+// LDS as two 8-byte pieces at columns 4lg and 16 + 4lg of the block.  Any
+// bijection of k leaves the contraction unchanged.
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+// Two D-layout tiles -> one permuted 32-k operand.
+__device__ __forceinline__ bf16x8 cat8(s16x4 a, s16x4 b) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// The matching operand read from LDS: p points at column 4lg of a 32-column block.
+__device__ __forceinline__ bf16x8 ld8p(const short* p) {
+    return cat8(*reinterpret_cast<const s16x4*>(p), *reinterpret_cast<const s16x4*>(p + 16));
+}
+__device__ __forceinline__ s16x4 ld4s(const short* p) { return *reinterpret_cast<const s16x4*>(p); }
+
+// Reductions over the four 16-lane rows of a wave, per lane column, with the
+// gfx950 row swaps: permlane16_swap(x, x) gives every row the value of the
+// even and of the odd row of its pair (rows 0/1, 2/3); permlane32_swap(y, y)
+// gives the values of rows 0/1 and of rows 2/3 when y is uniform per pair.
+__device__ __forceinline__ void pair_rows(float x, float& even, float& odd) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    even = __uint_as_float(r[0]);
+    odd = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void half_rows(float y, float& lo, float& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float rows4_sum(float x) {
+    float e, o, lo, hi;
+    pair_rows(x, e, o);
+    half_rows(e + o, lo, hi);
+    return lo + hi;
+}
+// Products over the rows of x per lane column: below = rows < lg, above =
+// rows > lg, total = all four.
+__device__ __forceinline__ void rows4_prod_scan(float x, int lg, float& below, float& above, float& total) {
+    float e, o, lo, hi;
+    pair_rows(x, e, o);
+    half_rows(e * o, lo, hi);
+    total = lo * hi;
+    below = ((lg & 1) ? e : 1.f) * ((lg & 2) ? lo : 1.f);
+    above = ((lg & 1) ? 1.f : o) * ((lg & 2) ? 1.f : hi);
+}
+
+// Workspace of the split schedule, fp32, for every (b,h) and chunk n (all
+// taken at the chunk-start state): Z [m][d], the gates g [m][C] and kappa
+// [m][C] (token-contiguous per slot) and h [d][C] (token-contiguous per
+// column).  The state-passing kernel writes it, the read-out kernel reads it.
+struct Workspace {
+    float* z;
+    float* g;
+    float* k;
+    float* h;
+};
+template <int M, int D>
+__device__ __forceinline__ Workspace workspace_at(const Params& p, int bh, int n) {
+    const int C = p.chunk, NC = p.T / C;
+    const int64_t nch = static_cast<int64_t>(p.B) * p.H * NC, i = static_cast<int64_t>(bh) * NC + n;
+    float* g0 = p.zbuf + nch * M * D;
+    float* k0 = g0 + nch * M * C;
+    float* h0 = k0 + nch * M * C;
+    return Workspace{p.zbuf + i * M * D, g0 + i * M * C, k0 + i * M * C, h0 + i * D * C};
+}
+
 template <int M, int D, int C0, bool WITH_Y>
 struct Cfg {
     static constexpr int M_ = M, D_ = D, C0_ = C0;
@@ -631,39 +700,6 @@ __global__ __launch_bounds__(4 * D) void osr_chunk_loop_kernel(Params p) {
     }
     project_state<M, D, G>(acc, smem);
     store_rows<M, D>(acc, p.state_out + static_cast<int64_t>(bh) * M * D);
-}
-
-// Intra-chunk read-out: each workgroup takes cpw consecutive chunks of one
-// (b, h), each starting from the chunk-start state the state-passing kernel
-// stored.
-template <int M, int D, int C0>
-__global__ __launch_bounds__(4 * D) void osr_intra_chunk_kernel(Params p, int cpw) {
-    using G = Cfg<M, D, C0, true>;
-    __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
-    short* stage = reinterpret_cast<short*>(smem + G::O_KS);
-    const int C = p.chunk, NC = p.T / C, SPC = C / C0;
-    const int groups = NC / cpw;
-    const int bh = blockIdx.x / groups, grp = blockIdx.x % groups;
-    const int b = bh / p.H, hd = bh % p.H;
-    const int ch0 = grp * cpw, NS = cpw * SPC;
-    f32x4 acc[G::MT];
-    s16x4 zfh[G::MT], zfl[G::MT];
-    bf16x8 z8h[(M + 31) / 32], z8l[(M + 31) / 32];
-    Pre<G> nxt;
-    prefetch<G, true>(nxt, p, b, hd, ch0 * C);
-    commit<G, true>(nxt, stage, p.gamma_per_slot != 0);
-    for (int s = 0; s < NS; ++s) {
-        const int ch = ch0 + s / SPC, t0 = ch0 * C + s * C0;
-        if (s % SPC == 0) {
-            load_rows<M, D>(acc, p.zbuf + (static_cast<int64_t>(bh) * NC + ch) * M * D);
-            __syncthreads();  // previous chunk's readers of Z are done; first staged inputs visible
-            stage_z<M, D, G>(acc, zfh, zfl, z8h, z8l, smem);
-        }
-        const bool has_next = s + 1 < NS;
-        prefetch<G, true>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
-        osr_subblock<M, D, C0, true>(p, smem, acc, zfh, zfl, z8h, z8l, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
-                                     stage + ((s + 1) & 1) * G::STAGE, has_next, (s + 1) % SPC != 0, b, hd, t0);
-    }
 }
 
 }  // namespace mfma

@@ -1,0 +1,288 @@
+// osr_mfma_readout.h -- read-out of the chunk-wise OSR forward on gfx950
+// matrix cores, in parallel over chunks.
+//
+// Method: "Lattice: Learning to Efficiently Compress the Memory" (arXiv
+// 2504.05646), section "Parallel and Hardware Efficient Form", eq.
+// recurrence_linear2 and its gated-linear-attention form.  Inside a chunk the
+// state evolves as s_i <- g_{t,i} s_i + kappa_{t,i} h_t with gates and h_t
+// taken at the chunk-start state Z; the read-out is y_t = sum_i q_{t,i} s_i.
+// The state-passing kernel stores, per chunk, Z, g, kappa and h (workspace);
+// here each workgroup takes cpw consecutive chunks of one (b, h) and, over
+// sub-blocks of C0 tokens with R the state at the sub-block start and A the
+// running product of g inside the sub-block,
+//   Y  = (Q (.) A) R + tril[(Q (.) A)(kappa (/) A)^T] H
+//   R <- diag(A_end) R + W^T H,   W_t = kappa_t (.) prod_{l > t} g_l.
+// R starts at Z for every chunk.  Products whose operands derive from the
+// state, the gates or h run as three bf16 MFMAs on a hi/lo split.
+//
+// Work layout: D/16 waves; wave w owns columns [16w, 16w + 16) of R, H and Y
+// (R as MFMA accumulator tiles, which are B operands with k = slot).  The
+// per-(token, slot) gate products are formed by the wave that owns the slot
+// block, which writes Q.A, kappa/A (token-major) and W^T (slot-major) to
+// LDS; one barrier per sub-block (the LDS buffers alternate between
+// sub-blocks).  All global inputs of sub-block s+1 are loaded into registers
+// while s computes.
+#pragma once
+
+#include "osr_mfma_kernels.h"
+
+namespace osr {
+namespace mfma {
+
+template <int M, int D, int C0>
+struct ReadCfg {
+    static constexpr int NW = D / 16;  // wave w owns columns [16w, 16w + 16)
+    static constexpr int NT = 64 * NW;
+    static constexpr int MT = M / 16;
+    static constexpr int TB = C0 / 16;
+    static constexpr int MPW = (MT + NW - 1) / NW;  // slot tiles per wave in the gate phase
+    // Row strides (bf16 elements): 8-byte operand reads of 16 rows and
+    // scattered 2-byte writes of rows 4lg + r are conflict-free with a stride
+    // of 2 (mod 4) words.
+    static constexpr int QA_LD = M + 4;
+    static constexpr int WT_LD = C0 + 4;
+    static constexpr bool K32_C = C0 % 32 == 0; // R += W^T H          (k = token)
+    // One LDS buffer set (bytes); two sets alternate between sub-blocks.
+    static constexpr int B_QH = 0;                       // Q.A hi      [C0][QA_LD]
+    static constexpr int B_QL = B_QH + C0 * QA_LD * 2;   // Q.A lo
+    static constexpr int B_KH = B_QL + C0 * QA_LD * 2;   // kappa/A hi  [C0][QA_LD]
+    static constexpr int B_KL = B_KH + C0 * QA_LD * 2;   // kappa/A lo
+    static constexpr int B_WH = B_KL + C0 * QA_LD * 2;   // W^T hi      [M][WT_LD]
+    static constexpr int B_WL = B_WH + M * WT_LD * 2;    // W^T lo
+    static constexpr int B_AE = B_WL + M * WT_LD * 2;    // A_end       [M] fp32
+    static constexpr int SET = B_AE + M * 4;
+    static constexpr int BYTES = 2 * SET;
+    static_assert(M % 16 == 0 && D % 16 == 0 && C0 % 16 == 0, "tile multiples");
+};
+
+template <int M, int D, int C0>
+constexpr bool readout_fits() {
+    return ReadCfg<M, D, C0>::BYTES <= 160 * 1024;
+}
+
+// Register inputs of one sub-block for one lane.
+template <class G>
+struct RdIn {
+    f32x4 g[G::MPW][G::TB], k[G::MPW][G::TB];  // slot 16mb + lc, tokens 16tb + 4lg + (0..3)
+    f32x4 h[G::TB];                             // column 16w + lc, same tokens
+    uint16_t q[G::MPW][G::TB][4];               // q of those (token, slot) pairs, bf16
+};
+
+// All loads unconditional: slot tiles past the last one read the last tile.
+template <class G>
+__device__ __forceinline__ void rd_load(RdIn<G>& in, const Params& p, const Workspace& ws, int b, int hd, int t0,
+                                        int tc0) {
+    constexpr int M = G::MT * 16;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
+    const int C = p.chunk;
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q);
+#pragma unroll
+    for (int mi = 0; mi < G::MPW; ++mi) {
+        const int mb = w + mi * G::NW < G::MT ? w + mi * G::NW : G::MT - 1;
+        const int slot = 16 * mb + lc;
+#pragma unroll
+        for (int tb = 0; tb < G::TB; ++tb) {
+            const int64_t o = static_cast<int64_t>(slot) * C + tc0 + 16 * tb + 4 * lg;
+            in.g[mi][tb] = *reinterpret_cast<const f32x4*>(ws.g + o);
+            in.k[mi][tb] = *reinterpret_cast<const f32x4*>(ws.k + o);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = (static_cast<int64_t>(b) * p.T + t0 + 16 * tb + 4 * lg + r) * p.H + hd;
+                in.q[mi][tb][r] = qg[row * M + slot];
+            }
+        }
+    }
+#pragma unroll
+    for (int tb = 0; tb < G::TB; ++tb)
+        in.h[tb] = *reinterpret_cast<const f32x4*>(ws.h + static_cast<int64_t>(16 * w + lc) * C + tc0 + 16 * tb + 4 * lg);
+}
+
+template <int M, int D>
+__device__ __forceinline__ void rd_load_z(f32x4 (&z)[M / 16], const float* src) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
+#pragma unroll
+    for (int mt = 0; mt < M / 16; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) z[mt][r] = src[(16 * mt + 4 * lg + r) * D + 16 * w + lc];
+}
+
+template <int M, int D, int C0>
+__global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
+    using G = ReadCfg<M, D, C0>;
+    constexpr int MT = G::MT, TB = G::TB;
+    __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
+    const int C = p.chunk, NC = p.T / C, SPC = C / C0;
+    const int groups = NC / cpw;
+    const int bh = blockIdx.x / groups, grp = blockIdx.x % groups;
+    const int b = bh / p.H, hd = bh % p.H;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
+    const int dcol = 16 * w + lc;
+    const int ch0 = grp * cpw, NS = cpw * SPC;
+
+    f32x4 acc[MT];  // R tiles: acc[mt][r] = R[16mt + 4lg + r][dcol]
+    f32x4 zn[MT];   // next chunk's Z
+    RdIn<G> cur, nxt;
+    {
+        const Workspace ws = workspace_at<M, D>(p, bh, ch0);
+        rd_load_z<M, D>(acc, ws.z);
+        rd_load<G>(cur, p, ws, b, hd, ch0 * C, 0);
+    }
+    for (int s = 0; s < NS; ++s) {
+        const int sl = s % SPC, n = ch0 + s / SPC;
+        const int tc0 = sl * C0, t0 = n * C + tc0;
+        char* buf = smem + (s & 1) * G::SET;
+        short* qah = reinterpret_cast<short*>(buf + G::B_QH);
+        short* qal = reinterpret_cast<short*>(buf + G::B_QL);
+        short* kah = reinterpret_cast<short*>(buf + G::B_KH);
+        short* kal = reinterpret_cast<short*>(buf + G::B_KL);
+        short* wth = reinterpret_cast<short*>(buf + G::B_WH);
+        short* wtl = reinterpret_cast<short*>(buf + G::B_WL);
+        float* aend = reinterpret_cast<float*>(buf + G::B_AE);
+        const bool last_in_chunk = sl + 1 == SPC;
+
+        // Inputs of the next sub-block (the last one re-reads its own).
+        {
+            const int s1 = s + 1 < NS ? s + 1 : s;
+            const int n1 = ch0 + s1 / SPC, tc1 = (s1 % SPC) * C0;
+            const Workspace ws1 = workspace_at<M, D>(p, bh, n1);
+            rd_load<G>(nxt, p, ws1, b, hd, n1 * C + tc1, tc1);
+            if (last_in_chunk) rd_load_z<M, D>(zn, ws1.z);
+        }
+
+        // ---- gate products of this wave's slot tiles ------------------------
+#pragma unroll
+        for (int mi = 0; mi < G::MPW; ++mi) {
+            const int mb = w + mi * G::NW;
+            if (mb < MT) {
+                const int slot = 16 * mb + lc;
+                float below[TB], above[TB], tot[TB];
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const f32x4 g = cur.g[mi][tb];
+                    rows4_prod_scan(g[0] * g[1] * g[2] * g[3], lg, below[tb], above[tb], tot[tb]);
+                }
+                // A (running product, inclusive), Q.A and kappa/A, token-major.
+                float fwd = 1.f;
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const f32x4 g = cur.g[mi][tb], kp = cur.k[mi][tb];
+                    float a = fwd * below[tb];
+                    f32x4 qa, ka;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        a *= g[r];
+                        qa[r] = bf16u(cur.q[mi][tb][r]) * a;
+                        ka[r] = kp[r] / a;
+                    }
+                    s16x4 qh, ql, kh, kl;
+                    split4(qa, qh, ql);
+                    split4(ka, kh, kl);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int o = (16 * tb + 4 * lg + r) * G::QA_LD + slot;
+                        qah[o] = qh[r];
+                        qal[o] = ql[r];
+                        kah[o] = kh[r];
+                        kal[o] = kl[r];
+                    }
+                    fwd *= tot[tb];
+                }
+                // W_t = kappa_t (.) prod_{l > t} g_l, slot-major.
+                float bwd = 1.f;
+#pragma unroll
+                for (int tb = TB - 1; tb >= 0; --tb) {
+                    const f32x4 g = cur.g[mi][tb], kp = cur.k[mi][tb];
+                    float sfx = bwd * above[tb];
+                    f32x4 wv;
+#pragma unroll
+                    for (int r = 3; r >= 0; --r) {
+                        wv[r] = kp[r] * sfx;
+                        sfx *= g[r];
+                    }
+                    s16x4 wh, wl;
+                    split4(wv, wh, wl);
+                    *reinterpret_cast<s16x4*>(wth + slot * G::WT_LD + 16 * tb + 4 * lg) = wh;
+                    *reinterpret_cast<s16x4*>(wtl + slot * G::WT_LD + 16 * tb + 4 * lg) = wl;
+                    bwd *= tot[tb];
+                }
+                if (lg == 0) aend[slot] = fwd;
+            }
+        }
+        __syncthreads();  // Q.A, kappa/A, W^T, A_end visible
+
+        // ---- Y = (Q.A) R + tril(P) H, P^T = (kappa/A)(Q.A)^T ------------------
+        s16x4 rh[MT], rl[MT], hh[TB], hl[TB];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) split4(acc[mt], rh[mt], rl[mt]);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) split4(cur.h[tb], hh[tb], hl[tb]);
+        const int64_t row0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            f32x4 pt[TB];
+#pragma unroll
+            for (int jb = 0; jb <= tb; ++jb) pt[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            // 16x16x16 products here: the same contractions as 16x16x32 on
+            // permuted operands gave wrong results on gfx950 in this kernel
+            // (correct once nops padded the MFMA sequence), so this path keeps
+            // the 16-deep form, which is exact to rounding.
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const int qo = (16 * tb + lc) * G::QA_LD + 16 * mt + 4 * lg;
+                const s16x4 qh4 = ld4s(qah + qo), ql4 = ld4s(qal + qo);
+                y = mma3(qh4, ql4, rh[mt], rl[mt], y);
+#pragma unroll
+                for (int jb = 0; jb <= tb; ++jb) {
+                    const int ko = (16 * jb + lc) * G::QA_LD + 16 * mt + 4 * lg;
+                    pt[jb] = mma3(ld4s(kah + ko), ld4s(kal + ko), qh4, ql4, pt[jb]);
+                }
+            }
+#pragma unroll
+            for (int jb = 0; jb <= tb; ++jb) {
+                f32x4 pj = pt[jb];  // lane (lg, lc): P^T[16jb + 4lg + r][16tb + lc]
+                if (jb == tb) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (4 * lg + r > lc) pj[r] = 0.f;  // causal: j <= t
+                }
+                s16x4 ph, pl;
+                split4(pj, ph, pl);
+                y = mma3(ph, pl, hh[jb], hl[jb], y);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                st_y1(p.y, (row0 + static_cast<int64_t>(16 * tb + 4 * lg + r) * p.H) * D + dcol, y[r], p.y_bf16);
+        }
+
+        // ---- R <- diag(A_end) R + W^T H (next sub-block of the same chunk) ----
+        if (!last_in_chunk) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const f32x4 ae = *reinterpret_cast<const f32x4*>(aend + 16 * mt + 4 * lg);
+                f32x4 a = acc[mt];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) a[r] *= ae[r];
+                if constexpr (G::K32_C) {
+#pragma unroll
+                    for (int kt = 0; kt < C0 / 32; ++kt) {
+                        const int wo = (16 * mt + lc) * G::WT_LD + 32 * kt + 4 * lg;
+                        a = mma32x3(ld8p(wth + wo), ld8p(wtl + wo), cat8(hh[2 * kt], hh[2 * kt + 1]),
+                                    cat8(hl[2 * kt], hl[2 * kt + 1]), a);
+                    }
+                } else {
+                    const int wo = (16 * mt + lc) * G::WT_LD + 4 * lg;
+                    a = mma3(ld4s(wth + wo), ld4s(wtl + wo), hh[0], hl[0], a);
+                }
+                acc[mt] = a;
+            }
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[mt] = zn[mt];
+        }
+        cur = nxt;
+    }
+}
+
+}  // namespace mfma
+}  // namespace osr
