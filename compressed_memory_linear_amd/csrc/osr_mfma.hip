@@ -1,11 +1,12 @@
 // osr_mfma.hip -- selection of the MFMA chunk schedule (bf16 inputs, C >= 16).
 //
-// Two schedules evaluate the same per-chunk arithmetic (osr_mfma_kernels.h):
-//   split: the inter-chunk state-passing kernel (one workgroup per (b,h),
-//          sequential over chunks) stores each chunk-start state in the
-//          workspace; the intra-chunk kernel then forms every read-out with
-//          one workgroup per (chunk, b, h), in parallel over the sequence.
-//   fused: one workgroup per (b,h) does both; no workspace.
+// Two schedules evaluate the same chunk formula (eq. recurrence_linear2):
+//   split: the state-passing kernel (osr_mfma_chain.h; one workgroup per
+//          (b,h), sequential over chunks) stores each chunk's start state,
+//          gates and h in the workspace; the read-out kernel
+//          (osr_mfma_readout.h) then forms every y_t in parallel over chunks.
+//   fused: one workgroup per (b,h) does both (osr_mfma_kernels.h); no
+//          workspace.
 // split wins when B*H alone cannot fill the 256 compute units.
 #include <stdlib.h>
 #include <string.h>

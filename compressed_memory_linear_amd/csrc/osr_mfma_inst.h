@@ -10,11 +10,10 @@
 namespace osr {
 namespace mfma {
 
-// Sub-block length C0 (<= C) of the read-out kernels.  Longer sub-blocks
-// mean fewer barriers per chunk but more live registers (gates, H fragments
-// and the prefetched inputs grow with C0); the read-out kernels stay at <= 32
-// because their causal block grows as C0^2, and at 16 for d = 128 to stay
-// within the register file.
+// Sub-block length C0 (<= C) of the fused kernel.  Longer sub-blocks mean
+// fewer barriers per chunk but more live registers (gates, H fragments and
+// the prefetched inputs grow with C0); it stays at <= 32 because its causal
+// block grows as C0^2, and at 16 for d = 128 to stay within the register file.
 template <int M, int D, bool WITH_Y>
 constexpr bool fits_c0(int c0) {
     return c0 == 64 ? fits<M, D, 64, WITH_Y>() : c0 == 32 ? fits<M, D, 32, WITH_Y>() : fits<M, D, 16, WITH_Y>();
@@ -26,9 +25,8 @@ template <int M, int D>
 constexpr int pick_c0_split_readout(int C) {
     return C >= 32 && readout_fits<M, D, 32>() && !(M == 128 && D == 16) ? 32 : 16;
 }
-// Sub-block of the fused kernel.
 template <int M, int D>
-constexpr int pick_c0_readout(int C) {
+constexpr int pick_c0_fused(int C) {
     int c0 = D == 128 ? 16 : 32;
     while (c0 > 16 && (c0 > C || !fits_c0<M, D, true>(c0))) c0 /= 2;
     return c0;
@@ -38,13 +36,13 @@ constexpr int pick_c0_readout(int C) {
 template <int M>
 int launch_chain_m(int d, const Params& p, hipStream_t st);
 
-template <int M, int D, int C0, bool WITH_Y, bool WRITE_Z>
-static int launch_loop(const Params& p, hipStream_t st) {
-    if constexpr (!fits<M, D, C0, WITH_Y>()) {
+template <int M, int D, int C0>
+static int launch_fused(const Params& p, hipStream_t st) {
+    if constexpr (!fits<M, D, C0, true>()) {
         return -3;
     } else {
         const unsigned BH = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H);
-        hipLaunchKernelGGL((osr_chunk_loop_kernel<M, D, C0, WITH_Y, WRITE_Z>), dim3(BH), dim3(4 * D), 0, st, p);
+        hipLaunchKernelGGL((osr_fused_kernel<M, D, C0>), dim3(BH), dim3(4 * D), 0, st, p);
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }
 }
@@ -69,13 +67,13 @@ static int launch_readout(const Params& p, hipStream_t st) {
 template <int M, int D>
 static int launch_md(bool split, const Params& p, hipStream_t st) {
     const int C = p.chunk;
-    const int c0 = pick_c0_readout<M, D>(C);
+    const int c0 = pick_c0_fused<M, D>(C);
     if (split) {
         const int rc = launch_chain_m<M>(D, p, st);
         if (rc) return rc;
         return pick_c0_split_readout<M, D>(C) == 32 ? launch_readout<M, D, 32>(p, st) : launch_readout<M, D, 16>(p, st);
     }
-    return c0 == 32 ? launch_loop<M, D, 32, true, false>(p, st) : launch_loop<M, D, 16, true, false>(p, st);
+    return c0 == 32 ? launch_fused<M, D, 32>(p, st) : launch_fused<M, D, 16>(p, st);
 }
 
 template <int M>

@@ -1,4 +1,6 @@
-// osr_mfma_kernels.h -- chunk-wise OSR forward on gfx950 matrix cores.
+// osr_mfma_kernels.h -- chunk-wise OSR forward on gfx950 matrix cores: shared
+// operand helpers, input staging, the workspace layout and the fused kernel
+// (the split schedule's kernels are in osr_mfma_chain.h and osr_mfma_readout.h).
 //
 // Method: "Lattice: Learning to Efficiently Compress the Memory" (arXiv
 // 2504.05646), section "Parallel and Hardware Efficient Form".  Within a chunk
@@ -20,7 +22,7 @@
 // as three bf16 MFMAs on a hi/lo split (hi*hi + hi*lo + lo*hi); k and q are
 // exact bf16 inputs.
 //
-// Work layout: one workgroup of D/16 waves; wave w owns columns
+// Fused kernel's work layout: one workgroup of D/16 waves; wave w owns columns
 // [16w, 16w + 16) of the state (as MFMA accumulators), of H and of Y.  With
 // v_mfma_f32_16x16x16_bf16 an accumulator tile (lane l holds rows
 // 4(l/16)+r of column l%16) is directly a B operand whose k index is the
@@ -662,41 +664,33 @@ __device__ __forceinline__ void stage_z(const f32x4 (&acc)[M / 16], s16x4 (&zfh)
     }
 }
 
-// Sequential chunk loop for one (b, h) per workgroup.
-//   WITH_Y = false, WRITE_Z = true : inter-chunk state-passing kernel; stores
-//       every chunk-start state to p.zbuf for the intra-chunk kernel.
-//   WITH_Y = true,  WRITE_Z = false: fused forward (state passing + read-out).
-template <int M, int D, int C0, bool WITH_Y, bool WRITE_Z>
-__global__ __launch_bounds__(4 * D) void osr_chunk_loop_kernel(Params p) {
-    using G = Cfg<M, D, C0, WITH_Y>;
+// Fused forward: one workgroup per (b, h), sequential over chunks, state
+// passing and read-out together (no workspace).  Used when the (b, h)
+// sequences alone fill the GPU.
+template <int M, int D, int C0>
+__global__ __launch_bounds__(4 * D) void osr_fused_kernel(Params p) {
+    using G = Cfg<M, D, C0, true>;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
     short* stage = reinterpret_cast<short*>(smem + G::O_KS);
     const int bh = blockIdx.x, b = bh / p.H, hd = bh % p.H;
-    const int C = p.chunk, NC = p.T / C, NS = p.T / C0, SPC = C / C0;
+    const int C = p.chunk, NS = p.T / C0, SPC = C / C0;
     f32x4 acc[G::MT];
     s16x4 zfh[G::MT], zfl[G::MT];
     bf16x8 z8h[(M + 31) / 32], z8l[(M + 31) / 32];
     Pre<G> nxt;
     load_rows<M, D>(acc, p.state_in + static_cast<int64_t>(bh) * M * D);
-    prefetch<G, WITH_Y>(nxt, p, b, hd, 0);
-    commit<G, WITH_Y>(nxt, stage, p.gamma_per_slot != 0);
+    prefetch<G, true>(nxt, p, b, hd, 0);
+    commit<G, true>(nxt, stage, p.gamma_per_slot != 0);
     for (int s = 0; s < NS; ++s) {
         const int t0 = s * C0;
         // Unconditional (the last sub-block re-reads its own tile) so the
         // prefetch registers are never a conditionally written aggregate.
-        // Issued before the chunk-start stores below: the memory counter
-        // retires in order, so loads issued after those stores would make
-        // the commit wait for the stores as well.
         const bool has_next = s + 1 < NS;
         if (s % SPC == 0) project_state<M, D, G>(acc, smem);  // its barriers also publish the first staged inputs
-        prefetch<G, WITH_Y>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
-        if (s % SPC == 0) {
-            if constexpr (WRITE_Z)
-                store_rows<M, D>(acc, p.zbuf + (static_cast<int64_t>(bh) * NC + s / SPC) * M * D);
-            stage_z<M, D, G>(acc, zfh, zfl, z8h, z8l, smem);
-        }
-        osr_subblock<M, D, C0, WITH_Y>(p, smem, acc, zfh, zfl, z8h, z8l, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
-                                       stage + ((s + 1) & 1) * G::STAGE, has_next, true, b, hd, t0);
+        prefetch<G, true>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
+        if (s % SPC == 0) stage_z<M, D, G>(acc, zfh, zfl, z8h, z8l, smem);
+        osr_subblock<M, D, C0, true>(p, smem, acc, zfh, zfl, z8h, z8l, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
+                                     stage + ((s + 1) & 1) * G::STAGE, has_next, true, b, hd, t0);
     }
     project_state<M, D, G>(acc, smem);
     store_rows<M, D>(acc, p.state_out + static_cast<int64_t>(bh) * M * D);
