@@ -2,6 +2,9 @@
 // (included once per M by osr_chain_m*.hip).
 #pragma once
 
+#include <stdlib.h>
+#include <string.h>
+
 #include "osr_launch.h"
 #include "osr_mfma_chain.h"
 
@@ -23,16 +26,45 @@ constexpr int pick_c0_chain(int C) {
     return c0;
 }
 
+// Two waves per slot block (two token halves per chunk) when a chunk is one
+// sub-block of at least two token tiles and m <= 32: there the one-wave form
+// leaves SIMDs idle (m/16 < 4 waves), and the pair form measured 10-20%
+// faster (m=32 d=32 C=64: 87 vs 97 us; m=16 d=64: 129 vs 161 us for
+// B4 H8 T2048).  From m = 64 every SIMD already holds one wave, the phases are
+// bound by the CU's shared LDS and issue throughput, and the extra exchange
+// made it slower (169 vs 159 us at m=d=64 C=64).  LATTICE_OSR_CHAIN_PAIRS=0
+// turns it off.
+template <int M, int D, int C0>
+constexpr bool pair_capable() {
+    if constexpr (M <= 32 && C0 >= 32)
+        return chain_fits<M, D, C0, true>();
+    else
+        return false;
+}
+static bool pairs_enabled() {
+    const char* e = getenv("LATTICE_OSR_CHAIN_PAIRS");
+    return !(e && strcmp(e, "0") == 0);
+}
+
 template <int M, int D, int C0>
 static int launch_chain(const Params& p, hipStream_t st) {
     if constexpr (!chain_fits<M, D, C0>()) {
         return -3;
     } else {
         const unsigned BH = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H);
-        if (p.chunk == C0)
-            hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true>), dim3(BH), dim3(4 * M), 0, st, p);
-        else
-            hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false>), dim3(BH), dim3(4 * M), 0, st, p);
+        if (p.chunk != C0) {
+            hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false, false>), dim3(BH), dim3(4 * M), 0, st, p);
+        } else {
+            bool launched = false;
+            if constexpr (pair_capable<M, D, C0>()) {
+                if (pairs_enabled()) {
+                    hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, true>), dim3(BH), dim3(8 * M), 0, st, p);
+                    launched = true;
+                }
+            }
+            if (!launched)
+                hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, false>), dim3(BH), dim3(4 * M), 0, st, p);
+        }
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }
 }

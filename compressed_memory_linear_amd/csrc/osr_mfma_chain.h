@@ -43,20 +43,25 @@
 namespace osr {
 namespace mfma {
 
-template <int M, int D, int C0>
+// PAIR: two waves per slot block (one group of m/16 waves per token half of
+// the chunk); see osr_chain_kernel.
+template <int M, int D, int C0, bool PAIR = false>
 struct ChainCfg {
     static constexpr int M_ = M, D_ = D, C0_ = C0;
-    static constexpr int NW = M / 16;  // wave w owns slots [16w, 16w + 16)
+    static constexpr int NWS = M / 16;        // slot blocks; wave w owns slots [16(w%NWS), +16)
+    static constexpr int NG = PAIR ? 2 : 1;   // wave groups, each over C0/NG tokens
+    static constexpr int NW = NG * NWS;
     static constexpr int NT = 64 * NW;
     static constexpr int DB = D / 16;   // column tiles
     static constexpr int TB = C0 / 16;  // token tiles per sub-block
-    // H = K Z - V work split: TG waves take distinct token tiles, and the WS
-    // waves that share a token tile split its column tiles; WSE of those have
-    // work (WSE partial |h|^2 sums per token).
-    static constexpr int TG = TB < NW ? TB : NW;
-    static constexpr int WS = NW / TG;
+    static constexpr int TBW = TB / NG; // token tiles per group
+    // H = K Z - V work split inside a group: TG waves take distinct token
+    // tiles, and the WS waves that share a token tile split its column tiles;
+    // WSE of those have work (WSE partial |h|^2 sums per token).
+    static constexpr int TG = TBW < NWS ? TBW : NWS;
+    static constexpr int WS = NWS / TG;
     static constexpr int WSE = WS < DB ? WS : DB;
-    static constexpr int TPW = TB / TG;   // token tiles per wave
+    static constexpr int TPW = TBW / TG;  // token tiles per wave
     static constexpr int DPW = DB / WSE;  // column tiles per wave
     // Row strides (bf16 elements).  Buffers read as 16-byte MFMA operands
     // (rows lc = 0..15) pad by 8: a stride of 4 (mod 8) words puts the 8 lanes
@@ -69,9 +74,9 @@ struct ChainCfg {
     static constexpr int HS_LD = D + 4;
     static constexpr int HT_LD = C0 + 4;
     static constexpr int GS_LD = M;
-    static constexpr bool K32_M = M % 32 == 0;   // H = K Z     (k = slot)
-    static constexpr bool K32_D = D % 32 == 0;   // c = H Z^T   (k = column)
-    static constexpr bool K32_C = C0 % 32 == 0;  // R^T += H^T W (k = token)
+    static constexpr bool K32_M = M % 32 == 0;      // H = K Z     (k = slot)
+    static constexpr bool K32_D = D % 32 == 0;      // c = H Z^T   (k = column)
+    static constexpr bool K32_C = TBW % 2 == 0;     // R^T += H^T W (k = token, a group's tokens)
     // Staged inputs, as in the read-out kernels (no q).
     static constexpr int KPC = C0 * M / 8, KPT = (KPC + NT - 1) / NT;
     static constexpr int VPC = C0 * D / 8, VPT = (VPC + NT - 1) / NT;
@@ -90,15 +95,18 @@ struct ChainCfg {
     static constexpr int O_TH = O_HL + C0 * HS_LD * 2;       // H^T hi [D][HT_LD]
     static constexpr int O_TL = O_TH + D * HT_LD * 2;        // H^T lo
     static constexpr int O_HP = O_TL + D * HT_LD * 2;        // |h|^2 partials [C0][WSE]
-    static constexpr int BYTES = O_HP + C0 * WSE * 4;
+    static constexpr int O_XU = O_HP + C0 * WSE * 4;         // pair exchange: U [NW][64 lanes][DB] f32x4
+    static constexpr int O_XT = O_XU + (PAIR ? NW * 64 * DB * 16 : 0);  // and the half products [NW][64]
+    static constexpr int BYTES = O_XT + (PAIR ? NW * 64 * 4 : 0);
 
     static_assert(M % 16 == 0 && D % 16 == 0 && C0 % 16 == 0, "tile multiples");
+    static_assert(TB % NG == 0, "token tiles split evenly between the groups");
     static_assert(NT <= 1024, "waves");
 };
 
-template <int M, int D, int C0>
+template <int M, int D, int C0, bool PAIR = false>
 constexpr bool chain_fits() {
-    return ChainCfg<M, D, C0>::BYTES <= 160 * 1024;
+    return ChainCfg<M, D, C0, PAIR>::BYTES <= 160 * 1024;
 }
 
 // Unit-sphere projection of the wave's slot rows (eq. normalized_recurrence):
@@ -116,10 +124,21 @@ __device__ __forceinline__ float row_inv_norm(const f32x4 (&acc)[DB]) {
 
 // ONE: one sub-block per chunk (C0 = C), known at compile time so the
 // chunk-start work is straight-line code.
-template <int M, int D, int C0, bool WRITE_Z, bool ONE>
-__global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
-    using G = ChainCfg<M, D, C0>;
-    constexpr int DB = G::DB, TB = G::TB;
+// PAIR (requires ONE): two waves per slot block, group g = 0, 1 of m/16 waves
+// taking the chunk's token half g.  Inside a chunk every gate depends only on
+// Z and the inputs, so the halves are independent except for the suffix
+// products that cross from half 0 into half 1: with U_g = sum over half g of
+// kappa_t (.) (prod of g_l over l > t within half g) h_t^T and t_g the
+// per-slot product of the gates over half g,
+//   R_end = diag(t_0 t_1) Z + diag(t_1) U_0 + U_1.
+// Each wave of a pair forms its U_g and t_g, the pair swaps them through
+// LDS, and both form R_end (and its projection) identically.  This doubles
+// the waves per SIMD (latency hiding) at one extra barrier per chunk.
+template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR>
+__global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Params p) {
+    using G = ChainCfg<M, D, C0, PAIR>;
+    static_assert(!PAIR || ONE, "the pair split covers one sub-block per chunk");
+    constexpr int DB = G::DB, TBW = G::TBW;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
     short* stage = reinterpret_cast<short*>(smem + G::O_KS);
     short* zth = reinterpret_cast<short*>(smem + G::O_ZTH);
@@ -133,10 +152,13 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
     const int bh = blockIdx.x, b = bh / p.H, hd = bh % p.H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lg = lane >> 4, lc = lane & 15;
-    const int slot = 16 * w + lc;
+    const int grp = PAIR ? w / G::NWS : 0;  // token half of this wave
+    const int wv = w % G::NWS;              // slot block of this wave
+    const int slot = 16 * wv + lc;
+    const int tbg = grp * TBW;              // first token tile of the group
     const int C = p.chunk, NS = p.T / C0, SPC = C / C0;
-    // H = K Z - V assignment of this wave.
-    const int g1_tb0 = w % G::TG, g1_grp = w / G::TG;
+    // H = K Z - V assignment of this wave (inside its group).
+    const int g1_tb0 = tbg + wv % G::TG, g1_grp = wv / G::TG;
     const bool g1_active = g1_grp < G::WSE;
 
     f32x4 acc[DB];             // R^T tiles: acc[j][r] = R[slot][16j + 4lg + r]
@@ -178,21 +200,24 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
         prefetch<G, false>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
         if (chunk_start) {
             if constexpr (WRITE_Z) {
-                float* dst = ws.z + static_cast<int64_t>(slot) * D + 4 * lg;
+                if (grp == 0) {
+                    float* dst = ws.z + static_cast<int64_t>(slot) * D + 4 * lg;
 #pragma unroll
-                for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
+                    for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
+                }
             }
             // Z^T to LDS (read by every wave's H = K Z); the split tiles stay
             // in registers.  No wave reads Z^T between the last sub-block's
-            // barrier (A) and the barrier (S) below.
+            // barrier (A) and the barrier (S) below.  A pair writes the hi
+            // (group 0) and lo (group 1) halves.
 #pragma unroll
             for (int j = 0; j < DB; ++j) {
                 split4(acc[j], zfh[j], zfl[j]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int col = 16 * j + 4 * lg + r;
-                    zth[col * G::ZT_LD + slot] = zfh[j][r];
-                    ztl[col * G::ZT_LD + slot] = zfl[j][r];
+                    if (!PAIR || grp == 0) zth[col * G::ZT_LD + slot] = zfh[j][r];
+                    if (!PAIR || grp == 1) ztl[col * G::ZT_LD + slot] = zfl[j][r];
                 }
             }
         }
@@ -291,16 +316,17 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
         }
         __syncthreads();  // (A) H, H^T and |h|^2 partials visible
 
-
-        // ---- c = H Z^T for this wave's slots; gates ------------------------
-        // Gate inputs of this wave's slots are read before the products.
-        float hh[TB][4], av[TB][4], muv[TB][4];
+        // ---- c = H Z^T for this wave's slots and its group's tokens; gates --
+        // Gate inputs are read before the products.  Tile i of the group is
+        // token tile tbg + i of the sub-block.
+        float hh[TBW][4], av[TBW][4], muv[TBW][4];
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
+        for (int i = 0; i < TBW; ++i) {
+            const int tb = tbg + i;
             if constexpr (G::WSE == 1) {
                 const f32x4 h4 = *reinterpret_cast<const f32x4*>(hp + 16 * tb + 4 * lg);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) hh[tb][r] = h4[r];
+                for (int r = 0; r < 4; ++r) hh[i][r] = h4[r];
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -308,7 +334,7 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
                     float x = 0.f;
 #pragma unroll
                     for (int g = 0; g < G::WSE; ++g) x += q4[g];
-                    hh[tb][r] = x;
+                    hh[i][r] = x;
                 }
             }
             const f32x4 mu4 = *reinterpret_cast<const f32x4*>(mus + 16 * tb + 4 * lg);
@@ -316,104 +342,107 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
             for (int r = 0; r < 4; ++r) {
                 const int tau = 16 * tb + 4 * lg + r;
                 const float k = bf16_val(ks[tau * G::KS_LD + slot]);
-                av[tb][r] = bf16_val(gs[tau * G::GS_LD + slot]) * k;
-                muv[tb][r] = mu4[r];
+                av[i][r] = bf16_val(gs[tau * G::GS_LD + slot]) * k;
+                muv[i][r] = mu4[r];
             }
         }
-        f32x4 cc[TB];
+        f32x4 cc[TBW];
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) cc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < TBW; ++i) cc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (G::K32_D) {
 #pragma unroll
             for (int kd = 0; kd < D / 32; ++kd) {
-                bf16x8 ah[TB], al[TB];
+                bf16x8 ah[TBW], al[TBW];
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    const int ao = (16 * tb + lc) * G::HS_LD + 32 * kd + 4 * lg;
-                    ah[tb] = ld8p(hsh + ao);
-                    al[tb] = ld8p(hsl + ao);
+                for (int i = 0; i < TBW; ++i) {
+                    const int ao = (16 * (tbg + i) + lc) * G::HS_LD + 32 * kd + 4 * lg;
+                    ah[i] = ld8p(hsh + ao);
+                    al[i] = ld8p(hsl + ao);
                 }
                 const bf16x8 bh = cat8(zfh[2 * kd], zfh[2 * kd + 1]), bl = cat8(zfl[2 * kd], zfl[2 * kd + 1]);
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) cc[tb] = mma32(al[tb], bh, cc[tb]);
+                for (int i = 0; i < TBW; ++i) cc[i] = mma32(al[i], bh, cc[i]);
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) cc[tb] = mma32(ah[tb], bl, cc[tb]);
+                for (int i = 0; i < TBW; ++i) cc[i] = mma32(ah[i], bl, cc[i]);
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) cc[tb] = mma32(ah[tb], bh, cc[tb]);
+                for (int i = 0; i < TBW; ++i) cc[i] = mma32(ah[i], bh, cc[i]);
             }
         } else {
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const int ao = (16 * tb + lc) * G::HS_LD + 4 * lg;
-                cc[tb] = mma3(ld4s(hsh + ao), ld4s(hsl + ao), zfh[0], zfl[0], cc[tb]);
+            for (int i = 0; i < TBW; ++i) {
+                const int ao = (16 * (tbg + i) + lc) * G::HS_LD + 4 * lg;
+                cc[i] = mma3(ld4s(hsh + ao), ld4s(hsl + ao), zfh[0], zfl[0], cc[i]);
             }
         }
-        float gt[TB][4], kp[TB][4], tot[TB], ex_lo[TB], ex_hi[TB];
+        float gt[TBW][4], kp[TBW][4], tot[TBW], ex_lo[TBW], ex_hi[TBW];
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
+        for (int i = 0; i < TBW; ++i) {
             float prod = 1.f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float a = av[tb][r], mu = muv[tb][r], cr = cc[tb][r];
-                const float wv = fmaxf(fmaf(-cr, cr, hh[tb][r]), 0.f);
-                const float beta = __builtin_amdgcn_rsqf(fmaf(mu, mu, a * a * wv));
-                gt[tb][r] = beta * fmaf(a, cr, mu);
-                kp[tb][r] = -beta * a;
-                prod *= gt[tb][r];
+                const float a = av[i][r], mu = muv[i][r], cr = cc[i][r];
+                const float wvv = fmaxf(fmaf(-cr, cr, hh[i][r]), 0.f);
+                const float beta = __builtin_amdgcn_rsqf(fmaf(mu, mu, a * a * wvv));
+                gt[i][r] = beta * fmaf(a, cr, mu);
+                kp[i][r] = -beta * a;
+                prod *= gt[i][r];
             }
-            rows4_prod_scan(prod, lg, ex_lo[tb], ex_hi[tb], tot[tb]);
+            rows4_prod_scan(prod, lg, ex_lo[i], ex_hi[i], tot[i]);
             if constexpr (WRITE_Z) {
-                const int64_t o = static_cast<int64_t>(slot) * C + tc0 + 16 * tb + 4 * lg;
-                *reinterpret_cast<f32x4*>(ws.g + o) = f32x4{gt[tb][0], gt[tb][1], gt[tb][2], gt[tb][3]};
-                *reinterpret_cast<f32x4*>(ws.k + o) = f32x4{kp[tb][0], kp[tb][1], kp[tb][2], kp[tb][3]};
+                const int64_t o = static_cast<int64_t>(slot) * C + tc0 + 16 * (tbg + i) + 4 * lg;
+                *reinterpret_cast<f32x4*>(ws.g + o) = f32x4{gt[i][0], gt[i][1], gt[i][2], gt[i][3]};
+                *reinterpret_cast<f32x4*>(ws.k + o) = f32x4{kp[i][0], kp[i][1], kp[i][2], kp[i][3]};
             }
         }
-        // W_t = kappa_t (.) prod_{l > t} g_l inside the sub-block, split into
-        // B operands of the update (k = token); A_end = prod of all g.
-        s16x4 wh4[TB], wl4[TB];
+        // W_t = kappa_t (.) prod_{l > t} g_l over the group's tokens, split into
+        // B operands of the update (k = token); aend = prod of the group's g.
+        s16x4 wh4[TBW], wl4[TBW];
         float aend = 1.f;
 #pragma unroll
-        for (int tb = TB - 1; tb >= 0; --tb) {
-            float s_ = aend * ex_hi[tb];
-            f32x4 wv;
+        for (int i = TBW - 1; i >= 0; --i) {
+            float s_ = aend * ex_hi[i];
+            f32x4 wvec;
 #pragma unroll
             for (int r = 3; r >= 0; --r) {
-                wv[r] = kp[tb][r] * s_;
-                s_ *= gt[tb][r];
+                wvec[r] = kp[i][r] * s_;
+                s_ *= gt[i][r];
             }
-            split4(wv, wh4[tb], wl4[tb]);
-            aend *= tot[tb];
+            split4(wvec, wh4[i], wl4[i]);
+            aend *= tot[i];
         }
 
-        // ---- R^T <- R^T diag(A_end) + H^T W ---------------------------------
+        // ---- R^T <- R^T diag(A_end) + H^T W (PAIR: U_g = H^T W over half g) --
+        f32x4 u[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[db][r] *= aend;
+            for (int r = 0; r < 4; ++r) u[db][r] = PAIR ? 0.f : acc[db][r] * aend;
         if constexpr (G::K32_C) {
 #pragma unroll
-            for (int kt = 0; kt < C0 / 32; ++kt) {
+            for (int kt = 0; kt < TBW / 2; ++kt) {
                 bf16x8 th[DB], tl[DB];
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
-                    const int ao = (16 * db + lc) * G::HT_LD + 32 * kt + 4 * lg;
+                    const int ao = (16 * db + lc) * G::HT_LD + 16 * tbg + 32 * kt + 4 * lg;
                     th[db] = ld8p(hth + ao);
                     tl[db] = ld8p(htl + ao);
                 }
                 const bf16x8 bh = cat8(wh4[2 * kt], wh4[2 * kt + 1]), bl = cat8(wl4[2 * kt], wl4[2 * kt + 1]);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) acc[db] = mma32(tl[db], bh, acc[db]);
+                for (int db = 0; db < DB; ++db) u[db] = mma32(tl[db], bh, u[db]);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) acc[db] = mma32(th[db], bl, acc[db]);
+                for (int db = 0; db < DB; ++db) u[db] = mma32(th[db], bl, u[db]);
 #pragma unroll
-                for (int db = 0; db < DB; ++db) acc[db] = mma32(th[db], bh, acc[db]);
+                for (int db = 0; db < DB; ++db) u[db] = mma32(th[db], bh, u[db]);
             }
         } else {
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int ao = (16 * db + lc) * G::HT_LD + 4 * lg;
-                acc[db] = mma3(ld4s(hth + ao), ld4s(htl + ao), wh4[0], wl4[0], acc[db]);
-            }
+            for (int i = 0; i < TBW; ++i)
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int ao = (16 * db + lc) * G::HT_LD + 16 * (tbg + i) + 4 * lg;
+                    u[db] = mma3(ld4s(hth + ao), ld4s(htl + ao), wh4[i], wl4[i], u[db]);
+                }
         }
 
         // Next sub-block's inputs into the other staging buffer (its last
@@ -422,16 +451,43 @@ __global__ __launch_bounds__(4 * M) void osr_chain_kernel(Params p) {
         // were issued before this sub-block's workspace stores, so the wait
         // for them here leaves those stores in flight.
         if (has_next) commit<G, false>(nxt, stage + ((s + 1) & 1) * G::STAGE, p.gamma_per_slot != 0);
+
+        if constexpr (PAIR) {
+            // Swap (U_g, t_g) within the pair; both form
+            // R_end = diag(t_0 t_1) Z + diag(t_1) U_0 + U_1 (acc holds Z).
+            f32x4* xu = reinterpret_cast<f32x4*>(smem + G::O_XU);
+            float* xt = reinterpret_cast<float*>(smem + G::O_XT);
+#pragma unroll
+            for (int db = 0; db < DB; ++db) xu[(w * 64 + lane) * DB + db] = u[db];
+            xt[w * 64 + lane] = aend;
+            __syncthreads();  // (X) both halves' U and t visible
+            const int pw = (1 - grp) * G::NWS + wv;  // partner wave
+            const float tp = xt[pw * 64 + lane];
+            const float t0h = grp == 0 ? aend : tp, t1h = grp == 0 ? tp : aend;
+            const float az = t0h * t1h;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const f32x4 up = xu[(pw * 64 + lane) * DB + db];
+                const f32x4 u0 = grp == 0 ? u[db] : up, u1 = grp == 0 ? up : u[db];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[db][r] = fmaf(acc[db][r], az, fmaf(u0[r], t1h, u1[r]));
+            }
+        } else {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] = u[db];
+        }
     }
 
     const float inv = row_inv_norm<DB>(acc);
-    float* dst = p.state_out + static_cast<int64_t>(bh) * M * D + static_cast<int64_t>(slot) * D + 4 * lg;
+    if (grp == 0) {
+        float* dst = p.state_out + static_cast<int64_t>(bh) * M * D + static_cast<int64_t>(slot) * D + 4 * lg;
 #pragma unroll
-    for (int j = 0; j < DB; ++j) {
-        f32x4 z = acc[j];
+        for (int j = 0; j < DB; ++j) {
+            f32x4 z = acc[j];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) z[r] *= inv;
-        *reinterpret_cast<f32x4*>(dst + 16 * j) = z;
+            for (int r = 0; r < 4; ++r) z[r] *= inv;
+            *reinterpret_cast<f32x4*>(dst + 16 * j) = z;
+        }
     }
 }
 

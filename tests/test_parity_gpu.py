@@ -268,3 +268,38 @@ def test_mfma_split_and_fused_agree(monkeypatch, mode):
     # output), not bit for bit; each one separately meets the oracle tolerance.
     assert (ys - yf).abs().max().item() <= 2e-4 * ys.abs().max().item()
     assert (Ss - Sf).abs().max().item() <= 1e-4
+
+
+# ------------------------------------ state passing with and without pairs --
+# Pairs run for m <= 32 with C >= 32; the m = 64 case checks that the
+# override leaves the one-wave kernel in place there.
+PAIR_CASES = [(32, 32, 32), (32, 32, 64), (16, 64, 64), (16, 16, 32), (32, 64, 64), (32, 128, 32), (64, 64, 64)]
+
+
+@pytest.mark.parametrize("pairs", ["1", "0"])
+@pytest.mark.parametrize("m,d,C", PAIR_CASES)
+def test_chain_pairs(monkeypatch, pairs, m, d, C):
+    """Shapes where a chunk is one sub-block: the two-waves-per-slot-block
+    state passing (default) and the one-wave form, both against the oracle,
+    over several chunks and both objectives."""
+    _say(f"state passing pairs={pairs} m={m} d={d} C={C}")
+    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "split")
+    monkeypatch.setenv("LATTICE_OSR_CHAIN_PAIRS", pairs)
+    for mode in (osr.MODE_DEC, osr.MODE_SIM):
+        inp = synth.make_inputs(2, 6 * C, 2, m, d, seed=300 + m + d + C + mode, in_dtype=synth.BF16)
+        y, S = _run("chunked", inp, C, mode=mode)
+        _check(inp, y, S, C, mode)
+
+
+def test_chain_pairs_agree(monkeypatch):
+    """The pair split regroups the chunk's suffix products exactly; the two
+    forms agree to the split-bf16 rounding of their products."""
+    _say("state passing pairs vs one wave per slot block")
+    inp = synth.make_inputs(2, 512, 2, 32, 64, seed=404, in_dtype=synth.BF16)
+    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "split")
+    monkeypatch.setenv("LATTICE_OSR_CHAIN_PAIRS", "1")
+    y1, S1 = _run("chunked", inp, 64)
+    monkeypatch.setenv("LATTICE_OSR_CHAIN_PAIRS", "0")
+    y0, S0 = _run("chunked", inp, 64)
+    assert (y1 - y0).abs().max().item() <= 2e-4 * y0.abs().max().item()
+    assert (S1 - S0).abs().max().item() <= 1e-4
