@@ -291,7 +291,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                     const int dcol = 16 * (g1_grp + G::WSE * dj) + lc;
                     const f32x4 a = ha[ti][dj];
                     if constexpr (WRITE_Z)
-                        *reinterpret_cast<f32x4*>(ws.h + static_cast<int64_t>(dcol) * C + tc0 + 16 * tb + 4 * lg) = a;
+                        *reinterpret_cast<f32x4*>(ws.h + ws_frag(g1_grp + G::WSE * dj, tc0 / 16 + tb, C / 16, lane)) = a;
                     s16x4 hh4, hl4;
                     split4(a, hh4, hl4);
                     *reinterpret_cast<s16x4*>(hth + dcol * G::HT_LD + 16 * tb + 4 * lg) = hh4;
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
             }
             rows4_prod_scan(prod, lg, ex_lo[i], ex_hi[i], tot[i]);
             if constexpr (WRITE_Z) {
-                const int64_t o = static_cast<int64_t>(slot) * C + tc0 + 16 * (tbg + i) + 4 * lg;
+                const int64_t o = ws_frag(wv, tc0 / 16 + tbg + i, C / 16, lane);
                 *reinterpret_cast<f32x4*>(ws.g + o) = f32x4{gt[i][0], gt[i][1], gt[i][2], gt[i][3]};
                 *reinterpret_cast<f32x4*>(ws.k + o) = f32x4{kp[i][0], kp[i][1], kp[i][2], kp[i][3]};
             }

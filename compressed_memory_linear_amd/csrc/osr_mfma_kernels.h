@@ -146,15 +146,23 @@ __device__ __forceinline__ void rows4_prod_scan(float x, int lg, float& below, f
 }
 
 // Workspace of the split schedule, fp32, for every (b,h) and chunk n (all
-// taken at the chunk-start state): Z [m][d], the gates g [m][C] and kappa
-// [m][C] (token-contiguous per slot) and h [d][C] (token-contiguous per
-// column).  The state-passing kernel writes it, the read-out kernel reads it.
+// taken at the chunk-start state): Z [m][d], the gates g and kappa and the
+// vectors h.  The state-passing kernel writes it, the read-out kernel reads it.
+// g, kappa (per slot block) and h (per column block) are stored in MFMA lane
+// order, 1 KiB per (16-row block, 16-token tile): lane (lg, lc) holds row
+// 16*block + lc at tokens 16*tile + 4*lg .. +3.  Both kernels hold them in
+// exactly that lane layout, so every store and load moves one contiguous KiB.
 struct Workspace {
     float* z;
     float* g;
     float* k;
     float* h;
 };
+// Offset (floats) of the 4 values of one lane: block of 16 rows, token tile
+// of the chunk (C/16 tiles per block).
+__device__ __forceinline__ int64_t ws_frag(int block, int tile, int tiles_per_chunk, int lane) {
+    return ((static_cast<int64_t>(block) * tiles_per_chunk + tile) * 64 + lane) * 4;
+}
 template <int M, int D>
 __device__ __forceinline__ Workspace workspace_at(const Params& p, int bh, int n) {
     const int C = p.chunk, NC = p.T / C;

@@ -6,7 +6,8 @@
 // recurrence_linear2 and its gated-linear-attention form.  Inside a chunk the
 // state evolves as s_i <- g_{t,i} s_i + kappa_{t,i} h_t with gates and h_t
 // taken at the chunk-start state Z; the read-out is y_t = sum_i q_{t,i} s_i.
-// The state-passing kernel stores, per chunk, Z, g, kappa and h (workspace);
+// The state-passing kernel stores, per chunk, Z, g, kappa and h (workspace,
+// the per-token values in MFMA lane order);
 // here each workgroup takes cpw consecutive chunks of one (b, h) and, over
 // sub-blocks of C0 tokens with R the state at the sub-block start and A the
 // running product of g inside the sub-block,
@@ -82,7 +83,7 @@ __device__ __forceinline__ void rd_load(RdIn<G>& in, const Params& p, const Work
         const int slot = 16 * mb + lc;
 #pragma unroll
         for (int tb = 0; tb < G::TB; ++tb) {
-            const int64_t o = static_cast<int64_t>(slot) * C + tc0 + 16 * tb + 4 * lg;
+            const int64_t o = ws_frag(mb, tc0 / 16 + tb, C / 16, lane);
             in.g[mi][tb] = *reinterpret_cast<const f32x4*>(ws.g + o);
             in.k[mi][tb] = *reinterpret_cast<const f32x4*>(ws.k + o);
 #pragma unroll
@@ -94,7 +95,7 @@ __device__ __forceinline__ void rd_load(RdIn<G>& in, const Params& p, const Work
     }
 #pragma unroll
     for (int tb = 0; tb < G::TB; ++tb)
-        in.h[tb] = *reinterpret_cast<const f32x4*>(ws.h + static_cast<int64_t>(16 * w + lc) * C + tc0 + 16 * tb + 4 * lg);
+        in.h[tb] = *reinterpret_cast<const f32x4*>(ws.h + ws_frag(w, tc0 / 16 + tb, C / 16, lane));
 }
 
 template <int M, int D>
