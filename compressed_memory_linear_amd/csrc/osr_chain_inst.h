@@ -71,11 +71,14 @@ static int launch_chain(const Params& p, hipStream_t st) {
 
 template <int M, int D>
 static int launch_chain_md(const Params& p, hipStream_t st) {
-    switch (pick_c0_chain<M, D>(p.chunk)) {
-        case 64: return launch_chain<M, D, 64>(p, st);
-        case 32: return launch_chain<M, D, 32>(p, st);
-        default: return launch_chain<M, D, 16>(p, st);
-    }
+    // Only sub-block lengths the pick can return are instantiated.
+    constexpr int cmax = pick_c0_chain<M, D>(64);
+    const int c0 = pick_c0_chain<M, D>(p.chunk);
+    if constexpr (cmax >= 64)
+        if (c0 == 64) return launch_chain<M, D, 64>(p, st);
+    if constexpr (cmax >= 32)
+        if (c0 == 32) return launch_chain<M, D, 32>(p, st);
+    return launch_chain<M, D, 16>(p, st);
 }
 
 template <int M>

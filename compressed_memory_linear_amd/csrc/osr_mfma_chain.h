@@ -170,7 +170,8 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
 #pragma unroll
         for (int j = 0; j < DB; ++j) acc[j] = *reinterpret_cast<const f32x4*>(src + 16 * j);
     }
-    prefetch<G, false>(nxt, p, b, hd, 0);
+    const PreOff<G> poff = prefetch_offsets<G>(p);
+    prefetch<G, false>(nxt, poff, p, b, hd, 0);
     commit<G, false>(nxt, stage, p.gamma_per_slot != 0);
 
     for (int s = 0; s < NS; ++s) {
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // Loads of the next sub-block, issued before the chunk-start stores
         // below (the memory counter retires in order).  Unconditional: the
         // last sub-block re-reads its own tile.
-        prefetch<G, false>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
+        prefetch<G, false>(nxt, poff, p, b, hd, has_next ? t0 + C0 : t0);
         if (chunk_start) {
             if constexpr (WRITE_Z) {
                 if (grp == 0) {
@@ -327,6 +328,16 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                 const f32x4 h4 = *reinterpret_cast<const f32x4*>(hp + 16 * tb + 4 * lg);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) hh[i][r] = h4[r];
+            } else if constexpr (G::WSE % 4 == 0) {
+                // WSE partials per token, contiguous: 16-byte broadcast reads.
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const f32x4* q4 = reinterpret_cast<const f32x4*>(hp + (16 * tb + 4 * lg + r) * G::WSE);
+                    f32x4 x = q4[0];
+#pragma unroll
+                    for (int g = 1; g < G::WSE / 4; ++g) x += q4[g];
+                    hh[i][r] = (x[0] + x[1]) + (x[2] + x[3]);
+                }
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {

@@ -248,6 +248,43 @@ struct Pre {
     uint16_t mu;            // thread tau < C0 holds token tau
 };
 
+// Per-lane byte offsets of a thread's staged pieces, relative to the
+// sub-block's first token row of its (b, h).  They do not change from one
+// sub-block to the next (only the wave-uniform base does), so they are
+// computed once and every load is a uniform 64-bit base plus a 32-bit lane
+// offset.
+template <class G>
+struct PreOff {
+    uint32_t kq[G::KPT];   // k, a per-slot gamma tile and q pieces
+    uint32_t gtok[G::KPT]; // gamma of each k piece's token (per-token gamma), or its first slot
+    uint32_t v[G::VPT];
+    uint32_t mu;
+};
+
+template <class G>
+__device__ __forceinline__ PreOff<G> prefetch_offsets(const Params& p) {
+    constexpr int M = G::M_, D = G::D_, C0 = G::C0_;
+    const int tid = threadIdx.x;
+    const uint32_t rs = static_cast<uint32_t>(p.H);  // token stride in rows
+    PreOff<G> o;
+#pragma unroll
+    for (int j = 0; j < G::KPT; ++j) {
+        int e = tid + j * G::NT;
+        if (G::KPC % G::NT != 0) e = e < G::KPC ? e : G::KPC - 1;
+        const uint32_t row = static_cast<uint32_t>(e / (M / 8)) * rs;
+        o.kq[j] = (row * M + (e % (M / 8)) * 8) * 2;
+        o.gtok[j] = (p.gamma_per_slot ? row * M : row) * 2;
+    }
+#pragma unroll
+    for (int j = 0; j < G::VPT; ++j) {
+        int e = tid + j * G::NT;
+        if (G::VPC % G::NT != 0) e = e < G::VPC ? e : G::VPC - 1;
+        o.v[j] = (static_cast<uint32_t>(e / (D / 8)) * rs * D + (e % (D / 8)) * 8) * 2;
+    }
+    o.mu = static_cast<uint32_t>(tid % C0) * rs * 2;
+    return o;
+}
+
 // Every load below is unconditional (indices are clamped) so none sits behind
 // a branch, which would make the compiler wait for it at the join.  A
 // per-token gamma is broadcast over the 8 slots of each piece at commit, so the
@@ -255,36 +292,26 @@ struct Pre {
 // k, for a per-token gamma) and the scalar load (the first slot's gamma for a
 // per-slot gamma) are issued, and commit picks one.
 template <class G, bool WITH_Y>
-__device__ __forceinline__ void prefetch(Pre<G>& pf, const Params& p, int b, int hd, int t0) {
-    constexpr int M = G::M_, D = G::D_, C0 = G::C0_;
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void prefetch(Pre<G>& pf, const PreOff<G>& o, const Params& p, int b, int hd, int t0) {
+    constexpr int M = G::M_, D = G::D_;
     const bool gslot = p.gamma_per_slot != 0;
-    const uint16_t* kg = static_cast<const uint16_t*>(p.k);
-    const uint16_t* vg = static_cast<const uint16_t*>(p.v);
-    const uint16_t* gg = static_cast<const uint16_t*>(p.gamma);
-    const uint16_t* gtile = gslot ? gg : kg;
-    const uint16_t* qg = static_cast<const uint16_t*>(p.q);
-    const uint16_t* mug = static_cast<const uint16_t*>(p.mu);
     const int64_t row0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;  // token t0
-    const int64_t rs = p.H;                                               // token stride in rows
+    const char* kb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.k) + row0 * M);
+    const char* gb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.gamma) + (gslot ? row0 * M : row0));
+    const char* tb = gslot ? gb : kb;  // per-slot gamma tile, or a valid dummy
+    const char* qb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.q) + row0 * M);
+    const char* vb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.v) + row0 * D);
+    const char* mb = reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.mu) + row0);
 #pragma unroll
     for (int j = 0; j < G::KPT; ++j) {
-        int e = tid + j * G::NT;
-        if (G::KPC % G::NT != 0) e = e < G::KPC ? e : G::KPC - 1;
-        const int64_t row = row0 + (e / (M / 8)) * rs;
-        const int64_t off = row * M + (e % (M / 8)) * 8;
-        pf.k[j] = *reinterpret_cast<const u32x4*>(kg + off);
-        pf.g[j] = *reinterpret_cast<const u32x4*>(gtile + off);
-        pf.gtok[j] = gg[gslot ? row * M : row];
-        if constexpr (WITH_Y) pf.q[j] = *reinterpret_cast<const u32x4*>(qg + off);
+        pf.k[j] = *reinterpret_cast<const u32x4*>(kb + o.kq[j]);
+        pf.g[j] = *reinterpret_cast<const u32x4*>(tb + o.kq[j]);
+        pf.gtok[j] = *reinterpret_cast<const uint16_t*>(gb + o.gtok[j]);
+        if constexpr (WITH_Y) pf.q[j] = *reinterpret_cast<const u32x4*>(qb + o.kq[j]);
     }
 #pragma unroll
-    for (int j = 0; j < G::VPT; ++j) {
-        int e = tid + j * G::NT;
-        if (G::VPC % G::NT != 0) e = e < G::VPC ? e : G::VPC - 1;
-        pf.v[j] = *reinterpret_cast<const u32x4*>(vg + (row0 + (e / (D / 8)) * rs) * D + (e % (D / 8)) * 8);
-    }
-    pf.mu = mug[row0 + (tid % C0) * rs];
+    for (int j = 0; j < G::VPT; ++j) pf.v[j] = *reinterpret_cast<const u32x4*>(vb + o.v[j]);
+    pf.mu = *reinterpret_cast<const uint16_t*>(mb + o.mu);
 }
 
 template <class G, bool WITH_Y>
@@ -686,8 +713,9 @@ __global__ __launch_bounds__(4 * D) void osr_fused_kernel(Params p) {
     s16x4 zfh[G::MT], zfl[G::MT];
     bf16x8 z8h[(M + 31) / 32], z8l[(M + 31) / 32];
     Pre<G> nxt;
+    const PreOff<G> poff = prefetch_offsets<G>(p);
     load_rows<M, D>(acc, p.state_in + static_cast<int64_t>(bh) * M * D);
-    prefetch<G, true>(nxt, p, b, hd, 0);
+    prefetch<G, true>(nxt, poff, p, b, hd, 0);
     commit<G, true>(nxt, stage, p.gamma_per_slot != 0);
     for (int s = 0; s < NS; ++s) {
         const int t0 = s * C0;
@@ -695,7 +723,7 @@ __global__ __launch_bounds__(4 * D) void osr_fused_kernel(Params p) {
         // prefetch registers are never a conditionally written aggregate.
         const bool has_next = s + 1 < NS;
         if (s % SPC == 0) project_state<M, D, G>(acc, smem);  // its barriers also publish the first staged inputs
-        prefetch<G, true>(nxt, p, b, hd, has_next ? t0 + C0 : t0);
+        prefetch<G, true>(nxt, poff, p, b, hd, has_next ? t0 + C0 : t0);
         if (s % SPC == 0) stage_z<M, D, G>(acc, zfh, zfl, z8h, z8l, smem);
         osr_subblock<M, D, C0, true>(p, smem, acc, zfh, zfl, z8h, z8l, s % SPC == 0, stage + (s & 1) * G::STAGE, nxt,
                                      stage + ((s + 1) & 1) * G::STAGE, has_next, true, b, hd, t0);
