@@ -73,7 +73,7 @@ struct ChainCfg {
     static constexpr int VS_LD = D + 8;
     static constexpr int HS_LD = D + 4;
     static constexpr int HT_LD = C0 + 4;
-    static constexpr int GS_LD = M;
+    static constexpr int GS_LD = M + 8;
     static constexpr bool K32_M = M % 32 == 0;      // H = K Z     (k = slot)
     static constexpr bool K32_D = D % 32 == 0;      // c = H Z^T   (k = column)
     static constexpr bool K32_C = TBW % 2 == 0;     // R^T += H^T W (k = token, a group's tokens)
@@ -160,6 +160,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
     // H = K Z - V assignment of this wave (inside its group).
     const int g1_tb0 = tbg + wv % G::TG, g1_grp = wv / G::TG;
     const bool g1_active = g1_grp < G::WSE;
+    const s16x4 eye = eye_operand(false), neg_eye = eye_operand(true);
 
     f32x4 acc[DB];             // R^T tiles: acc[j][r] = R[slot][16j + 4lg + r]
     s16x4 zfh[DB], zfl[DB];    // split Z^T tiles: B operands of c = H Z^T
@@ -214,12 +215,10 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
 #pragma unroll
             for (int j = 0; j < DB; ++j) {
                 split4(acc[j], zfh[j], zfl[j]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int col = 16 * j + 4 * lg + r;
-                    if (!PAIR || grp == 0) zth[col * G::ZT_LD + slot] = zfh[j][r];
-                    if (!PAIR || grp == 1) ztl[col * G::ZT_LD + slot] = zfl[j][r];
-                }
+                // transposed, the lane holds slots 16wv + 4lg .. +3 of column 16j + lc
+                const int zo = (16 * j + lc) * G::ZT_LD + 16 * wv + 4 * lg;
+                if (!PAIR || grp == 0) *reinterpret_cast<s16x4*>(zth + zo) = tr16(zfh[j], eye);
+                if (!PAIR || grp == 1) *reinterpret_cast<s16x4*>(ztl + zo) = tr16(zfl[j], eye);
             }
         }
         __syncthreads();  // (S) Z^T and this sub-block's staged inputs visible; H buffers free
@@ -229,15 +228,15 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // accumulators), then the epilogue.
         if (g1_active) {
             constexpr int TPW = G::TPW, DPW = G::DPW;
-            // Accumulators start at -V.
+            // Accumulators start at -V: rows of V read 8 bytes at a time and
+            // brought into the accumulator layout by the negated identity.
             f32x4 ha[TPW][DPW];
 #pragma unroll
             for (int ti = 0; ti < TPW; ++ti)
 #pragma unroll
                 for (int dj = 0; dj < DPW; ++dj) {
-                    const int tb = g1_tb0 + G::TG * ti, dcol = 16 * (g1_grp + G::WSE * dj) + lc;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) ha[ti][dj][r] = -bf16_val(vs[(16 * tb + 4 * lg + r) * G::VS_LD + dcol]);
+                    const int tb = g1_tb0 + G::TG * ti, dc0 = 16 * (g1_grp + G::WSE * dj);
+                    ha[ti][dj] = tr16f(ld4s(vs + (16 * tb + lc) * G::VS_LD + dc0 + 4 * lg), neg_eye);
                 }
             if (p.mode == 0) {
                 if constexpr (G::K32_M) {
@@ -297,13 +296,13 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                     split4(a, hh4, hl4);
                     *reinterpret_cast<s16x4*>(hth + dcol * G::HT_LD + 16 * tb + 4 * lg) = hh4;
                     *reinterpret_cast<s16x4*>(htl + dcol * G::HT_LD + 16 * tb + 4 * lg) = hl4;
+                    // token-major copy: transposed, the lane holds columns
+                    // dcol - lc + 4lg .. +3 of token 16tb + lc
+                    const int so = (16 * tb + lc) * G::HS_LD + dcol - lc + 4 * lg;
+                    *reinterpret_cast<s16x4*>(hsh + so) = tr16(hh4, eye);
+                    *reinterpret_cast<s16x4*>(hsl + so) = tr16(hl4, eye);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = 16 * tb + 4 * lg + r;
-                        hsh[row * G::HS_LD + dcol] = hh4[r];
-                        hsl[row * G::HS_LD + dcol] = hl4[r];
-                        sq[r] = fmaf(a[r], a[r], sq[r]);
-                    }
+                    for (int r = 0; r < 4; ++r) sq[r] = fmaf(a[r], a[r], sq[r]);
                 }
                 // |h_t|^2 over this wave's columns: reductions first, one
                 // guarded block of stores.
@@ -349,11 +348,13 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                 }
             }
             const f32x4 mu4 = *reinterpret_cast<const f32x4*>(mus + 16 * tb + 4 * lg);
+            // k and gamma of tokens 16tb + 4lg + r for this lane's slot, from
+            // 8-byte row reads brought into the accumulator layout
+            const f32x4 k4 = tr16f(ld4s(ks + (16 * tb + lc) * G::KS_LD + 16 * wv + 4 * lg), eye);
+            const f32x4 g4 = tr16f(ld4s(gs + (16 * tb + lc) * G::GS_LD + 16 * wv + 4 * lg), eye);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int tau = 16 * tb + 4 * lg + r;
-                const float k = bf16_val(ks[tau * G::KS_LD + slot]);
-                av[i][r] = bf16_val(gs[tau * G::GS_LD + slot]) * k;
+                av[i][r] = g4[r] * k4[r];
                 muv[i][r] = mu4[r];
             }
         }

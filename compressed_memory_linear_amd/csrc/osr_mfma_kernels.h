@@ -114,6 +114,28 @@ __device__ __forceinline__ bf16x8 ld8p(const short* p) {
 }
 __device__ __forceinline__ s16x4 ld4s(const short* p) { return *reinterpret_cast<const s16x4*>(p); }
 
+// Tile transposes on the matrix core.  A lane passes the four values it holds
+// in the accumulator layout, X[4lg + r][lc], as an A operand, which reads them
+// as A[lc][4lg + r], i.e. X^T; times the identity the product returns in the
+// accumulator layout, so the lane then holds X[lc][4lg + r]: four consecutive
+// columns of row lc, one 8-byte LDS access instead of four 2-byte ones.  The
+// same product turns four consecutive bf16 values of row lc read from LDS
+// into the accumulator layout (fp32).  Every product is x * 1 or x * 0, so the
+// results are the bf16 inputs exactly (times -1 with the negated identity).
+__device__ __forceinline__ s16x4 eye_operand(bool negate) {
+    const int lane = threadIdx.x & 63, lg = lane >> 4, lc = lane & 15;
+    const short one = negate ? static_cast<short>(0xBF80) : static_cast<short>(0x3F80);
+    s16x4 e;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = 4 * lg + j == lc ? one : static_cast<short>(0);
+    return e;
+}
+__device__ __forceinline__ f32x4 tr16f(s16x4 x, s16x4 eye) { return mma(x, eye, f32x4{0.f, 0.f, 0.f, 0.f}); }
+__device__ __forceinline__ s16x4 tr16(s16x4 x, s16x4 eye) {
+    const f32x4 t = tr16f(x, eye);  // bf16 values: the conversions are exact
+    return __builtin_bit_cast(s16x4, u32x2{cvt2_bf16(t[0], t[1]), cvt2_bf16(t[2], t[3])});
+}
+
 // Reductions over the four 16-lane rows of a wave, per lane column, with the
 // gfx950 row swaps: permlane16_swap(x, x) gives every row the value of the
 // even and of the odd row of its pair (rows 0/1, 2/3); permlane32_swap(y, y)
