@@ -196,18 +196,11 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[j][r] *= inv;
         }
-        // Loads of the next sub-block, issued before the chunk-start stores
-        // below (the memory counter retires in order).  Unconditional: the
-        // last sub-block re-reads its own tile.
+        // Loads of the next sub-block, issued before this sub-block's
+        // workspace stores (the memory counter retires in order).
+        // Unconditional: the last sub-block re-reads its own tile.
         prefetch<G, false>(nxt, poff, p, b, hd, has_next ? t0 + C0 : t0);
         if (chunk_start) {
-            if constexpr (WRITE_Z) {
-                if (grp == 0) {
-                    float* dst = ws.z + static_cast<int64_t>(slot) * D + 4 * lg;
-#pragma unroll
-                    for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
-                }
-            }
             // Z^T to LDS (read by every wave's H = K Z); the split tiles stay
             // in registers.  No wave reads Z^T between the last sub-block's
             // barrier (A) and the barrier (S) below.  A pair writes the hi
@@ -316,6 +309,16 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         }
         __syncthreads();  // (A) H, H^T and |h|^2 partials visible
 
+        // Z to the workspace, here rather than at the chunk start: there the
+        // stores queue behind the prefetch loads on the way to barrier (S).
+        // acc holds Z until the update below.
+        if constexpr (WRITE_Z) {
+            if (chunk_start && grp == 0) {
+                float* dst = ws.z + static_cast<int64_t>(slot) * D + 4 * lg;
+#pragma unroll
+                for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
+            }
+        }
         // ---- c = H Z^T for this wave's slots and its group's tokens; gates --
         // Gate inputs are read before the products.  Tile i of the group is
         // token tile tbg + i of the sub-block.
