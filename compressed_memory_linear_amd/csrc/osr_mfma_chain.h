@@ -311,12 +311,18 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
 
         // Z to the workspace, here rather than at the chunk start: there the
         // stores queue behind the prefetch loads on the way to barrier (S).
-        // acc holds Z until the update below.
+        // Stored as its bf16 hi/lo split (the operands every product of this
+        // chunk used), transposed to the read-out kernel's accumulator layout
+        // (slots 16wv + 4lg .. +3 of column 16j + lc), one 16-byte piece per
+        // lane and tile.
         if constexpr (WRITE_Z) {
             if (chunk_start && grp == 0) {
-                float* dst = ws.z + static_cast<int64_t>(slot) * D + 4 * lg;
 #pragma unroll
-                for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
+                for (int j = 0; j < DB; ++j) {
+                    const s16x4 th = tr16(zfh[j], eye), tl = tr16(zfl[j], eye);
+                    *reinterpret_cast<s16x8*>(ws.z + z_frag<D>(wv, j, lane)) =
+                        __builtin_shufflevector(th, tl, 0, 1, 2, 3, 4, 5, 6, 7);
+                }
             }
         }
         // ---- c = H Z^T for this wave's slots and its group's tokens; gates --

@@ -185,6 +185,13 @@ struct Workspace {
 __device__ __forceinline__ int64_t ws_frag(int block, int tile, int tiles_per_chunk, int lane) {
     return ((static_cast<int64_t>(block) * tiles_per_chunk + tile) * 64 + lane) * 4;
 }
+// Offset (floats) of one lane's piece of Z: slot block mt, column tile j; the
+// piece holds the bf16 hi parts of Z[16mt + 4lg + r][16j + lc], r = 0..3,
+// then the lo parts (16 bytes).
+template <int D>
+__device__ __forceinline__ int64_t z_frag(int mt, int j, int lane) {
+    return ((static_cast<int64_t>(mt) * (D / 16) + j) * 64 + lane) * 4;
+}
 template <int M, int D>
 __device__ __forceinline__ Workspace workspace_at(const Params& p, int bh, int n) {
     const int C = p.chunk, NC = p.T / C;

@@ -98,13 +98,20 @@ __device__ __forceinline__ void rd_load(RdIn<G>& in, const Params& p, const Work
         in.h[tb] = *reinterpret_cast<const f32x4*>(ws.h + ws_frag(w, tc0 / 16 + tb, C / 16, lane));
 }
 
+// Z of a chunk, stored as its bf16 hi/lo split in this kernel's accumulator
+// layout (one 16-byte piece per lane and slot tile); hi + lo is exact in fp32
+// and splits back into the same hi and lo.
 template <int M, int D>
 __device__ __forceinline__ void rd_load_z(f32x4 (&z)[M / 16], const float* src) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-    for (int mt = 0; mt < M / 16; ++mt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) z[mt][r] = src[(16 * mt + 4 * lg + r) * D + 16 * w + lc];
+    for (int mt = 0; mt < M / 16; ++mt) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(src + z_frag<D>(mt, w, lane));
+        z[mt][0] = __uint_as_float(v[0] << 16) + __uint_as_float(v[2] << 16);
+        z[mt][1] = __uint_as_float(v[0] & 0xffff0000u) + __uint_as_float(v[2] & 0xffff0000u);
+        z[mt][2] = __uint_as_float(v[1] << 16) + __uint_as_float(v[3] << 16);
+        z[mt][3] = __uint_as_float(v[1] & 0xffff0000u) + __uint_as_float(v[3] & 0xffff0000u);
+    }
 }
 
 template <int M, int D, int C0>
@@ -119,6 +126,7 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
     const int dcol = 16 * w + lc;
     const int ch0 = grp * cpw, NS = cpw * SPC;
+    const s16x4 eye = eye_operand(false);
 
     f32x4 acc[MT];  // R tiles: acc[mt][r] = R[16mt + 4lg + r][dcol]
     f32x4 zn[MT];   // next chunk's Z
@@ -178,14 +186,12 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
                     s16x4 qh, ql, kh, kl;
                     split4(qa, qh, ql);
                     split4(ka, kh, kl);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int o = (16 * tb + 4 * lg + r) * G::QA_LD + slot;
-                        qah[o] = qh[r];
-                        qal[o] = ql[r];
-                        kah[o] = kh[r];
-                        kal[o] = kl[r];
-                    }
+                    // transposed, the lane holds slots 16mb + 4lg .. +3 of token 16tb + lc
+                    const int o = (16 * tb + lc) * G::QA_LD + 16 * mb + 4 * lg;
+                    *reinterpret_cast<s16x4*>(qah + o) = tr16(qh, eye);
+                    *reinterpret_cast<s16x4*>(qal + o) = tr16(ql, eye);
+                    *reinterpret_cast<s16x4*>(kah + o) = tr16(kh, eye);
+                    *reinterpret_cast<s16x4*>(kal + o) = tr16(kl, eye);
                     fwd *= tot[tb];
                 }
                 // W_t = kappa_t (.) prod_{l > t} g_l, slot-major.
@@ -251,6 +257,9 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
                 split4(pj, ph, pl);
                 y = mma3(ph, pl, hh[jb], hl[jb], y);
             }
+            // 4-byte stores: 16 lanes cover 64 contiguous bytes of a token row
+            // (a transposed tile, 16 bytes per lane across 16 rows, issues four
+            // times the memory requests)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 st_y1(p.y, (row0 + static_cast<int64_t>(16 * tb + 4 * lg + r) * p.H) * D + dcol, y[r], p.y_bf16);
