@@ -171,6 +171,32 @@ def test_bf16_modes_and_gamma_layouts(mode, per_slot):
     _check(inp, y, S, 32, mode)
 
 
+# ------------------------------------------------------------ decode sweep --
+# 37 x 64 = 2368 states: more than the persistent decode grid holds at once for
+# every shape, and not a multiple of it, so workgroups take several states
+# each (the next state streams in while the current one is updated) and the
+# last round is ragged.
+DECODE_SHAPES = [(16, 16), (32, 64), (64, 128), (128, 128)]
+
+
+@pytest.mark.parametrize("m,d", DECODE_SHAPES)
+@pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM])
+@pytest.mark.parametrize("per_slot", [True, False])
+def test_decode_sweep_bf16(m, d, mode, per_slot):
+    _say(f"decode sweep bf16 m={m} d={d} mode={mode} per_slot={per_slot} (2368 states)")
+    inp = synth.make_inputs(37, 1, 64, m, d, seed=400 + m + d, in_dtype=synth.BF16, gamma_per_slot=per_slot)
+    y, S = _run("decode", inp, mode=mode)
+    _check(inp, y, S, 1, mode)
+
+
+@pytest.mark.parametrize("m,d", [(16, 32), (128, 128)])
+def test_decode_sweep_f32(m, d):
+    _say(f"decode sweep fp32 m={m} d={d} (2368 states)")
+    inp = synth.make_inputs(37, 1, 64, m, d, seed=500 + m + d, in_dtype=synth.F32)
+    y, S = _run("decode", inp)
+    _check(inp, y, S, 1, osr.MODE_DEC)
+
+
 # ------------------------------------------------------- workload-size runs --
 def test_workload_decode_s256h32_m128d128():
     _say("decode workload 256 seq x 32 heads, m=d=128")
