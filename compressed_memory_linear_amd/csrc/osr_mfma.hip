@@ -25,11 +25,16 @@ extern template int launch_m<128>(int, bool, const Params&, hipStream_t);
 
 // Schedule choice.  LATTICE_OSR_CHUNK_SCHEDULE=split|fused overrides the
 // default (split when there are fewer (b,h) sequences than compute units).
-bool use_split(int B, int H) {
+// The split schedule (state passing, then a read-out parallel over chunks)
+// wins while the sequences leave CUs idle; the fused kernel, with no
+// workspace round trip, once they fill the device: measured crossovers
+// between 128 and 256 (b,h) at d = 128 and between 256 and 512 at d = 64.
+bool use_split(int B, int H, int d) {
     const char* e = getenv("LATTICE_OSR_CHUNK_SCHEDULE");
     if (e && strcmp(e, "split") == 0) return true;
     if (e && strcmp(e, "fused") == 0) return false;
-    return static_cast<int64_t>(B) * H < 256;
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    return bh < 256 || (d <= 64 && bh < 512);
 }
 }  // namespace mfma
 
@@ -39,14 +44,14 @@ bool mfma_supported(int m, int d, int C) {
 }
 
 size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C) {
-    if (!mfma::use_split(B, H)) return 0;
+    if (!mfma::use_split(B, H, d)) return 0;
     // per (b,h,chunk): Z [m][d], g and kappa [m][C], h [d][C], fp32
     const size_t per_chunk = static_cast<size_t>(m) * d + 2 * static_cast<size_t>(m) * C + static_cast<size_t>(d) * C;
     return static_cast<size_t>(B) * H * (T / C) * per_chunk * sizeof(float);
 }
 
 int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st) {
-    const bool split = mfma::use_split(p.B, p.H);
+    const bool split = mfma::use_split(p.B, p.H, d);
     switch (m) {
         case 16: return mfma::launch_m<16>(d, split, p, st);
         case 32: return mfma::launch_m<32>(d, split, p, st);
