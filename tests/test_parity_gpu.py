@@ -280,6 +280,20 @@ def test_mfma_schedules(monkeypatch, schedule, m, d, C):
     _check(inp, y, S, C, osr.MODE_DEC)
 
 
+# Odd chunk counts: the read-out kernel then takes one chunk per workgroup
+# (its chunk groups must divide the count), and (b,h) counts that are not
+# powers of two.
+@pytest.mark.parametrize("schedule", ["split", "fused"])
+@pytest.mark.parametrize("m,d,C,nc", [(64, 64, 64, 5), (64, 128, 64, 3), (128, 128, 128, 3), (32, 64, 32, 7),
+                                      (16, 32, 16, 9)])
+def test_mfma_odd_chunk_counts(monkeypatch, schedule, m, d, C, nc):
+    _say(f"mfma schedule={schedule} m={m} d={d} C={C} chunks={nc}")
+    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", schedule)
+    inp = synth.make_inputs(3, nc * C, 5, m, d, seed=600 + m + d + nc, in_dtype=synth.BF16)
+    y, S = _run("chunked", inp, C)
+    _check(inp, y, S, C, osr.MODE_DEC)
+
+
 @pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM])
 def test_mfma_split_and_fused_agree(monkeypatch, mode):
     _say(f"mfma split vs fused mode={mode}")
