@@ -210,7 +210,10 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
 template <int M, int D>
 static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_t st) {
     constexpr int TPR = D / 4;
-    constexpr int NT_DEC = (M * TPR < 256) ? M * TPR : 256;
+    // Decode: up to 8 waves per state (fewer rows per thread: ~100 VGPRs, 4 waves per SIMD), which
+    // shortens each workgroup's arithmetic between its state load and store; measured 9% faster
+    // than 4 waves at m = d = 128.
+    constexpr int NT_DEC = (M * TPR < 512) ? M * TPR : 512;
     constexpr int NT_TOK = (M * TPR < 512) ? M * TPR : 512;
     const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H));
     if (decode) {
