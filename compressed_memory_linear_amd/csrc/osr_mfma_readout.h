@@ -99,18 +99,24 @@ __device__ __forceinline__ void rd_load(RdIn<G>& in, const Params& p, const Work
 }
 
 // Z of a chunk, stored as its bf16 hi/lo split in this kernel's accumulator
-// layout (one 16-byte piece per lane and slot tile); hi + lo is exact in fp32
-// and splits back into the same hi and lo.
+// layout (one 16-byte piece per lane and slot tile).  The pieces stay packed
+// in registers until the chunk starts (converting at the load would make the
+// load's latency wait there); hi + lo is exact in fp32 and splits back into
+// the same hi and lo.
 template <int M, int D>
-__device__ __forceinline__ void rd_load_z(f32x4 (&z)[M / 16], const float* src) {
+__device__ __forceinline__ void rd_load_z(u32x4 (&z)[M / 16], const float* src) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
+    for (int mt = 0; mt < M / 16; ++mt) z[mt] = *reinterpret_cast<const u32x4*>(src + z_frag<D>(mt, w, lane));
+}
+template <int M>
+__device__ __forceinline__ void rd_unpack_z(f32x4 (&z)[M / 16], const u32x4 (&v)[M / 16]) {
+#pragma unroll
     for (int mt = 0; mt < M / 16; ++mt) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(src + z_frag<D>(mt, w, lane));
-        z[mt][0] = __uint_as_float(v[0] << 16) + __uint_as_float(v[2] << 16);
-        z[mt][1] = __uint_as_float(v[0] & 0xffff0000u) + __uint_as_float(v[2] & 0xffff0000u);
-        z[mt][2] = __uint_as_float(v[1] << 16) + __uint_as_float(v[3] << 16);
-        z[mt][3] = __uint_as_float(v[1] & 0xffff0000u) + __uint_as_float(v[3] & 0xffff0000u);
+        z[mt][0] = __uint_as_float(v[mt][0] << 16) + __uint_as_float(v[mt][2] << 16);
+        z[mt][1] = __uint_as_float(v[mt][0] & 0xffff0000u) + __uint_as_float(v[mt][2] & 0xffff0000u);
+        z[mt][2] = __uint_as_float(v[mt][1] << 16) + __uint_as_float(v[mt][3] << 16);
+        z[mt][3] = __uint_as_float(v[mt][1] & 0xffff0000u) + __uint_as_float(v[mt][3] & 0xffff0000u);
     }
 }
 
@@ -129,11 +135,12 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
     const s16x4 eye = eye_operand(false);
 
     f32x4 acc[MT];  // R tiles: acc[mt][r] = R[16mt + 4lg + r][dcol]
-    f32x4 zn[MT];   // next chunk's Z
+    u32x4 zn[MT];   // next chunk's Z (packed hi/lo)
     RdIn<G> cur, nxt;
     {
         const Workspace ws = workspace_at<M, D>(p, bh, ch0);
-        rd_load_z<M, D>(acc, ws.z);
+        rd_load_z<M, D>(zn, ws.z);
+        rd_unpack_z<M>(acc, zn);
         rd_load<G>(cur, p, ws, b, hd, ch0 * C, 0);
     }
     for (int s = 0; s < NS; ++s) {
@@ -287,8 +294,7 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
                 acc[mt] = a;
             }
         } else {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) acc[mt] = zn[mt];
+            rd_unpack_z<M>(acc, zn);
         }
         cur = nxt;
     }
