@@ -20,9 +20,10 @@
 // (R as MFMA accumulator tiles, which are B operands with k = slot).  The
 // per-(token, slot) gate products are formed by the wave that owns the slot
 // block, which writes Q.A, kappa/A (token-major) and W^T (slot-major) to
-// LDS; one barrier per sub-block (the LDS buffers alternate between
-// sub-blocks).  All global inputs of sub-block s+1 are loaded into registers
-// while s computes.
+// LDS; the causal tiles P are formed once and shared through LDS; two
+// barriers per sub-block (the LDS buffers alternate between sub-blocks).
+// All global inputs of sub-block s+1 are loaded into registers while s
+// computes.
 #pragma once
 
 #include "osr_mfma_kernels.h"
@@ -51,7 +52,9 @@ struct ReadCfg {
     static constexpr int B_WH = B_KL + C0 * QA_LD * 2;   // W^T hi      [M][WT_LD]
     static constexpr int B_WL = B_WH + M * WT_LD * 2;    // W^T lo
     static constexpr int B_AE = B_WL + M * WT_LD * 2;    // A_end       [M] fp32
-    static constexpr int SET = B_AE + M * 4;
+    static constexpr int NPT = TB * (TB + 1) / 2;        // causal P^T tiles (tb, jb <= tb)
+    static constexpr int B_P = B_AE + M * 4;             // P^T hi, lo  [NPT][2][64 lanes] bf16 x4
+    static constexpr int SET = B_P + NPT * 2 * 64 * 8;
     static constexpr int BYTES = 2 * SET;
     static_assert(M % 16 == 0 && D % 16 == 0 && C0 % 16 == 0, "tile multiples");
 };
@@ -231,37 +234,58 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) split4(cur.h[tb], hh[tb], hl[tb]);
         const int64_t row0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;
+        // The causal tiles P^T (tb, jb <= tb) do not depend on the wave's
+        // columns: tile k = tb(tb+1)/2 + jb is formed once, by wave k % NW
+        // (masked, split), and shared through LDS in lane order; meanwhile
+        // every wave forms (Q.A) R for its columns.
+        // 16x16x16 products here: the same contractions as 16x16x32 on
+        // permuted operands gave wrong results on gfx950 in this kernel
+        // (correct once nops padded the MFMA sequence), so this path keeps
+        // the 16-deep form, which is exact to rounding.
+        short* pbuf = reinterpret_cast<short*>(buf + G::B_P);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int jb = 0; jb <= tb; ++jb) {
+                const int k = tb * (tb + 1) / 2 + jb;
+                if (k % G::NW == w) {
+                    f32x4 pj = {0.f, 0.f, 0.f, 0.f};  // lane (lg, lc): P^T[16jb + 4lg + r][16tb + lc]
+#pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        const int qo = (16 * tb + lc) * G::QA_LD + 16 * mt + 4 * lg;
+                        const int ko = (16 * jb + lc) * G::QA_LD + 16 * mt + 4 * lg;
+                        pj = mma3(ld4s(kah + ko), ld4s(kal + ko), ld4s(qah + qo), ld4s(qal + qo), pj);
+                    }
+                    if (jb == tb) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (4 * lg + r > lc) pj[r] = 0.f;  // causal: j <= t
+                    }
+                    s16x4 ph, pl;
+                    split4(pj, ph, pl);
+                    *reinterpret_cast<s16x4*>(pbuf + ((2 * k) * 64 + lane) * 4) = ph;
+                    *reinterpret_cast<s16x4*>(pbuf + ((2 * k + 1) * 64 + lane) * 4) = pl;
+                }
+            }
+        f32x4 yt[TB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-            f32x4 pt[TB];
-#pragma unroll
-            for (int jb = 0; jb <= tb; ++jb) pt[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            // 16x16x16 products here: the same contractions as 16x16x32 on
-            // permuted operands gave wrong results on gfx950 in this kernel
-            // (correct once nops padded the MFMA sequence), so this path keeps
-            // the 16-deep form, which is exact to rounding.
+            yt[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
                 const int qo = (16 * tb + lc) * G::QA_LD + 16 * mt + 4 * lg;
-                const s16x4 qh4 = ld4s(qah + qo), ql4 = ld4s(qal + qo);
-                y = mma3(qh4, ql4, rh[mt], rl[mt], y);
-#pragma unroll
-                for (int jb = 0; jb <= tb; ++jb) {
-                    const int ko = (16 * jb + lc) * G::QA_LD + 16 * mt + 4 * lg;
-                    pt[jb] = mma3(ld4s(kah + ko), ld4s(kal + ko), qh4, ql4, pt[jb]);
-                }
+                yt[tb] = mma3(ld4s(qah + qo), ld4s(qal + qo), rh[mt], rl[mt], yt[tb]);
             }
+        }
+        __syncthreads();  // P^T tiles visible
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            f32x4 y = yt[tb];
 #pragma unroll
             for (int jb = 0; jb <= tb; ++jb) {
-                f32x4 pj = pt[jb];  // lane (lg, lc): P^T[16jb + 4lg + r][16tb + lc]
-                if (jb == tb) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (4 * lg + r > lc) pj[r] = 0.f;  // causal: j <= t
-                }
-                s16x4 ph, pl;
-                split4(pj, ph, pl);
+                const int k = tb * (tb + 1) / 2 + jb;
+                const s16x4 ph = *reinterpret_cast<const s16x4*>(pbuf + ((2 * k) * 64 + lane) * 4);
+                const s16x4 pl = *reinterpret_cast<const s16x4*>(pbuf + ((2 * k + 1) * 64 + lane) * 4);
                 y = mma3(ph, pl, hh[jb], hl[jb], y);
             }
             // 4-byte stores: 16 lanes cover 64 contiguous bytes of a token row
