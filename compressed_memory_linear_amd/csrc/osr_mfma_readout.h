@@ -72,7 +72,8 @@ struct RdIn {
     uint16_t q[G::MPW][G::TB][4];               // q of those (token, slot) pairs, bf16
 };
 
-// All loads unconditional: slot tiles past the last one read the last tile.
+// Waves without a slot tile in the gate phase (more column tiles than slot
+// tiles) load only h.
 template <class G>
 __device__ __forceinline__ void rd_load(RdIn<G>& in, const Params& p, const Workspace& ws, int b, int hd, int t0,
                                         int tc0) {
@@ -82,7 +83,8 @@ __device__ __forceinline__ void rd_load(RdIn<G>& in, const Params& p, const Work
     const uint16_t* qg = static_cast<const uint16_t*>(p.q);
 #pragma unroll
     for (int mi = 0; mi < G::MPW; ++mi) {
-        const int mb = w + mi * G::NW < G::MT ? w + mi * G::NW : G::MT - 1;
+        const int mb = w + mi * G::NW;
+        if (mb >= G::MT) continue;  // wave-uniform
         const int slot = 16 * mb + lc;
 #pragma unroll
         for (int tb = 0; tb < G::TB; ++tb) {
