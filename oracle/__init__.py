@@ -25,6 +25,7 @@ _LIB = os.path.join(_HERE, "libosr_oracle.so")
 
 MODE_DEC = 0
 MODE_SIM = 1
+MODE_ENC = 2
 
 STATUS = {
     0: "ok",

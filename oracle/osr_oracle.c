@@ -21,22 +21,28 @@
  *
  *     h_t      = phi(S_{t'}) k_t - v_t   (decoding objective, e_t)
  *              = -v_t                    (similarity objective)
+ *              = v_t                     (encoding layer)
  *                                         (eq. OSR and the table of (h_t, c_t)
  *                                          in the general-form appendix)
  *     h~_t     = S_{t'}^T h_t            (per slot: s_{t',i} . h_t)
- *     |ds_i|^2 = (gamma_i k_i)^2 (|h_t|^2 - h~_{t,i}^2), clamped at 0
+ *     c_{t,i}  = k_{t,i}                 (decoding, similarity)
+ *              = h~_{t,i} - k_{t,i}      (encoding layer: the per-slot error
+ *                                         e_t = phi(S)^T v_t - k_t of
+ *                                         eq. encoding_stateNorm_loss, the
+ *                                         coefficient of eq. encoding_recurrence)
+ *     |ds_i|^2 = (gamma_i c_i)^2 (|h_t|^2 - h~_{t,i}^2), clamped at 0
  *                                         (norm of the orthogonal update,
  *                                          appendix paragraph "Computing beta")
  *     beta_i   = (mu_t^2 + |ds_i|^2)^(-1/2)
  *                                         (eq. normalized_recurrence with the
  *                                          forget gate of eq. dacay_recurrence)
- *     k^_t     = gamma_t (.) beta_t (.) k_t          (eq. recurrence_detailed)
+ *     k^_t     = gamma_t (.) beta_t (.) c_t          (eq. recurrence_detailed)
  *     G^_t     = mu_t beta_t + h~_t (.) k^_t         (eq. recurrence_linear2)
  *     s_{t,i}  = G^_{t,i} s_{t-1,i} - k^_{t,i} h_t   (eq. recurrence_linear2)
  *     y_t      = S_t q_t = sum_i q_{t,i} s_{t,i}     (memory read-out)
  *
  *   With C = 1 the chunk-start state is the current state, so each step is the
- *   exact normalised OSR step s_i <- (mu s_i - gamma_i k_i P(s_i) h)/|...|.
+ *   exact normalised OSR step s_i <- (mu s_i - gamma_i c_i P(s_i) h)/|...|.
  *   The returned state is projected onto the unit sphere once more.
  *
  * Readings where the pages are silent or disagree (each is listed in the
@@ -64,11 +70,12 @@
 
 #define ORACLE_MODE_DEC 0
 #define ORACLE_MODE_SIM 1
+#define ORACLE_MODE_ENC 2
 
 typedef struct {
     int32_t B, T, H, m, d;
     int32_t gamma_per_slot; /* 1: gamma is [B,T,H,m]; 0: gamma is [B,T,H] */
-    int32_t mode;           /* ORACLE_MODE_DEC or ORACLE_MODE_SIM */
+    int32_t mode;           /* ORACLE_MODE_DEC, ORACLE_MODE_SIM or ORACLE_MODE_ENC */
     int32_t chunk_size;     /* C >= 1, T % C == 0 */
 } oracle_osr_problem;
 
@@ -120,12 +127,12 @@ static int run_sequence(const oracle_job* job, int b, int hd, double* work) {
             const double mu = job->mu[bth];
             double* yt = job->y + bth * d;
 
-            /* h_t: the decoding error phi(S_t') k_t - v_t, or -v_t. */
+            /* h_t: the decoding error phi(S_t') k_t - v_t, -v_t, or v_t. */
             for (int j = 0; j < d; ++j) {
                 double acc = 0.0;
                 if (p->mode == ORACLE_MODE_DEC)
                     for (int i = 0; i < m; ++i) acc += kt[i] * Z[(size_t)i * d + j];
-                h[j] = acc - vt[j];
+                h[j] = p->mode == ORACLE_MODE_ENC ? vt[j] : acc - vt[j];
             }
             double hsq = 0.0;
             for (int j = 0; j < d; ++j) hsq += h[j] * h[j];
@@ -135,11 +142,13 @@ static int run_sequence(const oracle_job* job, int b, int hd, double* work) {
                 for (int j = 0; j < d; ++j) dot += Z[(size_t)i * d + j] * h[j];
                 htil[i] = dot;
                 const double g = p->gamma_per_slot ? gt[i] : gt[0];
-                const double wi = g * kt[i];                 /* writing intensity */
+                /* coefficient c_i: k_i, or the encoding error s_i . v - k_i */
+                const double ci = p->mode == ORACLE_MODE_ENC ? dot - kt[i] : kt[i];
+                const double wi = g * ci;                    /* writing intensity */
                 double dsq = wi * wi * (hsq - dot * dot);    /* |ds_i|^2 */
                 if (dsq < 0.0) dsq = 0.0;
                 const double beta = 1.0 / sqrt(mu * mu + dsq);
-                khat[i] = g * beta * kt[i];
+                khat[i] = g * beta * ci;
                 Ghat[i] = mu * beta + htil[i] * khat[i];
             }
 
@@ -209,7 +218,8 @@ int oracle_osr_forward(const oracle_osr_problem* p, const double* q, const doubl
     if (!p || !q || !k || !v || !gamma || !mu || !state_in || !state_out || !y)
         return ORACLE_ERR_NULL;
     if (p->B <= 0 || p->T <= 0 || p->H <= 0 || p->m <= 0 || p->d <= 0 || p->chunk_size <= 0 ||
-        p->T % p->chunk_size != 0 || (p->mode != ORACLE_MODE_DEC && p->mode != ORACLE_MODE_SIM))
+        p->T % p->chunk_size != 0 ||
+        (p->mode != ORACLE_MODE_DEC && p->mode != ORACLE_MODE_SIM && p->mode != ORACLE_MODE_ENC))
         return ORACLE_ERR_SHAPE;
 
     oracle_job job;
