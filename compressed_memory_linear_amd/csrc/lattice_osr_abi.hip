@@ -32,7 +32,8 @@ int check_desc(const lattice_osr_desc* d) {
     if (!pow2_dim(d->m) || !pow2_dim(d->d)) return LATTICE_OSR_ERR_UNSUPPORTED;
     if (d->in_dtype != LATTICE_OSR_F32 && d->in_dtype != LATTICE_OSR_BF16) return LATTICE_OSR_ERR_UNSUPPORTED;
     if (d->y_dtype != LATTICE_OSR_F32 && d->y_dtype != LATTICE_OSR_BF16) return LATTICE_OSR_ERR_UNSUPPORTED;
-    if (d->mode != LATTICE_OSR_MODE_DEC && d->mode != LATTICE_OSR_MODE_SIM) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->mode != LATTICE_OSR_MODE_DEC && d->mode != LATTICE_OSR_MODE_SIM && d->mode != LATTICE_OSR_MODE_ENC)
+        return LATTICE_OSR_ERR_UNSUPPORTED;
     if (d->gamma_per_slot != 0 && d->gamma_per_slot != 1) return LATTICE_OSR_ERR_UNSUPPORTED;
     return LATTICE_OSR_OK;
 }

@@ -24,7 +24,7 @@ struct Params {
     int B, T, H;
     int chunk;         // C
     int gamma_per_slot;
-    int mode;          // 0 = decoding objective, 1 = similarity objective
+    int mode;          // 0 = decoding objective, 1 = similarity objective, 2 = encoding layer
     int y_bf16;        // 1: y is bf16, 0: y is fp32
 };
 

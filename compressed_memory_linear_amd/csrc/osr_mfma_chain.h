@@ -134,7 +134,9 @@ __device__ __forceinline__ float row_inv_norm(const f32x4 (&acc)[DB]) {
 // Each wave of a pair forms its U_g and t_g, the pair swaps them through
 // LDS, and both form R_end (and its projection) identically.  This doubles
 // the waves per SIMD (latency hiding) at one extra barrier per chunk.
-template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR>
+// ENC: the encoding layer (h = v, writing coefficient c - k), a separate
+// instantiation so that the other objectives carry none of its selects.
+template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR, bool ENC>
 __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Params p) {
     using G = ChainCfg<M, D, C0, PAIR>;
     static_assert(!PAIR || ONE, "the pair split covers one sub-block per chunk");
@@ -221,15 +223,17 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // accumulators), then the epilogue.
         if (g1_active) {
             constexpr int TPW = G::TPW, DPW = G::DPW;
-            // Accumulators start at -V: rows of V read 8 bytes at a time and
-            // brought into the accumulator layout by the negated identity.
+            // Accumulators start at -V (+V for the encoding layer, whose h is
+            // v): rows of V read 8 bytes at a time and brought into the
+            // accumulator layout by the (negated) identity.
+            const s16x4 v_eye = ENC ? eye : neg_eye;
             f32x4 ha[TPW][DPW];
 #pragma unroll
             for (int ti = 0; ti < TPW; ++ti)
 #pragma unroll
                 for (int dj = 0; dj < DPW; ++dj) {
                     const int tb = g1_tb0 + G::TG * ti, dc0 = 16 * (g1_grp + G::WSE * dj);
-                    ha[ti][dj] = tr16f(ld4s(vs + (16 * tb + lc) * G::VS_LD + dc0 + 4 * lg), neg_eye);
+                    ha[ti][dj] = tr16f(ld4s(vs + (16 * tb + lc) * G::VS_LD + dc0 + 4 * lg), v_eye);
                 }
             if (p.mode == 0) {
                 if constexpr (G::K32_M) {
@@ -328,6 +332,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // ---- c = H Z^T for this wave's slots and its group's tokens; gates --
         // Gate inputs are read before the products.  Tile i of the group is
         // token tile tbg + i of the sub-block.
+        constexpr bool enc = ENC;
         float hh[TBW][4], av[TBW][4], muv[TBW][4];
 #pragma unroll
         for (int i = 0; i < TBW; ++i) {
@@ -363,7 +368,9 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
             const f32x4 g4 = tr16f(ld4s(gs + (16 * tb + lc) * G::GS_LD + 16 * wv + 4 * lg), eye);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                av[i][r] = g4[r] * k4[r];
+                // the encoding layer writes with gamma (c - k): keep -gamma k
+                // here and add gamma c once c is known
+                av[i][r] = enc ? -g4[r] * k4[r] : g4[r] * k4[r];
                 muv[i][r] = mu4[r];
             }
         }
@@ -399,9 +406,12 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
 #pragma unroll
         for (int i = 0; i < TBW; ++i) {
             float prod = 1.f;
+            f32x4 g4 = {0.f, 0.f, 0.f, 0.f};  // gamma of the tile, read again for the encoding layer only
+            if (enc) g4 = tr16f(ld4s(gs + (16 * (tbg + i) + lc) * G::GS_LD + 16 * wv + 4 * lg), eye);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float a = av[i][r], mu = muv[i][r], cr = cc[i][r];
+                const float mu = muv[i][r], cr = cc[i][r];
+                const float a = enc ? fmaf(g4[r], cr, av[i][r]) : av[i][r];
                 const float wvv = fmaxf(fmaf(-cr, cr, hh[i][r]), 0.f);
                 const float beta = __builtin_amdgcn_rsqf(fmaf(mu, mu, a * a * wvv));
                 gt[i][r] = beta * fmaf(a, cr, mu);

@@ -454,8 +454,9 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
                 }
             }
         }
+        const float vsign = p.mode == 2 ? 1.f : -1.f;  // h = v for the encoding layer
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] -= bf16_val(vs[(16 * tb + 4 * lg + r) * G::VS_LD + dcol]);
+        for (int r = 0; r < 4; ++r) a[r] = fmaf(vsign, bf16_val(vs[(16 * tb + 4 * lg + r) * G::VS_LD + dcol]), a[r]);
         accH[tb] = a;
         split4(a, hfh[tb], hfl[tb]);
         if constexpr (G::K32_C) {
@@ -521,7 +522,8 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
                     for (int ww = 0; ww < G::NW; ++ww) hh += hp[ww * C0 + tau];
                     const float k = bf16_val(ks[tau * G::KS_LD + i]);
                     const float mu = mus[tau];
-                    const float a = bf16_val(gs[tau * G::GS_LD + i]) * k;
+                    // writing coefficient: k, or the encoding error c - k
+                    const float a = bf16_val(gs[tau * G::GS_LD + i]) * (p.mode == 2 ? c[r] - k : k);
                     const float wv = fmaxf(fmaf(-c[r], c[r], hh), 0.f);
                     const float beta = __builtin_amdgcn_rsqf(fmaf(mu, mu, a * a * wv));
                     gt[tb][r] = beta * fmaf(a, c[r], mu);

@@ -6,8 +6,10 @@
 // 2504.05646).  Per token, with Z the unit-projected chunk-start state
 // (section "Stabilizing Memory Updates via Normalization") and S the running
 // state, both m x d with row i = slot i:
-//   h   = sum_i k_i z_i - v  (decoding objective)  or  -v  (similarity)
-//   c_i = z_i . h,  a_i = gamma_i k_i,  w_i = max(|h|^2 - c_i^2, 0)
+//   h   = sum_i k_i z_i - v  (decoding objective), -v (similarity) or v
+//         (encoding layer, subsection "Encoding layer")
+//   c_i = z_i . h,  a_i = gamma_i k_i (gamma_i (c_i - k_i) for the encoding
+//         layer: its per-slot error z_i . v - k_i),  w_i = max(|h|^2 - c_i^2, 0)
 //   beta_i = (mu^2 + a_i^2 w_i)^(-1/2)            (eq. normalized_recurrence
 //                                                  with the forget gate)
 //   s_i <- beta_i (mu + a_i c_i) s_i - beta_i a_i h   (eq. recurrence_detailed;
@@ -111,6 +113,8 @@ __device__ __forceinline__ float4 osr_token(const float4 (&z)[L::RPT], float4 (&
 #pragma unroll
         for (int i = 0; i < L::RPT; ++i) hp = fma4(in.k[i], z[i], hp);
         h = col_sum<L, D>(hp, red_h, lane, wave, cg) - in.v;
+    } else if (mode == 2) {
+        h = in.v;
     } else {
         h = f4(0.f) - in.v;
     }
@@ -125,7 +129,7 @@ __device__ __forceinline__ float4 osr_token(const float4 (&z)[L::RPT], float4 (&
     float4 yp = f4(0.f);
 #pragma unroll
     for (int i = 0; i < L::RPT; ++i) {
-        const float a = in.g[i] * in.k[i];
+        const float a = in.g[i] * (mode == 2 ? cc[i] - in.k[i] : in.k[i]);
         const float w = fmaxf(fmaf(-cc[i], cc[i], hh), 0.f);
         const float beta = rsqrtf(fmaf(mu, mu, a * a * w));
         const float gate = beta * fmaf(a, cc[i], mu);

@@ -18,7 +18,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblattice_osr.so")
 
 F32, BF16 = 0, 1
-MODE_DEC, MODE_SIM = 0, 1
+MODE_DEC, MODE_SIM, MODE_ENC = 0, 1, 2
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_ALIGN = -1, -2, -3, -4, -5, -6, -7

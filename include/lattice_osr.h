@@ -72,6 +72,10 @@ extern "C" {
 /* Objective that defines h_t. */
 #define LATTICE_OSR_MODE_DEC 0 /* decoding (l2 reconstruction): h = phi(S)k - v */
 #define LATTICE_OSR_MODE_SIM 1 /* dot-product similarity:       h = -v        */
+#define LATTICE_OSR_MODE_ENC 2 /* encoding layer: h = v, and each slot writes with the
+                                  error of its encoding, e_i = (s_i . v)/|s_i| - k_i,
+                                  in place of k_i ("Encoding layer" subsection,
+                                  eq. encoding_stateNorm_loss / encoding_recurrence) */
 
 /* Status codes. */
 #define LATTICE_OSR_OK 0
@@ -92,7 +96,7 @@ typedef struct {
     int32_t gamma_per_slot; /* 1: gamma is [B,T,H,m]; 0: gamma is [B,T,H]        */
     int32_t in_dtype;       /* LATTICE_OSR_F32 or LATTICE_OSR_BF16               */
     int32_t y_dtype;        /* LATTICE_OSR_F32 or LATTICE_OSR_BF16               */
-    int32_t mode;           /* LATTICE_OSR_MODE_DEC or LATTICE_OSR_MODE_SIM      */
+    int32_t mode;           /* LATTICE_OSR_MODE_DEC, _SIM or _ENC                */
 } lattice_osr_desc;
 
 /*

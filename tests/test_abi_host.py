@@ -74,7 +74,7 @@ def test_null_pointers(fn):
     ("B", 0, osr.ERR_SHAPE), ("T", 0, osr.ERR_SHAPE), ("H", -1, osr.ERR_SHAPE),
     ("m", 0, osr.ERR_SHAPE), ("m", 48, osr.ERR_UNSUPPORTED), ("d", 256, osr.ERR_UNSUPPORTED),
     ("in_dtype", 2, osr.ERR_UNSUPPORTED), ("y_dtype", 7, osr.ERR_UNSUPPORTED),
-    ("mode", 2, osr.ERR_UNSUPPORTED), ("gamma_per_slot", 2, osr.ERR_UNSUPPORTED),
+    ("mode", 3, osr.ERR_UNSUPPORTED), ("mode", -1, osr.ERR_UNSUPPORTED), ("gamma_per_slot", 2, osr.ERR_UNSUPPORTED),
 ])
 def test_bad_descriptor(field, value, status):
     d = osr.make_desc(2, 8, 2, 32, 32)

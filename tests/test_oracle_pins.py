@@ -106,6 +106,32 @@ def test_autograd_pin_detects_encoding_mistakes():
     np.testing.assert_allclose(y[0, :, 0], yr, rtol=0, atol=1e-11)
 
 
+def test_conditioning_encoding_amplifies_decoding_damps():
+    """How the recurrences carry a small change of the initial state (fp64
+    oracle, chunk 16, 512 tokens, workload-like inputs): the decoding and
+    similarity recurrences damp it, the encoding layer, whose writing
+    intensity depends on the state, amplifies it (here ~35x within 512
+    tokens; ~1e4x over the 2048-token workload).  This is why the GPU parity of the encoding layer is
+    checked over short sequences."""
+    q, k, v, g, mu, S0 = _rand_problem(31, B=2, T=512, H=2, m=32, d=32)
+    rng = np.random.default_rng(1)
+    S1 = S0 * (1.0 + 1e-9 * rng.standard_normal(S0.shape))
+    growth = {}
+    for mode in (DEC, SIM, ENC):
+        ya, _ = oracle.osr_forward(q, k, v, g, mu, S0, chunk_size=16, mode=mode)
+        yb, _ = oracle.osr_forward(q, k, v, g, mu, S1, chunk_size=16, mode=mode)
+        rms = np.sqrt(np.mean(ya ** 2))
+        first = np.max(np.abs(yb[:, :16] - ya[:, :16])) / rms
+        peak = np.max(np.abs(yb - ya)) / rms
+        last = np.max(np.abs(yb[:, -64:] - ya[:, -64:])) / rms
+        growth[mode] = (first, peak, last)
+    for mode in (DEC, SIM):
+        first, peak, last = growth[mode]
+        assert last < 1e-3 * first, (mode, growth[mode])
+    first, peak, _ = growth[ENC]
+    assert peak > 10 * first, growth[ENC]
+
+
 @pytest.mark.parametrize("C", [1, 4, 16])
 def test_enc_no_write_when_k_is_the_encoding_of_v(C):
     """Encoding layer: if every k_t equals phi(S_0)^T v_t the loss is zero, the
