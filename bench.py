@@ -87,10 +87,10 @@ class Case:
     sets, so a working set larger than the 256 MB Infinity Cache is read from
     HBM rather than from the cache."""
 
-    def __init__(self, name: str, entry: str, chunk: int, y_dtype=None, copies: int = 1):
+    def __init__(self, name: str, entry: str, chunk: int, y_dtype=None, copies: int = 1, mode: int = 0):
         import torch
         from compressed_memory_linear_amd import osr, synth
-        self.name, self.entry, self.chunk = name, entry, chunk
+        self.name, self.entry, self.chunk, self.mode = name, entry, chunk, mode
         self.w = dict(synth.WORKLOADS[name])
         inp = synth.workload_inputs(name)
         self.inp = inp
@@ -103,7 +103,7 @@ class Case:
         self.ws = None
         if entry == "chunked":
             desc = osr.make_desc(inp.B, inp.T, inp.H, inp.m, inp.d, 1,
-                                 osr.BF16 if inp.in_dtype == "bf16" else osr.F32, osr.F32)
+                                 osr.BF16 if inp.in_dtype == "bf16" else osr.F32, osr.F32, mode)
             need = osr.lattice_osr_workspace_bytes(desc, chunk)
             if need:
                 self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
@@ -114,13 +114,14 @@ class Case:
         self.i += 1
         args = (t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"])
         if self.entry == "chunked":
-            osr.lattice_osr_fwd_chunked(*args, self.chunk, y_dtype=self.y_dtype, state_out=self.state_out,
-                                        y=self.y, workspace=self.ws)
+            osr.lattice_osr_fwd_chunked(*args, self.chunk, mode=self.mode, y_dtype=self.y_dtype,
+                                        state_out=self.state_out, y=self.y, workspace=self.ws)
         elif self.entry == "recurrent":
-            osr.lattice_osr_fwd_recurrent(*args, y_dtype=self.y_dtype, state_out=self.state_out, y=self.y)
+            osr.lattice_osr_fwd_recurrent(*args, mode=self.mode, y_dtype=self.y_dtype, state_out=self.state_out,
+                                          y=self.y)
         else:
             # decode keeps stepping the same state in place, as a decoder would
-            osr.lattice_osr_decode_step(*args, y_dtype=self.y_dtype, state_out=t["state"], y=self.y)
+            osr.lattice_osr_decode_step(*args, mode=self.mode, y_dtype=self.y_dtype, state_out=t["state"], y=self.y)
 
     @property
     def head_tokens(self) -> int:
@@ -260,14 +261,16 @@ def main() -> int:
 
     if not args.no_secondary:
         sec = []
-        for name, entry, chunk, steps in (("decode_s256h32_m128d128", "decode", 1, 50),
-                                          ("chunked_b8h16_t4096_m64d128_c64", "chunked", 64, 3),
-                                          ("chunked_b1h16_t65536_m128d128_c128", "chunked", 128, 2),
-                                          (HEADLINE, "recurrent", 1, 2)):
-            c = Case(name, entry, chunk)
+        for name, entry, chunk, steps, mode in (("decode_s256h32_m128d128", "decode", 1, 50, 0),
+                                                ("chunked_b8h16_t4096_m64d128_c64", "chunked", 64, 3, 0),
+                                                ("chunked_b1h16_t65536_m128d128_c128", "chunked", 128, 2, 0),
+                                                (HEADLINE, "recurrent", 1, 2, 0),
+                                                (HEADLINE, "chunked", 64, 10, 2)):
+            c = Case(name, entry, chunk, copies=8 if name == HEADLINE and entry == "chunked" else 1, mode=mode)
             t_ms = time_case(c, steps, 1)
             ab = algorithmic_bytes(c.w)
-            sec.append({"workload": name, "entry": entry, "chunk": chunk, "ms_per_step": t_ms,
+            sec.append({"workload": name, "entry": entry, "chunk": chunk,
+                        "objective": {0: "decoding", 1: "similarity", 2: "encoding"}[mode], "ms_per_step": t_ms,
                         "head_tokens_per_s": c.head_tokens / (t_ms * 1e-3),
                         "hbm_gbs_algorithmic": ab / (t_ms * 1e-3) / 1e9,
                         "hbm_frac": ab / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
