@@ -13,6 +13,9 @@
  * read-out y_t = S_t q_t of the updated state (general form of the layer).
  *   decoding objective:   h_t = phi(S) k_t - v_t   (eq. decoding_recurrence)
  *   similarity objective: h_t = -v_t               (eq. similarity_recurrence)
+ *   encoding layer:       h_t = v_t, each slot writing with its encoding error
+ *                         phi(S)^T v_t - k_t in place of k_t
+ *                         (subsection "Encoding layer", eq. encoding_recurrence)
  * Chunked evaluation takes the update's projections at the chunk-start state
  * (section "Parallel and Hardware Efficient Form", eq. recurrence_linear2);
  * with chunk size 1 it is the exact recurrence.
