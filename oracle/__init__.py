@@ -27,6 +27,9 @@ MODE_DEC = 0
 MODE_SIM = 1
 MODE_ENC = 2
 
+LIN2 = 0  # eq. recurrence_linear2 (default)
+LIN1 = 1  # eq. recurrence_linear1
+
 STATUS = {
     0: "ok",
     -1: "null pointer",
@@ -46,6 +49,7 @@ class _Problem(ctypes.Structure):
         ("gamma_per_slot", ctypes.c_int32),
         ("mode", ctypes.c_int32),
         ("chunk_size", ctypes.c_int32),
+        ("linearisation", ctypes.c_int32),
     ]
 
 
@@ -91,7 +95,7 @@ def _ptr(a: np.ndarray):
 
 
 def osr_forward(q, k, v, gamma, mu, state, chunk_size: int = 1, mode: int = MODE_DEC,
-                nthreads: int = 0, return_threads: bool = False):
+                nthreads: int = 0, return_threads: bool = False, linearisation: int = LIN2):
     """Run OSR-C over a whole batch in float64.
 
     q, k: [B,T,H,m]; v: [B,T,H,d]; gamma: [B,T,H,m] or [B,T,H]; mu: [B,T,H];
@@ -109,7 +113,7 @@ def osr_forward(q, k, v, gamma, mu, state, chunk_size: int = 1, mode: int = MODE
         per_slot = 0
     else:
         raise ValueError("oracle: gamma must be [B,T,H,m] or [B,T,H]")
-    prob = _Problem(B, T, H, m, d, per_slot, int(mode), int(chunk_size))
+    prob = _Problem(B, T, H, m, d, per_slot, int(mode), int(chunk_size), int(linearisation))
     y = np.zeros((B, T, H, d), dtype=np.float64)
     out = np.zeros((B, H, m, d), dtype=np.float64)
     used = ctypes.c_int(0)

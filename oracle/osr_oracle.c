@@ -43,6 +43,13 @@
  *
  *   With C = 1 the chunk-start state is the current state, so each step is the
  *   exact normalised OSR step s_i <- (mu s_i - gamma_i c_i P(s_i) h)/|...|.
+ *
+ *   The pages derive two chunk linearisations.  The one above (the default,
+ *   eq. recurrence_linear2) puts the projection term on the running slot.
+ *   The first one (eq. recurrence_linear1) keeps only mu beta on the running
+ *   slot and takes the projection term at the chunk-start slot z_i:
+ *     s_{t,i}  = mu_t beta_i s_{t-1,i} + h~_{t,i} k^_{t,i} z_i - k^_{t,i} h_t
+ *   (the same step when C = 1).
  *   The returned state is projected onto the unit sphere once more.
  *
  * Readings where the pages are silent or disagree (each is listed in the
@@ -72,11 +79,15 @@
 #define ORACLE_MODE_SIM 1
 #define ORACLE_MODE_ENC 2
 
+#define ORACLE_LIN2 0 /* eq. recurrence_linear2 (default) */
+#define ORACLE_LIN1 1 /* eq. recurrence_linear1 */
+
 typedef struct {
     int32_t B, T, H, m, d;
     int32_t gamma_per_slot; /* 1: gamma is [B,T,H,m]; 0: gamma is [B,T,H] */
     int32_t mode;           /* ORACLE_MODE_DEC, ORACLE_MODE_SIM or ORACLE_MODE_ENC */
     int32_t chunk_size;     /* C >= 1, T % C == 0 */
+    int32_t linearisation;  /* ORACLE_LIN2 or ORACLE_LIN1 */
 } oracle_osr_problem;
 
 typedef struct {
@@ -149,12 +160,22 @@ static int run_sequence(const oracle_job* job, int b, int hd, double* work) {
                 if (dsq < 0.0) dsq = 0.0;
                 const double beta = 1.0 / sqrt(mu * mu + dsq);
                 khat[i] = g * beta * ci;
-                Ghat[i] = mu * beta + htil[i] * khat[i];
+                /* gate on the running slot: mu beta (eq. recurrence_linear1), or
+                   mu beta plus the projection term (eq. recurrence_linear2) */
+                Ghat[i] = p->linearisation == ORACLE_LIN1 ? mu * beta : mu * beta + htil[i] * khat[i];
             }
 
-            for (int i = 0; i < m; ++i)
-                for (int j = 0; j < d; ++j)
-                    S[(size_t)i * d + j] = Ghat[i] * S[(size_t)i * d + j] - khat[i] * h[j];
+            if (p->linearisation == ORACLE_LIN1) {
+                /* the projection term is taken at the chunk-start slot z_i */
+                for (int i = 0; i < m; ++i)
+                    for (int j = 0; j < d; ++j)
+                        S[(size_t)i * d + j] = Ghat[i] * S[(size_t)i * d + j] + htil[i] * khat[i] * Z[(size_t)i * d + j]
+                                               - khat[i] * h[j];
+            } else {
+                for (int i = 0; i < m; ++i)
+                    for (int j = 0; j < d; ++j)
+                        S[(size_t)i * d + j] = Ghat[i] * S[(size_t)i * d + j] - khat[i] * h[j];
+            }
 
             for (int j = 0; j < d; ++j) {
                 double acc = 0.0;
@@ -219,7 +240,8 @@ int oracle_osr_forward(const oracle_osr_problem* p, const double* q, const doubl
         return ORACLE_ERR_NULL;
     if (p->B <= 0 || p->T <= 0 || p->H <= 0 || p->m <= 0 || p->d <= 0 || p->chunk_size <= 0 ||
         p->T % p->chunk_size != 0 ||
-        (p->mode != ORACLE_MODE_DEC && p->mode != ORACLE_MODE_SIM && p->mode != ORACLE_MODE_ENC))
+        (p->mode != ORACLE_MODE_DEC && p->mode != ORACLE_MODE_SIM && p->mode != ORACLE_MODE_ENC) ||
+        (p->linearisation != ORACLE_LIN2 && p->linearisation != ORACLE_LIN1))
         return ORACLE_ERR_SHAPE;
 
     oracle_job job;

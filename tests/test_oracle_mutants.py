@@ -27,8 +27,14 @@ MUTANTS = [
      "const double beta = 1.0 / sqrt(mu * mu + dsq);",
      "const double beta = 1.0 / sqrt(1.0 + dsq);"),
     ("gate without the projection coefficient",
-     "Ghat[i] = mu * beta + htil[i] * khat[i];",
-     "Ghat[i] = mu * beta;"),
+     "? mu * beta : mu * beta + htil[i] * khat[i];",
+     "? mu * beta : mu * beta;"),
+    ("first linearisation: projection term on the running slot",
+     "+ htil[i] * khat[i] * Z[(size_t)i * d + j]",
+     "+ htil[i] * khat[i] * S[(size_t)i * d + j]"),
+    ("first linearisation: projection term dropped",
+     "+ htil[i] * khat[i] * Z[(size_t)i * d + j]",
+     "+ 0.0 * Z[(size_t)i * d + j]"),
     ("decoding error from the running state instead of the chunk-start state",
      "acc += kt[i] * Z[(size_t)i * d + j];",
      "acc += kt[i] * S[(size_t)i * d + j];"),

@@ -11,7 +11,9 @@ checked against:
 * a brute-force chunk-parallel evaluator (GLA form of eq. recurrence_linear2,
   with the update norms taken from the materialised update matrices of the
   appendix paragraph "Computing beta"), which must agree with the oracle's
-  token loop to 1e-10;
+  token loop to 1e-10; likewise the chunk-level form of the first
+  linearisation (eq. chunkwise_OSR, with the tensors Omega, f, F and P built
+  explicitly);
 * closed forms (rotation on the circle), invariants (unit slots, update
   orthogonal to its slot, slot-permutation equivariance, (b,h) independence,
   chunk-aligned resume) and degenerate cases (no write when gamma or k is 0;
@@ -260,6 +262,84 @@ def test_chunk_parallel_form_matches_token_loop(mode, C, per_slot):
     scale = np.sqrt(np.mean(yr ** 2))
     assert np.max(np.abs(y[0, :, 0] - yr)) <= 1e-10 * scale
     assert np.max(np.abs(Sout[0, 0] - Sr)) <= 1e-10
+
+
+def _chunk_level_reference_lin1(q, k, v, gamma, mu, S0, C, mode):
+    """The first linearisation at chunk level (eq. chunkwise_OSR, rows of S =
+    slots): with a_tau = prod of mu beta over the chunk so far, the segmented
+    products Omega[j, i] = a_j / a_i (i <= j), f and F built from them by
+    explicit sums over Omega, and P[t, j] = sum_n Q[t,n] K^[j,n] Omega[t,j,n],
+      S_end = (a_C + f) (.) Z - sum_tau K^_tau Omega[C, tau] h_tau,
+      Y     = (Q (.) (a + F)) Z - P H."""
+    T, m = q.shape
+    gam = gamma if gamma.ndim == 2 else np.repeat(gamma[:, None], m, axis=1)
+    S = S0 / np.linalg.norm(S0, axis=1, keepdims=True)
+    Y = np.zeros((T, v.shape[1]))
+    for b0 in range(0, T, C):
+        sl = slice(b0, b0 + C)
+        Z = S / np.linalg.norm(S, axis=1, keepdims=True)
+        K, Q, V, G, M = k[sl], q[sl], v[sl], gam[sl], mu[sl]
+        Hm = (K @ Z - V) if mode == DEC else (V if mode == ENC else -V)
+        Ht = Hm @ Z.T
+        W = G * ((Ht - K) if mode == ENC else K)
+        dsq = np.zeros_like(Ht)
+        for tau in range(C):
+            DS = (Ht[tau] * W[tau])[:, None] * Z - W[tau][:, None] * Hm[tau][None, :]
+            dsq[tau] = np.sum(DS * DS, axis=1)
+        beta = 1.0 / np.sqrt(M[:, None] ** 2 + dsq)
+        khat = W * beta
+        a = np.cumprod(M[:, None] * beta, axis=0)        # C x m
+        Om = np.zeros((C, C, m))
+        for j in range(C):
+            for i in range(j + 1):
+                Om[j, i] = a[j] / a[i]
+        hk = Ht * khat
+        F = np.einsum("jim,im->jm", Om, hk)              # F[t] = sum_{tau<=t} Omega[t,tau] (h~ k^)_tau
+        f = F[-1]
+        P = np.einsum("tn,jn,tjn->tj", Q, khat, Om)
+        Y[sl] = (Q * (a + F)) @ Z - P @ Hm
+        S = (a[-1] + f)[:, None] * Z - (khat * Om[-1]).T @ Hm
+    S = S / np.linalg.norm(S, axis=1, keepdims=True)
+    return Y, S
+
+
+@pytest.mark.parametrize("mode", [DEC, SIM, ENC])
+@pytest.mark.parametrize("C", [2, 4, 8, 32])
+@pytest.mark.parametrize("per_slot", [True, False])
+def test_lin1_chunk_level_form_matches_token_loop(mode, C, per_slot):
+    T = 32
+    q, k, v, g, mu, S0 = _rand_problem(300 + C, T=T, m=6, d=5, per_slot=per_slot)
+    y, Sout = oracle.osr_forward(q, k, v, g, mu, S0, chunk_size=C, mode=mode, linearisation=oracle.LIN1)
+    yr, Sr = _chunk_level_reference_lin1(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0],
+                                         mu[0, :, 0], S0[0, 0], C, mode)
+    scale = np.sqrt(np.mean(yr ** 2))
+    assert np.max(np.abs(y[0, :, 0] - yr)) <= 1e-10 * scale
+    assert np.max(np.abs(Sout[0, 0] - Sr)) <= 1e-10
+
+
+@pytest.mark.parametrize("mode", [DEC, SIM, ENC])
+def test_lin1_exact_at_c1_and_distinct_from_lin2(mode):
+    """At C = 1 both linearisations are the exact step (autograd pin); with
+    C > 1 they differ (the projection term rides on the chunk-start slot)."""
+    q, k, v, g, mu, S0 = _rand_problem(41, T=24, m=6, d=9)
+    y1, S1 = oracle.osr_forward(q, k, v, g, mu, S0, chunk_size=1, mode=mode, linearisation=oracle.LIN1)
+    yr, Sr, _ = _exact_sequence_autograd(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0],
+                                         mu[0, :, 0], S0[0, 0], mode)
+    np.testing.assert_allclose(y1[0, :, 0], yr, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(S1[0, 0], Sr, rtol=0, atol=1e-12)
+    ya, _ = oracle.osr_forward(q, k, v, g, mu, S0, chunk_size=8, mode=mode, linearisation=oracle.LIN1)
+    yb, _ = oracle.osr_forward(q, k, v, g, mu, S0, chunk_size=8, mode=mode, linearisation=oracle.LIN2)
+    assert np.max(np.abs(ya - yb)) > 1e-6 * np.sqrt(np.mean(yb ** 2))
+
+
+def test_lin1_resume_at_chunk_boundary():
+    q, k, v, g, mu, S0 = _rand_problem(42, B=2, T=32, H=2, m=5, d=6)
+    kw = dict(chunk_size=8, mode=DEC, linearisation=oracle.LIN1)
+    y, Sout = oracle.osr_forward(q, k, v, g, mu, S0, **kw)
+    y1, S1 = oracle.osr_forward(q[:, :16], k[:, :16], v[:, :16], g[:, :16], mu[:, :16], S0, **kw)
+    y2, S2 = oracle.osr_forward(q[:, 16:], k[:, 16:], v[:, 16:], g[:, 16:], mu[:, 16:], S1, **kw)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), y, atol=1e-13)
+    np.testing.assert_allclose(S2, Sout, atol=1e-14)
 
 
 def test_first_token_of_each_chunk_is_exact_step():
