@@ -35,14 +35,17 @@ int check_desc(const lattice_osr_desc* d) {
     if (d->mode != LATTICE_OSR_MODE_DEC && d->mode != LATTICE_OSR_MODE_SIM && d->mode != LATTICE_OSR_MODE_ENC)
         return LATTICE_OSR_ERR_UNSUPPORTED;
     if (d->gamma_per_slot != 0 && d->gamma_per_slot != 1) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->linearisation != LATTICE_OSR_LIN2 && d->linearisation != LATTICE_OSR_LIN1) return LATTICE_OSR_ERR_UNSUPPORTED;
     return LATTICE_OSR_OK;
 }
 
 // Which implementation runs a chunked call.
 enum class Path { TokenLoop, Mfma };
 
+// The first linearisation runs on the token-loop kernel only.
 Path chunk_path(const lattice_osr_desc* d, int C) {
-    if (C > 1 && d->in_dtype == LATTICE_OSR_BF16 && osr::mfma_supported(d->m, d->d, C))
+    if (C > 1 && d->in_dtype == LATTICE_OSR_BF16 && d->linearisation == LATTICE_OSR_LIN2 &&
+        osr::mfma_supported(d->m, d->d, C))
         return Path::Mfma;
     return Path::TokenLoop;
 }
@@ -110,6 +113,7 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     p.chunk = C;
     p.gamma_per_slot = d->gamma_per_slot;
     p.mode = d->mode;
+    p.lin1 = d->linearisation == LATTICE_OSR_LIN1 ? 1 : 0;
     p.y_bf16 = d->y_dtype == LATTICE_OSR_BF16 ? 1 : 0;
     return p;
 }

@@ -15,6 +15,8 @@
 //   s_i <- beta_i (mu + a_i c_i) s_i - beta_i a_i h   (eq. recurrence_detailed;
 //                                                  eq. recurrence_linear2 when
 //                                                  C > 1)
+//   or, with the first chunk linearisation (eq. recurrence_linear1),
+//   s_i <- beta_i mu s_i + beta_i a_i c_i z_i - beta_i a_i h
 //   y   = sum_i q_i s_i                           (memory read-out)
 // With C = 1, Z = S and the step is the exact projected orthogonal update.
 //
@@ -105,7 +107,7 @@ __device__ __forceinline__ void project_rows(float4 (&s)[L::RPT]) {
 // same buffer.
 template <class L, int D>
 __device__ __forceinline__ float4 osr_token(const float4 (&z)[L::RPT], float4 (&s)[L::RPT],
-                                            const TokenIn<L::RPT>& in, int mode, float* red_h,
+                                            const TokenIn<L::RPT>& in, int mode, int lin1, float* red_h,
                                             float* red_y, int lane, int wave, int cg) {
     float4 h;
     if (mode == 0) {
@@ -132,9 +134,14 @@ __device__ __forceinline__ float4 osr_token(const float4 (&z)[L::RPT], float4 (&
         const float a = in.g[i] * (mode == 2 ? cc[i] - in.k[i] : in.k[i]);
         const float w = fmaxf(fmaf(-cc[i], cc[i], hh), 0.f);
         const float beta = rsqrtf(fmaf(mu, mu, a * a * w));
-        const float gate = beta * fmaf(a, cc[i], mu);
         const float kap = -beta * a;
-        s[i] = fma4(gate, s[i], kap * h);
+        if (lin1) {
+            // mu beta on the running slot, the projection term on z
+            s[i] = fma4(beta * mu, s[i], fma4(beta * a * cc[i], z[i], kap * h));
+        } else {
+            const float gate = beta * fmaf(a, cc[i], mu);
+            s[i] = fma4(gate, s[i], kap * h);
+        }
         yp = fma4(in.q[i], s[i], yp);
     }
     return col_sum<L, D>(yp, red_y, lane, wave, cg);
@@ -161,7 +168,7 @@ __global__ __launch_bounds__(NT) void osr_decode_kernel(Params p) {
     float4 z[L::RPT];
 #pragma unroll
     for (int i = 0; i < L::RPT; ++i) z[i] = s[i];
-    const float4 y = osr_token<L, D>(z, s, in, p.mode, red[0], red[1], lane, wave, cg);
+    const float4 y = osr_token<L, D>(z, s, in, p.mode, 0, red[0], red[1], lane, wave, cg);
     if (rg == 0) st_y4(p.y, static_cast<int64_t>(bh) * D + cg * 4, y, p.y_bf16);
 
     project_rows<L>(s);
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
         for (int i = 0; i < L::RPT; ++i) z[i] = s[i];
         for (int t = t0; t < t0 + C; ++t) {
             if (t + 1 < T) load_token<L, M, D, TIn>(nxt, p, bth_of(t + 1), rg, cg);
-            const float4 y = osr_token<L, D>(z, s, cur, p.mode, red[2], red[t & 1], lane, wave, cg);
+            const float4 y = osr_token<L, D>(z, s, cur, p.mode, p.lin1, red[2], red[t & 1], lane, wave, cg);
             if (rg == 0) st_y4(p.y, bth_of(t) * D + cg * 4, y, p.y_bf16);
             cur = nxt;
         }

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblattice_
 
 F32, BF16 = 0, 1
 MODE_DEC, MODE_SIM, MODE_ENC = 0, 1, 2
+LIN2, LIN1 = 0, 1
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_ALIGN = -1, -2, -3, -4, -5, -6, -7
@@ -29,7 +30,7 @@ EXPORTED = ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr
 
 class lattice_osr_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("B", "T", "H", "m", "d", "gamma_per_slot", "in_dtype", "y_dtype", "mode")]
+                ("B", "T", "H", "m", "d", "gamma_per_slot", "in_dtype", "y_dtype", "mode", "linearisation")]
 
 
 class OSRError(RuntimeError):
@@ -77,8 +78,8 @@ def status_string(status: int) -> str:
 lattice_osr_status_string = status_string
 
 
-def make_desc(B, T, H, m, d, gamma_per_slot=1, in_dtype=BF16, y_dtype=F32, mode=MODE_DEC):
-    return lattice_osr_desc(B, T, H, m, d, gamma_per_slot, in_dtype, y_dtype, mode)
+def make_desc(B, T, H, m, d, gamma_per_slot=1, in_dtype=BF16, y_dtype=F32, mode=MODE_DEC, linearisation=LIN2):
+    return lattice_osr_desc(B, T, H, m, d, gamma_per_slot, in_dtype, y_dtype, mode, linearisation)
 
 
 def lattice_osr_workspace_bytes(desc: lattice_osr_desc, chunk_size: int) -> int:
@@ -96,7 +97,7 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode) -> lattice_osr_desc:
+def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation=0) -> lattice_osr_desc:
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q/k/gamma are [B,T,H,m], v is [B,T,H,d]")
     B, T, H, m = q.shape
@@ -109,7 +110,7 @@ def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode) -> lattice_osr_desc:
     if state_in.dtype != torch.float32 or not state_in.is_contiguous():
         raise ValueError("state must be contiguous float32 [B,H,m,d]")
     per_slot = 1 if gamma.dim() == 4 else 0
-    return make_desc(B, T, H, m, d, per_slot, _DT[q.dtype], _DT[y_dtype], mode)
+    return make_desc(B, T, H, m, d, per_slot, _DT[q.dtype], _DT[y_dtype], mode, linearisation)
 
 
 def _outputs(desc, q, state_in, state_out, y, y_dtype):
@@ -128,10 +129,11 @@ def _stream(stream) -> int:
 
 def lattice_osr_fwd_chunked(q, k, v, gamma, mu, state_in, chunk_size: int, *, mode: int = MODE_DEC,
                             y_dtype=torch.float32, state_out=None, y=None, workspace=None,
-                            stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Chunk-wise OSR forward.  Returns (y [B,T,H,d], state_out [B,H,m,d])."""
+                            stream=None, linearisation: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunk-wise OSR forward.  Returns (y [B,T,H,d], state_out [B,H,m,d]).
+    linearisation: LIN2 (default, eq. recurrence_linear2) or LIN1."""
     lib = load_library()
-    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode)
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation)
     state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
     need = lattice_osr_workspace_bytes(desc, chunk_size)
     if workspace is None and need > 0:

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define LATTICE_OSR_ABI_VERSION 1
+#define LATTICE_OSR_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define LATTICE_OSR_API __attribute__((visibility("default")))
@@ -79,6 +79,14 @@ extern "C" {
                                   error of its encoding, e_i = (s_i . v)/|s_i| - k_i,
                                   in place of k_i ("Encoding layer" subsection,
                                   eq. encoding_stateNorm_loss / encoding_recurrence) */
+
+/* Chunk linearisation (section "Parallel and Hardware Efficient Form"): how
+ * the update inside a chunk uses the chunk-start state.  Irrelevant at chunk
+ * size 1, where both are the exact recurrence. */
+#define LATTICE_OSR_LIN2 0 /* eq. recurrence_linear2 (default): the projection term
+                              rides on the running slot, gate mu beta + h~ k^       */
+#define LATTICE_OSR_LIN1 1 /* eq. recurrence_linear1: gate mu beta on the running
+                              slot, the projection term h~ k^ on the chunk-start slot */
 
 /* Status codes. */
 #define LATTICE_OSR_OK 0
@@ -100,14 +108,16 @@ typedef struct {
     int32_t in_dtype;       /* LATTICE_OSR_F32 or LATTICE_OSR_BF16               */
     int32_t y_dtype;        /* LATTICE_OSR_F32 or LATTICE_OSR_BF16               */
     int32_t mode;           /* LATTICE_OSR_MODE_DEC, _SIM or _ENC                */
+    int32_t linearisation;  /* LATTICE_OSR_LIN2 (0) or LATTICE_OSR_LIN1 (1)      */
 } lattice_osr_desc;
 
 /*
  * Chunk-wise forward (training / prefill).  Each chunk of C = chunk_size
  * tokens takes its projections, gates and (decoding objective) h_t from the
  * chunk-start state (eq. recurrence_linear2, the gated-linear-attention form
- * of the section "Parallel and Hardware Efficient Form"); C = 1 is the exact
- * recurrence.  Requires T % chunk_size == 0 and chunk_size a power of two in
+ * of the section "Parallel and Hardware Efficient Form", or eq.
+ * recurrence_linear1 with desc->linearisation = LATTICE_OSR_LIN1, which runs
+ * on the token-loop kernel); C = 1 is the exact recurrence.  Requires T % chunk_size == 0 and chunk_size a power of two in
  * [1, 128].  workspace must hold lattice_osr_workspace_bytes(desc, chunk_size)
  * bytes (it may be NULL when that is 0); its contents on entry are ignored.
  */

@@ -34,7 +34,7 @@ def test_header_declarations_are_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert osr.lattice_osr_abi_version() == 1
+    assert osr.lattice_osr_abi_version() == 2
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = osr.status_string(code)
         assert s and s != "unknown status"
@@ -75,6 +75,7 @@ def test_null_pointers(fn):
     ("m", 0, osr.ERR_SHAPE), ("m", 48, osr.ERR_UNSUPPORTED), ("d", 256, osr.ERR_UNSUPPORTED),
     ("in_dtype", 2, osr.ERR_UNSUPPORTED), ("y_dtype", 7, osr.ERR_UNSUPPORTED),
     ("mode", 3, osr.ERR_UNSUPPORTED), ("mode", -1, osr.ERR_UNSUPPORTED), ("gamma_per_slot", 2, osr.ERR_UNSUPPORTED),
+    ("linearisation", 2, osr.ERR_UNSUPPORTED), ("linearisation", -1, osr.ERR_UNSUPPORTED),
 ])
 def test_bad_descriptor(field, value, status):
     d = osr.make_desc(2, 8, 2, 32, 32)
@@ -85,6 +86,16 @@ def test_bad_descriptor(field, value, status):
         assert _call(fn, d, _ptrs(d)) == status, fn
         d.T = 8 if field != "T" else value
     assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), 4) == status
+
+
+def test_first_linearisation_needs_no_workspace():
+    """The first linearisation runs on the token-loop kernel: no workspace at
+    any chunk size, where the default needs one for bf16 inputs and C >= 16."""
+    d2 = osr.make_desc(2, 256, 4, 64, 64)
+    d1 = osr.make_desc(2, 256, 4, 64, 64, linearisation=osr.LIN1)
+    assert osr.lattice_osr_workspace_bytes(d2, 64) > 0
+    for C in (1, 4, 16, 64):
+        assert osr.lattice_osr_workspace_bytes(d1, C) == 0
 
 
 def test_chunk_size_rules():

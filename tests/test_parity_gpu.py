@@ -171,6 +171,56 @@ def test_bf16_modes_and_gamma_layouts(mode, per_slot):
     _check(inp, y, S, 32, mode)
 
 
+# ---------------------------------------------- first chunk linearisation --
+# eq. recurrence_linear1 (desc linearisation = LIN1), on the token-loop kernel.
+def _oracle_lin1(inp, C, mode):
+    q, k, v, g, mu, S = inp.values_f64()
+    return oracle.osr_forward(q, k, v, g, mu, S, chunk_size=C, mode=mode, linearisation=oracle.LIN1)
+
+
+def _check_lin1(inp, y, S, C, mode):
+    tol = TOL[inp.in_dtype]
+    yr, Sr = _oracle_lin1(inp, C, mode)
+    ey, es = _rel(y.float().cpu().numpy(), yr), _rel(S.cpu().numpy(), Sr)
+    _say(f"  y err/rms = {ey:.3e}, state err/rms = {es:.3e} (tol {tol:g})")
+    assert ey <= tol and es <= tol, (ey, es)
+
+
+@pytest.mark.parametrize("C", [1, 4, 16, 64])
+@pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM, osr.MODE_ENC])
+def test_tiny_chunked_lin1(C, mode):
+    _say(f"tiny chunked, first linearisation, C={C} mode={mode}")
+    inp = _tiny()
+    t = osr.to_device(inp)
+    y, S = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], C,
+                                       mode=mode, linearisation=osr.LIN1)
+    torch.cuda.synchronize()
+    _check_lin1(inp, y, S, C, mode)
+
+
+@pytest.mark.parametrize("m,d,C", [(16, 32, 4), (64, 64, 64), (128, 128, 16), (32, 128, 128)])
+@pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM, osr.MODE_ENC])
+@pytest.mark.parametrize("per_slot", [True, False])
+def test_bf16_chunked_lin1(m, d, C, mode, per_slot):
+    _say(f"bf16 chunked, first linearisation, m={m} d={d} C={C} mode={mode} per_slot={per_slot}")
+    inp = synth.make_inputs(2, 256, 3, m, d, seed=800 + m + d + C, in_dtype=synth.BF16, gamma_per_slot=per_slot)
+    t = osr.to_device(inp)
+    y, S = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], C,
+                                       mode=mode, linearisation=osr.LIN1)
+    torch.cuda.synchronize()
+    _check_lin1(inp, y, S, C, mode)
+
+
+def test_workload_chunked_b4h8_t2048_m64d64_c64_lin1():
+    _say("chunked workload B4 H8 T2048 m64 d64 C64, first linearisation (full compare)")
+    inp = synth.workload_inputs("chunked_b4h8_t2048_m64d64_c64")
+    t = osr.to_device(inp)
+    y, S = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], 64,
+                                       linearisation=osr.LIN1)
+    torch.cuda.synchronize()
+    _check_lin1(inp, y, S, 64, osr.MODE_DEC)
+
+
 # ------------------------------------------------------------ decode sweep --
 # 37 x 64 = 2368 states: more than the persistent decode grid holds at once for
 # every shape, and not a multiple of it, so workgroups take several states
