@@ -87,10 +87,11 @@ class Case:
     sets, so a working set larger than the 256 MB Infinity Cache is read from
     HBM rather than from the cache."""
 
-    def __init__(self, name: str, entry: str, chunk: int, y_dtype=None, copies: int = 1, mode: int = 0):
+    def __init__(self, name: str, entry: str, chunk: int, y_dtype=None, copies: int = 1, mode: int = 0,
+                 linearisation: int = 0):
         import torch
         from compressed_memory_linear_amd import osr, synth
-        self.name, self.entry, self.chunk, self.mode = name, entry, chunk, mode
+        self.name, self.entry, self.chunk, self.mode, self.lin = name, entry, chunk, mode, linearisation
         self.w = dict(synth.WORKLOADS[name])
         inp = synth.workload_inputs(name)
         self.inp = inp
@@ -103,7 +104,7 @@ class Case:
         self.ws = None
         if entry == "chunked":
             desc = osr.make_desc(inp.B, inp.T, inp.H, inp.m, inp.d, 1,
-                                 osr.BF16 if inp.in_dtype == "bf16" else osr.F32, osr.F32, mode)
+                                 osr.BF16 if inp.in_dtype == "bf16" else osr.F32, osr.F32, mode, linearisation)
             need = osr.lattice_osr_workspace_bytes(desc, chunk)
             if need:
                 self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
@@ -115,7 +116,8 @@ class Case:
         args = (t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"])
         if self.entry == "chunked":
             osr.lattice_osr_fwd_chunked(*args, self.chunk, mode=self.mode, y_dtype=self.y_dtype,
-                                        state_out=self.state_out, y=self.y, workspace=self.ws)
+                                        state_out=self.state_out, y=self.y, workspace=self.ws,
+                                        linearisation=self.lin)
         elif self.entry == "recurrent":
             osr.lattice_osr_fwd_recurrent(*args, mode=self.mode, y_dtype=self.y_dtype, state_out=self.state_out,
                                           y=self.y)
@@ -261,16 +263,19 @@ def main() -> int:
 
     if not args.no_secondary:
         sec = []
-        for name, entry, chunk, steps, mode in (("decode_s256h32_m128d128", "decode", 1, 50, 0),
-                                                ("chunked_b8h16_t4096_m64d128_c64", "chunked", 64, 3, 0),
-                                                ("chunked_b1h16_t65536_m128d128_c128", "chunked", 128, 2, 0),
-                                                (HEADLINE, "recurrent", 1, 2, 0),
-                                                (HEADLINE, "chunked", 64, 10, 2)):
-            c = Case(name, entry, chunk, copies=8 if name == HEADLINE and entry == "chunked" else 1, mode=mode)
+        for name, entry, chunk, steps, mode, lin in (("decode_s256h32_m128d128", "decode", 1, 50, 0, 0),
+                                                     ("chunked_b8h16_t4096_m64d128_c64", "chunked", 64, 3, 0, 0),
+                                                     ("chunked_b1h16_t65536_m128d128_c128", "chunked", 128, 2, 0, 0),
+                                                     (HEADLINE, "recurrent", 1, 2, 0, 0),
+                                                     (HEADLINE, "chunked", 64, 10, 2, 0),
+                                                     (HEADLINE, "chunked", 64, 2, 0, 1)):
+            c = Case(name, entry, chunk, copies=8 if name == HEADLINE and entry == "chunked" and not lin else 1,
+                     mode=mode, linearisation=lin)
             t_ms = time_case(c, steps, 1)
             ab = algorithmic_bytes(c.w)
             sec.append({"workload": name, "entry": entry, "chunk": chunk,
-                        "objective": {0: "decoding", 1: "similarity", 2: "encoding"}[mode], "ms_per_step": t_ms,
+                        "objective": {0: "decoding", 1: "similarity", 2: "encoding"}[mode],
+                        "linearisation": "recurrence_linear1" if lin else "recurrence_linear2", "ms_per_step": t_ms,
                         "head_tokens_per_s": c.head_tokens / (t_ms * 1e-3),
                         "hbm_gbs_algorithmic": ab / (t_ms * 1e-3) / 1e9,
                         "hbm_frac": ab / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
