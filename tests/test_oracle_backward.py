@@ -1,0 +1,181 @@
+"""Pins for the fp64 gradient oracle (oracle/osr_backward.py), CPU only.
+
+The gradient oracle differentiates, by torch autograd, a torch transcription
+of the forward.  It is pinned to things other than itself:
+
+* its forward agrees with the C oracle (osr_oracle.c, pinned on its own in
+  test_oracle_pins.py) to rounding, for every objective, both chunk
+  linearisations, both gamma layouts and several chunk sizes;
+* every gradient agrees with central finite differences of the C oracle's
+  forward along random directions (the definition of a vector-Jacobian
+  product; the C oracle shares no code with the torch transcription);
+* closed forms: with gamma = 0 nothing is written, so y_t = sum_i q_{t,i} z_i
+  with Z the projected initial state, and the gradients follow by hand;
+* invariants: the forward does not change when a slot of the initial state
+  is rescaled, so the initial-state gradient is orthogonal to every slot;
+  slot permutation permutes the gradients;
+* planted mistakes in copies of the oracle's source fail the finite-difference
+  pin (a stop-gradient on beta, a state gradient not chained across segments,
+  the returned state's projection left out of the backward).
+"""
+import os
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import osr_backward as ob
+from compressed_memory_linear_amd import synth
+
+DEC, SIM, ENC = oracle.MODE_DEC, oracle.MODE_SIM, oracle.MODE_ENC
+LIN2, LIN1 = oracle.LIN2, oracle.LIN1
+NAMES = ("q", "k", "v", "gamma", "mu", "state")
+
+
+def _problem(seed, B=1, T=12, H=2, m=4, d=5, per_slot=True):
+    inp = synth.make_inputs(B, T, H, m, d, seed=seed, in_dtype=synth.F32, gamma_per_slot=per_slot)
+    return list(inp.values_f64())
+
+
+def _upstream(args, seed):
+    rng = np.random.default_rng(seed + 77)
+    return rng.standard_normal(args[2].shape), rng.standard_normal(args[5].shape)
+
+
+def _loss_c(args, dy, dso, C, mode, lin):
+    y, so = oracle.osr_forward(*args, chunk_size=C, mode=mode, linearisation=lin, nthreads=1)
+    return float(np.sum(dy * y) + np.sum(dso * so))
+
+
+def _fd_check(mod, seed, C, mode, lin, per_slot, which=NAMES, eps=1e-6, segment=None):
+    """Largest relative gap between <grad, u> and the central difference of
+    the C oracle's loss along u, over the inputs in `which`."""
+    args = _problem(seed, per_slot=per_slot)
+    dy, dso = _upstream(args, seed)
+    g = mod.osr_backward(*args, dy, dso, chunk_size=C, mode=mode, linearisation=lin, segment=segment)
+    rng = np.random.default_rng(seed + 5)
+    worst = 0.0
+    for name in which:
+        i = NAMES.index(name)
+        u = rng.standard_normal(args[i].shape)
+        plus = [a.copy() for a in args]
+        minus = [a.copy() for a in args]
+        plus[i] = plus[i] + eps * u
+        minus[i] = minus[i] - eps * u
+        fd = (_loss_c(plus, dy, dso, C, mode, lin) - _loss_c(minus, dy, dso, C, mode, lin)) / (2 * eps)
+        key = "dstate_in" if name == "state" else "d" + name
+        an = float(np.sum(g[key] * u))
+        scale = float(np.sum(np.abs(g[key] * u))) + 1e-12
+        worst = max(worst, abs(fd - an) / scale)
+    return worst
+
+
+@pytest.mark.parametrize("mode", [DEC, SIM, ENC])
+@pytest.mark.parametrize("lin", [LIN2, LIN1])
+@pytest.mark.parametrize("C", [1, 2, 4, 12])
+@pytest.mark.parametrize("per_slot", [True, False])
+def test_torch_forward_matches_c_oracle(mode, lin, C, per_slot):
+    args = _problem(3, T=24 if C != 12 else 12, per_slot=per_slot)
+    y1, s1 = oracle.osr_forward(*args, chunk_size=C, mode=mode, linearisation=lin)
+    y2, s2 = ob.osr_forward_torch(*args, chunk_size=C, mode=mode, linearisation=lin)
+    assert np.max(np.abs(y1 - y2)) <= 1e-12 * max(1.0, np.max(np.abs(y1)))
+    assert np.max(np.abs(s1 - s2)) <= 1e-12
+
+
+@pytest.mark.parametrize("mode", [DEC, SIM, ENC])
+@pytest.mark.parametrize("C", [1, 4])
+@pytest.mark.parametrize("per_slot", [True, False])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_gradient_matches_finite_differences(mode, C, per_slot, seed):
+    # segment = C: the gradient is chained across several segments.
+    assert _fd_check(ob, seed, C, mode, LIN2, per_slot, segment=C) <= 1e-6
+
+
+@pytest.mark.parametrize("mode", [DEC, SIM, ENC])
+def test_gradient_first_linearisation_matches_finite_differences(mode):
+    assert _fd_check(ob, 2, 4, mode, LIN1, True) <= 1e-6
+
+
+@pytest.mark.parametrize("mode", [DEC, SIM, ENC])
+def test_gradient_whole_chunk_matches_finite_differences(mode):
+    # one chunk of the whole sequence: every h, gate and projection frozen at S_0
+    assert _fd_check(ob, 4, 12, mode, LIN2, True) <= 1e-6
+
+
+@pytest.mark.parametrize("mode", [DEC, SIM, ENC])
+@pytest.mark.parametrize("C", [1, 4])
+def test_no_write_closed_form(mode, C):
+    """gamma = 0: S stays at Z = projected S_0 and y_t = sum_i q_{t,i} z_i."""
+    args = _problem(6)
+    q, k, v, gamma, mu, S0 = args
+    gamma = np.zeros_like(gamma)
+    dy, dso = _upstream(args, 6)
+    g = ob.osr_backward(q, k, v, gamma, mu, S0, dy, dso, chunk_size=C, mode=mode)
+    n = np.linalg.norm(S0, axis=-1, keepdims=True)
+    Z = S0 / n
+    # y[b,t,h,:] = sum_i q[b,t,h,i] Z[b,h,i,:]
+    assert np.allclose(g["dq"], np.einsum("bhid,bthd->bthi", Z, dy), rtol=0, atol=1e-12)
+    for key in ("dk", "dv", "dmu"):
+        assert np.max(np.abs(g[key])) <= 1e-12, key
+    G = np.einsum("bthi,bthd->bhid", q, dy) + dso          # dL/dZ
+    dS0 = (G - Z * np.sum(Z * G, axis=-1, keepdims=True)) / n
+    assert np.allclose(g["dstate_in"], dS0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", [DEC, SIM, ENC])
+def test_state_gradient_orthogonal_to_slots(mode):
+    """Rescaling a slot of S_0 changes nothing, so dS_0 . s_i = 0 per slot."""
+    args = _problem(7)
+    args[5] = args[5] * np.random.default_rng(1).uniform(0.5, 2.0, size=args[5].shape[:-1] + (1,))
+    dy, dso = _upstream(args, 7)
+    g = ob.osr_backward(*args, dy, dso, chunk_size=4, mode=mode)
+    dots = np.sum(g["dstate_in"] * args[5], axis=-1)
+    assert np.max(np.abs(dots)) <= 1e-12 * np.max(np.abs(g["dstate_in"]))
+
+
+@pytest.mark.parametrize("mode", [DEC, SIM, ENC])
+def test_slot_permutation_permutes_gradients(mode):
+    args = _problem(8)
+    dy, dso = _upstream(args, 8)
+    perm = np.random.default_rng(2).permutation(args[0].shape[-1])
+    g = ob.osr_backward(*args, dy, dso, chunk_size=4, mode=mode)
+    q, k, v, gamma, mu, S0 = args
+    gp = ob.osr_backward(q[..., perm], k[..., perm], v, gamma[..., perm], mu, S0[:, :, perm],
+                         dy, dso[:, :, perm], chunk_size=4, mode=mode)
+    for key in ("dq", "dk", "dgamma"):
+        assert np.allclose(gp[key], g[key][..., perm], rtol=0, atol=1e-12), key
+    for key in ("dv", "dmu"):
+        assert np.allclose(gp[key], g[key], rtol=0, atol=1e-12), key
+    assert np.allclose(gp["dstate_in"], g["dstate_in"][:, :, perm], rtol=0, atol=1e-12)
+
+
+def test_segments_chain_to_the_same_gradient():
+    args = _problem(9, T=24)
+    dy, dso = _upstream(args, 9)
+    a = ob.osr_backward(*args, dy, dso, chunk_size=4, segment=4)
+    b = ob.osr_backward(*args, dy, dso, chunk_size=4, segment=24)
+    for key in a:
+        assert np.allclose(a[key], b[key], rtol=0, atol=1e-12), key
+
+
+_MUTANTS = {
+    "beta_stop_gradient": ("beta = 1.0 / torch.sqrt(mut * mut + dsq)",
+                           "beta = (1.0 / torch.sqrt(mut * mut + dsq)).detach()"),
+    "state_gradient_not_chained": ("dS = g[0]\n", "dS = dS\n"),
+    "final_projection_skipped": ("(dS,) = torch.autograd.grad(_project(Se), Se, grad_outputs=dSo)",
+                                 "dS = dSo"),
+    "mu_left_out_of_gate": ("R = (mut * beta + htil * khat)[..., None] * R",
+                            "R = (mut.detach() * beta + htil * khat)[..., None] * R"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_MUTANTS))
+def test_planted_mistake_fails_finite_differences(name):
+    src = open(os.path.join(os.path.dirname(ob.__file__), "osr_backward.py")).read()
+    old, new = _MUTANTS[name]
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("osr_backward_mutant")
+    exec(compile(src.replace(old, new), "osr_backward_mutant.py", "exec"), mod.__dict__)
+    worst = max(_fd_check(mod, s, 4, DEC, LIN2, True, segment=4) for s in (0, 1))
+    assert worst > 1e-3, (name, worst)
