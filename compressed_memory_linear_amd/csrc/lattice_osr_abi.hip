@@ -118,6 +118,59 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     return p;
 }
 
+// Backward: pointer, alignment and overlap checks.  Every gradient buffer and
+// the workspace is an output; none may overlap another output or any input.
+int check_bwd_buffers(const lattice_osr_desc* d, const void* q, const void* k, const void* v,
+                      const void* gamma, const void* mu, const float* sin, const void* dy,
+                      const float* dso, const float* dq, const float* dk, const float* dv,
+                      const float* dgamma, const float* dmu, const float* dsi, const void* ws,
+                      size_t ws_bytes, size_t ws_needed) {
+    if (!q || !k || !v || !gamma || !mu || !sin || !dy || !dso || !dq || !dk || !dv || !dgamma || !dmu || !dsi)
+        return LATTICE_OSR_ERR_NULL;
+    if (ws_needed > 0 && !ws) return LATTICE_OSR_ERR_NULL;
+    if (ws_bytes < ws_needed) return LATTICE_OSR_ERR_WORKSPACE;
+    const size_t ein_align = d->in_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const void* vec[] = {q, k, v, d->gamma_per_slot ? gamma : nullptr, sin, dy, dso, dv, dsi, ws};
+    for (const void* ptr : vec)
+        if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return LATTICE_OSR_ERR_ALIGN;
+    const void* elem[] = {mu, gamma};
+    for (const void* ptr : elem)
+        if (reinterpret_cast<uintptr_t>(ptr) % ein_align != 0) return LATTICE_OSR_ERR_ALIGN;
+    const void* f32s[] = {dq, dk, dgamma, dmu};
+    for (const void* ptr : f32s)
+        if (reinterpret_cast<uintptr_t>(ptr) % 4 != 0) return LATTICE_OSR_ERR_ALIGN;
+
+    const size_t ein = d->in_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const size_t ey = d->y_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const size_t tok = static_cast<size_t>(d->B) * d->T * d->H;
+    const size_t gsz = tok * (d->gamma_per_slot ? d->m : 1);
+    const size_t st = static_cast<size_t>(d->B) * d->H * d->m * d->d * sizeof(float);
+    const Range ins[] = {range_of(q, tok * d->m * ein), range_of(k, tok * d->m * ein),
+                         range_of(v, tok * d->d * ein), range_of(gamma, gsz * ein), range_of(mu, tok * ein),
+                         range_of(sin, st), range_of(dy, tok * d->d * ey), range_of(dso, st)};
+    const Range outs[] = {range_of(dq, tok * d->m * 4), range_of(dk, tok * d->m * 4),
+                          range_of(dv, tok * d->d * 4), range_of(dgamma, gsz * 4), range_of(dmu, tok * 4),
+                          range_of(dsi, st), range_of(ws, ws_needed)};
+    const int nout = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return LATTICE_OSR_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return LATTICE_OSR_ERR_ALIAS;
+    }
+    return LATTICE_OSR_OK;
+}
+
+// Shape rules of the backward: those of the chunked forward, with the default
+// linearisation only.
+int check_bwd_desc(const lattice_osr_desc* d, int C) {
+    int rc = check_desc(d);
+    if (rc) return rc;
+    if (C <= 0 || d->T % C != 0) return LATTICE_OSR_ERR_SHAPE;
+    if (!pow2_chunk(C) || d->linearisation != LATTICE_OSR_LIN2) return LATTICE_OSR_ERR_UNSUPPORTED;
+    return LATTICE_OSR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -186,6 +239,42 @@ int lattice_osr_decode_step(const lattice_osr_desc* desc, const void* q, const v
     const osr::Params p = make_params(desc, 1, q, k, v, gamma, mu, state_in, state_out, y, workspace);
     return osr::launch_valu(true, desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16,
                             static_cast<hipStream_t>(hip_stream));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* desc, int32_t chunk_size) {
+    if (check_bwd_desc(desc, chunk_size) != LATTICE_OSR_OK) return static_cast<size_t>(-1);
+    return osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
+}
+
+int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, const void* q, const void* k,
+                            const void* v, const void* gamma, const void* mu, const float* state_in,
+                            const void* dy, const float* dstate_out, float* dq, float* dk, float* dv,
+                            float* dgamma, float* dmu, float* dstate_in, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+    int rc = check_bwd_desc(desc, chunk_size);
+    if (rc) return rc;
+    const size_t need = osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
+    rc = check_bwd_buffers(desc, q, k, v, gamma, mu, state_in, dy, dstate_out, dq, dk, dv, dgamma, dmu,
+                           dstate_in, workspace, workspace_bytes, need);
+    if (rc) return rc;
+    osr::BwdParams p;
+    p.f = make_params(desc, chunk_size, q, k, v, gamma, mu, state_in, nullptr, nullptr, nullptr);
+    p.dy = dy;
+    p.dstate_out = dstate_out;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dgamma = dgamma;
+    p.dmu = dmu;
+    p.dstate_in = dstate_in;
+    p.ws = static_cast<float*>(workspace);
+    p.dy_bf16 = desc->y_dtype == LATTICE_OSR_BF16 ? 1 : 0;
+    return osr::launch_bwd(desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16,
+                           static_cast<hipStream_t>(hip_stream));
 }
 
 }  // extern "C"

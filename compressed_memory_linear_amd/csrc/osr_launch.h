@@ -21,4 +21,23 @@ bool mfma_supported(int m, int d, int C);
 size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C);
 int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st);
 
+// Backward of the chunk-wise forward (fp32 VALU, one workgroup per (b,h)).
+// f carries the forward's inputs and shape (its state_out, y and zbuf are
+// unused); the gradients are fp32 in the inputs' layouts.
+struct BwdParams {
+    Params f;
+    const void* dy;          // [B,T,H,d], fp32 or bf16 (dy_bf16)
+    const float* dstate_out; // [B,H,m,d]
+    float* dq;               // [B,T,H,m]
+    float* dk;               // [B,T,H,m]
+    float* dv;               // [B,T,H,d]
+    float* dgamma;           // [B,T,H,m] or [B,T,H]
+    float* dmu;              // [B,T,H]
+    float* dstate_in;        // [B,H,m,d]
+    float* ws;               // bwd_workspace_bytes(...)
+    int dy_bf16;
+};
+size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C);
+int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
+
 }  // namespace osr

@@ -20,84 +20,11 @@
 //   y   = sum_i q_i s_i                           (memory read-out)
 // With C = 1, Z = S and the step is the exact projected orthogonal update.
 //
-// Thread layout: the m x d fp32 state lives in registers.  TPR = d/4 threads
-// cover one slot row with float4 columns; NT/TPR row groups take rows
-// rg, rg + RG, ...  Reductions over d stay inside a group of TPR consecutive
-// lanes (shuffles); reductions over slots go across row groups (shuffles,
-// then one LDS exchange across waves).
-#include "osr_device.h"
+// Thread layout and reductions: osr_valu.h.
 #include "osr_launch.h"
+#include "osr_valu.h"
 
 namespace osr {
-
-template <int M, int D, int NT>
-struct ValuLayout {
-    static constexpr int TPR = D / 4;         // threads per slot row
-    static constexpr int RG = NT / TPR;       // row groups
-    static constexpr int RPT = M / RG;        // rows per thread
-    static constexpr int NW = NT / 64;        // waves
-    static_assert(NT % 64 == 0, "whole waves");
-    static_assert(TPR >= 1 && TPR <= 32 && 64 % TPR == 0, "row group inside a wave");
-    static_assert(RG * RPT == M && RPT >= 1, "rows divide evenly");
-};
-
-template <int RPT>
-struct TokenIn {
-    float k[RPT], q[RPT], g[RPT];
-    float4 v;
-    float mu;
-};
-
-// Column sums (over slots) of a per-thread float4 partial.  Uses red[NW*D]
-// and one barrier (see osr_token for how callers rotate buffers).
-template <class L, int D>
-__device__ __forceinline__ float4 col_sum(float4 p, float* red, int lane, int wave, int cg) {
-    if constexpr (L::TPR < 64) {
-        p.x = strided_sum<L::TPR>(p.x);
-        p.y = strided_sum<L::TPR>(p.y);
-        p.z = strided_sum<L::TPR>(p.z);
-        p.w = strided_sum<L::TPR>(p.w);
-    }
-    if constexpr (L::NW == 1) {
-        return p;
-    } else {
-        if (lane < L::TPR) *reinterpret_cast<float4*>(red + wave * D + cg * 4) = p;
-        __syncthreads();
-        float4 s = *reinterpret_cast<const float4*>(red + cg * 4);
-#pragma unroll
-        for (int w = 1; w < L::NW; ++w) s = s + *reinterpret_cast<const float4*>(red + w * D + cg * 4);
-        return s;
-    }
-}
-
-template <class L, int M, int D, typename TIn>
-__device__ __forceinline__ void load_token(TokenIn<L::RPT>& in, const Params& p, int64_t bth,
-                                           int rg, int cg) {
-    const TIn* q = static_cast<const TIn*>(p.q);
-    const TIn* k = static_cast<const TIn*>(p.k);
-    const TIn* g = static_cast<const TIn*>(p.gamma);
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) {
-        const int row = rg + L::RG * i;
-        in.k[i] = ld<TIn>(k, bth * M + row);
-        in.q[i] = ld<TIn>(q, bth * M + row);
-        in.g[i] = p.gamma_per_slot ? ld<TIn>(g, bth * M + row) : ld<TIn>(g, bth);
-    }
-    in.v = ld4<TIn>(static_cast<const TIn*>(p.v), bth * D + cg * 4);
-    in.mu = ld<TIn>(static_cast<const TIn*>(p.mu), bth);
-}
-
-// Row sums of squares -> scale every row onto the unit sphere.
-template <class L>
-__device__ __forceinline__ void project_rows(float4 (&s)[L::RPT]) {
-    float n2[L::RPT];
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) n2[i] = dot4(s[i], s[i]);
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) n2[i] = group_sum<L::TPR>(n2[i]);
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) s[i] = rsqrtf(n2[i]) * s[i];
-}
 
 // One token: update the running state s from the chunk-start state z and
 // return the read-out for this thread's 4 columns (valid in every thread).

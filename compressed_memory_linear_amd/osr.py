@@ -25,7 +25,8 @@ OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_ALIGN = -1, -2, -3, -4, -5, -6, -7
 
 EXPORTED = ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step",
-            "lattice_osr_workspace_bytes", "lattice_osr_status_string", "lattice_osr_abi_version")
+            "lattice_osr_workspace_bytes", "lattice_osr_status_string", "lattice_osr_abi_version",
+            "lattice_osr_bwd_chunked", "lattice_osr_bwd_workspace_bytes")
 
 
 class lattice_osr_desc(ctypes.Structure):
@@ -57,6 +58,10 @@ def load_library():
         lib.lattice_osr_decode_step.argtypes = fwd
         for f in ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step"):
             getattr(lib, f).restype = ctypes.c_int
+        lib.lattice_osr_bwd_chunked.argtypes = [dp, ctypes.c_int32] + [vp] * 15 + [ctypes.c_size_t, vp]
+        lib.lattice_osr_bwd_chunked.restype = ctypes.c_int
+        lib.lattice_osr_bwd_workspace_bytes.argtypes = [dp, ctypes.c_int32]
+        lib.lattice_osr_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.lattice_osr_workspace_bytes.argtypes = [dp, ctypes.c_int32]
         lib.lattice_osr_workspace_bytes.restype = ctypes.c_size_t
         lib.lattice_osr_status_string.argtypes = [ctypes.c_int]
@@ -175,6 +180,46 @@ def lattice_osr_decode_step(q, k, v, gamma, mu, state_in, *, mode: int = MODE_DE
     if rc != OK:
         raise OSRError(rc, "lattice_osr_decode_step")
     return y, state_out
+
+
+def lattice_osr_bwd_workspace_bytes(desc: lattice_osr_desc, chunk_size: int) -> int:
+    n = int(load_library().lattice_osr_bwd_workspace_bytes(ctypes.byref(desc), int(chunk_size)))
+    if n == ctypes.c_size_t(-1).value:
+        raise OSRError(ERR_UNSUPPORTED, "lattice_osr_bwd_workspace_bytes")
+    return n
+
+
+def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size: int, *,
+                            mode: int = MODE_DEC, grads: Optional[dict] = None, workspace=None,
+                            stream=None) -> dict:
+    """Backward of the chunk-wise forward: gradients of sum(dy*y) +
+    sum(dstate_out*state_out) with respect to q, k, v, gamma, mu and
+    state_in.  dy has y's shape (float32 or bfloat16), dstate_out the state's.
+    Returns a dict of float32 tensors dq, dk, dv, dgamma, dmu, dstate_in
+    (allocated unless passed in `grads`)."""
+    lib = load_library()
+    desc = _desc_from(q, k, v, gamma, mu, state_in, dy.dtype, mode)
+    if not dy.is_contiguous() or dy.shape != v.shape or dy.device != q.device:
+        raise ValueError("dy must be contiguous with v's shape")
+    if dstate_out.dtype != torch.float32 or not dstate_out.is_contiguous() or dstate_out.shape != state_in.shape:
+        raise ValueError("dstate_out must be contiguous float32 with the state's shape")
+    if grads is None:
+        grads = {"d" + n: torch.empty(t.shape, dtype=torch.float32, device=q.device)
+                 for n, t in (("q", q), ("k", k), ("v", v), ("gamma", gamma), ("mu", mu),
+                              ("state_in", state_in))}
+    need = lattice_osr_bwd_workspace_bytes(desc, chunk_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    g = grads
+    rc = lib.lattice_osr_bwd_chunked(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(dy), _ptr(dstate_out),
+                                     _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dgamma"]),
+                                     _ptr(g["dmu"]), _ptr(g["dstate_in"]), _ptr(workspace), wbytes,
+                                     _stream(stream))
+    if rc != OK:
+        raise OSRError(rc, "lattice_osr_bwd_chunked")
+    return grads
 
 
 # ------------------------------------------------------------ host inputs --

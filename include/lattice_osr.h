@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define LATTICE_OSR_ABI_VERSION 2
+#define LATTICE_OSR_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define LATTICE_OSR_API __attribute__((visibility("default")))
@@ -149,6 +149,42 @@ LATTICE_OSR_API int lattice_osr_decode_step(const lattice_osr_desc* desc, const 
 /* Workspace bytes lattice_osr_fwd_chunked needs for this shape (0 if none);
  * (size_t)-1 if the arguments are invalid. */
 LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc, int32_t chunk_size);
+
+/*
+ * Backward of the chunk-wise forward (training).  The pages train the layer
+ * through its chunk-wise form (section "Parallel and Hardware Efficient
+ * Form"); this call returns the gradient of
+ *     L = sum(dy * y) + sum(dstate_out * state_out)
+ * with respect to q, k, v, gamma, mu and state_in, where (y, state_out) is
+ * lattice_osr_fwd_chunked at the same desc and chunk_size with
+ * desc->linearisation = LATTICE_OSR_LIN2 (eq. recurrence_linear2; LIN1 is
+ * LATTICE_OSR_ERR_UNSUPPORTED).  The forward is recomputed inside the call:
+ * the forward's y and state_out are not needed.
+ *   dy          [B,T,H,d]   y_dtype            (16-byte aligned)
+ *   dstate_out  [B,H,m,d]   float32            (16-byte aligned)
+ *   dq, dk      [B,T,H,m]   float32            (4-byte aligned)
+ *   dv          [B,T,H,d]   float32            (16-byte aligned)
+ *   dgamma      gamma's shape, float32         (4-byte aligned)
+ *   dmu         [B,T,H]     float32            (4-byte aligned)
+ *   dstate_in   [B,H,m,d]   float32            (16-byte aligned)
+ * Every gradient is written in full (no accumulation into existing values).
+ * The gradient buffers and the workspace must not overlap one another or any
+ * input.  workspace must hold lattice_osr_bwd_workspace_bytes(desc,
+ * chunk_size) bytes: per (b,h), 4 (T/C + 1 + C) m d bytes of states plus
+ * 4 C (2m + d + 4) bytes of per-token values.  The remaining rules (shapes,
+ * chunk sizes, alignment of the inputs, status codes, asynchrony) are those
+ * of lattice_osr_fwd_chunked.
+ */
+LATTICE_OSR_API int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size,
+                            const void* q, const void* k, const void* v, const void* gamma,
+                            const void* mu, const float* state_in, const void* dy,
+                            const float* dstate_out, float* dq, float* dk, float* dv, float* dgamma,
+                            float* dmu, float* dstate_in, void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+
+/* Workspace bytes lattice_osr_bwd_chunked needs for this shape; (size_t)-1 if
+ * the arguments are invalid or the configuration has no backward. */
+LATTICE_OSR_API size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* desc, int32_t chunk_size);
 
 /* Static text for a status code (never NULL). */
 LATTICE_OSR_API const char* lattice_osr_status_string(int status);

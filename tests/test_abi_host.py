@@ -34,7 +34,7 @@ def test_header_declarations_are_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert osr.lattice_osr_abi_version() == 2
+    assert osr.lattice_osr_abi_version() == 3
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = osr.status_string(code)
         assert s and s != "unknown status"
@@ -174,3 +174,82 @@ def test_workspace_too_small_is_rejected():
         assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), C, BASE * 4, need - 1) == osr.ERR_WORKSPACE
         # workspace overlapping an input
         assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), C, _ptrs(d)[0], need) == osr.ERR_ALIAS
+
+
+# ---------------------------------------------------------------- backward --
+# Argument order after (desc, chunk): q, k, v, gamma, mu, state_in, dy,
+# dstate_out (inputs 0..7), dq, dk, dv, dgamma, dmu, dstate_in (outputs 8..13).
+def _bwd_ptrs(gap=1 << 32):
+    return [BASE + i * gap for i in range(14)]
+
+
+def _bwd_call(d, ptrs, chunk, ws=None, ws_bytes=None):
+    lib = osr.load_library()
+    if ws_bytes is None:
+        need = lib.lattice_osr_bwd_workspace_bytes(ctypes.byref(d), chunk)
+        ws_bytes = need if need != ctypes.c_size_t(-1).value else 0
+    if ws is None:
+        ws = BASE + 14 * (1 << 32)
+    return lib.lattice_osr_bwd_chunked(ctypes.byref(d), chunk, *ptrs, ws, ws_bytes, None)
+
+
+def test_bwd_workspace_formula():
+    """Per (b,h): 4 (T/C + 1 + C) m d bytes of states and 4 C (2m + d + 4)
+    bytes of per-token values."""
+    for (B, T, H, m, dd, C) in ((4, 2048, 8, 64, 64, 64), (1, 64, 1, 16, 32, 1), (2, 512, 3, 128, 128, 128)):
+        d = osr.make_desc(B, T, H, m, dd)
+        per = 4 * ((T // C + 1 + C) * m * dd + C * (2 * m + dd + 4))
+        assert osr.lattice_osr_bwd_workspace_bytes(d, C) == B * H * per
+
+
+def test_bwd_null_pointers_and_shapes():
+    d = osr.make_desc(1, 8, 1, 16, 16)
+    lib = osr.load_library()
+    assert lib.lattice_osr_bwd_chunked(None, 4, *_bwd_ptrs(), None, 0, None) == osr.ERR_NULL
+    for i in range(14):
+        p = _bwd_ptrs()
+        p[i] = None
+        assert _bwd_call(d, p, 4) == osr.ERR_NULL, i
+    assert _bwd_call(d, _bwd_ptrs(), 4, ws=None, ws_bytes=0) in (osr.ERR_WORKSPACE,)
+    lib2 = osr.load_library()
+    assert lib2.lattice_osr_bwd_chunked(ctypes.byref(d), 4, *_bwd_ptrs(), None, 1 << 30, None) == osr.ERR_NULL
+    assert _bwd_call(d, _bwd_ptrs(), 3) == osr.ERR_SHAPE          # ragged tail
+    assert _bwd_call(d, _bwd_ptrs(), 0) == osr.ERR_SHAPE
+    d2 = osr.make_desc(1, 8, 1, 16, 48)
+    assert _bwd_call(d2, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED
+    d3 = osr.make_desc(1, 8, 1, 16, 16, linearisation=osr.LIN1)
+    assert _bwd_call(d3, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED  # only eq. recurrence_linear2
+    with pytest.raises(osr.OSRError):
+        osr.lattice_osr_bwd_workspace_bytes(d3, 4)
+
+
+def test_bwd_workspace_too_small():
+    d = osr.make_desc(2, 64, 2, 32, 32)
+    need = osr.lattice_osr_bwd_workspace_bytes(d, 16)
+    assert _bwd_call(d, _bwd_ptrs(), 16, ws_bytes=need - 1) == osr.ERR_WORKSPACE
+
+
+def test_bwd_aliasing_rules():
+    d = osr.make_desc(1, 8, 1, 16, 16, in_dtype=osr.F32)
+    for out in range(8, 14):
+        for other in list(range(0, 8)) + [o for o in range(8, 14) if o != out]:
+            p = _bwd_ptrs()
+            p[out] = p[other]
+            assert _bwd_call(d, p, 4) == osr.ERR_ALIAS, (out, other)
+    # workspace overlapping an input or an output
+    for other in (0, 5, 9, 13):
+        assert _bwd_call(d, _bwd_ptrs(), 4, ws=_bwd_ptrs()[other]) == osr.ERR_ALIAS, other
+
+
+def test_bwd_alignment_rules():
+    d = osr.make_desc(1, 8, 1, 16, 16, in_dtype=osr.F32)
+    sixteen = [0, 1, 2, 3, 5, 6, 7, 10, 13]     # vector-accessed buffers
+    for i in sixteen:
+        p = _bwd_ptrs()
+        p[i] += 8
+        assert _bwd_call(d, p, 4) == osr.ERR_ALIGN, i
+    for i in (8, 9, 11, 12):                    # scalar fp32 outputs
+        p = _bwd_ptrs()
+        p[i] += 2
+        assert _bwd_call(d, p, 4) == osr.ERR_ALIGN, i
+    assert _bwd_call(d, _bwd_ptrs(), 4, ws=BASE + 14 * (1 << 32) + 8) == osr.ERR_ALIGN
