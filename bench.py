@@ -9,7 +9,7 @@ called through the C ABI.  The metric is head-tokens per second (B*H*T per
 step).  Printed: one JSON line with the headline value, the roofline of the
 chunk path measured live with HIP events on the launch stream, the fp64 CPU
 oracle timed on this host, and secondary lines for the decode, recurrent and
-other chunked workloads.
+other chunked workloads and for the backward of the headline workload.
 """
 from __future__ import annotations
 
@@ -52,6 +52,16 @@ def algorithmic_flops(w: dict, chunk: int) -> float:
     return float(f * w["B"] * w["H"] * w["T"])
 
 
+def algorithmic_bytes_bwd(w: dict) -> float:
+    """Compulsory HBM bytes of one backward: the forward's inputs and fp32 dy
+    read once, the fp32 gradients of every input written once, and per (b,h)
+    the state, its upstream gradient and its gradient moved once each."""
+    e = 2 if w["in_dtype"] == "bf16" else 4
+    tok = w["B"] * w["H"] * w["T"]
+    per_tok = (e + 4) * (3 * w["m"] + w["d"] + 1) + 4 * w["d"]
+    return float(tok * per_tok + 3 * 4 * w["B"] * w["H"] * w["m"] * w["d"])
+
+
 def chain_reference_ms(w: dict, chunk: int) -> float:
     """Dependency-chain reference: the chunks of one (b,h) run in sequence, so
     the step cannot beat (T/C) x (per-chunk flops at one CU's bf16 MFMA peak)."""
@@ -59,9 +69,17 @@ def chain_reference_ms(w: dict, chunk: int) -> float:
     return (w["T"] / chunk) * per_chunk / (BF16_MFMA_PEAK_TFLOPS * 1e12 / 256) * 1e3
 
 
+# Sources of the backward kernel: not part of the forward and decode kernels
+# whose traffic counters are keyed by the hash below.
+BWD_SOURCES = ("osr_bwd.hip",)
+
+
 def source_hash() -> str:
+    """Hash of the sources the forward and decode kernels are built from."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "compressed_memory_linear_amd", "csrc", "*"))):
+        if os.path.basename(p) in BWD_SOURCES:
+            continue
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -102,6 +120,18 @@ class Case:
         self.y = torch.empty((inp.B, inp.T, inp.H, inp.d), dtype=self.y_dtype, device="cuda")
         self.state_out = torch.empty_like(self.sets[0]["state"])
         self.ws = None
+        if entry == "backward":
+            desc = osr.make_desc(inp.B, inp.T, inp.H, inp.m, inp.d, 1,
+                                 osr.BF16 if inp.in_dtype == "bf16" else osr.F32, osr.F32, mode, linearisation)
+            self.ws = torch.empty(osr.lattice_osr_bwd_workspace_bytes(desc, chunk), dtype=torch.uint8,
+                                  device="cuda")
+            g = torch.Generator(device="cuda").manual_seed(7)
+            self.dy = torch.randn(self.y.shape, generator=g, device="cuda")
+            self.dso = torch.randn(self.state_out.shape, generator=g, device="cuda")
+            t0 = self.sets[0]
+            self.grads = {"d" + n: torch.empty(t0[n].shape, dtype=torch.float32, device="cuda")
+                          for n in ("q", "k", "v", "gamma", "mu")}
+            self.grads["dstate_in"] = torch.empty_like(t0["state"])
         if entry == "chunked":
             desc = osr.make_desc(inp.B, inp.T, inp.H, inp.m, inp.d, 1,
                                  osr.BF16 if inp.in_dtype == "bf16" else osr.F32, osr.F32, mode, linearisation)
@@ -118,6 +148,9 @@ class Case:
             osr.lattice_osr_fwd_chunked(*args, self.chunk, mode=self.mode, y_dtype=self.y_dtype,
                                         state_out=self.state_out, y=self.y, workspace=self.ws,
                                         linearisation=self.lin)
+        elif self.entry == "backward":
+            osr.lattice_osr_bwd_chunked(*args, self.dy, self.dso, self.chunk, mode=self.mode, grads=self.grads,
+                                        workspace=self.ws)
         elif self.entry == "recurrent":
             osr.lattice_osr_fwd_recurrent(*args, mode=self.mode, y_dtype=self.y_dtype, state_out=self.state_out,
                                           y=self.y)
@@ -268,18 +301,20 @@ def main() -> int:
                                                      ("chunked_b1h16_t65536_m128d128_c128", "chunked", 128, 2, 0, 0),
                                                      (HEADLINE, "recurrent", 1, 2, 0, 0),
                                                      (HEADLINE, "chunked", 64, 10, 2, 0),
-                                                     (HEADLINE, "chunked", 64, 2, 0, 1)):
+                                                     (HEADLINE, "chunked", 64, 2, 0, 1),
+                                                     (HEADLINE, "backward", 64, 2, 0, 0)):
             c = Case(name, entry, chunk, copies=8 if name == HEADLINE and entry == "chunked" and not lin else 1,
                      mode=mode, linearisation=lin)
             t_ms = time_case(c, steps, 1)
-            ab = algorithmic_bytes(c.w)
+            ab = algorithmic_bytes_bwd(c.w) if entry == "backward" else algorithmic_bytes(c.w)
             sec.append({"workload": name, "entry": entry, "chunk": chunk,
                         "objective": {0: "decoding", 1: "similarity", 2: "encoding"}[mode],
                         "linearisation": "recurrence_linear1" if lin else "recurrence_linear2", "ms_per_step": t_ms,
                         "head_tokens_per_s": c.head_tokens / (t_ms * 1e-3),
                         "hbm_gbs_algorithmic": ab / (t_ms * 1e-3) / 1e9,
                         "hbm_frac": ab / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                        "tflops_algorithmic": algorithmic_flops(c.w, chunk) / (t_ms * 1e-3) / 1e12})
+                        "tflops_algorithmic": None if entry == "backward"
+                        else algorithmic_flops(c.w, chunk) / (t_ms * 1e-3) / 1e12})
             del c
             torch.cuda.empty_cache()
         out["secondary"] = sec

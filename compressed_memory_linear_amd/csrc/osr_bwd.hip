@@ -117,10 +117,49 @@ __device__ __forceinline__ void slot_sum2(float4& col, float4& sc, float* red, i
     }
 }
 
+// What the reverse walk reads for one token: its inputs, its record, dy and
+// (when prefetched) the state before it.
+template <int RPT>
+struct RevIn {
+    TokenIn<RPT> in;
+    float c[RPT], beta[RPT];
+    float4 h, dy;
+    float hh;
+    float4 rp[RPT];
+};
+
+template <class L, int M, int D, typename TIn, bool PF_STATE>
+__device__ __forceinline__ void load_rev(RevIn<L::RPT>& x, const BwdParams& p, const float* trec,
+                                         const float* rtok, int64_t bth, int tau, int rg, int cg, int el0) {
+    using TR = TokRec<M, D>;
+    load_token<L, M, D, TIn>(x.in, p.f, bth, rg, cg);
+    const float* rec = trec + static_cast<int64_t>(tau) * TR::SIZE;
+#pragma unroll
+    for (int i = 0; i < L::RPT; ++i) {
+        x.c[i] = rec[TR::C_OFF + rg + L::RG * i];
+        x.beta[i] = rec[TR::B_OFF + rg + L::RG * i];
+    }
+    x.h = *reinterpret_cast<const float4*>(rec + TR::H_OFF + cg * 4);
+    x.hh = rec[TR::HH_OFF];
+    x.dy = p.dy_bf16 ? ld4<uint16_t>(static_cast<const uint16_t*>(p.dy), bth * D + cg * 4)
+                     : ld4<float>(static_cast<const float*>(p.dy), bth * D + cg * 4);
+    if constexpr (PF_STATE) {
+        const float* rpre = rtok + static_cast<int64_t>(tau) * M * D;
+#pragma unroll
+        for (int i = 0; i < L::RPT; ++i)
+            x.rp[i] = *reinterpret_cast<const float4*>(rpre + el0 + i * L::RG * D);
+    }
+}
+
 template <int M, int D, int NT, typename TIn>
 __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     using L = ValuLayout<M, D, NT>;
     using TR = TokRec<M, D>;
+    // The reverse walk loads the next token's inputs and record while it works on
+    // the current one, and the state before it too, where registers allow (at
+    // 8 slot rows per thread either would spill).
+    constexpr bool PF_TOKEN = L::RPT <= 4;
+    constexpr bool PF_STATE = L::RPT <= 2;
     __shared__ float red[2][L::NW * (D + 4)];
     const int bh = blockIdx.x;
     const int b = bh / p.f.H, hd = bh % p.f.H;
@@ -142,6 +181,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     const float* sin = p.f.state_in + static_cast<int64_t>(bh) * M * D;
 #pragma unroll
     for (int i = 0; i < L::RPT; ++i) r[i] = *reinterpret_cast<const float4*>(sin + el(i));
+    TokenIn<L::RPT> cur, nxt;
+    if constexpr (PF_TOKEN) load_token<L, M, D, TIn>(cur, p.f, bth_of(0), rg, cg);
     for (int n = 0; n < NC; ++n) {
 #pragma unroll
         for (int i = 0; i < L::RPT; ++i) *reinterpret_cast<float4*>(sck + static_cast<int64_t>(n) * M * D + el(i)) = r[i];
@@ -149,12 +190,16 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < L::RPT; ++i) z[i] = r[i];
         for (int t = n * C; t < (n + 1) * C; ++t) {
-            TokenIn<L::RPT> in;
-            load_token<L, M, D, TIn>(in, p.f, bth_of(t), rg, cg);
+            if constexpr (PF_TOKEN) {
+                if (t + 1 < T) load_token<L, M, D, TIn>(nxt, p.f, bth_of(t + 1), rg, cg);
+            } else {
+                load_token<L, M, D, TIn>(cur, p.f, bth_of(t), rg, cg);
+            }
             float c[L::RPT], beta[L::RPT], hh;
             float4 h;
-            fwd_token_keep<L, D>(z, r, in, mode, red[nred & 1], lane, wave, cg, c, beta, h, hh);
+            fwd_token_keep<L, D>(z, r, cur, mode, red[nred & 1], lane, wave, cg, c, beta, h, hh);
             nred += mode == 0;  // only the decoding objective reduces over slots here
+            if constexpr (PF_TOKEN) cur = nxt;
         }
     }
 #pragma unroll
@@ -177,9 +222,6 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
         for (int i = 0; i < L::RPT; ++i) dR[i] = rsqrtf(n2[i]) * fma4(-pr[i], o[i], dR[i]);
     }
 
-    const float* dyp = static_cast<const float*>(p.dy);
-    const uint16_t* dyb = static_cast<const uint16_t*>(p.dy);
-
     // ---- phase 2: chunks in reverse ----
     for (int n = NC - 1; n >= 0; --n) {
         __syncthreads();  // the previous chunk's reverse walk has read rtok / trec
@@ -195,15 +237,20 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
             }
         }
         // forward again over the chunk, keeping what the reverse walk needs
+        if constexpr (PF_TOKEN) load_token<L, M, D, TIn>(cur, p.f, bth_of(n * C), rg, cg);
         for (int tau = 0; tau < C; ++tau) {
 #pragma unroll
             for (int i = 0; i < L::RPT; ++i)
                 *reinterpret_cast<float4*>(rtok + static_cast<int64_t>(tau) * M * D + el(i)) = r[i];
-            TokenIn<L::RPT> in;
-            load_token<L, M, D, TIn>(in, p.f, bth_of(n * C + tau), rg, cg);
+            if constexpr (PF_TOKEN) {
+                if (tau + 1 < C) load_token<L, M, D, TIn>(nxt, p.f, bth_of(n * C + tau + 1), rg, cg);
+            } else {
+                load_token<L, M, D, TIn>(cur, p.f, bth_of(n * C + tau), rg, cg);
+            }
             float c[L::RPT], beta[L::RPT], hh;
             float4 h;
-            fwd_token_keep<L, D>(z, r, in, mode, red[nred & 1], lane, wave, cg, c, beta, h, hh);
+            fwd_token_keep<L, D>(z, r, cur, mode, red[nred & 1], lane, wave, cg, c, beta, h, hh);
+            if constexpr (PF_TOKEN) cur = nxt;
             nred += mode == 0;  // only the decoding objective reduces over slots here
             float* rec = trec + static_cast<int64_t>(tau) * TR::SIZE;
             if (cg == 0) {
@@ -221,34 +268,53 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
         float4 dZ[L::RPT];
 #pragma unroll
         for (int i = 0; i < L::RPT; ++i) dZ[i] = f4(0.f);
-        for (int tau = C - 1; tau >= 0; --tau) {
-            const int t = n * C + tau;
-            const int64_t bth = bth_of(t);
-            TokenIn<L::RPT> in;
-            load_token<L, M, D, TIn>(in, p.f, bth, rg, cg);
-            const float* rec = trec + static_cast<int64_t>(tau) * TR::SIZE;
-            float c[L::RPT], beta[L::RPT];
+        // The state after the chunk's last token is the next chunk's stored start;
+        // the state before token tau is the state after token tau - 1.
+        float4 rpost[L::RPT];
+        if constexpr (PF_STATE) {
+            const float* s1 = sck + static_cast<int64_t>(n + 1) * M * D;
 #pragma unroll
-            for (int i = 0; i < L::RPT; ++i) {
-                c[i] = rec[TR::C_OFF + rg + L::RG * i];
-                beta[i] = rec[TR::B_OFF + rg + L::RG * i];
+            for (int i = 0; i < L::RPT; ++i) rpost[i] = *reinterpret_cast<const float4*>(s1 + el(i));
+        }
+        RevIn<L::RPT> rc, rn;
+        if constexpr (PF_TOKEN)
+            load_rev<L, M, D, TIn, PF_STATE>(rc, p, trec, rtok, bth_of(n * C + C - 1), C - 1, rg, cg, el(0));
+        for (int tau = C - 1; tau >= 0; --tau) {
+            const int64_t bth = bth_of(n * C + tau);
+            if constexpr (PF_TOKEN) {
+                if (tau > 0)
+                    load_rev<L, M, D, TIn, PF_STATE>(rn, p, trec, rtok, bth_of(n * C + tau - 1), tau - 1, rg, cg, el(0));
+            } else {
+                load_rev<L, M, D, TIn, false>(rc, p, trec, rtok, bth, tau, rg, cg, el(0));
             }
-            const float4 h = *reinterpret_cast<const float4*>(rec + TR::H_OFF + cg * 4);
-            const float hh = rec[TR::HH_OFF];
-            const float4 dy = p.dy_bf16 ? ld4<uint16_t>(dyb, bth * D + cg * 4) : ld4<float>(dyp, bth * D + cg * 4);
-            // the states after and before this token (the state after the chunk's
-            // last token is the next chunk's stored start)
-            const float* rpost = tau == C - 1 ? sck + static_cast<int64_t>(n + 1) * M * D
-                                              : rtok + static_cast<int64_t>(tau + 1) * M * D;
-            const float* rpre = rtok + static_cast<int64_t>(tau) * M * D;
+            const TokenIn<L::RPT>& in = rc.in;
+            const float* c = rc.c;
+            const float* beta = rc.beta;
+            const float4 h = rc.h;
+            const float hh = rc.hh;
+            const float4 dy = rc.dy;
+            float4 rp[L::RPT];
+            if constexpr (PF_STATE) {
+#pragma unroll
+                for (int i = 0; i < L::RPT; ++i) rp[i] = rc.rp[i];
+            } else {
+                const float* rpre = rtok + static_cast<int64_t>(tau) * M * D;
+                const float* rnext = tau == C - 1 ? sck + static_cast<int64_t>(n + 1) * M * D
+                                                  : rtok + static_cast<int64_t>(tau + 1) * M * D;
+#pragma unroll
+                for (int i = 0; i < L::RPT; ++i) {
+                    rp[i] = *reinterpret_cast<const float4*>(rpre + el(i));
+                    rpost[i] = *reinterpret_cast<const float4*>(rnext + el(i));
+                }
+            }
 
             // reductions over d: dq, dg, dkap
             float dq[L::RPT], dg[L::RPT], dk2[L::RPT];
 #pragma unroll
             for (int i = 0; i < L::RPT; ++i) {
-                dq[i] = dot4(*reinterpret_cast<const float4*>(rpost + el(i)), dy);
+                dq[i] = dot4(rpost[i], dy);
                 dR[i] = fma4(in.q[i], dy, dR[i]);
-                dg[i] = dot4(*reinterpret_cast<const float4*>(rpre + el(i)), dR[i]);
+                dg[i] = dot4(rp[i], dR[i]);
                 dk2[i] = dot4(h, dR[i]);
             }
 #pragma unroll
@@ -317,7 +383,10 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                 for (int i = 0; i < L::RPT; ++i) dkz[i] = group_sum<L::TPR>(dkz[i]);
             }
 #pragma unroll
-            for (int i = 0; i < L::RPT; ++i) dR[i] = gate[i] * dR[i];
+            for (int i = 0; i < L::RPT; ++i) {
+                dR[i] = gate[i] * dR[i];
+                if constexpr (PF_STATE) rpost[i] = rp[i];
+            }
 
             // stores
             if (cg == 0) {
@@ -337,6 +406,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                 const float4 dv = mode == 2 ? dh : f4(0.f) - dh;
                 *reinterpret_cast<float4*>(p.dv + bth * D + cg * 4) = dv;
             }
+            if constexpr (PF_TOKEN) rc = rn;
         }
 
         // gradient of Z (running path + frozen uses) back through the projection
@@ -357,6 +427,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
 template <int M, int D>
 static int launch_bwd_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
     constexpr int TPR = D / 4;
+    // 512 threads (1024 at m = d = 128, where 512 would need 8 slot rows per
+    // thread and spill).
     constexpr int NT = (M * TPR < 512) ? M * TPR : 512;
     const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H));
     if (in_bf16)
