@@ -119,32 +119,81 @@ __device__ __forceinline__ float dot4(float4 a, float4 b) {
 }
 
 // ---------------------------------------------------------- reductions ----
+// Cross-lane moves on the vector ALU: DPP inside 16-lane rows, and the gfx950
+// row swaps across rows (no LDS round trip, unlike a shuffle through
+// ds_bpermute).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_1032 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_MIRROR = 0x140;   // lane i <- lane 15 - i of its row
+constexpr int DPP_HALF_MIRROR = 0x141;  // lane i <- lane 7 - i of its half row
+constexpr int DPP_ROW_ROR = 0x120;      // + n: lane i <- lane (i + n) % 16 of its row
+
+// Value of the same lane column in the even and in the odd row of the lane's
+// row pair (rows 0/1, 2/3), and in the lower and upper half of the wave.
+__device__ __forceinline__ void row_pair_values(float x, float& even, float& odd) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    even = __uint_as_float(r[0]);
+    odd = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void wave_half_values(float x, float& lo, float& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+
 // Sum over groups of G consecutive lanes of a wave64 (G a power of two <= 64);
 // every lane of the group receives the sum.
 template <int G>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "power of two");
+    if constexpr (G >= 2) x += dpp_mov<DPP_QUAD_1032>(x);
+    if constexpr (G >= 4) x += dpp_mov<DPP_QUAD_2301>(x);
+    if constexpr (G >= 8) x += dpp_mov<DPP_HALF_MIRROR>(x);
+    if constexpr (G >= 16) x += dpp_mov<DPP_ROW_MIRROR>(x);
+    if constexpr (G >= 32) {
+        float e, o;
+        row_pair_values(x, e, o);
+        x = e + o;
+    }
+    if constexpr (G >= 64) {
+        float lo, hi;
+        wave_half_values(x, lo, hi);
+        x = lo + hi;
+    }
     return x;
 }
 
 // Sum over each row of 16 lanes (lanes 16r .. 16r+15) with DPP row
 // rotations; every lane of the row receives the sum.
 __device__ __forceinline__ float row16_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror:8
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror:4
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));  // row_ror:2
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));  // row_ror:1
+    x += dpp_mov<DPP_ROW_ROR + 8>(x);
+    x += dpp_mov<DPP_ROW_ROR + 4>(x);
+    x += dpp_mov<DPP_ROW_ROR + 2>(x);
+    x += dpp_mov<DPP_ROW_ROR + 1>(x);
     return x;
 }
 
-// Sum over lanes that share (lane % S), S a power of two < 64: butterfly over
-// the lane bits >= log2(S).  Every lane receives the sum of its class.
+// Sum over lanes that share (lane % S), S a power of two < 64.  Every lane
+// receives the sum of its class.
 template <int S>
 __device__ __forceinline__ float strided_sum(float x) {
-#pragma unroll
-    for (int off = S; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-    return x;
+    static_assert(S >= 1 && S < 64 && (S & (S - 1)) == 0, "power of two below 64");
+    if constexpr (S <= 8) x += dpp_mov<DPP_ROW_ROR + 8>(x);
+    if constexpr (S <= 4) x += dpp_mov<DPP_ROW_ROR + 4>(x);
+    if constexpr (S <= 2) x += dpp_mov<DPP_ROW_ROR + 2>(x);
+    if constexpr (S <= 1) x += dpp_mov<DPP_ROW_ROR + 1>(x);
+    if constexpr (S <= 16) {
+        float e, o;
+        row_pair_values(x, e, o);
+        x = e + o;
+    }
+    float lo, hi;
+    wave_half_values(x, lo, hi);
+    return lo + hi;
 }
 
 }  // namespace osr

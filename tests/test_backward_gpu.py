@@ -9,9 +9,10 @@ RMS of the oracle's gradient at most 1e-4 for fp32 inputs and 2e-2 for bf16
 inputs.  Small shapes are compared in full; at the workload sizes the oracle
 recomputes a sample of whole (batch, head) sequences (sequences are
 independent, so their gradients are too).  The encoding layer's gradient
-amplifies rounding-size perturbations, so it is compared element by element
-over short sequences, and at 1024 tokens through a property that holds at
-any length.
+amplifies rounding-size perturbations: it is compared element by element over
+16 tokens against a bar derived from the oracle's own sensitivity to such
+perturbations, and at 1024 tokens through a property that holds at any
+length.
 """
 import concurrent.futures as cf
 import sys
@@ -116,17 +117,35 @@ def test_bwd_tiny_fp32(mode, C, per_slot):
     _check(inp, _gpu_bwd(inp, dy, dso, C, mode), _oracle(inp, dy, dso, C, mode))
 
 
-@pytest.mark.parametrize("C", [1, 4, 8])
+def _conditioned_tol(inp, dy, dso, C, mode, ref):
+    """Bar for a badly conditioned gradient, derived from the oracle itself:
+    the largest relative change of any oracle gradient (max-abs over RMS)
+    when every input is perturbed by 1e-7 relative (fp32 rounding size),
+    times 20 for the many roundings of an fp32 evaluation; never below the
+    standard bar."""
+    a = list(inp.values_f64())
+    rng = np.random.default_rng(99)
+    a2 = [x * (1 + 1e-7 * rng.standard_normal(x.shape)) for x in a]
+    g2 = ob.osr_backward(*a2, dy, dso, chunk_size=C, mode=mode)
+    sens = max(_rel(g2[k], ref[k]) for k in KEYS)
+    tol = max(TOL[inp.in_dtype], 20.0 * sens)
+    _say(f"  oracle sensitivity {sens:.2e} -> bar {tol:.2e}")
+    return tol
+
+
+@pytest.mark.parametrize("C", [1, 4, 16])
 @pytest.mark.parametrize("per_slot", [True, False])
 def test_bwd_encoding_layer_short_fp32(C, per_slot):
     """The encoding layer's gradient amplifies rounding-size perturbations
     (in the fp64 oracle a 1e-7 relative change of the inputs moves it by
-    up to 1e-3 of its RMS at 16 tokens and by O(1) at 64), so it is compared
-    element by element over 8 tokens only."""
-    _say(f"bwd encoding layer fp32 B1 H2 T8 m16 d32 C{C} per_slot{per_slot}")
-    inp = synth.make_inputs(1, 8, 2, 16, 32, seed=11, in_dtype=synth.F32, gamma_per_slot=per_slot)
+    1e-5 - 1e-3 of its RMS at 8 - 32 tokens and by up to O(1) at 64), so it
+    is compared over 16 tokens against a bar derived from that sensitivity."""
+    _say(f"bwd encoding layer fp32 B1 H2 T16 m16 d32 C{C} per_slot{per_slot}")
+    inp = synth.make_inputs(1, 16, 2, 16, 32, seed=11, in_dtype=synth.F32, gamma_per_slot=per_slot)
     dy, dso = _upstream(inp, 11)
-    _check(inp, _gpu_bwd(inp, dy, dso, C, osr.MODE_ENC), _oracle(inp, dy, dso, C, osr.MODE_ENC))
+    ref = _oracle(inp, dy, dso, C, osr.MODE_ENC)
+    tol = _conditioned_tol(inp, dy, dso, C, osr.MODE_ENC, ref)
+    _check(inp, _gpu_bwd(inp, dy, dso, C, osr.MODE_ENC), ref, tol=tol)
 
 
 @pytest.mark.parametrize("m,d", [(16, 16), (32, 64), (64, 64), (64, 128), (128, 32), (128, 128)])
@@ -143,7 +162,9 @@ def test_bwd_other_objectives_bf16(mode, T):
     _say(f"bwd bf16 B2 H3 T{T} m64 d64 C16 mode{mode}")
     inp = synth.make_inputs(2, T, 3, 64, 64, seed=13, in_dtype=synth.BF16)
     dy, dso = _upstream(inp, 13)
-    _check(inp, _gpu_bwd(inp, dy, dso, 16, mode), _oracle(inp, dy, dso, 16, mode))
+    ref = _oracle(inp, dy, dso, 16, mode)
+    tol = _conditioned_tol(inp, dy, dso, 16, mode, ref) if mode == osr.MODE_ENC else None
+    _check(inp, _gpu_bwd(inp, dy, dso, 16, mode), ref, tol=tol)
 
 
 @pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM, osr.MODE_ENC])
