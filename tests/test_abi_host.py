@@ -194,11 +194,11 @@ def _bwd_call(d, ptrs, chunk, ws=None, ws_bytes=None):
 
 
 def test_bwd_workspace_formula():
-    """Per (b,h): 4 (T/C + 1 + C) m d bytes of states and 4 C (2m + d + 4)
+    """Per (b,h): 4 (T/C + 1 + C) m d bytes of states and 4 C (2m + 4)
     bytes of per-token values."""
     for (B, T, H, m, dd, C) in ((4, 2048, 8, 64, 64, 64), (1, 64, 1, 16, 32, 1), (2, 512, 3, 128, 128, 128)):
         d = osr.make_desc(B, T, H, m, dd)
-        per = 4 * ((T // C + 1 + C) * m * dd + C * (2 * m + dd + 4))
+        per = 4 * ((T // C + 1 + C) * m * dd + C * (2 * m + 4))
         assert osr.lattice_osr_bwd_workspace_bytes(d, C) == B * H * per
 
 
