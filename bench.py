@@ -71,7 +71,8 @@ def chain_reference_ms(w: dict, chunk: int) -> float:
 
 # Sources of the backward kernel: not part of the forward and decode kernels
 # whose traffic counters are keyed by the hash below.
-BWD_SOURCES = ("osr_bwd.hip",)
+BWD_SOURCES = ("osr_bwd.hip", "osr_bwd_kernel.h", "osr_bwd_m16.hip", "osr_bwd_m32.hip", "osr_bwd_m64.hip",
+               "osr_bwd_m128.hip")
 
 
 def source_hash() -> str:

@@ -161,13 +161,12 @@ int check_bwd_buffers(const lattice_osr_desc* d, const void* q, const void* k, c
     return LATTICE_OSR_OK;
 }
 
-// Shape rules of the backward: those of the chunked forward, with the default
-// linearisation only.
+// Shape rules of the backward: those of the chunked forward.
 int check_bwd_desc(const lattice_osr_desc* d, int C) {
     int rc = check_desc(d);
     if (rc) return rc;
     if (C <= 0 || d->T % C != 0) return LATTICE_OSR_ERR_SHAPE;
-    if (!pow2_chunk(C) || d->linearisation != LATTICE_OSR_LIN2) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (!pow2_chunk(C)) return LATTICE_OSR_ERR_UNSUPPORTED;
     return LATTICE_OSR_OK;
 }
 

@@ -1,530 +1,16 @@
-// osr_bwd.hip -- backward of the chunk-wise OSR forward on gfx950 (fp32 VALU).
-//
-// Method: "Lattice: Learning to Efficiently Compress the Memory" (arXiv
-// 2504.05646).  The layer is trained through its chunk-wise form (section
-// "Parallel and Hardware Efficient Form", eq. recurrence_linear2); this kernel
-// returns the vector-Jacobian product of that forward at chunk size C (exact
-// recurrence at C = 1): given dy and the gradient of the returned state, the
-// gradients of q, k, v, gamma, mu and the initial state.
-//
-// Forward per token t of a chunk (Z = unit-projected chunk-start state, R the
-// running state, rows = slots):
-//   h = sum_i k_i z_i - v | -v | v      c_i = z_i . h      hh = |h|^2
-//   a_i = gamma_i k_i (encoding layer: gamma_i (c_i - k_i))
-//   w_i = max(hh - c_i^2, 0)            beta_i = (mu^2 + a_i^2 w_i)^(-1/2)
-//   g_i = beta_i (mu + a_i c_i)         kap_i = -beta_i a_i
-//   r_i <- g_i r_i + kap_i h            y = sum_i q_i r_i
-// Reverse of one token, with D the gradient of the state after the token:
-//   dq_i = r_i . dy;  D_i += q_i dy
-//   dg_i = r_prev_i . D_i;  dkap_i = h . D_i
-//   (beta, a, c, mu) from (dg, dkap) by the chain rule through g and kap,
-//   then through beta = (mu^2 + a^2 w)^(-1/2) and w (only where w > 0)
-//   dh = sum_i (kap_i D_i + dc_i z_i) + 2 h dhh
-//   dZ_i += dc_i h (+ k_i dh, decoding objective: dk_i += z_i . dh)
-//   dv = -dh (decoding, similarity) or dh (encoding layer)
-//   D_i <- g_i D_i  (the gradient of the state before the token)
-// At the chunk start dZ + D (the gradient of Z) goes back through the
-// projection onto the sphere: dS_i = (dz_i - z_i (z_i . dz_i)) / |s_i|.
-//
-// Inside a chunk neither h (it depends on Z and the inputs only) nor any of the
-// reverse walk's sums over slots feeds back into the state recurrence, which
-// is elementwise per slot.  So the sums over slots, the only reductions that
-// cross waves, are batched: h for a batch of BT tokens in one LDS exchange, and
-// in the reverse walk the per-token partials of dh (with d|h|^2, dmu and a
-// per-token dgamma) for BT tokens in another.  The per-token steps in between
-// reduce only over d, inside a row group (DPP).
-//
-// One workgroup per (b,h), state in registers in the layout of osr_valu.h.
-// Phase 1 runs the forward and keeps every chunk-start state (before
-// projection) in the workspace.  Phase 2 walks the chunks backwards: it forms
-// the chunk's h in LDS, runs the chunk forward again from its stored start
-// (keeping the state before each token and the per-token c, beta, |h|^2 in the
-// workspace), then walks the chunk's tokens backwards.
+// osr_bwd.hip -- dispatch and workspace size of the backward of the chunk-wise
+// OSR forward (kernels: osr_bwd_kernel.h, instantiated per slot count in
+// osr_bwd_m<M>.hip).
 #include "osr_launch.h"
-#include "osr_valu.h"
 
 namespace osr {
 
-// Per-token record kept for the reverse walk: c[M], beta[M], |h|^2, pad.
-template <int M, int D>
-struct TokRec {
-    static constexpr int C_OFF = 0, B_OFF = M, HH_OFF = 2 * M;
-    static constexpr int SIZE = 2 * M + 4;
-};
-
-template <int M, int D>
-__host__ __device__ inline int64_t bwd_floats_per_bh(int T, int C) {
-    return (static_cast<int64_t>(T / C) + 1 + C) * M * D + static_cast<int64_t>(C) * TokRec<M, D>::SIZE;
-}
-
-constexpr int BWD_CMAX = 128;  // largest chunk size (the chunk's h is held in LDS)
-
-// Tokens per batched exchange over slots: the reverse walk keeps 3 values per
-// slot row and token of a batch in registers.
-template <class L>
-struct BwdBatch {
-    static constexpr int BT = L::RPT <= 2 ? 8 : (L::RPT <= 4 ? 4 : 2);
-};
-
-// h of every token of the chunk [t0, t0 + C) into hbuf[C][D] (fp32), from the
-// projected chunk-start state z.  Decoding objective: h = sum_i k_i z_i - v,
-// the sum over slots exchanged through red once per BT tokens; otherwise -v
-// or v.  Ends with a barrier (hbuf visible to all threads).
-template <class L, int M, int D, typename TIn>
-__device__ __forceinline__ void chunk_h(const float4 (&z)[L::RPT], const Params& f, int64_t bth0,
-                                        int64_t tstride, int C, int mode, float* hbuf, float* red,
-                                        int& nred, int tid, int lane, int wave, int rg, int cg) {
-    constexpr int BT = BwdBatch<L>::BT, W = D + 4, Q = D / 4;
-    static_assert(BT * Q <= L::NW * 64, "one output float4 per thread");
-    const TIn* kp = static_cast<const TIn*>(f.k);
-    const TIn* vp = static_cast<const TIn*>(f.v);
-    if (mode != 0) {
-        const float sgn = mode == 2 ? 1.f : -1.f;
-        for (int idx = tid; idx < C * Q; idx += L::NW * 64) {
-            const int u = idx / Q, c4 = idx % Q;
-            *reinterpret_cast<float4*>(hbuf + u * D + c4 * 4) = sgn * ld4<TIn>(vp, (bth0 + u * tstride) * D + c4 * 4);
-        }
-        __syncthreads();
-        return;
-    }
-    const int nb = C < BT ? C : BT;
-    for (int u0 = 0; u0 < C; u0 += nb) {
-        float* rb = red + (nred++ & 1) * (BT * L::NW * W);
-#pragma unroll
-        for (int u = 0; u < BT; ++u) {
-            if (u < nb) {
-                const int64_t bth = bth0 + (u0 + u) * tstride;
-                float4 hp = f4(0.f);
-#pragma unroll
-                for (int i = 0; i < L::RPT; ++i) hp = fma4(ld<TIn>(kp, bth * M + rg + L::RG * i), z[i], hp);
-                hp.x = strided_sum<L::TPR>(hp.x);
-                hp.y = strided_sum<L::TPR>(hp.y);
-                hp.z = strided_sum<L::TPR>(hp.z);
-                hp.w = strided_sum<L::TPR>(hp.w);
-                if (lane < L::TPR) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + cg * 4) = hp;
-            }
-        }
-        __syncthreads();
-        if (tid < nb * Q) {
-            const int u = tid / Q, c4 = tid % Q;
-            float4 acc = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + c4 * 4);
-#pragma unroll
-            for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + c4 * 4);
-            const float4 v = ld4<TIn>(vp, (bth0 + (u0 + u) * tstride) * D + c4 * 4);
-            *reinterpret_cast<float4*>(hbuf + (u0 + u) * D + c4 * 4) = acc - v;
-        }
-    }
-    __syncthreads();
-}
-
-// One forward token given its h: updates r, returns the per-slot c and beta
-// and |h|^2 (valid in every thread of a row group).  No cross-wave exchange.
-template <class L>
-__device__ __forceinline__ void fwd_token_h(const float4 (&z)[L::RPT], float4 (&r)[L::RPT], const float (&k)[L::RPT],
-                                            const float (&g)[L::RPT], float mu, float4 h, int mode,
-                                            float (&c)[L::RPT], float (&beta)[L::RPT], float& hh) {
-    float cc[L::RPT + 1];
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) cc[i] = dot4(z[i], h);
-    cc[L::RPT] = dot4(h, h);
-#pragma unroll
-    for (int i = 0; i <= L::RPT; ++i) cc[i] = group_sum<L::TPR>(cc[i]);
-    hh = cc[L::RPT];
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) {
-        const float a = g[i] * (mode == 2 ? cc[i] - k[i] : k[i]);
-        const float w = fmaxf(fmaf(-cc[i], cc[i], hh), 0.f);
-        const float b = rsqrtf(fmaf(mu, mu, a * a * w));
-        r[i] = fma4(b * fmaf(a, cc[i], mu), r[i], (-b * a) * h);
-        c[i] = cc[i];
-        beta[i] = b;
-    }
-}
-
-// k, gamma (per slot row of this thread) and mu of one token.
-template <class L, int M, typename TIn>
-__device__ __forceinline__ void load_kgm(const Params& f, int64_t bth, int rg, float (&k)[L::RPT],
-                                         float (&g)[L::RPT], float& mu) {
-    const TIn* kp = static_cast<const TIn*>(f.k);
-    const TIn* gp = static_cast<const TIn*>(f.gamma);
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) {
-        const int row = rg + L::RG * i;
-        k[i] = ld<TIn>(kp, bth * M + row);
-        g[i] = f.gamma_per_slot ? ld<TIn>(gp, bth * M + row) : ld<TIn>(gp, bth);
-    }
-    mu = ld<TIn>(static_cast<const TIn*>(f.mu), bth);
-}
-
-// What the reverse walk reads for one token besides h: its inputs, its
-// record, dy and (PF_STATE) the state before it.
-template <int RPT>
-struct RevIn {
-    TokenIn<RPT> in;
-    float c[RPT], beta[RPT];
-    float hh;
-    float4 dy;
-    float4 rp[RPT];
-};
-
-template <class L, int M, int D, typename TIn, bool PF_STATE>
-__device__ __forceinline__ void load_rev(RevIn<L::RPT>& x, const BwdParams& p, const float* trec,
-                                         const float* rtok, int64_t bth, int tau, int rg, int cg, int el0) {
-    using TR = TokRec<M, D>;
-    load_token<L, M, D, TIn>(x.in, p.f, bth, rg, cg);
-    const float* rec = trec + static_cast<int64_t>(tau) * TR::SIZE;
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) {
-        x.c[i] = rec[TR::C_OFF + rg + L::RG * i];
-        x.beta[i] = rec[TR::B_OFF + rg + L::RG * i];
-    }
-    x.hh = rec[TR::HH_OFF];
-    x.dy = p.dy_bf16 ? ld4<uint16_t>(static_cast<const uint16_t*>(p.dy), bth * D + cg * 4)
-                     : ld4<float>(static_cast<const float*>(p.dy), bth * D + cg * 4);
-    if constexpr (PF_STATE) {
-        const float* rpre = rtok + static_cast<int64_t>(tau) * M * D;
-#pragma unroll
-        for (int i = 0; i < L::RPT; ++i)
-            x.rp[i] = *reinterpret_cast<const float4*>(rpre + el0 + i * L::RG * D);
-    }
-}
-
-template <int M, int D, int NT, typename TIn>
-__global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
-    using L = ValuLayout<M, D, NT>;
-    using TR = TokRec<M, D>;
-    constexpr int BT = BwdBatch<L>::BT, W = D + 4;
-    // The reverse walk loads the next token's inputs and record while it works on
-    // the current one, and the state before it too, where registers allow.
-    constexpr bool PF_TOKEN = L::RPT <= 4;
-    constexpr bool PF_STATE = L::RPT <= 2;
-    __shared__ __attribute__((aligned(16))) float hbuf[BWD_CMAX * D];
-    __shared__ __attribute__((aligned(16))) float red[2 * BT * L::NW * W];
-    const int bh = blockIdx.x;
-    const int b = bh / p.f.H, hd = bh % p.f.H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cg = tid % L::TPR, rg = tid / L::TPR;
-    const int T = p.f.T, C = p.f.chunk, NC = T / C;
-    const int mode = p.f.mode;
-    const int64_t tstride = p.f.H;  // consecutive tokens of one (b,h) are H rows apart
-
-    float* ws = p.ws + static_cast<int64_t>(bh) * bwd_floats_per_bh<M, D>(T, C);
-    float* sck = ws;                                          // [NC+1][M][D]
-    float* rtok = sck + static_cast<int64_t>(NC + 1) * M * D;  // [C][M][D]
-    float* trec = rtok + static_cast<int64_t>(C) * M * D;      // [C][TR::SIZE]
-    auto el = [&](int i) { return (rg + L::RG * i) * D + cg * 4; };  // this thread's state elements
-    auto bth_of = [&](int t) { return (static_cast<int64_t>(b) * T + t) * p.f.H + hd; };
-    int nred = 0;  // LDS exchanges so far: consecutive ones use alternate halves of red
-
-    // ---- phase 1: forward, keeping every chunk-start state ----
-    float4 r[L::RPT], z[L::RPT];
-    const float* sin = p.f.state_in + static_cast<int64_t>(bh) * M * D;
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) r[i] = *reinterpret_cast<const float4*>(sin + el(i));
-    for (int n = 0; n < NC; ++n) {
-#pragma unroll
-        for (int i = 0; i < L::RPT; ++i) *reinterpret_cast<float4*>(sck + static_cast<int64_t>(n) * M * D + el(i)) = r[i];
-        project_rows<L>(r);
-#pragma unroll
-        for (int i = 0; i < L::RPT; ++i) z[i] = r[i];
-        __syncthreads();  // every thread is done with the previous chunk's hbuf
-        chunk_h<L, M, D, TIn>(z, p.f, bth_of(n * C), tstride, C, mode, hbuf, red, nred, tid, lane, wave, rg, cg);
-        float kc[L::RPT], gc[L::RPT], muc, kn[L::RPT], gn[L::RPT], mun;
-        load_kgm<L, M, TIn>(p.f, bth_of(n * C), rg, kc, gc, muc);
-        for (int tau = 0; tau < C; ++tau) {
-            if (tau + 1 < C) load_kgm<L, M, TIn>(p.f, bth_of(n * C + tau + 1), rg, kn, gn, mun);
-            const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
-            float c[L::RPT], beta[L::RPT], hh;
-            fwd_token_h<L>(z, r, kc, gc, muc, h, mode, c, beta, hh);
-#pragma unroll
-            for (int i = 0; i < L::RPT; ++i) {
-                kc[i] = kn[i];
-                gc[i] = gn[i];
-            }
-            muc = mun;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) *reinterpret_cast<float4*>(sck + static_cast<int64_t>(NC) * M * D + el(i)) = r[i];
-
-    // ---- the returned state is the end state projected: its backward ----
-    float4 dR[L::RPT];
-    {
-        const float* dso = p.dstate_out + static_cast<int64_t>(bh) * M * D;
-        float n2[L::RPT], pr[L::RPT];
-        float4 o[L::RPT];
-#pragma unroll
-        for (int i = 0; i < L::RPT; ++i) {
-            dR[i] = *reinterpret_cast<const float4*>(dso + el(i));
-            n2[i] = group_sum<L::TPR>(dot4(r[i], r[i]));
-            o[i] = rsqrtf(n2[i]) * r[i];
-            pr[i] = group_sum<L::TPR>(dot4(o[i], dR[i]));
-        }
-#pragma unroll
-        for (int i = 0; i < L::RPT; ++i) dR[i] = rsqrtf(n2[i]) * fma4(-pr[i], o[i], dR[i]);
-    }
-
-    // ---- phase 2: chunks in reverse ----
-    for (int n = NC - 1; n >= 0; --n) {
-        float inv[L::RPT];
-        {
-            const float* s0 = sck + static_cast<int64_t>(n) * M * D;
-#pragma unroll
-            for (int i = 0; i < L::RPT; ++i) {
-                r[i] = *reinterpret_cast<const float4*>(s0 + el(i));
-                inv[i] = rsqrtf(group_sum<L::TPR>(dot4(r[i], r[i])));
-                r[i] = inv[i] * r[i];
-                z[i] = r[i];
-            }
-        }
-        __syncthreads();  // the previous chunk's reverse walk is done with hbuf, red and the records
-        chunk_h<L, M, D, TIn>(z, p.f, bth_of(n * C), tstride, C, mode, hbuf, red, nred, tid, lane, wave, rg, cg);
-
-        // forward again over the chunk, keeping what the reverse walk needs
-        {
-            float kc[L::RPT], gc[L::RPT], muc, kn[L::RPT], gn[L::RPT], mun;
-            load_kgm<L, M, TIn>(p.f, bth_of(n * C), rg, kc, gc, muc);
-            for (int tau = 0; tau < C; ++tau) {
-#pragma unroll
-                for (int i = 0; i < L::RPT; ++i)
-                    *reinterpret_cast<float4*>(rtok + static_cast<int64_t>(tau) * M * D + el(i)) = r[i];
-                if (tau + 1 < C) load_kgm<L, M, TIn>(p.f, bth_of(n * C + tau + 1), rg, kn, gn, mun);
-                const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
-                float c[L::RPT], beta[L::RPT], hh;
-                fwd_token_h<L>(z, r, kc, gc, muc, h, mode, c, beta, hh);
-                float* rec = trec + static_cast<int64_t>(tau) * TR::SIZE;
-                if (cg == 0) {
-#pragma unroll
-                    for (int i = 0; i < L::RPT; ++i) {
-                        rec[TR::C_OFF + rg + L::RG * i] = c[i];
-                        rec[TR::B_OFF + rg + L::RG * i] = beta[i];
-                    }
-                }
-                if (tid == 0) rec[TR::HH_OFF] = hh;
-#pragma unroll
-                for (int i = 0; i < L::RPT; ++i) {
-                    kc[i] = kn[i];
-                    gc[i] = gn[i];
-                }
-                muc = mun;
-            }
-        }
-        __syncthreads();  // records visible to every thread
-
-        // reverse walk, BT tokens per exchange over slots
-        float4 dZ[L::RPT];
-#pragma unroll
-        for (int i = 0; i < L::RPT; ++i) dZ[i] = f4(0.f);
-        const int nb = C < BT ? C : BT;
-        // the state after the chunk's last token is the next chunk's stored start;
-        // the state after token tau - 1 is the state before token tau
-        float4 rpost[L::RPT];
-        if constexpr (PF_STATE) {
-            const float* s1 = sck + static_cast<int64_t>(n + 1) * M * D;
-#pragma unroll
-            for (int i = 0; i < L::RPT; ++i) rpost[i] = *reinterpret_cast<const float4*>(s1 + el(i));
-        }
-        RevIn<L::RPT> rc, rn;
-        if constexpr (PF_TOKEN)
-            load_rev<L, M, D, TIn, PF_STATE>(rc, p, trec, rtok, bth_of(n * C + C - 1), C - 1, rg, cg, el(0));
-        for (int ub = C - nb; ub >= 0; ub -= nb) {
-            float* rb = red + (nred++ & 1) * (BT * L::NW * W);
-            float dcv[BT][L::RPT], kv[BT][L::RPT], dkin[BT][L::RPT];
-#pragma unroll
-            for (int u = BT - 1; u >= 0; --u) {
-                if (u < nb) {
-                    const int tau = ub + u;
-                    const int64_t bth = bth_of(n * C + tau);
-                    if constexpr (PF_TOKEN) {
-                        if (tau > 0)
-                            load_rev<L, M, D, TIn, PF_STATE>(rn, p, trec, rtok, bth_of(n * C + tau - 1), tau - 1, rg,
-                                                             cg, el(0));
-                    } else {
-                        load_rev<L, M, D, TIn, false>(rc, p, trec, rtok, bth, tau, rg, cg, el(0));
-                    }
-                    const TokenIn<L::RPT>& in = rc.in;
-                    const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
-                    const float hh = rc.hh;
-                    const float4 dy = rc.dy;
-                    float4 rp[L::RPT];
-                    if constexpr (PF_STATE) {
-#pragma unroll
-                        for (int i = 0; i < L::RPT; ++i) rp[i] = rc.rp[i];
-                    } else {
-                        const float* rpre = rtok + static_cast<int64_t>(tau) * M * D;
-                        const float* rnext = tau == C - 1 ? sck + static_cast<int64_t>(n + 1) * M * D
-                                                          : rtok + static_cast<int64_t>(tau + 1) * M * D;
-#pragma unroll
-                        for (int i = 0; i < L::RPT; ++i) {
-                            rp[i] = *reinterpret_cast<const float4*>(rpre + el(i));
-                            rpost[i] = *reinterpret_cast<const float4*>(rnext + el(i));
-                        }
-                    }
-
-                    // reductions over d: dq, dg, dkap
-                    float dq[L::RPT], dg[L::RPT], dk2[L::RPT];
-#pragma unroll
-                    for (int i = 0; i < L::RPT; ++i) {
-                        dq[i] = dot4(rpost[i], dy);
-                        dR[i] = fma4(in.q[i], dy, dR[i]);
-                        dg[i] = dot4(rp[i], dR[i]);
-                        dk2[i] = dot4(h, dR[i]);
-                    }
-#pragma unroll
-                    for (int i = 0; i < L::RPT; ++i) {
-                        dq[i] = group_sum<L::TPR>(dq[i]);
-                        dg[i] = group_sum<L::TPR>(dg[i]);
-                        dk2[i] = group_sum<L::TPR>(dk2[i]);
-                    }
-
-                    // scalar chain rule per slot
-                    const float mu = in.mu;
-                    float gate[L::RPT], dgam[L::RPT];
-                    float4 hp = f4(0.f);
-                    float4 sc = f4(0.f);  // (d|h|^2, dmu, dgamma summed over slots, 0)
-#pragma unroll
-                    for (int i = 0; i < L::RPT; ++i) {
-                        const float ci = rc.c[i];
-                        const float bt = rc.beta[i];
-                        const float coef = mode == 2 ? ci - in.k[i] : in.k[i];
-                        const float a = in.g[i] * coef;
-                        const float wraw = fmaf(-ci, ci, hh);
-                        const float w = fmaxf(wraw, 0.f);
-                        const float num = fmaf(a, ci, mu);
-                        gate[i] = bt * num;
-                        const float kap = -bt * a;
-                        const float dbeta = num * dg[i] - a * dk2[i];
-                        float da = bt * (ci * dg[i] - dk2[i]);
-                        float dmu_i = bt * dg[i];
-                        float dci = bt * a * dg[i];
-                        const float tb = -0.5f * bt * bt * bt * dbeta;
-                        dmu_i = fmaf(2.f * mu, tb, dmu_i);
-                        da = fmaf(2.f * a * w, tb, da);
-                        const float dw = a * a * tb;
-                        float dhh_i = 0.f;
-                        if (wraw > 0.f) {
-                            dhh_i = dw;
-                            dci = fmaf(-2.f * ci, dw, dci);
-                        }
-                        if (mode == 2) {
-                            dci = fmaf(in.g[i], da, dci);
-                            dkin[u][i] = -in.g[i] * da;
-                            dgam[i] = coef * da;
-                        } else {
-                            dkin[u][i] = in.g[i] * da;
-                            dgam[i] = in.k[i] * da;
-                        }
-                        dcv[u][i] = dci;
-                        kv[u][i] = in.k[i];
-                        hp = fma4(kap, dR[i], fma4(dci, z[i], hp));
-                        sc.x += dhh_i;
-                        sc.y += dmu_i;
-                        sc.z += dgam[i];
-                    }
-                    // this token's partial sums over the wave's slots, to LDS
-                    hp.x = strided_sum<L::TPR>(hp.x);
-                    hp.y = strided_sum<L::TPR>(hp.y);
-                    hp.z = strided_sum<L::TPR>(hp.z);
-                    hp.w = strided_sum<L::TPR>(hp.w);
-                    sc.x = strided_sum<L::TPR>(sc.x);
-                    sc.y = strided_sum<L::TPR>(sc.y);
-                    sc.z = strided_sum<L::TPR>(sc.z);
-                    if (lane < L::TPR) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + cg * 4) = hp;
-                    if (lane == 0) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + D) = sc;
-#pragma unroll
-                    for (int i = 0; i < L::RPT; ++i) {
-                        dR[i] = gate[i] * dR[i];
-                        if constexpr (PF_STATE) rpost[i] = rp[i];
-                    }
-                    if constexpr (PF_TOKEN) rc = rn;
-                    if (cg == 0) {
-#pragma unroll
-                        for (int i = 0; i < L::RPT; ++i) {
-                            const int64_t o = bth * M + rg + L::RG * i;
-                            p.dq[o] = dq[i];
-                            if (p.f.gamma_per_slot) p.dgamma[o] = dgam[i];
-                        }
-                    }
-                }
-            }
-            __syncthreads();  // the batch's partial sums visible
-#pragma unroll
-            for (int u = 0; u < BT; ++u) {
-                if (u < nb) {
-                    const int tau = ub + u;
-                    const int64_t bth = bth_of(n * C + tau);
-                    float4 hsum = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + cg * 4);
-                    float4 ssum = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + D);
-#pragma unroll
-                    for (int w = 1; w < L::NW; ++w) {
-                        hsum = hsum + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + cg * 4);
-                        ssum = ssum + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + D);
-                    }
-                    const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
-                    const float4 dh = fma4(2.f * ssum.x, h, hsum);
-                    float dkz[L::RPT] = {};
-#pragma unroll
-                    for (int i = 0; i < L::RPT; ++i) {
-                        dZ[i] = fma4(dcv[u][i], h, dZ[i]);
-                        if (mode == 0) {
-                            dZ[i] = fma4(kv[u][i], dh, dZ[i]);
-                            dkz[i] = dot4(z[i], dh);
-                        }
-                    }
-                    if (mode == 0) {
-#pragma unroll
-                        for (int i = 0; i < L::RPT; ++i) dkz[i] = group_sum<L::TPR>(dkz[i]);
-                    }
-                    if (cg == 0) {
-#pragma unroll
-                        for (int i = 0; i < L::RPT; ++i) p.dk[bth * M + rg + L::RG * i] = dkin[u][i] + dkz[i];
-                    }
-                    if (tid == 0) {
-                        p.dmu[bth] = ssum.y;
-                        if (!p.f.gamma_per_slot) p.dgamma[bth] = ssum.z;
-                    }
-                    if (rg == 0) *reinterpret_cast<float4*>(p.dv + bth * D + cg * 4) = mode == 2 ? dh : f4(0.f) - dh;
-                }
-            }
-        }
-
-        // gradient of Z (running path + frozen uses) back through the projection
-#pragma unroll
-        for (int i = 0; i < L::RPT; ++i) {
-            const float4 dz = dR[i] + dZ[i];
-            const float pz = group_sum<L::TPR>(dot4(z[i], dz));
-            dR[i] = inv[i] * fma4(-pz, z[i], dz);
-        }
-    }
-
-    float* dsi = p.dstate_in + static_cast<int64_t>(bh) * M * D;
-#pragma unroll
-    for (int i = 0; i < L::RPT; ++i) *reinterpret_cast<float4*>(dsi + el(i)) = dR[i];
-}
-
-// ----------------------------------------------------------------- launch --
-template <int M, int D>
-static int launch_bwd_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
-    constexpr int TPR = D / 4;
-    constexpr int NT = (M * TPR < 512) ? M * TPR : 512;
-    const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H));
-    if (in_bf16)
-        hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, uint16_t>), grid, dim3(NT), 0, st, p);
-    else
-        hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, float>), grid, dim3(NT), 0, st, p);
-    return hipGetLastError() == hipSuccess ? 0 : -5;
-}
-
 template <int M>
-static int launch_bwd_m(int d, const BwdParams& p, bool in_bf16, hipStream_t st) {
-    switch (d) {
-        case 16: return launch_bwd_md<M, 16>(p, in_bf16, st);
-        case 32: return launch_bwd_md<M, 32>(p, in_bf16, st);
-        case 64: return launch_bwd_md<M, 64>(p, in_bf16, st);
-        case 128: return launch_bwd_md<M, 128>(p, in_bf16, st);
-        default: return -3;
-    }
-}
+int launch_bwd_m(int d, const BwdParams& p, bool in_bf16, hipStream_t st);
+extern template int launch_bwd_m<16>(int, const BwdParams&, bool, hipStream_t);
+extern template int launch_bwd_m<32>(int, const BwdParams&, bool, hipStream_t);
+extern template int launch_bwd_m<64>(int, const BwdParams&, bool, hipStream_t);
+extern template int launch_bwd_m<128>(int, const BwdParams&, bool, hipStream_t);
 
 int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st) {
     switch (m) {
@@ -536,27 +22,14 @@ int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st) {
     }
 }
 
-template <int M>
-static size_t bwd_ws_m(int d, int T, int C) {
-    switch (d) {
-        case 16: return static_cast<size_t>(bwd_floats_per_bh<M, 16>(T, C));
-        case 32: return static_cast<size_t>(bwd_floats_per_bh<M, 32>(T, C));
-        case 64: return static_cast<size_t>(bwd_floats_per_bh<M, 64>(T, C));
-        case 128: return static_cast<size_t>(bwd_floats_per_bh<M, 128>(T, C));
-        default: return 0;
-    }
+// Workspace floats per (b,h): the T/C + 1 chunk-start states, the running state
+// before each token of one chunk, and per token c, beta (m each), |h|^2 and pad.
+static size_t bwd_floats(int T, int m, int d, int C) {
+    return (static_cast<size_t>(T / C) + 1 + C) * m * d + static_cast<size_t>(C) * (2 * m + 4);
 }
 
 size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C) {
-    size_t per = 0;
-    switch (m) {
-        case 16: per = bwd_ws_m<16>(d, T, C); break;
-        case 32: per = bwd_ws_m<32>(d, T, C); break;
-        case 64: per = bwd_ws_m<64>(d, T, C); break;
-        case 128: per = bwd_ws_m<128>(d, T, C); break;
-        default: return 0;
-    }
-    return per * sizeof(float) * static_cast<size_t>(B) * static_cast<size_t>(H);
+    return bwd_floats(T, m, d, C) * sizeof(float) * static_cast<size_t>(B) * static_cast<size_t>(H);
 }
 
 }  // namespace osr

@@ -191,14 +191,14 @@ def lattice_osr_bwd_workspace_bytes(desc: lattice_osr_desc, chunk_size: int) -> 
 
 def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size: int, *,
                             mode: int = MODE_DEC, grads: Optional[dict] = None, workspace=None,
-                            stream=None) -> dict:
+                            stream=None, linearisation: int = LIN2) -> dict:
     """Backward of the chunk-wise forward: gradients of sum(dy*y) +
     sum(dstate_out*state_out) with respect to q, k, v, gamma, mu and
     state_in.  dy has y's shape (float32 or bfloat16), dstate_out the state's.
     Returns a dict of float32 tensors dq, dk, dv, dgamma, dmu, dstate_in
     (allocated unless passed in `grads`)."""
     lib = load_library()
-    desc = _desc_from(q, k, v, gamma, mu, state_in, dy.dtype, mode)
+    desc = _desc_from(q, k, v, gamma, mu, state_in, dy.dtype, mode, linearisation)
     if not dy.is_contiguous() or dy.shape != v.shape or dy.device != q.device:
         raise ValueError("dy must be contiguous with v's shape")
     if dstate_out.dtype != torch.float32 or not dstate_out.is_contiguous() or dstate_out.shape != state_in.shape:

@@ -156,10 +156,9 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * Form"); this call returns the gradient of
  *     L = sum(dy * y) + sum(dstate_out * state_out)
  * with respect to q, k, v, gamma, mu and state_in, where (y, state_out) is
- * lattice_osr_fwd_chunked at the same desc and chunk_size with
- * desc->linearisation = LATTICE_OSR_LIN2 (eq. recurrence_linear2; LIN1 is
- * LATTICE_OSR_ERR_UNSUPPORTED).  The forward is recomputed inside the call:
- * the forward's y and state_out are not needed.
+ * lattice_osr_fwd_chunked at the same desc (either linearisation) and
+ * chunk_size.  The forward is recomputed inside the call: the forward's y and
+ * state_out are not needed.
  *   dy          [B,T,H,d]   y_dtype            (16-byte aligned)
  *   dstate_out  [B,H,m,d]   float32            (16-byte aligned)
  *   dq, dk      [B,T,H,m]   float32            (4-byte aligned)

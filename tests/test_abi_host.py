@@ -218,9 +218,11 @@ def test_bwd_null_pointers_and_shapes():
     d2 = osr.make_desc(1, 8, 1, 16, 48)
     assert _bwd_call(d2, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED
     d3 = osr.make_desc(1, 8, 1, 16, 16, linearisation=osr.LIN1)
-    assert _bwd_call(d3, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED  # only eq. recurrence_linear2
+    assert osr.lattice_osr_bwd_workspace_bytes(d3, 4) == osr.lattice_osr_bwd_workspace_bytes(d, 4)
+    d4 = osr.make_desc(1, 8, 1, 16, 16, linearisation=2)
+    assert _bwd_call(d4, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED
     with pytest.raises(osr.OSRError):
-        osr.lattice_osr_bwd_workspace_bytes(d3, 4)
+        osr.lattice_osr_bwd_workspace_bytes(d4, 4)
 
 
 def test_bwd_workspace_too_small():

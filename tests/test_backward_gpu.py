@@ -59,28 +59,28 @@ def _upstream(inp, seed, dy_bf16=False):
     return dy, dso
 
 
-def _gpu_bwd(inp, dy, dso, C, mode, dy_bf16=False):
+def _gpu_bwd(inp, dy, dso, C, mode, dy_bf16=False, lin=osr.LIN2):
     t = osr.to_device(inp, "cuda")
     dyt = torch.from_numpy(dy).cuda()
     if dy_bf16:
         dyt = dyt.to(torch.bfloat16)   # exact: dy already holds bf16 values
     g = osr.lattice_osr_bwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], dyt,
-                                    torch.from_numpy(dso).cuda(), C, mode=mode)
+                                    torch.from_numpy(dso).cuda(), C, mode=mode, linearisation=lin)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in g.items()}
 
 
-def _oracle(inp, dy, dso, C, mode, bh=None):
+def _oracle(inp, dy, dso, C, mode, bh=None, lin=ob.LIN2):
     a = inp.values_f64()
     if bh is None:
-        return ob.osr_backward(*a, dy, dso, chunk_size=C, mode=mode)
+        return ob.osr_backward(*a, dy, dso, chunk_size=C, mode=mode, linearisation=lin)
     q, k, v, g, mu, S = a
 
     def one(pair):
         b, h = pair
         sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
         return ob.osr_backward(q[sl], k[sl], v[sl], g[sl], mu[b:b + 1, :, h:h + 1], S[b:b + 1, h:h + 1],
-                               dy[sl], dso[b:b + 1, h:h + 1], chunk_size=C, mode=mode)
+                               dy[sl], dso[b:b + 1, h:h + 1], chunk_size=C, mode=mode, linearisation=lin)
 
     with cf.ThreadPoolExecutor(min(len(bh), 8)) as ex:
         return list(ex.map(one, bh))
@@ -117,7 +117,7 @@ def test_bwd_tiny_fp32(mode, C, per_slot):
     _check(inp, _gpu_bwd(inp, dy, dso, C, mode), _oracle(inp, dy, dso, C, mode))
 
 
-def _conditioned_tol(inp, dy, dso, C, mode, ref):
+def _conditioned_tol(inp, dy, dso, C, mode, ref, lin=ob.LIN2):
     """Bar for a badly conditioned gradient, derived from the oracle itself:
     the largest relative change of any oracle gradient (max-abs over RMS)
     when every input is perturbed by 1e-7 relative (fp32 rounding size),
@@ -126,7 +126,7 @@ def _conditioned_tol(inp, dy, dso, C, mode, ref):
     a = list(inp.values_f64())
     rng = np.random.default_rng(99)
     a2 = [x * (1 + 1e-7 * rng.standard_normal(x.shape)) for x in a]
-    g2 = ob.osr_backward(*a2, dy, dso, chunk_size=C, mode=mode)
+    g2 = ob.osr_backward(*a2, dy, dso, chunk_size=C, mode=mode, linearisation=lin)
     sens = max(_rel(g2[k], ref[k]) for k in KEYS)
     tol = max(TOL[inp.in_dtype], 20.0 * sens)
     _say(f"  oracle sensitivity {sens:.2e} -> bar {tol:.2e}")
@@ -236,3 +236,47 @@ def test_bwd_long_context_shape_prefix():
     got = _gpu_bwd(inp, dy, dso, 128, osr.MODE_DEC)
     bh = [(0, 0), (0, 9)]
     _check(inp, got, _oracle(inp, dy, dso, 128, osr.MODE_DEC, bh), bh=bh)
+
+
+# ---------------------------------------------------------------------------
+# The first chunk linearisation (eq. recurrence_linear1)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM])
+@pytest.mark.parametrize("C", [4, 16, 64])
+@pytest.mark.parametrize("per_slot", [True, False])
+def test_bwd_first_linearisation_tiny_fp32(mode, C, per_slot):
+    _say(f"bwd LIN1 tiny fp32 B1 H2 T64 m16 d32 C{C} mode{mode} per_slot{per_slot}")
+    inp = synth.make_inputs(1, 64, 2, 16, 32, seed=21, in_dtype=synth.F32, gamma_per_slot=per_slot)
+    dy, dso = _upstream(inp, 21)
+    _check(inp, _gpu_bwd(inp, dy, dso, C, mode, lin=osr.LIN1),
+           _oracle(inp, dy, dso, C, mode, lin=ob.LIN1))
+
+
+@pytest.mark.parametrize("m,d", [(64, 64), (64, 128), (128, 32)])
+def test_bwd_first_linearisation_bf16(m, d):
+    _say(f"bwd LIN1 bf16 B2 H2 T256 m{m} d{d} C64")
+    inp = synth.make_inputs(2, 256, 2, m, d, seed=22, in_dtype=synth.BF16)
+    dy, dso = _upstream(inp, 22)
+    _check(inp, _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC, lin=osr.LIN1),
+           _oracle(inp, dy, dso, 64, osr.MODE_DEC, lin=ob.LIN1))
+
+
+@pytest.mark.parametrize("C", [4, 16])
+def test_bwd_first_linearisation_encoding_layer_fp32(C):
+    _say(f"bwd LIN1 encoding layer fp32 B1 H2 T16 m16 d32 C{C}")
+    inp = synth.make_inputs(1, 16, 2, 16, 32, seed=23, in_dtype=synth.F32)
+    dy, dso = _upstream(inp, 23)
+    ref = _oracle(inp, dy, dso, C, osr.MODE_ENC, lin=ob.LIN1)
+    tol = _conditioned_tol(inp, dy, dso, C, osr.MODE_ENC, ref, lin=ob.LIN1)
+    _check(inp, _gpu_bwd(inp, dy, dso, C, osr.MODE_ENC, lin=osr.LIN1), ref, tol=tol)
+
+
+def test_bwd_first_linearisation_headline_sampled():
+    """B4 H8 T2048 m64 d64 C64 with the first linearisation, two sequences
+    recomputed by the oracle."""
+    _say("bwd LIN1 headline chunked_b4h8_t2048_m64d64_c64, sampled (b,h)")
+    inp = synth.workload_inputs("chunked_b4h8_t2048_m64d64_c64")
+    dy, dso = _upstream(inp, 24)
+    got = _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC, lin=osr.LIN1)
+    bh = [(0, 2), (3, 6)]
+    _check(inp, got, _oracle(inp, dy, dso, 64, osr.MODE_DEC, bh, lin=ob.LIN1), bh=bh)
