@@ -374,37 +374,12 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                 muv[i][r] = mu4[r];
             }
         }
+        // Tile-major: the products of token tile i are issued before the gates
+        // of tile i - 1, so the gate arithmetic (VALU) of one tile can run under
+        // the matrix-core products of the next.
         f32x4 cc[TBW];
-#pragma unroll
-        for (int i = 0; i < TBW; ++i) cc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (G::K32_D) {
-#pragma unroll
-            for (int kd = 0; kd < D / 32; ++kd) {
-                bf16x8 ah[TBW], al[TBW];
-#pragma unroll
-                for (int i = 0; i < TBW; ++i) {
-                    const int ao = (16 * (tbg + i) + lc) * G::HS_LD + 32 * kd + 4 * lg;
-                    ah[i] = ld8p(hsh + ao);
-                    al[i] = ld8p(hsl + ao);
-                }
-                const bf16x8 bh = cat8(zfh[2 * kd], zfh[2 * kd + 1]), bl = cat8(zfl[2 * kd], zfl[2 * kd + 1]);
-#pragma unroll
-                for (int i = 0; i < TBW; ++i) cc[i] = mma32(al[i], bh, cc[i]);
-#pragma unroll
-                for (int i = 0; i < TBW; ++i) cc[i] = mma32(ah[i], bl, cc[i]);
-#pragma unroll
-                for (int i = 0; i < TBW; ++i) cc[i] = mma32(ah[i], bh, cc[i]);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < TBW; ++i) {
-                const int ao = (16 * (tbg + i) + lc) * G::HS_LD + 4 * lg;
-                cc[i] = mma3(ld4s(hsh + ao), ld4s(hsl + ao), zfh[0], zfl[0], cc[i]);
-            }
-        }
         float gt[TBW][4], kp[TBW][4], tot[TBW], ex_lo[TBW], ex_hi[TBW];
-#pragma unroll
-        for (int i = 0; i < TBW; ++i) {
+        auto gates = [&](int i) {
             float prod = 1.f;
             f32x4 g4 = {0.f, 0.f, 0.f, 0.f};  // gamma of the tile, read again for the encoding layer only
             if (enc) g4 = tr16f(ld4s(gs + (16 * (tbg + i) + lc) * G::GS_LD + 16 * wv + 4 * lg), eye);
@@ -424,6 +399,47 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                 *reinterpret_cast<f32x4*>(ws.g + o) = f32x4{gt[i][0], gt[i][1], gt[i][2], gt[i][3]};
                 *reinterpret_cast<f32x4*>(ws.k + o) = f32x4{kp[i][0], kp[i][1], kp[i][2], kp[i][3]};
             }
+        };
+        if constexpr (G::K32_D) {
+            constexpr int KD = D / 32;
+            bf16x8 bhk[KD], blk[KD];
+#pragma unroll
+            for (int kd = 0; kd < KD; ++kd) {
+                bhk[kd] = cat8(zfh[2 * kd], zfh[2 * kd + 1]);
+                blk[kd] = cat8(zfl[2 * kd], zfl[2 * kd + 1]);
+            }
+            auto products = [&](int i) {
+                bf16x8 ah[KD], al[KD];
+#pragma unroll
+                for (int kd = 0; kd < KD; ++kd) {
+                    const int ao = (16 * (tbg + i) + lc) * G::HS_LD + 32 * kd + 4 * lg;
+                    ah[kd] = ld8p(hsh + ao);
+                    al[kd] = ld8p(hsl + ao);
+                }
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kd = 0; kd < KD; ++kd) {
+                    c = mma32(al[kd], bhk[kd], c);
+                    c = mma32(ah[kd], blk[kd], c);
+                    c = mma32(ah[kd], bhk[kd], c);
+                }
+                cc[i] = c;
+            };
+            products(0);
+#pragma unroll
+            for (int i = 1; i < TBW; ++i) {
+                products(i);
+                gates(i - 1);
+            }
+            gates(TBW - 1);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TBW; ++i) {
+                const int ao = (16 * (tbg + i) + lc) * G::HS_LD + 4 * lg;
+                cc[i] = mma3(ld4s(hsh + ao), ld4s(hsl + ao), zfh[0], zfl[0], f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+#pragma unroll
+            for (int i = 0; i < TBW; ++i) gates(i);
         }
         // W_t = kappa_t (.) prod_{l > t} g_l over the group's tokens, split into
         // B operands of the update (k = token); aend = prod of the group's g.
