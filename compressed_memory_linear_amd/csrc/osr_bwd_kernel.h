@@ -34,7 +34,9 @@
 // is elementwise per slot.  So the sums over slots, the only reductions that
 // cross waves, are batched: h for a batch of BT tokens in one LDS exchange, and
 // in the reverse walk the per-token partials of dh (with d|h|^2, dmu and a
-// per-token dgamma) for BT tokens in another.  The per-token steps in between
+// per-token dgamma) for BT tokens in another.  In both, the sums over waves
+// are spread over the threads (one float4 of the batch each) rather than
+// repeated by every thread.  The per-token steps in between
 // reduce only over d, inside a row group (DPP).
 //
 // One workgroup per (b,h), state in registers in the layout of osr_valu.h.
@@ -210,6 +212,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     constexpr bool PF_STATE = L::RPT <= 2;
     __shared__ __attribute__((aligned(16))) float hbuf[BWD_CMAX * D];
     __shared__ __attribute__((aligned(16))) float red[2 * BT * L::NW * W];
+    __shared__ __attribute__((aligned(16))) float tot[BT * W];  // a batch's sums over slots
+    static_assert(BT * (D / 4 + 1) <= NT, "one float4 of a batch's sums per thread");
     const int bh = blockIdx.x;
     const int b = bh / p.f.H, hd = bh % p.f.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -476,18 +480,22 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                 }
             }
             __syncthreads();  // the batch's partial sums visible
+            // the sums over waves, one float4 of the batch per thread
+            if (tid < nb * (D / 4 + 1)) {
+                const int u = tid / (D / 4 + 1), c4 = tid % (D / 4 + 1);
+                float4 acc = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + c4 * 4);
+#pragma unroll
+                for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + c4 * 4);
+                *reinterpret_cast<float4*>(tot + u * W + c4 * 4) = acc;
+            }
+            __syncthreads();  // the batch's sums visible
 #pragma unroll
             for (int u = 0; u < BT; ++u) {
                 if (u < nb) {
                     const int tau = ub + u;
                     const int64_t bth = bth_of(n * C + tau);
-                    float4 hsum = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + cg * 4);
-                    float4 ssum = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + D);
-#pragma unroll
-                    for (int w = 1; w < L::NW; ++w) {
-                        hsum = hsum + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + cg * 4);
-                        ssum = ssum + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + D);
-                    }
+                    const float4 hsum = *reinterpret_cast<const float4*>(tot + u * W + cg * 4);
+                    const float4 ssum = *reinterpret_cast<const float4*>(tot + u * W + D);
                     const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
                     const float4 dh = fma4(2.f * ssum.x, h, hsum);
                     float dkz[L::RPT] = {};
