@@ -64,66 +64,6 @@ __host__ __device__ inline int64_t bwd_floats_per_bh(int T, int C) {
     return (static_cast<int64_t>(T / C) + 1 + C) * M * D + static_cast<int64_t>(C) * TokRec<M, D>::SIZE;
 }
 
-constexpr int BWD_CMAX = 128;  // largest chunk size (the chunk's h is held in LDS)
-
-// Tokens per batched exchange over slots: the reverse walk keeps 3 values per
-// slot row and token of a batch in registers.
-template <class L>
-struct BwdBatch {
-    static constexpr int BT = L::RPT <= 2 ? 8 : (L::RPT <= 4 ? 4 : 2);
-};
-
-// h of every token of the chunk [t0, t0 + C) into hbuf[C][D] (fp32), from the
-// projected chunk-start state z.  Decoding objective: h = sum_i k_i z_i - v,
-// the sum over slots exchanged through red once per BT tokens; otherwise -v
-// or v.  Ends with a barrier (hbuf visible to all threads).
-template <class L, int M, int D, typename TIn>
-__device__ __forceinline__ void chunk_h(const float4 (&z)[L::RPT], const Params& f, int64_t bth0,
-                                        int64_t tstride, int C, int mode, float* hbuf, float* red,
-                                        int& nred, int tid, int lane, int wave, int rg, int cg) {
-    constexpr int BT = BwdBatch<L>::BT, W = D + 4, Q = D / 4;
-    static_assert(BT * Q <= L::NW * 64, "one output float4 per thread");
-    const TIn* kp = static_cast<const TIn*>(f.k);
-    const TIn* vp = static_cast<const TIn*>(f.v);
-    if (mode != 0) {
-        const float sgn = mode == 2 ? 1.f : -1.f;
-        for (int idx = tid; idx < C * Q; idx += L::NW * 64) {
-            const int u = idx / Q, c4 = idx % Q;
-            *reinterpret_cast<float4*>(hbuf + u * D + c4 * 4) = sgn * ld4<TIn>(vp, (bth0 + u * tstride) * D + c4 * 4);
-        }
-        __syncthreads();
-        return;
-    }
-    const int nb = C < BT ? C : BT;
-    for (int u0 = 0; u0 < C; u0 += nb) {
-        float* rb = red + (nred++ & 1) * (BT * L::NW * W);
-#pragma unroll
-        for (int u = 0; u < BT; ++u) {
-            if (u < nb) {
-                const int64_t bth = bth0 + (u0 + u) * tstride;
-                float4 hp = f4(0.f);
-#pragma unroll
-                for (int i = 0; i < L::RPT; ++i) hp = fma4(ld<TIn>(kp, bth * M + rg + L::RG * i), z[i], hp);
-                hp.x = strided_sum<L::TPR>(hp.x);
-                hp.y = strided_sum<L::TPR>(hp.y);
-                hp.z = strided_sum<L::TPR>(hp.z);
-                hp.w = strided_sum<L::TPR>(hp.w);
-                if (lane < L::TPR) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + cg * 4) = hp;
-            }
-        }
-        __syncthreads();
-        if (tid < nb * Q) {
-            const int u = tid / Q, c4 = tid % Q;
-            float4 acc = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + c4 * 4);
-#pragma unroll
-            for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + c4 * 4);
-            const float4 v = ld4<TIn>(vp, (bth0 + (u0 + u) * tstride) * D + c4 * 4);
-            *reinterpret_cast<float4*>(hbuf + (u0 + u) * D + c4 * 4) = acc - v;
-        }
-    }
-    __syncthreads();
-}
-
 // One forward token given its h: updates r, returns the per-slot c and beta
 // and |h|^2 (valid in every thread of a row group).  No cross-wave exchange.
 // lin1: the first chunk linearisation, r_i <- mu beta_i r_i + beta_i a_i c_i z_i
@@ -205,12 +145,12 @@ template <int M, int D, int NT, typename TIn, bool LIN1>
 __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     using L = ValuLayout<M, D, NT>;
     using TR = TokRec<M, D>;
-    constexpr int BT = BwdBatch<L>::BT, W = D + 4;
+    constexpr int BT = TokBatch<L>::BT, W = D + 4;
     // The reverse walk loads the next token's inputs and record while it works on
     // the current one, and the state before it too, where registers allow.
     constexpr bool PF_TOKEN = L::RPT <= 4;
     constexpr bool PF_STATE = L::RPT <= 2;
-    __shared__ __attribute__((aligned(16))) float hbuf[BWD_CMAX * D];
+    extern __shared__ __attribute__((aligned(16))) float hbuf[];  // [C][D], dynamic
     __shared__ __attribute__((aligned(16))) float red[2 * BT * L::NW * W];
     __shared__ __attribute__((aligned(16))) float tot[BT * W];  // a batch's sums over slots
     static_assert(BT * (D / 4 + 1) <= NT, "one float4 of a batch's sums per thread");
@@ -544,17 +484,18 @@ static int launch_bwd_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
     constexpr int TPR = D / 4;
     constexpr int NT = (M * TPR < 512) ? M * TPR : 512;
     const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H));
+    const size_t lds = static_cast<size_t>(p.f.chunk) * D * sizeof(float);  // the chunk's h
     // the first linearisation is its own instantiation, so the default carries none of its work
     if (in_bf16) {
         if (p.f.lin1)
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, uint16_t, true>), grid, dim3(NT), 0, st, p);
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, uint16_t, true>), grid, dim3(NT), lds, st, p);
         else
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, uint16_t, false>), grid, dim3(NT), 0, st, p);
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, uint16_t, false>), grid, dim3(NT), lds, st, p);
     } else {
         if (p.f.lin1)
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, float, true>), grid, dim3(NT), 0, st, p);
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, float, true>), grid, dim3(NT), lds, st, p);
         else
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, float, false>), grid, dim3(NT), 0, st, p);
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, float, false>), grid, dim3(NT), lds, st, p);
     }
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }

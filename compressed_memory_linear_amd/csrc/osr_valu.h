@@ -82,4 +82,65 @@ __device__ __forceinline__ void project_rows(float4 (&s)[L::RPT]) {
     for (int i = 0; i < L::RPT; ++i) s[i] = rsqrtf(n2[i]) * s[i];
 }
 
+
+// Tokens per batched exchange over slots (the backward's reverse walk keeps 3
+// values per slot row and token of a batch in registers).
+template <class L>
+struct TokBatch {
+    static constexpr int BT_REG = L::RPT <= 2 ? 8 : (L::RPT <= 4 ? 4 : 2);
+    // at d = 128 at most 4, so that the exchange buffers and a chunk's h fit in LDS
+    static constexpr int BT = (L::TPR == 32 && BT_REG > 4) ? 4 : BT_REG;
+};
+
+// h of every token of the chunk [t0, t0 + C) into hbuf[C][D] (fp32), from the
+// projected chunk-start state z.  Decoding objective: h = sum_i k_i z_i - v,
+// the sum over slots exchanged through red once per BT tokens; otherwise -v
+// or v.  Ends with a barrier (hbuf visible to all threads).
+template <class L, int M, int D, typename TIn>
+__device__ __forceinline__ void chunk_h(const float4 (&z)[L::RPT], const Params& f, int64_t bth0,
+                                        int64_t tstride, int C, int mode, float* hbuf, float* red,
+                                        int& nred, int tid, int lane, int wave, int rg, int cg) {
+    constexpr int BT = TokBatch<L>::BT, W = D + 4, Q = D / 4;
+    static_assert(BT * Q <= L::NW * 64, "one output float4 per thread");
+    const TIn* kp = static_cast<const TIn*>(f.k);
+    const TIn* vp = static_cast<const TIn*>(f.v);
+    if (mode != 0) {
+        const float sgn = mode == 2 ? 1.f : -1.f;
+        for (int idx = tid; idx < C * Q; idx += L::NW * 64) {
+            const int u = idx / Q, c4 = idx % Q;
+            *reinterpret_cast<float4*>(hbuf + u * D + c4 * 4) = sgn * ld4<TIn>(vp, (bth0 + u * tstride) * D + c4 * 4);
+        }
+        __syncthreads();
+        return;
+    }
+    const int nb = C < BT ? C : BT;
+    for (int u0 = 0; u0 < C; u0 += nb) {
+        float* rb = red + (nred++ & 1) * (BT * L::NW * W);
+#pragma unroll
+        for (int u = 0; u < BT; ++u) {
+            if (u < nb) {
+                const int64_t bth = bth0 + (u0 + u) * tstride;
+                float4 hp = f4(0.f);
+#pragma unroll
+                for (int i = 0; i < L::RPT; ++i) hp = fma4(ld<TIn>(kp, bth * M + rg + L::RG * i), z[i], hp);
+                hp.x = strided_sum<L::TPR>(hp.x);
+                hp.y = strided_sum<L::TPR>(hp.y);
+                hp.z = strided_sum<L::TPR>(hp.z);
+                hp.w = strided_sum<L::TPR>(hp.w);
+                if (lane < L::TPR) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + cg * 4) = hp;
+            }
+        }
+        __syncthreads();
+        if (tid < nb * Q) {
+            const int u = tid / Q, c4 = tid % Q;
+            float4 acc = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + c4 * 4);
+#pragma unroll
+            for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + c4 * 4);
+            const float4 v = ld4<TIn>(vp, (bth0 + (u0 + u) * tstride) * D + c4 * 4);
+            *reinterpret_cast<float4*>(hbuf + (u0 + u) * D + c4 * 4) = acc - v;
+        }
+    }
+    __syncthreads();
+}
+
 }  // namespace osr

@@ -106,15 +106,32 @@ __global__ __launch_bounds__(NT) void osr_decode_kernel(Params p) {
 }
 
 // -------------------------------------------------------------- token loop --
+// The read-outs y do not feed back into the recurrence, so their sums over
+// slots are batched: each token leaves its per-wave partials in LDS and every
+// BT tokens one barrier lets the threads add them up (one float4 of the batch
+// each) and store y.  With C > 1, h depends only on the chunk-start state and
+// the inputs, so the chunk's h is formed up front in LDS (chunk_h) and a token
+// needs no exchange across waves at all; with C = 1 h is summed over slots per
+// token (col_sum).
 template <int M, int D, int NT, typename TIn>
 __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
     using L = ValuLayout<M, D, NT>;
-    __shared__ float red[3][L::NW * D];
+    constexpr int BT = TokBatch<L>::BT, W = D + 4, Q = D / 4;
+    static_assert(BT * Q <= NT, "one float4 of a batch's read-outs per thread");
+    // With C > 1 the chunk's h and chunk_h's exchange buffers sit in dynamic
+    // LDS (tokenloop_dyn_lds floats); with C = 1 there is none, so several
+    // workgroups can share a CU.
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
+    float* hbuf = dyn;                   // [C][D]
+    float* redc = dyn + p.chunk * D;     // [2][BT][NW][W]
+    __shared__ __attribute__((aligned(16))) float redy[2 * BT * L::NW * W];  // y batches
+    __shared__ __attribute__((aligned(16))) float redh[2][L::NW * D];        // h at C = 1
     const int bh = blockIdx.x;
     const int b = bh / p.H, hd = bh % p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cg = tid % L::TPR, rg = tid / L::TPR;
     const int T = p.T, C = p.chunk;
+    const int64_t tstride = p.H;  // consecutive tokens of one (b,h) are H rows apart
 
     const float* sin = p.state_in + static_cast<int64_t>(bh) * M * D;
     float4 s[L::RPT], z[L::RPT];
@@ -125,23 +142,91 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
     auto bth_of = [&](int t) { return (static_cast<int64_t>(b) * T + t) * p.H + hd; };
     TokenIn<L::RPT> cur, nxt;
     load_token<L, M, D, TIn>(cur, p, bth_of(0), rg, cg);
+    int nredc = 0, ybatch = 0;
 
-    for (int t0 = 0; t0 < T; t0 += C) {
-        project_rows<L>(s);
+    for (int t = 0; t < T; ++t) {
+        const int tau = t % C;
+        if (tau == 0) {
+            project_rows<L>(s);
 #pragma unroll
-        for (int i = 0; i < L::RPT; ++i) z[i] = s[i];
-        for (int t = t0; t < t0 + C; ++t) {
-            if (t + 1 < T) load_token<L, M, D, TIn>(nxt, p, bth_of(t + 1), rg, cg);
-            const float4 y = osr_token<L, D>(z, s, cur, p.mode, p.lin1, red[2], red[t & 1], lane, wave, cg);
-            if (rg == 0) st_y4(p.y, bth_of(t) * D + cg * 4, y, p.y_bf16);
-            cur = nxt;
+            for (int i = 0; i < L::RPT; ++i) z[i] = s[i];
+            if (C > 1) {
+                __syncthreads();  // every thread is done with the previous chunk's h
+                chunk_h<L, M, D, TIn>(z, p, bth_of(t), tstride, C, p.mode, hbuf, redc, nredc, tid, lane, wave,
+                                      rg, cg);
+            }
         }
+        if (t + 1 < T) load_token<L, M, D, TIn>(nxt, p, bth_of(t + 1), rg, cg);
+
+        float4 h;
+        if (C > 1) {
+            h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
+        } else if (p.mode == 0) {
+            float4 hp = f4(0.f);
+#pragma unroll
+            for (int i = 0; i < L::RPT; ++i) hp = fma4(cur.k[i], z[i], hp);
+            h = col_sum<L, D>(hp, redh[t & 1], lane, wave, cg) - cur.v;
+        } else {
+            h = p.mode == 2 ? cur.v : f4(0.f) - cur.v;
+        }
+        float cc[L::RPT + 1];
+#pragma unroll
+        for (int i = 0; i < L::RPT; ++i) cc[i] = dot4(z[i], h);
+        cc[L::RPT] = dot4(h, h);
+#pragma unroll
+        for (int i = 0; i <= L::RPT; ++i) cc[i] = group_sum<L::TPR>(cc[i]);
+        const float hh = cc[L::RPT];
+        const float mu = cur.mu;
+        float4 yp = f4(0.f);
+#pragma unroll
+        for (int i = 0; i < L::RPT; ++i) {
+            const float a = cur.g[i] * (p.mode == 2 ? cc[i] - cur.k[i] : cur.k[i]);
+            const float w = fmaxf(fmaf(-cc[i], cc[i], hh), 0.f);
+            const float beta = rsqrtf(fmaf(mu, mu, a * a * w));
+            const float kap = -beta * a;
+            if (p.lin1) {
+                // mu beta on the running slot, the projection term on z
+                s[i] = fma4(beta * mu, s[i], fma4(beta * a * cc[i], z[i], kap * h));
+            } else {
+                s[i] = fma4(beta * fmaf(a, cc[i], mu), s[i], kap * h);
+            }
+            yp = fma4(cur.q[i], s[i], yp);
+        }
+
+        // this token's read-out partial over the wave's slots, to LDS
+        const int u = t % BT;
+        float* rb = redy + (ybatch & 1) * (BT * L::NW * W);
+        yp.x = strided_sum<L::TPR>(yp.x);
+        yp.y = strided_sum<L::TPR>(yp.y);
+        yp.z = strided_sum<L::TPR>(yp.z);
+        yp.w = strided_sum<L::TPR>(yp.w);
+        if (lane < L::TPR) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + cg * 4) = yp;
+        if (u == BT - 1 || t == T - 1) {
+            __syncthreads();  // the batch's partials visible
+            const int nb = u + 1, t0 = t - u;
+            if (tid < nb * Q) {
+                const int uu = tid / Q, c4 = tid % Q;
+                float4 acc = *reinterpret_cast<const float4*>(rb + (uu * L::NW) * W + c4 * 4);
+#pragma unroll
+                for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (uu * L::NW + w) * W + c4 * 4);
+                st_y4(p.y, bth_of(t0 + uu) * D + c4 * 4, acc, p.y_bf16);
+            }
+            ++ybatch;
+        }
+        cur = nxt;
     }
     project_rows<L>(s);
     float* sout = p.state_out + static_cast<int64_t>(bh) * M * D;
 #pragma unroll
     for (int i = 0; i < L::RPT; ++i)
         *reinterpret_cast<float4*>(sout + (rg + L::RG * i) * D + cg * 4) = s[i];
+}
+
+// Dynamic LDS of the token loop (floats): C > 1 only.
+template <int M, int D, int NT>
+static size_t tokenloop_dyn_lds(int C) {
+    using L = ValuLayout<M, D, NT>;
+    return C > 1 ? static_cast<size_t>(C) * D + 2 * TokBatch<L>::BT * L::NW * (D + 4) : 0;
 }
 
 // ----------------------------------------------------------------- launch --
@@ -160,10 +245,11 @@ static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_
         else
             hipLaunchKernelGGL((osr_decode_kernel<M, D, NT_DEC, float>), grid, dim3(NT_DEC), 0, st, p);
     } else {
+        const size_t lds = tokenloop_dyn_lds<M, D, NT_TOK>(p.chunk) * sizeof(float);
         if (in_bf16)
-            hipLaunchKernelGGL((osr_tokenloop_kernel<M, D, NT_TOK, uint16_t>), grid, dim3(NT_TOK), 0, st, p);
+            hipLaunchKernelGGL((osr_tokenloop_kernel<M, D, NT_TOK, uint16_t>), grid, dim3(NT_TOK), lds, st, p);
         else
-            hipLaunchKernelGGL((osr_tokenloop_kernel<M, D, NT_TOK, float>), grid, dim3(NT_TOK), 0, st, p);
+            hipLaunchKernelGGL((osr_tokenloop_kernel<M, D, NT_TOK, float>), grid, dim3(NT_TOK), lds, st, p);
     }
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
