@@ -42,16 +42,15 @@ int check_desc(const lattice_osr_desc* d) {
 // Which implementation runs a chunked call.
 enum class Path { TokenLoop, Mfma };
 
-// The first linearisation runs on the token-loop kernel only.
+// bf16 inputs with C >= 16 run on the MFMA kernels (either linearisation).
 Path chunk_path(const lattice_osr_desc* d, int C) {
-    if (C > 1 && d->in_dtype == LATTICE_OSR_BF16 && d->linearisation == LATTICE_OSR_LIN2 &&
-        osr::mfma_supported(d->m, d->d, C))
-        return Path::Mfma;
+    if (C > 1 && d->in_dtype == LATTICE_OSR_BF16 && osr::mfma_supported(d->m, d->d, C)) return Path::Mfma;
     return Path::TokenLoop;
 }
 
 size_t workspace_needed(const lattice_osr_desc* d, int C) {
-    if (chunk_path(d, C) == Path::Mfma) return osr::mfma_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C);
+    if (chunk_path(d, C) == Path::Mfma)
+        return osr::mfma_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1);
     return 0;
 }
 

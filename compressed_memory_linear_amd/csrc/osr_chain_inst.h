@@ -46,20 +46,22 @@ static bool pairs_enabled() {
     return !(e && strcmp(e, "0") == 0);
 }
 
-template <int M, int D, int C0, bool ENC>
+template <int M, int D, int C0, bool ENC, bool LIN1>
 static void launch_chain_mode(const Params& p, hipStream_t st) {
     const unsigned BH = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H);
     if (p.chunk != C0) {
-        hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false, false, ENC>), dim3(BH), dim3(4 * M), 0, st, p);
+        hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false, false, ENC, LIN1>), dim3(BH), dim3(4 * M), 0, st,
+                           p);
         return;
     }
     if constexpr (pair_capable<M, D, C0>()) {
         if (pairs_enabled()) {
-            hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, true, ENC>), dim3(BH), dim3(8 * M), 0, st, p);
+            hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, true, ENC, LIN1>), dim3(BH), dim3(8 * M), 0, st,
+                               p);
             return;
         }
     }
-    hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, false, ENC>), dim3(BH), dim3(4 * M), 0, st, p);
+    hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, false, ENC, LIN1>), dim3(BH), dim3(4 * M), 0, st, p);
 }
 
 template <int M, int D, int C0>
@@ -67,10 +69,18 @@ static int launch_chain(const Params& p, hipStream_t st) {
     if constexpr (!chain_fits<M, D, C0>()) {
         return -3;
     } else {
-        if (p.mode == 2)
-            launch_chain_mode<M, D, C0, true>(p, st);
-        else
-            launch_chain_mode<M, D, C0, false>(p, st);
+        // the encoding layer and the first linearisation are instantiations of their own
+        if (p.mode == 2) {
+            if (p.lin1)
+                launch_chain_mode<M, D, C0, true, true>(p, st);
+            else
+                launch_chain_mode<M, D, C0, true, false>(p, st);
+        } else {
+            if (p.lin1)
+                launch_chain_mode<M, D, C0, false, true>(p, st);
+            else
+                launch_chain_mode<M, D, C0, false, false>(p, st);
+        }
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }
 }

@@ -1,6 +1,7 @@
 // osr_mfma.hip -- selection of the MFMA chunk schedule (bf16 inputs, C >= 16).
 //
-// Two schedules evaluate the same chunk formula (eq. recurrence_linear2):
+// Two schedules evaluate the same chunk formula (eq. recurrence_linear2, or
+// eq. recurrence_linear1 on the split schedule only):
 //   split: the state-passing kernel (osr_mfma_chain.h; one workgroup per
 //          (b,h), sequential over chunks) stores each chunk's start state,
 //          gates and h in the workspace; the read-out kernel
@@ -43,15 +44,17 @@ bool mfma_supported(int m, int d, int C) {
     return dims && C >= 16 && C <= 128 && (C & (C - 1)) == 0;
 }
 
-size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C) {
-    if (!mfma::use_split(B, H, d)) return 0;
-    // per (b,h,chunk): Z [m][d], g and kappa [m][C], h [d][C], fp32
-    const size_t per_chunk = static_cast<size_t>(m) * d + 2 * static_cast<size_t>(m) * C + static_cast<size_t>(d) * C;
+// The first linearisation runs on the split schedule only.
+size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1) {
+    if (!lin1 && !mfma::use_split(B, H, d)) return 0;
+    // per (b,h,chunk): Z [m][d], g and kappa [m][C], h [d][C] (and e [m][C]), fp32
+    const size_t per_chunk = static_cast<size_t>(m) * d + (lin1 ? 3 : 2) * static_cast<size_t>(m) * C +
+                             static_cast<size_t>(d) * C;
     return static_cast<size_t>(B) * H * (T / C) * per_chunk * sizeof(float);
 }
 
 int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st) {
-    const bool split = mfma::use_split(p.B, p.H, d);
+    const bool split = p.lin1 || mfma::use_split(p.B, p.H, d);
     switch (m) {
         case 16: return mfma::launch_m<16>(d, split, p, st);
         case 32: return mfma::launch_m<32>(d, split, p, st);

@@ -136,7 +136,11 @@ __device__ __forceinline__ float row_inv_norm(const f32x4 (&acc)[DB]) {
 // the waves per SIMD (latency hiding) at one extra barrier per chunk.
 // ENC: the encoding layer (h = v, writing coefficient c - k), a separate
 // instantiation so that the other objectives carry none of its selects.
-template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR, bool ENC>
+// LIN1: the first chunk linearisation (eq. recurrence_linear1): gate mu beta
+// and a term e Z with e = beta a c on the chunk-start slots, so that
+//   R_end = diag(A_end) R + diag(sum_t e_t (.) prod_{l > t} g_l) Z + H^T W
+// (the coefficient of Z is summed alongside W); e goes to the workspace too.
+template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR, bool ENC, bool LIN1 = false>
 __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Params p) {
     using G = ChainCfg<M, D, C0, PAIR>;
     static_assert(!PAIR || ONE, "the pair split covers one sub-block per chunk");
@@ -378,7 +382,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // of tile i - 1, so the gate arithmetic (VALU) of one tile can run under
         // the matrix-core products of the next.
         f32x4 cc[TBW];
-        float gt[TBW][4], kp[TBW][4], tot[TBW], ex_lo[TBW], ex_hi[TBW];
+        float gt[TBW][4], kp[TBW][4], ev[TBW][4], tot[TBW], ex_lo[TBW], ex_hi[TBW];
         auto gates = [&](int i) {
             float prod = 1.f;
             f32x4 g4 = {0.f, 0.f, 0.f, 0.f};  // gamma of the tile, read again for the encoding layer only
@@ -389,7 +393,12 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                 const float a = enc ? fmaf(g4[r], cr, av[i][r]) : av[i][r];
                 const float wvv = fmaxf(fmaf(-cr, cr, hh[i][r]), 0.f);
                 const float beta = __builtin_amdgcn_rsqf(fmaf(mu, mu, a * a * wvv));
-                gt[i][r] = beta * fmaf(a, cr, mu);
+                if constexpr (LIN1) {
+                    gt[i][r] = beta * mu;
+                    ev[i][r] = beta * a * cr;
+                } else {
+                    gt[i][r] = beta * fmaf(a, cr, mu);
+                }
                 kp[i][r] = -beta * a;
                 prod *= gt[i][r];
             }
@@ -398,6 +407,8 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                 const int64_t o = ws_frag(wv, tc0 / 16 + tbg + i, C / 16, lane);
                 *reinterpret_cast<f32x4*>(ws.g + o) = f32x4{gt[i][0], gt[i][1], gt[i][2], gt[i][3]};
                 *reinterpret_cast<f32x4*>(ws.k + o) = f32x4{kp[i][0], kp[i][1], kp[i][2], kp[i][3]};
+                if constexpr (LIN1)
+                    *reinterpret_cast<f32x4*>(ws.e + o) = f32x4{ev[i][0], ev[i][1], ev[i][2], ev[i][3]};
             }
         };
         if constexpr (G::K32_D) {
@@ -444,7 +455,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // W_t = kappa_t (.) prod_{l > t} g_l over the group's tokens, split into
         // B operands of the update (k = token); aend = prod of the group's g.
         s16x4 wh4[TBW], wl4[TBW];
-        float aend = 1.f;
+        float aend = 1.f, ez = 0.f;  // ez (LIN1): the lane's part of the coefficient of Z
 #pragma unroll
         for (int i = TBW - 1; i >= 0; --i) {
             float s_ = aend * ex_hi[i];
@@ -452,18 +463,34 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
 #pragma unroll
             for (int r = 3; r >= 0; --r) {
                 wvec[r] = kp[i][r] * s_;
+                if constexpr (LIN1) ez = fmaf(ev[i][r], s_, ez);
                 s_ *= gt[i][r];
             }
             split4(wvec, wh4[i], wl4[i]);
             aend *= tot[i];
         }
+        if constexpr (LIN1) ez = rows4_sum(ez);
 
         // ---- R^T <- R^T diag(A_end) + H^T W (PAIR: U_g = H^T W over half g) --
         f32x4 u[DB];
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db) {
+            if constexpr (LIN1) {
+                // Z: the running state itself when a chunk is one sub-block,
+                // else its split (hi + lo) kept from the chunk start
+                f32x4 zf = acc[db];
+                if constexpr (!ONE) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) u[db][r] = PAIR ? 0.f : acc[db][r] * aend;
+                    for (int r = 0; r < 4; ++r) zf[r] = bf16_bits_to_f32(static_cast<uint16_t>(zfh[db][r])) +
+                                                      bf16_bits_to_f32(static_cast<uint16_t>(zfl[db][r]));
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u[db][r] = PAIR ? zf[r] * ez : fmaf(acc[db][r], aend, zf[r] * ez);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) u[db][r] = PAIR ? 0.f : acc[db][r] * aend;
+            }
+        }
         if constexpr (G::K32_C) {
 #pragma unroll
             for (int kt = 0; kt < TBW / 2; ++kt) {

@@ -49,7 +49,8 @@ static int launch_fused(const Params& p, hipStream_t st) {
 
 template <int M, int D, int C0>
 static int launch_readout(const Params& p, hipStream_t st) {
-    if constexpr (!readout_fits<M, D, C0>()) {
+    if constexpr (!readout_fits<M, D, C0>() || !readout_fits<M, D, C0, true>()) {
+        // (every built m, d and sub-block fits both layouts)
         return -3;
     } else {
         const int BH = p.B * p.H, NC = p.T / p.chunk;
@@ -59,7 +60,10 @@ static int launch_readout(const Params& p, hipStream_t st) {
         int cpw = 1;
         while (cpw * 2 <= NC && NC % (cpw * 2) == 0 && static_cast<int64_t>(BH) * NC / (cpw * 2) >= 1024) cpw *= 2;
         const unsigned grid = static_cast<unsigned>(BH) * static_cast<unsigned>(NC / cpw);
-        hipLaunchKernelGGL((osr_readout_kernel<M, D, C0>), dim3(grid), dim3(4 * D), 0, st, p, cpw);
+        if (p.lin1)
+            hipLaunchKernelGGL((osr_readout_kernel<M, D, C0, true>), dim3(grid), dim3(4 * D), 0, st, p, cpw);
+        else
+            hipLaunchKernelGGL((osr_readout_kernel<M, D, C0, false>), dim3(grid), dim3(4 * D), 0, st, p, cpw);
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }
 }

@@ -156,6 +156,14 @@ __device__ __forceinline__ float rows4_sum(float x) {
     half_rows(e + o, lo, hi);
     return lo + hi;
 }
+// Sums over the rows of x per lane column: below = rows < lg, total = all four.
+__device__ __forceinline__ void rows4_sum_scan(float x, int lg, float& below, float& total) {
+    float e, o, lo, hi;
+    pair_rows(x, e, o);
+    half_rows(e + o, lo, hi);
+    total = lo + hi;
+    below = ((lg & 1) ? e : 0.f) + ((lg & 2) ? lo : 0.f);
+}
 // Products over the rows of x per lane column: below = rows < lg, above =
 // rows > lg, total = all four.
 __device__ __forceinline__ void rows4_prod_scan(float x, int lg, float& below, float& above, float& total) {
@@ -169,7 +177,8 @@ __device__ __forceinline__ void rows4_prod_scan(float x, int lg, float& below, f
 
 // Workspace of the split schedule, fp32, for every (b,h) and chunk n (all
 // taken at the chunk-start state): Z [m][d], the gates g and kappa and the
-// vectors h.  The state-passing kernel writes it, the read-out kernel reads it.
+// vectors h (and, with the first linearisation, the coefficient e of the
+// chunk-start slot in each token's update).  The state-passing kernel writes it, the read-out kernel reads it.
 // g, kappa (per slot block) and h (per column block) are stored in MFMA lane
 // order, 1 KiB per (16-row block, 16-token tile): lane (lg, lc) holds row
 // 16*block + lc at tokens 16*tile + 4*lg .. +3.  Both kernels hold them in
@@ -179,6 +188,7 @@ struct Workspace {
     float* g;
     float* k;
     float* h;
+    float* e;  // first linearisation only: the chunk-start term's coefficient beta a c
 };
 // Offset (floats) of the 4 values of one lane: block of 16 rows, token tile
 // of the chunk (C/16 tiles per block).
@@ -199,7 +209,9 @@ __device__ __forceinline__ Workspace workspace_at(const Params& p, int bh, int n
     float* g0 = p.zbuf + nch * M * D;
     float* k0 = g0 + nch * M * C;
     float* h0 = k0 + nch * M * C;
-    return Workspace{p.zbuf + i * M * D, g0 + i * M * C, k0 + i * M * C, h0 + i * D * C};
+    float* e0 = h0 + nch * D * C;  // present with the first linearisation only
+    return Workspace{p.zbuf + i * M * D, g0 + i * M * C, k0 + i * M * C, h0 + i * D * C,
+                     p.lin1 ? e0 + i * M * C : nullptr};
 }
 
 template <int M, int D, int C0, bool WITH_Y>

@@ -31,8 +31,9 @@
 namespace osr {
 namespace mfma {
 
-template <int M, int D, int C0>
+template <int M, int D, int C0, bool LIN1 = false>
 struct ReadCfg {
+    static constexpr bool LIN1_ = LIN1;
     static constexpr int NW = D / 16;  // wave w owns columns [16w, 16w + 16)
     static constexpr int NT = 64 * NW;
     static constexpr int MT = M / 16;
@@ -54,20 +55,25 @@ struct ReadCfg {
     static constexpr int B_AE = B_WL + M * WT_LD * 2;    // A_end       [M] fp32
     static constexpr int NPT = TB * (TB + 1) / 2;        // causal P^T tiles (tb, jb <= tb)
     static constexpr int B_P = B_AE + M * 4;             // P^T hi, lo  [NPT][2][64 lanes] bf16 x4
-    static constexpr int SET = B_P + NPT * 2 * 64 * 8;
+    // first linearisation: Q.A.E hi, lo [C0][QA_LD] (coefficients of Z) and A_end E_end [M] fp32
+    static constexpr int B_ZH = B_P + NPT * 2 * 64 * 8;
+    static constexpr int B_ZL = B_ZH + (LIN1 ? C0 * QA_LD * 2 : 0);
+    static constexpr int B_AZ = B_ZL + (LIN1 ? C0 * QA_LD * 2 : 0);
+    static constexpr int SET = B_AZ + (LIN1 ? M * 4 : 0);
     static constexpr int BYTES = 2 * SET;
     static_assert(M % 16 == 0 && D % 16 == 0 && C0 % 16 == 0, "tile multiples");
 };
 
-template <int M, int D, int C0>
+template <int M, int D, int C0, bool LIN1 = false>
 constexpr bool readout_fits() {
-    return ReadCfg<M, D, C0>::BYTES <= 160 * 1024;
+    return ReadCfg<M, D, C0, LIN1>::BYTES <= 160 * 1024;
 }
 
 // Register inputs of one sub-block for one lane.
 template <class G>
 struct RdIn {
     f32x4 g[G::MPW][G::TB], k[G::MPW][G::TB];  // slot 16mb + lc, tokens 16tb + 4lg + (0..3)
+    f32x4 e[G::MPW][G::TB];                     // first linearisation only
     f32x4 h[G::TB];                             // column 16w + lc, same tokens
     uint16_t q[G::MPW][G::TB][4];               // q of those (token, slot) pairs, bf16
 };
@@ -91,6 +97,7 @@ __device__ __forceinline__ void rd_load(RdIn<G>& in, const Params& p, const Work
             const int64_t o = ws_frag(mb, tc0 / 16 + tb, C / 16, lane);
             in.g[mi][tb] = *reinterpret_cast<const f32x4*>(ws.g + o);
             in.k[mi][tb] = *reinterpret_cast<const f32x4*>(ws.k + o);
+            if constexpr (G::LIN1_) in.e[mi][tb] = *reinterpret_cast<const f32x4*>(ws.e + o);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int64_t row = (static_cast<int64_t>(b) * p.T + t0 + 16 * tb + 4 * lg + r) * p.H + hd;
@@ -114,20 +121,25 @@ __device__ __forceinline__ void rd_load_z(u32x4 (&z)[M / 16], const float* src) 
 #pragma unroll
     for (int mt = 0; mt < M / 16; ++mt) z[mt] = *reinterpret_cast<const u32x4*>(src + z_frag<D>(mt, w, lane));
 }
+__device__ __forceinline__ void rd_unpack_z1(f32x4& z, const u32x4& v) {
+    z[0] = __uint_as_float(v[0] << 16) + __uint_as_float(v[2] << 16);
+    z[1] = __uint_as_float(v[0] & 0xffff0000u) + __uint_as_float(v[2] & 0xffff0000u);
+    z[2] = __uint_as_float(v[1] << 16) + __uint_as_float(v[3] << 16);
+    z[3] = __uint_as_float(v[1] & 0xffff0000u) + __uint_as_float(v[3] & 0xffff0000u);
+}
 template <int M>
 __device__ __forceinline__ void rd_unpack_z(f32x4 (&z)[M / 16], const u32x4 (&v)[M / 16]) {
 #pragma unroll
-    for (int mt = 0; mt < M / 16; ++mt) {
-        z[mt][0] = __uint_as_float(v[mt][0] << 16) + __uint_as_float(v[mt][2] << 16);
-        z[mt][1] = __uint_as_float(v[mt][0] & 0xffff0000u) + __uint_as_float(v[mt][2] & 0xffff0000u);
-        z[mt][2] = __uint_as_float(v[mt][1] << 16) + __uint_as_float(v[mt][3] << 16);
-        z[mt][3] = __uint_as_float(v[mt][1] & 0xffff0000u) + __uint_as_float(v[mt][3] & 0xffff0000u);
-    }
+    for (int mt = 0; mt < M / 16; ++mt) rd_unpack_z1(z[mt], v[mt]);
 }
 
-template <int M, int D, int C0>
+// LIN1: the first chunk linearisation (eq. recurrence_linear1): every token
+// also adds e (.) Z, Z the chunk-start state, so with E_t the running sum of
+// e_j / A_j inside the sub-block
+//   Y  += (Q (.) A (.) E) Z,   R <- ... + diag(A_end E_end) Z.
+template <int M, int D, int C0, bool LIN1 = false>
 __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
-    using G = ReadCfg<M, D, C0>;
+    using G = ReadCfg<M, D, C0, LIN1>;
     constexpr int MT = G::MT, TB = G::TB;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
     const int C = p.chunk, NC = p.T / C, SPC = C / C0;
@@ -141,11 +153,16 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
 
     f32x4 acc[MT];  // R tiles: acc[mt][r] = R[16mt + 4lg + r][dcol]
     u32x4 zn[MT];   // next chunk's Z (packed hi/lo)
+    u32x4 zc[MT];   // this chunk's Z (packed hi/lo; first linearisation)
     RdIn<G> cur, nxt;
     {
         const Workspace ws = workspace_at<M, D>(p, bh, ch0);
         rd_load_z<M, D>(zn, ws.z);
         rd_unpack_z<M>(acc, zn);
+        if constexpr (LIN1) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) zc[mt] = zn[mt];
+        }
         rd_load<G>(cur, p, ws, b, hd, ch0 * C, 0);
     }
     for (int s = 0; s < NS; ++s) {
@@ -159,6 +176,9 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
         short* wth = reinterpret_cast<short*>(buf + G::B_WH);
         short* wtl = reinterpret_cast<short*>(buf + G::B_WL);
         float* aend = reinterpret_cast<float*>(buf + G::B_AE);
+        short* zqh = reinterpret_cast<short*>(buf + G::B_ZH);
+        short* zql = reinterpret_cast<short*>(buf + G::B_ZL);
+        float* aez = reinterpret_cast<float*>(buf + G::B_AZ);
         const bool last_in_chunk = sl + 1 == SPC;
 
         // Inputs of the next sub-block (the last one re-reads its own).
@@ -182,18 +202,40 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
                     const f32x4 g = cur.g[mi][tb];
                     rows4_prod_scan(g[0] * g[1] * g[2] * g[3], lg, below[tb], above[tb], tot[tb]);
                 }
-                // A (running product, inclusive), Q.A and kappa/A, token-major.
-                float fwd = 1.f;
+                // A (running product, inclusive), Q.A and kappa/A, token-major;
+                // first linearisation: E (running sum of e/A, inclusive) and Q.A.E.
+                float fwd = 1.f, esum = 0.f;
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
                     const f32x4 g = cur.g[mi][tb], kp = cur.k[mi][tb];
                     float a = fwd * below[tb];
-                    f32x4 qa, ka;
+                    float E = 0.f;
+                    f32x4 ea;
+                    if constexpr (LIN1) {
+                        // e/A of this lane's tokens, then the sums of the lane rows below
+                        const f32x4 e = cur.e[mi][tb];
+                        float a2 = a, es = 0.f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            a2 *= g[r];
+                            ea[r] = e[r] / a2;
+                            es += ea[r];
+                        }
+                        float es_below, es_tot;
+                        rows4_sum_scan(es, lg, es_below, es_tot);
+                        E = esum + es_below;
+                        esum += es_tot;
+                    }
+                    f32x4 qa, ka, qz;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         a *= g[r];
                         qa[r] = bf16u(cur.q[mi][tb][r]) * a;
                         ka[r] = kp[r] / a;
+                        if constexpr (LIN1) {
+                            E += ea[r];
+                            qz[r] = qa[r] * E;
+                        }
                     }
                     s16x4 qh, ql, kh, kl;
                     split4(qa, qh, ql);
@@ -204,6 +246,12 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
                     *reinterpret_cast<s16x4*>(qal + o) = tr16(ql, eye);
                     *reinterpret_cast<s16x4*>(kah + o) = tr16(kh, eye);
                     *reinterpret_cast<s16x4*>(kal + o) = tr16(kl, eye);
+                    if constexpr (LIN1) {
+                        s16x4 zh, zl;
+                        split4(qz, zh, zl);
+                        *reinterpret_cast<s16x4*>(zqh + o) = tr16(zh, eye);
+                        *reinterpret_cast<s16x4*>(zql + o) = tr16(zl, eye);
+                    }
                     fwd *= tot[tb];
                 }
                 // W_t = kappa_t (.) prod_{l > t} g_l, slot-major.
@@ -224,7 +272,10 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
                     *reinterpret_cast<s16x4*>(wtl + slot * G::WT_LD + 16 * tb + 4 * lg) = wl;
                     bwd *= tot[tb];
                 }
-                if (lg == 0) aend[slot] = fwd;
+                if (lg == 0) {
+                    aend[slot] = fwd;
+                    if constexpr (LIN1) aez[slot] = fwd * esum;
+                }
             }
         }
         __syncthreads();  // Q.A, kappa/A, W^T, A_end visible
@@ -277,6 +328,12 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
             for (int mt = 0; mt < MT; ++mt) {
                 const int qo = (16 * tb + lc) * G::QA_LD + 16 * mt + 4 * lg;
                 yt[tb] = mma3(ld4s(qah + qo), ld4s(qal + qo), rh[mt], rl[mt], yt[tb]);
+                if constexpr (LIN1) {
+                    // (Q.A.E) Z with Z's own hi/lo split as the B operand
+                    const s16x4 zh = __builtin_bit_cast(s16x4, u32x2{zc[mt][0], zc[mt][1]});
+                    const s16x4 zl = __builtin_bit_cast(s16x4, u32x2{zc[mt][2], zc[mt][3]});
+                    yt[tb] = mma3(ld4s(zqh + qo), ld4s(zql + qo), zh, zl, yt[tb]);
+                }
             }
         }
         __syncthreads();  // P^T tiles visible
@@ -306,6 +363,13 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
                 f32x4 a = acc[mt];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) a[r] *= ae[r];
+                if constexpr (LIN1) {
+                    const f32x4 az = *reinterpret_cast<const f32x4*>(aez + 16 * mt + 4 * lg);
+                    f32x4 zf;
+                    rd_unpack_z1(zf, zc[mt]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a[r] = fmaf(zf[r], az[r], a[r]);
+                }
                 if constexpr (G::K32_C) {
 #pragma unroll
                     for (int kt = 0; kt < C0 / 32; ++kt) {
@@ -321,6 +385,10 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
             }
         } else {
             rd_unpack_z<M>(acc, zn);
+            if constexpr (LIN1) {
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt) zc[mt] = zn[mt];
+            }
         }
         cur = nxt;
     }

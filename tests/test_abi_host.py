@@ -88,14 +88,25 @@ def test_bad_descriptor(field, value, status):
     assert _call("lattice_osr_fwd_chunked", d, _ptrs(d), 4) == status
 
 
-def test_first_linearisation_needs_no_workspace():
-    """The first linearisation runs on the token-loop kernel: no workspace at
-    any chunk size, where the default needs one for bf16 inputs and C >= 16."""
-    d2 = osr.make_desc(2, 256, 4, 64, 64)
-    d1 = osr.make_desc(2, 256, 4, 64, 64, linearisation=osr.LIN1)
-    assert osr.lattice_osr_workspace_bytes(d2, 64) > 0
-    for C in (1, 4, 16, 64):
+def test_first_linearisation_workspace():
+    """bf16 inputs with C >= 16 run both linearisations on the split MFMA
+    schedule; the first keeps one more per-chunk array (e, m x C fp32).  The
+    token loop (fp32 inputs or C < 16) needs none."""
+    B, T, H, m, d = 2, 256, 4, 64, 64
+    d2 = osr.make_desc(B, T, H, m, d)
+    d1 = osr.make_desc(B, T, H, m, d, linearisation=osr.LIN1)
+    for C in (16, 64):
+        extra = B * H * (T // C) * m * C * 4
+        assert osr.lattice_osr_workspace_bytes(d1, C) == osr.lattice_osr_workspace_bytes(d2, C) + extra
+    for C in (1, 4):
         assert osr.lattice_osr_workspace_bytes(d1, C) == 0
+    f1 = osr.make_desc(B, T, H, m, d, in_dtype=osr.F32, linearisation=osr.LIN1)
+    assert osr.lattice_osr_workspace_bytes(f1, 64) == 0
+    # many sequences: the default switches to the fused kernel (no workspace), the first stays split
+    big2 = osr.make_desc(64, 256, 8, m, d)
+    big1 = osr.make_desc(64, 256, 8, m, d, linearisation=osr.LIN1)
+    assert osr.lattice_osr_workspace_bytes(big2, 64) == 0
+    assert osr.lattice_osr_workspace_bytes(big1, 64) > 0
 
 
 def test_chunk_size_rules():

@@ -178,9 +178,28 @@ def _oracle_lin1(inp, C, mode):
     return oracle.osr_forward(q, k, v, g, mu, S, chunk_size=C, mode=mode, linearisation=oracle.LIN1)
 
 
+def _encoding_layer_bar(inp, C, yr, Sr):
+    """Bar for the encoding layer with the first linearisation on the matrix
+    cores, derived from the oracle itself: its largest relative change (y or
+    state, max-abs over RMS) when every input is perturbed by 2^-17 relative,
+    the precision of the hi + lo bf16 operands of the split products; never
+    below the standard bar.  This recurrence amplifies perturbations (at
+    m = d = 128, C = 16, 256 tokens that change reaches 0.18), the decoding
+    and similarity ones damp them."""
+    a = list(inp.values_f64())
+    rng = np.random.default_rng(17)
+    a2 = [x * (1 + 2.0 ** -17 * rng.standard_normal(x.shape)) for x in a]
+    y2, S2 = oracle.osr_forward(*a2, chunk_size=C, mode=osr.MODE_ENC, linearisation=oracle.LIN1)
+    sens = max(_rel(y2, yr), _rel(S2, Sr))
+    _say(f"  oracle sensitivity at 2^-17: {sens:.2e}")
+    return max(TOL[inp.in_dtype], sens)
+
+
 def _check_lin1(inp, y, S, C, mode):
     tol = TOL[inp.in_dtype]
     yr, Sr = _oracle_lin1(inp, C, mode)
+    if mode == osr.MODE_ENC and inp.in_dtype == synth.BF16 and C >= 16:
+        tol = _encoding_layer_bar(inp, C, yr, Sr)
     ey, es = _rel(y.float().cpu().numpy(), yr), _rel(S.cpu().numpy(), Sr)
     _say(f"  y err/rms = {ey:.3e}, state err/rms = {es:.3e} (tol {tol:g})")
     assert ey <= tol and es <= tol, (ey, es)
