@@ -302,9 +302,9 @@ def main() -> int:
                                                      ("chunked_b1h16_t65536_m128d128_c128", "chunked", 128, 2, 0, 0),
                                                      (HEADLINE, "recurrent", 1, 2, 0, 0),
                                                      (HEADLINE, "chunked", 64, 10, 2, 0),
-                                                     (HEADLINE, "chunked", 64, 2, 0, 1),
+                                                     (HEADLINE, "chunked", 64, 10, 0, 1),
                                                      (HEADLINE, "backward", 64, 2, 0, 0)):
-            c = Case(name, entry, chunk, copies=8 if name == HEADLINE and entry == "chunked" and not lin else 1,
+            c = Case(name, entry, chunk, copies=8 if name == HEADLINE and entry == "chunked" else 1,
                      mode=mode, linearisation=lin)
             t_ms = time_case(c, steps, 1)
             ab = algorithmic_bytes_bwd(c.w) if entry == "backward" else algorithmic_bytes(c.w)

@@ -116,10 +116,12 @@ typedef struct {
  * tokens takes its projections, gates and (decoding objective) h_t from the
  * chunk-start state (eq. recurrence_linear2, the gated-linear-attention form
  * of the section "Parallel and Hardware Efficient Form", or eq.
- * recurrence_linear1 with desc->linearisation = LATTICE_OSR_LIN1, which runs
- * on the token-loop kernel); C = 1 is the exact recurrence.  Requires T % chunk_size == 0 and chunk_size a power of two in
- * [1, 128].  workspace must hold lattice_osr_workspace_bytes(desc, chunk_size)
- * bytes (it may be NULL when that is 0); its contents on entry are ignored.
+ * recurrence_linear1 with desc->linearisation = LATTICE_OSR_LIN1); C = 1 is
+ * the exact recurrence.  Requires T % chunk_size == 0 and chunk_size a power
+ * of two in [1, 128].  workspace must hold lattice_osr_workspace_bytes(desc,
+ * chunk_size) bytes (it may be NULL when that is 0; bf16 inputs with
+ * chunk_size >= 16 need one unless many sequences take the default
+ * linearisation's fused kernel); its contents on entry are ignored.
  */
 LATTICE_OSR_API int lattice_osr_fwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size,
                             const void* q, const void* k, const void* v, const void* gamma,

@@ -451,3 +451,33 @@ def test_chain_pairs_agree(monkeypatch):
     y0, S0 = _run("chunked", inp, 64)
     assert (y1 - y0).abs().max().item() <= 2e-4 * y0.abs().max().item()
     assert (S1 - S0).abs().max().item() <= 1e-4
+
+
+@pytest.mark.parametrize("pairs", ["1", "0"])
+@pytest.mark.parametrize("m,d,C", [(32, 32, 64), (16, 64, 64), (32, 128, 32), (64, 128, 64), (128, 64, 128)])
+def test_chain_pairs_first_linearisation(monkeypatch, pairs, m, d, C):
+    """The first linearisation on the matrix cores, with the state passing in
+    both its pair and one-wave forms (where a chunk is one sub-block) and in
+    sub-blocks (m64 d128 C64, m128 d64 C128), several chunks, all objectives."""
+    _say(f"first linearisation, state passing pairs={pairs} m={m} d={d} C={C}")
+    monkeypatch.setenv("LATTICE_OSR_CHAIN_PAIRS", pairs)
+    for mode in (osr.MODE_DEC, osr.MODE_SIM, osr.MODE_ENC):
+        inp = synth.make_inputs(2, 4 * C, 2, m, d, seed=900 + m + d + C + mode, in_dtype=synth.BF16)
+        t = osr.to_device(inp)
+        y, S = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], C,
+                                           mode=mode, linearisation=osr.LIN1)
+        torch.cuda.synchronize()
+        _check_lin1(inp, y, S, C, mode)
+
+
+def test_first_linearisation_ignores_fused_override(monkeypatch):
+    """The first linearisation runs on the split schedule even where the
+    default would take the fused kernel (many sequences) or it is asked for."""
+    _say("first linearisation with LATTICE_OSR_CHUNK_SCHEDULE=fused, B32 H8 m64 d64 C64")
+    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "fused")
+    inp = synth.make_inputs(32, 128, 8, 64, 64, seed=950, in_dtype=synth.BF16)
+    t = osr.to_device(inp)
+    y, S = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], 64,
+                                       linearisation=osr.LIN1)
+    torch.cuda.synchronize()
+    _check_lin1(inp, y, S, 64, osr.MODE_DEC)
