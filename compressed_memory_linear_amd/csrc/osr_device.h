@@ -25,7 +25,7 @@ struct Params {
     int chunk;         // C
     int gamma_per_slot;
     int mode;          // 0 = decoding objective, 1 = similarity objective, 2 = encoding layer
-    int lin1;          // 1: first chunk linearisation (token-loop kernel only)
+    int lin1;          // 1: first chunk linearisation (token loop, or the split MFMA schedule)
     int y_bf16;        // 1: y is bf16, 0: y is fp32
 };
 

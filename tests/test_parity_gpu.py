@@ -172,7 +172,8 @@ def test_bf16_modes_and_gamma_layouts(mode, per_slot):
 
 
 # ---------------------------------------------- first chunk linearisation --
-# eq. recurrence_linear1 (desc linearisation = LIN1), on the token-loop kernel.
+# eq. recurrence_linear1 (desc linearisation = LIN1): the token loop for fp32 inputs
+# or C < 16, the split matrix-core schedule for bf16 inputs with C >= 16.
 def _oracle_lin1(inp, C, mode):
     q, k, v, g, mu, S = inp.values_f64()
     return oracle.osr_forward(q, k, v, g, mu, S, chunk_size=C, mode=mode, linearisation=oracle.LIN1)
