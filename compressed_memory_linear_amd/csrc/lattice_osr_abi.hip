@@ -106,6 +106,8 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     p.state_out = sout;
     p.y = y;
     p.zbuf = static_cast<float*>(ws);
+    p.raw = nullptr;
+    p.raw_stride = 0;
     p.B = d->B;
     p.T = d->T;
     p.H = d->H;
@@ -158,6 +160,22 @@ int check_bwd_buffers(const lattice_osr_desc* d, const void* q, const void* k, c
             if (overlap(outs[i], outs[j])) return LATTICE_OSR_ERR_ALIAS;
     }
     return LATTICE_OSR_OK;
+}
+
+// The backward takes its chunk-start states from the matrix-core state-passing
+// kernel where the forward would run on it (bf16 inputs, C >= 16), except for
+// the encoding layer, whose gradient is too sensitive to the split products'
+// rounding; otherwise its own fp32 forward pass finds them.
+bool bwd_uses_chain(const lattice_osr_desc* d, int C) {
+    return d->in_dtype == LATTICE_OSR_BF16 && C >= 16 && osr::mfma_supported(d->m, d->d, C) &&
+           d->mode != LATTICE_OSR_MODE_ENC;
+}
+
+size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
+    size_t n = osr::bwd_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C);
+    if (bwd_uses_chain(d, C))
+        n += osr::mfma_chain_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1);
+    return n;
 }
 
 // Shape rules of the backward: those of the chunked forward.
@@ -245,7 +263,7 @@ extern "C" {
 
 size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* desc, int32_t chunk_size) {
     if (check_bwd_desc(desc, chunk_size) != LATTICE_OSR_OK) return static_cast<size_t>(-1);
-    return osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
+    return bwd_workspace_needed(desc, chunk_size);
 }
 
 int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, const void* q, const void* k,
@@ -255,10 +273,23 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
                             size_t workspace_bytes, void* hip_stream) {
     int rc = check_bwd_desc(desc, chunk_size);
     if (rc) return rc;
-    const size_t need = osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
+    const size_t need = bwd_workspace_needed(desc, chunk_size);
     rc = check_bwd_buffers(desc, q, k, v, gamma, mu, state_in, dy, dstate_out, dq, dk, dv, dgamma, dmu,
                            dstate_in, workspace, workspace_bytes, need);
     if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    const bool chain = bwd_uses_chain(desc, chunk_size);
+    if (chain) {
+        // chunk-start states (before projection) straight into the backward's part of the
+        // workspace; the state-passing kernel's own per-chunk arrays follow it
+        const size_t bwd_bytes = osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
+        osr::Params pc = make_params(desc, chunk_size, q, k, v, gamma, mu, state_in, nullptr, nullptr,
+                                     static_cast<char*>(workspace) + bwd_bytes);
+        pc.raw = static_cast<float*>(workspace);
+        pc.raw_stride = static_cast<int64_t>(bwd_bytes / sizeof(float)) / (static_cast<int64_t>(desc->B) * desc->H);
+        rc = osr::launch_mfma_chain_only(desc->m, desc->d, pc, st);
+        if (rc) return rc;
+    }
     osr::BwdParams p;
     p.f = make_params(desc, chunk_size, q, k, v, gamma, mu, state_in, nullptr, nullptr, nullptr);
     p.dy = dy;
@@ -271,8 +302,8 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
     p.dstate_in = dstate_in;
     p.ws = static_cast<float*>(workspace);
     p.dy_bf16 = desc->y_dtype == LATTICE_OSR_BF16 ? 1 : 0;
-    return osr::launch_bwd(desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16,
-                           static_cast<hipStream_t>(hip_stream));
+    p.states_ready = chain ? 1 : 0;
+    return osr::launch_bwd(desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, st);
 }
 
 }  // extern "C"

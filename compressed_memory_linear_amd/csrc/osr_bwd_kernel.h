@@ -171,11 +171,14 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     int nred = 0;  // LDS exchanges so far: consecutive ones use alternate halves of red
 
     // ---- phase 1: forward, keeping every chunk-start state ----
+    // (skipped when the state-passing kernel has stored them: then only the end
+    // state is read back)
     float4 r[L::RPT], z[L::RPT];
-    const float* sin = p.f.state_in + static_cast<int64_t>(bh) * M * D;
+    const float* sin = p.states_ready ? sck + static_cast<int64_t>(NC) * M * D
+                                      : p.f.state_in + static_cast<int64_t>(bh) * M * D;
 #pragma unroll
     for (int i = 0; i < L::RPT; ++i) r[i] = *reinterpret_cast<const float4*>(sin + el(i));
-    for (int n = 0; n < NC; ++n) {
+    for (int n = 0; n < (p.states_ready ? 0 : NC); ++n) {
 #pragma unroll
         for (int i = 0; i < L::RPT; ++i) *reinterpret_cast<float4*>(sck + static_cast<int64_t>(n) * M * D + el(i)) = r[i];
         project_rows<L>(r);
@@ -198,8 +201,10 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
             muc = mun;
         }
     }
+    if (!p.states_ready) {
 #pragma unroll
-    for (int i = 0; i < L::RPT; ++i) *reinterpret_cast<float4*>(sck + static_cast<int64_t>(NC) * M * D + el(i)) = r[i];
+        for (int i = 0; i < L::RPT; ++i) *reinterpret_cast<float4*>(sck + static_cast<int64_t>(NC) * M * D + el(i)) = r[i];
+    }
 
     // ---- the returned state is the end state projected: its backward ----
     float4 dR[L::RPT];

@@ -21,6 +21,9 @@ struct Params {
     float* state_out;
     void* y;
     float* zbuf;       // chunk-start states [B,H,NC,m,d] (split chunk path only)
+    float* raw;        // if set (backward): every chunk-start state before projection, and the
+                       // end state, row-major [m][d], at raw + bh * raw_stride + n * m * d
+    int64_t raw_stride;
     int B, T, H;
     int chunk;         // C
     int gamma_per_slot;

@@ -19,6 +19,11 @@ int launch_valu(bool decode, int m, int d, const Params& p, bool in_bf16, hipStr
 // followed by the read-out kernel (split schedule), or the fused kernel.
 bool mfma_supported(int m, int d, int C);
 size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1);
+// The split schedule's per-chunk workspace whatever the schedule choice, and
+// the state-passing kernel alone (the backward takes its chunk-start states
+// from it, through Params::raw).
+size_t mfma_chain_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1);
+int launch_mfma_chain_only(int m, int d, const Params& p, hipStream_t st);
 int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st);
 
 // Backward of the chunk-wise forward (fp32 VALU, one workgroup per (b,h)).
@@ -36,6 +41,7 @@ struct BwdParams {
     float* dstate_in;        // [B,H,m,d]
     float* ws;               // bwd_workspace_bytes(...)
     int dy_bf16;
+    int states_ready;        // 1: the chunk-start states are already in the workspace
 };
 size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C);
 int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);

@@ -19,6 +19,8 @@ namespace osr {
 namespace mfma {
 template <int M>
 int launch_m(int d, bool split, const Params& p, hipStream_t st);
+template <int M>
+int launch_chain_m(int d, const Params& p, hipStream_t st);
 extern template int launch_m<16>(int, bool, const Params&, hipStream_t);
 extern template int launch_m<32>(int, bool, const Params&, hipStream_t);
 extern template int launch_m<64>(int, bool, const Params&, hipStream_t);
@@ -44,13 +46,27 @@ bool mfma_supported(int m, int d, int C) {
     return dims && C >= 16 && C <= 128 && (C & (C - 1)) == 0;
 }
 
-// The first linearisation runs on the split schedule only.
-size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1) {
-    if (!lin1 && !mfma::use_split(B, H, d)) return 0;
+size_t mfma_chain_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1) {
     // per (b,h,chunk): Z [m][d], g and kappa [m][C], h [d][C] (and e [m][C]), fp32
     const size_t per_chunk = static_cast<size_t>(m) * d + (lin1 ? 3 : 2) * static_cast<size_t>(m) * C +
                              static_cast<size_t>(d) * C;
     return static_cast<size_t>(B) * H * (T / C) * per_chunk * sizeof(float);
+}
+
+// The first linearisation runs on the split schedule only.
+size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1) {
+    if (!lin1 && !mfma::use_split(B, H, d)) return 0;
+    return mfma_chain_workspace_bytes(B, H, T, m, d, C, lin1);
+}
+
+int launch_mfma_chain_only(int m, int d, const Params& p, hipStream_t st) {
+    switch (m) {
+        case 16: return mfma::launch_chain_m<16>(d, p, st);
+        case 32: return mfma::launch_chain_m<32>(d, p, st);
+        case 64: return mfma::launch_chain_m<64>(d, p, st);
+        case 128: return mfma::launch_chain_m<128>(d, p, st);
+        default: return -3;
+    }
 }
 
 int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st) {

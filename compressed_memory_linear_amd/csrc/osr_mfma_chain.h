@@ -196,6 +196,13 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         const int tc0 = ONE ? 0 : (s % SPC) * C0;
 
         if (chunk_start) {
+            if (p.raw && grp == 0) {
+                // the chunk-start state before projection, for the backward
+                float* dst = p.raw + bh * p.raw_stride + static_cast<int64_t>(chunk) * M * D +
+                             static_cast<int64_t>(slot) * D + 4 * lg;
+#pragma unroll
+                for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
+            }
             const float inv = row_inv_norm<DB>(acc);
 #pragma unroll
             for (int j = 0; j < DB; ++j)
@@ -552,8 +559,14 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         }
     }
 
+    if (p.raw && grp == 0) {
+        float* dst = p.raw + bh * p.raw_stride + static_cast<int64_t>(p.T / C) * M * D +
+                     static_cast<int64_t>(slot) * D + 4 * lg;
+#pragma unroll
+        for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
+    }
     const float inv = row_inv_norm<DB>(acc);
-    if (grp == 0) {
+    if (grp == 0 && p.state_out) {
         float* dst = p.state_out + static_cast<int64_t>(bh) * M * D + static_cast<int64_t>(slot) * D + 4 * lg;
 #pragma unroll
         for (int j = 0; j < DB; ++j) {
