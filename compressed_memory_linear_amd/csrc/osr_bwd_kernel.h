@@ -41,10 +41,11 @@
 //
 // One workgroup per (b,h), state in registers in the layout of osr_valu.h.
 // Phase 1 runs the forward and keeps every chunk-start state (before
-// projection) in the workspace.  Phase 2 walks the chunks backwards: it forms
-// the chunk's h in LDS, runs the chunk forward again from its stored start
-// (keeping the state before each token and the per-token c, beta, |h|^2 in the
-// workspace), then walks the chunk's tokens backwards.
+// projection) in the workspace, unless the matrix-core state-passing kernel
+// has already stored them there (states_ready).  Phase 2 walks the chunks
+// backwards: it forms the chunk's h in LDS, runs the chunk forward again from
+// its stored start (keeping the state before each token and the per-token c,
+// beta, |h|^2 in the workspace), then walks the chunk's tokens backwards.
 #pragma once
 
 #include "osr_launch.h"
@@ -66,7 +67,7 @@ __host__ __device__ inline int64_t bwd_floats_per_bh(int T, int C) {
 
 // One forward token given its h: updates r, returns the per-slot c and beta
 // and |h|^2 (valid in every thread of a row group).  No cross-wave exchange.
-// lin1: the first chunk linearisation, r_i <- mu beta_i r_i + beta_i a_i c_i z_i
+// LIN1: the first chunk linearisation, r_i <- mu beta_i r_i + beta_i a_i c_i z_i
 // + kap_i h (eq. recurrence_linear1).
 template <class L, bool LIN1>
 __device__ __forceinline__ void fwd_token_h(const float4 (&z)[L::RPT], float4 (&r)[L::RPT], const float (&k)[L::RPT],
