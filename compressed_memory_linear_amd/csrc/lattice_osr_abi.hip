@@ -303,6 +303,15 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
     p.ws = static_cast<float*>(workspace);
     p.dy_bf16 = desc->y_dtype == LATTICE_OSR_BF16 ? 1 : 0;
     p.states_ready = chain ? 1 : 0;
+    p.chain_h = nullptr;
+    if (chain) {
+        // h of every chunk in the state-passing kernel's part of the workspace, after its
+        // Z [m][d] and g, kappa [m][C] arrays
+        const size_t bwd_bytes = osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
+        const int64_t nch = static_cast<int64_t>(desc->B) * desc->H * (desc->T / chunk_size);
+        const float* zb = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + bwd_bytes);
+        p.chain_h = zb + nch * desc->m * desc->d + 2 * nch * desc->m * chunk_size;
+    }
     return osr::launch_bwd(desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, st);
 }
 

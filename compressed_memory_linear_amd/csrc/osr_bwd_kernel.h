@@ -238,7 +238,20 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
             }
         }
         __syncthreads();  // the previous chunk's reverse walk is done with hbuf, red and the records
-        chunk_h<L, M, D, TIn>(z, p.f, bth_of(n * C), tstride, C, mode, hbuf, red, nred, tid, lane, wave, rg, cg);
+        if (p.chain_h && mode == 0) {
+            // the chunk's h as the state-passing kernel formed it (lane (lg, lc) of the
+            // fragment for column block jb and token tile tb holds h[16tb + 4lg + r][16jb + lc])
+            const float* hs = p.chain_h + (static_cast<int64_t>(bh) * NC + n) * D * C;
+            for (int idx = tid; idx < C * D; idx += NT) {
+                const int tau = idx / D, j = idx % D;
+                const int lane_f = ((tau & 15) >> 2) * 16 + (j & 15);
+                hbuf[idx] = hs[((static_cast<int64_t>(j >> 4) * (C >> 4) + (tau >> 4)) * 64 + lane_f) * 4 + (tau & 3)];
+            }
+            __syncthreads();
+        } else {
+            chunk_h<L, M, D, TIn>(z, p.f, bth_of(n * C), tstride, C, mode, hbuf, red, nred, tid, lane, wave, rg,
+                                  cg);
+        }
 
         // forward again over the chunk, keeping what the reverse walk needs
         {

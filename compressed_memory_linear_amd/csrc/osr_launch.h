@@ -42,6 +42,8 @@ struct BwdParams {
     float* ws;               // bwd_workspace_bytes(...)
     int dy_bf16;
     int states_ready;        // 1: the chunk-start states are already in the workspace
+    const float* chain_h;    // with states_ready: the state-passing kernel's h of every chunk,
+                             // [B*H*NC][d/16][C/16][64 lanes][4] (its workspace layout)
 };
 size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C);
 int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
