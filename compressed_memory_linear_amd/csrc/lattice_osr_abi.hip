@@ -108,6 +108,7 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     p.zbuf = static_cast<float*>(ws);
     p.raw = nullptr;
     p.raw_stride = 0;
+    p.raw_c = p.raw_b = p.raw_hh = nullptr;
     p.B = d->B;
     p.T = d->T;
     p.H = d->H;
@@ -171,10 +172,19 @@ bool bwd_uses_chain(const lattice_osr_desc* d, int C) {
            d->mode != LATTICE_OSR_MODE_ENC;
 }
 
+// With the state-passing kernel, the backward's workspace is its own part, then
+// that kernel's per-chunk arrays (Z, g, kappa, h[, e]), then c, beta (m x C)
+// and |h|^2 (C) of every chunk.
+size_t bwd_chain_extra_bytes(const lattice_osr_desc* d, int C) {
+    const size_t nch = static_cast<size_t>(d->B) * d->H * (d->T / C);
+    return nch * (2 * static_cast<size_t>(d->m) * C + C) * sizeof(float);
+}
+
 size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
     size_t n = osr::bwd_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C);
     if (bwd_uses_chain(d, C))
-        n += osr::mfma_chain_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1);
+        n += osr::mfma_chain_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1) +
+             bwd_chain_extra_bytes(d, C);
     return n;
 }
 
@@ -283,10 +293,17 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
         // chunk-start states (before projection) straight into the backward's part of the
         // workspace; the state-passing kernel's own per-chunk arrays follow it
         const size_t bwd_bytes = osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
+        const bool lin1 = desc->linearisation == LATTICE_OSR_LIN1;
+        const size_t chain_bytes =
+            osr::mfma_chain_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size, lin1);
+        const int64_t nch = static_cast<int64_t>(desc->B) * desc->H * (desc->T / chunk_size);
         osr::Params pc = make_params(desc, chunk_size, q, k, v, gamma, mu, state_in, nullptr, nullptr,
                                      static_cast<char*>(workspace) + bwd_bytes);
         pc.raw = static_cast<float*>(workspace);
         pc.raw_stride = static_cast<int64_t>(bwd_bytes / sizeof(float)) / (static_cast<int64_t>(desc->B) * desc->H);
+        pc.raw_c = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_bytes + chain_bytes);
+        pc.raw_b = pc.raw_c + nch * desc->m * chunk_size;
+        pc.raw_hh = pc.raw_b + nch * desc->m * chunk_size;
         rc = osr::launch_mfma_chain_only(desc->m, desc->d, pc, st);
         if (rc) return rc;
     }
@@ -303,14 +320,24 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
     p.ws = static_cast<float*>(workspace);
     p.dy_bf16 = desc->y_dtype == LATTICE_OSR_BF16 ? 1 : 0;
     p.states_ready = chain ? 1 : 0;
-    p.chain_h = nullptr;
+    p.chain_g = p.chain_k = p.chain_h = p.chain_e = p.chain_c = p.chain_b = p.chain_hh = nullptr;
     if (chain) {
-        // h of every chunk in the state-passing kernel's part of the workspace, after its
-        // Z [m][d] and g, kappa [m][C] arrays
+        // the state-passing kernel's arrays: Z [m][d], g, kappa [m][C], h [d][C] (e [m][C]) per
+        // chunk, then c, beta [m][C] and |h|^2 [C] per chunk
+        const bool lin1 = desc->linearisation == LATTICE_OSR_LIN1;
         const size_t bwd_bytes = osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
+        const size_t chain_bytes =
+            osr::mfma_chain_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size, lin1);
         const int64_t nch = static_cast<int64_t>(desc->B) * desc->H * (desc->T / chunk_size);
+        const int64_t mc = static_cast<int64_t>(desc->m) * chunk_size, dc = static_cast<int64_t>(desc->d) * chunk_size;
         const float* zb = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + bwd_bytes);
-        p.chain_h = zb + nch * desc->m * desc->d + 2 * nch * desc->m * chunk_size;
+        p.chain_g = zb + nch * desc->m * desc->d;
+        p.chain_k = p.chain_g + nch * mc;
+        p.chain_h = p.chain_k + nch * mc;
+        p.chain_e = lin1 ? p.chain_h + nch * dc : nullptr;
+        p.chain_c = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + bwd_bytes + chain_bytes);
+        p.chain_b = p.chain_c + nch * mc;
+        p.chain_hh = p.chain_b + nch * mc;
     }
     return osr::launch_bwd(desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, st);
 }

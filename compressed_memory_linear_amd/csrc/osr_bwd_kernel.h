@@ -120,18 +120,42 @@ struct RevIn {
     float4 rp[RPT];
 };
 
+// Offset of (row, token tau) in one chunk's per-slot array of the state-passing
+// kernel's workspace: lane (lg, lc) of the fragment for row block row/16 and
+// token tile tau/16 holds row 16 (row/16) + lc at tokens 16 (tau/16) + 4 lg .. +3.
+__device__ __forceinline__ int64_t gate_frag(int row, int tau, int C) {
+    return ((static_cast<int64_t>(row >> 4) * (C >> 4) + (tau >> 4)) * 64 + ((tau & 15) >> 2) * 16 + (row & 15)) * 4 +
+           (tau & 3);
+}
+
+// ch: this (b,h)'s chunk index b*H*NC + n, for the state-passing kernel's
+// records (chain_c set); otherwise the records are the kernel's own (trec).
 template <class L, int M, int D, typename TIn, bool PF_STATE>
 __device__ __forceinline__ void load_rev(RevIn<L::RPT>& x, const BwdParams& p, const float* trec,
-                                         const float* rtok, int64_t bth, int tau, int rg, int cg, int el0) {
+                                         const float* rtok, int64_t bth, int64_t ch, int tau, int rg, int cg,
+                                         int el0) {
     using TR = TokRec<M, D>;
     load_token<L, M, D, TIn>(x.in, p.f, bth, rg, cg);
-    const float* rec = trec + static_cast<int64_t>(tau) * TR::SIZE;
+    if (p.chain_c) {
+        const int C = p.f.chunk;
+        const float* cc = p.chain_c + ch * M * C;
+        const float* cb = p.chain_b + ch * M * C;
 #pragma unroll
-    for (int i = 0; i < L::RPT; ++i) {
-        x.c[i] = rec[TR::C_OFF + rg + L::RG * i];
-        x.beta[i] = rec[TR::B_OFF + rg + L::RG * i];
+        for (int i = 0; i < L::RPT; ++i) {
+            const int64_t o = gate_frag(rg + L::RG * i, tau, C);
+            x.c[i] = cc[o];
+            x.beta[i] = cb[o];
+        }
+        x.hh = p.chain_hh[ch * C + tau];
+    } else {
+        const float* rec = trec + static_cast<int64_t>(tau) * TR::SIZE;
+#pragma unroll
+        for (int i = 0; i < L::RPT; ++i) {
+            x.c[i] = rec[TR::C_OFF + rg + L::RG * i];
+            x.beta[i] = rec[TR::B_OFF + rg + L::RG * i];
+        }
+        x.hh = rec[TR::HH_OFF];
     }
-    x.hh = rec[TR::HH_OFF];
     x.dy = p.dy_bf16 ? ld4<uint16_t>(static_cast<const uint16_t*>(p.dy), bth * D + cg * 4)
                      : ld4<float>(static_cast<const float*>(p.dy), bth * D + cg * 4);
     if constexpr (PF_STATE) {
@@ -253,8 +277,42 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                                   cg);
         }
 
+        const int64_t ch = static_cast<int64_t>(bh) * NC + n;
         // forward again over the chunk, keeping what the reverse walk needs
-        {
+        if (p.chain_c) {
+            // elementwise, from the state-passing kernel's gates of this chunk
+            const float* gch = p.chain_g + ch * M * C;
+            const float* kch = p.chain_k + ch * M * C;
+            const float* ech = LIN1 ? p.chain_e + ch * M * C : nullptr;
+            float gcur[L::RPT], kcur[L::RPT], ecur[L::RPT] = {}, gnx[L::RPT], knx[L::RPT], enx[L::RPT] = {};
+            auto load_g = [&](int tau, float (&g)[L::RPT], float (&k)[L::RPT], float (&e)[L::RPT]) {
+#pragma unroll
+                for (int i = 0; i < L::RPT; ++i) {
+                    const int64_t o = gate_frag(rg + L::RG * i, tau, C);
+                    g[i] = gch[o];
+                    k[i] = kch[o];
+                    if constexpr (LIN1) e[i] = ech[o];
+                }
+            };
+            load_g(0, gcur, kcur, ecur);
+            for (int tau = 0; tau < C; ++tau) {
+#pragma unroll
+                for (int i = 0; i < L::RPT; ++i)
+                    *reinterpret_cast<float4*>(rtok + static_cast<int64_t>(tau) * M * D + el(i)) = r[i];
+                if (tau + 1 < C) load_g(tau + 1, gnx, knx, enx);
+                const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
+#pragma unroll
+                for (int i = 0; i < L::RPT; ++i) {
+                    if constexpr (LIN1)
+                        r[i] = fma4(gcur[i], r[i], fma4(ecur[i], z[i], kcur[i] * h));
+                    else
+                        r[i] = fma4(gcur[i], r[i], kcur[i] * h);
+                    gcur[i] = gnx[i];
+                    kcur[i] = knx[i];
+                    if constexpr (LIN1) ecur[i] = enx[i];
+                }
+            }
+        } else {
             float kc[L::RPT], gc[L::RPT], muc, kn[L::RPT], gn[L::RPT], mun;
             load_kgm<L, M, TIn>(p.f, bth_of(n * C), rg, kc, gc, muc);
             for (int tau = 0; tau < C; ++tau) {
@@ -299,7 +357,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
         }
         RevIn<L::RPT> rc, rn;
         if constexpr (PF_TOKEN)
-            load_rev<L, M, D, TIn, PF_STATE>(rc, p, trec, rtok, bth_of(n * C + C - 1), C - 1, rg, cg, el(0));
+            load_rev<L, M, D, TIn, PF_STATE>(rc, p, trec, rtok, bth_of(n * C + C - 1), ch, C - 1, rg, cg, el(0));
         for (int ub = C - nb; ub >= 0; ub -= nb) {
             float* rb = red + (nred++ & 1) * (BT * L::NW * W);
             float dcv[BT][L::RPT], kv[BT][L::RPT], dkin[BT][L::RPT];
@@ -310,10 +368,10 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                     const int64_t bth = bth_of(n * C + tau);
                     if constexpr (PF_TOKEN) {
                         if (tau > 0)
-                            load_rev<L, M, D, TIn, PF_STATE>(rn, p, trec, rtok, bth_of(n * C + tau - 1), tau - 1, rg,
-                                                             cg, el(0));
+                            load_rev<L, M, D, TIn, PF_STATE>(rn, p, trec, rtok, bth_of(n * C + tau - 1), ch, tau - 1,
+                                                             rg, cg, el(0));
                     } else {
-                        load_rev<L, M, D, TIn, false>(rc, p, trec, rtok, bth, tau, rg, cg, el(0));
+                        load_rev<L, M, D, TIn, false>(rc, p, trec, rtok, bth, ch, tau, rg, cg, el(0));
                     }
                     const TokenIn<L::RPT>& in = rc.in;
                     const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);

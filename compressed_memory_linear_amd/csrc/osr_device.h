@@ -24,6 +24,9 @@ struct Params {
     float* raw;        // if set (backward): every chunk-start state before projection, and the
                        // end state, row-major [m][d], at raw + bh * raw_stride + n * m * d
     int64_t raw_stride;
+    float* raw_c;      // if set (backward): c and beta of every token and slot, [B*H*NC][m*C] in
+    float* raw_b;      // the layout of the gates, and |h|^2 of every token, [B*H*NC][C]
+    float* raw_hh;
     int B, T, H;
     int chunk;         // C
     int gamma_per_slot;

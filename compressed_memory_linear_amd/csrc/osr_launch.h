@@ -42,8 +42,10 @@ struct BwdParams {
     float* ws;               // bwd_workspace_bytes(...)
     int dy_bf16;
     int states_ready;        // 1: the chunk-start states are already in the workspace
-    const float* chain_h;    // with states_ready: the state-passing kernel's h of every chunk,
-                             // [B*H*NC][d/16][C/16][64 lanes][4] (its workspace layout)
+    // With states_ready: the state-passing kernel's per-chunk arrays in its
+    // workspace layout ([B*H*NC][rows/16][C/16][64 lanes][4], rows = m or d):
+    // g, kappa, h, e (first linearisation) and c, beta; |h|^2 as [B*H*NC][C].
+    const float *chain_g, *chain_k, *chain_h, *chain_e, *chain_c, *chain_b, *chain_hh;
 };
 size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C);
 int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);

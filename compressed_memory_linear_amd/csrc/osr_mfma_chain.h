@@ -392,6 +392,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         float gt[TBW][4], kp[TBW][4], ev[TBW][4], tot[TBW], ex_lo[TBW], ex_hi[TBW];
         auto gates = [&](int i) {
             float prod = 1.f;
+            f32x4 bsave;  // beta of the tile's tokens (kept for the backward)
             f32x4 g4 = {0.f, 0.f, 0.f, 0.f};  // gamma of the tile, read again for the encoding layer only
             if (enc) g4 = tr16f(ld4s(gs + (16 * (tbg + i) + lc) * G::GS_LD + 16 * wv + 4 * lg), eye);
 #pragma unroll
@@ -400,6 +401,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                 const float a = enc ? fmaf(g4[r], cr, av[i][r]) : av[i][r];
                 const float wvv = fmaxf(fmaf(-cr, cr, hh[i][r]), 0.f);
                 const float beta = __builtin_amdgcn_rsqf(fmaf(mu, mu, a * a * wvv));
+                bsave[r] = beta;
                 if constexpr (LIN1) {
                     gt[i][r] = beta * mu;
                     ev[i][r] = beta * a * cr;
@@ -410,6 +412,18 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                 prod *= gt[i][r];
             }
             rows4_prod_scan(prod, lg, ex_lo[i], ex_hi[i], tot[i]);
+            if (p.raw_c) {
+                // c, beta and |h|^2 of these tokens, for the backward
+                const int64_t ch = static_cast<int64_t>(bh) * (p.T / C) + chunk;
+                const int64_t o = ch * M * C + ws_frag(wv, tc0 / 16 + tbg + i, C / 16, lane);
+                *reinterpret_cast<f32x4*>(p.raw_c + o) = cc[i];
+                *reinterpret_cast<f32x4*>(p.raw_b + o) = bsave;
+                if (wv == 0 && lc == 0) {
+                    float* dst = p.raw_hh + ch * C + tc0 + 16 * (tbg + i) + 4 * lg;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[r] = hh[i][r];
+                }
+            }
             if constexpr (WRITE_Z) {
                 const int64_t o = ws_frag(wv, tc0 / 16 + tbg + i, C / 16, lane);
                 *reinterpret_cast<f32x4*>(ws.g + o) = f32x4{gt[i][0], gt[i][1], gt[i][2], gt[i][3]};

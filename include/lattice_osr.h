@@ -175,8 +175,8 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * 4 C (2m + 4) bytes of per-token values, and, for bf16 inputs with
  * chunk_size >= 16 (decoding and similarity objectives, whose chunk-start
  * states then come from the matrix-core state-passing kernel), that kernel's
- * per-chunk arrays: 4 (m d + 2 m C + d C) bytes per chunk (4 m C more with
- * LATTICE_OSR_LIN1).  The remaining rules (shapes,
+ * per-chunk arrays: 4 (m d + 4 m C + d C + C) bytes per chunk (4 m C more
+ * with LATTICE_OSR_LIN1).  The remaining rules (shapes,
  * chunk sizes, alignment of the inputs, status codes, asynchrony) are those
  * of lattice_osr_fwd_chunked.
  */

@@ -208,7 +208,8 @@ def test_bwd_workspace_formula():
     """Per (b,h): 4 (T/C + 1 + C) m d bytes of states and 4 C (2m + 4)
     bytes of per-token values; with bf16 inputs and C >= 16 (not the encoding
     layer) also the state-passing kernel's per-chunk arrays, 4 (m d + 2 m C +
-    d C) bytes per chunk (one more m C with the first linearisation)."""
+    d C) bytes per chunk (one more m C with the first linearisation), and the
+    c, beta and |h|^2 it keeps for the backward, 4 (2 m C + C) per chunk."""
     for (B, T, H, m, dd, C) in ((4, 2048, 8, 64, 64, 64), (1, 64, 1, 16, 32, 1), (2, 512, 3, 128, 128, 128)):
         for in_dtype in (osr.BF16, osr.F32):
             for mode in (osr.MODE_DEC, osr.MODE_ENC):
@@ -218,6 +219,7 @@ def test_bwd_workspace_formula():
                     want = B * H * per
                     if in_dtype == osr.BF16 and C >= 16 and mode != osr.MODE_ENC:
                         per_chunk = m * dd + (3 if lin == osr.LIN1 else 2) * m * C + dd * C
+                        per_chunk += 2 * m * C + C  # c, beta and |h|^2 kept for the backward
                         want += B * H * (T // C) * per_chunk * 4
                     assert osr.lattice_osr_bwd_workspace_bytes(d, C) == want, (B, T, H, m, dd, C, in_dtype, mode, lin)
 
