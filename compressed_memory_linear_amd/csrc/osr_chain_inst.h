@@ -46,22 +46,23 @@ static bool pairs_enabled() {
     return !(e && strcmp(e, "0") == 0);
 }
 
-template <int M, int D, int C0, bool ENC, bool LIN1>
+template <int M, int D, int C0, bool ENC, bool LIN1, bool RAW>
 static void launch_chain_mode(const Params& p, hipStream_t st) {
     const unsigned BH = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H);
     if (p.chunk != C0) {
-        hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false, false, ENC, LIN1>), dim3(BH), dim3(4 * M), 0, st,
-                           p);
+        hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false, false, ENC, LIN1, RAW>), dim3(BH), dim3(4 * M), 0,
+                           st, p);
         return;
     }
     if constexpr (pair_capable<M, D, C0>()) {
         if (pairs_enabled()) {
-            hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, true, ENC, LIN1>), dim3(BH), dim3(8 * M), 0, st,
-                               p);
+            hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, true, ENC, LIN1, RAW>), dim3(BH), dim3(8 * M), 0,
+                               st, p);
             return;
         }
     }
-    hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, false, ENC, LIN1>), dim3(BH), dim3(4 * M), 0, st, p);
+    hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, false, ENC, LIN1, RAW>), dim3(BH), dim3(4 * M), 0, st,
+                       p);
 }
 
 template <int M, int D, int C0>
@@ -70,16 +71,23 @@ static int launch_chain(const Params& p, hipStream_t st) {
         return -3;
     } else {
         // the encoding layer and the first linearisation are instantiations of their own
+        // (the backward's raw outputs are built for the decoding and similarity objectives)
         if (p.mode == 2) {
+            if (p.raw) return -3;
             if (p.lin1)
-                launch_chain_mode<M, D, C0, true, true>(p, st);
+                launch_chain_mode<M, D, C0, true, true, false>(p, st);
             else
-                launch_chain_mode<M, D, C0, true, false>(p, st);
+                launch_chain_mode<M, D, C0, true, false, false>(p, st);
+        } else if (p.raw) {
+            if (p.lin1)
+                launch_chain_mode<M, D, C0, false, true, true>(p, st);
+            else
+                launch_chain_mode<M, D, C0, false, false, true>(p, st);
         } else {
             if (p.lin1)
-                launch_chain_mode<M, D, C0, false, true>(p, st);
+                launch_chain_mode<M, D, C0, false, true, false>(p, st);
             else
-                launch_chain_mode<M, D, C0, false, false>(p, st);
+                launch_chain_mode<M, D, C0, false, false, false>(p, st);
         }
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }

@@ -140,7 +140,11 @@ __device__ __forceinline__ float row_inv_norm(const f32x4 (&acc)[DB]) {
 // and a term e Z with e = beta a c on the chunk-start slots, so that
 //   R_end = diag(A_end) R + diag(sum_t e_t (.) prod_{l > t} g_l) Z + H^T W
 // (the coefficient of Z is summed alongside W); e goes to the workspace too.
-template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR, bool ENC, bool LIN1 = false>
+// RAW: also store, for the backward, every chunk-start state before projection
+// and the end state (Params::raw) and c, beta, |h|^2 of every token
+// (Params::raw_c, raw_b, raw_hh); its own instantiation, so the forward carries
+// none of it.
+template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR, bool ENC, bool LIN1 = false, bool RAW = false>
 __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Params p) {
     using G = ChainCfg<M, D, C0, PAIR>;
     static_assert(!PAIR || ONE, "the pair split covers one sub-block per chunk");
@@ -196,7 +200,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         const int tc0 = ONE ? 0 : (s % SPC) * C0;
 
         if (chunk_start) {
-            if (p.raw && grp == 0) {
+            if (RAW && grp == 0) {
                 // the chunk-start state before projection, for the backward
                 float* dst = p.raw + bh * p.raw_stride + static_cast<int64_t>(chunk) * M * D +
                              static_cast<int64_t>(slot) * D + 4 * lg;
@@ -412,7 +416,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                 prod *= gt[i][r];
             }
             rows4_prod_scan(prod, lg, ex_lo[i], ex_hi[i], tot[i]);
-            if (p.raw_c) {
+            if constexpr (RAW) {
                 // c, beta and |h|^2 of these tokens, for the backward
                 const int64_t ch = static_cast<int64_t>(bh) * (p.T / C) + chunk;
                 const int64_t o = ch * M * C + ws_frag(wv, tc0 / 16 + tbg + i, C / 16, lane);
@@ -573,7 +577,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         }
     }
 
-    if (p.raw && grp == 0) {
+    if (RAW && grp == 0) {
         float* dst = p.raw + bh * p.raw_stride + static_cast<int64_t>(p.T / C) * M * D +
                      static_cast<int64_t>(slot) * D + 4 * lg;
 #pragma unroll
