@@ -9,7 +9,8 @@ called through the C ABI.  The metric is head-tokens per second (B*H*T per
 step).  Printed: one JSON line with the headline value, the roofline of the
 chunk path measured live with HIP events on the launch stream, the fp64 CPU
 oracle timed on this host, and secondary lines for the decode, recurrent and
-other chunked workloads and for the backward of the headline workload.
+other chunked workloads, the backward of the headline workload and the layer
+glue around the recurrence.
 """
 from __future__ import annotations
 
@@ -73,13 +74,15 @@ def chain_reference_ms(w: dict, chunk: int) -> float:
 # whose traffic counters are keyed by the hash below.
 BWD_SOURCES = ("osr_bwd.hip", "osr_bwd_kernel.h", "osr_bwd_m16.hip", "osr_bwd_m32.hip", "osr_bwd_m64.hip",
                "osr_bwd_m128.hip")
+# Source of the layer-glue kernels: not part of either.
+GLUE_SOURCES = ("osr_glue.hip",)
 
 
 def source_hash() -> str:
     """Hash of the sources the forward and decode kernels are built from."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "compressed_memory_linear_amd", "csrc", "*"))):
-        if os.path.basename(p) in BWD_SOURCES:
+        if os.path.basename(p) in BWD_SOURCES + GLUE_SOURCES:
             continue
         with open(p, "rb") as f:
             h.update(f.read())
@@ -162,6 +165,57 @@ class Case:
     @property
     def head_tokens(self) -> int:
         return self.inp.B * self.inp.H * self.inp.T
+
+
+class GlueCase:
+    """Device-resident inputs of the layer glue on a workload's shape (bf16 projections,
+    fp32 filters, fp32 y): entry "glue_pre" (short convolutions of q and k, sigmoid
+    writing intensity) or "glue_post" (GeLU post-gate)."""
+
+    def __init__(self, name: str, entry: str):
+        import torch
+        from compressed_memory_linear_amd import osr, synth
+        self.name, self.entry = name, entry
+        self.w = dict(synth.WORKLOADS[name])
+        w = self.w
+        g = synth.make_glue_inputs(w["B"], w["T"], w["H"], w["m"], w["d"], seed=w["seed"] + 50)
+
+        def dev(a):
+            t = torch.from_numpy(a)
+            return (t.view(torch.bfloat16) if a.dtype.itemsize == 2 else t).to("cuda")
+
+        if entry == "glue_pre":
+            self.args = [dev(a) for a in (g.xq, g.xk, g.logit, g.wq, g.wk, g.bq, g.bk, g.hist_q, g.hist_k)]
+            self.outs = dict(q=torch.empty_like(self.args[0]), k=torch.empty_like(self.args[1]),
+                             gamma=torch.empty_like(self.args[2]), hist_q_out=torch.empty_like(self.args[7]),
+                             hist_k_out=torch.empty_like(self.args[8]))
+        else:
+            self.y, self.gate = dev(g.y), dev(g.gate)
+            self.out = torch.empty_like(self.y)
+        del g
+        self.osr = osr
+
+    def step(self):
+        if self.entry == "glue_pre":
+            self.osr.lattice_osr_glue_pre(*self.args, **self.outs, return_history=True)
+        else:
+            self.osr.lattice_osr_glue_post(self.y, self.gate, out=self.out)
+
+    @property
+    def head_tokens(self) -> int:
+        return self.w["B"] * self.w["H"] * self.w["T"]
+
+
+def algorithmic_bytes_glue(w: dict, entry: str) -> float:
+    """Compulsory HBM bytes of one glue call (bf16 projections and gates, fp32 y):
+    pre reads xq, xk and the per-slot logits and writes q, k and gamma (each
+    B T H m bf16), plus the filters, biases and histories; post reads y (fp32)
+    and the gate (bf16) and writes y * GeLU(gate) (fp32)."""
+    rows = w["B"] * w["T"] * w["H"]
+    if entry == "glue_pre":
+        n = w["H"] * w["m"]
+        return rows * w["m"] * 2 * 3 * 2 + 2 * n * 5 * 4 + 2 * 2 * w["B"] * 3 * n * 2
+    return rows * w["d"] * (4 + 2 + 4)
 
 
 def time_case(case: Case, steps: int, warmup: int):
@@ -251,7 +305,7 @@ def main() -> int:
         return 0
     if args.only:
         name, entry, chunk = args.only.split(":")
-        case = Case(name, entry, int(chunk))
+        case = GlueCase(name, entry) if entry.startswith("glue") else Case(name, entry, int(chunk))
         ms = time_case(case, args.steps, args.warmup)
         print(json.dumps({"only": args.only, "ms_per_step": ms,
                           "head_tokens_per_s": case.head_tokens / (ms * 1e-3)}), flush=True)
@@ -316,6 +370,17 @@ def main() -> int:
                         "hbm_frac": ab / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "tflops_algorithmic": None if entry == "backward"
                         else algorithmic_flops(c.w, chunk) / (t_ms * 1e-3) / 1e12})
+            del c
+            torch.cuda.empty_cache()
+        for entry in ("glue_pre", "glue_post"):
+            name = "chunked_b8h16_t4096_m64d128_c64"
+            c = GlueCase(name, entry)
+            t_ms = time_case(c, 10, 2)
+            ab = algorithmic_bytes_glue(c.w, entry)
+            sec.append({"workload": name, "entry": entry, "ms_per_step": t_ms,
+                        "head_tokens_per_s": c.head_tokens / (t_ms * 1e-3),
+                        "hbm_gbs_algorithmic": ab / (t_ms * 1e-3) / 1e9,
+                        "hbm_frac": ab / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
             del c
             torch.cuda.empty_cache()
         out["secondary"] = sec

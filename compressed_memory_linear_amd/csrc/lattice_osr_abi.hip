@@ -343,3 +343,90 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
 }
 
 }  // extern "C"
+
+// Layer glue: shape rules are those of the descriptor; every buffer is the
+// caller's device memory, outputs overlap nothing.
+namespace {
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int lattice_osr_glue_pre(const lattice_osr_desc* desc, const void* xq, const void* xk, const void* gamma_logit,
+                         const float* conv_wq, const float* conv_wk, const float* conv_bq, const float* conv_bk,
+                         const void* hist_q_in, const void* hist_k_in, void* q, void* k, void* gamma,
+                         void* hist_q_out, void* hist_k_out, void* hip_stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (!xq || !xk || !gamma_logit || !conv_wq || !conv_wk || !q || !k || !gamma) return LATTICE_OSR_ERR_NULL;
+    if ((hist_q_in == nullptr) != (hist_k_in == nullptr) || (hist_q_out == nullptr) != (hist_k_out == nullptr))
+        return LATTICE_OSR_ERR_NULL;
+    const size_t ein = desc->in_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const void* vec[] = {xq, xk, conv_wq, conv_wk, hist_q_in, hist_k_in, q, k, hist_q_out, hist_k_out,
+                         desc->gamma_per_slot ? gamma_logit : nullptr, desc->gamma_per_slot ? gamma : nullptr};
+    for (const void* ptr : vec)
+        if (!aligned(ptr, 16)) return LATTICE_OSR_ERR_ALIGN;
+    if (!aligned(gamma_logit, ein) || !aligned(gamma, ein) || !aligned(conv_bq, 4) || !aligned(conv_bk, 4))
+        return LATTICE_OSR_ERR_ALIGN;
+
+    const size_t N = static_cast<size_t>(desc->H) * desc->m;
+    const size_t G = desc->gamma_per_slot ? N : static_cast<size_t>(desc->H);
+    const size_t rows = static_cast<size_t>(desc->B) * desc->T;
+    const size_t hist = static_cast<size_t>(desc->B) * 3 * N * ein;
+    const Range ins[] = {range_of(xq, rows * N * ein),       range_of(xk, rows * N * ein),
+                         range_of(gamma_logit, rows * G * ein), range_of(conv_wq, N * 4 * sizeof(float)),
+                         range_of(conv_wk, N * 4 * sizeof(float)), range_of(conv_bq, conv_bq ? N * sizeof(float) : 0),
+                         range_of(conv_bk, conv_bk ? N * sizeof(float) : 0), range_of(hist_q_in, hist_q_in ? hist : 0),
+                         range_of(hist_k_in, hist_k_in ? hist : 0)};
+    const Range outs[] = {range_of(q, rows * N * ein), range_of(k, rows * N * ein), range_of(gamma, rows * G * ein),
+                          range_of(hist_q_out, hist_q_out ? hist : 0), range_of(hist_k_out, hist_k_out ? hist : 0)};
+    const int nout = sizeof(outs) / sizeof(outs[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (const Range& r : ins)
+            if (overlap(outs[i], r)) return LATTICE_OSR_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(outs[i], outs[j])) return LATTICE_OSR_ERR_ALIAS;
+    }
+
+    osr::GlueParams p;
+    p.xq = xq;
+    p.xk = xk;
+    p.glogit = gamma_logit;
+    p.wq = conv_wq;
+    p.wk = conv_wk;
+    p.bq = conv_bq;
+    p.bk = conv_bk;
+    p.hq_in = hist_q_in;
+    p.hk_in = hist_k_in;
+    p.q = q;
+    p.k = k;
+    p.gamma = gamma;
+    p.hq_out = hist_q_out;
+    p.hk_out = hist_k_out;
+    p.B = desc->B;
+    p.T = desc->T;
+    p.N = static_cast<int>(N);
+    p.G = static_cast<int>(G);
+    p.gvec = desc->gamma_per_slot;
+    if (N > static_cast<size_t>(INT_MAX) / 2) return LATTICE_OSR_ERR_SHAPE;
+    return osr::launch_glue_pre(p, desc->in_dtype == LATTICE_OSR_BF16, static_cast<hipStream_t>(hip_stream));
+}
+
+int lattice_osr_glue_post(const lattice_osr_desc* desc, const void* y, const void* gate, void* out,
+                          void* hip_stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (!y || !gate || !out) return LATTICE_OSR_ERR_NULL;
+    if (!aligned(y, 16) || !aligned(gate, 16) || !aligned(out, 16)) return LATTICE_OSR_ERR_ALIGN;
+    const size_t n = static_cast<size_t>(desc->B) * desc->T * desc->H * desc->d;
+    const size_t ey = desc->y_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const size_t eg = desc->in_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const Range ry = range_of(y, n * ey), rg = range_of(gate, n * eg), ro = range_of(out, n * ey);
+    if (overlap(ro, rg) || (ro.lo != ry.lo && overlap(ro, ry))) return LATTICE_OSR_ERR_ALIAS;
+    return osr::launch_glue_post(y, desc->y_dtype == LATTICE_OSR_BF16, gate, desc->in_dtype == LATTICE_OSR_BF16, out,
+                                 static_cast<int64_t>(n), static_cast<hipStream_t>(hip_stream));
+}
+
+}  // extern "C"

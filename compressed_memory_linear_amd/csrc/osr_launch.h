@@ -50,4 +50,23 @@ struct BwdParams {
 size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C);
 int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 
+// Layer glue (HBM-bound streaming kernels).  pre: q = conv4(xq), k = conv4(xk)
+// (depthwise causal, width 4, N = H*m channels per token row), gamma =
+// sigmoid(logit) (G = H*m or H values per token row), the last three raw rows
+// as the next call's history.  All element buffers share the input dtype.
+struct GlueParams {
+    const void *xq, *xk, *glogit;    // [B,T,N], [B,T,N], [B,T,G]
+    const float *wq, *wk;            // [N,4]; tap 3 weighs the current token
+    const float *bq, *bk;            // [N] or null
+    const void *hq_in, *hk_in;       // [B,3,N] or null (zeros)
+    void *q, *k, *gamma;             // outputs, like the inputs
+    void *hq_out, *hk_out;           // [B,3,N] or null
+    int B, T, N, G;
+    int gvec;                        // 1: G % 8 == 0 and glogit, gamma 16-byte aligned
+};
+// Return 0, -3 (shape outside what the kernels take) or -5 (launch error).
+int launch_glue_pre(const GlueParams& p, bool in_bf16, hipStream_t st);
+// out = y * GeLU(g) elementwise over n values (n % 8 == 0, 16-byte aligned).
+int launch_glue_post(const void* y, bool y_bf16, const void* g, bool g_bf16, void* out, int64_t n, hipStream_t st);
+
 }  // namespace osr

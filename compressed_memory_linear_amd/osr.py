@@ -26,7 +26,8 @@ ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_
 
 EXPORTED = ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step",
             "lattice_osr_workspace_bytes", "lattice_osr_status_string", "lattice_osr_abi_version",
-            "lattice_osr_bwd_chunked", "lattice_osr_bwd_workspace_bytes")
+            "lattice_osr_bwd_chunked", "lattice_osr_bwd_workspace_bytes", "lattice_osr_glue_pre",
+            "lattice_osr_glue_post")
 
 
 class lattice_osr_desc(ctypes.Structure):
@@ -64,6 +65,10 @@ def load_library():
         lib.lattice_osr_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.lattice_osr_workspace_bytes.argtypes = [dp, ctypes.c_int32]
         lib.lattice_osr_workspace_bytes.restype = ctypes.c_size_t
+        lib.lattice_osr_glue_pre.argtypes = [dp] + [vp] * 15
+        lib.lattice_osr_glue_pre.restype = ctypes.c_int
+        lib.lattice_osr_glue_post.argtypes = [dp, vp, vp, vp, vp]
+        lib.lattice_osr_glue_post.restype = ctypes.c_int
         lib.lattice_osr_status_string.argtypes = [ctypes.c_int]
         lib.lattice_osr_status_string.restype = ctypes.c_char_p
         lib.lattice_osr_abi_version.argtypes = []
@@ -223,6 +228,61 @@ def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_
 
 
 # ------------------------------------------------------------ host inputs --
+def lattice_osr_glue_pre(xq, xk, gamma_logit, conv_wq, conv_wk, conv_bq=None, conv_bk=None, hist_q=None,
+                         hist_k=None, *, q=None, k=None, gamma=None, hist_q_out=None, hist_k_out=None,
+                         return_history: bool = False, stream=None):
+    """q = conv4(xq), k = conv4(xk), gamma = sigmoid(gamma_logit) in one pass.
+
+    xq, xk [B,T,H,m] and gamma_logit [B,T,H,m] or [B,T,H] share a dtype (float32 or
+    bfloat16); conv_w* [H,m,4] and conv_b* [H,m] are float32; hist_* [B,3,H,m] carry
+    the three raw rows before this call.  Returns (q, k, gamma) and, with
+    return_history, also the history for the next call."""
+    lib = load_library()
+    if xq.dim() != 4 or xq.dtype not in _DT:
+        raise ValueError("xq/xk are [B,T,H,m] float32 or bfloat16")
+    B, T, H, m = xq.shape
+    for t in (xk, gamma_logit):
+        if t.dtype != xq.dtype or not t.is_contiguous() or t.device != xq.device:
+            raise ValueError("xq, xk, gamma_logit must share dtype/device and be contiguous")
+    for t in (conv_wq, conv_wk, conv_bq, conv_bk):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError("convolution weights and biases are contiguous float32")
+    per_slot = 1 if gamma_logit.dim() == 4 else 0
+    desc = make_desc(B, T, H, m, m, per_slot, _DT[xq.dtype], F32)
+    q = torch.empty_like(xq) if q is None else q
+    k = torch.empty_like(xk) if k is None else k
+    gamma = torch.empty_like(gamma_logit) if gamma is None else gamma
+    if return_history:
+        hist_q_out = xq.new_empty((B, 3, H, m)) if hist_q_out is None else hist_q_out
+        hist_k_out = xk.new_empty((B, 3, H, m)) if hist_k_out is None else hist_k_out
+    rc = lib.lattice_osr_glue_pre(ctypes.byref(desc), _ptr(xq), _ptr(xk), _ptr(gamma_logit), _ptr(conv_wq),
+                                  _ptr(conv_wk), _ptr(conv_bq), _ptr(conv_bk), _ptr(hist_q), _ptr(hist_k),
+                                  _ptr(q), _ptr(k), _ptr(gamma), _ptr(hist_q_out), _ptr(hist_k_out),
+                                  _stream(stream))
+    if rc != OK:
+        raise OSRError(rc, "lattice_osr_glue_pre")
+    if return_history:
+        return q, k, gamma, hist_q_out, hist_k_out
+    return q, k, gamma
+
+
+def lattice_osr_glue_post(y, gate, *, out=None, stream=None):
+    """out = y * GeLU(gate) (exact GeLU); y [B,T,H,d] float32 or bfloat16, gate of y's shape in
+    float32 or bfloat16.  out may be y (in place)."""
+    lib = load_library()
+    if y.dim() != 4 or y.dtype not in _DT or gate.dtype not in _DT or gate.shape != y.shape:
+        raise ValueError("y and gate are [B,T,H,d] float32 or bfloat16 tensors of one shape")
+    if not (y.is_contiguous() and gate.is_contiguous()):
+        raise ValueError("y and gate must be contiguous")
+    B, T, H, d = y.shape
+    desc = make_desc(B, T, H, 16, d, 1, _DT[gate.dtype], _DT[y.dtype])
+    out = torch.empty_like(y) if out is None else out
+    rc = lib.lattice_osr_glue_post(ctypes.byref(desc), _ptr(y), _ptr(gate), _ptr(out), _stream(stream))
+    if rc != OK:
+        raise OSRError(rc, "lattice_osr_glue_post")
+    return out
+
+
 def to_device(inp, device="cuda") -> dict:
     """Move an OSRInputs batch (numpy, storage form) to device tensors.
 

@@ -104,6 +104,69 @@ def make_inputs(B: int, T: int, H: int, m: int, d: int, seed: int, in_dtype: str
     return OSRInputs(B, T, H, m, d, in_dtype, gamma_per_slot, q, k, v, gamma, mu, s0)
 
 
+@dataclass
+class GlueInputs:
+    """Inputs of the layer glue in storage form (uint16 bf16 bit patterns or float32).
+
+    xq, xk: [B,T,H,m] raw projections before the short convolution; logit:
+    [B,T,H,m] or [B,T,H] (the writing intensity's pre-activation); wq, wk:
+    [H,m,4] float32 filters (tap 3 = current token); bq, bk: [H,m] float32;
+    hist_q, hist_k: [B,3,H,m] raw rows before the sequence; y: [B,T,H,d] the
+    recurrence's output (float32, or bf16 when y_dtype is bf16); gate:
+    [B,T,H,d] the post-gate branch's projection.
+    """
+    in_dtype: str
+    y_dtype: str
+    xq: np.ndarray
+    xk: np.ndarray
+    logit: np.ndarray
+    wq: np.ndarray
+    wk: np.ndarray
+    bq: np.ndarray
+    bk: np.ndarray
+    hist_q: np.ndarray
+    hist_k: np.ndarray
+    y: np.ndarray
+    gate: np.ndarray
+
+    def value(self, name: str) -> np.ndarray:
+        """The float64 values an input stands for (exact for bf16)."""
+        a = getattr(self, name)
+        bf = (self.y_dtype if name == "y" else self.in_dtype) == BF16
+        if name in ("wq", "wk", "bq", "bk") or not bf:
+            return a.astype(np.float64)
+        return bf16_bits_to_f32(a).astype(np.float64)
+
+
+def make_glue_inputs(B: int, T: int, H: int, m: int, d: int, seed: int, in_dtype: str = BF16,
+                     y_dtype: str = F32, gamma_per_slot: bool = True) -> GlueInputs:
+    """Draw order: xq, xk, logit, wq, wk, bq, bk, hist_q, hist_k, y, gate (PCG64, float32).
+    Projections and y ~ N(0,1); logits ~ N(0,2^2); filters ~ N(0,1/4) per tap (a
+    short filter of unit-scale output); biases ~ N(0, 0.1^2); gate ~ N(0,2^2)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f = np.float32
+    xq = rng.standard_normal((B, T, H, m), dtype=f)
+    xk = rng.standard_normal((B, T, H, m), dtype=f)
+    logit = rng.standard_normal((B, T, H, m) if gamma_per_slot else (B, T, H), dtype=f) * f(2)
+    wq = rng.standard_normal((H, m, 4), dtype=f) * f(0.5)
+    wk = rng.standard_normal((H, m, 4), dtype=f) * f(0.5)
+    bq = rng.standard_normal((H, m), dtype=f) * f(0.1)
+    bk = rng.standard_normal((H, m), dtype=f) * f(0.1)
+    hist_q = rng.standard_normal((B, 3, H, m), dtype=f)
+    hist_k = rng.standard_normal((B, 3, H, m), dtype=f)
+    y = rng.standard_normal((B, T, H, d), dtype=f)
+    gate = rng.standard_normal((B, T, H, d), dtype=f) * f(2)
+    if in_dtype == BF16:
+        xq, xk, logit, hist_q, hist_k, gate = (bf16_round_bits(a) for a in (xq, xk, logit, hist_q, hist_k, gate))
+    elif in_dtype != F32:
+        raise ValueError(in_dtype)
+    if y_dtype == BF16:
+        y = bf16_round_bits(y)
+    elif y_dtype != F32:
+        raise ValueError(y_dtype)
+    return GlueInputs(in_dtype, y_dtype, xq, xk, logit, wq, wk, bq, bk, hist_q, hist_k, y, gate)
+
+
 # The workloads, named by what they are.  chunk=None means "several chunk sizes".
 WORKLOADS = {
     "tiny_f32_m16d32_t64": dict(B=1, H=1, T=64, m=16, d=32, in_dtype=F32, chunk=None,

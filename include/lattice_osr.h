@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define LATTICE_OSR_ABI_VERSION 3
+#define LATTICE_OSR_ABI_VERSION 4
 
 #if defined(__GNUC__) || defined(__clang__)
 #define LATTICE_OSR_API __attribute__((visibility("default")))
@@ -190,6 +190,55 @@ LATTICE_OSR_API int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_
 /* Workspace bytes lattice_osr_bwd_chunked needs for this shape; (size_t)-1 if
  * the arguments are invalid or the configuration has no backward. */
 LATTICE_OSR_API size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* desc, int32_t chunk_size);
+
+/*
+ * Layer glue before the recurrence (section "Experiments", paragraph on the
+ * Lattice block: a pair of short convolutions for q and k, which share one
+ * projection, and the writing intensity gamma_t = sigmoid(W_gamma x_t); the
+ * experiment-details appendix sets the convolution width to 4).  The
+ * projections are the caller's; this call does, in one pass:
+ *   q = conv4(xq), k = conv4(xk)  depthwise and causal along T, one filter per
+ *                                 channel (h, i): out_t = b + sum_j w[j] x_{t-3+j},
+ *                                 j = 0..3 (w[3] weighs the current token);
+ *                                 the three rows before t = 0 come from the
+ *                                 history (zeros when it is NULL: sequence start);
+ *   gamma = sigmoid(gamma_logit)  elementwise.
+ * The outputs are ready for lattice_osr_fwd_chunked with the same desc (which
+ * supplies B, T, H, m, gamma_per_slot and in_dtype; every element buffer is
+ * in_dtype, the weights fp32; d, y_dtype, mode, linearisation are validated
+ * but unused).  Arithmetic is fp32.
+ *   xq, xk, q, k            [B, T, H, m]
+ *   gamma_logit, gamma      [B, T, H, m] (gamma_per_slot = 1) or [B, T, H]
+ *   conv_wq, conv_wk        [H, m, 4]  float32
+ *   conv_bq, conv_bk        [H, m]     float32, or NULL (no bias)
+ *   hist_q_in, hist_k_in    [B, 3, H, m], the raw xq / xk rows of the three
+ *                           tokens before this call, oldest first; both NULL
+ *                           at a sequence start
+ *   hist_q_out, hist_k_out  [B, 3, H, m] receive the last three raw rows
+ *                           (of the history followed by x), for the next call;
+ *                           both NULL: not written
+ * Alignment: 16 bytes for every buffer except the biases (4 bytes) and a
+ * per-token gamma_logit / gamma (element alignment).  No output may overlap
+ * another output or any input (ERR_ALIAS); pass a second history buffer
+ * rather than updating one in place.  Errors and asynchrony as above.
+ */
+LATTICE_OSR_API int lattice_osr_glue_pre(const lattice_osr_desc* desc, const void* xq, const void* xk,
+                                         const void* gamma_logit, const float* conv_wq, const float* conv_wk,
+                                         const float* conv_bq, const float* conv_bk, const void* hist_q_in,
+                                         const void* hist_k_in, void* q, void* k, void* gamma, void* hist_q_out,
+                                         void* hist_k_out, void* hip_stream);
+
+/*
+ * Layer glue after the recurrence: the GeLU post-gate on the layer's output
+ * (section "Experiments", paragraph on the Lattice block),
+ *   out = y * GeLU(gate),  GeLU(x) = x Phi(x), Phi the standard normal CDF
+ * (the exact form), elementwise in fp32.
+ *   y, out  [B, T, H, d]  y_dtype;  gate  [B, T, H, d]  in_dtype
+ * out may be y itself (in place); any other overlap is ERR_ALIAS.  All three
+ * must be 16-byte aligned.  Errors and asynchrony as above.
+ */
+LATTICE_OSR_API int lattice_osr_glue_post(const lattice_osr_desc* desc, const void* y, const void* gate, void* out,
+                                          void* hip_stream);
 
 /* Static text for a status code (never NULL). */
 LATTICE_OSR_API const char* lattice_osr_status_string(int status);

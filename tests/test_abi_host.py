@@ -34,7 +34,7 @@ def test_header_declarations_are_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert osr.lattice_osr_abi_version() == 3
+    assert osr.lattice_osr_abi_version() == 4
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = osr.status_string(code)
         assert s and s != "unknown status"
@@ -277,3 +277,75 @@ def test_bwd_alignment_rules():
         p[i] += 2
         assert _bwd_call(d, p, 4) == osr.ERR_ALIGN, i
     assert _bwd_call(d, _bwd_ptrs(), 4, ws=BASE + 14 * (1 << 32) + 8) == osr.ERR_ALIGN
+
+
+# ------------------------------------------------------------ layer glue --
+# lattice_osr_glue_pre pointers: xq, xk, gamma_logit, conv_wq, conv_wk, conv_bq, conv_bk,
+# hist_q_in, hist_k_in, q, k, gamma, hist_q_out, hist_k_out
+def _glue_ptrs(gap=1 << 32):
+    return [BASE + i * gap for i in range(14)]
+
+
+def _glue_pre(d, ptrs):
+    return osr.load_library().lattice_osr_glue_pre(ctypes.byref(d) if d is not None else None, *ptrs, None)
+
+
+def test_glue_pre_null_pointers():
+    d = osr.make_desc(1, 8, 2, 16, 16)
+    assert _glue_pre(None, _glue_ptrs()) == osr.ERR_NULL
+    for i in (0, 1, 2, 3, 4, 9, 10, 11):
+        p = _glue_ptrs()
+        p[i] = None
+        assert _glue_pre(d, p) == osr.ERR_NULL, i
+    # the histories come in pairs; an unpaired one is a null-pointer error
+    for i in (7, 8, 12, 13):
+        p = _glue_ptrs()
+        p[i] = None
+        assert _glue_pre(d, p) == osr.ERR_NULL, i
+
+
+def test_glue_pre_alignment_and_descriptor():
+    d = osr.make_desc(1, 8, 2, 16, 16)
+    for i in (0, 1, 3, 4, 7, 8, 9, 10, 11, 12, 13):  # moved in 16-byte pieces
+        q = _glue_ptrs()
+        q[i] += 8
+        assert _glue_pre(d, q) == osr.ERR_ALIGN, i
+    for i in (5, 6):  # biases: 4-byte alignment
+        q = _glue_ptrs()
+        q[i] += 2
+        assert _glue_pre(d, q) == osr.ERR_ALIGN, i
+    # per-slot gamma moves in 16-byte pieces; per-token gamma element by element
+    q = _glue_ptrs()
+    q[2] += 8
+    assert _glue_pre(d, q) == osr.ERR_ALIGN
+    dt = osr.make_desc(1, 8, 2, 16, 16, gamma_per_slot=0)
+    q = _glue_ptrs()
+    q[2] += 1
+    assert _glue_pre(dt, q) == osr.ERR_ALIGN
+    assert _glue_pre(osr.make_desc(1, 8, 2, 24, 16), _glue_ptrs()) == osr.ERR_UNSUPPORTED
+    assert _glue_pre(osr.make_desc(1, 0, 2, 16, 16), _glue_ptrs()) == osr.ERR_SHAPE
+    assert _glue_pre(osr.make_desc(1, 8, 2, 16, 16, in_dtype=7), _glue_ptrs()) == osr.ERR_UNSUPPORTED
+
+
+def test_glue_pre_aliasing_rules():
+    d = osr.make_desc(1, 8, 2, 16, 16)
+    for out in (9, 10, 11, 12, 13):
+        for other in [o for o in range(14) if o != out]:
+            p = _glue_ptrs()
+            p[out] = p[other]
+            assert _glue_pre(d, p) == osr.ERR_ALIAS, (out, other)
+
+
+def test_glue_post_argument_checks():
+    lib = osr.load_library()
+    d = osr.make_desc(1, 8, 2, 16, 16)
+    y, g, o = BASE, BASE + (1 << 32), BASE + (2 << 32)
+    assert lib.lattice_osr_glue_post(None, y, g, o, None) == osr.ERR_NULL
+    for args in ((None, g, o), (y, None, o), (y, g, None)):
+        assert lib.lattice_osr_glue_post(ctypes.byref(d), *args, None) == osr.ERR_NULL
+    for args in ((y + 8, g, o), (y, g + 8, o), (y, g, o + 8)):
+        assert lib.lattice_osr_glue_post(ctypes.byref(d), *args, None) == osr.ERR_ALIGN
+    assert lib.lattice_osr_glue_post(ctypes.byref(d), y, g, g, None) == osr.ERR_ALIAS
+    assert lib.lattice_osr_glue_post(ctypes.byref(d), y, g, y + 16, None) == osr.ERR_ALIAS
+    assert lib.lattice_osr_glue_post(ctypes.byref(osr.make_desc(1, 8, 2, 16, 20)), y, g, o, None) == \
+        osr.ERR_UNSUPPORTED

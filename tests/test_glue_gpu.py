@@ -1,0 +1,181 @@
+"""GPU parity of the layer glue (lattice_osr_glue_pre / lattice_osr_glue_post)
+against the fp64 oracle (oracle/osr_glue.c), element by element.
+
+The glue is the Lattice block's short causal convolution of q and k (width 4),
+the sigmoid writing intensity and the GeLU post-gate ("Lattice: Learning to
+Efficiently Compress the Memory", section "Experiments", paragraph on the
+Lattice block).  Bars, from the kernels' fp32 arithmetic on exactly
+representable inputs:
+  * convolution: four fused multiply-adds onto the bias, each rounding once,
+    so |err| <= 8 u S with u = 2^-24 and S = |b| + sum_j |w_j x_j|;
+  * sigmoid and the GeLU gate: the device's expf / erfcf (a few ulp) and a
+    division or two products: relative 2^-19; the gate's erfc also takes the
+    rounded argument -g/sqrt 2, and in the negative tail Phi(g) moves by a
+    relative g^2 delta when its argument moves by a relative delta (the Mills
+    ratio), so the gate adds 2 g^2 u;
+  * a bf16 output adds its rounding: half an ulp, at most 2^-8 of the value.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from compressed_memory_linear_amd import osr, synth
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def _dev(a: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a).copy())
+    if a.dtype == np.uint16:
+        t = t.view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def _f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _out_rel(dtype: str) -> float:
+    return 2.0 ** -8 if dtype == synth.BF16 else 0.0
+
+
+def _conv_scale(x, w, b, hist):
+    """S = |b| + sum_j |w_j x_{t-3+j}| per output, with the history in front."""
+    B, T = x.shape[:2]
+    xe = np.concatenate([hist if hist is not None else np.zeros((B, 3) + x.shape[2:]), x], axis=1)
+    S = np.abs(b)[None, None] if b is not None else np.zeros(x.shape[2:])[None, None]
+    S = S + sum(np.abs(w[..., j])[None, None] * np.abs(xe[:, j:j + T]) for j in range(4))
+    return S
+
+
+def _check(got, ref, bound, what):
+    err = np.abs(got - ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        raise AssertionError(f"{what}: {bad.sum()} of {err.size} beyond the bar; worst at {i}: "
+                             f"got {got[i]!r}, oracle {ref[i]!r}, bar {bound[i]!r}")
+
+
+def _run_pre(inp, with_bias=True, with_hist=True, return_history=True):
+    args = [_dev(inp.xq), _dev(inp.xk), _dev(inp.logit), _dev(inp.wq), _dev(inp.wk)]
+    args += [_dev(inp.bq), _dev(inp.bk)] if with_bias else [None, None]
+    args += [_dev(inp.hist_q), _dev(inp.hist_k)] if with_hist else [None, None]
+    out = osr.lattice_osr_glue_pre(*args, return_history=return_history)
+    torch.cuda.synchronize()
+    return out
+
+
+def _check_pre(inp, out, with_bias=True, with_hist=True):
+    v = inp.value
+    bq, bk = (v("bq"), v("bk")) if with_bias else (None, None)
+    hq, hk = (v("hist_q"), v("hist_k")) if with_hist else (None, None)
+    ref = oracle.glue_pre(v("xq"), v("xk"), v("logit"), v("wq"), v("wk"), bq, bk, hq, hk)
+    rel = _out_rel(inp.in_dtype)
+    for name, got, want, x, w, b, h in (("q", out[0], ref[0], v("xq"), v("wq"), bq, hq),
+                                        ("k", out[1], ref[1], v("xk"), v("wk"), bk, hk)):
+        bound = rel * np.abs(want) + (16 if rel else 8) * U * _conv_scale(x, w, b, h) + 1e-30
+        _check(_f64(got), want, bound, name)
+    _check(_f64(out[2]), ref[2], (rel + 2.0 ** -19) * np.abs(ref[2]) + 1e-30, "gamma")
+    if len(out) == 5:
+        # the history is raw input rows: bit-exact
+        np.testing.assert_array_equal(_f64(out[3]), ref[3])
+        np.testing.assert_array_equal(_f64(out[4]), ref[4])
+
+
+@pytest.mark.parametrize("B,T,H,m,in_dtype,per_slot", [
+    (2, 77, 3, 16, synth.BF16, True),    # several 32-token tiles and a ragged tail
+    (1, 64, 2, 32, synth.F32, True),
+    (2, 45, 3, 16, synth.BF16, False),   # per-token gamma, H not a multiple of 8
+    (1, 33, 16, 64, synth.F32, False),   # per-token gamma, rows of 16
+    (1, 128, 1, 128, synth.BF16, True),
+])
+def test_glue_pre_matches_oracle(B, T, H, m, in_dtype, per_slot):
+    inp = synth.make_glue_inputs(B, T, H, m, 16, seed=500 + T, in_dtype=in_dtype, gamma_per_slot=per_slot)
+    print(f"glue_pre B{B} T{T} H{H} m{m} {in_dtype} per_slot={per_slot}", flush=True)
+    _check_pre(inp, _run_pre(inp))
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_glue_pre_short_sequences_and_history(T):
+    """Fewer tokens than the filter: the output and the next history both draw on the
+    carried rows."""
+    inp = synth.make_glue_inputs(2, T, 2, 16, 16, seed=600 + T)
+    _check_pre(inp, _run_pre(inp))
+
+
+def test_glue_pre_without_bias_or_history():
+    inp = synth.make_glue_inputs(1, 40, 2, 32, 16, seed=700)
+    out = _run_pre(inp, with_bias=False, with_hist=False, return_history=False)
+    assert len(out) == 3
+    _check_pre(inp, out, with_bias=False, with_hist=False)
+
+
+def test_glue_pre_split_sequence_equals_one_call():
+    """Two calls chained through the history give the single call's outputs bit for bit
+    (the same fp32 operations on the same values)."""
+    inp = synth.make_glue_inputs(2, 70, 2, 16, 16, seed=800)
+    whole = _run_pre(inp)
+    xq, xk, lg = _dev(inp.xq), _dev(inp.xk), _dev(inp.logit)
+    w = [_dev(inp.wq), _dev(inp.wk), _dev(inp.bq), _dev(inp.bk)]
+    cut = 37
+    a = osr.lattice_osr_glue_pre(xq[:, :cut].contiguous(), xk[:, :cut].contiguous(), lg[:, :cut].contiguous(), *w,
+                                 _dev(inp.hist_q), _dev(inp.hist_k), return_history=True)
+    b = osr.lattice_osr_glue_pre(xq[:, cut:].contiguous(), xk[:, cut:].contiguous(), lg[:, cut:].contiguous(), *w,
+                                 a[3], a[4], return_history=True)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.equal(torch.cat([a[i], b[i]], dim=1), whole[i]), i
+    assert torch.equal(b[3], whole[3]) and torch.equal(b[4], whole[4])
+
+
+def test_glue_pre_headline_size():
+    """The layer of the chunked workload B4 H8 T2048 m64 (bf16), every element."""
+    inp = synth.make_glue_inputs(4, 2048, 8, 64, 64, seed=900)
+    _check_pre(inp, _run_pre(inp))
+
+
+def _gate_rel(g):
+    return 2.0 ** -19 + 2 * g * g * U
+
+
+def _check_post(inp, got):
+    g = inp.value("gate")
+    ref = oracle.glue_gelu_gate(inp.value("y"), g)
+    rel = _out_rel(inp.y_dtype)
+    _check(_f64(got), ref, (rel + _gate_rel(g)) * np.abs(ref) + 1e-30, "out")
+
+
+@pytest.mark.parametrize("in_dtype,y_dtype", [(synth.BF16, synth.F32), (synth.BF16, synth.BF16),
+                                              (synth.F32, synth.F32), (synth.F32, synth.BF16)])
+def test_glue_post_matches_oracle(in_dtype, y_dtype):
+    inp = synth.make_glue_inputs(2, 53, 3, 16, 32, seed=1000, in_dtype=in_dtype, y_dtype=y_dtype)
+    print(f"glue_post {in_dtype} gate, {y_dtype} y", flush=True)
+    out = osr.lattice_osr_glue_post(_dev(inp.y), _dev(inp.gate))
+    torch.cuda.synchronize()
+    _check_post(inp, out)
+
+
+def test_glue_post_in_place_and_headline_size():
+    inp = synth.make_glue_inputs(4, 2048, 8, 16, 64, seed=1100)
+    y = _dev(inp.y)
+    out = osr.lattice_osr_glue_post(y, _dev(inp.gate), out=y)
+    torch.cuda.synchronize()
+    assert out.data_ptr() == y.data_ptr()
+    _check_post(inp, out)
+
+
+def test_glue_post_tails_of_the_gate():
+    """Far out the gate passes y (GeLU(x) ~ x) or shuts it; the erfc form keeps the
+    negative tail's relative accuracy."""
+    g = torch.tensor([0.0, 1e-3, -1e-3, 5.0, -5.0, 9.0, -9.0, 12.0, -12.0, 30.0, -30.0, 2.0, -2.0, 0.5, -0.5, 40.0],
+                     dtype=torch.float32)
+    y = torch.linspace(-1.5, 2.0, g.numel(), dtype=torch.float32)
+    out = osr.lattice_osr_glue_post(y.reshape(1, 1, 1, 16).cuda(), g.reshape(1, 1, 1, 16).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.glue_gelu_gate(y.double().numpy(), g.double().numpy())
+    got = out.reshape(-1).cpu().double().numpy()
+    _check(got, ref, _gate_rel(g.double().numpy()) * np.abs(ref) + 1e-38, "tails")
