@@ -130,34 +130,33 @@ __device__ __forceinline__ int64_t gate_frag(int row, int tau, int C) {
 
 // ch: this (b,h)'s chunk index b*H*NC + n, for the state-passing kernel's
 // records (chain_c set); otherwise the records are the kernel's own (trec).
-template <class L, int M, int D, typename TIn, bool PF_STATE>
+template <class L, int M, int D, typename TIn, bool PF_STATE, bool DYB>
 __device__ __forceinline__ void load_rev(RevIn<L::RPT>& x, const BwdParams& p, const float* trec,
                                          const float* rtok, int64_t bth, int64_t ch, int tau, int rg, int cg,
                                          int el0) {
     using TR = TokRec<M, D>;
     load_token<L, M, D, TIn>(x.in, p.f, bth, rg, cg);
-    if (p.chain_c) {
-        const int C = p.f.chunk;
-        const float* cc = p.chain_c + ch * M * C;
-        const float* cb = p.chain_b + ch * M * C;
+    // c, beta and |h|^2 from the state-passing kernel's arrays or from this
+    // kernel's own records: the source is chosen by address, not by branch,
+    // so each value is one load whose wait can trail it (a load on either arm
+    // of a branch is waited for where the arms join)
+    const int C = p.f.chunk;
+    const bool chain = p.chain_c != nullptr;
+    const float* rec = trec + static_cast<int64_t>(tau) * TR::SIZE;
+    const float* cc = chain ? p.chain_c + ch * M * C : rec + TR::C_OFF;
+    const float* cb = chain ? p.chain_b + ch * M * C : rec + TR::B_OFF;
 #pragma unroll
-        for (int i = 0; i < L::RPT; ++i) {
-            const int64_t o = gate_frag(rg + L::RG * i, tau, C);
-            x.c[i] = cc[o];
-            x.beta[i] = cb[o];
-        }
-        x.hh = p.chain_hh[ch * C + tau];
-    } else {
-        const float* rec = trec + static_cast<int64_t>(tau) * TR::SIZE;
-#pragma unroll
-        for (int i = 0; i < L::RPT; ++i) {
-            x.c[i] = rec[TR::C_OFF + rg + L::RG * i];
-            x.beta[i] = rec[TR::B_OFF + rg + L::RG * i];
-        }
-        x.hh = rec[TR::HH_OFF];
+    for (int i = 0; i < L::RPT; ++i) {
+        const int row = rg + L::RG * i;
+        const int64_t o = chain ? gate_frag(row, tau, C) : row;
+        x.c[i] = cc[o];
+        x.beta[i] = cb[o];
     }
-    x.dy = p.dy_bf16 ? ld4<uint16_t>(static_cast<const uint16_t*>(p.dy), bth * D + cg * 4)
-                     : ld4<float>(static_cast<const float*>(p.dy), bth * D + cg * 4);
+    x.hh = *(chain ? p.chain_hh + ch * C + tau : rec + TR::HH_OFF);
+    if constexpr (DYB)
+        x.dy = ld4<uint16_t>(static_cast<const uint16_t*>(p.dy), bth * D + cg * 4);
+    else
+        x.dy = ld4<float>(static_cast<const float*>(p.dy), bth * D + cg * 4);
     if constexpr (PF_STATE) {
         const float* rpre = rtok + static_cast<int64_t>(tau) * M * D;
 #pragma unroll
@@ -166,7 +165,7 @@ __device__ __forceinline__ void load_rev(RevIn<L::RPT>& x, const BwdParams& p, c
     }
 }
 
-template <int M, int D, int NT, typename TIn, bool LIN1>
+template <int M, int D, int NT, typename TIn, bool LIN1, bool DYB>
 __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     using L = ValuLayout<M, D, NT>;
     using TR = TokRec<M, D>;
@@ -175,6 +174,9 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     // the current one, and the state before it too, where registers allow.
     constexpr bool PF_TOKEN = L::RPT <= 4;
     constexpr bool PF_STATE = L::RPT <= 2;
+    // Two token buffers used in turn (no register copy of loads in flight) where
+    // registers allow; at 4 slot rows per thread the second buffer spilled.
+    constexpr bool DBUF = L::RPT <= 2;
     extern __shared__ __attribute__((aligned(16))) float hbuf[];  // [C][D], dynamic
     __shared__ __attribute__((aligned(16))) float red[2 * BT * L::NW * W];
     __shared__ __attribute__((aligned(16))) float tot[BT * W];  // a batch's sums over slots
@@ -355,9 +357,20 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int i = 0; i < L::RPT; ++i) rpost[i] = *reinterpret_cast<const float4*>(s1 + el(i));
         }
-        RevIn<L::RPT> rc, rn;
-        if constexpr (PF_TOKEN)
-            load_rev<L, M, D, TIn, PF_STATE>(rc, p, trec, rtok, bth_of(n * C + C - 1), ch, C - 1, rg, cg, el(0));
+        // With DBUF, token tau's values live in rv[tau & 1] (the batch starts ub are
+        // even, so tau & 1 == u & 1 is fixed in the unrolled batch): the next
+        // token's loads go to the other buffer, and no copy of registers with loads
+        // in flight forces a wait.  Otherwise rv[0] is the current token and rv[1]
+        // the prefetched next one, copied over at the end of each token.
+        RevIn<L::RPT> rv[2];
+        if constexpr (PF_TOKEN) {
+            // (static indices only: a computed one would put rv in scratch memory)
+            const int64_t bl = bth_of(n * C + C - 1);
+            if (DBUF && C > 1)
+                load_rev<L, M, D, TIn, PF_STATE, DYB>(rv[1], p, trec, rtok, bl, ch, C - 1, rg, cg, el(0));
+            else
+                load_rev<L, M, D, TIn, PF_STATE, DYB>(rv[0], p, trec, rtok, bl, ch, C - 1, rg, cg, el(0));
+        }
         for (int ub = C - nb; ub >= 0; ub -= nb) {
             float* rb = red + (nred++ & 1) * (BT * L::NW * W);
             float dcv[BT][L::RPT], kv[BT][L::RPT], dkin[BT][L::RPT];
@@ -367,12 +380,15 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                     const int tau = ub + u;
                     const int64_t bth = bth_of(n * C + tau);
                     if constexpr (PF_TOKEN) {
-                        if (tau > 0)
-                            load_rev<L, M, D, TIn, PF_STATE>(rn, p, trec, rtok, bth_of(n * C + tau - 1), ch, tau - 1,
-                                                             rg, cg, el(0));
+                        // unconditional (token 0 loads itself again): a load under a
+                        // branch would be waited for where the branch joins
+                        const int tp = tau > 0 ? tau - 1 : 0;
+                        load_rev<L, M, D, TIn, PF_STATE, DYB>(rv[DBUF ? (u + 1) & 1 : 1], p, trec, rtok,
+                                                              bth_of(n * C + tp), ch, tp, rg, cg, el(0));
                     } else {
-                        load_rev<L, M, D, TIn, false>(rc, p, trec, rtok, bth, ch, tau, rg, cg, el(0));
+                        load_rev<L, M, D, TIn, false, DYB>(rv[0], p, trec, rtok, bth, ch, tau, rg, cg, el(0));
                     }
+                    const RevIn<L::RPT>& rc = rv[DBUF ? u & 1 : 0];
                     const TokenIn<L::RPT>& in = rc.in;
                     const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
                     const float hh = rc.hh;
@@ -485,7 +501,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                         dR[i] = gate[i] * dR[i];
                         if constexpr (PF_STATE) rpost[i] = rp[i];
                     }
-                    if constexpr (PF_TOKEN) rc = rn;
+                    if constexpr (PF_TOKEN && !DBUF) rv[0] = rv[1];
                     if (cg == 0) {
 #pragma unroll
                         for (int i = 0; i < L::RPT; ++i) {
@@ -555,6 +571,21 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     for (int i = 0; i < L::RPT; ++i) *reinterpret_cast<float4*>(dsi + el(i)) = dR[i];
 }
 
+template <int M, int D, int NT, typename TIn>
+static void launch_bwd_dy(const BwdParams& p, dim3 grid, size_t lds, hipStream_t st) {
+    if (p.f.lin1) {
+        if (p.dy_bf16)
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, true, true>), grid, dim3(NT), lds, st, p);
+        else
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, true, false>), grid, dim3(NT), lds, st, p);
+    } else {
+        if (p.dy_bf16)
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, false, true>), grid, dim3(NT), lds, st, p);
+        else
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, false, false>), grid, dim3(NT), lds, st, p);
+    }
+}
+
 // Launch for one slot count M (instantiated in osr_bwd_m<M>.hip).
 template <int M, int D>
 static int launch_bwd_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
@@ -562,18 +593,12 @@ static int launch_bwd_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
     constexpr int NT = (M * TPR < 512) ? M * TPR : 512;
     const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H));
     const size_t lds = static_cast<size_t>(p.f.chunk) * D * sizeof(float);  // the chunk's h
-    // the first linearisation is its own instantiation, so the default carries none of its work
-    if (in_bf16) {
-        if (p.f.lin1)
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, uint16_t, true>), grid, dim3(NT), lds, st, p);
-        else
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, uint16_t, false>), grid, dim3(NT), lds, st, p);
-    } else {
-        if (p.f.lin1)
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, float, true>), grid, dim3(NT), lds, st, p);
-        else
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, float, false>), grid, dim3(NT), lds, st, p);
-    }
+    // the first linearisation is its own instantiation, so the default carries none of its work;
+    // so is a bf16 dy (its loads then need no branch)
+    if (in_bf16)
+        launch_bwd_dy<M, D, NT, uint16_t>(p, grid, lds, st);
+    else
+        launch_bwd_dy<M, D, NT, float>(p, grid, lds, st);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

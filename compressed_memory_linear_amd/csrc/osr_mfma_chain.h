@@ -184,6 +184,11 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
     const PreOff<G> poff = prefetch_offsets<G>(p);
     prefetch<G, false>(nxt, poff, p, b, hd, 0);
     commit<G, false>(nxt, stage, p.gamma_per_slot != 0);
+    // Drain the loads above before the loop.  Left pending, they make the
+    // compiler's wait analysis treat the loop-carried state tiles as possibly
+    // still in flight at the loop head, and it then waits there for every
+    // memory operation of the previous sub-block, stores included.
+    __builtin_amdgcn_s_waitcnt(0);
 
     for (int s = 0; s < NS; ++s) {
         const int t0 = s * C0;

@@ -64,7 +64,9 @@ __device__ __forceinline__ void load_token(TokenIn<L::RPT>& in, const Params& p,
         const int row = rg + L::RG * i;
         in.k[i] = ld<TIn>(k, bth * M + row);
         in.q[i] = ld<TIn>(q, bth * M + row);
-        in.g[i] = p.gamma_per_slot ? ld<TIn>(g, bth * M + row) : ld<TIn>(g, bth);
+        // one load at a selected index: a load on either arm of a branch would be
+        // waited for where the arms join, which undoes any prefetch of the token
+        in.g[i] = ld<TIn>(g, p.gamma_per_slot ? bth * M + row : bth);
     }
     in.v = ld4<TIn>(static_cast<const TIn*>(p.v), bth * D + cg * 4);
     in.mu = ld<TIn>(static_cast<const TIn*>(p.mu), bth);
