@@ -355,6 +355,7 @@ def main() -> int:
                                                      ("chunked_b8h16_t4096_m64d128_c64", "chunked", 64, 3, 0, 0),
                                                      ("chunked_b1h16_t65536_m128d128_c128", "chunked", 128, 2, 0, 0),
                                                      (HEADLINE, "recurrent", 1, 2, 0, 0),
+                                                     (HEADLINE, "chunked", 4, 3, 0, 0),
                                                      (HEADLINE, "chunked", 64, 10, 2, 0),
                                                      (HEADLINE, "chunked", 64, 10, 0, 1),
                                                      (HEADLINE, "backward", 64, 2, 0, 0)):

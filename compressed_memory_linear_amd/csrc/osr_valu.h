@@ -118,13 +118,24 @@ __device__ __forceinline__ void chunk_h(const float4 (&z)[L::RPT], const Params&
     const int nb = C < BT ? C : BT;
     for (int u0 = 0; u0 < C; u0 += nb) {
         float* rb = red + (nred++ & 1) * (BT * L::NW * W);
+        // Every load of the batch is issued before any is used, and none under a
+        // branch (indices past the batch repeat its last token): a load inside a
+        // branch is waited for where the branch joins, one latency per token.
+        float kv[BT][L::RPT];
+#pragma unroll
+        for (int u = 0; u < BT; ++u) {
+            const int64_t bth = bth0 + (u0 + (u < nb ? u : nb - 1)) * tstride;
+#pragma unroll
+            for (int i = 0; i < L::RPT; ++i) kv[u][i] = ld<TIn>(kp, bth * M + rg + L::RG * i);
+        }
+        const int uo = tid / Q < nb ? tid / Q : nb - 1, co = tid % Q;  // this thread's output float4
+        const float4 vo = ld4<TIn>(vp, (bth0 + (u0 + uo) * tstride) * D + co * 4);
 #pragma unroll
         for (int u = 0; u < BT; ++u) {
             if (u < nb) {
-                const int64_t bth = bth0 + (u0 + u) * tstride;
                 float4 hp = f4(0.f);
 #pragma unroll
-                for (int i = 0; i < L::RPT; ++i) hp = fma4(ld<TIn>(kp, bth * M + rg + L::RG * i), z[i], hp);
+                for (int i = 0; i < L::RPT; ++i) hp = fma4(kv[u][i], z[i], hp);
                 hp.x = strided_sum<L::TPR>(hp.x);
                 hp.y = strided_sum<L::TPR>(hp.y);
                 hp.z = strided_sum<L::TPR>(hp.z);
@@ -134,12 +145,10 @@ __device__ __forceinline__ void chunk_h(const float4 (&z)[L::RPT], const Params&
         }
         __syncthreads();
         if (tid < nb * Q) {
-            const int u = tid / Q, c4 = tid % Q;
-            float4 acc = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + c4 * 4);
+            float4 acc = *reinterpret_cast<const float4*>(rb + (uo * L::NW) * W + co * 4);
 #pragma unroll
-            for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + c4 * 4);
-            const float4 v = ld4<TIn>(vp, (bth0 + (u0 + u) * tstride) * D + c4 * 4);
-            *reinterpret_cast<float4*>(hbuf + (u0 + u) * D + c4 * 4) = acc - v;
+            for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (uo * L::NW + w) * W + co * 4);
+            *reinterpret_cast<float4*>(hbuf + (u0 + uo) * D + co * 4) = acc - vo;
         }
     }
     __syncthreads();

@@ -156,7 +156,9 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
                                       rg, cg);
             }
         }
-        if (t + 1 < T) load_token<L, M, D, TIn>(nxt, p, bth_of(t + 1), rg, cg);
+        // unconditional (the last token loads itself again): a load under a branch
+        // is waited for where the branch joins, which would undo the prefetch
+        load_token<L, M, D, TIn>(nxt, p, bth_of(t + 1 < T ? t + 1 : t), rg, cg);
 
         float4 h;
         if (C > 1) {
