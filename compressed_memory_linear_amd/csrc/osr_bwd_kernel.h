@@ -104,7 +104,7 @@ __device__ __forceinline__ void load_kgm(const Params& f, int64_t bth, int rg, f
     for (int i = 0; i < L::RPT; ++i) {
         const int row = rg + L::RG * i;
         k[i] = ld<TIn>(kp, bth * M + row);
-        g[i] = f.gamma_per_slot ? ld<TIn>(gp, bth * M + row) : ld<TIn>(gp, bth);
+        g[i] = ld<TIn>(gp, f.gamma_per_slot ? bth * M + row : bth);  // one load, no branch
     }
     mu = ld<TIn>(static_cast<const TIn*>(f.mu), bth);
 }
@@ -216,7 +216,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
         float kc[L::RPT], gc[L::RPT], muc, kn[L::RPT], gn[L::RPT], mun;
         load_kgm<L, M, TIn>(p.f, bth_of(n * C), rg, kc, gc, muc);
         for (int tau = 0; tau < C; ++tau) {
-            if (tau + 1 < C) load_kgm<L, M, TIn>(p.f, bth_of(n * C + tau + 1), rg, kn, gn, mun);
+            // unconditional (the last token loads itself again): no load under a branch
+            load_kgm<L, M, TIn>(p.f, bth_of(n * C + (tau + 1 < C ? tau + 1 : tau)), rg, kn, gn, mun);
             const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
             float c[L::RPT], beta[L::RPT], hh;
             fwd_token_h<L, LIN1>(z, r, kc, gc, muc, h, mode, c, beta, hh);
@@ -268,10 +269,20 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
             // the chunk's h as the state-passing kernel formed it (lane (lg, lc) of the
             // fragment for column block jb and token tile tb holds h[16tb + 4lg + r][16jb + lc])
             const float* hs = p.chain_h + (static_cast<int64_t>(bh) * NC + n) * D * C;
-            for (int idx = tid; idx < C * D; idx += NT) {
-                const int tau = idx / D, j = idx % D;
-                const int lane_f = ((tau & 15) >> 2) * 16 + (j & 15);
-                hbuf[idx] = hs[((static_cast<int64_t>(j >> 4) * (C >> 4) + (tau >> 4)) * 64 + lane_f) * 4 + (tau & 3)];
+            // 8 loads in flight per thread before any LDS write (clamped, unconditional)
+            constexpr int G8 = 8;
+            for (int base = tid; base < C * D; base += G8 * NT) {
+                float hv[G8];
+#pragma unroll
+                for (int g = 0; g < G8; ++g) {
+                    const int idx = min(base + g * NT, C * D - 1);
+                    const int tau = idx / D, j = idx % D;
+                    const int lane_f = ((tau & 15) >> 2) * 16 + (j & 15);
+                    hv[g] = hs[((static_cast<int64_t>(j >> 4) * (C >> 4) + (tau >> 4)) * 64 + lane_f) * 4 + (tau & 3)];
+                }
+#pragma unroll
+                for (int g = 0; g < G8; ++g)
+                    if (base + g * NT < C * D) hbuf[base + g * NT] = hv[g];
             }
             __syncthreads();
         } else {
@@ -298,10 +309,14 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
             };
             load_g(0, gcur, kcur, ecur);
             for (int tau = 0; tau < C; ++tau) {
+                // the next token's loads go first, unconditionally (the last token loads
+                // itself again): a wave's memory counter drains in issue order, so the
+                // wait for them then covers no store of this token, and none of them
+                // sits under a branch (waited for where the branch joins)
+                load_g(tau + 1 < C ? tau + 1 : tau, gnx, knx, enx);
 #pragma unroll
                 for (int i = 0; i < L::RPT; ++i)
                     *reinterpret_cast<float4*>(rtok + static_cast<int64_t>(tau) * M * D + el(i)) = r[i];
-                if (tau + 1 < C) load_g(tau + 1, gnx, knx, enx);
                 const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
 #pragma unroll
                 for (int i = 0; i < L::RPT; ++i) {
@@ -318,10 +333,11 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
             float kc[L::RPT], gc[L::RPT], muc, kn[L::RPT], gn[L::RPT], mun;
             load_kgm<L, M, TIn>(p.f, bth_of(n * C), rg, kc, gc, muc);
             for (int tau = 0; tau < C; ++tau) {
+                // loads before stores, unconditional, as in the elementwise rerun above
+                load_kgm<L, M, TIn>(p.f, bth_of(n * C + (tau + 1 < C ? tau + 1 : tau)), rg, kn, gn, mun);
 #pragma unroll
                 for (int i = 0; i < L::RPT; ++i)
                     *reinterpret_cast<float4*>(rtok + static_cast<int64_t>(tau) * M * D + el(i)) = r[i];
-                if (tau + 1 < C) load_kgm<L, M, TIn>(p.f, bth_of(n * C + tau + 1), rg, kn, gn, mun);
                 const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
                 float c[L::RPT], beta[L::RPT], hh;
                 fwd_token_h<L, LIN1>(z, r, kc, gc, muc, h, mode, c, beta, hh);
