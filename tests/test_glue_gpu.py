@@ -179,3 +179,34 @@ def test_glue_post_tails_of_the_gate():
     ref = oracle.glue_gelu_gate(y.double().numpy(), g.double().numpy())
     got = out.reshape(-1).cpu().double().numpy()
     _check(got, ref, _gate_rel(g.double().numpy()) * np.abs(ref) + 1e-38, "tails")
+
+
+@pytest.mark.parametrize("C", [4, 16])
+def test_layer_pipeline_glue_forward_glue(C):
+    """glue_pre -> lattice_osr_fwd_chunked -> glue_post, every call through the C ABI with one
+    descriptor's layouts.  The forward is checked against the oracle run on the glue's own bf16
+    outputs (q, k, gamma as the GPU produced them, which the tests above pin to the glue oracle), at
+    the bf16 forward bar (max error 2e-2 of the oracle's RMS); the post-gate against the oracle's
+    gate of the GPU's y, at the gate's bar.  C = 4 runs the token loop, C = 16 the matrix-core path."""
+    B, T, H, m, d = 2, 64, 2, 16, 32
+    g = synth.make_glue_inputs(B, T, H, m, d, seed=1200 + C)
+    base = synth.make_inputs(B, T, H, m, d, seed=1300 + C)
+    print(f"layer pipeline C={C}", flush=True)
+    q, k, gamma = osr.lattice_osr_glue_pre(_dev(g.xq), _dev(g.xk), _dev(g.logit), _dev(g.wq), _dev(g.wk),
+                                           _dev(g.bq), _dev(g.bk))
+    t = osr.to_device(base)
+    y, S = osr.lattice_osr_fwd_chunked(q, k, t["v"], gamma, t["mu"], t["state"], C)
+    out = osr.lattice_osr_glue_post(y, _dev(g.gate))
+    torch.cuda.synchronize()
+
+    qv, kv, gv = _f64(q), _f64(k), _f64(gamma)
+    v64, mu64, s64 = (base.value(n).astype(np.float64) for n in ("v", "mu", "state"))
+    yr, Sr = oracle.osr_forward(qv, kv, v64, gv, mu64, s64, chunk_size=C)
+    yg, Sg = _f64(y), S.cpu().numpy().astype(np.float64)
+    for got, ref, what in ((yg, yr, "y"), (Sg, Sr, "state")):
+        err = np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2))
+        print(f"  {what} err/rms {err:.3e}", flush=True)
+        assert np.isfinite(got).all() and err <= 2e-2, (what, err)
+    gate = g.value("gate")
+    ref = oracle.glue_gelu_gate(yg, gate)
+    _check(_f64(out), ref, _gate_rel(gate) * np.abs(ref) + 1e-30, "out")
