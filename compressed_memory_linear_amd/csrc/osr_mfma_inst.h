@@ -54,11 +54,11 @@ static int launch_readout(const Params& p, hipStream_t st) {
         return -3;
     } else {
         const int BH = p.B * p.H, NC = p.T / p.chunk;
-        // At least 1024 workgroups (4 per CU); each takes cpw consecutive
-        // chunks (a power of two dividing NC), which keeps the register
-        // prefetch running across chunk boundaries.
+        // At least 512 workgroups (the kernel's registers and LDS hold two per
+        // CU); each takes cpw consecutive chunks (a power of two dividing NC),
+        // which keeps the register prefetch running across chunk boundaries.
         int cpw = 1;
-        while (cpw * 2 <= NC && NC % (cpw * 2) == 0 && static_cast<int64_t>(BH) * NC / (cpw * 2) >= 1024) cpw *= 2;
+        while (cpw * 2 <= NC && NC % (cpw * 2) == 0 && static_cast<int64_t>(BH) * NC / (cpw * 2) >= 512) cpw *= 2;
         const unsigned grid = static_cast<unsigned>(BH) * static_cast<unsigned>(NC / cpw);
         if (p.lin1)
             hipLaunchKernelGGL((osr_readout_kernel<M, D, C0, true>), dim3(grid), dim3(4 * D), 0, st, p, cpw);
