@@ -242,12 +242,14 @@ __global__ __launch_bounds__(256) void osr_glue_post_kernel(const TY* y, const T
          i0 += kPost * stride) {
         Raw8<TY> ry[kPost];
         Raw8<TG> rg[kPost];
+        // unconditional loads (a piece past the end reads the thread's own first
+        // piece again, which it writes only after every load): a load under a
+        // branch is waited for where the branch joins
 #pragma unroll
         for (int k = 0; k < kPost; ++k) {
-            if (i0 + k * stride < n) {
-                load_raw(y, i0 + k * stride, ry[k]);
-                load_raw(g, i0 + k * stride, rg[k]);
-            }
+            const int64_t ik = i0 + k * stride < n ? i0 + k * stride : i0;
+            load_raw(y, ik, ry[k]);
+            load_raw(g, ik, rg[k]);
         }
 #pragma unroll
         for (int k = 0; k < kPost; ++k) {
