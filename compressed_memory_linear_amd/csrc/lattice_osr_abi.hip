@@ -320,6 +320,7 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
     p.ws = static_cast<float*>(workspace);
     p.dy_bf16 = desc->y_dtype == LATTICE_OSR_BF16 ? 1 : 0;
     p.states_ready = chain ? 1 : 0;
+    p.stage_gk = 0;  // set by the launch where LDS allows
     p.chain_g = p.chain_k = p.chain_h = p.chain_e = p.chain_c = p.chain_b = p.chain_hh = nullptr;
     if (chain) {
         // the state-passing kernel's arrays: Z [m][d], g, kappa [m][C], h [d][C] (e [m][C]) per

@@ -178,6 +178,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     // registers allow; at 4 slot rows per thread the second buffer spilled.
     constexpr bool DBUF = L::RPT <= 2;
     extern __shared__ __attribute__((aligned(16))) float hbuf[];  // [C][D], dynamic
+    float* const gst = hbuf + p.f.chunk * D;  // [2 or 3][M*C]: staged gates (stage_gk)
     __shared__ __attribute__((aligned(16))) float red[2 * BT * L::NW * W];
     __shared__ __attribute__((aligned(16))) float tot[BT * W];  // a batch's sums over slots
     static_assert(BT * (D / 4 + 1) <= NT, "one float4 of a batch's sums per thread");
@@ -265,6 +266,29 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
             }
         }
         __syncthreads();  // the previous chunk's reverse walk is done with hbuf, red and the records
+        if (p.stage_gk) {
+            // the chunk's g, kappa (and e) into LDS, all loads of a round in flight
+            // before any LDS write; visible after the barrier that ends the h step below
+            const int64_t chs = (static_cast<int64_t>(bh) * NC + n) * M * C;
+            const int n4 = M * C / 4, narr = LIN1 ? 3 : 2;
+            const float* src[3] = {p.chain_g + chs, p.chain_k + chs, LIN1 ? p.chain_e + chs : p.chain_g + chs};
+            for (int base = tid; base < n4; base += 2 * NT) {
+                float4 v[3][2];
+#pragma unroll
+                for (int a = 0; a < 3; ++a)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int idx = min(base + j * NT, n4 - 1);
+                        if (a < narr) v[a][j] = reinterpret_cast<const float4*>(src[a])[idx];
+                    }
+#pragma unroll
+                for (int a = 0; a < 3; ++a)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        if (a < narr && base + j * NT < n4)
+                            reinterpret_cast<float4*>(gst + a * M * C)[base + j * NT] = v[a][j];
+            }
+        }
         if (p.chain_h && mode == 0) {
             // the chunk's h as the state-passing kernel formed it (lane (lg, lc) of the
             // fragment for column block jb and token tile tb holds h[16tb + 4lg + r][16jb + lc])
@@ -293,42 +317,48 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
         const int64_t ch = static_cast<int64_t>(bh) * NC + n;
         // forward again over the chunk, keeping what the reverse walk needs
         if (p.chain_c) {
-            // elementwise, from the state-passing kernel's gates of this chunk
-            const float* gch = p.chain_g + ch * M * C;
-            const float* kch = p.chain_k + ch * M * C;
-            const float* ech = LIN1 ? p.chain_e + ch * M * C : nullptr;
-            float gcur[L::RPT], kcur[L::RPT], ecur[L::RPT] = {}, gnx[L::RPT], knx[L::RPT], enx[L::RPT] = {};
-            auto load_g = [&](int tau, float (&g)[L::RPT], float (&k)[L::RPT], float (&e)[L::RPT]) {
+            // elementwise, from the state-passing kernel's gates of this chunk, staged in
+            // LDS above when they fit (read from memory, each token's gates cost one load
+            // latency, as the rerun's work per token is small).  One copy of the loop per
+            // source, so each reads through a pointer of one address space.
+            auto rerun = [&](const float* gch, const float* kch, const float* ech) __attribute__((always_inline)) {
+                float gcur[L::RPT], kcur[L::RPT], ecur[L::RPT] = {}, gnx[L::RPT], knx[L::RPT], enx[L::RPT] = {};
+                auto load_g = [&](int tau, float (&g)[L::RPT], float (&k)[L::RPT], float (&e)[L::RPT]) {
 #pragma unroll
-                for (int i = 0; i < L::RPT; ++i) {
-                    const int64_t o = gate_frag(rg + L::RG * i, tau, C);
-                    g[i] = gch[o];
-                    k[i] = kch[o];
-                    if constexpr (LIN1) e[i] = ech[o];
+                    for (int i = 0; i < L::RPT; ++i) {
+                        const int64_t o = gate_frag(rg + L::RG * i, tau, C);
+                        g[i] = gch[o];
+                        k[i] = kch[o];
+                        if constexpr (LIN1) e[i] = ech[o];
+                    }
+                };
+                load_g(0, gcur, kcur, ecur);
+                for (int tau = 0; tau < C; ++tau) {
+                    // the next token's loads go first, unconditionally (the last token loads
+                    // itself again): a wave's memory counter drains in issue order, so the
+                    // wait for them then covers no store of this token, and none of them
+                    // sits under a branch (waited for where the branch joins)
+                    load_g(tau + 1 < C ? tau + 1 : tau, gnx, knx, enx);
+#pragma unroll
+                    for (int i = 0; i < L::RPT; ++i)
+                        *reinterpret_cast<float4*>(rtok + static_cast<int64_t>(tau) * M * D + el(i)) = r[i];
+                    const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
+#pragma unroll
+                    for (int i = 0; i < L::RPT; ++i) {
+                        if constexpr (LIN1)
+                            r[i] = fma4(gcur[i], r[i], fma4(ecur[i], z[i], kcur[i] * h));
+                        else
+                            r[i] = fma4(gcur[i], r[i], kcur[i] * h);
+                        gcur[i] = gnx[i];
+                        kcur[i] = knx[i];
+                        if constexpr (LIN1) ecur[i] = enx[i];
+                    }
                 }
             };
-            load_g(0, gcur, kcur, ecur);
-            for (int tau = 0; tau < C; ++tau) {
-                // the next token's loads go first, unconditionally (the last token loads
-                // itself again): a wave's memory counter drains in issue order, so the
-                // wait for them then covers no store of this token, and none of them
-                // sits under a branch (waited for where the branch joins)
-                load_g(tau + 1 < C ? tau + 1 : tau, gnx, knx, enx);
-#pragma unroll
-                for (int i = 0; i < L::RPT; ++i)
-                    *reinterpret_cast<float4*>(rtok + static_cast<int64_t>(tau) * M * D + el(i)) = r[i];
-                const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
-#pragma unroll
-                for (int i = 0; i < L::RPT; ++i) {
-                    if constexpr (LIN1)
-                        r[i] = fma4(gcur[i], r[i], fma4(ecur[i], z[i], kcur[i] * h));
-                    else
-                        r[i] = fma4(gcur[i], r[i], kcur[i] * h);
-                    gcur[i] = gnx[i];
-                    kcur[i] = knx[i];
-                    if constexpr (LIN1) ecur[i] = enx[i];
-                }
-            }
+            if (p.stage_gk)
+                rerun(gst, gst + M * C, gst + 2 * M * C);
+            else
+                rerun(p.chain_g + ch * M * C, p.chain_k + ch * M * C, LIN1 ? p.chain_e + ch * M * C : p.chain_g);
         } else {
             float kc[L::RPT], gc[L::RPT], muc, kn[L::RPT], gn[L::RPT], mun;
             load_kgm<L, M, TIn>(p.f, bth_of(n * C), rg, kc, gc, muc);
@@ -608,13 +638,21 @@ static int launch_bwd_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
     constexpr int TPR = D / 4;
     constexpr int NT = (M * TPR < 512) ? M * TPR : 512;
     const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H));
-    const size_t lds = static_cast<size_t>(p.f.chunk) * D * sizeof(float);  // the chunk's h
+    using L = ValuLayout<M, D, NT>;
+    constexpr int BT = TokBatch<L>::BT, W = D + 4;
+    constexpr size_t static_lds = (2 * BT * L::NW * W + BT * W) * sizeof(float);  // red, tot
+    const size_t h_lds = static_cast<size_t>(p.f.chunk) * D * sizeof(float);      // the chunk's h
+    const size_t gk_lds = static_cast<size_t>(p.f.lin1 ? 3 : 2) * M * p.f.chunk * sizeof(float);
+    // the chunk's gates from the state-passing kernel, staged in LDS where it fits
+    BwdParams q = p;
+    q.stage_gk = p.chain_c != nullptr && static_lds + h_lds + gk_lds <= 128 * 1024;
+    const size_t lds = h_lds + (q.stage_gk ? gk_lds : 0);
     // the first linearisation is its own instantiation, so the default carries none of its work;
     // so is a bf16 dy (its loads then need no branch)
     if (in_bf16)
-        launch_bwd_dy<M, D, NT, uint16_t>(p, grid, lds, st);
+        launch_bwd_dy<M, D, NT, uint16_t>(q, grid, lds, st);
     else
-        launch_bwd_dy<M, D, NT, float>(p, grid, lds, st);
+        launch_bwd_dy<M, D, NT, float>(q, grid, lds, st);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -42,6 +42,7 @@ struct BwdParams {
     float* ws;               // bwd_workspace_bytes(...)
     int dy_bf16;
     int states_ready;        // 1: the chunk-start states are already in the workspace
+    int stage_gk;            // 1: the chunk's g, kappa (and e) are staged in dynamic LDS after h
     // With states_ready: the state-passing kernel's per-chunk arrays in its
     // workspace layout ([B*H*NC][rows/16][C/16][64 lanes][4], rows = m or d):
     // g, kappa, h, e (first linearisation) and c, beta; |h|^2 as [B*H*NC][C].
