@@ -3,8 +3,9 @@
 Each case plants one mistake in a copy of the oracle's C source (a dropped
 term, a flipped sign, a wrong index, the running state used where the pages
 take the chunk-start state, ...), builds the copy, and runs the pin suite
-(tests/test_oracle_pins.py) against it in a separate process: the suite must
-fail.  The real oracle is never modified.
+(tests/test_oracle_pins.py, or tests/test_oracle_glue.py for the layer glue's
+oracle) against it in a separate process: the suite must fail.  The real
+oracle is never modified.
 """
 import os
 import shutil
@@ -75,15 +76,15 @@ def _copy_tree(dst):
         f.write("")
     tdir = os.path.join(dst, "tests")
     os.makedirs(tdir)
-    for name in ("test_oracle_pins.py", "conftest.py"):
+    for name in ("test_oracle_pins.py", "test_oracle_glue.py", "conftest.py"):
         shutil.copy(os.path.join(ROOT, "tests", name), tdir)
     shutil.copy(os.path.join(ROOT, "pytest.ini"), dst)
 
 
-def _run_pins(dst):
+def _run_pins(dst, suite="test_oracle_pins.py"):
     env = dict(os.environ, PYTHONPATH=dst, OMP_NUM_THREADS="1")
     return subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                           os.path.join("tests", "test_oracle_pins.py")],
+                           os.path.join("tests", suite)],
                           cwd=dst, env=env, capture_output=True, text=True, timeout=600)
 
 
@@ -107,4 +108,48 @@ def test_pins_catch_planted_mistake(tmp_path, what, old, new):
         f.write(text.replace(old, new))
     r = _run_pins(dst)
     # a pin assertion must fail (not a build or collection error)
+    assert " failed" in r.stdout and r.returncode == 1, f"no pin caught: {what}\n{r.stdout[-2000:]}"
+
+
+# Mistakes in the layer glue's oracle (osr_glue.c), caught by tests/test_oracle_glue.py.
+GLUE_MUTANTS = [
+    ("convolution taps reversed",
+     "acc += w[(size_t)n * GLUE_W + j] * xv;",
+     "acc += w[(size_t)n * GLUE_W + (GLUE_W - 1 - j)] * xv;"),
+    ("convolution bias dropped",
+     "double acc = b ? b[n] : 0.0;",
+     "double acc = 0.0;"),
+    ("handed-on history one row early",
+     "const int s = T - P + r;",
+     "const int s = T - P + r - 1;"),
+    ("sigmoid of the negated logit",
+     "out[i] = 1.0 / (1.0 + exp(-logit[i]));",
+     "out[i] = 1.0 / (1.0 + exp(logit[i]));"),
+    ("GeLU with Phi(-x)",
+     "out[i] = y[i] * (x * (0.5 * erfc(-x / sqrt(2.0))));",
+     "out[i] = y[i] * (x * (0.5 * erfc(x / sqrt(2.0))));"),
+    ("GeLU without its factor x",
+     "out[i] = y[i] * (x * (0.5 * erfc(-x / sqrt(2.0))));",
+     "out[i] = y[i] * (0.5 * erfc(-x / sqrt(2.0)));"),
+]
+
+
+def test_unmodified_copy_passes_glue_pins(tmp_path):
+    dst = str(tmp_path)
+    _copy_tree(dst)
+    r = _run_pins(dst, "test_oracle_glue.py")
+    assert r.returncode == 0 and " passed" in r.stdout and "failed" not in r.stdout, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("what,old,new", GLUE_MUTANTS, ids=[m[0] for m in GLUE_MUTANTS])
+def test_glue_pins_catch_planted_mistake(tmp_path, what, old, new):
+    dst = str(tmp_path)
+    _copy_tree(dst)
+    src = os.path.join(dst, "oracle", "osr_glue.c")
+    with open(src) as f:
+        text = f.read()
+    assert text.count(old) == 1, f"mutation site not found once: {what}"
+    with open(src, "w") as f:
+        f.write(text.replace(old, new))
+    r = _run_pins(dst, "test_oracle_glue.py")
     assert " failed" in r.stdout and r.returncode == 1, f"no pin caught: {what}\n{r.stdout[-2000:]}"
