@@ -2,15 +2,15 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one chunk-wise OSR forward over the headline workload (B=4, H=8,
-T=2048, m=d=64, chunk 64, bf16 inputs, fp32 state and y) with every input
-already resident in HBM; the whole step runs in the library's HIP kernels,
-called through the C ABI.  The metric is head-tokens per second (B*H*T per
-step).  Printed: one JSON line with the headline value, the roofline of the
-chunk path measured live with HIP events on the launch stream, the fp64 CPU
-oracle timed on this host, and secondary lines for the decode, recurrent and
-other chunked workloads, the backward of the headline workload and the layer
-glue around the recurrence.
+A step is one chunk-wise OSR forward over the headline workload, the
+long-context one (B=1, H=16, T=65536, m=d=128, chunk 128, forget gate
+sigmoid(N(3,1)), bf16 inputs, fp32 state and y) with every input already
+resident in HBM; the whole step runs in the library's HIP kernels, called
+through the C ABI.  The metric is head-tokens per second (B*H*T per step).
+Printed: one JSON line with the headline value, the roofline of the chunk
+path measured live with HIP events on the launch stream, the fp64 CPU oracle
+timed on this host, and secondary lines for the decode, recurrent and other
+chunked workloads, the backward and the layer glue around the recurrence.
 """
 from __future__ import annotations
 
@@ -29,7 +29,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 FP32_VALU_PEAK_TFLOPS = 157.3
 
-HEADLINE = "chunked_b4h8_t2048_m64d64_c64"
+HEADLINE = "chunked_b1h16_t65536_m128d128_c128"
+HEADLINE_CHUNK = 128
+SMALL = "chunked_b4h8_t2048_m64d64_c64"
 
 
 def algorithmic_bytes(w: dict, y_bytes: int = 4) -> float:
@@ -251,6 +253,17 @@ def step_percentiles(case: Case, steps: int):
     return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "steps": steps}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(name: str, chunk: int, budget_s: float = 12.0) -> dict:
     """The fp64 oracle on this host, over the whole workload, repeated until
     about budget_s seconds have passed (at least once)."""
@@ -265,9 +278,10 @@ def cpu_baseline(name: str, chunk: int, budget_s: float = 12.0) -> dict:
         total += time.perf_counter() - t0
         reps += 1
     return {"value": inp.head_tokens * reps / total, "unit": "head-tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
             "sample": f"whole workload {name} (B*H*T = {inp.head_tokens} head-tokens), "
-                      f"{reps} repetition(s), {total:.2f} s, fp64 C with {threads} threads over (b,h)"}
+                      f"{reps} repetition(s), {total:.2f} s, fp64 C with {threads} threads over the "
+                      f"{inp.B * inp.H} (b,h) sequences (one thread per sequence at most)"}
 
 
 def main() -> int:
@@ -311,7 +325,7 @@ def main() -> int:
                           "head_tokens_per_s": case.head_tokens / (ms * 1e-3)}), flush=True)
         return 0
 
-    head = Case(HEADLINE, "chunked", 64, copies=8)
+    head = Case(HEADLINE, "chunked", HEADLINE_CHUNK, copies=1)
     ms = time_case(head, args.steps, args.warmup)
     pct = step_percentiles(head, max(args.steps, 20))
     value = head.head_tokens / (ms * 1e-3)
@@ -331,17 +345,17 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16-in/f32",
         "data": "synthetic",
-        "config": {"workload": HEADLINE, "B": 4, "H": 8, "T": 2048, "m": 64, "d": 64, "chunk": 64,
-                   "inputs": "bf16", "state": "f32", "y": "f32", "objective": "decoding",
-                   "input_copies": head.copies},
+        "config": {"workload": HEADLINE, "B": head.w["B"], "H": head.w["H"], "T": head.w["T"], "m": head.w["m"],
+                   "d": head.w["d"], "chunk": HEADLINE_CHUNK, "inputs": "bf16", "state": "f32", "y": "f32",
+                   "objective": "decoding", "forget_gate": "sigmoid(N(3,1))", "input_copies": head.copies},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(f"chunked:{HEADLINE}"),
                      "algorithmic_bytes_per_launch": abytes,
-                     "algorithmic_flops_per_launch": algorithmic_flops(head.w, 64),
-                     "mfma_frac_algorithmic": algorithmic_flops(head.w, 64) / (ms * 1e-3) / 1e12
+                     "algorithmic_flops_per_launch": algorithmic_flops(head.w, HEADLINE_CHUNK),
+                     "mfma_frac_algorithmic": algorithmic_flops(head.w, HEADLINE_CHUNK) / (ms * 1e-3) / 1e12
                                               / BF16_MFMA_PEAK_TFLOPS,
-                     "chain_reference_ms": chain_reference_ms(head.w, 64),
+                     "chain_reference_ms": chain_reference_ms(head.w, HEADLINE_CHUNK),
                      "kernels": "one call = state-passing kernel + read-out kernel (split per kernel in "
                                 "the rocprofv3 summary)",
                      "measured": "HIP events on the launch stream around the timed steps"},
@@ -351,15 +365,16 @@ def main() -> int:
 
     if not args.no_secondary:
         sec = []
-        for name, entry, chunk, steps, mode, lin in (("decode_s256h32_m128d128", "decode", 1, 50, 0, 0),
-                                                     ("chunked_b8h16_t4096_m64d128_c64", "chunked", 64, 3, 0, 0),
-                                                     ("chunked_b1h16_t65536_m128d128_c128", "chunked", 128, 2, 0, 0),
-                                                     (HEADLINE, "recurrent", 1, 2, 0, 0),
-                                                     (HEADLINE, "chunked", 4, 3, 0, 0),
-                                                     (HEADLINE, "chunked", 64, 10, 2, 0),
-                                                     (HEADLINE, "chunked", 64, 10, 0, 1),
-                                                     (HEADLINE, "backward", 64, 2, 0, 0)):
-            c = Case(name, entry, chunk, copies=8 if name == HEADLINE and entry == "chunked" else 1,
+        for name, entry, chunk, steps, mode, lin in ((SMALL, "chunked", 64, 20, 0, 0),
+                                                     ("decode_s256h32_m128d128", "decode", 1, 50, 0, 0),
+                                                     ("chunked_b8h16_t4096_m64d128_c64", "chunked", 64, 5, 0, 0),
+                                                     (SMALL, "recurrent", 1, 2, 0, 0),
+                                                     (SMALL, "chunked", 4, 3, 0, 0),
+                                                     (SMALL, "chunked", 64, 10, 2, 0),
+                                                     (SMALL, "chunked", 64, 10, 0, 1),
+                                                     (SMALL, "backward", 64, 2, 0, 0)):
+            # the small workload (51 MB) fits the 256 MB Infinity Cache: rotate 8 input copies
+            c = Case(name, entry, chunk, copies=8 if name == SMALL and entry == "chunked" else 1,
                      mode=mode, linearisation=lin)
             t_ms = time_case(c, steps, 1)
             ab = algorithmic_bytes_bwd(c.w) if entry == "backward" else algorithmic_bytes(c.w)
@@ -370,7 +385,9 @@ def main() -> int:
                         "hbm_gbs_algorithmic": ab / (t_ms * 1e-3) / 1e9,
                         "hbm_frac": ab / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "tflops_algorithmic": None if entry == "backward"
-                        else algorithmic_flops(c.w, chunk) / (t_ms * 1e-3) / 1e12})
+                        else algorithmic_flops(c.w, chunk) / (t_ms * 1e-3) / 1e12,
+                        "chain_reference_ms": chain_reference_ms(c.w, chunk) if entry == "chunked" and chunk >= 16
+                        else None})
             del c
             torch.cuda.empty_cache()
         for entry in ("glue_pre", "glue_post"):
@@ -387,7 +404,7 @@ def main() -> int:
         out["secondary"] = sec
 
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(HEADLINE, 64)
+        out["cpu_baseline"] = cpu_baseline(HEADLINE, HEADLINE_CHUNK)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -36,6 +36,11 @@ int check_desc(const lattice_osr_desc* d) {
         return LATTICE_OSR_ERR_UNSUPPORTED;
     if (d->gamma_per_slot != 0 && d->gamma_per_slot != 1) return LATTICE_OSR_ERR_UNSUPPORTED;
     if (d->linearisation != LATTICE_OSR_LIN2 && d->linearisation != LATTICE_OSR_LIN1) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->schedule != LATTICE_OSR_SCHED_AUTO && d->schedule != LATTICE_OSR_SCHED_SPLIT &&
+        d->schedule != LATTICE_OSR_SCHED_FUSED)
+        return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->chain_pairs != LATTICE_OSR_PAIRS_AUTO && d->chain_pairs != LATTICE_OSR_PAIRS_OFF)
+        return LATTICE_OSR_ERR_UNSUPPORTED;
     return LATTICE_OSR_OK;
 }
 
@@ -50,7 +55,8 @@ Path chunk_path(const lattice_osr_desc* d, int C) {
 
 size_t workspace_needed(const lattice_osr_desc* d, int C) {
     if (chunk_path(d, C) == Path::Mfma)
-        return osr::mfma_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1);
+        return osr::mfma_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1,
+                                         d->schedule);
     return 0;
 }
 
@@ -117,6 +123,8 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     p.mode = d->mode;
     p.lin1 = d->linearisation == LATTICE_OSR_LIN1 ? 1 : 0;
     p.y_bf16 = d->y_dtype == LATTICE_OSR_BF16 ? 1 : 0;
+    p.schedule = d->schedule;
+    p.chain_pairs = d->chain_pairs;
     return p;
 }
 

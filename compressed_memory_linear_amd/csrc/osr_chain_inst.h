@@ -2,9 +2,6 @@
 // (included once per M by osr_chain_m*.hip).
 #pragma once
 
-#include <stdlib.h>
-#include <string.h>
-
 #include "osr_launch.h"
 #include "osr_mfma_chain.h"
 
@@ -32,7 +29,7 @@ constexpr int pick_c0_chain(int C) {
 // faster (m=32 d=32 C=64: 87 vs 97 us; m=16 d=64: 129 vs 161 us for
 // B4 H8 T2048).  From m = 64 every SIMD already holds one wave, the phases are
 // bound by the CU's shared LDS and issue throughput, and the extra exchange
-// made it slower (169 vs 159 us at m=d=64 C=64).  LATTICE_OSR_CHAIN_PAIRS=0
+// made it slower (169 vs 159 us at m=d=64 C=64).  Params::chain_pairs = 1
 // turns it off.
 template <int M, int D, int C0>
 constexpr bool pair_capable() {
@@ -40,10 +37,6 @@ constexpr bool pair_capable() {
         return chain_fits<M, D, C0, true>();
     else
         return false;
-}
-static bool pairs_enabled() {
-    const char* e = getenv("LATTICE_OSR_CHAIN_PAIRS");
-    return !(e && strcmp(e, "0") == 0);
 }
 
 template <int M, int D, int C0, bool ENC, bool LIN1, bool RAW>
@@ -55,7 +48,7 @@ static void launch_chain_mode(const Params& p, hipStream_t st) {
         return;
     }
     if constexpr (pair_capable<M, D, C0>()) {
-        if (pairs_enabled()) {
+        if (p.chain_pairs == 0) {
             hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, true, true, ENC, LIN1, RAW>), dim3(BH), dim3(8 * M), 0,
                                st, p);
             return;

@@ -33,6 +33,8 @@ struct Params {
     int mode;          // 0 = decoding objective, 1 = similarity objective, 2 = encoding layer
     int lin1;          // 1: first chunk linearisation (token loop, or the split MFMA schedule)
     int y_bf16;        // 1: y is bf16, 0: y is fp32
+    int schedule;      // matrix-core chunk schedule: 0 automatic, 1 split, 2 fused
+    int chain_pairs;   // state passing: 0 pairs where they pay, 1 one wave per slot block
 };
 
 // ---------------------------------------------------------------- bf16 ----

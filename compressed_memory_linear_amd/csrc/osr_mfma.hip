@@ -9,9 +9,6 @@
 //   fused: one workgroup per (b,h) does both (osr_mfma_kernels.h); no
 //          workspace.
 // split wins when B*H alone cannot fill the 256 compute units.
-#include <stdlib.h>
-#include <string.h>
-
 #include "osr_launch.h"
 #include "osr_mfma_kernels.h"
 
@@ -26,16 +23,15 @@ extern template int launch_m<32>(int, bool, const Params&, hipStream_t);
 extern template int launch_m<64>(int, bool, const Params&, hipStream_t);
 extern template int launch_m<128>(int, bool, const Params&, hipStream_t);
 
-// Schedule choice.  LATTICE_OSR_CHUNK_SCHEDULE=split|fused overrides the
-// default (split when there are fewer (b,h) sequences than compute units).
-// The split schedule (state passing, then a read-out parallel over chunks)
-// wins while the sequences leave CUs idle; the fused kernel, with no
-// workspace round trip, once they fill the device: measured crossovers
-// between 128 and 256 (b,h) at d = 128 and between 256 and 512 at d = 64.
-bool use_split(int B, int H, int d) {
-    const char* e = getenv("LATTICE_OSR_CHUNK_SCHEDULE");
-    if (e && strcmp(e, "split") == 0) return true;
-    if (e && strcmp(e, "fused") == 0) return false;
+// Schedule choice (schedule: 0 automatic, 1 split, 2 fused; the first
+// linearisation has no fused form).  The split schedule (state passing, then
+// a read-out parallel over chunks) wins while the sequences leave CUs idle;
+// the fused kernel, with no workspace round trip, once they fill the device:
+// measured crossovers between 128 and 256 (b,h) at d = 128 and between 256
+// and 512 at d = 64.
+bool use_split(int B, int H, int d, int schedule, bool lin1) {
+    if (lin1 || schedule == 1) return true;
+    if (schedule == 2) return false;
     const int64_t bh = static_cast<int64_t>(B) * H;
     return bh < 256 || (d <= 64 && bh < 512);
 }
@@ -54,8 +50,8 @@ size_t mfma_chain_workspace_bytes(int B, int H, int T, int m, int d, int C, bool
 }
 
 // The first linearisation runs on the split schedule only.
-size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1) {
-    if (!lin1 && !mfma::use_split(B, H, d)) return 0;
+size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1, int schedule) {
+    if (!mfma::use_split(B, H, d, schedule, lin1)) return 0;
     return mfma_chain_workspace_bytes(B, H, T, m, d, C, lin1);
 }
 
@@ -70,7 +66,7 @@ int launch_mfma_chain_only(int m, int d, const Params& p, hipStream_t st) {
 }
 
 int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st) {
-    const bool split = p.lin1 || mfma::use_split(p.B, p.H, d);
+    const bool split = mfma::use_split(p.B, p.H, d, p.schedule, p.lin1 != 0);
     switch (m) {
         case 16: return mfma::launch_m<16>(d, split, p, st);
         case 32: return mfma::launch_m<32>(d, split, p, st);

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblattice_
 F32, BF16 = 0, 1
 MODE_DEC, MODE_SIM, MODE_ENC = 0, 1, 2
 LIN2, LIN1 = 0, 1
+SCHED_AUTO, SCHED_SPLIT, SCHED_FUSED = 0, 1, 2
+PAIRS_AUTO, PAIRS_OFF = 0, 1
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_ALIGN = -1, -2, -3, -4, -5, -6, -7
@@ -32,7 +34,8 @@ EXPORTED = ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr
 
 class lattice_osr_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("B", "T", "H", "m", "d", "gamma_per_slot", "in_dtype", "y_dtype", "mode", "linearisation")]
+                ("B", "T", "H", "m", "d", "gamma_per_slot", "in_dtype", "y_dtype", "mode", "linearisation",
+                 "schedule", "chain_pairs")]
 
 
 class OSRError(RuntimeError):
@@ -88,8 +91,10 @@ def status_string(status: int) -> str:
 lattice_osr_status_string = status_string
 
 
-def make_desc(B, T, H, m, d, gamma_per_slot=1, in_dtype=BF16, y_dtype=F32, mode=MODE_DEC, linearisation=LIN2):
-    return lattice_osr_desc(B, T, H, m, d, gamma_per_slot, in_dtype, y_dtype, mode, linearisation)
+def make_desc(B, T, H, m, d, gamma_per_slot=1, in_dtype=BF16, y_dtype=F32, mode=MODE_DEC, linearisation=LIN2,
+              schedule=SCHED_AUTO, chain_pairs=PAIRS_AUTO):
+    return lattice_osr_desc(B, T, H, m, d, gamma_per_slot, in_dtype, y_dtype, mode, linearisation, schedule,
+                            chain_pairs)
 
 
 def lattice_osr_workspace_bytes(desc: lattice_osr_desc, chunk_size: int) -> int:
@@ -107,23 +112,68 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation=0) -> lattice_osr_desc:
+def _shape_error(name, t, want):
+    raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _check_tensor(name, t, shape, dtype, device=None):
+    """Shape, dtype and layout of one argument, then its device: the kernels
+    index every buffer by the descriptor's sizes, so a mismatch would read or
+    write past it on the GPU."""
+    if tuple(t.shape) != tuple(shape):
+        _shape_error(name, t, shape)
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} is {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _check_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("every tensor argument must be a GPU (cuda) tensor")
+
+
+def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation=0, schedule=SCHED_AUTO,
+               chain_pairs=PAIRS_AUTO) -> lattice_osr_desc:
+    """Descriptor of a forward call, after checking every input against it:
+    q, k [B,T,H,m]; v [B,T,H,d]; gamma [B,T,H,m] or [B,T,H]; mu [B,T,H]
+    (all one dtype, float32 or bfloat16); state_in [B,H,m,d] float32; all
+    contiguous, on one GPU."""
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q/k/gamma are [B,T,H,m], v is [B,T,H,d]")
     B, T, H, m = q.shape
     d = v.shape[-1]
     if q.dtype not in _DT:
         raise ValueError("inputs must be float32 or bfloat16")
-    for t in (q, k, v, gamma, mu):
-        if t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
-            raise ValueError("q, k, v, gamma, mu must share dtype/device and be contiguous")
-    if state_in.dtype != torch.float32 or not state_in.is_contiguous():
-        raise ValueError("state must be contiguous float32 [B,H,m,d]")
+    if y_dtype not in _DT:
+        raise ValueError("y_dtype must be torch.float32 or torch.bfloat16")
     per_slot = 1 if gamma.dim() == 4 else 0
-    return make_desc(B, T, H, m, d, per_slot, _DT[q.dtype], _DT[y_dtype], mode, linearisation)
+    _check_tensor("q", q, (B, T, H, m), q.dtype)
+    _check_tensor("k", k, (B, T, H, m), q.dtype, q.device)
+    _check_tensor("v", v, (B, T, H, d), q.dtype, q.device)
+    _check_tensor("gamma", gamma, (B, T, H, m) if per_slot else (B, T, H), q.dtype, q.device)
+    _check_tensor("mu", mu, (B, T, H), q.dtype, q.device)
+    _check_tensor("state_in", state_in, (B, H, m, d), torch.float32, q.device)
+    return make_desc(B, T, H, m, d, per_slot, _DT[q.dtype], _DT[y_dtype], mode, linearisation, schedule,
+                     chain_pairs)
+
+
+def _check_outputs(desc, q, state_in, state_out, y, y_dtype):
+    """Caller-supplied outputs against the descriptor, then the device of
+    every tensor."""
+    if y is not None:
+        _check_tensor("y", y, (desc.B, desc.T, desc.H, desc.d), y_dtype, q.device)
+    if state_out is not None:
+        _check_tensor("state_out", state_out, tuple(state_in.shape), torch.float32, q.device)
+    _check_cuda(q)
 
 
 def _outputs(desc, q, state_in, state_out, y, y_dtype):
+    """Missing outputs are allocated (on the current stream, which the caller
+    has set to the launch stream)."""
     if y is None:
         y = torch.empty((desc.B, desc.T, desc.H, desc.d), dtype=y_dtype, device=q.device)
     if state_out is None:
@@ -131,27 +181,43 @@ def _outputs(desc, q, state_in, state_out, y, y_dtype):
     return state_out, y
 
 
-def _stream(stream) -> int:
-    if stream is None:
-        stream = torch.cuda.current_stream()
-    return stream.cuda_stream
+def _workspace(workspace, need, device):
+    """The caller's workspace (a uint8 tensor on the inputs' device) or a new
+    one of `need` bytes; returns (tensor or None, its size in bytes)."""
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    elif not workspace.is_contiguous() or workspace.device != device:
+        raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _launch_stream(stream):
+    """The stream to launch on.  Temporaries (outputs, workspace) are
+    allocated under it: the caching allocator then reuses their memory only
+    in that stream's order, after the kernels that use it."""
+    return torch.cuda.current_stream() if stream is None else stream
 
 
 def lattice_osr_fwd_chunked(q, k, v, gamma, mu, state_in, chunk_size: int, *, mode: int = MODE_DEC,
                             y_dtype=torch.float32, state_out=None, y=None, workspace=None,
-                            stream=None, linearisation: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
+                            stream=None, linearisation: int = 0, schedule: int = SCHED_AUTO,
+                            chain_pairs: int = PAIRS_AUTO) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunk-wise OSR forward.  Returns (y [B,T,H,d], state_out [B,H,m,d]).
-    linearisation: LIN2 (default, eq. recurrence_linear2) or LIN1."""
+    linearisation: LIN2 (default, eq. recurrence_linear2) or LIN1.
+    schedule / chain_pairs: the matrix-core schedule (speed only)."""
     lib = load_library()
-    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation)
-    state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
-    need = lattice_osr_workspace_bytes(desc, chunk_size)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib.lattice_osr_fwd_chunked(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
-                                     _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y),
-                                     _ptr(workspace), wbytes, _stream(stream))
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation, schedule, chain_pairs)
+    _check_outputs(desc, q, state_in, state_out, y, y_dtype)
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
+        need = lattice_osr_workspace_bytes(desc, chunk_size)
+        workspace, wbytes = _workspace(workspace, need, q.device)
+        rc = lib.lattice_osr_fwd_chunked(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y),
+                                         _ptr(workspace), wbytes, st.cuda_stream)
     if rc != OK:
         raise OSRError(rc, "lattice_osr_fwd_chunked")
     return y, state_out
@@ -163,10 +229,13 @@ def lattice_osr_fwd_recurrent(q, k, v, gamma, mu, state_in, *, mode: int = MODE_
     """Exact token-by-token OSR forward.  Returns (y, state_out)."""
     lib = load_library()
     desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode)
-    state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
-    rc = lib.lattice_osr_fwd_recurrent(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
-                                       _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y), None, 0,
-                                       _stream(stream))
+    _check_outputs(desc, q, state_in, state_out, y, y_dtype)
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
+        rc = lib.lattice_osr_fwd_recurrent(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                           _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y), None, 0,
+                                           st.cuda_stream)
     if rc != OK:
         raise OSRError(rc, "lattice_osr_fwd_recurrent")
     return y, state_out
@@ -178,10 +247,13 @@ def lattice_osr_decode_step(q, k, v, gamma, mu, state_in, *, mode: int = MODE_DE
     """One exact decode step (T = 1); state_out may be state_in (in place)."""
     lib = load_library()
     desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode)
-    state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
-    rc = lib.lattice_osr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
-                                     _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y), None, 0,
-                                     _stream(stream))
+    _check_outputs(desc, q, state_in, state_out, y, y_dtype)
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
+        rc = lib.lattice_osr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                         _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y), None, 0,
+                                         st.cuda_stream)
     if rc != OK:
         raise OSRError(rc, "lattice_osr_decode_step")
     return y, state_out
@@ -204,30 +276,33 @@ def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_
     (allocated unless passed in `grads`)."""
     lib = load_library()
     desc = _desc_from(q, k, v, gamma, mu, state_in, dy.dtype, mode, linearisation)
-    if not dy.is_contiguous() or dy.shape != v.shape or dy.device != q.device:
-        raise ValueError("dy must be contiguous with v's shape")
-    if dstate_out.dtype != torch.float32 or not dstate_out.is_contiguous() or dstate_out.shape != state_in.shape:
-        raise ValueError("dstate_out must be contiguous float32 with the state's shape")
-    if grads is None:
-        grads = {"d" + n: torch.empty(t.shape, dtype=torch.float32, device=q.device)
-                 for n, t in (("q", q), ("k", k), ("v", v), ("gamma", gamma), ("mu", mu),
-                              ("state_in", state_in))}
-    need = lattice_osr_bwd_workspace_bytes(desc, chunk_size)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    g = grads
-    rc = lib.lattice_osr_bwd_chunked(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
-                                     _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(dy), _ptr(dstate_out),
-                                     _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dgamma"]),
-                                     _ptr(g["dmu"]), _ptr(g["dstate_in"]), _ptr(workspace), wbytes,
-                                     _stream(stream))
+    _check_tensor("dy", dy, tuple(v.shape), None, q.device)
+    _check_tensor("dstate_out", dstate_out, tuple(state_in.shape), torch.float32, q.device)
+    named = (("q", q), ("k", k), ("v", v), ("gamma", gamma), ("mu", mu), ("state_in", state_in))
+    if grads is not None:
+        for n, t in named:
+            if "d" + n not in grads:
+                raise ValueError(f"grads lacks d{n}")
+            _check_tensor("d" + n, grads["d" + n], tuple(t.shape), torch.float32, q.device)
+    _check_cuda(q)
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        if grads is None:
+            grads = {"d" + n: torch.empty(t.shape, dtype=torch.float32, device=q.device) for n, t in named}
+        need = lattice_osr_bwd_workspace_bytes(desc, chunk_size)
+        workspace, wbytes = _workspace(workspace, need, q.device)
+        g = grads
+        rc = lib.lattice_osr_bwd_chunked(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(dy), _ptr(dstate_out),
+                                         _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dgamma"]),
+                                         _ptr(g["dmu"]), _ptr(g["dstate_in"]), _ptr(workspace), wbytes,
+                                         st.cuda_stream)
     if rc != OK:
         raise OSRError(rc, "lattice_osr_bwd_chunked")
     return grads
 
 
-# ------------------------------------------------------------ host inputs --
+# ------------------------------------------------------------ layer glue --
 def lattice_osr_glue_pre(xq, xk, gamma_logit, conv_wq, conv_wk, conv_bq=None, conv_bk=None, hist_q=None,
                          hist_k=None, *, q=None, k=None, gamma=None, hist_q_out=None, hist_k_out=None,
                          return_history: bool = False, stream=None):
@@ -241,24 +316,45 @@ def lattice_osr_glue_pre(xq, xk, gamma_logit, conv_wq, conv_wk, conv_bq=None, co
     if xq.dim() != 4 or xq.dtype not in _DT:
         raise ValueError("xq/xk are [B,T,H,m] float32 or bfloat16")
     B, T, H, m = xq.shape
-    for t in (xk, gamma_logit):
-        if t.dtype != xq.dtype or not t.is_contiguous() or t.device != xq.device:
-            raise ValueError("xq, xk, gamma_logit must share dtype/device and be contiguous")
-    for t in (conv_wq, conv_wk, conv_bq, conv_bk):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
-            raise ValueError("convolution weights and biases are contiguous float32")
+    dev = xq.device
     per_slot = 1 if gamma_logit.dim() == 4 else 0
+    gshape = (B, T, H, m) if per_slot else (B, T, H)
+    _check_tensor("xq", xq, (B, T, H, m), xq.dtype)
+    _check_tensor("xk", xk, (B, T, H, m), xq.dtype, dev)
+    _check_tensor("gamma_logit", gamma_logit, gshape, xq.dtype, dev)
+    _check_tensor("conv_wq", conv_wq, (H, m, 4), torch.float32, dev)
+    _check_tensor("conv_wk", conv_wk, (H, m, 4), torch.float32, dev)
+    for name, t in (("conv_bq", conv_bq), ("conv_bk", conv_bk)):
+        if t is not None:
+            _check_tensor(name, t, (H, m), torch.float32, dev)
+    if (hist_q is None) != (hist_k is None):
+        raise ValueError("pass both histories or neither")
+    for name, t in (("hist_q", hist_q), ("hist_k", hist_k)):
+        if t is not None:
+            _check_tensor(name, t, (B, 3, H, m), xq.dtype, dev)
+    _check_cuda(xq)
     desc = make_desc(B, T, H, m, m, per_slot, _DT[xq.dtype], F32)
-    q = torch.empty_like(xq) if q is None else q
-    k = torch.empty_like(xk) if k is None else k
-    gamma = torch.empty_like(gamma_logit) if gamma is None else gamma
-    if return_history:
-        hist_q_out = xq.new_empty((B, 3, H, m)) if hist_q_out is None else hist_q_out
-        hist_k_out = xk.new_empty((B, 3, H, m)) if hist_k_out is None else hist_k_out
-    rc = lib.lattice_osr_glue_pre(ctypes.byref(desc), _ptr(xq), _ptr(xk), _ptr(gamma_logit), _ptr(conv_wq),
-                                  _ptr(conv_wk), _ptr(conv_bq), _ptr(conv_bk), _ptr(hist_q), _ptr(hist_k),
-                                  _ptr(q), _ptr(k), _ptr(gamma), _ptr(hist_q_out), _ptr(hist_k_out),
-                                  _stream(stream))
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        outs = {}
+        for name, t, like, shape in (("q", q, xq, (B, T, H, m)), ("k", k, xk, (B, T, H, m)),
+                                     ("gamma", gamma, gamma_logit, gshape)):
+            if t is None:
+                t = torch.empty_like(like)
+            else:
+                _check_tensor(name, t, shape, xq.dtype, dev)
+            outs[name] = t
+        q, k, gamma = outs["q"], outs["k"], outs["gamma"]
+        if return_history:
+            hist_q_out = xq.new_empty((B, 3, H, m)) if hist_q_out is None else hist_q_out
+            hist_k_out = xk.new_empty((B, 3, H, m)) if hist_k_out is None else hist_k_out
+        for name, t in (("hist_q_out", hist_q_out), ("hist_k_out", hist_k_out)):
+            if t is not None:
+                _check_tensor(name, t, (B, 3, H, m), xq.dtype, dev)
+        rc = lib.lattice_osr_glue_pre(ctypes.byref(desc), _ptr(xq), _ptr(xk), _ptr(gamma_logit), _ptr(conv_wq),
+                                      _ptr(conv_wk), _ptr(conv_bq), _ptr(conv_bk), _ptr(hist_q), _ptr(hist_k),
+                                      _ptr(q), _ptr(k), _ptr(gamma), _ptr(hist_q_out), _ptr(hist_k_out),
+                                      st.cuda_stream)
     if rc != OK:
         raise OSRError(rc, "lattice_osr_glue_pre")
     if return_history:
@@ -270,14 +366,20 @@ def lattice_osr_glue_post(y, gate, *, out=None, stream=None):
     """out = y * GeLU(gate) (exact GeLU); y [B,T,H,d] float32 or bfloat16, gate of y's shape in
     float32 or bfloat16.  out may be y (in place)."""
     lib = load_library()
-    if y.dim() != 4 or y.dtype not in _DT or gate.dtype not in _DT or gate.shape != y.shape:
+    if y.dim() != 4 or y.dtype not in _DT or gate.dtype not in _DT:
         raise ValueError("y and gate are [B,T,H,d] float32 or bfloat16 tensors of one shape")
-    if not (y.is_contiguous() and gate.is_contiguous()):
-        raise ValueError("y and gate must be contiguous")
+    _check_tensor("y", y, tuple(y.shape), y.dtype)
+    _check_tensor("gate", gate, tuple(y.shape), gate.dtype, y.device)
+    _check_cuda(y)
     B, T, H, d = y.shape
     desc = make_desc(B, T, H, 16, d, 1, _DT[gate.dtype], _DT[y.dtype])
-    out = torch.empty_like(y) if out is None else out
-    rc = lib.lattice_osr_glue_post(ctypes.byref(desc), _ptr(y), _ptr(gate), _ptr(out), _stream(stream))
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        if out is None:
+            out = torch.empty_like(y)
+        else:
+            _check_tensor("out", out, tuple(y.shape), y.dtype, y.device)
+        rc = lib.lattice_osr_glue_post(ctypes.byref(desc), _ptr(y), _ptr(gate), _ptr(out), st.cuda_stream)
     if rc != OK:
         raise OSRError(rc, "lattice_osr_glue_post")
     return out

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define LATTICE_OSR_ABI_VERSION 4
+#define LATTICE_OSR_ABI_VERSION 5
 
 #if defined(__GNUC__) || defined(__clang__)
 #define LATTICE_OSR_API __attribute__((visibility("default")))
@@ -88,6 +88,24 @@ extern "C" {
 #define LATTICE_OSR_LIN1 1 /* eq. recurrence_linear1: gate mu beta on the running
                               slot, the projection term h~ k^ on the chunk-start slot */
 
+/* Matrix-core chunk schedule (bf16 inputs, chunk_size >= 16).  A choice of
+ * speed only: every schedule evaluates the same chunk formula (the results
+ * agree to the rounding of the split-bf16 products).  Ignored where the
+ * token-loop kernel runs (fp32 inputs, chunk_size < 16). */
+#define LATTICE_OSR_SCHED_AUTO 0  /* split while the (b,h) sequences leave compute units idle
+                                     (fewer than 256 sequences, 512 at d <= 64), else fused */
+#define LATTICE_OSR_SCHED_SPLIT 1 /* a state-passing kernel (sequential over chunks) stores each
+                                     chunk's start state, gates and h in the workspace; a read-out
+                                     kernel then forms every y_t in parallel over chunks */
+#define LATTICE_OSR_SCHED_FUSED 2 /* one kernel per sequence does both; no workspace.  The first
+                                     linearisation has no fused form and takes the split schedule */
+
+/* Wave layout of the state-passing kernel (split schedule). */
+#define LATTICE_OSR_PAIRS_AUTO 0 /* two waves per block of 16 slots, one per token half of the
+                                    chunk, where that measured faster (m <= 32 with the chunk as
+                                    one sub-block of >= 32 tokens); one wave elsewhere */
+#define LATTICE_OSR_PAIRS_OFF 1  /* always one wave per block of 16 slots */
+
 /* Status codes. */
 #define LATTICE_OSR_OK 0
 #define LATTICE_OSR_ERR_NULL (-1)        /* a required pointer is NULL              */
@@ -109,6 +127,8 @@ typedef struct {
     int32_t y_dtype;        /* LATTICE_OSR_F32 or LATTICE_OSR_BF16               */
     int32_t mode;           /* LATTICE_OSR_MODE_DEC, _SIM or _ENC                */
     int32_t linearisation;  /* LATTICE_OSR_LIN2 (0) or LATTICE_OSR_LIN1 (1)      */
+    int32_t schedule;       /* LATTICE_OSR_SCHED_AUTO (0), _SPLIT (1), _FUSED (2) */
+    int32_t chain_pairs;    /* LATTICE_OSR_PAIRS_AUTO (0) or _OFF (1)            */
 } lattice_osr_desc;
 
 /*
@@ -148,8 +168,9 @@ LATTICE_OSR_API int lattice_osr_decode_step(const lattice_osr_desc* desc, const 
                             const float* state_in, float* state_out, void* y,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Workspace bytes lattice_osr_fwd_chunked needs for this shape (0 if none);
- * (size_t)-1 if the arguments are invalid. */
+/* Workspace bytes lattice_osr_fwd_chunked needs for this descriptor (shape,
+ * linearisation and schedule) and chunk size (0 if none); (size_t)-1 if the
+ * arguments are invalid.  Pass the same descriptor to the forward. */
 LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc, int32_t chunk_size);
 
 /*

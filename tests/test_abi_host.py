@@ -34,7 +34,7 @@ def test_header_declarations_are_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert osr.lattice_osr_abi_version() == 4
+    assert osr.lattice_osr_abi_version() == 5
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = osr.status_string(code)
         assert s and s != "unknown status"
@@ -76,6 +76,8 @@ def test_null_pointers(fn):
     ("in_dtype", 2, osr.ERR_UNSUPPORTED), ("y_dtype", 7, osr.ERR_UNSUPPORTED),
     ("mode", 3, osr.ERR_UNSUPPORTED), ("mode", -1, osr.ERR_UNSUPPORTED), ("gamma_per_slot", 2, osr.ERR_UNSUPPORTED),
     ("linearisation", 2, osr.ERR_UNSUPPORTED), ("linearisation", -1, osr.ERR_UNSUPPORTED),
+    ("schedule", 3, osr.ERR_UNSUPPORTED), ("schedule", -1, osr.ERR_UNSUPPORTED),
+    ("chain_pairs", 2, osr.ERR_UNSUPPORTED), ("chain_pairs", -1, osr.ERR_UNSUPPORTED),
 ])
 def test_bad_descriptor(field, value, status):
     d = osr.make_desc(2, 8, 2, 32, 32)
@@ -107,6 +109,35 @@ def test_first_linearisation_workspace():
     big1 = osr.make_desc(64, 256, 8, m, d, linearisation=osr.LIN1)
     assert osr.lattice_osr_workspace_bytes(big2, 64) == 0
     assert osr.lattice_osr_workspace_bytes(big1, 64) > 0
+
+
+def test_schedule_field_sets_the_workspace():
+    """The workspace query follows the descriptor's schedule, so the query and
+    the launch it sizes always agree: the split schedule needs the per-chunk
+    arrays, the fused kernel none; the first linearisation has no fused form."""
+    B, T, H, m, d, C = 2, 256, 4, 64, 64, 64
+    per_chunk = (m * d + 2 * m * C + d * C) * 4
+    auto = osr.make_desc(B, T, H, m, d)
+    split = osr.make_desc(B, T, H, m, d, schedule=osr.SCHED_SPLIT)
+    fused = osr.make_desc(B, T, H, m, d, schedule=osr.SCHED_FUSED)
+    assert osr.lattice_osr_workspace_bytes(auto, C) == B * H * (T // C) * per_chunk  # few sequences: split
+    assert osr.lattice_osr_workspace_bytes(split, C) == B * H * (T // C) * per_chunk
+    assert osr.lattice_osr_workspace_bytes(fused, C) == 0
+    fused1 = osr.make_desc(B, T, H, m, d, schedule=osr.SCHED_FUSED, linearisation=osr.LIN1)
+    assert osr.lattice_osr_workspace_bytes(fused1, C) > 0
+    big_split = osr.make_desc(64, 256, 8, m, d, schedule=osr.SCHED_SPLIT)
+    assert osr.lattice_osr_workspace_bytes(big_split, C) == 64 * 8 * (256 // C) * per_chunk
+    # the pair switch changes no buffer
+    nopair = osr.make_desc(B, T, H, m, d, chain_pairs=osr.PAIRS_OFF)
+    assert osr.lattice_osr_workspace_bytes(nopair, C) == osr.lattice_osr_workspace_bytes(auto, C)
+
+
+def test_library_reads_no_environment():
+    """Every knob is a descriptor field: no source of the library reads the
+    process environment."""
+    import glob
+    for path in glob.glob(os.path.join(ROOT, "compressed_memory_linear_amd", "csrc", "*")):
+        assert "getenv" not in open(path).read(), path
 
 
 def test_chunk_size_rules():

@@ -9,10 +9,10 @@ RMS of the oracle's gradient at most 1e-4 for fp32 inputs and 2e-2 for bf16
 inputs.  Small shapes are compared in full; at the workload sizes the oracle
 recomputes a sample of whole (batch, head) sequences (sequences are
 independent, so their gradients are too).  The encoding layer's gradient
-amplifies rounding-size perturbations: it is compared element by element over
-16 tokens against a bar derived from the oracle's own sensitivity to such
-perturbations, and at 1024 tokens through a property that holds at any
-length.
+amplifies rounding-size perturbations: it is compared element by element at
+the same fixed bars over short sequences where the oracle's own change under
+such perturbations stays well below the bar, and at 1024 tokens through a
+property that holds at any length.
 """
 import concurrent.futures as cf
 import sys
@@ -117,35 +117,25 @@ def test_bwd_tiny_fp32(mode, C, per_slot):
     _check(inp, _gpu_bwd(inp, dy, dso, C, mode), _oracle(inp, dy, dso, C, mode))
 
 
-def _conditioned_tol(inp, dy, dso, C, mode, ref, lin=ob.LIN2):
-    """Bar for a badly conditioned gradient, derived from the oracle itself:
-    the largest relative change of any oracle gradient (max-abs over RMS)
-    when every input is perturbed by 1e-7 relative (fp32 rounding size),
-    times 20 for the many roundings of an fp32 evaluation; never below the
-    standard bar."""
-    a = list(inp.values_f64())
-    rng = np.random.default_rng(99)
-    a2 = [x * (1 + 1e-7 * rng.standard_normal(x.shape)) for x in a]
-    g2 = ob.osr_backward(*a2, dy, dso, chunk_size=C, mode=mode, linearisation=lin)
-    sens = max(_rel(g2[k], ref[k]) for k in KEYS)
-    tol = max(TOL[inp.in_dtype], 20.0 * sens)
-    _say(f"  oracle sensitivity {sens:.2e} -> bar {tol:.2e}")
-    return tol
+# The encoding layer's gradient is badly conditioned: in the fp64 gradient
+# oracle a 1e-7 relative change of every input (fp32 rounding size) moves it by
+# up to 2.5e-3 of its RMS at 16 tokens (C = 1) and by 5e-6 - 1e-4 at 4 - 16
+# tokens, depending on the draw.  fp32 evaluation can meet the fixed 1e-4 bar
+# only where that change is a few 1e-5 or less, so each case is a stated
+# (chunk size, length, seed) where the oracle's change at 1e-7 is measured at
+# <= 3e-5: C1 T4 seed 23 (per token) 5.9e-6 and seed 11 (per slot) 1.4e-5;
+# C4 T8 seed 41 (per slot) 1.5e-5 and seed 31 (per token) 7.9e-6; C16 T16
+# seed 11 5.1e-6 (per slot) and 6.3e-6 (per token).
+ENC_FP32_CASES = [(1, 4, 23, False), (1, 4, 11, True), (4, 8, 41, True), (4, 8, 31, False), (16, 16, 11, True),
+                  (16, 16, 11, False)]
 
 
-@pytest.mark.parametrize("C", [1, 4, 16])
-@pytest.mark.parametrize("per_slot", [True, False])
-def test_bwd_encoding_layer_short_fp32(C, per_slot):
-    """The encoding layer's gradient amplifies rounding-size perturbations
-    (in the fp64 oracle a 1e-7 relative change of the inputs moves it by
-    1e-5 - 1e-3 of its RMS at 8 - 32 tokens and by up to O(1) at 64), so it
-    is compared over 16 tokens against a bar derived from that sensitivity."""
-    _say(f"bwd encoding layer fp32 B1 H2 T16 m16 d32 C{C} per_slot{per_slot}")
-    inp = synth.make_inputs(1, 16, 2, 16, 32, seed=11, in_dtype=synth.F32, gamma_per_slot=per_slot)
-    dy, dso = _upstream(inp, 11)
-    ref = _oracle(inp, dy, dso, C, osr.MODE_ENC)
-    tol = _conditioned_tol(inp, dy, dso, C, osr.MODE_ENC, ref)
-    _check(inp, _gpu_bwd(inp, dy, dso, C, osr.MODE_ENC), ref, tol=tol)
+@pytest.mark.parametrize("C,T,seed,per_slot", ENC_FP32_CASES)
+def test_bwd_encoding_layer_short_fp32(C, T, seed, per_slot):
+    _say(f"bwd encoding layer fp32 B1 H2 T{T} m16 d32 C{C} per_slot{per_slot} seed{seed}")
+    inp = synth.make_inputs(1, T, 2, 16, 32, seed=seed, in_dtype=synth.F32, gamma_per_slot=per_slot)
+    dy, dso = _upstream(inp, seed)
+    _check(inp, _gpu_bwd(inp, dy, dso, C, osr.MODE_ENC), _oracle(inp, dy, dso, C, osr.MODE_ENC))
 
 
 @pytest.mark.parametrize("m,d", [(16, 16), (32, 64), (64, 64), (64, 128), (128, 32), (128, 128)])
@@ -157,14 +147,14 @@ def test_bwd_shapes_bf16(m, d, C):
     _check(inp, _gpu_bwd(inp, dy, dso, C, osr.MODE_DEC), _oracle(inp, dy, dso, C, osr.MODE_DEC))
 
 
+# encoding layer: 16 tokens, where a 2^-17 relative change of the inputs moves
+# the oracle's gradient by 1.3e-3 of its RMS (2.1e-2 at 32 tokens)
 @pytest.mark.parametrize("mode,T", [(osr.MODE_SIM, 128), (osr.MODE_ENC, 16)])
 def test_bwd_other_objectives_bf16(mode, T):
     _say(f"bwd bf16 B2 H3 T{T} m64 d64 C16 mode{mode}")
     inp = synth.make_inputs(2, T, 3, 64, 64, seed=13, in_dtype=synth.BF16)
     dy, dso = _upstream(inp, 13)
-    ref = _oracle(inp, dy, dso, 16, mode)
-    tol = _conditioned_tol(inp, dy, dso, 16, mode, ref) if mode == osr.MODE_ENC else None
-    _check(inp, _gpu_bwd(inp, dy, dso, 16, mode), ref, tol=tol)
+    _check(inp, _gpu_bwd(inp, dy, dso, 16, mode), _oracle(inp, dy, dso, 16, mode))
 
 
 @pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM, osr.MODE_ENC])
@@ -261,14 +251,16 @@ def test_bwd_first_linearisation_bf16(m, d):
            _oracle(inp, dy, dso, 64, osr.MODE_DEC, lin=ob.LIN1))
 
 
-@pytest.mark.parametrize("C", [4, 16])
-def test_bwd_first_linearisation_encoding_layer_fp32(C):
-    _say(f"bwd LIN1 encoding layer fp32 B1 H2 T16 m16 d32 C{C}")
-    inp = synth.make_inputs(1, 16, 2, 16, 32, seed=23, in_dtype=synth.F32)
-    dy, dso = _upstream(inp, 23)
-    ref = _oracle(inp, dy, dso, C, osr.MODE_ENC, lin=ob.LIN1)
-    tol = _conditioned_tol(inp, dy, dso, C, osr.MODE_ENC, ref, lin=ob.LIN1)
-    _check(inp, _gpu_bwd(inp, dy, dso, C, osr.MODE_ENC, lin=osr.LIN1), ref, tol=tol)
+# (chunk size, length, seed) where the oracle's gradient moves by <= 1e-5 of
+# its RMS under a 1e-7 relative change of the inputs (C4 T8 seed 23: 1.0e-5;
+# C16 T16 seed 11: 5.1e-6)
+@pytest.mark.parametrize("C,T,seed", [(4, 8, 23), (16, 16, 11)])
+def test_bwd_first_linearisation_encoding_layer_fp32(C, T, seed):
+    _say(f"bwd LIN1 encoding layer fp32 B1 H2 T{T} m16 d32 C{C} seed{seed}")
+    inp = synth.make_inputs(1, T, 2, 16, 32, seed=seed, in_dtype=synth.F32)
+    dy, dso = _upstream(inp, seed)
+    _check(inp, _gpu_bwd(inp, dy, dso, C, osr.MODE_ENC, lin=osr.LIN1),
+           _oracle(inp, dy, dso, C, osr.MODE_ENC, lin=ob.LIN1))
 
 
 def test_bwd_first_linearisation_headline_sampled():

@@ -179,31 +179,23 @@ def _oracle_lin1(inp, C, mode):
     return oracle.osr_forward(q, k, v, g, mu, S, chunk_size=C, mode=mode, linearisation=oracle.LIN1)
 
 
-def _encoding_layer_bar(inp, C, yr, Sr):
-    """Bar for the encoding layer with the first linearisation on the matrix
-    cores, derived from the oracle itself: its largest relative change (y or
-    state, max-abs over RMS) when every input is perturbed by 2^-17 relative,
-    the precision of the hi + lo bf16 operands of the split products; never
-    below the standard bar.  This recurrence amplifies perturbations (at
-    m = d = 128, C = 16, 256 tokens that change reaches 0.18), the decoding
-    and similarity ones damp them."""
-    a = list(inp.values_f64())
-    rng = np.random.default_rng(17)
-    a2 = [x * (1 + 2.0 ** -17 * rng.standard_normal(x.shape)) for x in a]
-    y2, S2 = oracle.osr_forward(*a2, chunk_size=C, mode=osr.MODE_ENC, linearisation=oracle.LIN1)
-    sens = max(_rel(y2, yr), _rel(S2, Sr))
-    _say(f"  oracle sensitivity at 2^-17: {sens:.2e}")
-    return max(TOL[inp.in_dtype], sens)
-
-
 def _check_lin1(inp, y, S, C, mode):
     tol = TOL[inp.in_dtype]
     yr, Sr = _oracle_lin1(inp, C, mode)
-    if mode == osr.MODE_ENC and inp.in_dtype == synth.BF16 and C >= 16:
-        tol = _encoding_layer_bar(inp, C, yr, Sr)
     ey, es = _rel(y.float().cpu().numpy(), yr), _rel(S.cpu().numpy(), Sr)
     _say(f"  y err/rms = {ey:.3e}, state err/rms = {es:.3e} (tol {tol:g})")
     assert ey <= tol and es <= tol, (ey, es)
+
+
+# The encoding layer with the first linearisation amplifies perturbations
+# fast: in the fp64 oracle a 2^-17 relative change of every input (the
+# precision of the split-bf16 operands) moves y or the state by O(1) of their
+# RMS within 128 - 256 tokens at m = 16 (C = 4) and m = d = 128 (C = 16), where
+# the decoding and similarity objectives damp it.  Element-wise parity at the
+# fixed bar is therefore checked over lengths where that change stays below
+# 7e-3 (measured: m16 d32 C4 T32 <= 6.3e-3; m64 d64 C64 T128 <= 1.6e-3;
+# m128 d128 C16 T32 <= 6.6e-3; m32 d128 C128 T256 <= 3.2e-3).
+ENC_LIN1_T = {4: 32, 16: 32, 64: 128, 128: 256}
 
 
 @pytest.mark.parametrize("C", [1, 4, 16, 64])
@@ -222,8 +214,9 @@ def test_tiny_chunked_lin1(C, mode):
 @pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM, osr.MODE_ENC])
 @pytest.mark.parametrize("per_slot", [True, False])
 def test_bf16_chunked_lin1(m, d, C, mode, per_slot):
-    _say(f"bf16 chunked, first linearisation, m={m} d={d} C={C} mode={mode} per_slot={per_slot}")
-    inp = synth.make_inputs(2, 256, 3, m, d, seed=800 + m + d + C, in_dtype=synth.BF16, gamma_per_slot=per_slot)
+    T = ENC_LIN1_T[C] if mode == osr.MODE_ENC else 256
+    _say(f"bf16 chunked, first linearisation, m={m} d={d} C={C} T={T} mode={mode} per_slot={per_slot}")
+    inp = synth.make_inputs(2, T, 3, m, d, seed=800 + m + d + C, in_dtype=synth.BF16, gamma_per_slot=per_slot)
     t = osr.to_device(inp)
     y, S = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], C,
                                        mode=mode, linearisation=osr.LIN1)
@@ -362,17 +355,17 @@ def test_deterministic(entry, C):
 
 
 # ----------------------------------------------------- MFMA chunk schedules --
+SCHED = {"split": osr.SCHED_SPLIT, "fused": osr.SCHED_FUSED}
 MFMA_CASES = [(16, 16, 16), (32, 32, 32), (64, 64, 64), (64, 128, 64), (128, 64, 32), (128, 128, 128),
               (32, 128, 16), (128, 32, 64)]
 
 
 @pytest.mark.parametrize("schedule", ["split", "fused"])
 @pytest.mark.parametrize("m,d,C", MFMA_CASES)
-def test_mfma_schedules(monkeypatch, schedule, m, d, C):
+def test_mfma_schedules(schedule, m, d, C):
     _say(f"mfma schedule={schedule} m={m} d={d} C={C}")
-    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", schedule)
     inp = synth.make_inputs(2, 4 * C, 3, m, d, seed=100 + m + 3 * d + C, in_dtype=synth.BF16)
-    y, S = _run("chunked", inp, C)
+    y, S = _run("chunked", inp, C, schedule=SCHED[schedule])
     _check(inp, y, S, C, osr.MODE_DEC)
 
 
@@ -381,11 +374,10 @@ def test_mfma_schedules(monkeypatch, schedule, m, d, C):
 # start H at +V and write with gamma (c - k)).
 @pytest.mark.parametrize("schedule", ["split", "fused"])
 @pytest.mark.parametrize("m,d,C", [(16, 16, 16), (64, 64, 64), (64, 128, 64), (128, 128, 128), (32, 128, 16)])
-def test_mfma_schedules_encoding(monkeypatch, schedule, m, d, C):
+def test_mfma_schedules_encoding(schedule, m, d, C):
     _say(f"mfma encoding layer schedule={schedule} m={m} d={d} C={C}")
-    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", schedule)
     inp = synth.make_inputs(2, 4 * C, 3, m, d, seed=700 + m + 3 * d + C, in_dtype=synth.BF16)
-    y, S = _run("chunked", inp, C, mode=osr.MODE_ENC)
+    y, S = _run("chunked", inp, C, mode=osr.MODE_ENC, schedule=SCHED[schedule])
     _check(inp, y, S, C, osr.MODE_ENC)
 
 
@@ -395,22 +387,19 @@ def test_mfma_schedules_encoding(monkeypatch, schedule, m, d, C):
 @pytest.mark.parametrize("schedule", ["split", "fused"])
 @pytest.mark.parametrize("m,d,C,nc", [(64, 64, 64, 5), (64, 128, 64, 3), (128, 128, 128, 3), (32, 64, 32, 7),
                                       (16, 32, 16, 9)])
-def test_mfma_odd_chunk_counts(monkeypatch, schedule, m, d, C, nc):
+def test_mfma_odd_chunk_counts(schedule, m, d, C, nc):
     _say(f"mfma schedule={schedule} m={m} d={d} C={C} chunks={nc}")
-    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", schedule)
     inp = synth.make_inputs(3, nc * C, 5, m, d, seed=600 + m + d + nc, in_dtype=synth.BF16)
-    y, S = _run("chunked", inp, C)
+    y, S = _run("chunked", inp, C, schedule=SCHED[schedule])
     _check(inp, y, S, C, osr.MODE_DEC)
 
 
 @pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM, osr.MODE_ENC])
-def test_mfma_split_and_fused_agree(monkeypatch, mode):
+def test_mfma_split_and_fused_agree(mode):
     _say(f"mfma split vs fused mode={mode}")
     inp = synth.make_inputs(2, 256, 2, 64, 64, seed=77, in_dtype=synth.BF16)
-    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "split")
-    ys, Ss = _run("chunked", inp, 64, mode=mode)
-    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "fused")
-    yf, Sf = _run("chunked", inp, 64, mode=mode)
+    ys, Ss = _run("chunked", inp, 64, mode=mode, schedule=osr.SCHED_SPLIT)
+    yf, Sf = _run("chunked", inp, 64, mode=mode, schedule=osr.SCHED_FUSED)
     # The schedules evaluate the same chunk formula with different sub-block
     # lengths and MFMA shapes, so they agree to the rounding of the split-bf16
     # products (about 2^-16 relative each, summed over tens of products per
@@ -423,62 +412,56 @@ def test_mfma_split_and_fused_agree(monkeypatch, mode):
 # Pairs run for m <= 32 with C >= 32; the m = 64 case checks that the
 # override leaves the one-wave kernel in place there.
 PAIR_CASES = [(32, 32, 32), (32, 32, 64), (16, 64, 64), (16, 16, 32), (32, 64, 64), (32, 128, 32), (64, 64, 64)]
+PAIRS = {"1": osr.PAIRS_AUTO, "0": osr.PAIRS_OFF}
 
 
 @pytest.mark.parametrize("pairs", ["1", "0"])
 @pytest.mark.parametrize("m,d,C", PAIR_CASES)
-def test_chain_pairs(monkeypatch, pairs, m, d, C):
+def test_chain_pairs(pairs, m, d, C):
     """Shapes where a chunk is one sub-block: the two-waves-per-slot-block
     state passing (default) and the one-wave form, both against the oracle,
     over several chunks and both objectives."""
     _say(f"state passing pairs={pairs} m={m} d={d} C={C}")
-    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "split")
-    monkeypatch.setenv("LATTICE_OSR_CHAIN_PAIRS", pairs)
     for mode in (osr.MODE_DEC, osr.MODE_SIM):
         inp = synth.make_inputs(2, 6 * C, 2, m, d, seed=300 + m + d + C + mode, in_dtype=synth.BF16)
-        y, S = _run("chunked", inp, C, mode=mode)
+        y, S = _run("chunked", inp, C, mode=mode, schedule=osr.SCHED_SPLIT, chain_pairs=PAIRS[pairs])
         _check(inp, y, S, C, mode)
 
 
-def test_chain_pairs_agree(monkeypatch):
+def test_chain_pairs_agree():
     """The pair split regroups the chunk's suffix products exactly; the two
     forms agree to the split-bf16 rounding of their products."""
     _say("state passing pairs vs one wave per slot block")
     inp = synth.make_inputs(2, 512, 2, 32, 64, seed=404, in_dtype=synth.BF16)
-    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "split")
-    monkeypatch.setenv("LATTICE_OSR_CHAIN_PAIRS", "1")
-    y1, S1 = _run("chunked", inp, 64)
-    monkeypatch.setenv("LATTICE_OSR_CHAIN_PAIRS", "0")
-    y0, S0 = _run("chunked", inp, 64)
+    y1, S1 = _run("chunked", inp, 64, schedule=osr.SCHED_SPLIT, chain_pairs=osr.PAIRS_AUTO)
+    y0, S0 = _run("chunked", inp, 64, schedule=osr.SCHED_SPLIT, chain_pairs=osr.PAIRS_OFF)
     assert (y1 - y0).abs().max().item() <= 2e-4 * y0.abs().max().item()
     assert (S1 - S0).abs().max().item() <= 1e-4
 
 
 @pytest.mark.parametrize("pairs", ["1", "0"])
 @pytest.mark.parametrize("m,d,C", [(32, 32, 64), (16, 64, 64), (32, 128, 32), (64, 128, 64), (128, 64, 128)])
-def test_chain_pairs_first_linearisation(monkeypatch, pairs, m, d, C):
+def test_chain_pairs_first_linearisation(pairs, m, d, C):
     """The first linearisation on the matrix cores, with the state passing in
     both its pair and one-wave forms (where a chunk is one sub-block) and in
     sub-blocks (m64 d128 C64, m128 d64 C128), several chunks, all objectives."""
     _say(f"first linearisation, state passing pairs={pairs} m={m} d={d} C={C}")
-    monkeypatch.setenv("LATTICE_OSR_CHAIN_PAIRS", pairs)
     for mode in (osr.MODE_DEC, osr.MODE_SIM, osr.MODE_ENC):
         inp = synth.make_inputs(2, 4 * C, 2, m, d, seed=900 + m + d + C + mode, in_dtype=synth.BF16)
         t = osr.to_device(inp)
         y, S = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], C,
-                                           mode=mode, linearisation=osr.LIN1)
+                                           mode=mode, linearisation=osr.LIN1, chain_pairs=PAIRS[pairs])
         torch.cuda.synchronize()
         _check_lin1(inp, y, S, C, mode)
 
 
-def test_first_linearisation_ignores_fused_override(monkeypatch):
+def test_first_linearisation_ignores_fused_override():
     """The first linearisation runs on the split schedule even where the
     default would take the fused kernel (many sequences) or it is asked for."""
-    _say("first linearisation with LATTICE_OSR_CHUNK_SCHEDULE=fused, B32 H8 m64 d64 C64")
-    monkeypatch.setenv("LATTICE_OSR_CHUNK_SCHEDULE", "fused")
+    _say("first linearisation with the fused schedule asked for, B32 H8 m64 d64 C64")
     inp = synth.make_inputs(32, 128, 8, 64, 64, seed=950, in_dtype=synth.BF16)
     t = osr.to_device(inp)
     y, S = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], 64,
-                                       linearisation=osr.LIN1)
+                                       linearisation=osr.LIN1, schedule=osr.SCHED_FUSED)
     torch.cuda.synchronize()
     _check_lin1(inp, y, S, 64, osr.MODE_DEC)
