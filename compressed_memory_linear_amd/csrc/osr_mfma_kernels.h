@@ -175,6 +175,35 @@ __device__ __forceinline__ void rows4_prod_scan(float x, int lg, float& below, f
     above = ((lg & 1) ? 1.f : o) * ((lg & 2) ? 1.f : hi);
 }
 
+// Product of the first two of the four 16-lane rows of x, per lane column
+// (the first 8 tokens of a 16-token tile when each row holds 4 of them).
+__device__ __forceinline__ float rows01_prod(float x) {
+    float e, o, lo, hi;
+    pair_rows(x, e, o);
+    half_rows(e * o, lo, hi);
+    return lo;
+}
+
+// Scale reference of the in-sub-block gate products.  The causal part of the
+// read-out pairs q_t A_t with kappa_j / A_j, A the running product of g from
+// the sub-block start; with small gates A_j underflows (and 1/A_j overflows)
+// although every ratio A_t / A_j (j <= t) is a product of gates.  Both factors
+// are therefore taken relative to A at the middle of the sub-block, a_ref (the
+// product of g over its first half): q_t A_t / a_ref and kappa_j a_ref / A_j,
+// whose exponents span half the range each; the (Q.A) R term then takes R
+// scaled by a_ref.
+template <int TB>
+__device__ __forceinline__ float half_product(const float (&tot)[TB], float first_rows) {
+    if constexpr (TB == 1) {
+        return first_rows;
+    } else {
+        float a = 1.f;
+#pragma unroll
+        for (int tb = 0; tb < TB / 2; ++tb) a *= tot[tb];
+        return a;
+    }
+}
+
 // Workspace of the split schedule, fp32, for every (b,h) and chunk n (all
 // taken at the chunk-start state): Z [m][d], the gates g and kappa and the
 // vectors h (and, with the first linearisation, the coefficient e of the
@@ -260,7 +289,8 @@ struct Cfg {
     static constexpr int O_WH = O_TL + (K32_C ? D * HT_LD * 2 : 0); // W^T hi [M][WT_LD]
     static constexpr int O_WL = O_WH + M * WT_LD * 2;               // W^T lo
     static constexpr int O_AE = O_WL + M * WT_LD * 2;               // A_end [M]
-    static constexpr int O_NP = O_AE + M * 4;                       // norm partials [NW][M]
+    static constexpr int O_AR = O_AE + M * 4;                       // a_ref [M] (see half_product)
+    static constexpr int O_NP = O_AR + M * 4;                       // norm partials [NW][M]
     static constexpr int O_QH = O_NP + NW * M * 4;                  // Q.A hi [C0][QA_LD]
     static constexpr int O_QL = O_QH + (WITH_Y ? C0 * QA_LD * 2 : 0);
     static constexpr int O_KH = O_QL + (WITH_Y ? C0 * QA_LD * 2 : 0);  // kappa/A hi
@@ -438,6 +468,7 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
     short* wth = reinterpret_cast<short*>(smem + G::O_WH);
     short* wtl = reinterpret_cast<short*>(smem + G::O_WL);
     float* aend = reinterpret_cast<float*>(smem + G::O_AE);
+    float* arefs = reinterpret_cast<float*>(smem + G::O_AR);
     short* qah = reinterpret_cast<short*>(smem + G::O_QH);
     short* qal = reinterpret_cast<short*>(smem + G::O_QL);
     short* kah = reinterpret_cast<short*>(smem + G::O_KH);
@@ -505,7 +536,7 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
         const int mb = w + mi * G::NW;
         if (mb < MT) {
             const int i = 16 * mb + lc;  // this lane's slot
-            float gt[TB][4], kp[TB][4], tot[TB], ex_lo[TB], ex_hi[TB];
+            float gt[TB][4], kp[TB][4], tot[TB], ex_lo[TB], ex_hi[TB], first_rows = 1.f;
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
                 f32x4 c = {0.f, 0.f, 0.f, 0.f};
@@ -543,9 +574,12 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
                     prod *= gt[tb][r];
                 }
                 group_scan(prod, lg, ex_lo[tb], ex_hi[tb], tot[tb]);
+                if (TB == 1) first_rows = rows01_prod(prod);
             }
-            // Running (A) and suffix (prod_{l > t}) products over the sub-block.
-            float fwd = 1.f;
+            // Running (A, relative to a_ref) and suffix (prod_{l > t}) products
+            // over the sub-block.
+            const float aref = half_product<TB>(tot, first_rows);
+            float fwd = 1.f / aref;
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
                 float bwd = 1.f;
@@ -579,7 +613,10 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
                 *reinterpret_cast<s16x4*>(wtl + i * G::WT_LD + 16 * tb + 4 * lg) = wl4;
                 fwd *= tot[tb];
             }
-            if (lg == 0) aend[i] = fwd;
+            if (lg == 0) {
+                aend[i] = fwd * aref;
+                arefs[i] = aref;
+            }
         }
     }
     if (has_next) commit<G, WITH_Y>(nxt, st_next, p.gamma_per_slot != 0);
@@ -587,15 +624,15 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
 
     // ---- read-out: Y = (Q.A) R + tril(P) H, P^T = (kappa/A)(Q.A)^T ---
     if constexpr (WITH_Y) {
+        // R scaled by a_ref per slot (the Q.A tiles are relative to it)
         s16x4 rfh[MT], rfl[MT];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            if (r_is_z) {
-                rfh[mt] = zfh[mt];
-                rfl[mt] = zfl[mt];
-            } else {
-                split4(acc_R[mt], rfh[mt], rfl[mt]);
-            }
+            const f32x4 ar = *reinterpret_cast<const f32x4*>(arefs + 16 * mt + 4 * lg);
+            f32x4 rs = acc_R[mt];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rs[r] *= ar[r];
+            split4(rs, rfh[mt], rfl[mt]);
         }
         const int64_t row0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;
 #pragma unroll

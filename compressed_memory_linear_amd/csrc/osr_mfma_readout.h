@@ -53,8 +53,9 @@ struct ReadCfg {
     static constexpr int B_WH = B_KL + C0 * QA_LD * 2;   // W^T hi      [M][WT_LD]
     static constexpr int B_WL = B_WH + M * WT_LD * 2;    // W^T lo
     static constexpr int B_AE = B_WL + M * WT_LD * 2;    // A_end       [M] fp32
+    static constexpr int B_AR = B_AE + M * 4;            // a_ref       [M] fp32 (see half_product)
     static constexpr int NPT = TB * (TB + 1) / 2;        // causal P^T tiles (tb, jb <= tb)
-    static constexpr int B_P = B_AE + M * 4;             // P^T hi, lo  [NPT][2][64 lanes] bf16 x4
+    static constexpr int B_P = B_AR + M * 4;             // P^T hi, lo  [NPT][2][64 lanes] bf16 x4
     // first linearisation: Q.A.E hi, lo [C0][QA_LD] (coefficients of Z) and A_end E_end [M] fp32
     static constexpr int B_ZH = B_P + NPT * 2 * 64 * 8;
     static constexpr int B_ZL = B_ZH + (LIN1 ? C0 * QA_LD * 2 : 0);
@@ -176,6 +177,7 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
         short* wth = reinterpret_cast<short*>(buf + G::B_WH);
         short* wtl = reinterpret_cast<short*>(buf + G::B_WL);
         float* aend = reinterpret_cast<float*>(buf + G::B_AE);
+        float* arefs = reinterpret_cast<float*>(buf + G::B_AR);
         short* zqh = reinterpret_cast<short*>(buf + G::B_ZH);
         short* zql = reinterpret_cast<short*>(buf + G::B_ZL);
         float* aez = reinterpret_cast<float*>(buf + G::B_AZ);
@@ -196,15 +198,19 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
             const int mb = w + mi * G::NW;
             if (mb < MT) {
                 const int slot = 16 * mb + lc;
-                float below[TB], above[TB], tot[TB];
+                float below[TB], above[TB], tot[TB], first_rows = 1.f;
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
                     const f32x4 g = cur.g[mi][tb];
-                    rows4_prod_scan(g[0] * g[1] * g[2] * g[3], lg, below[tb], above[tb], tot[tb]);
+                    const float x = g[0] * g[1] * g[2] * g[3];
+                    rows4_prod_scan(x, lg, below[tb], above[tb], tot[tb]);
+                    if (TB == 1) first_rows = rows01_prod(x);
                 }
-                // A (running product, inclusive), Q.A and kappa/A, token-major;
-                // first linearisation: E (running sum of e/A, inclusive) and Q.A.E.
-                float fwd = 1.f, esum = 0.f;
+                // A (running product, inclusive, relative to a_ref), Q.A and
+                // kappa/A, token-major; first linearisation: E (running sum of
+                // e/A, inclusive) and Q.A.E.
+                const float aref = half_product<TB>(tot, first_rows);
+                float fwd = 1.f / aref, esum = 0.f;
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
                     const f32x4 g = cur.g[mi][tb], kp = cur.k[mi][tb];
@@ -273,17 +279,25 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
                     bwd *= tot[tb];
                 }
                 if (lg == 0) {
-                    aend[slot] = fwd;
-                    if constexpr (LIN1) aez[slot] = fwd * esum;
+                    aend[slot] = fwd * aref;
+                    arefs[slot] = aref;
+                    if constexpr (LIN1) aez[slot] = fwd * esum;  // A_end E_end: the a_ref factors cancel
                 }
             }
         }
         __syncthreads();  // Q.A, kappa/A, W^T, A_end visible
 
         // ---- Y = (Q.A) R + tril(P) H, P^T = (kappa/A)(Q.A)^T ------------------
+        // R scaled by a_ref per slot (the Q.A tiles are relative to it)
         s16x4 rh[MT], rl[MT], hh[TB], hl[TB];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) split4(acc[mt], rh[mt], rl[mt]);
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 ar = *reinterpret_cast<const f32x4*>(arefs + 16 * mt + 4 * lg);
+            f32x4 rs = acc[mt];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rs[r] *= ar[r];
+            split4(rs, rh[mt], rl[mt]);
+        }
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) split4(cur.h[tb], hh[tb], hl[tb]);
         const int64_t row0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;
