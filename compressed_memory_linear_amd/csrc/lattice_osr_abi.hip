@@ -41,6 +41,7 @@ int check_desc(const lattice_osr_desc* d) {
         return LATTICE_OSR_ERR_UNSUPPORTED;
     if (d->chain_pairs != LATTICE_OSR_PAIRS_AUTO && d->chain_pairs != LATTICE_OSR_PAIRS_OFF)
         return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->chain_wgs != LATTICE_OSR_WGS_AUTO && d->chain_wgs != LATTICE_OSR_WGS_ONE) return LATTICE_OSR_ERR_UNSUPPORTED;
     return LATTICE_OSR_OK;
 }
 
@@ -56,7 +57,7 @@ Path chunk_path(const lattice_osr_desc* d, int C) {
 size_t workspace_needed(const lattice_osr_desc* d, int C) {
     if (chunk_path(d, C) == Path::Mfma)
         return osr::mfma_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1,
-                                         d->schedule);
+                                         d->schedule, d->chain_wgs);
     return 0;
 }
 
@@ -125,6 +126,9 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     p.y_bf16 = d->y_dtype == LATTICE_OSR_BF16 ? 1 : 0;
     p.schedule = d->schedule;
     p.chain_pairs = d->chain_pairs;
+    p.chain_wgs = d->chain_wgs;
+    p.xbuf = nullptr;
+    p.xflags = nullptr;
     return p;
 }
 

@@ -39,9 +39,44 @@ constexpr bool pair_capable() {
         return false;
 }
 
+// Sub-block length of the state-passing kernel for (d, C) at this M.
+template <int M>
+int chain_subblock_m(int d, int C) {
+    switch (d) {
+        case 16: return pick_c0_chain<M, 16>(C);
+        case 32: return pick_c0_chain<M, 32>(C);
+        case 64: return pick_c0_chain<M, 64>(C);
+        case 128: return pick_c0_chain<M, 128>(C);
+        default: return 0;
+    }
+}
+
+template <int N>
+__global__ void osr_zero_ints(int* x, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) x[i] = N;
+}
+
 template <int M, int D, int C0, bool ENC, bool LIN1, bool RAW>
 static void launch_chain_mode(const Params& p, hipStream_t st) {
     const unsigned BH = static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H);
+    if constexpr (!RAW && C0 <= 64) {
+        // Split over P = C / C0 workgroups per sequence (the caller set up the
+        // hand-off buffers only where that applies): counters to zero first.
+        if (p.xbuf && (p.chunk == 2 * C0 || p.chunk == 4 * C0)) {
+            const int P = p.chunk / C0;
+            const int nflags = static_cast<int>(BH) * P * (M / 16) * XFLAG_STRIDE;
+            hipLaunchKernelGGL(osr_zero_ints<0>, dim3((nflags + 255) / 256), dim3(256), 0, st, p.xflags, nflags);
+            const unsigned grid = (BH + 7) / 8 * 8 * static_cast<unsigned>(P);
+            if (P == 2)
+                hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false, false, ENC, LIN1, false, 2>), dim3(grid),
+                                   dim3(4 * M), 0, st, p);
+            else
+                hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false, false, ENC, LIN1, false, 4>), dim3(grid),
+                                   dim3(4 * M), 0, st, p);
+            return;
+        }
+    }
     if (p.chunk != C0) {
         hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false, false, ENC, LIN1, RAW>), dim3(BH), dim3(4 * M), 0,
                            st, p);

@@ -4,5 +4,6 @@
 namespace osr {
 namespace mfma {
 template int launch_chain_m<32>(int d, const Params& p, hipStream_t st);
+template int chain_subblock_m<32>(int d, int C);
 }  // namespace mfma
 }  // namespace osr

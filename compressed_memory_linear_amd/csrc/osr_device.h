@@ -35,6 +35,13 @@ struct Params {
     int y_bf16;        // 1: y is bf16, 0: y is fp32
     int schedule;      // matrix-core chunk schedule: 0 automatic, 1 split, 2 fused
     int chain_pairs;   // state passing: 0 pairs where they pay, 1 one wave per slot block
+    int chain_wgs;     // state passing: 0 split over workgroups where it applies, 1 one workgroup
+    // State passing with P > 1 workgroups per (b,h) (each takes one sub-block
+    // of every chunk): per (b,h), chunk parity and workgroup, that
+    // workgroup's part of the chunk-end update and its gate products; and one
+    // progress counter per workgroup (128 bytes apart), zeroed before the launch.
+    float* xbuf;
+    int* xflags;
 };
 
 // ---------------------------------------------------------------- bf16 ----

@@ -18,7 +18,7 @@ int launch_valu(bool decode, int m, int d, const Params& p, bool in_bf16, hipStr
 // workspace it needs, and the launch of the inter-chunk state-passing kernel
 // followed by the read-out kernel (split schedule), or the fused kernel.
 bool mfma_supported(int m, int d, int C);
-size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1, int schedule);
+size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1, int schedule, int chain_wgs);
 // The split schedule's per-chunk workspace whatever the schedule choice, and
 // the state-passing kernel alone (the backward takes its chunk-start states
 // from it, through Params::raw).

@@ -18,6 +18,12 @@ template <int M>
 int launch_m(int d, bool split, const Params& p, hipStream_t st);
 template <int M>
 int launch_chain_m(int d, const Params& p, hipStream_t st);
+template <int M>
+int chain_subblock_m(int d, int C);
+extern template int chain_subblock_m<16>(int, int);
+extern template int chain_subblock_m<32>(int, int);
+extern template int chain_subblock_m<64>(int, int);
+extern template int chain_subblock_m<128>(int, int);
 extern template int launch_m<16>(int, bool, const Params&, hipStream_t);
 extern template int launch_m<32>(int, bool, const Params&, hipStream_t);
 extern template int launch_m<64>(int, bool, const Params&, hipStream_t);
@@ -35,6 +41,42 @@ bool use_split(int B, int H, int d, int schedule, bool lin1) {
     const int64_t bh = static_cast<int64_t>(B) * H;
     return bh < 256 || (d <= 64 && bh < 512);
 }
+
+int chain_subblock(int m, int d, int C) {
+    switch (m) {
+        case 16: return chain_subblock_m<16>(d, C);
+        case 32: return chain_subblock_m<32>(d, C);
+        case 64: return chain_subblock_m<64>(d, C);
+        case 128: return chain_subblock_m<128>(d, C);
+        default: return 0;
+    }
+}
+
+// Workgroups per sequence of the state-passing kernel: P = C / C0 when the
+// chunk is 2 or 4 of its sub-blocks and B*H*P workgroups (one per compute
+// unit: its LDS use allows no second) fit the 256 compute units, so that
+// every workgroup of a sequence is resident while it waits for the others.
+int chain_split_p(int B, int H, int m, int d, int C, int chain_wgs) {
+    if (chain_wgs != 0) return 1;
+    const int c0 = chain_subblock(m, d, C);
+    if (c0 <= 0 || C % c0 != 0) return 1;
+    const int P = C / c0;
+    if (P != 2 && P != 4) return 1;
+    return static_cast<int64_t>(B) * H * P <= 256 ? P : 1;
+}
+
+size_t chain_xchg_bytes(int B, int H, int m, int d, int P) {
+    if (P <= 1) return 0;
+    const size_t per = static_cast<size_t>(m / 16) * (d / 16) * 64 * 4 + static_cast<size_t>(m / 16) * 64;
+    return static_cast<size_t>(B) * H * (2 * P * per * sizeof(float) + static_cast<size_t>(P) * (m / 16) * 32 * sizeof(int));
+}
+
+int device_compute_units() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
 }  // namespace mfma
 
 bool mfma_supported(int m, int d, int C) {
@@ -50,9 +92,10 @@ size_t mfma_chain_workspace_bytes(int B, int H, int T, int m, int d, int C, bool
 }
 
 // The first linearisation runs on the split schedule only.
-size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1, int schedule) {
+size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1, int schedule, int chain_wgs) {
     if (!mfma::use_split(B, H, d, schedule, lin1)) return 0;
-    return mfma_chain_workspace_bytes(B, H, T, m, d, C, lin1);
+    return mfma_chain_workspace_bytes(B, H, T, m, d, C, lin1) +
+           mfma::chain_xchg_bytes(B, H, m, d, mfma::chain_split_p(B, H, m, d, C, chain_wgs));
 }
 
 int launch_mfma_chain_only(int m, int d, const Params& p, hipStream_t st) {
@@ -65,8 +108,19 @@ int launch_mfma_chain_only(int m, int d, const Params& p, hipStream_t st) {
     }
 }
 
-int launch_mfma_chunked(int m, int d, const Params& p, hipStream_t st) {
-    const bool split = mfma::use_split(p.B, p.H, d, p.schedule, p.lin1 != 0);
+int launch_mfma_chunked(int m, int d, const Params& p0, hipStream_t st) {
+    const bool split = mfma::use_split(p0.B, p0.H, d, p0.schedule, p0.lin1 != 0);
+    Params p = p0;
+    if (split) {
+        // the state passing split over workgroups: hand-off buffers after the per-chunk arrays
+        const int P = mfma::chain_split_p(p.B, p.H, m, d, p.chunk, p.chain_wgs);
+        if (P > 1 && static_cast<int64_t>(p.B) * p.H * P <= mfma::device_compute_units()) {
+            const size_t off = mfma_chain_workspace_bytes(p.B, p.H, p.T, m, d, p.chunk, p.lin1 != 0);
+            const size_t per = static_cast<size_t>(m / 16) * (d / 16) * 64 * 4 + static_cast<size_t>(m / 16) * 64;
+            p.xbuf = reinterpret_cast<float*>(reinterpret_cast<char*>(p.zbuf) + off);
+            p.xflags = reinterpret_cast<int*>(p.xbuf + static_cast<size_t>(p.B) * p.H * 2 * P * per);
+        }
+    }
     switch (m) {
         case 16: return mfma::launch_m<16>(d, split, p, st);
         case 32: return mfma::launch_m<32>(d, split, p, st);

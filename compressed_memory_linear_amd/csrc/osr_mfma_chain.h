@@ -30,6 +30,21 @@
 // LDS once per chunk and the H tiles are shared through LDS in both the
 // token-major (for c) and the column-major (for the update) layout.
 //
+// Split over P workgroups (P > 1; few sequences, so the chip is otherwise
+// idle).  Inside a chunk the gates, h_t and the update of a group of tokens
+// depend only on Z and that group's inputs, and the update is linear in the
+// state: with U_p = sum over sub-block p of diag(kappa_t (.) prod_{l > t,
+// l in p} g_l) 1 h_t^T and t_p the product of g over sub-block p,
+//   R_end = diag(t_0 ... t_{P-1}) Z + sum_p diag(t_{p+1} ... t_{P-1}) U_p.
+// Workgroup p takes sub-block p of every chunk: it forms H, c, the gates, the
+// workspace entries, U_p and t_p for its tokens, publishes (U_p, t_p), reads
+// the other workgroups' and forms R_end; every workgroup holds the same Z.
+// The hand-off goes through device memory with agent-scope (coherent across
+// XCDs) accesses: the data, then a completion counter once the data stores
+// have retired; readers wait for the counter (a bounded wait), then read.
+// Consecutive chunks use alternate buffers; a workgroup reuses a buffer only
+// after every workgroup has read it (it has seen their next counters).
+//
 // 16x16x32 operands built from accumulator tiles use a permuted k order: two
 // D-layout tiles t0, t1 (lane (lg, lc) holds rows 4lg..4lg+3 of column lc)
 // concatenated form a B operand whose k index 8lg + j stands for row
@@ -144,10 +159,32 @@ __device__ __forceinline__ float row_inv_norm(const f32x4 (&acc)[DB]) {
 // and the end state (Params::raw) and c, beta, |h|^2 of every token
 // (Params::raw_c, raw_b, raw_hh); its own instantiation, so the forward carries
 // none of it.
-template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR, bool ENC, bool LIN1 = false, bool RAW = false>
+// Floats of one workgroup's hand-off: U_p as [wave][column tile][lane] f32x4,
+// then t_p as [wave][lane].
+template <int M, int D>
+constexpr int64_t xchg_floats() {
+    return static_cast<int64_t>(M / 16) * (D / 16) * 64 * 4 + (M / 16) * 64;
+}
+constexpr int XFLAG_STRIDE = 32;  // ints between progress counters (128 bytes)
+constexpr int XSPIN = 1 << 22;    // polls before a wait gives up (never reached when all run)
+
+// Hand-off accesses with the device-coherence bit (sc1): they bypass the
+// non-coherent caches (the per-XCD L2 included), so readers on any XCD see
+// the data once the writer's stores have retired; no write-back or
+// invalidation of the rest of the cache is needed.  Progress counters: one
+// per (sequence, workgroup, wave), XFLAG_STRIDE ints apart.  Buffer instructions keep
+// them ordinary loads and stores for the compiler (issued back to back).
+constexpr int XCPOL_SC1 = 16;  // cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(float* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
+
+template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR, bool ENC, bool LIN1 = false, bool RAW = false,
+          int P = 1>
 __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Params p) {
     using G = ChainCfg<M, D, C0, PAIR>;
     static_assert(!PAIR || ONE, "the pair split covers one sub-block per chunk");
+    static_assert(P == 1 || (!ONE && !PAIR && !RAW), "the workgroup split takes one sub-block per workgroup");
     constexpr int DB = G::DB, TBW = G::TBW;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
     short* stage = reinterpret_cast<short*>(smem + G::O_KS);
@@ -159,14 +196,24 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
     short* htl = reinterpret_cast<short*>(smem + G::O_TL);
     float* hp = reinterpret_cast<float*>(smem + G::O_HP);
 
-    const int bh = blockIdx.x, b = bh / p.H, hd = bh % p.H;
+    // P > 1: the P workgroups of a sequence are 8 block indices apart, so the
+    // round-robin dispatch puts them on one XCD (correctness does not depend
+    // on it); blocks past the last sequence exit at once.
+    int bh = blockIdx.x, pidx = 0;
+    if constexpr (P > 1) {
+        pidx = (blockIdx.x / 8) % P;
+        bh = blockIdx.x % 8 + 8 * (blockIdx.x / (8 * P));
+        if (bh >= p.B * p.H) return;
+    }
+    const int b = bh / p.H, hd = bh % p.H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int lg = lane >> 4, lc = lane & 15;
     const int grp = PAIR ? w / G::NWS : 0;  // token half of this wave
     const int wv = w % G::NWS;              // slot block of this wave
     const int slot = 16 * wv + lc;
     const int tbg = grp * TBW;              // first token tile of the group
-    const int C = p.chunk, NS = p.T / C0, SPC = C / C0;
+    const int C = p.chunk, NS = P > 1 ? p.T / C : p.T / C0, SPC = C / C0;
+    bool xbroken = false;  // a hand-off wait gave up: stop waiting (the results are then wrong)
     // H = K Z - V assignment of this wave (inside its group).
     const int g1_tb0 = tbg + wv % G::TG, g1_grp = wv / G::TG;
     const bool g1_active = g1_grp < G::WSE;
@@ -182,7 +229,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         for (int j = 0; j < DB; ++j) acc[j] = *reinterpret_cast<const f32x4*>(src + 16 * j);
     }
     const PreOff<G> poff = prefetch_offsets<G>(p);
-    prefetch<G, false>(nxt, poff, p, b, hd, 0);
+    prefetch<G, false>(nxt, poff, p, b, hd, pidx * C0);
     commit<G, false>(nxt, stage, p.gamma_per_slot != 0);
     // Drain the loads above before the loop.  Left pending, they make the
     // compiler's wait analysis treat the loop-carried state tiles as possibly
@@ -191,9 +238,10 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
     __builtin_amdgcn_s_waitcnt(0);
 
     for (int s = 0; s < NS; ++s) {
-        const int t0 = s * C0;
-        const bool chunk_start = ONE || s % SPC == 0;
-        const int chunk = ONE ? s : s / SPC;
+        // P > 1: iteration s is chunk s, this workgroup's sub-block pidx of it
+        const int t0 = P > 1 ? s * C + pidx * C0 : s * C0;
+        const bool chunk_start = ONE || P > 1 || s % SPC == 0;
+        const int chunk = ONE || P > 1 ? s : s / SPC;
         const bool has_next = s + 1 < NS;
         const short* st = stage + (s & 1) * G::STAGE;
         const short* ks = st + G::SO_K;
@@ -202,7 +250,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         const float* mus = reinterpret_cast<const float*>(st + G::SO_MU);
         // this sub-block's part of the chunk's workspace (read-out inputs)
         const Workspace ws = workspace_at<M, D>(p, bh, chunk);
-        const int tc0 = ONE ? 0 : (s % SPC) * C0;
+        const int tc0 = ONE ? 0 : P > 1 ? pidx * C0 : (s % SPC) * C0;
 
         if (chunk_start) {
             if (RAW && grp == 0) {
@@ -221,7 +269,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // Loads of the next sub-block, issued before this sub-block's
         // workspace stores (the memory counter retires in order).
         // Unconditional: the last sub-block re-reads its own tile.
-        prefetch<G, false>(nxt, poff, p, b, hd, has_next ? t0 + C0 : t0);
+        prefetch<G, false>(nxt, poff, p, b, hd, has_next ? t0 + (P > 1 ? C : C0) : t0);
         if (chunk_start) {
             // Z^T to LDS (read by every wave's H = K Z); the split tiles stay
             // in registers.  No wave reads Z^T between the last sub-block's
@@ -340,7 +388,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // (slots 16wv + 4lg .. +3 of column 16j + lc), one 16-byte piece per
         // lane and tile.
         if constexpr (WRITE_Z) {
-            if (chunk_start && grp == 0) {
+            if (chunk_start && grp == 0 && pidx == 0) {
 #pragma unroll
                 for (int j = 0; j < DB; ++j) {
                     const s16x4 th = tr16(zfh[j], eye), tl = tr16(zfl[j], eye);
@@ -506,19 +554,21 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             if constexpr (LIN1) {
-                // Z: the running state itself when a chunk is one sub-block,
-                // else its split (hi + lo) kept from the chunk start
+                // Z: the running state itself when a chunk is one sub-block
+                // (or with the workgroup split, where acc holds Z), else its
+                // split (hi + lo) kept from the chunk start
                 f32x4 zf = acc[db];
-                if constexpr (!ONE) {
+                if constexpr (!ONE && P == 1) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) zf[r] = bf16_bits_to_f32(static_cast<uint16_t>(zfh[db][r])) +
                                                       bf16_bits_to_f32(static_cast<uint16_t>(zfl[db][r]));
                 }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) u[db][r] = PAIR ? zf[r] * ez : fmaf(acc[db][r], aend, zf[r] * ez);
+                for (int r = 0; r < 4; ++r)
+                    u[db][r] = PAIR || P > 1 ? zf[r] * ez : fmaf(acc[db][r], aend, zf[r] * ez);
             } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) u[db][r] = PAIR ? 0.f : acc[db][r] * aend;
+                for (int r = 0; r < 4; ++r) u[db][r] = PAIR || P > 1 ? 0.f : acc[db][r] * aend;
             }
         }
         if constexpr (G::K32_C) {
@@ -576,6 +626,79 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[db][r] = fmaf(acc[db][r], az, fmaf(u0[r], t1h, u1[r]));
             }
+        } else if constexpr (P > 1) {
+            // Publish (U_p, t_p), then R_end = diag(prod_q t_q) Z +
+            // sum_q diag(prod_{q' > q} t_q') U_q, summed in q order by every
+            // workgroup (so all hold the same bits).
+            const int64_t xs = xchg_floats<M, D>();
+            float* xb = p.xbuf + (static_cast<int64_t>(bh) * 2 + (s & 1)) * P * xs;
+            const __amdgpu_buffer_rsrc_t xr = xrsrc(xb, static_cast<uint32_t>(P * xs * sizeof(float)));
+            {
+                const uint32_t mine = static_cast<uint32_t>(pidx * xs) * 4;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, u[db]), xr,
+                                                           mine + ((w * DB + db) * 64 + lane) * 16, 0, XCPOL_SC1);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(aend), xr,
+                                                      mine + ((M / 16) * DB * 64 * 4 + w * 64 + lane) * 4, 0,
+                                                      XCPOL_SC1);
+            }
+            // Each wave hands off its own slot rows: they are all that the
+            // same wave of the other workgroups reads, so the counters are
+            // per (workgroup, wave) and no workgroup barrier is needed.
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's hand-off stores have retired
+            int* myflag = p.xflags + ((bh * P + pidx) * G::NWS + w) * XFLAG_STRIDE;
+            if (lane == 0) __hip_atomic_store(myflag, s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                if (q == pidx || xbroken) continue;
+                const int* f = p.xflags + ((bh * P + q) * G::NWS + w) * XFLAG_STRIDE;
+                int n = 0;
+                while (__hip_atomic_load(const_cast<int*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= s) {
+                    if (++n >= XSPIN) {
+                        xbroken = true;
+                        break;
+                    }
+                }
+            }
+            asm volatile("" ::: "memory");  // the reads below stay after the waits
+            float tq[P];
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+                tq[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    xr, static_cast<uint32_t>(q * xs) * 4 + ((M / 16) * DB * 64 * 4 + w * 64 + lane) * 4, 0,
+                    XCPOL_SC1));
+            float sq[P], t_all = 1.f;
+#pragma unroll
+            for (int q = P - 1; q >= 0; --q) {
+                sq[q] = t_all;
+                t_all *= tq[q];
+            }
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[db][e] *= t_all;
+            // the parts in two batches of q (at most two parts of loads in
+            // flight in registers), each added in q order
+            constexpr int QB = P < 2 ? P : 2;
+#pragma unroll
+            for (int q0 = 0; q0 < P; q0 += QB) {
+                f32x4 uq[QB][DB];
+#pragma unroll
+                for (int qi = 0; qi < QB; ++qi)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        uq[qi][db] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       xr, static_cast<uint32_t>((q0 + qi) * xs) * 4 + ((w * DB + db) * 64 + lane) * 16,
+                                       0, XCPOL_SC1));
+#pragma unroll
+                for (int qi = 0; qi < QB; ++qi)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[db][e] = fmaf(sq[q0 + qi], uq[qi][db][e], acc[db][e]);
+            }
         } else {
 #pragma unroll
             for (int db = 0; db < DB; ++db) acc[db] = u[db];
@@ -589,7 +712,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
     }
     const float inv = row_inv_norm<DB>(acc);
-    if (grp == 0 && p.state_out) {
+    if (grp == 0 && pidx == 0 && p.state_out) {
         float* dst = p.state_out + static_cast<int64_t>(bh) * M * D + static_cast<int64_t>(slot) * D + 4 * lg;
 #pragma unroll
         for (int j = 0; j < DB; ++j) {

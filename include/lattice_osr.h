@@ -106,6 +106,14 @@ extern "C" {
                                     one sub-block of >= 32 tokens); one wave elsewhere */
 #define LATTICE_OSR_PAIRS_OFF 1  /* always one wave per block of 16 slots */
 
+/* Workgroups per (b,h) sequence in the state-passing kernel (split schedule). */
+#define LATTICE_OSR_WGS_AUTO 0 /* where a chunk is 2 or 4 of that kernel's sub-blocks and at
+                                  most one workgroup per compute unit results (few sequences:
+                                  B*H*P <= 256 on the device's compute units), one workgroup per
+                                  sub-block of the chunk, exchanging their parts of the chunk-end
+                                  state through the workspace; else one workgroup */
+#define LATTICE_OSR_WGS_ONE 1  /* always one workgroup per sequence */
+
 /* Status codes. */
 #define LATTICE_OSR_OK 0
 #define LATTICE_OSR_ERR_NULL (-1)        /* a required pointer is NULL              */
@@ -129,6 +137,7 @@ typedef struct {
     int32_t linearisation;  /* LATTICE_OSR_LIN2 (0) or LATTICE_OSR_LIN1 (1)      */
     int32_t schedule;       /* LATTICE_OSR_SCHED_AUTO (0), _SPLIT (1), _FUSED (2) */
     int32_t chain_pairs;    /* LATTICE_OSR_PAIRS_AUTO (0) or _OFF (1)            */
+    int32_t chain_wgs;      /* LATTICE_OSR_WGS_AUTO (0) or _ONE (1)              */
 } lattice_osr_desc;
 
 /*

@@ -78,6 +78,7 @@ def test_null_pointers(fn):
     ("linearisation", 2, osr.ERR_UNSUPPORTED), ("linearisation", -1, osr.ERR_UNSUPPORTED),
     ("schedule", 3, osr.ERR_UNSUPPORTED), ("schedule", -1, osr.ERR_UNSUPPORTED),
     ("chain_pairs", 2, osr.ERR_UNSUPPORTED), ("chain_pairs", -1, osr.ERR_UNSUPPORTED),
+    ("chain_wgs", 2, osr.ERR_UNSUPPORTED), ("chain_wgs", -1, osr.ERR_UNSUPPORTED),
 ])
 def test_bad_descriptor(field, value, status):
     d = osr.make_desc(2, 8, 2, 32, 32)
@@ -130,6 +131,27 @@ def test_schedule_field_sets_the_workspace():
     # the pair switch changes no buffer
     nopair = osr.make_desc(B, T, H, m, d, chain_pairs=osr.PAIRS_OFF)
     assert osr.lattice_osr_workspace_bytes(nopair, C) == osr.lattice_osr_workspace_bytes(auto, C)
+
+
+def test_workgroup_split_workspace():
+    """The state passing split over P workgroups per sequence (a chunk of P
+    sub-blocks, few sequences) adds its hand-off buffers to the workspace: per
+    (b,h), two chunk parities x P parts of (m d + 4 m) floats, and P m/16
+    counters of 128 bytes.  chain_wgs ONE, or too many sequences, adds none."""
+    m = d = C = 128
+    T = 1024
+    per_chunk = (m * d + 2 * m * C + d * C) * 4
+    for BH, P in ((16, 4), (64, 4), (65, 1), (200, 1)):
+        auto = osr.make_desc(1, T, BH, m, d)
+        one = osr.make_desc(1, T, BH, m, d, chain_wgs=osr.WGS_ONE)
+        base = BH * (T // C) * per_chunk
+        xchg = BH * (2 * P * (m * d + 4 * m) * 4 + P * (m // 16) * 128) if P > 1 else 0
+        assert osr.lattice_osr_workspace_bytes(auto, C) == base + xchg, (BH, P)
+        assert osr.lattice_osr_workspace_bytes(one, C) == base
+    # a chunk of two sub-blocks (m = d = 128, C = 64: 32-token sub-blocks)
+    two = osr.make_desc(1, 256, 16, 128, 128)
+    assert osr.lattice_osr_workspace_bytes(two, 64) == 16 * 4 * (m * d + 2 * m * 64 + d * 64) * 4 + \
+        16 * (2 * 2 * (m * d + 4 * m) * 4 + 2 * 8 * 128)
 
 
 def test_library_reads_no_environment():
