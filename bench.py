@@ -138,7 +138,10 @@ class Case:
             self.grads = {"d" + n: torch.empty(t0[n].shape, dtype=torch.float32, device="cuda")
                           for n in ("q", "k", "v", "gamma", "mu")}
             self.grads["dstate_in"] = torch.empty_like(t0["state"])
-        if entry == "chunked":
+        if entry == "chunked_gated":
+            g = torch.Generator(device="cuda").manual_seed(9)
+            self.gate = (torch.randn(self.y.shape, generator=g, device="cuda") * 2).to(self.sets[0]["q"].dtype)
+        if entry in ("chunked", "chunked_gated"):
             desc = osr.make_desc(inp.B, inp.T, inp.H, inp.m, inp.d, 1,
                                  osr.BF16 if inp.in_dtype == "bf16" else osr.F32, osr.F32, mode, linearisation)
             need = osr.lattice_osr_workspace_bytes(desc, chunk)
@@ -154,6 +157,11 @@ class Case:
             osr.lattice_osr_fwd_chunked(*args, self.chunk, mode=self.mode, y_dtype=self.y_dtype,
                                         state_out=self.state_out, y=self.y, workspace=self.ws,
                                         linearisation=self.lin)
+        elif self.entry == "chunked_gated":
+            osr.lattice_osr_fwd_chunked_gated(t["q"], t["k"], t["v"], t["gamma"], t["mu"], self.gate, t["state"],
+                                              self.chunk, mode=self.mode, y_dtype=self.y_dtype,
+                                              state_out=self.state_out, y=self.y, workspace=self.ws,
+                                              linearisation=self.lin)
         elif self.entry == "backward":
             osr.lattice_osr_bwd_chunked(*args, self.dy, self.dso, self.chunk, mode=self.mode, grads=self.grads,
                                         workspace=self.ws)
@@ -368,6 +376,8 @@ def main() -> int:
         for name, entry, chunk, steps, mode, lin in ((SMALL, "chunked", 64, 20, 0, 0),
                                                      ("decode_s256h32_m128d128", "decode", 1, 50, 0, 0),
                                                      ("chunked_b8h16_t4096_m64d128_c64", "chunked", 64, 5, 0, 0),
+                                                     ("chunked_b8h16_t4096_m64d128_c64", "chunked_gated", 64, 5, 0,
+                                                      0),
                                                      (SMALL, "recurrent", 1, 2, 0, 0),
                                                      (SMALL, "chunked", 4, 3, 0, 0),
                                                      (SMALL, "chunked", 64, 10, 2, 0),
@@ -378,6 +388,8 @@ def main() -> int:
                      mode=mode, linearisation=lin)
             t_ms = time_case(c, steps, 1)
             ab = algorithmic_bytes_bwd(c.w) if entry == "backward" else algorithmic_bytes(c.w)
+            if entry == "chunked_gated":  # the gate is read once more (in the inputs' dtype)
+                ab += c.head_tokens * c.w["d"] * (2 if c.w["in_dtype"] == "bf16" else 4)
             sec.append({"workload": name, "entry": entry, "chunk": chunk,
                         "objective": {0: "decoding", 1: "similarity", 2: "encoding"}[mode],
                         "linearisation": "recurrence_linear1" if lin else "recurrence_linear2", "ms_per_step": t_ms,

@@ -129,6 +129,7 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     p.chain_wgs = d->chain_wgs;
     p.xbuf = nullptr;
     p.xflags = nullptr;
+    p.gate = nullptr;
     return p;
 }
 
@@ -250,6 +251,35 @@ int lattice_osr_fwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
     hipStream_t st = static_cast<hipStream_t>(hip_stream);
     if (chunk_path(desc, chunk_size) == Path::Mfma) return osr::launch_mfma_chunked(desc->m, desc->d, p, st);
     return osr::launch_valu(false, desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, st);
+}
+
+int lattice_osr_fwd_chunked_gated(const lattice_osr_desc* desc, int32_t chunk_size, const void* q,
+                                  const void* k, const void* v, const void* gamma, const void* mu,
+                                  const void* gate, const float* state_in, float* state_out, void* y,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (chunk_size <= 0 || desc->T % chunk_size != 0) return LATTICE_OSR_ERR_SHAPE;
+    if (!pow2_chunk(chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    const size_t need = workspace_needed(desc, chunk_size);
+    rc = check_buffers(desc, q, k, v, gamma, mu, state_in, state_out, y, workspace, workspace_bytes, need);
+    if (rc) return rc;
+    // the gate is one more input: [B,T,H,d] in_dtype, 16-byte aligned, overlapping no output
+    if (!gate) return LATTICE_OSR_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(gate) % 16 != 0) return LATTICE_OSR_ERR_ALIGN;
+    const size_t ein = desc->in_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const size_t ey = desc->y_dtype == LATTICE_OSR_BF16 ? 2 : 4;
+    const size_t tok = static_cast<size_t>(desc->B) * desc->T * desc->H;
+    const size_t st = static_cast<size_t>(desc->B) * desc->H * desc->m * desc->d * sizeof(float);
+    const Range rg = range_of(gate, tok * desc->d * ein);
+    if (overlap(rg, range_of(y, tok * desc->d * ey)) || overlap(rg, range_of(state_out, st)) ||
+        overlap(rg, range_of(workspace, need)))
+        return LATTICE_OSR_ERR_ALIAS;
+    osr::Params p = make_params(desc, chunk_size, q, k, v, gamma, mu, state_in, state_out, y, workspace);
+    p.gate = gate;
+    hipStream_t hs = static_cast<hipStream_t>(hip_stream);
+    if (chunk_path(desc, chunk_size) == Path::Mfma) return osr::launch_mfma_chunked(desc->m, desc->d, p, hs);
+    return osr::launch_valu(false, desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, hs);
 }
 
 int lattice_osr_fwd_recurrent(const lattice_osr_desc* desc, const void* q, const void* k,

@@ -42,6 +42,9 @@ struct Params {
     // progress counter per workgroup (128 bytes apart), zeroed before the launch.
     float* xbuf;
     int* xflags;
+    // GeLU post-gate of the layer fused into the y store: y_t <- y_t * GeLU(gate_t)
+    // with gate [B,T,H,d] in the inputs' dtype, or null (plain y).
+    const void* gate;
 };
 
 // ---------------------------------------------------------------- bf16 ----
@@ -82,6 +85,12 @@ __device__ __forceinline__ float4 ld4<uint16_t>(const uint16_t* p, int64_t i) {
     return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
                        __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
 }
+
+// GeLU(x) = x Phi(x), the exact form (Phi through erfc, which keeps its
+// relative accuracy in the negative tail where 1 + erf cancels): the layer's
+// post-gate on the recurrence's output (section "Experiments", the Lattice
+// block).
+__device__ __forceinline__ float gelu(float x) { return x * (0.5f * erfcf(-x * 0.70710678118654752f)); }
 
 // Store four consecutive y values as fp32 or bf16.
 __device__ __forceinline__ void st_y4(void* y, int64_t i, float4 val, int y_bf16) {

@@ -92,8 +92,6 @@ __device__ __forceinline__ void store1(float* p, int64_t i, float x) { p[i] = x;
 __device__ __forceinline__ void store1(uint16_t* p, int64_t i, float x) { p[i] = f32_to_bf16_bits(x); }
 
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
-// Phi(x) through erfc keeps its relative accuracy where 1 + erf(x / sqrt 2) cancels.
-__device__ __forceinline__ float gelu(float x) { return x * (0.5f * erfcf(-x * 0.70710678118654752f)); }
 
 // Work unit u of a token tile: u < 2 nc is a group of 8 q (u < nc) or k
 // channels; the rest are groups of up to 8 gamma logits.

@@ -474,6 +474,18 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
     short* kah = reinterpret_cast<short*>(smem + G::O_KH);
     short* kal = reinterpret_cast<short*>(smem + G::O_KL);
 
+    // The post-gate of this sub-block's y (if fused), loaded here so the
+    // loads land while the products below run.
+    uint16_t gq[TB][4] = {};
+    if (WITH_Y && p.gate) {
+        const uint16_t* gp = static_cast<const uint16_t*>(p.gate);
+        const int64_t g0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gq[tb][r] = gp[(g0 + static_cast<int64_t>(16 * tb + 4 * lg + r) * p.H) * D + dcol];
+    }
+
     // ---- H = K Z - V for this wave's columns; |h|^2 partials; H to LDS ----
     f32x4 accH[TB];
     s16x4 hfh[TB], hfl[TB];
@@ -662,6 +674,10 @@ __device__ __forceinline__ void osr_subblock(const Params& p, char* smem, f32x4 
                 s16x4 ph, pl;
                 split4(pt, ph, pl);
                 y = mma3(ph, pl, hfh[jb], hfl[jb], y);
+            }
+            if (p.gate) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] *= gelu(bf16u(gq[tb][r]));
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r)

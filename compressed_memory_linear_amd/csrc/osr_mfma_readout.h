@@ -192,6 +192,18 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
             if (last_in_chunk) rd_load_z<M, D>(zn, ws1.z);
         }
 
+        // The post-gate of this sub-block's y (if fused), loaded here so the
+        // loads land while the products below run.
+        uint16_t gq[TB][4] = {};
+        if (p.gate) {
+            const uint16_t* gp = static_cast<const uint16_t*>(p.gate);
+            const int64_t g0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gq[tb][r] = gp[(g0 + static_cast<int64_t>(16 * tb + 4 * lg + r) * p.H) * D + dcol];
+        }
+
         // ---- gate products of this wave's slot tiles ------------------------
 #pragma unroll
         for (int mi = 0; mi < G::MPW; ++mi) {
@@ -364,6 +376,10 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
             // 4-byte stores: 16 lanes cover 64 contiguous bytes of a token row
             // (a transposed tile, 16 bytes per lane across 16 rows, issues four
             // times the memory requests)
+            if (p.gate) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] *= gelu(bf16u(gq[tb][r]));
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 st_y1(p.y, (row0 + static_cast<int64_t>(16 * tb + 4 * lg + r) * p.H) * D + dcol, y[r], p.y_bf16);

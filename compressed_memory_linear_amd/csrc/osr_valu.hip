@@ -96,7 +96,14 @@ __global__ __launch_bounds__(NT) void osr_decode_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < L::RPT; ++i) z[i] = s[i];
     const float4 y = osr_token<L, D>(z, s, in, p.mode, 0, red[0], red[1], lane, wave, cg);
-    if (rg == 0) st_y4(p.y, static_cast<int64_t>(bh) * D + cg * 4, y, p.y_bf16);
+    if (rg == 0) {
+        float4 yg = y;
+        if (p.gate) {
+            const float4 g = ld4<TIn>(static_cast<const TIn*>(p.gate), static_cast<int64_t>(bh) * D + cg * 4);
+            yg = make_float4(y.x * gelu(g.x), y.y * gelu(g.y), y.z * gelu(g.z), y.w * gelu(g.w));
+        }
+        st_y4(p.y, static_cast<int64_t>(bh) * D + cg * 4, yg, p.y_bf16);
+    }
 
     project_rows<L>(s);
     float* sout = p.state_out + static_cast<int64_t>(bh) * M * D;
@@ -211,6 +218,10 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
                 float4 acc = *reinterpret_cast<const float4*>(rb + (uu * L::NW) * W + c4 * 4);
 #pragma unroll
                 for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (uu * L::NW + w) * W + c4 * 4);
+                if (p.gate) {
+                    const float4 g = ld4<TIn>(static_cast<const TIn*>(p.gate), bth_of(t0 + uu) * D + c4 * 4);
+                    acc = make_float4(acc.x * gelu(g.x), acc.y * gelu(g.y), acc.z * gelu(g.z), acc.w * gelu(g.w));
+                }
                 st_y4(p.y, bth_of(t0 + uu) * D + c4 * 4, acc, p.y_bf16);
             }
             ++ybatch;

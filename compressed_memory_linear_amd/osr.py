@@ -30,7 +30,7 @@ ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_
 EXPORTED = ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step",
             "lattice_osr_workspace_bytes", "lattice_osr_status_string", "lattice_osr_abi_version",
             "lattice_osr_bwd_chunked", "lattice_osr_bwd_workspace_bytes", "lattice_osr_glue_pre",
-            "lattice_osr_glue_post")
+            "lattice_osr_glue_post", "lattice_osr_fwd_chunked_gated")
 
 
 class lattice_osr_desc(ctypes.Structure):
@@ -59,6 +59,8 @@ def load_library():
         vp, dp = ctypes.c_void_p, ctypes.POINTER(lattice_osr_desc)
         fwd = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         lib.lattice_osr_fwd_chunked.argtypes = [dp, ctypes.c_int32] + fwd[1:]
+        lib.lattice_osr_fwd_chunked_gated.argtypes = [dp, ctypes.c_int32] + [vp] * 6 + fwd[6:]
+        lib.lattice_osr_fwd_chunked_gated.restype = ctypes.c_int
         lib.lattice_osr_fwd_recurrent.argtypes = fwd
         lib.lattice_osr_decode_step.argtypes = fwd
         for f in ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step"):
@@ -221,6 +223,30 @@ def lattice_osr_fwd_chunked(q, k, v, gamma, mu, state_in, chunk_size: int, *, mo
                                          _ptr(workspace), wbytes, st.cuda_stream)
     if rc != OK:
         raise OSRError(rc, "lattice_osr_fwd_chunked")
+    return y, state_out
+
+
+def lattice_osr_fwd_chunked_gated(q, k, v, gamma, mu, gate, state_in, chunk_size: int, *, mode: int = MODE_DEC,
+                                  y_dtype=torch.float32, state_out=None, y=None, workspace=None, stream=None,
+                                  linearisation: int = 0, schedule: int = SCHED_AUTO, chain_pairs: int = PAIRS_AUTO,
+                                  chain_wgs: int = WGS_AUTO) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunk-wise OSR forward with the GeLU post-gate fused into the output:
+    y = OSR(...) * GeLU(gate), gate [B,T,H,d] in the inputs' dtype.
+    Returns (y, state_out)."""
+    lib = load_library()
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation, schedule, chain_pairs, chain_wgs)
+    _check_tensor("gate", gate, tuple(v.shape), q.dtype, q.device)
+    _check_outputs(desc, q, state_in, state_out, y, y_dtype)
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
+        need = lattice_osr_workspace_bytes(desc, chunk_size)
+        workspace, wbytes = _workspace(workspace, need, q.device)
+        rc = lib.lattice_osr_fwd_chunked_gated(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
+                                               _ptr(gamma), _ptr(mu), _ptr(gate), _ptr(state_in), _ptr(state_out),
+                                               _ptr(y), _ptr(workspace), wbytes, st.cuda_stream)
+    if rc != OK:
+        raise OSRError(rc, "lattice_osr_fwd_chunked_gated")
     return y, state_out
 
 

@@ -158,6 +158,24 @@ LATTICE_OSR_API int lattice_osr_fwd_chunked(const lattice_osr_desc* desc, int32_
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * Chunk-wise forward with the layer's GeLU post-gate fused into the output
+ * (section "Experiments", paragraph on the Lattice block, where a GeLU
+ * post-gate follows the recurrence): y_t = (S_t q_t) * GeLU(gate_t)
+ * elementwise, GeLU(x) = x Phi(x) in its exact form, in fp32 before y is
+ * rounded to y_dtype.  The same as lattice_osr_fwd_chunked followed by
+ * lattice_osr_glue_post, without writing and reading back the ungated y.
+ *   gate  [B, T, H, d]  in_dtype, 16-byte aligned; an input (it may overlap
+ *                       other inputs, no output: ERR_ALIAS otherwise)
+ * Every other argument, rule and status is that of lattice_osr_fwd_chunked
+ * (the same workspace size).
+ */
+LATTICE_OSR_API int lattice_osr_fwd_chunked_gated(const lattice_osr_desc* desc, int32_t chunk_size,
+                                                  const void* q, const void* k, const void* v,
+                                                  const void* gamma, const void* mu, const void* gate,
+                                                  const float* state_in, float* state_out, void* y,
+                                                  void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
  * Exact recurrent forward: the recurrence of eq. recurrence_detailed applied
  * token by token (chunk size 1), the state held on chip across tokens.
  * Needs no workspace (workspace may be NULL, workspace_bytes 0).

@@ -174,6 +174,26 @@ def test_chunk_size_rules():
         osr.lattice_osr_workspace_bytes(d, 32)
 
 
+def test_gated_forward_rejects_bad_gate():
+    """The gate of the fused post-gate is an input: null, misaligned or
+    overlapping an output is rejected before any HIP call."""
+    lib = osr.load_library()
+    d = osr.make_desc(1, 8, 1, 16, 16, in_dtype=osr.F32)
+    p = _ptrs(d)
+    gate = BASE + 20 * (1 << 32)
+
+    def call(g, ptrs=p):
+        return lib.lattice_osr_fwd_chunked_gated(ctypes.byref(d), 4, *ptrs[:5], g, *ptrs[5:], None, 0, None)
+
+    assert call(None) == osr.ERR_NULL
+    assert call(gate + 4) == osr.ERR_ALIGN
+    assert call(p[7]) == osr.ERR_ALIAS      # the gate is y
+    assert call(p[6]) == osr.ERR_ALIAS      # the gate is state_out
+    bad = list(p)
+    bad[0] = None
+    assert call(gate, bad) == osr.ERR_NULL  # the other rules are the forward's
+
+
 def test_decode_requires_single_token():
     d = osr.make_desc(4, 2, 2, 32, 32)
     assert _call("lattice_osr_decode_step", d, _ptrs(d)) == osr.ERR_SHAPE

@@ -111,3 +111,14 @@ def test_glue_checks():
         osr.lattice_osr_glue_post(y, torch.zeros(B, T, H, d + 1))
     with pytest.raises(ValueError, match="GPU"):
         osr.lattice_osr_glue_post(y, torch.zeros(B, T, H, d))
+
+
+def test_gated_forward_checks():
+    x = _inputs()
+    args = [x[n] for n in ("q", "k", "v", "gamma", "mu")]
+    with pytest.raises(ValueError, match="gate has shape"):
+        osr.lattice_osr_fwd_chunked_gated(*args, torch.zeros(B, T, H, d + 1, dtype=torch.bfloat16), x["state_in"], 4)
+    with pytest.raises(ValueError, match="gate is"):
+        osr.lattice_osr_fwd_chunked_gated(*args, torch.zeros(B, T, H, d), x["state_in"], 4)
+    with pytest.raises(ValueError, match="GPU"):
+        osr.lattice_osr_fwd_chunked_gated(*args, torch.zeros(B, T, H, d, dtype=torch.bfloat16), x["state_in"], 4)

@@ -210,3 +210,60 @@ def test_layer_pipeline_glue_forward_glue(C):
     gate = g.value("gate")
     ref = oracle.glue_gelu_gate(yg, gate)
     _check(_f64(out), ref, _gate_rel(gate) * np.abs(ref) + 1e-30, "out")
+
+
+# ------------------------------------------- post-gate fused into the forward --
+# lattice_osr_fwd_chunked_gated: y = OSR(...) * GeLU(gate) written once.  With
+# fp32 y it is bit for bit the unfused forward followed by glue_post (the same
+# fp32 product, rounded once); against the oracle (the fp64 forward, then the
+# fp64 gate) the stated forward bar applies to the gated output relative to its
+# RMS: 2e-2 for bf16 inputs, 1e-4 for fp32 (here the gate is N(0, 2^2), and
+# the forward's error relative to y's RMS is 1e-4 - 1e-6 on these paths, far
+# below the bars after the gate's scaling).
+GATED = [("split", synth.BF16, 64, osr.SCHED_SPLIT, 2, 256, 2, 64, 128),
+         ("fused", synth.BF16, 32, osr.SCHED_FUSED, 2, 256, 2, 64, 128),
+         ("split-wgs", synth.BF16, 128, osr.SCHED_AUTO, 1, 512, 4, 128, 128),
+         ("tokenloop-bf16", synth.BF16, 4, osr.SCHED_AUTO, 2, 64, 2, 32, 64),
+         ("tokenloop-f32", synth.F32, 4, osr.SCHED_AUTO, 2, 64, 2, 32, 64)]
+
+
+@pytest.mark.parametrize("case", GATED, ids=[c[0] for c in GATED])
+@pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM])
+def test_forward_with_fused_post_gate(case, mode):
+    name, dt, C, sched, B, T, H, m, d = case
+    print(f"[case] gated forward {name} B{B} T{T} H{H} m{m} d{d} C{C} mode{mode}", flush=True)
+    inp = synth.make_inputs(B, T, H, m, d, seed=3100 + C + m + mode, in_dtype=dt)
+    g32 = np.random.default_rng(31).standard_normal((B, T, H, d)).astype(np.float32) * np.float32(2)
+    gate_store = synth.bf16_round_bits(g32) if dt == synth.BF16 else g32
+    gate_vals = synth.bf16_bits_to_f32(gate_store) if dt == synth.BF16 else g32
+    t = osr.to_device(inp)
+    gate = _dev(gate_store)
+    args = (t["q"], t["k"], t["v"], t["gamma"], t["mu"])
+    yg, Sg = osr.lattice_osr_fwd_chunked_gated(*args, gate, t["state"], C, mode=mode, schedule=sched)
+    y, S = osr.lattice_osr_fwd_chunked(*args, t["state"], C, mode=mode, schedule=sched)
+    post = osr.lattice_osr_glue_post(y, gate)
+    torch.cuda.synchronize()
+    assert torch.equal(yg, post), "fused gate differs from forward + glue_post"
+    assert torch.equal(Sg, S)
+    yr, _ = oracle.osr_forward(*inp.values_f64(), chunk_size=C, mode=mode)
+    ref = oracle.glue_gelu_gate(yr, gate_vals.astype(np.float64))
+    got = _f64(yg)
+    e = float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)))
+    tol = 2e-2 if dt == synth.BF16 else 1e-4
+    print(f"[case]   gated y err/rms {e:.3e} (tol {tol:g})", flush=True)
+    assert e <= tol
+
+
+def test_forward_with_fused_post_gate_bf16_output():
+    """bf16 y: the fused product rounded once to bf16 (round to nearest even)."""
+    print("[case] gated forward, bf16 y, split schedule", flush=True)
+    inp = synth.make_inputs(2, 256, 2, 64, 128, seed=3200, in_dtype=synth.BF16)
+    g = synth.bf16_round_bits(np.random.default_rng(32).standard_normal((2, 256, 2, 128)).astype(np.float32))
+    t = osr.to_device(inp)
+    gate = _dev(g)
+    args = (t["q"], t["k"], t["v"], t["gamma"], t["mu"], gate, t["state"])
+    y16, _ = osr.lattice_osr_fwd_chunked_gated(*args, 64, y_dtype=torch.bfloat16)
+    y32, _ = osr.lattice_osr_fwd_chunked_gated(*args, 64)
+    torch.cuda.synchronize()
+    rounded = synth.bf16_bits_to_f32(synth.bf16_round_bits(y32.cpu().numpy()))
+    assert np.array_equal(rounded, y16.float().cpu().numpy())
