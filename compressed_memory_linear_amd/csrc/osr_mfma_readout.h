@@ -193,15 +193,16 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
         }
 
         // The post-gate of this sub-block's y (if fused), loaded here so the
-        // loads land while the products below run.
-        uint16_t gq[TB][4] = {};
+        // loads land while the products below run: lane (lg, lc) reads 4
+        // consecutive columns of token row lc (8 bytes; 16 lanes cover a 32-byte
+        // row piece), and the identity product brings them into the layout of y.
+        s16x4 gq[TB] = {};
         if (p.gate) {
-            const uint16_t* gp = static_cast<const uint16_t*>(p.gate);
+            const short* gp = static_cast<const short*>(p.gate);
             const int64_t g0 = (static_cast<int64_t>(b) * p.T + t0) * p.H + hd;
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) gq[tb][r] = gp[(g0 + static_cast<int64_t>(16 * tb + 4 * lg + r) * p.H) * D + dcol];
+                gq[tb] = *reinterpret_cast<const s16x4*>(gp + (g0 + static_cast<int64_t>(16 * tb + lc) * p.H) * D + 16 * w + 4 * lg);
         }
 
         // ---- gate products of this wave's slot tiles ------------------------
@@ -377,8 +378,9 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
             // (a transposed tile, 16 bytes per lane across 16 rows, issues four
             // times the memory requests)
             if (p.gate) {
+                const f32x4 gf = tr16f(gq[tb], eye);  // gate of tokens 16tb + 4lg + r, column dcol
 #pragma unroll
-                for (int r = 0; r < 4; ++r) y[r] *= gelu(bf16u(gq[tb][r]));
+                for (int r = 0; r < 4; ++r) y[r] *= gelu(gf[r]);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
