@@ -388,7 +388,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // (slots 16wv + 4lg .. +3 of column 16j + lc), one 16-byte piece per
         // lane and tile.
         if constexpr (WRITE_Z) {
-            if (chunk_start && grp == 0 && pidx == 0) {
+            if (chunk_start && grp == 0 && wv % P == pidx) {  // split: each workgroup stores some slot blocks
 #pragma unroll
                 for (int j = 0; j < DB; ++j) {
                     const s16x4 th = tr16(zfh[j], eye), tl = tr16(zfl[j], eye);
