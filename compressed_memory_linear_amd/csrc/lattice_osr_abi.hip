@@ -4,6 +4,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/lattice_osr.h"
 #include "osr_launch.h"
 
@@ -280,6 +282,61 @@ int lattice_osr_fwd_chunked_gated(const lattice_osr_desc* desc, int32_t chunk_si
     hipStream_t hs = static_cast<hipStream_t>(hip_stream);
     if (chunk_path(desc, chunk_size) == Path::Mfma) return osr::launch_mfma_chunked(desc->m, desc->d, p, hs);
     return osr::launch_valu(false, desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, hs);
+}
+
+}  // extern "C"
+
+// Scratch of lattice_osr_fwd_chunked_noalloc: the workspace of the split
+// schedule in device memory the library owns, one copy per GPU (held until
+// the process ends).  In host code `scratch` names a host-side stand-in, not
+// a device address: its address on a device comes from hipGetSymbolAddress,
+// taken once per device with that device current and kept here.
+namespace {
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;  // LATTICE_OSR_NOALLOC_SCRATCH_BYTES
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+void* scratch_dev[kMaxDevices];
+std::mutex scratch_mu;
+
+// The current device's copy of the scratch array (its address, looked up on
+// the first use on that device).
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LATTICE_OSR_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return LATTICE_OSR_ERR_LAUNCH;
+        scratch_dev[dev] = ptr;
+    }
+    *out = scratch_dev[dev];
+    return LATTICE_OSR_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int lattice_osr_fwd_chunked_noalloc(const lattice_osr_desc* desc, int32_t chunk_size, const void* q,
+                                    const void* k, const void* v, const void* gamma, const void* mu,
+                                    const float* state_in, float* state_out, void* y, void* hip_stream) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (chunk_size <= 0 || desc->T % chunk_size != 0) return LATTICE_OSR_ERR_SHAPE;
+    if (!pow2_chunk(chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    const size_t need = workspace_needed(desc, chunk_size);
+    if (need > kScratchBytes) return LATTICE_OSR_ERR_WORKSPACE;
+    // inputs and outputs as for lattice_osr_fwd_chunked (the scratch overlaps nothing of the caller's)
+    rc = check_buffers(desc, q, k, v, gamma, mu, state_in, state_out, y, nullptr, 0, 0);
+    if (rc) return rc;
+    void* ws = nullptr;
+    if (need > 0) {
+        rc = scratch_address(&ws);
+        if (rc) return rc;
+    }
+    const osr::Params p = make_params(desc, chunk_size, q, k, v, gamma, mu, state_in, state_out, y, ws);
+    hipStream_t st = static_cast<hipStream_t>(hip_stream);
+    if (chunk_path(desc, chunk_size) == Path::Mfma) return osr::launch_mfma_chunked(desc->m, desc->d, p, st);
+    return osr::launch_valu(false, desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, st);
 }
 
 int lattice_osr_fwd_recurrent(const lattice_osr_desc* desc, const void* q, const void* k,

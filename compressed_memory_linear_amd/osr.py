@@ -30,7 +30,8 @@ ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_
 EXPORTED = ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step",
             "lattice_osr_workspace_bytes", "lattice_osr_status_string", "lattice_osr_abi_version",
             "lattice_osr_bwd_chunked", "lattice_osr_bwd_workspace_bytes", "lattice_osr_glue_pre",
-            "lattice_osr_glue_post", "lattice_osr_fwd_chunked_gated")
+            "lattice_osr_glue_post", "lattice_osr_fwd_chunked_gated", "lattice_osr_fwd_chunked_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class lattice_osr_desc(ctypes.Structure):
@@ -61,6 +62,8 @@ def load_library():
         lib.lattice_osr_fwd_chunked.argtypes = [dp, ctypes.c_int32] + fwd[1:]
         lib.lattice_osr_fwd_chunked_gated.argtypes = [dp, ctypes.c_int32] + [vp] * 6 + fwd[6:]
         lib.lattice_osr_fwd_chunked_gated.restype = ctypes.c_int
+        lib.lattice_osr_fwd_chunked_noalloc.argtypes = [dp, ctypes.c_int32] + [vp] * 9
+        lib.lattice_osr_fwd_chunked_noalloc.restype = ctypes.c_int
         lib.lattice_osr_fwd_recurrent.argtypes = fwd
         lib.lattice_osr_decode_step.argtypes = fwd
         for f in ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step"):
@@ -247,6 +250,26 @@ def lattice_osr_fwd_chunked_gated(q, k, v, gamma, mu, gate, state_in, chunk_size
                                                _ptr(y), _ptr(workspace), wbytes, st.cuda_stream)
     if rc != OK:
         raise OSRError(rc, "lattice_osr_fwd_chunked_gated")
+    return y, state_out
+
+
+def lattice_osr_fwd_chunked_noalloc(q, k, v, gamma, mu, state_in, chunk_size: int, *, state_out, y,
+                                    mode: int = MODE_DEC, stream=None, linearisation: int = 0,
+                                    schedule: int = SCHED_AUTO, chain_pairs: int = PAIRS_AUTO,
+                                    chain_wgs: int = WGS_AUTO) -> Tuple[torch.Tensor, torch.Tensor]:
+    """lattice_osr_fwd_chunked without a workspace: the library's per-GPU
+    scratch holds it (at most NOALLOC_SCRATCH_BYTES).  The caller passes the
+    outputs (y with y's dtype, state_out); nothing is allocated.  Calls that
+    overlap on one GPU race on the scratch."""
+    lib = load_library()
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y.dtype, mode, linearisation, schedule, chain_pairs, chain_wgs)
+    _check_outputs(desc, q, state_in, state_out, y, y.dtype)
+    st = _launch_stream(stream)
+    rc = lib.lattice_osr_fwd_chunked_noalloc(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
+                                             _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y),
+                                             st.cuda_stream)
+    if rc != OK:
+        raise OSRError(rc, "lattice_osr_fwd_chunked_noalloc")
     return y, state_out
 
 

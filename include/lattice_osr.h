@@ -176,6 +176,28 @@ LATTICE_OSR_API int lattice_osr_fwd_chunked_gated(const lattice_osr_desc* desc, 
                                                   void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * lattice_osr_fwd_chunked for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and arguments without the workspace.  The
+ * split schedule's per-chunk arrays (and the state passing's hand-off
+ * buffers) live in a scratch array the library keeps in device memory, one
+ * per GPU, allocated with the library's code object and held until the
+ * process ends; the call itself allocates nothing.  Limit: configurations
+ * whose lattice_osr_workspace_bytes() exceeds
+ * LATTICE_OSR_NOALLOC_SCRATCH_BYTES return LATTICE_OSR_ERR_WORKSPACE.  The
+ * scratch is shared by every call on one GPU and keeps the last call's
+ * contents: calls that overlap in time on one GPU (distinct streams, or
+ * another thread) race on it and must be serialised by the caller.  The
+ * first call on a device looks up that device's copy (hipGetSymbolAddress,
+ * the device that is current); LATTICE_OSR_ERR_LAUNCH if that fails.
+ */
+#define LATTICE_OSR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+LATTICE_OSR_API int lattice_osr_fwd_chunked_noalloc(const lattice_osr_desc* desc, int32_t chunk_size,
+                                                    const void* q, const void* k, const void* v,
+                                                    const void* gamma, const void* mu, const float* state_in,
+                                                    float* state_out, void* y, void* hip_stream);
+
+/*
  * Exact recurrent forward: the recurrence of eq. recurrence_detailed applied
  * token by token (chunk size 1), the state held on chip across tokens.
  * Needs no workspace (workspace may be NULL, workspace_bytes 0).
