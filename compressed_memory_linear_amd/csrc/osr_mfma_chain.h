@@ -291,17 +291,22 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // accumulators), then the epilogue.
         if (g1_active) {
             constexpr int TPW = G::TPW, DPW = G::DPW;
-            // Accumulators start at -V (+V for the encoding layer, whose h is
-            // v): rows of V read 8 bytes at a time and brought into the
-            // accumulator layout by the (negated) identity.
+            // -V (+V for the encoding layer, whose h is v): rows of V read 8
+            // bytes at a time and brought into the accumulator layout by the
+            // (negated) identity on the 16-deep matrix core.  Where K Z runs
+            // on the 32-deep form, its chain starts from zero and -V is added
+            // on the VALU afterwards, so no 16-deep result is ever the
+            // accumulator input of a 32-deep product (no shared accumulator
+            // between the two shapes anywhere in this kernel).
             const s16x4 v_eye = ENC ? eye : neg_eye;
-            f32x4 ha[TPW][DPW];
+            f32x4 ha[TPW][DPW], vt[TPW][DPW];
 #pragma unroll
             for (int ti = 0; ti < TPW; ++ti)
 #pragma unroll
                 for (int dj = 0; dj < DPW; ++dj) {
                     const int tb = g1_tb0 + G::TG * ti, dc0 = 16 * (g1_grp + G::WSE * dj);
-                    ha[ti][dj] = tr16f(ld4s(vs + (16 * tb + lc) * G::VS_LD + dc0 + 4 * lg), v_eye);
+                    vt[ti][dj] = tr16f(ld4s(vs + (16 * tb + lc) * G::VS_LD + dc0 + 4 * lg), v_eye);
+                    ha[ti][dj] = (G::K32_M && p.mode == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : vt[ti][dj];
                 }
             if (p.mode == 0) {
                 if constexpr (G::K32_M) {
@@ -330,6 +335,10 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
 #pragma unroll
                             for (int dj = 0; dj < DPW; ++dj) ha[ti][dj] = mma32(kf[ti][km], zh8[dj], ha[ti][dj]);
                     }
+#pragma unroll
+                    for (int ti = 0; ti < TPW; ++ti)
+#pragma unroll
+                        for (int dj = 0; dj < DPW; ++dj) ha[ti][dj] += vt[ti][dj];
                 } else {
                     s16x4 kf[TPW];
 #pragma unroll
