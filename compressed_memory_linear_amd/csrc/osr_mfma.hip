@@ -53,16 +53,21 @@ int chain_subblock(int m, int d, int C) {
 }
 
 // Workgroups per sequence of the state-passing kernel: P = C / C0 when the
-// chunk is 2 or 4 of its sub-blocks and B*H*P workgroups (one per compute
-// unit: its LDS use allows no second) fit the 256 compute units, so that
-// every workgroup of a sequence is resident while it waits for the others.
+// chunk is 2 or 4 of its sub-blocks and there are at most 32 sequences (so
+// B*H*P workgroups, one per compute unit -- its LDS use allows no second --
+// fit the 256 compute units and every workgroup of a sequence is resident
+// while it waits for the others).  Measured (T = 2048 - 4096, split vs one
+// workgroup per sequence): m = d = 128, C = 128: 1.49x at 16 sequences,
+// 1.26x at 32, 1.00x at 64, 0.91x at 128; m64 d128 C64: 1.09x / 1.09x /
+// 1.04x / 1.03x; m = d = 128, C = 64: 1.12x / 1.04x / 0.96x / 0.79x.
 int chain_split_p(int B, int H, int m, int d, int C, int chain_wgs) {
     if (chain_wgs != 0) return 1;
     const int c0 = chain_subblock(m, d, C);
     if (c0 <= 0 || C % c0 != 0) return 1;
     const int P = C / c0;
     if (P != 2 && P != 4) return 1;
-    return static_cast<int64_t>(B) * H * P <= 256 ? P : 1;
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    return bh <= 32 && bh * P <= 256 ? P : 1;
 }
 
 size_t chain_xchg_bytes(int B, int H, int m, int d, int P) {

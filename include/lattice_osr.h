@@ -107,11 +107,11 @@ extern "C" {
 #define LATTICE_OSR_PAIRS_OFF 1  /* always one wave per block of 16 slots */
 
 /* Workgroups per (b,h) sequence in the state-passing kernel (split schedule). */
-#define LATTICE_OSR_WGS_AUTO 0 /* where a chunk is 2 or 4 of that kernel's sub-blocks and at
-                                  most one workgroup per compute unit results (few sequences:
-                                  B*H*P <= 256 on the device's compute units), one workgroup per
-                                  sub-block of the chunk, exchanging their parts of the chunk-end
-                                  state through the workspace; else one workgroup */
+#define LATTICE_OSR_WGS_AUTO 0 /* where a chunk is 2 or 4 (P) of that kernel's sub-blocks and
+                                  the sequences are few (B*H <= 32, and B*H*P no more than the
+                                  device's compute units), one workgroup per sub-block of the
+                                  chunk, exchanging their parts of the chunk-end state through
+                                  the workspace; else one workgroup */
 #define LATTICE_OSR_WGS_ONE 1  /* always one workgroup per sequence */
 
 /* Status codes. */

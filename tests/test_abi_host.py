@@ -137,11 +137,11 @@ def test_workgroup_split_workspace():
     """The state passing split over P workgroups per sequence (a chunk of P
     sub-blocks, few sequences) adds its hand-off buffers to the workspace: per
     (b,h), two chunk parities x P parts of (m d + 4 m) floats, and P m/16
-    counters of 128 bytes.  chain_wgs ONE, or too many sequences, adds none."""
+    counters of 128 bytes.  chain_wgs ONE, or more than 32 sequences, adds none."""
     m = d = C = 128
     T = 1024
     per_chunk = (m * d + 2 * m * C + d * C) * 4
-    for BH, P in ((16, 4), (64, 4), (65, 1), (200, 1)):
+    for BH, P in ((16, 4), (32, 4), (33, 1), (200, 1)):
         auto = osr.make_desc(1, T, BH, m, d)
         one = osr.make_desc(1, T, BH, m, d, chain_wgs=osr.WGS_ONE)
         base = BH * (T // C) * per_chunk
