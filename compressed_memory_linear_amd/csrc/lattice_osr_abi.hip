@@ -44,6 +44,8 @@ int check_desc(const lattice_osr_desc* d) {
     if (d->chain_pairs != LATTICE_OSR_PAIRS_AUTO && d->chain_pairs != LATTICE_OSR_PAIRS_OFF)
         return LATTICE_OSR_ERR_UNSUPPORTED;
     if (d->chain_wgs != LATTICE_OSR_WGS_AUTO && d->chain_wgs != LATTICE_OSR_WGS_ONE) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->readout_overlap != LATTICE_OSR_OVERLAP_AUTO && d->readout_overlap != LATTICE_OSR_OVERLAP_OFF)
+        return LATTICE_OSR_ERR_UNSUPPORTED;
     return LATTICE_OSR_OK;
 }
 
@@ -59,7 +61,7 @@ Path chunk_path(const lattice_osr_desc* d, int C) {
 size_t workspace_needed(const lattice_osr_desc* d, int C) {
     if (chunk_path(d, C) == Path::Mfma)
         return osr::mfma_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1,
-                                         d->schedule, d->chain_wgs);
+                                         d->schedule, d->chain_wgs, d->readout_overlap);
     return 0;
 }
 
@@ -129,9 +131,13 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     p.schedule = d->schedule;
     p.chain_pairs = d->chain_pairs;
     p.chain_wgs = d->chain_wgs;
+    p.readout_overlap = d->readout_overlap;
     p.xbuf = nullptr;
     p.xflags = nullptr;
     p.gate = nullptr;
+    p.n_begin = 0;
+    p.n_end = 0;
+    p.carry = nullptr;
     return p;
 }
 
@@ -323,6 +329,10 @@ int lattice_osr_fwd_chunked_noalloc(const lattice_osr_desc* desc, int32_t chunk_
     if (rc) return rc;
     if (chunk_size <= 0 || desc->T % chunk_size != 0) return LATTICE_OSR_ERR_SHAPE;
     if (!pow2_chunk(chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    // everything on the caller's stream: no side stream or events are touched
+    lattice_osr_desc dl = *desc;
+    dl.readout_overlap = LATTICE_OSR_OVERLAP_OFF;
+    desc = &dl;
     const size_t need = workspace_needed(desc, chunk_size);
     if (need > kScratchBytes) return LATTICE_OSR_ERR_WORKSPACE;
     // inputs and outputs as for lattice_osr_fwd_chunked (the scratch overlaps nothing of the caller's)

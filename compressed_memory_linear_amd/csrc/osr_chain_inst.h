@@ -66,7 +66,9 @@ static void launch_chain_mode(const Params& p, hipStream_t st) {
         if (p.xbuf && (p.chunk == 2 * C0 || p.chunk == 4 * C0)) {
             const int P = p.chunk / C0;
             const int nflags = static_cast<int>(BH) * P * (M / 16) * XFLAG_STRIDE;
-            hipLaunchKernelGGL(osr_zero_ints<0>, dim3((nflags + 255) / 256), dim3(256), 0, st, p.xflags, nflags);
+            // (the counters run on across the chunk ranges of one forward: zeroed before its first)
+            if (p.n_begin == 0)
+                hipLaunchKernelGGL(osr_zero_ints<0>, dim3((nflags + 255) / 256), dim3(256), 0, st, p.xflags, nflags);
             const unsigned grid = (BH + 7) / 8 * 8 * static_cast<unsigned>(P);
             if (P == 2)
                 hipLaunchKernelGGL((osr_chain_kernel<M, D, C0, true, false, false, ENC, LIN1, false, 2>), dim3(grid),

@@ -36,12 +36,18 @@ struct Params {
     int schedule;      // matrix-core chunk schedule: 0 automatic, 1 split, 2 fused
     int chain_pairs;   // state passing: 0 pairs where they pay, 1 one wave per slot block
     int chain_wgs;     // state passing: 0 split over workgroups where it applies, 1 one workgroup
+    int readout_overlap;  // split schedule: 0 read-out overlapped by chunk ranges where it applies, 1 not
     // State passing with P > 1 workgroups per (b,h) (each takes one sub-block
     // of every chunk): per (b,h), chunk parity and workgroup, that
     // workgroup's part of the chunk-end update and its gate products; and one
     // progress counter per workgroup (128 bytes apart), zeroed before the launch.
     float* xbuf;
     int* xflags;
+    // Chunk range of a split-schedule launch: chunks [n_begin, n_end) (n_end = 0:
+    // all).  Between ranges the state passing hands the unprojected state on
+    // through carry ([B*H][m][d] fp32); only the last range writes state_out.
+    int n_begin, n_end;
+    float* carry;
     // GeLU post-gate of the layer fused into the y store: y_t <- y_t * GeLU(gate_t)
     // with gate [B,T,H,d] in the inputs' dtype, or null (plain y).
     const void* gate;

@@ -18,7 +18,18 @@ int launch_valu(bool decode, int m, int d, const Params& p, bool in_bf16, hipStr
 // workspace it needs, and the launch of the inter-chunk state-passing kernel
 // followed by the read-out kernel (split schedule), or the fused kernel.
 bool mfma_supported(int m, int d, int C);
-size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1, int schedule, int chain_wgs);
+// Side stream and events of the overlapped read-out (split schedule): nseg
+// chunk ranges (ends in `end`), each range's read-out on `side` while the next range's state
+// passing runs on the caller's stream.
+constexpr int kMaxRanges = 8;
+struct Overlap {
+    int nseg;
+    int end[kMaxRanges];  // chunk end of each range (the first starts at chunk 0)
+    hipStream_t side;
+    hipEvent_t ev_chain, ev_side;
+};
+size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1, int schedule, int chain_wgs,
+                            int readout_overlap);
 // The split schedule's per-chunk workspace whatever the schedule choice, and
 // the state-passing kernel alone (the backward takes its chunk-start states
 // from it, through Params::raw).

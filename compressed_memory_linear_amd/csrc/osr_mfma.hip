@@ -9,13 +9,15 @@
 //   fused: one workgroup per (b,h) does both (osr_mfma_kernels.h); no
 //          workspace.
 // split wins when B*H alone cannot fill the 256 compute units.
+#include <mutex>
+
 #include "osr_launch.h"
 #include "osr_mfma_kernels.h"
 
 namespace osr {
 namespace mfma {
 template <int M>
-int launch_m(int d, bool split, const Params& p, hipStream_t st);
+int launch_m(int d, bool split, const Params& p, hipStream_t st, const Overlap* ov);
 template <int M>
 int launch_chain_m(int d, const Params& p, hipStream_t st);
 template <int M>
@@ -24,10 +26,10 @@ extern template int chain_subblock_m<16>(int, int);
 extern template int chain_subblock_m<32>(int, int);
 extern template int chain_subblock_m<64>(int, int);
 extern template int chain_subblock_m<128>(int, int);
-extern template int launch_m<16>(int, bool, const Params&, hipStream_t);
-extern template int launch_m<32>(int, bool, const Params&, hipStream_t);
-extern template int launch_m<64>(int, bool, const Params&, hipStream_t);
-extern template int launch_m<128>(int, bool, const Params&, hipStream_t);
+extern template int launch_m<16>(int, bool, const Params&, hipStream_t, const Overlap*);
+extern template int launch_m<32>(int, bool, const Params&, hipStream_t, const Overlap*);
+extern template int launch_m<64>(int, bool, const Params&, hipStream_t, const Overlap*);
+extern template int launch_m<128>(int, bool, const Params&, hipStream_t, const Overlap*);
 
 // Schedule choice (schedule: 0 automatic, 1 split, 2 fused; the first
 // linearisation has no fused form).  The split schedule (state passing, then
@@ -76,6 +78,39 @@ size_t chain_xchg_bytes(int B, int H, int m, int d, int P) {
     return static_cast<size_t>(B) * H * (2 * P * per * sizeof(float) + static_cast<size_t>(P) * (m / 16) * 32 * sizeof(int));
 }
 
+// Chunk ranges of an overlapped read-out (split schedule).  With at most 64
+// state-passing workgroups (three quarters of the compute units or more left
+// to the read-out; at 128, B8 H16 T4096 m64 d128 C64, it measured no faster)
+// and a multiple of 64 chunks: 8 ranges of 16, 16, 16, 8, 4, 2, 1
+// and 1 64ths of the chunks.  A range's read-out (on the side stream) then
+// takes no longer than the next range's state passing, even where it shares
+// the device with it, and the read-out of the last range, the only one not
+// hidden, is 1/64 of the whole; each range costs one event hand-off (~7 us).
+// Else 1 (no overlap).  Returns the ranges' chunk ends in `end`.
+int overlap_ranges(int B, int H, int m, int d, int C, int T, int chain_wgs, int readout_overlap, int* end) {
+    const int NC = T / C;
+    const int64_t wgs = static_cast<int64_t>(B) * H * chain_split_p(B, H, m, d, C, chain_wgs);
+    if (readout_overlap != 0 || wgs > 64 || NC < 64 || NC % 64 != 0) return 1;
+    static constexpr int kParts[kMaxRanges] = {16, 16, 16, 8, 4, 2, 1, 1};
+    int n = 0;
+    for (int k = 0; k < kMaxRanges; ++k) {
+        n += kParts[k] * (NC / 64);
+        if (end) end[k] = n;
+    }
+    return kMaxRanges;
+}
+
+// The side stream and events of the overlapped read-out, one set per device,
+// created on first use (default priority) and kept until the process ends.
+struct SideStream {
+    bool tried = false, ok = false;
+    hipStream_t s = nullptr;
+    hipEvent_t ev_chain = nullptr, ev_side = nullptr;
+};
+constexpr int kMaxDev = 64;
+SideStream g_side[kMaxDev];
+std::mutex g_side_mu;
+
 int device_compute_units() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -97,10 +132,15 @@ size_t mfma_chain_workspace_bytes(int B, int H, int T, int m, int d, int C, bool
 }
 
 // The first linearisation runs on the split schedule only.
-size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1, int schedule, int chain_wgs) {
+size_t mfma_workspace_bytes(int B, int H, int T, int m, int d, int C, bool lin1, int schedule, int chain_wgs,
+                            int readout_overlap) {
     if (!mfma::use_split(B, H, d, schedule, lin1)) return 0;
+    // per-chunk arrays, hand-off buffers of the split state passing, the state
+    // handed from one chunk range to the next
+    const size_t carry = mfma::overlap_ranges(B, H, m, d, C, T, chain_wgs, readout_overlap, nullptr) > 1
+                             ? static_cast<size_t>(B) * H * m * d * sizeof(float) : 0;
     return mfma_chain_workspace_bytes(B, H, T, m, d, C, lin1) +
-           mfma::chain_xchg_bytes(B, H, m, d, mfma::chain_split_p(B, H, m, d, C, chain_wgs));
+           mfma::chain_xchg_bytes(B, H, m, d, mfma::chain_split_p(B, H, m, d, C, chain_wgs)) + carry;
 }
 
 int launch_mfma_chain_only(int m, int d, const Params& p, hipStream_t st) {
@@ -116,21 +156,46 @@ int launch_mfma_chain_only(int m, int d, const Params& p, hipStream_t st) {
 int launch_mfma_chunked(int m, int d, const Params& p0, hipStream_t st) {
     const bool split = mfma::use_split(p0.B, p0.H, d, p0.schedule, p0.lin1 != 0);
     Params p = p0;
+    Overlap ov{};
+    ov.nseg = 1;
+    std::unique_lock<std::mutex> side_lock;
     if (split) {
         // the state passing split over workgroups: hand-off buffers after the per-chunk arrays
         const int P = mfma::chain_split_p(p.B, p.H, m, d, p.chunk, p.chain_wgs);
+        const size_t off = mfma_chain_workspace_bytes(p.B, p.H, p.T, m, d, p.chunk, p.lin1 != 0);
+        const size_t xb = mfma::chain_xchg_bytes(p.B, p.H, m, d, P);
         if (P > 1 && static_cast<int64_t>(p.B) * p.H * P <= mfma::device_compute_units()) {
-            const size_t off = mfma_chain_workspace_bytes(p.B, p.H, p.T, m, d, p.chunk, p.lin1 != 0);
             const size_t per = static_cast<size_t>(m / 16) * (d / 16) * 64 * 4 + static_cast<size_t>(m / 16) * 64;
             p.xbuf = reinterpret_cast<float*>(reinterpret_cast<char*>(p.zbuf) + off);
             p.xflags = reinterpret_cast<int*>(p.xbuf + static_cast<size_t>(p.B) * p.H * 2 * P * per);
         }
+        // the read-out overlapped with the state passing, by chunk ranges, on the device's side stream
+        const int nseg = mfma::overlap_ranges(p.B, p.H, m, d, p.chunk, p.T, p.chain_wgs, p.readout_overlap, ov.end);
+        int dev = -1;
+        if (nseg > 1 && hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < mfma::kMaxDev) {
+            side_lock = std::unique_lock<std::mutex>(mfma::g_side_mu);
+            mfma::SideStream& ss = mfma::g_side[dev];
+            if (!ss.tried) {
+                ss.tried = true;
+                ss.ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess &&
+                        hipEventCreateWithFlags(&ss.ev_chain, hipEventDisableTiming) == hipSuccess &&
+                        hipEventCreateWithFlags(&ss.ev_side, hipEventDisableTiming) == hipSuccess;
+            }
+            if (ss.ok) {
+                ov.nseg = nseg;
+                ov.side = ss.s;
+                ov.ev_chain = ss.ev_chain;
+                ov.ev_side = ss.ev_side;
+                p.carry = reinterpret_cast<float*>(reinterpret_cast<char*>(p.zbuf) + off + xb);
+            }
+        }
     }
+    const Overlap* ovp = ov.nseg > 1 ? &ov : nullptr;
     switch (m) {
-        case 16: return mfma::launch_m<16>(d, split, p, st);
-        case 32: return mfma::launch_m<32>(d, split, p, st);
-        case 64: return mfma::launch_m<64>(d, split, p, st);
-        case 128: return mfma::launch_m<128>(d, split, p, st);
+        case 16: return mfma::launch_m<16>(d, split, p, st, ovp);
+        case 32: return mfma::launch_m<32>(d, split, p, st, ovp);
+        case 64: return mfma::launch_m<64>(d, split, p, st, ovp);
+        case 128: return mfma::launch_m<128>(d, split, p, st, ovp);
         default: return -3;
     }
 }

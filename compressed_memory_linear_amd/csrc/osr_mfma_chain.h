@@ -212,7 +212,10 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
     const int wv = w % G::NWS;              // slot block of this wave
     const int slot = 16 * wv + lc;
     const int tbg = grp * TBW;              // first token tile of the group
-    const int C = p.chunk, NS = P > 1 ? p.T / C : p.T / C0, SPC = C / C0;
+    const int C = p.chunk, SPC = C / C0, NC = p.T / C;
+    // chunk range [n0, n1): iterations s over chunks (P > 1) or sub-blocks
+    const int n0 = p.n_begin, n1 = p.n_end > 0 ? p.n_end : NC;
+    const int S0 = P > 1 ? n0 : n0 * SPC, NS = P > 1 ? n1 : n1 * SPC;
     bool xbroken = false;  // a hand-off wait gave up: stop waiting (the results are then wrong)
     // H = K Z - V assignment of this wave (inside its group).
     const int g1_tb0 = tbg + wv % G::TG, g1_grp = wv / G::TG;
@@ -224,12 +227,14 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
     Pre<G> nxt;
 
     {
-        const float* src = p.state_in + static_cast<int64_t>(bh) * M * D + static_cast<int64_t>(slot) * D + 4 * lg;
+        // the initial state, or the unprojected state a previous chunk range handed on
+        const float* src = (n0 > 0 ? p.carry : p.state_in) + static_cast<int64_t>(bh) * M * D +
+                           static_cast<int64_t>(slot) * D + 4 * lg;
 #pragma unroll
         for (int j = 0; j < DB; ++j) acc[j] = *reinterpret_cast<const f32x4*>(src + 16 * j);
     }
     const PreOff<G> poff = prefetch_offsets<G>(p);
-    prefetch<G, false>(nxt, poff, p, b, hd, pidx * C0);
+    prefetch<G, false>(nxt, poff, p, b, hd, n0 * C + pidx * C0);
     commit<G, false>(nxt, stage, p.gamma_per_slot != 0);
     // Drain the loads above before the loop.  Left pending, they make the
     // compiler's wait analysis treat the loop-carried state tiles as possibly
@@ -237,13 +242,13 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
     // memory operation of the previous sub-block, stores included.
     __builtin_amdgcn_s_waitcnt(0);
 
-    for (int s = 0; s < NS; ++s) {
+    for (int s = S0; s < NS; ++s) {
         // P > 1: iteration s is chunk s, this workgroup's sub-block pidx of it
         const int t0 = P > 1 ? s * C + pidx * C0 : s * C0;
         const bool chunk_start = ONE || P > 1 || s % SPC == 0;
         const int chunk = ONE || P > 1 ? s : s / SPC;
         const bool has_next = s + 1 < NS;
-        const short* st = stage + (s & 1) * G::STAGE;
+        const short* st = stage + ((s - S0) & 1) * G::STAGE;
         const short* ks = st + G::SO_K;
         const short* vs = st + G::SO_V;
         const short* gs = st + G::SO_G;
@@ -613,7 +618,7 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
         // The memory counter retires loads and stores in order; the loads
         // were issued before this sub-block's workspace stores, so the wait
         // for them here leaves those stores in flight.
-        if (has_next) commit<G, false>(nxt, stage + ((s + 1) & 1) * G::STAGE, p.gamma_per_slot != 0);
+        if (has_next) commit<G, false>(nxt, stage + ((s + 1 - S0) & 1) * G::STAGE, p.gamma_per_slot != 0);
 
         if constexpr (PAIR) {
             // Swap (U_g, t_g) within the pair; both form
@@ -719,6 +724,15 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                      static_cast<int64_t>(slot) * D + 4 * lg;
 #pragma unroll
         for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
+    }
+    if (n1 < NC) {
+        // hand the unprojected state on to the next chunk range
+        if (grp == 0 && pidx == 0) {
+            float* dst = p.carry + static_cast<int64_t>(bh) * M * D + static_cast<int64_t>(slot) * D + 4 * lg;
+#pragma unroll
+            for (int j = 0; j < DB; ++j) *reinterpret_cast<f32x4*>(dst + 16 * j) = acc[j];
+        }
+        return;
     }
     const float inv = row_inv_norm<DB>(acc);
     if (grp == 0 && pidx == 0 && p.state_out) {

@@ -53,7 +53,8 @@ static int launch_readout(const Params& p, hipStream_t st) {
         // (every built m, d and sub-block fits both layouts)
         return -3;
     } else {
-        const int BH = p.B * p.H, NC = p.T / p.chunk;
+        // the launch's chunk range
+        const int BH = p.B * p.H, NC = (p.n_end > 0 ? p.n_end : p.T / p.chunk) - p.n_begin;
         // At least 512 workgroups (the kernel's registers and LDS hold two per
         // CU); each takes cpw consecutive chunks (a power of two dividing NC),
         // which keeps the register prefetch running across chunk boundaries.
@@ -69,24 +70,54 @@ static int launch_readout(const Params& p, hipStream_t st) {
 }
 
 template <int M, int D>
-static int launch_md(bool split, const Params& p, hipStream_t st) {
+static int launch_readout_md(const Params& p, hipStream_t st) {
+    return pick_c0_split_readout<M, D>(p.chunk) == 32 ? launch_readout<M, D, 32>(p, st)
+                                                      : launch_readout<M, D, 16>(p, st);
+}
+
+// Split schedule with the read-out overlapped (ov set): the chunks in ov->nseg
+// ranges; range k's state passing runs on the caller's stream st, and its
+// read-out on the side stream once that range's state passing is done, while
+// range k + 1's state passing runs; the last read-out runs on st, which then
+// waits for the side stream.  The ranges hand the state on through p.carry.
+template <int M, int D>
+static int launch_md(bool split, const Params& p, hipStream_t st, const Overlap* ov) {
     const int C = p.chunk;
     const int c0 = pick_c0_fused<M, D>(C);
     if (split) {
-        const int rc = launch_chain_m<M>(D, p, st);
-        if (rc) return rc;
-        return pick_c0_split_readout<M, D>(C) == 32 ? launch_readout<M, D, 32>(p, st) : launch_readout<M, D, 16>(p, st);
+        if (!ov) {
+            const int rc = launch_chain_m<M>(D, p, st);
+            if (rc) return rc;
+            return launch_readout_md<M, D>(p, st);
+        }
+        Params q = p;
+        for (int k = 0; k < ov->nseg; ++k) {
+            q.n_begin = k == 0 ? 0 : ov->end[k - 1];
+            q.n_end = ov->end[k];
+            int rc = launch_chain_m<M>(D, q, st);
+            if (rc) return rc;
+            if (k + 1 < ov->nseg) {
+                if (hipEventRecord(ov->ev_chain, st) != hipSuccess) return -5;
+                if (hipStreamWaitEvent(ov->side, ov->ev_chain, 0) != hipSuccess) return -5;
+                rc = launch_readout_md<M, D>(q, ov->side);
+            } else {
+                rc = launch_readout_md<M, D>(q, st);
+            }
+            if (rc) return rc;
+        }
+        if (hipEventRecord(ov->ev_side, ov->side) != hipSuccess) return -5;
+        return hipStreamWaitEvent(st, ov->ev_side, 0) == hipSuccess ? 0 : -5;
     }
     return c0 == 32 ? launch_fused<M, D, 32>(p, st) : launch_fused<M, D, 16>(p, st);
 }
 
 template <int M>
-int launch_m(int d, bool split, const Params& p, hipStream_t st) {
+int launch_m(int d, bool split, const Params& p, hipStream_t st, const Overlap* ov) {
     switch (d) {
-        case 16: return launch_md<M, 16>(split, p, st);
-        case 32: return launch_md<M, 32>(split, p, st);
-        case 64: return launch_md<M, 64>(split, p, st);
-        case 128: return launch_md<M, 128>(split, p, st);
+        case 16: return launch_md<M, 16>(split, p, st, ov);
+        case 32: return launch_md<M, 32>(split, p, st, ov);
+        case 64: return launch_md<M, 64>(split, p, st, ov);
+        case 128: return launch_md<M, 128>(split, p, st, ov);
         default: return -3;
     }
 }

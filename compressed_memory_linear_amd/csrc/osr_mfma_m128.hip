@@ -3,6 +3,6 @@
 
 namespace osr {
 namespace mfma {
-template int launch_m<128>(int d, bool split, const Params& p, hipStream_t st);
+template int launch_m<128>(int d, bool split, const Params& p, hipStream_t st, const Overlap* ov);
 }  // namespace mfma
 }  // namespace osr

@@ -143,13 +143,14 @@ __global__ __launch_bounds__(4 * D) void osr_readout_kernel(Params p, int cpw) {
     using G = ReadCfg<M, D, C0, LIN1>;
     constexpr int MT = G::MT, TB = G::TB;
     __shared__ __attribute__((aligned(16))) char smem[G::BYTES];
-    const int C = p.chunk, NC = p.T / C, SPC = C / C0;
-    const int groups = NC / cpw;
+    const int C = p.chunk, SPC = C / C0;
+    const int n0 = p.n_begin, n1 = p.n_end > 0 ? p.n_end : p.T / C;  // chunk range of this launch
+    const int groups = (n1 - n0) / cpw;
     const int bh = blockIdx.x / groups, grp = blockIdx.x % groups;
     const int b = bh / p.H, hd = bh % p.H;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, lg = lane >> 4, lc = lane & 15;
     const int dcol = 16 * w + lc;
-    const int ch0 = grp * cpw, NS = cpw * SPC;
+    const int ch0 = n0 + grp * cpw, NS = cpw * SPC;
     const s16x4 eye = eye_operand(false);
 
     f32x4 acc[MT];  // R tiles: acc[mt][r] = R[16mt + 4lg + r][dcol]

@@ -23,6 +23,7 @@ LIN2, LIN1 = 0, 1
 SCHED_AUTO, SCHED_SPLIT, SCHED_FUSED = 0, 1, 2
 PAIRS_AUTO, PAIRS_OFF = 0, 1
 WGS_AUTO, WGS_ONE = 0, 1
+OVERLAP_AUTO, OVERLAP_OFF = 0, 1
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_ALIGN = -1, -2, -3, -4, -5, -6, -7
@@ -37,7 +38,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 class lattice_osr_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "H", "m", "d", "gamma_per_slot", "in_dtype", "y_dtype", "mode", "linearisation",
-                 "schedule", "chain_pairs", "chain_wgs")]
+                 "schedule", "chain_pairs", "chain_wgs", "readout_overlap")]
 
 
 class OSRError(RuntimeError):
@@ -98,9 +99,9 @@ lattice_osr_status_string = status_string
 
 
 def make_desc(B, T, H, m, d, gamma_per_slot=1, in_dtype=BF16, y_dtype=F32, mode=MODE_DEC, linearisation=LIN2,
-              schedule=SCHED_AUTO, chain_pairs=PAIRS_AUTO, chain_wgs=WGS_AUTO):
+              schedule=SCHED_AUTO, chain_pairs=PAIRS_AUTO, chain_wgs=WGS_AUTO, readout_overlap=OVERLAP_AUTO):
     return lattice_osr_desc(B, T, H, m, d, gamma_per_slot, in_dtype, y_dtype, mode, linearisation, schedule,
-                            chain_pairs, chain_wgs)
+                            chain_pairs, chain_wgs, readout_overlap)
 
 
 def lattice_osr_workspace_bytes(desc: lattice_osr_desc, chunk_size: int) -> int:
@@ -143,7 +144,7 @@ def _check_cuda(*tensors):
 
 
 def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation=0, schedule=SCHED_AUTO,
-               chain_pairs=PAIRS_AUTO, chain_wgs=WGS_AUTO) -> lattice_osr_desc:
+               chain_pairs=PAIRS_AUTO, chain_wgs=WGS_AUTO, readout_overlap=OVERLAP_AUTO) -> lattice_osr_desc:
     """Descriptor of a forward call, after checking every input against it:
     q, k [B,T,H,m]; v [B,T,H,d]; gamma [B,T,H,m] or [B,T,H]; mu [B,T,H]
     (all one dtype, float32 or bfloat16); state_in [B,H,m,d] float32; all
@@ -164,7 +165,7 @@ def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation=0, sch
     _check_tensor("mu", mu, (B, T, H), q.dtype, q.device)
     _check_tensor("state_in", state_in, (B, H, m, d), torch.float32, q.device)
     return make_desc(B, T, H, m, d, per_slot, _DT[q.dtype], _DT[y_dtype], mode, linearisation, schedule,
-                     chain_pairs, chain_wgs)
+                     chain_pairs, chain_wgs, readout_overlap)
 
 
 def _check_outputs(desc, q, state_in, state_out, y, y_dtype):
@@ -209,12 +210,15 @@ def _launch_stream(stream):
 def lattice_osr_fwd_chunked(q, k, v, gamma, mu, state_in, chunk_size: int, *, mode: int = MODE_DEC,
                             y_dtype=torch.float32, state_out=None, y=None, workspace=None,
                             stream=None, linearisation: int = 0, schedule: int = SCHED_AUTO,
-                            chain_pairs: int = PAIRS_AUTO, chain_wgs: int = WGS_AUTO) -> Tuple[torch.Tensor, torch.Tensor]:
+                            chain_pairs: int = PAIRS_AUTO, chain_wgs: int = WGS_AUTO,
+                            readout_overlap: int = OVERLAP_AUTO) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunk-wise OSR forward.  Returns (y [B,T,H,d], state_out [B,H,m,d]).
     linearisation: LIN2 (default, eq. recurrence_linear2) or LIN1.
-    schedule / chain_pairs / chain_wgs: the matrix-core schedule (speed only)."""
+    schedule / chain_pairs / chain_wgs / readout_overlap: the matrix-core
+    schedule (speed only)."""
     lib = load_library()
-    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation, schedule, chain_pairs, chain_wgs)
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation, schedule, chain_pairs, chain_wgs,
+                      readout_overlap)
     _check_outputs(desc, q, state_in, state_out, y, y_dtype)
     st = _launch_stream(stream)
     with torch.cuda.stream(st):
@@ -232,12 +236,14 @@ def lattice_osr_fwd_chunked(q, k, v, gamma, mu, state_in, chunk_size: int, *, mo
 def lattice_osr_fwd_chunked_gated(q, k, v, gamma, mu, gate, state_in, chunk_size: int, *, mode: int = MODE_DEC,
                                   y_dtype=torch.float32, state_out=None, y=None, workspace=None, stream=None,
                                   linearisation: int = 0, schedule: int = SCHED_AUTO, chain_pairs: int = PAIRS_AUTO,
-                                  chain_wgs: int = WGS_AUTO) -> Tuple[torch.Tensor, torch.Tensor]:
+                                  chain_wgs: int = WGS_AUTO,
+                                  readout_overlap: int = OVERLAP_AUTO) -> Tuple[torch.Tensor, torch.Tensor]:
     """Chunk-wise OSR forward with the GeLU post-gate fused into the output:
     y = OSR(...) * GeLU(gate), gate [B,T,H,d] in the inputs' dtype.
     Returns (y, state_out)."""
     lib = load_library()
-    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation, schedule, chain_pairs, chain_wgs)
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation, schedule, chain_pairs, chain_wgs,
+                      readout_overlap)
     _check_tensor("gate", gate, tuple(v.shape), q.dtype, q.device)
     _check_outputs(desc, q, state_in, state_out, y, y_dtype)
     st = _launch_stream(stream)
@@ -260,7 +266,8 @@ def lattice_osr_fwd_chunked_noalloc(q, k, v, gamma, mu, state_in, chunk_size: in
     """lattice_osr_fwd_chunked without a workspace: the library's per-GPU
     scratch holds it (at most NOALLOC_SCRATCH_BYTES).  The caller passes the
     outputs (y with y's dtype, state_out); nothing is allocated.  Calls that
-    overlap on one GPU race on the scratch."""
+    overlap on one GPU race on the scratch.  The read-out never overlaps
+    here (all work on the one stream)."""
     lib = load_library()
     desc = _desc_from(q, k, v, gamma, mu, state_in, y.dtype, mode, linearisation, schedule, chain_pairs, chain_wgs)
     _check_outputs(desc, q, state_in, state_out, y, y.dtype)

@@ -36,8 +36,10 @@
  *
  * Ownership: every pointer is a device pointer owned by the caller, including
  * the workspace.  The library never allocates, frees or retains device memory
- * and keeps no mutable global state; calls on distinct streams may run
- * concurrently.  state_out may alias state_in exactly (in-place update); any
+ * (the no-allocation entry's static scratch array aside).  Its only other
+ * global state is one side stream and two events per device, created on the
+ * first call that overlaps the read-out (LATTICE_OSR_OVERLAP_AUTO) and kept
+ * until the process ends; calls on distinct streams may run concurrently.  state_out may alias state_in exactly (in-place update); any
  * partial overlap between state_in and state_out, or any overlap of y with
  * another argument, is rejected.
  *
@@ -114,6 +116,17 @@ extern "C" {
                                   the workspace; else one workgroup */
 #define LATTICE_OSR_WGS_ONE 1  /* always one workgroup per sequence */
 
+/* Read-out of the split schedule overlapped with its state passing. */
+#define LATTICE_OSR_OVERLAP_AUTO 0 /* where the state passing takes at most 64 workgroups and
+                                      there are at least 64 chunks (a multiple of 64): the chunks
+                                      in 8 ranges of shrinking length (1/4, 1/4, 1/4, 1/8, 1/16,
+                                      1/32, 1/64, 1/64); each range's read-out runs on the
+                                      library's side stream for the device while the next range's
+                                      state passing runs on hip_stream, which waits for the side
+                                      stream before the call's work ends.  Same results, bit for
+                                      bit, as _OFF */
+#define LATTICE_OSR_OVERLAP_OFF 1  /* state passing, then read-out, both on hip_stream */
+
 /* Status codes. */
 #define LATTICE_OSR_OK 0
 #define LATTICE_OSR_ERR_NULL (-1)        /* a required pointer is NULL              */
@@ -138,6 +151,7 @@ typedef struct {
     int32_t schedule;       /* LATTICE_OSR_SCHED_AUTO (0), _SPLIT (1), _FUSED (2) */
     int32_t chain_pairs;    /* LATTICE_OSR_PAIRS_AUTO (0) or _OFF (1)            */
     int32_t chain_wgs;      /* LATTICE_OSR_WGS_AUTO (0) or _ONE (1)              */
+    int32_t readout_overlap; /* LATTICE_OSR_OVERLAP_AUTO (0) or _OFF (1)         */
 } lattice_osr_desc;
 
 /*
@@ -189,7 +203,10 @@ LATTICE_OSR_API int lattice_osr_fwd_chunked_gated(const lattice_osr_desc* desc, 
  * contents: calls that overlap in time on one GPU (distinct streams, or
  * another thread) race on it and must be serialised by the caller.  The
  * first call on a device looks up that device's copy (hipGetSymbolAddress,
- * the device that is current); LATTICE_OSR_ERR_LAUNCH if that fails.
+ * the device that is current); LATTICE_OSR_ERR_LAUNCH if that fails.  The
+ * read-out never overlaps here (desc->readout_overlap is taken as
+ * LATTICE_OSR_OVERLAP_OFF, and the workspace limit is that of _OFF): all work
+ * stays on hip_stream.
  */
 #define LATTICE_OSR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 LATTICE_OSR_API int lattice_osr_fwd_chunked_noalloc(const lattice_osr_desc* desc, int32_t chunk_size,

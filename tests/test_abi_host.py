@@ -79,6 +79,7 @@ def test_null_pointers(fn):
     ("schedule", 3, osr.ERR_UNSUPPORTED), ("schedule", -1, osr.ERR_UNSUPPORTED),
     ("chain_pairs", 2, osr.ERR_UNSUPPORTED), ("chain_pairs", -1, osr.ERR_UNSUPPORTED),
     ("chain_wgs", 2, osr.ERR_UNSUPPORTED), ("chain_wgs", -1, osr.ERR_UNSUPPORTED),
+    ("readout_overlap", 2, osr.ERR_UNSUPPORTED), ("readout_overlap", -1, osr.ERR_UNSUPPORTED),
 ])
 def test_bad_descriptor(field, value, status):
     d = osr.make_desc(2, 8, 2, 32, 32)
@@ -152,6 +153,24 @@ def test_workgroup_split_workspace():
     two = osr.make_desc(1, 256, 16, 128, 128)
     assert osr.lattice_osr_workspace_bytes(two, 64) == 16 * 4 * (m * d + 2 * m * 64 + d * 64) * 4 + \
         16 * (2 * 2 * (m * d + 4 * m) * 4 + 2 * 8 * 128)
+
+
+def test_overlapped_readout_workspace():
+    """The read-out overlapped by chunk ranges (at most 64 state-passing
+    workgroups, a multiple of 64 chunks) hands the state from range to range
+    through one more array of B H m d floats; OVERLAP_OFF, too few or ragged
+    chunk counts, or more workgroups add none."""
+    m = d = C = 128
+    per_chunk = (m * d + 2 * m * C + d * C) * 4
+    for BH, P, NC, carry in ((16, 4, 64, True), (16, 4, 512, True), (33, 1, 64, True), (64, 1, 128, True),
+                             (65, 1, 64, False), (16, 4, 32, False), (16, 4, 96, False)):
+        T = NC * C
+        auto = osr.make_desc(1, T, BH, m, d)
+        off = osr.make_desc(1, T, BH, m, d, readout_overlap=osr.OVERLAP_OFF)
+        base = BH * NC * per_chunk
+        base += BH * (2 * P * (m * d + 4 * m) * 4 + P * (m // 16) * 128) if P > 1 else 0
+        assert osr.lattice_osr_workspace_bytes(off, C) == base, (BH, NC)
+        assert osr.lattice_osr_workspace_bytes(auto, C) == base + (BH * m * d * 4 if carry else 0), (BH, NC)
 
 
 def test_library_reads_no_environment():

@@ -512,3 +512,49 @@ def test_chain_workgroup_split_deterministic():
     y1, S1 = _run("chunked", inp, 128)
     y2, S2 = _run("chunked", inp, 128)
     assert torch.equal(y1, y2) and torch.equal(S1, S2)
+
+
+# The read-out overlapped with the state passing by chunk ranges (64 chunks or
+# a multiple: 8 ranges, the state handed from range to range unprojected):
+# the same kernels over the same chunks, so the results equal those of the
+# serial launch bit for bit, and meet the bar against the oracle.
+OVERLAP_CASES = [  # (B, H, m, d, C, chunks): workgroups per sequence 4, 2 and 1
+    (1, 2, 128, 128, 128, 64), (1, 3, 128, 128, 64, 128), (2, 3, 64, 64, 32, 64), (1, 2, 32, 128, 64, 64),
+]
+
+
+@pytest.mark.parametrize("B,H,m,d,C,nc", OVERLAP_CASES)
+@pytest.mark.parametrize("mode", [osr.MODE_DEC, osr.MODE_SIM])
+def test_overlapped_readout(B, H, m, d, C, nc, mode):
+    _say(f"read-out overlapped by chunk ranges B{B} H{H} m={m} d={d} C={C} chunks={nc} mode={mode}")
+    inp = synth.make_inputs(B, nc * C, H, m, d, seed=1400 + m + d + C + nc + mode, in_dtype=synth.BF16)
+    yo, So = _run("chunked", inp, C, mode=mode)
+    ys, Ss = _run("chunked", inp, C, mode=mode, readout_overlap=osr.OVERLAP_OFF)
+    assert torch.equal(yo, ys) and torch.equal(So, Ss)
+    _check(inp, yo, So, C, mode)
+
+
+def test_overlapped_readout_first_linearisation_and_bf16_y():
+    _say("read-out overlapped by chunk ranges, first linearisation and bf16 y, B1 H2 m=d=128 C128, 64 chunks")
+    inp = synth.make_inputs(1, 64 * 128, 2, 128, 128, seed=1500, in_dtype=synth.BF16)
+    for kw in ({"linearisation": osr.LIN1}, {"y_dtype": torch.bfloat16}):
+        yo, So = _run("chunked", inp, 128, **kw)
+        ys, Ss = _run("chunked", inp, 128, readout_overlap=osr.OVERLAP_OFF, **kw)
+        assert torch.equal(yo, ys) and torch.equal(So, Ss), kw
+    _check_lin1(inp, *_run("chunked", inp, 128, linearisation=osr.LIN1), 128, osr.MODE_DEC)
+
+
+def test_overlapped_readout_on_a_side_stream_of_the_caller():
+    """A call on a stream other than the current one: the outputs are final
+    once that stream is synchronised (its last work waits for the library's
+    side stream)."""
+    _say("read-out overlapped, caller's own stream, B1 H2 m=d=64 C32, 64 chunks")
+    inp = synth.make_inputs(1, 64 * 32, 2, 64, 64, seed=1600, in_dtype=synth.BF16)
+    t = osr.to_device(inp)
+    args = (t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"])
+    ref_y, ref_S = osr.lattice_osr_fwd_chunked(*args, 32, readout_overlap=osr.OVERLAP_OFF)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    y, S = osr.lattice_osr_fwd_chunked(*args, 32, stream=s)
+    s.synchronize()
+    assert torch.equal(y, ref_y) and torch.equal(S, ref_S)
