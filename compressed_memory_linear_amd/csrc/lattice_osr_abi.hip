@@ -132,6 +132,7 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     p.chain_pairs = d->chain_pairs;
     p.chain_wgs = d->chain_wgs;
     p.readout_overlap = d->readout_overlap;
+    p.chain_p = 1;
     p.xbuf = nullptr;
     p.xflags = nullptr;
     p.gate = nullptr;

@@ -63,8 +63,8 @@ static void launch_chain_mode(const Params& p, hipStream_t st) {
     if constexpr (!RAW && C0 <= 64) {
         // Split over P = C / C0 workgroups per sequence (the caller set up the
         // hand-off buffers only where that applies): counters to zero first.
-        if (p.xbuf && (p.chunk == 2 * C0 || p.chunk == 4 * C0)) {
-            const int P = p.chunk / C0;
+        if (p.xbuf && (p.chain_p == 2 || p.chain_p == 4) && p.chunk == p.chain_p * C0) {
+            const int P = p.chain_p;
             const int nflags = static_cast<int>(BH) * P * (M / 16) * XFLAG_STRIDE;
             // (the counters run on across the chunk ranges of one forward: zeroed before its first)
             if (p.n_begin == 0)
@@ -127,7 +127,7 @@ template <int M, int D>
 static int launch_chain_md(const Params& p, hipStream_t st) {
     // Only sub-block lengths the pick can return are instantiated.
     constexpr int cmax = pick_c0_chain<M, D>(64);
-    const int c0 = pick_c0_chain<M, D>(p.chunk);
+    const int c0 = p.chain_p > 1 ? p.chunk / p.chain_p : pick_c0_chain<M, D>(p.chunk);
     if constexpr (cmax >= 64)
         if (c0 == 64) return launch_chain<M, D, 64>(p, st);
     if constexpr (cmax >= 32)

@@ -37,6 +37,7 @@ struct Params {
     int chain_pairs;   // state passing: 0 pairs where they pay, 1 one wave per slot block
     int chain_wgs;     // state passing: 0 split over workgroups where it applies, 1 one workgroup
     int readout_overlap;  // split schedule: 0 read-out overlapped by chunk ranges where it applies, 1 not
+    int chain_p;       // workgroups per sequence of the state passing (set by the launch; 1 = not split)
     // State passing with P > 1 workgroups per (b,h) (each takes one sub-block
     // of every chunk): per (b,h), chunk parity and workgroup, that
     // workgroup's part of the chunk-end update and its gate products; and one

@@ -61,7 +61,10 @@ int chain_subblock(int m, int d, int C) {
 // while it waits for the others).  Measured (T = 2048 - 4096, split vs one
 // workgroup per sequence): m = d = 128, C = 128: 1.49x at 16 sequences,
 // 1.26x at 32, 1.00x at 64, 0.91x at 128; m64 d128 C64: 1.09x / 1.09x /
-// 1.04x / 1.03x; m = d = 128, C = 64: 1.12x / 1.04x / 0.96x / 0.79x.
+// 1.04x / 1.03x; m = d = 128, C = 64: 1.12x / 1.04x / 0.96x / 0.79x.  Eight
+// workgroups of 16 tokens (m = d = 128, C = 128, 16 sequences) measured 6.49
+// against 5.06 ms for four of 32: each workgroup loads every other's part of
+// the chunk-end state (m d floats each), and that traffic grows with P.
 int chain_split_p(int B, int H, int m, int d, int C, int chain_wgs) {
     if (chain_wgs != 0) return 1;
     const int c0 = chain_subblock(m, d, C);
@@ -168,6 +171,7 @@ int launch_mfma_chunked(int m, int d, const Params& p0, hipStream_t st) {
             const size_t per = static_cast<size_t>(m / 16) * (d / 16) * 64 * 4 + static_cast<size_t>(m / 16) * 64;
             p.xbuf = reinterpret_cast<float*>(reinterpret_cast<char*>(p.zbuf) + off);
             p.xflags = reinterpret_cast<int*>(p.xbuf + static_cast<size_t>(p.B) * p.H * 2 * P * per);
+            p.chain_p = P;
         }
         // the read-out overlapped with the state passing, by chunk ranges, on the device's side stream
         const int nseg = mfma::overlap_ranges(p.B, p.H, m, d, p.chunk, p.T, p.chain_wgs, p.readout_overlap, ov.end);
