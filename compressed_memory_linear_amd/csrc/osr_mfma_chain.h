@@ -178,6 +178,19 @@ constexpr int XCPOL_SC1 = 16;  // cache-policy operand: sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(float* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
 }
+// Wait until wave w of workgroup q of sequence bh has published chunk s
+// (its counter passed s); gives up after XSPIN polls (broken = true).
+template <class G>
+__device__ __forceinline__ void xwait(const Params& p, int bh, int P, int q, int w, int s, bool& broken) {
+    const int* f = p.xflags + ((bh * P + q) * G::NWS + w) * XFLAG_STRIDE;
+    int n = 0;
+    while (__hip_atomic_load(const_cast<int*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= s) {
+        if (++n >= XSPIN) {
+            broken = true;
+            break;
+        }
+    }
+}
 
 template <int M, int D, int C0, bool WRITE_Z, bool ONE, bool PAIR, bool ENC, bool LIN1 = false, bool RAW = false,
           int P = 1>
@@ -642,8 +655,9 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
             }
         } else if constexpr (P > 1) {
             // Publish (U_p, t_p), then R_end = diag(prod_q t_q) Z +
-            // sum_q diag(prod_{q' > q} t_q') U_q, summed in q order by every
-            // workgroup (so all hold the same bits).
+            // sum_q diag(prod_{q' > q} t_q') U_q by Horner's rule in q order,
+            // R <- R (.) t_q + U_q from R = Z, with the same operations in the
+            // same order in every workgroup (so all hold the same bits).
             const int64_t xs = xchg_floats<M, D>();
             float* xb = p.xbuf + (static_cast<int64_t>(bh) * 2 + (s & 1)) * P * xs;
             const __amdgpu_buffer_rsrc_t xr = xrsrc(xb, static_cast<uint32_t>(P * xs * sizeof(float)));
@@ -663,55 +677,81 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's hand-off stores have retired
             int* myflag = p.xflags + ((bh * P + pidx) * G::NWS + w) * XFLAG_STRIDE;
             if (lane == 0) __hip_atomic_store(myflag, s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t t_off = ((M / 16) * DB * 64 * 4 + w * 64 + lane) * 4;
+            if constexpr (!ENC && !LIN1) {
+                // Part q is loaded as soon as its counter shows it, so the
+                // parts that are ready stream in while a later one is still
+                // computed; the workgroup's own part comes from its registers.
 #pragma unroll
-            for (int q = 0; q < P; ++q) {
-                if (q == pidx || xbroken) continue;
-                const int* f = p.xflags + ((bh * P + q) * G::NWS + w) * XFLAG_STRIDE;
-                int n = 0;
-                while (__hip_atomic_load(const_cast<int*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= s) {
-                    if (++n >= XSPIN) {
-                        xbroken = true;
-                        break;
+                for (int q = 0; q < P; ++q) {
+                    if (q == pidx) {
+#pragma unroll
+                        for (int db = 0; db < DB; ++db)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[db][e] = fmaf(acc[db][e], aend, u[db][e]);
+                        continue;
                     }
+                    if (!xbroken) xwait<G>(p, bh, P, q, w, s, xbroken);
+                    asm volatile("" ::: "memory");  // part q's reads stay after its wait
+                    const uint32_t base = static_cast<uint32_t>(q * xs) * 4;
+                    const float tq = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, base + t_off, 0, XCPOL_SC1));
+                    f32x4 uq[DB];
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+                        uq[db] = __builtin_bit_cast(
+                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, base + ((w * DB + db) * 64 + lane) * 16,
+                                                                         0, XCPOL_SC1));
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[db][e] = fmaf(acc[db][e], tq, uq[db][e]);
                 }
-            }
-            asm volatile("" ::: "memory");  // the reads below stay after the waits
-            float tq[P];
+            } else {
+                // The encoding and first-linearisation forms hold more
+                // registers: every part (its own too) is read back once all
+                // are published, R_end = diag(prod_q t_q) Z +
+                // sum_q diag(prod_{q' > q} t_q') U_q summed in q order.
 #pragma unroll
-            for (int q = 0; q < P; ++q)
-                tq[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                    xr, static_cast<uint32_t>(q * xs) * 4 + ((M / 16) * DB * 64 * 4 + w * 64 + lane) * 4, 0,
-                    XCPOL_SC1));
-            float sq[P], t_all = 1.f;
+                for (int q = 0; q < P; ++q)
+                    if (q != pidx && !xbroken) xwait<G>(p, bh, P, q, w, s, xbroken);
+                asm volatile("" ::: "memory");  // the reads below stay after the waits
+                float tq[P];
 #pragma unroll
-            for (int q = P - 1; q >= 0; --q) {
-                sq[q] = t_all;
-                t_all *= tq[q];
-            }
+                for (int q = 0; q < P; ++q)
+                    tq[q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        xr, static_cast<uint32_t>(q * xs) * 4 + ((M / 16) * DB * 64 * 4 + w * 64 + lane) * 4, 0,
+                        XCPOL_SC1));
+                float sq[P], t_all = 1.f;
 #pragma unroll
-            for (int db = 0; db < DB; ++db)
+                for (int q = P - 1; q >= 0; --q) {
+                    sq[q] = t_all;
+                    t_all *= tq[q];
+                }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[db][e] *= t_all;
-            // the parts in two batches of q (at most two parts of loads in
-            // flight in registers), each added in q order
-            constexpr int QB = P < 2 ? P : 2;
+                for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int q0 = 0; q0 < P; q0 += QB) {
-                f32x4 uq[QB][DB];
+                    for (int e = 0; e < 4; ++e) acc[db][e] *= t_all;
+                // the parts in two batches of q (at most two parts of loads in
+                // flight in registers), each added in q order
+                constexpr int QB = P < 2 ? P : 2;
 #pragma unroll
-                for (int qi = 0; qi < QB; ++qi)
+                for (int q0 = 0; q0 < P; q0 += QB) {
+                    f32x4 uq[QB][DB];
 #pragma unroll
-                    for (int db = 0; db < DB; ++db)
-                        uq[qi][db] = __builtin_bit_cast(
-                            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                       xr, static_cast<uint32_t>((q0 + qi) * xs) * 4 + ((w * DB + db) * 64 + lane) * 16,
-                                       0, XCPOL_SC1));
+                    for (int qi = 0; qi < QB; ++qi)
 #pragma unroll
-                for (int qi = 0; qi < QB; ++qi)
+                        for (int db = 0; db < DB; ++db)
+                            uq[qi][db] = __builtin_bit_cast(
+                                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           xr, static_cast<uint32_t>((q0 + qi) * xs) * 4 + ((w * DB + db) * 64 + lane) * 16,
+                                           0, XCPOL_SC1));
 #pragma unroll
-                    for (int db = 0; db < DB; ++db)
+                    for (int qi = 0; qi < QB; ++qi)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) acc[db][e] = fmaf(sq[q0 + qi], uq[qi][db][e], acc[db][e]);
+                        for (int db = 0; db < DB; ++db)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[db][e] = fmaf(sq[q0 + qi], uq[qi][db][e], acc[db][e]);
+                }
             }
         } else {
 #pragma unroll
