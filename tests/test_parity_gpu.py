@@ -235,10 +235,9 @@ def test_workload_chunked_b4h8_t2048_m64d64_c64_lin1():
 
 
 # ------------------------------------------------------------ decode sweep --
-# 37 x 64 = 2368 states: more than the persistent decode grid holds at once for
-# every shape, and not a multiple of it, so workgroups take several states
-# each (the next state streams in while the current one is updated) and the
-# last round is ragged.
+# 37 x 64 = 2368 states, one workgroup each: more workgroups than the device
+# holds at once for every shape, and not a multiple of its compute units, so
+# the grid runs in several rounds with a ragged last one.
 DECODE_SHAPES = [(16, 16), (32, 64), (64, 128), (128, 128)]
 
 
