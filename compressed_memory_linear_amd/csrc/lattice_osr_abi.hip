@@ -189,6 +189,14 @@ int check_bwd_buffers(const lattice_osr_desc* d, const void* q, const void* k, c
 // kernel where the forward would run on it (bf16 inputs, C >= 16), except for
 // the encoding layer, whose gradient is too sensitive to the split products'
 // rounding; otherwise its own fp32 forward pass finds them.
+// Compute units of the current device (0 if the query fails: no split then).
+int64_t device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
 bool bwd_uses_chain(const lattice_osr_desc* d, int C) {
     return d->in_dtype == LATTICE_OSR_BF16 && C >= 16 && osr::mfma_supported(d->m, d->d, C) &&
            d->mode != LATTICE_OSR_MODE_ENC;
@@ -202,12 +210,15 @@ size_t bwd_chain_extra_bytes(const lattice_osr_desc* d, int C) {
     return nch * (2 * static_cast<size_t>(d->m) * C + C) * sizeof(float);
 }
 
+// ... then, where the slot rows of a sequence split over several workgroups,
+// their hand-off buffers.
 size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
     size_t n = osr::bwd_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C);
-    if (bwd_uses_chain(d, C))
+    const bool chain = bwd_uses_chain(d, C);
+    if (chain)
         n += osr::mfma_chain_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1) +
              bwd_chain_extra_bytes(d, C);
-    return n;
+    return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, osr::bwd_split_p(d->B, d->H, d->m, chain, d->chain_wgs));
 }
 
 // Shape rules of the backward: those of the chunked forward.
@@ -449,6 +460,21 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
         p.chain_c = reinterpret_cast<const float*>(static_cast<const char*>(workspace) + bwd_bytes + chain_bytes);
         p.chain_b = p.chain_c + nch * mc;
         p.chain_hh = p.chain_b + nch * mc;
+    }
+    // slot rows split over workgroups: every workgroup of a sequence must be resident
+    // at once (they wait for each other), so no more workgroups than compute units
+    p.split_p = osr::bwd_split_p(desc->B, desc->H, desc->m, chain, desc->chain_wgs);
+    p.xbuf = nullptr;
+    p.xflags = nullptr;
+    if (p.split_p > 1) {
+        const size_t xoff = need - osr::bwd_xchg_bytes(desc->B, desc->H, desc->d, p.split_p);
+        const int64_t cus = device_cus();
+        while (p.split_p > 1 && static_cast<int64_t>(desc->B) * desc->H * p.split_p > cus) p.split_p /= 2;
+        if (p.split_p > 1) {
+            p.xbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + xoff);
+            p.xflags = reinterpret_cast<int*>(p.xbuf + static_cast<size_t>(desc->B) * desc->H * 2 * p.split_p * 8 *
+                                                           (desc->d + 4));
+        }
     }
     return osr::launch_bwd(desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, st);
 }

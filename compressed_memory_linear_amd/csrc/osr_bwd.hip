@@ -32,4 +32,26 @@ size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C) {
     return bwd_floats(T, m, d, C) * sizeof(float) * static_cast<size_t>(B) * static_cast<size_t>(H);
 }
 
+// The reverse walk's per-token work is per slot row except the sums over slots
+// of each batch of tokens, so the rows of one sequence split over P workgroups
+// that exchange those sums.  Where the state-passing kernel supplies the
+// chunk-start states and records (bf16 inputs, C >= 16, decoding and similarity
+// objectives): the largest P in {1, 2, 4, 8} with at least 16 rows per
+// workgroup and B*H*P <= 256 (one workgroup per compute unit, all resident).
+int bwd_split_p(int B, int H, int m, bool chain, int chain_wgs) {
+    if (!chain || chain_wgs != 0) return 1;
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    int P = 1;
+    while (P < 8 && m / (2 * P) >= 16 && bh * 2 * P <= 256) P *= 2;
+    return P;
+}
+
+// Per (b,h): 2 parities x P parts of at most 8 tokens x (d + 4) floats, then P
+// counters of XFLAG_STRIDE ints.
+size_t bwd_xchg_bytes(int B, int H, int d, int P) {
+    if (P <= 1) return 0;
+    const size_t bh = static_cast<size_t>(B) * H;
+    return bh * (2 * static_cast<size_t>(P) * 8 * (d + 4) * sizeof(float) + static_cast<size_t>(P) * XFLAG_STRIDE * sizeof(int));
+}
+
 }  // namespace osr

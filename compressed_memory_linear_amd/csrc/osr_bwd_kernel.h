@@ -53,6 +53,8 @@
 
 namespace osr {
 
+typedef unsigned int bwd_u32x4 __attribute__((ext_vector_type(4)));
+
 // Per-token record kept for the reverse walk: c[M], beta[M], |h|^2, pad.
 template <int M, int D>
 struct TokRec {
@@ -165,9 +167,13 @@ __device__ __forceinline__ void load_rev(RevIn<L::RPT>& x, const BwdParams& p, c
     }
 }
 
-template <int M, int D, int NT, typename TIn, bool LIN1, bool DYB>
+// P > 1: the slot rows of a sequence split over P workgroups (M / P rows
+// each); they exchange each batch's sums over slots (below).  Only with the
+// state-passing kernel's chunk-start states and records (the host ensures it).
+template <int M, int D, int NT, typename TIn, bool LIN1, bool DYB, int P = 1>
 __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
-    using L = ValuLayout<M, D, NT>;
+    static_assert(P == 1 || (M / P >= 16 && sizeof(TIn) == 2), "split: bf16 inputs, 16 rows or more each");
+    using L = ValuLayout<M / P, D, NT>;
     using TR = TokRec<M, D>;
     constexpr int BT = TokBatch<L>::BT, W = D + 4;
     // The reverse walk loads the next token's inputs and record while it works on
@@ -182,10 +188,12 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) float red[2 * BT * L::NW * W];
     __shared__ __attribute__((aligned(16))) float tot[BT * W];  // a batch's sums over slots
     static_assert(BT * (D / 4 + 1) <= NT, "one float4 of a batch's sums per thread");
-    const int bh = blockIdx.x;
+    const int bh = P > 1 ? blockIdx.x / P : blockIdx.x;
+    const int pidx = P > 1 ? blockIdx.x % P : 0;  // this workgroup's rows: [pidx M/P, (pidx + 1) M/P)
     const int b = bh / p.f.H, hd = bh % p.f.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cg = tid % L::TPR, rg = tid / L::TPR;
+    // rg: the (global) slot row of this thread's first row
+    const int cg = tid % L::TPR, rg = pidx * (M / P) + tid / L::TPR;
     const int T = p.f.T, C = p.f.chunk, NC = T / C;
     const int mode = p.f.mode;
     const int64_t tstride = p.f.H;  // consecutive tokens of one (b,h) are H rows apart
@@ -197,6 +205,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     auto el = [&](int i) { return (rg + L::RG * i) * D + cg * 4; };  // this thread's state elements
     auto bth_of = [&](int t) { return (static_cast<int64_t>(b) * T + t) * p.f.H + hd; };
     int nred = 0;  // LDS exchanges so far: consecutive ones use alternate halves of red
+    int nbatch = 0;  // batches exchanged with the other workgroups (P > 1)
+    bool xbroken = false;  // a wait for them gave up (then the results are wrong, but every wave ends)
 
     // ---- phase 1: forward, keeping every chunk-start state ----
     // (skipped when the state-passing kernel has stored them: then only the end
@@ -560,13 +570,64 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
             }
             __syncthreads();  // the batch's partial sums visible
             // the sums over waves, one float4 of the batch per thread
-            if (tid < nb * (D / 4 + 1)) {
-                const int u = tid / (D / 4 + 1), c4 = tid % (D / 4 + 1);
-                float4 acc = *reinterpret_cast<const float4*>(rb + (u * L::NW) * W + c4 * 4);
+            const bool mine = tid < nb * (D / 4 + 1);
+            const int xu = tid / (D / 4 + 1), xc4 = tid % (D / 4 + 1);
+            float4 acc = f4(0.f);
+            if (mine) {
+                acc = *reinterpret_cast<const float4*>(rb + (xu * L::NW) * W + xc4 * 4);
 #pragma unroll
-                for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (u * L::NW + w) * W + c4 * 4);
-                *reinterpret_cast<float4*>(tot + u * W + c4 * 4) = acc;
+                for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (xu * L::NW + w) * W + xc4 * 4);
             }
+            if constexpr (P > 1) {
+                // The other workgroups' sums of this batch (over their rows): publish
+                // this one's, wait for theirs, add all in workgroup order (the same
+                // operations in every workgroup).  Parts alternate between two
+                // buffers by batch parity: a buffer is rewritten two batches later,
+                // after every workgroup has published the batch in between, which
+                // each does only after reading this one.
+                constexpr int XW = 8 * W;  // floats per part (batches of at most 8 tokens)
+                static_assert(BT <= 8, "hand-off part size");
+                float* xb = p.xbuf + (static_cast<int64_t>(bh) * 2 + (nbatch & 1)) * P * XW;
+                const __amdgpu_buffer_rsrc_t xr = xrsrc(xb, static_cast<uint32_t>(P * XW * sizeof(float)));
+                const uint32_t off = static_cast<uint32_t>(xu * W + xc4 * 4) * 4;
+                if (mine)
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(bwd_u32x4, acc), xr,
+                                                           static_cast<uint32_t>(pidx * XW) * 4 + off, 0, XCPOL_SC1);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's part store has retired
+                __syncthreads();  // ... and every thread's
+                if (tid == 0) {
+                    __hip_atomic_store(p.xflags + (bh * P + pidx) * XFLAG_STRIDE, nbatch + 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    for (int q = 0; q < P; ++q) {
+                        if (q == pidx || xbroken) continue;
+                        const int* f = p.xflags + (bh * P + q) * XFLAG_STRIDE;
+                        int n = 0;
+                        while (__hip_atomic_load(const_cast<int*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <=
+                               nbatch) {
+                            if (++n >= XSPIN) {
+                                xbroken = true;
+                                break;
+                            }
+                        }
+                    }
+                }
+                __syncthreads();  // the other parts are published
+                asm volatile("" ::: "memory");  // the reads below stay after the barrier
+                if (mine) {
+                    float4 part[P];
+#pragma unroll
+                    for (int q = 0; q < P; ++q)
+                        part[q] = q == pidx ? acc
+                                            : __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                             xr, static_cast<uint32_t>(q * XW) * 4 + off,
+                                                                             0, XCPOL_SC1));
+                    acc = part[0];
+#pragma unroll
+                    for (int q = 1; q < P; ++q) acc = acc + part[q];
+                }
+                ++nbatch;
+            }
+            if (mine) *reinterpret_cast<float4*>(tot + xu * W + xc4 * 4) = acc;
             __syncthreads();  // the batch's sums visible
 #pragma unroll
             for (int u = 0; u < BT; ++u) {
@@ -594,7 +655,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
 #pragma unroll
                         for (int i = 0; i < L::RPT; ++i) p.dk[bth * M + rg + L::RG * i] = dkin[u][i] + dkz[i];
                     }
-                    if (tid == 0) {
+                    if (tid == 0 && pidx == 0) {
                         p.dmu[bth] = ssum.y;
                         if (!p.f.gamma_per_slot) p.dgamma[bth] = ssum.z;
                     }
@@ -617,28 +678,36 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     for (int i = 0; i < L::RPT; ++i) *reinterpret_cast<float4*>(dsi + el(i)) = dR[i];
 }
 
-template <int M, int D, int NT, typename TIn>
+template <int N>
+__global__ void osr_bwd_fill_ints(int* x, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) x[i] = N;
+}
+
+template <int M, int D, int NT, typename TIn, int P>
 static void launch_bwd_dy(const BwdParams& p, dim3 grid, size_t lds, hipStream_t st) {
     if (p.f.lin1) {
         if (p.dy_bf16)
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, true, true>), grid, dim3(NT), lds, st, p);
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, true, true, P>), grid, dim3(NT), lds, st, p);
         else
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, true, false>), grid, dim3(NT), lds, st, p);
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, true, false, P>), grid, dim3(NT), lds, st, p);
     } else {
         if (p.dy_bf16)
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, false, true>), grid, dim3(NT), lds, st, p);
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, false, true, P>), grid, dim3(NT), lds, st, p);
         else
-            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, false, false>), grid, dim3(NT), lds, st, p);
+            hipLaunchKernelGGL((osr_bwd_kernel<M, D, NT, TIn, false, false, P>), grid, dim3(NT), lds, st, p);
     }
 }
 
-// Launch for one slot count M (instantiated in osr_bwd_m<M>.hip).
-template <int M, int D>
-static int launch_bwd_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
+// Launch for one slot count M, width D and P workgroups per sequence (M / P
+// slot rows each; P > 1 only with bf16 inputs and the state-passing kernel's
+// arrays, which the host ensures).
+template <int M, int D, int P>
+static int launch_bwd_mdp(const BwdParams& p, bool in_bf16, hipStream_t st) {
     constexpr int TPR = D / 4;
-    constexpr int NT = (M * TPR < 512) ? M * TPR : 512;
-    const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H));
-    using L = ValuLayout<M, D, NT>;
+    constexpr int NT = ((M / P) * TPR < 512) ? (M / P) * TPR : 512;
+    const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H) * P);
+    using L = ValuLayout<M / P, D, NT>;
     constexpr int BT = TokBatch<L>::BT, W = D + 4;
     constexpr size_t static_lds = (2 * BT * L::NW * W + BT * W) * sizeof(float);  // red, tot
     const size_t h_lds = static_cast<size_t>(p.f.chunk) * D * sizeof(float);      // the chunk's h
@@ -647,13 +716,38 @@ static int launch_bwd_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
     BwdParams q = p;
     q.stage_gk = p.chain_c != nullptr && static_lds + h_lds + gk_lds <= 128 * 1024;
     const size_t lds = h_lds + (q.stage_gk ? gk_lds : 0);
-    // the first linearisation is its own instantiation, so the default carries none of its work;
-    // so is a bf16 dy (its loads then need no branch)
-    if (in_bf16)
-        launch_bwd_dy<M, D, NT, uint16_t>(q, grid, lds, st);
-    else
-        launch_bwd_dy<M, D, NT, float>(q, grid, lds, st);
+    if constexpr (P > 1) {
+        // progress counters to zero (they count the batches of this call)
+        const int nflags = p.f.B * p.f.H * P * XFLAG_STRIDE;
+        hipLaunchKernelGGL(osr_bwd_fill_ints<0>, dim3((nflags + 255) / 256), dim3(256), 0, st, p.xflags, nflags);
+        launch_bwd_dy<M, D, NT, uint16_t, P>(q, grid, lds, st);
+    } else {
+        // the first linearisation is its own instantiation, so the default carries none of its work;
+        // so is a bf16 dy (its loads then need no branch)
+        if (in_bf16)
+            launch_bwd_dy<M, D, NT, uint16_t, 1>(q, grid, lds, st);
+        else
+            launch_bwd_dy<M, D, NT, float, 1>(q, grid, lds, st);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+template <int M, int D>
+static int launch_bwd_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
+    if (p.split_p > 1 && (!in_bf16 || p.chain_c == nullptr || p.xbuf == nullptr)) return -3;
+    switch (p.split_p) {
+        case 1: return launch_bwd_mdp<M, D, 1>(p, in_bf16, st);
+        case 2:
+            if constexpr (M / 2 >= 16) return launch_bwd_mdp<M, D, 2>(p, in_bf16, st);
+            return -3;
+        case 4:
+            if constexpr (M / 4 >= 16) return launch_bwd_mdp<M, D, 4>(p, in_bf16, st);
+            return -3;
+        case 8:
+            if constexpr (M / 8 >= 16) return launch_bwd_mdp<M, D, 8>(p, in_bf16, st);
+            return -3;
+        default: return -3;
+    }
 }
 
 template <int M>

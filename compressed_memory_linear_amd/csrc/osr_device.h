@@ -122,6 +122,22 @@ __device__ __forceinline__ void st_y1(void* y, int64_t i, float val, int y_bf16)
 
 // Streaming (non-temporal) 16-byte loads/stores of fp32 state rows.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Hand-offs between the workgroups of one launch (a sequence split over
+// several workgroups).  The data goes with the device-coherence bit (sc1):
+// such accesses bypass the non-coherent caches (the per-XCD L2 included), so
+// readers on any XCD see the data once the writer's stores have retired; no
+// write-back or invalidation of the rest of the cache is needed.  Buffer
+// instructions keep them ordinary loads and stores for the compiler (issued
+// back to back).  A writer's stores retire (s_waitcnt vmcnt(0)) before it
+// sets its progress counter with an agent-scope atomic store; a reader polls
+// the counter with agent-scope atomic loads, at most XSPIN times.
+constexpr int XFLAG_STRIDE = 32;  // ints between progress counters (128 bytes)
+constexpr int XSPIN = 1 << 22;    // polls before a wait gives up (never reached when all run)
+constexpr int XCPOL_SC1 = 16;     // cache-policy operand: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(float* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
+}
 __device__ __forceinline__ float4 ld_nt4(const float* p) {
     const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
     return make_float4(v.x, v.y, v.z, v.w);

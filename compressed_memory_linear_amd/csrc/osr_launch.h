@@ -58,8 +58,19 @@ struct BwdParams {
     // workspace layout ([B*H*NC][rows/16][C/16][64 lanes][4], rows = m or d):
     // g, kappa, h, e (first linearisation) and c, beta; |h|^2 as [B*H*NC][C].
     const float *chain_g, *chain_k, *chain_h, *chain_e, *chain_c, *chain_b, *chain_hh;
+    // Slot rows split over split_p workgroups per sequence (1: not split; needs
+    // the state-passing kernel's arrays): per (b,h), two batch parities x
+    // split_p parts of one batch's sums over slots, and split_p progress counters.
+    int split_p;
+    float* xbuf;
+    int* xflags;
 };
 size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C);
+// Workgroups per sequence of the backward (slot rows split between them), and
+// the hand-off buffers that takes (0 for one).  chain: the state-passing
+// kernel supplies the chunk-start states and records; chain_wgs: 0 automatic, 1 one.
+int bwd_split_p(int B, int H, int m, bool chain, int chain_wgs);
+size_t bwd_xchg_bytes(int B, int H, int d, int P);
 int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 
 // Layer glue (HBM-bound streaming kernels).  pre: q = conv4(xq), k = conv4(xk)

@@ -165,19 +165,8 @@ template <int M, int D>
 constexpr int64_t xchg_floats() {
     return static_cast<int64_t>(M / 16) * (D / 16) * 64 * 4 + (M / 16) * 64;
 }
-constexpr int XFLAG_STRIDE = 32;  // ints between progress counters (128 bytes)
-constexpr int XSPIN = 1 << 22;    // polls before a wait gives up (never reached when all run)
-
-// Hand-off accesses with the device-coherence bit (sc1): they bypass the
-// non-coherent caches (the per-XCD L2 included), so readers on any XCD see
-// the data once the writer's stores have retired; no write-back or
-// invalidation of the rest of the cache is needed.  Progress counters: one
-// per (sequence, workgroup, wave), XFLAG_STRIDE ints apart.  Buffer instructions keep
-// them ordinary loads and stores for the compiler (issued back to back).
-constexpr int XCPOL_SC1 = 16;  // cache-policy operand: sc1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t xrsrc(float* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(base, 0, static_cast<int>(bytes), 0x00020000);
-}
+// Progress counters of the hand-off: one per (sequence, workgroup, wave),
+// XFLAG_STRIDE ints apart (XFLAG_STRIDE, XSPIN, XCPOL_SC1, xrsrc: osr_device.h).
 // Wait until wave w of workgroup q of sequence bh has published chunk s
 // (its counter passed s); gives up after XSPIN polls (broken = true).
 template <class G>

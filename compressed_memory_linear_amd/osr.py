@@ -325,14 +325,15 @@ def lattice_osr_bwd_workspace_bytes(desc: lattice_osr_desc, chunk_size: int) -> 
 
 def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size: int, *,
                             mode: int = MODE_DEC, grads: Optional[dict] = None, workspace=None,
-                            stream=None, linearisation: int = LIN2) -> dict:
+                            stream=None, linearisation: int = LIN2, chain_wgs: int = WGS_AUTO) -> dict:
     """Backward of the chunk-wise forward: gradients of sum(dy*y) +
     sum(dstate_out*state_out) with respect to q, k, v, gamma, mu and
     state_in.  dy has y's shape (float32 or bfloat16), dstate_out the state's.
     Returns a dict of float32 tensors dq, dk, dv, dgamma, dmu, dstate_in
-    (allocated unless passed in `grads`)."""
+    (allocated unless passed in `grads`).  chain_wgs: WGS_ONE keeps each
+    sequence on one workgroup (speed only)."""
     lib = load_library()
-    desc = _desc_from(q, k, v, gamma, mu, state_in, dy.dtype, mode, linearisation)
+    desc = _desc_from(q, k, v, gamma, mu, state_in, dy.dtype, mode, linearisation, chain_wgs=chain_wgs)
     _check_tensor("dy", dy, tuple(v.shape), None, q.device)
     _check_tensor("dstate_out", dstate_out, tuple(state_in.shape), torch.float32, q.device)
     named = (("q", q), ("k", k), ("v", v), ("gamma", gamma), ("mu", mu), ("state_in", state_in))

@@ -313,7 +313,33 @@ def test_bwd_workspace_formula():
                         per_chunk = m * dd + (3 if lin == osr.LIN1 else 2) * m * C + dd * C
                         per_chunk += 2 * m * C + C  # c, beta and |h|^2 kept for the backward
                         want += B * H * (T // C) * per_chunk * 4
+                        want += _bwd_xchg(B * H, m, dd)
                     assert osr.lattice_osr_bwd_workspace_bytes(d, C) == want, (B, T, H, m, dd, C, in_dtype, mode, lin)
+
+
+def _bwd_xchg(bh, m, d):
+    """Hand-off buffers of the backward split over P workgroups per sequence
+    (the largest P in 1, 2, 4, 8 with m / P >= 16 and B H P <= 256): per (b,h)
+    2 P parts of 8 (d + 4) floats and P counters of 128 bytes."""
+    P = 1
+    while P < 8 and m // (2 * P) >= 16 and bh * 2 * P <= 256:
+        P *= 2
+    return 0 if P == 1 else bh * (2 * P * 8 * (d + 4) * 4 + P * 128)
+
+
+def test_bwd_split_workspace():
+    """The split's hand-off buffers follow the descriptor's chain_wgs: ONE,
+    or a layout without the state-passing kernel's arrays, adds none."""
+    for (B, H, m, dd, P) in ((1, 16, 128, 128, 8), (4, 8, 64, 64, 4), (8, 16, 64, 128, 2), (16, 16, 64, 64, 1),
+                             (1, 4, 16, 32, 1), (2, 2, 32, 16, 2)):
+        T, C = 256, 64
+        auto = osr.make_desc(B, T, H, m, dd)
+        one = osr.make_desc(B, T, H, m, dd, chain_wgs=osr.WGS_ONE)
+        extra = 0 if P == 1 else B * H * (2 * P * 8 * (dd + 4) * 4 + P * 128)
+        assert extra == _bwd_xchg(B * H, m, dd)
+        assert osr.lattice_osr_bwd_workspace_bytes(auto, C) - osr.lattice_osr_bwd_workspace_bytes(one, C) == extra
+        f32 = osr.make_desc(B, T, H, m, dd, in_dtype=osr.F32)
+        assert osr.lattice_osr_bwd_workspace_bytes(f32, C) == B * H * 4 * ((T // C + 1 + C) * m * dd + C * (2 * m + 4))
 
 
 def test_bwd_null_pointers_and_shapes():

@@ -59,13 +59,14 @@ def _upstream(inp, seed, dy_bf16=False):
     return dy, dso
 
 
-def _gpu_bwd(inp, dy, dso, C, mode, dy_bf16=False, lin=osr.LIN2):
+def _gpu_bwd(inp, dy, dso, C, mode, dy_bf16=False, lin=osr.LIN2, chain_wgs=osr.WGS_AUTO):
     t = osr.to_device(inp, "cuda")
     dyt = torch.from_numpy(dy).cuda()
     if dy_bf16:
         dyt = dyt.to(torch.bfloat16)   # exact: dy already holds bf16 values
     g = osr.lattice_osr_bwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], dyt,
-                                    torch.from_numpy(dso).cuda(), C, mode=mode, linearisation=lin)
+                                    torch.from_numpy(dso).cuda(), C, mode=mode, linearisation=lin,
+                                    chain_wgs=chain_wgs)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in g.items()}
 
@@ -272,3 +273,33 @@ def test_bwd_first_linearisation_headline_sampled():
     got = _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC, lin=osr.LIN1)
     bh = [(0, 2), (3, 6)]
     _check(inp, got, _oracle(inp, dy, dso, 64, osr.MODE_DEC, bh, lin=ob.LIN1), bh=bh)
+
+
+# The slot rows of a sequence split over P workgroups (bf16 inputs, C >= 16,
+# decoding and similarity objectives; P = 8, 4, 2 below): each batch's sums
+# over slots are exchanged between them and added in workgroup order, so the
+# result is one workgroup's up to the order of those sums (fp32 rounding).
+SPLIT_CASES = [(1, 2, 128, 128, 64, 256), (4, 8, 64, 64, 64, 256), (2, 3, 32, 64, 16, 128), (1, 3, 64, 128, 32, 128)]
+
+
+@pytest.mark.parametrize("B,H,m,d,C,T", SPLIT_CASES)
+@pytest.mark.parametrize("mode,lin", [(osr.MODE_DEC, osr.LIN2), (osr.MODE_SIM, osr.LIN2), (osr.MODE_DEC, osr.LIN1)])
+def test_bwd_split_over_workgroups(B, H, m, d, C, T, mode, lin):
+    _say(f"bwd slot rows split over workgroups B{B} H{H} m{m} d{d} C{C} T{T} mode{mode} lin{lin}")
+    inp = synth.make_inputs(B, T, H, m, d, seed=2100 + m + d + C + mode, in_dtype=synth.BF16)
+    dy, dso = _upstream(inp, 2200 + m + d)
+    split = _gpu_bwd(inp, dy, dso, C, mode, lin=lin)
+    one = _gpu_bwd(inp, dy, dso, C, mode, lin=lin, chain_wgs=osr.WGS_ONE)
+    for key in split:
+        assert _rel(split[key], one[key]) <= 1e-5, key
+    _check(inp, split, _oracle(inp, dy, dso, C, mode, lin=ob.LIN1 if lin == osr.LIN1 else ob.LIN2))
+
+
+def test_bwd_split_deterministic():
+    _say("bwd split over workgroups: bit-identical reruns, B1 H4 T512 m=d=128 C64")
+    inp = synth.make_inputs(1, 512, 4, 128, 128, seed=2300, in_dtype=synth.BF16)
+    dy, dso = _upstream(inp, 2301)
+    a = _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC)
+    b = _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
