@@ -263,7 +263,14 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * chunk_size >= 16 (decoding and similarity objectives, whose chunk-start
  * states then come from the matrix-core state-passing kernel), that kernel's
  * per-chunk arrays: 4 (m d + 4 m C + d C + C) bytes per chunk (4 m C more
- * with LATTICE_OSR_LIN1).  The remaining rules (shapes,
+ * with LATTICE_OSR_LIN1).  On that path, with desc->chain_wgs =
+ * LATTICE_OSR_WGS_AUTO, the slot rows of each sequence are split over P
+ * workgroups (the largest P in {1, 2, 4, 8} with m / P >= 16 and B*H*P <= 256;
+ * fewer if the device has fewer compute units) that exchange each batch of
+ * tokens' sums over slots: the workspace then ends with their hand-off
+ * buffers, B*H*(2 P 8 (d + 4) * 4 + 128 P) bytes.  The result equals one
+ * workgroup's (LATTICE_OSR_WGS_ONE) up to the order of those fp32 sums;
+ * reruns are bit-identical.  The remaining rules (shapes,
  * chunk sizes, alignment of the inputs, status codes, asynchrony) are those
  * of lattice_osr_fwd_chunked.
  */
