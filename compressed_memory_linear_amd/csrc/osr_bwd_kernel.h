@@ -595,19 +595,17 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                                                            static_cast<uint32_t>(pidx * XW) * 4 + off, 0, XCPOL_SC1);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's part store has retired
                 __syncthreads();  // ... and every thread's
-                if (tid == 0) {
+                if (tid == 0)
                     __hip_atomic_store(p.xflags + (bh * P + pidx) * XFLAG_STRIDE, nbatch + 1, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
-                    for (int q = 0; q < P; ++q) {
-                        if (q == pidx || xbroken) continue;
-                        const int* f = p.xflags + (bh * P + q) * XFLAG_STRIDE;
-                        int n = 0;
-                        while (__hip_atomic_load(const_cast<int*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <=
-                               nbatch) {
-                            if (++n >= XSPIN) {
-                                xbroken = true;
-                                break;
-                            }
+                // thread q polls workgroup q's counter (all P at once, one round trip when they are set)
+                if (tid < P && tid != pidx && !xbroken) {
+                    const int* f = p.xflags + (bh * P + tid) * XFLAG_STRIDE;
+                    int n = 0;
+                    while (__hip_atomic_load(const_cast<int*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= nbatch) {
+                        if (++n >= XSPIN) {
+                            xbroken = true;
+                            break;
                         }
                     }
                 }
