@@ -382,7 +382,8 @@ def main() -> int:
                                                      (SMALL, "chunked", 4, 3, 0, 0),
                                                      (SMALL, "chunked", 64, 10, 2, 0),
                                                      (SMALL, "chunked", 64, 10, 0, 1),
-                                                     (SMALL, "backward", 64, 2, 0, 0)):
+                                                     (SMALL, "backward", 64, 2, 0, 0),
+                                                     (HEADLINE, "backward", HEADLINE_CHUNK, 2, 0, 0)):
             # the small workload (51 MB) fits the 256 MB Infinity Cache: rotate 8 input copies
             c = Case(name, entry, chunk, copies=8 if name == SMALL and entry == "chunked" else 1,
                      mode=mode, linearisation=lin)
