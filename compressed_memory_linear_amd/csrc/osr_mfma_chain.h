@@ -668,9 +668,24 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
             if (lane == 0) __hip_atomic_store(myflag, s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const uint32_t t_off = ((M / 16) * DB * 64 * 4 + w * 64 + lane) * 4;
             if constexpr (!ENC && !LIN1) {
-                // Part q is loaded as soon as its counter shows it, so the
-                // parts that are ready stream in while a later one is still
-                // computed; the workgroup's own part comes from its registers.
+                // Lane j < P - 1 polls the counter of the j-th other workgroup, all
+                // in one round trip; then the parts in q order, the workgroup's own
+                // from its registers.
+                if (!xbroken) {
+                    const int j = lane < P - 1 ? lane : 0;
+                    const int qj = j < pidx ? j : j + 1;
+                    const int* f = p.xflags + ((bh * P + qj) * G::NWS + w) * XFLAG_STRIDE;
+                    int n = 0;
+                    while (true) {
+                        const int v = __hip_atomic_load(const_cast<int*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (__all(lane >= P - 1 || v > s)) break;
+                        if (++n >= XSPIN) {
+                            xbroken = true;
+                            break;
+                        }
+                    }
+                }
+                asm volatile("" ::: "memory");  // the reads below stay after the waits
 #pragma unroll
                 for (int q = 0; q < P; ++q) {
                     if (q == pidx) {
@@ -680,8 +695,6 @@ __global__ __launch_bounds__(4 * M * (PAIR ? 2 : 1)) void osr_chain_kernel(Param
                             for (int e = 0; e < 4; ++e) acc[db][e] = fmaf(acc[db][e], aend, u[db][e]);
                         continue;
                     }
-                    if (!xbroken) xwait<G>(p, bh, P, q, w, s, xbroken);
-                    asm volatile("" ::: "memory");  // part q's reads stay after its wait
                     const uint32_t base = static_cast<uint32_t>(q * xs) * 4;
                     const float tq = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xr, base + t_off, 0, XCPOL_SC1));
                     f32x4 uq[DB];
