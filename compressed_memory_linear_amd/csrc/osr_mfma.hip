@@ -84,23 +84,26 @@ size_t chain_xchg_bytes(int B, int H, int m, int d, int P) {
 // Chunk ranges of an overlapped read-out (split schedule).  With at most 64
 // state-passing workgroups (three quarters of the compute units or more left
 // to the read-out; at 128, B8 H16 T4096 m64 d128 C64, it measured no faster)
-// and a multiple of 64 chunks: 8 ranges of 16, 16, 16, 8, 4, 2, 1
-// and 1 64ths of the chunks.  A range's read-out (on the side stream) then
-// takes no longer than the next range's state passing, even where it shares
-// the device with it, and the read-out of the last range, the only one not
-// hidden, is 1/64 of the whole; each range costs one event hand-off (~7 us).
-// Else 1 (no overlap).  Returns the ranges' chunk ends in `end`.
+// and a multiple of 64 chunks: 4 ranges of 48, 12, 3 and 1 64ths of the
+// chunks.  A range's read-out (on the side stream, where it runs at about a
+// quarter of the state passing's time per chunk while sharing the device) then
+// takes no longer than the next range's state passing, and the read-out of
+// the last range, the only one not hidden, is 1/64 of the whole; each range
+// boundary costs one event hand-off (~6.5 us), hence no more ranges than
+// that.  Else 1 (no overlap).  Returns the ranges' chunk ends in `end`.
 int overlap_ranges(int B, int H, int m, int d, int C, int T, int chain_wgs, int readout_overlap, int* end) {
     const int NC = T / C;
     const int64_t wgs = static_cast<int64_t>(B) * H * chain_split_p(B, H, m, d, C, chain_wgs);
     if (readout_overlap != 0 || wgs > 64 || NC < 64 || NC % 64 != 0) return 1;
-    static constexpr int kParts[kMaxRanges] = {16, 16, 16, 8, 4, 2, 1, 1};
+    static constexpr int kParts[] = {48, 12, 3, 1};
+    constexpr int kN = sizeof(kParts) / sizeof(kParts[0]);
+    static_assert(kN <= kMaxRanges, "ranges");
     int n = 0;
-    for (int k = 0; k < kMaxRanges; ++k) {
+    for (int k = 0; k < kN; ++k) {
         n += kParts[k] * (NC / 64);
         if (end) end[k] = n;
     }
-    return kMaxRanges;
+    return kN;
 }
 
 // The side stream and events of the overlapped read-out, one set per device,

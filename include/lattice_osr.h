@@ -119,8 +119,8 @@ extern "C" {
 /* Read-out of the split schedule overlapped with its state passing. */
 #define LATTICE_OSR_OVERLAP_AUTO 0 /* where the state passing takes at most 64 workgroups and
                                       there are at least 64 chunks (a multiple of 64): the chunks
-                                      in 8 ranges of shrinking length (1/4, 1/4, 1/4, 1/8, 1/16,
-                                      1/32, 1/64, 1/64); each range's read-out runs on the
+                                      in 4 ranges of shrinking length (48, 12, 3 and 1 64ths of
+                                      the chunks); each range's read-out runs on the
                                       library's side stream for the device while the next range's
                                       state passing runs on hip_stream, which waits for the side
                                       stream before the call's work ends.  Same results, bit for

@@ -514,7 +514,7 @@ def test_chain_workgroup_split_deterministic():
 
 
 # The read-out overlapped with the state passing by chunk ranges (64 chunks or
-# a multiple: 8 ranges, the state handed from range to range unprojected):
+# a multiple: 4 ranges, the state handed from range to range unprojected):
 # the same kernels over the same chunks, so the results equal those of the
 # serial launch bit for bit, and meet the bar against the oracle.
 OVERLAP_CASES = [  # (B, H, m, d, C, chunks): workgroups per sequence 4, 2 and 1
