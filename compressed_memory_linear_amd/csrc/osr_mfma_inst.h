@@ -91,22 +91,29 @@ static int launch_md(bool split, const Params& p, hipStream_t st, const Overlap*
             return launch_readout_md<M, D>(p, st);
         }
         Params q = p;
-        for (int k = 0; k < ov->nseg; ++k) {
+        int rc = 0;
+        for (int k = 0; k < ov->nseg && rc == 0; ++k) {
             q.n_begin = k == 0 ? 0 : ov->end[k - 1];
             q.n_end = ov->end[k];
-            int rc = launch_chain_m<M>(D, q, st);
-            if (rc) return rc;
+            rc = launch_chain_m<M>(D, q, st);
+            if (rc) break;
             if (k + 1 < ov->nseg) {
-                if (hipEventRecord(ov->ev_chain, st) != hipSuccess) return -5;
-                if (hipStreamWaitEvent(ov->side, ov->ev_chain, 0) != hipSuccess) return -5;
+                if (hipEventRecord(ov->ev_chain, st) != hipSuccess ||
+                    hipStreamWaitEvent(ov->side, ov->ev_chain, 0) != hipSuccess) {
+                    rc = -5;
+                    break;
+                }
                 rc = launch_readout_md<M, D>(q, ov->side);
             } else {
                 rc = launch_readout_md<M, D>(q, st);
             }
-            if (rc) return rc;
         }
-        if (hipEventRecord(ov->ev_side, ov->side) != hipSuccess) return -5;
-        return hipStreamWaitEvent(st, ov->ev_side, 0) == hipSuccess ? 0 : -5;
+        // the caller's stream waits for whatever reached the side stream, on
+        // failure too (the caller may reuse the workspace once its stream is done)
+        if (hipEventRecord(ov->ev_side, ov->side) != hipSuccess ||
+            hipStreamWaitEvent(st, ov->ev_side, 0) != hipSuccess)
+            rc = rc ? rc : -5;
+        return rc;
     }
     return c0 == 32 ? launch_fused<M, D, 32>(p, st) : launch_fused<M, D, 16>(p, st);
 }
