@@ -285,11 +285,25 @@ def cpu_baseline(name: str, chunk: int, budget_s: float = 12.0) -> dict:
         _, _, threads = oracle.osr_forward(*args, chunk_size=chunk, return_threads=True)
         total += time.perf_counter() - t0
         reps += 1
-    return {"value": inp.head_tokens * reps / total, "unit": "head-tokens/s", "cores": threads,
-            "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
-            "sample": f"whole workload {name} (B*H*T = {inp.head_tokens} head-tokens), "
-                      f"{reps} repetition(s), {total:.2f} s, fp64 C with {threads} threads over the "
-                      f"{inp.B * inp.H} (b,h) sequences (one thread per sequence at most)"}
+    out = {"value": inp.head_tokens * reps / total, "unit": "head-tokens/s", "cores": threads,
+           "kind": "oracle", "cpu_model": cpu_model(), "host_cpus": os.cpu_count(),
+           "sample": f"whole workload {name} (B*H*T = {inp.head_tokens} head-tokens), "
+                     f"{reps} repetition(s), {total:.2f} s, fp64 C with {threads} threads over the "
+                     f"{inp.B * inp.H} (b,h) sequences (one thread per sequence at most)"}
+    # the tiny fp32 workload on one thread, at each of its chunk sizes
+    tiny = synth.workload_inputs("tiny_f32_m16d32_t64")
+    targs = tiny.values_f64()
+    single = {}
+    for c in (1, 4, 16, 64):
+        reps, total = 0, 0.0
+        while reps == 0 or (total < 0.5 and reps < 10000):
+            t0 = time.perf_counter()
+            oracle.osr_forward(*targs, chunk_size=c, nthreads=1)
+            total += time.perf_counter() - t0
+            reps += 1
+        single[f"C{c}"] = tiny.head_tokens * reps / total
+    out["tiny_f32_m16d32_t64_one_thread"] = {"unit": "head-tokens/s", "cores": 1, **single}
+    return out
 
 
 def main() -> int:
