@@ -218,7 +218,7 @@ size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
     if (chain)
         n += osr::mfma_chain_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1) +
              bwd_chain_extra_bytes(d, C);
-    return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, osr::bwd_split_p(d->B, d->H, d->m, chain, d->chain_wgs));
+    return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, osr::bwd_split_p(d->B, d->H, d->m, d->d, C, chain, d->chain_wgs));
 }
 
 // Shape rules of the backward: those of the chunked forward.
@@ -463,13 +463,15 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
     }
     // slot rows split over workgroups: every workgroup of a sequence must be resident
     // at once (they wait for each other), so no more workgroups than compute units
-    p.split_p = osr::bwd_split_p(desc->B, desc->H, desc->m, chain, desc->chain_wgs);
+    p.split_p = osr::bwd_split_p(desc->B, desc->H, desc->m, desc->d, chunk_size, chain, desc->chain_wgs);
     p.xbuf = nullptr;
     p.xflags = nullptr;
     if (p.split_p > 1) {
         const size_t xoff = need - osr::bwd_xchg_bytes(desc->B, desc->H, desc->d, p.split_p);
         const int64_t cus = device_cus();
-        while (p.split_p > 1 && static_cast<int64_t>(desc->B) * desc->H * p.split_p > cus) p.split_p /= 2;
+        while (p.split_p > 1 && (static_cast<int64_t>(desc->B) * desc->H * p.split_p > cus ||
+                                 !osr::bwd_split_fits(desc->m, desc->d, chunk_size, p.split_p)))
+            p.split_p /= 2;
         if (p.split_p > 1) {
             p.xbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + xoff);
             p.xflags = reinterpret_cast<int*>(p.xbuf + static_cast<size_t>(desc->B) * desc->H * 2 * p.split_p * 8 *

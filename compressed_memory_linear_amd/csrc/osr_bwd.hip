@@ -37,13 +37,28 @@ size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C) {
 // that exchange those sums.  Where the state-passing kernel supplies the
 // chunk-start states and records (bf16 inputs, C >= 16, decoding and similarity
 // objectives): the largest P in {1, 2, 4, 8} with at least 16 rows per
-// workgroup and B*H*P <= 256 (one workgroup per compute unit, all resident).
-int bwd_split_p(int B, int H, int m, bool chain, int chain_wgs) {
+// workgroup, B*H*P <= 256 (one workgroup per compute unit, all resident) and
+// the workgroup's LDS (exchange buffers, the chunk's h and, at <= 32 rows and
+// <= 2 per thread, its rows' records and, at d <= 64, the chunk's dy; the
+// kernel's layout) within 160 KiB.
+bool bwd_split_fits(int m, int d, int C, int P) {
+    const int ML = m / P, TPR = d / 4, NT = ML * TPR < 512 ? ML * TPR : 512, RG = NT / TPR, RPT = ML / RG;
+    const int NW = NT / 64, W = d + 4;
+    int BT = RPT <= 2 ? 8 : (RPT <= 4 ? 4 : 2);
+    if (TPR == 32 && BT > 4) BT = 4;
+    size_t lds = (2 * static_cast<size_t>(BT) * NW * W + static_cast<size_t>(BT) * W) * 4 + static_cast<size_t>(C) * d * 4;
+    if (P > 1 && RPT <= 2 && ML <= 32)
+        lds += ((5 * static_cast<size_t>(ML) + 3) * C + (d <= 64 ? static_cast<size_t>(C) * d : 0)) * 4;
+    return lds <= 160 * 1024;
+}
+
+int bwd_split_p(int B, int H, int m, int d, int C, bool chain, int chain_wgs) {
     if (!chain || chain_wgs != 0) return 1;
     const int64_t bh = static_cast<int64_t>(B) * H;
-    int P = 1;
-    while (P < 8 && m / (2 * P) >= 16 && bh * 2 * P <= 256) P *= 2;
-    return P;
+    int best = 1;
+    for (int P = 2; P <= 8 && m / P >= 16 && bh * P <= 256; P *= 2)
+        if (bwd_split_fits(m, d, C, P)) best = P;
+    return best;
 }
 
 // Per (b,h): 2 parities x P parts of at most 8 tokens x (d + 4) floats, then P

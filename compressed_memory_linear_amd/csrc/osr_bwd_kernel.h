@@ -170,6 +170,49 @@ __device__ __forceinline__ void load_rev(RevIn<L::RPT>& x, const BwdParams& p, c
 // P > 1: the slot rows of a sequence split over P workgroups (M / P rows
 // each); they exchange each batch's sums over slots (below).  Only with the
 // state-passing kernel's chunk-start states and records (the host ensures it).
+// Split workgroups (P > 1, at most 32 rows, 2 per thread): the chunk's per-row
+// records of this workgroup's rows, and (d <= 64) the chunk's dy, are staged
+// in LDS at the chunk start, all loads in flight at once, so that per token
+// only the state before the token comes from memory (from L2, where the
+// chunk's rerun left it).  Layout, floats: [5][C][ML] c, beta, k, q, gamma (per
+// slot); [3][C] mu, |h|^2, gamma (per token); then (d <= 64) [C][D] dy.
+template <int ML, int D>
+struct StagedRec {
+    static constexpr int A_C = 0, A_B = 1, A_K = 2, A_Q = 3, A_G = 4;
+    static constexpr bool DY = D <= 64;
+    __host__ __device__ static constexpr int64_t floats(int C) {
+        return (5 * static_cast<int64_t>(ML) + 3) * C + (DY ? static_cast<int64_t>(C) * D : 0);
+    }
+};
+
+template <class L, int ML, int D, bool DYB>
+__device__ __forceinline__ void load_rev_staged(RevIn<L::RPT>& x, const BwdParams& p, const float* srec,
+                                                const float* rpre, int64_t bth, int tau, int rgl, int cg, int el0) {
+    using SR = StagedRec<ML, D>;
+    const int C = p.f.chunk;
+    const float* tok = srec + 5 * static_cast<int64_t>(ML) * C;
+#pragma unroll
+    for (int i = 0; i < L::RPT; ++i) {
+        const int rl = rgl + L::RG * i;
+        x.c[i] = srec[(SR::A_C * C + tau) * ML + rl];
+        x.beta[i] = srec[(SR::A_B * C + tau) * ML + rl];
+        x.in.k[i] = srec[(SR::A_K * C + tau) * ML + rl];
+        x.in.q[i] = srec[(SR::A_Q * C + tau) * ML + rl];
+        // (a per-token gamma: its own array, selected by address)
+        x.in.g[i] = (p.f.gamma_per_slot ? srec + (SR::A_G * C + tau) * ML + rl : tok + 2 * C + tau)[0];
+    }
+    x.in.mu = tok[tau];
+    x.hh = tok[C + tau];
+    if constexpr (SR::DY)
+        x.dy = *reinterpret_cast<const float4*>(tok + 3 * C + tau * D + cg * 4);
+    else if constexpr (DYB)
+        x.dy = ld4<uint16_t>(static_cast<const uint16_t*>(p.dy), bth * D + cg * 4);
+    else
+        x.dy = ld4<float>(static_cast<const float*>(p.dy), bth * D + cg * 4);
+#pragma unroll
+    for (int i = 0; i < L::RPT; ++i) x.rp[i] = *reinterpret_cast<const float4*>(rpre + el0 + i * L::RG * D);
+}
+
 template <int M, int D, int NT, typename TIn, bool LIN1, bool DYB, int P = 1>
 __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     static_assert(P == 1 || (M / P >= 16 && sizeof(TIn) == 2), "split: bf16 inputs, 16 rows or more each");
@@ -185,6 +228,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     constexpr bool DBUF = L::RPT <= 2;
     extern __shared__ __attribute__((aligned(16))) float hbuf[];  // [C][D], dynamic
     float* const gst = hbuf + p.f.chunk * D;  // [2 or 3][M*C]: staged gates (stage_gk)
+    float* const srec = gst + (p.stage_gk ? (LIN1 ? 3 : 2) * M * p.f.chunk : 0);  // StagedRec (STG)
     __shared__ __attribute__((aligned(16))) float red[2 * BT * L::NW * W];
     __shared__ __attribute__((aligned(16))) float tot[BT * W];  // a batch's sums over slots
     static_assert(BT * (D / 4 + 1) <= NT, "one float4 of a batch's sums per thread");
@@ -193,7 +237,10 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     const int b = bh / p.f.H, hd = bh % p.f.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // rg: the (global) slot row of this thread's first row
-    const int cg = tid % L::TPR, rg = pidx * (M / P) + tid / L::TPR;
+    const int cg = tid % L::TPR, rgl = tid / L::TPR, rg = pidx * (M / P) + rgl;
+    constexpr int ML = M / P;
+    // staged records (StagedRec): at most 32 rows and 2 rows per thread (more spilled)
+    constexpr bool STG = P > 1 && L::RPT <= 2 && ML <= 32;
     const int T = p.f.T, C = p.f.chunk, NC = T / C;
     const int mode = p.f.mode;
     const int64_t tstride = p.f.H;  // consecutive tokens of one (b,h) are H rows apart
@@ -297,6 +344,87 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                     for (int j = 0; j < 2; ++j)
                         if (a < narr && base + j * NT < n4)
                             reinterpret_cast<float4*>(gst + a * M * C)[base + j * NT] = v[a][j];
+            }
+        }
+        if constexpr (STG) {
+            // this workgroup's rows of the chunk's records (and dy): 8 loads in flight per
+            // thread before any LDS write (clamped, unconditional); visible after the
+            // barrier that ends the h step below
+            using SR = StagedRec<ML, D>;
+            const int64_t chc = (static_cast<int64_t>(bh) * NC + n) * M * C;
+            const int row0 = pidx * ML;
+            constexpr int G8 = 8;
+            // fp32 sources: c, beta [2][C][ML] (the state-passing kernel's arrays), |h|^2 [C]
+            const int nf = 2 * ML * C + C;
+            for (int base = tid; base < nf; base += G8 * NT) {
+                float v[G8];
+#pragma unroll
+                for (int g = 0; g < G8; ++g) {
+                    const int idx = min(base + g * NT, nf - 1);
+                    const int a = idx / (ML * C), r = idx % (ML * C);
+                    const float* src = a == 0   ? p.chain_c + chc + gate_frag(row0 + r % ML, r / ML, C)
+                                       : a == 1 ? p.chain_b + chc + gate_frag(row0 + r % ML, r / ML, C)
+                                                : p.chain_hh + (static_cast<int64_t>(bh) * NC + n) * C + (idx - 2 * ML * C);
+                    v[g] = *src;
+                }
+#pragma unroll
+                for (int g = 0; g < G8; ++g) {
+                    const int idx = base + g * NT;
+                    if (idx < nf) srec[idx < 2 * ML * C ? idx : 5 * ML * C + C + (idx - 2 * ML * C)] = v[g];
+                }
+            }
+            // input sources: k, q, gamma [3][C][ML], then mu and a per-token gamma [2][C]
+            const int ni = 3 * ML * C + 2 * C;
+            const TIn* kp = static_cast<const TIn*>(p.f.k);
+            const TIn* qp = static_cast<const TIn*>(p.f.q);
+            const TIn* gp = static_cast<const TIn*>(p.f.gamma);
+            const TIn* mp = static_cast<const TIn*>(p.f.mu);
+            for (int base = tid; base < ni; base += G8 * NT) {
+                float v[G8];
+#pragma unroll
+                for (int g = 0; g < G8; ++g) {
+                    const int idx = min(base + g * NT, ni - 1);
+                    const TIn* src;
+                    if (idx < 3 * ML * C) {
+                        const int a = idx / (ML * C), r = idx % (ML * C);
+                        const int64_t bt = bth_of(n * C + r / ML), o = bt * M + row0 + r % ML;
+                        // (a per-token gamma has no per-slot array: the token's value stands in)
+                        src = a == 0 ? kp + o : a == 1 ? qp + o : gp + (p.f.gamma_per_slot ? o : bt);
+                    } else {
+                        const int j = idx - 3 * ML * C;
+                        const int64_t bt = bth_of(n * C + j % C);
+                        src = j < C ? mp + bt : gp + (p.f.gamma_per_slot ? bt * M : bt);
+                    }
+                    v[g] = ld<TIn>(src, 0);
+                }
+#pragma unroll
+                for (int g = 0; g < G8; ++g) {
+                    const int idx = base + g * NT;
+                    if (idx < ni) {
+                        const int j = idx - 3 * ML * C;  // (the tail: mu, then a per-token gamma)
+                        srec[idx < 3 * ML * C ? 2 * ML * C + idx : 5 * ML * C + (j < C ? j : 2 * C + (j - C))] = v[g];
+                    }
+                }
+            }
+            if constexpr (SR::DY) {
+                // the chunk's dy [C][D] (fp32 in LDS), float4 pieces
+                float* sdy = srec + 5 * ML * C + 3 * C;
+                const int n4 = C * D / 4;
+                for (int base = tid; base < n4; base += G8 * NT) {
+                    float4 v[G8];
+#pragma unroll
+                    for (int g = 0; g < G8; ++g) {
+                        const int idx = min(base + g * NT, n4 - 1);
+                        const int64_t o = bth_of(n * C + idx / (D / 4)) * D + (idx % (D / 4)) * 4;
+                        if constexpr (DYB)
+                            v[g] = ld4<uint16_t>(static_cast<const uint16_t*>(p.dy), o);
+                        else
+                            v[g] = ld4<float>(static_cast<const float*>(p.dy), o);
+                    }
+#pragma unroll
+                    for (int g = 0; g < G8; ++g)
+                        if (base + g * NT < n4) reinterpret_cast<float4*>(sdy)[base + g * NT] = v[g];
+                }
             }
         }
         if (p.chain_h && mode == 0) {
@@ -404,7 +532,9 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
         float4 dZ[L::RPT];
 #pragma unroll
         for (int i = 0; i < L::RPT; ++i) dZ[i] = f4(0.f);
-        const int nb = C < BT ? C : BT;
+        // (the staged split path has C >= 16 > BT: every batch is full, known at compile
+        // time, so the batch is straight-line code)
+        const int nb = STG ? BT : (C < BT ? C : BT);
         // the state after the chunk's last token is the next chunk's stored start;
         // the state after token tau - 1 is the state before token tau
         float4 rpost[L::RPT];
@@ -419,13 +549,20 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
         // in flight forces a wait.  Otherwise rv[0] is the current token and rv[1]
         // the prefetched next one, copied over at the end of each token.
         RevIn<L::RPT> rv[2];
+        // token tau's inputs and record: from LDS (split workgroups) or memory
+        auto lrev = [&](RevIn<L::RPT>& x, int tau) __attribute__((always_inline)) {
+            if constexpr (STG)
+                load_rev_staged<L, ML, D, DYB>(x, p, srec, rtok + static_cast<int64_t>(tau) * M * D,
+                                               bth_of(n * C + tau), tau, rgl, cg, el(0));
+            else
+                load_rev<L, M, D, TIn, PF_STATE, DYB>(x, p, trec, rtok, bth_of(n * C + tau), ch, tau, rg, cg, el(0));
+        };
         if constexpr (PF_TOKEN) {
             // (static indices only: a computed one would put rv in scratch memory)
-            const int64_t bl = bth_of(n * C + C - 1);
             if (DBUF && C > 1)
-                load_rev<L, M, D, TIn, PF_STATE, DYB>(rv[1], p, trec, rtok, bl, ch, C - 1, rg, cg, el(0));
+                lrev(rv[1], C - 1);
             else
-                load_rev<L, M, D, TIn, PF_STATE, DYB>(rv[0], p, trec, rtok, bl, ch, C - 1, rg, cg, el(0));
+                lrev(rv[0], C - 1);
         }
         for (int ub = C - nb; ub >= 0; ub -= nb) {
             float* rb = red + (nred++ & 1) * (BT * L::NW * W);
@@ -439,8 +576,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                         // unconditional (token 0 loads itself again): a load under a
                         // branch would be waited for where the branch joins
                         const int tp = tau > 0 ? tau - 1 : 0;
-                        load_rev<L, M, D, TIn, PF_STATE, DYB>(rv[DBUF ? (u + 1) & 1 : 1], p, trec, rtok,
-                                                              bth_of(n * C + tp), ch, tp, rg, cg, el(0));
+                        lrev(rv[DBUF ? (u + 1) & 1 : 1], tp);
                     } else {
                         load_rev<L, M, D, TIn, false, DYB>(rv[0], p, trec, rtok, bth, ch, tau, rg, cg, el(0));
                     }
@@ -711,9 +847,13 @@ static int launch_bwd_mdp(const BwdParams& p, bool in_bf16, hipStream_t st) {
     const size_t h_lds = static_cast<size_t>(p.f.chunk) * D * sizeof(float);      // the chunk's h
     const size_t gk_lds = static_cast<size_t>(p.f.lin1 ? 3 : 2) * M * p.f.chunk * sizeof(float);
     // the chunk's gates from the state-passing kernel, staged in LDS where it fits
+    // split workgroups: the chunk's records of their rows (StagedRec)
+    constexpr bool STG = P > 1 && L::RPT <= 2 && M / P <= 32;
+    const size_t rec_lds = STG ? static_cast<size_t>(StagedRec<M / P, D>::floats(p.f.chunk)) * sizeof(float) : 0;
     BwdParams q = p;
-    q.stage_gk = p.chain_c != nullptr && static_lds + h_lds + gk_lds <= 128 * 1024;
-    const size_t lds = h_lds + (q.stage_gk ? gk_lds : 0);
+    q.stage_gk = p.chain_c != nullptr && static_lds + h_lds + rec_lds + gk_lds <= 128 * 1024;
+    const size_t lds = h_lds + (q.stage_gk ? gk_lds : 0) + rec_lds;
+    if (static_lds + lds > 160 * 1024) return -3;  // (the split policy never picks such a P)
     if constexpr (P > 1) {
         // progress counters to zero (they count the batches of this call)
         const int nflags = p.f.B * p.f.H * P * XFLAG_STRIDE;

@@ -69,7 +69,9 @@ size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C);
 // Workgroups per sequence of the backward (slot rows split between them), and
 // the hand-off buffers that takes (0 for one).  chain: the state-passing
 // kernel supplies the chunk-start states and records; chain_wgs: 0 automatic, 1 one.
-int bwd_split_p(int B, int H, int m, bool chain, int chain_wgs);
+int bwd_split_p(int B, int H, int m, int d, int C, bool chain, int chain_wgs);
+// Whether P workgroups of m / P rows each fit the kernel's LDS budget.
+bool bwd_split_fits(int m, int d, int C, int P);
 size_t bwd_xchg_bytes(int B, int H, int d, int P);
 int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 

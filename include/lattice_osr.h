@@ -265,8 +265,9 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * per-chunk arrays: 4 (m d + 4 m C + d C + C) bytes per chunk (4 m C more
  * with LATTICE_OSR_LIN1).  On that path, with desc->chain_wgs =
  * LATTICE_OSR_WGS_AUTO, the slot rows of each sequence are split over P
- * workgroups (the largest P in {1, 2, 4, 8} with m / P >= 16 and B*H*P <= 256;
- * fewer if the device has fewer compute units) that exchange each batch of
+ * workgroups (the largest P in {1, 2, 4, 8} with m / P >= 16, B*H*P <= 256 and
+ * a workgroup's working set within its 160 KiB of LDS; fewer if the device has
+ * fewer compute units) that exchange each batch of
  * tokens' sums over slots: the workspace then ends with their hand-off
  * buffers, B*H*(2 P 8 (d + 4) * 4 + 128 P) bytes.  The result equals one
  * workgroup's (LATTICE_OSR_WGS_ONE) up to the order of those fp32 sums;
