@@ -243,6 +243,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     constexpr bool STG = P > 1 && L::RPT <= 2 && ML <= 32;
     const int T = p.f.T, C = p.f.chunk, NC = T / C;
     const int mode = p.f.mode;
+    const bool enc = !STG && mode == 2;  // (the split path never runs the encoding layer)
     const int64_t tstride = p.f.H;  // consecutive tokens of one (b,h) are H rows apart
 
     float* ws = p.ws + static_cast<int64_t>(bh) * bwd_floats_per_bh<M, D>(T, C);
@@ -567,6 +568,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
         for (int ub = C - nb; ub >= 0; ub -= nb) {
             float* rb = red + (nred++ & 1) * (BT * L::NW * W);
             float dcv[BT][L::RPT], kv[BT][L::RPT], dkin[BT][L::RPT];
+            float dqv[STG ? BT : 1][L::RPT], dgv[STG ? BT : 1][L::RPT];  // (STG: this batch's dq, dgamma)
 #pragma unroll
             for (int u = BT - 1; u >= 0; --u) {
                 if (u < nb) {
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                     for (int i = 0; i < L::RPT; ++i) {
                         const float ci = rc.c[i];
                         const float bt = rc.beta[i];
-                        const float coef = mode == 2 ? ci - in.k[i] : in.k[i];
+                        const float coef = enc ? ci - in.k[i] : in.k[i];
                         const float a = in.g[i] * coef;
                         const float wraw = fmaf(-ci, ci, hh);
                         const float w = fmaxf(wraw, 0.f);
@@ -663,7 +665,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                             dhh_i = dw;
                             dci = fmaf(-2.f * ci, dw, dci);
                         }
-                        if (mode == 2) {
+                        if (enc) {
                             dci = fmaf(in.g[i], da, dci);
                             dkin[u][i] = -in.g[i] * da;
                             dgam[i] = coef * da;
@@ -686,15 +688,29 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                     sc.x = strided_sum<L::TPR>(sc.x);
                     sc.y = strided_sum<L::TPR>(sc.y);
                     sc.z = strided_sum<L::TPR>(sc.z);
-                    if (lane < L::TPR) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + cg * 4) = hp;
-                    if (lane == 0) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + D) = sc;
+                    if constexpr (STG) {
+                        // every row group holds the same sums: all lanes write (the same values
+                        // to the same addresses), so the batch stays straight-line code
+                        *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + cg * 4) = hp;
+                        *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + D) = sc;
+                    } else {
+                        if (lane < L::TPR) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + cg * 4) = hp;
+                        if (lane == 0) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + D) = sc;
+                    }
 #pragma unroll
                     for (int i = 0; i < L::RPT; ++i) {
                         dR[i] = gate[i] * dR[i];
                         if constexpr (PF_STATE) rpost[i] = rp[i];
                     }
                     if constexpr (PF_TOKEN && !DBUF) rv[0] = rv[1];
-                    if (cg == 0) {
+                    if constexpr (STG) {
+                        // stored after the batch (no branch in the token's code)
+#pragma unroll
+                        for (int i = 0; i < L::RPT; ++i) {
+                            dqv[u][i] = dq[i];
+                            dgv[u][i] = dgam[i];
+                        }
+                    } else if (cg == 0) {
 #pragma unroll
                         for (int i = 0; i < L::RPT; ++i) {
                             const int64_t o = bth * M + rg + L::RG * i;
@@ -788,6 +804,14 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                     if (cg == 0) {
 #pragma unroll
                         for (int i = 0; i < L::RPT; ++i) p.dk[bth * M + rg + L::RG * i] = dkin[u][i] + dkz[i];
+                        if constexpr (STG) {
+#pragma unroll
+                            for (int i = 0; i < L::RPT; ++i) {
+                                const int64_t o = bth * M + rg + L::RG * i;
+                                p.dq[o] = dqv[u][i];
+                                if (p.f.gamma_per_slot) p.dgamma[o] = dgv[u][i];
+                            }
+                        }
                     }
                     if (tid == 0 && pidx == 0) {
                         p.dmu[bth] = ssum.y;
