@@ -223,6 +223,9 @@ def test_layer_pipeline_glue_forward_glue(C):
 GATED = [("split", synth.BF16, 64, osr.SCHED_SPLIT, 2, 256, 2, 64, 128),
          ("fused", synth.BF16, 32, osr.SCHED_FUSED, 2, 256, 2, 64, 128),
          ("split-wgs", synth.BF16, 128, osr.SCHED_AUTO, 1, 512, 4, 128, 128),
+         # 64 chunks: the read-out overlapped by chunk ranges (one and four workgroups per sequence)
+         ("overlap", synth.BF16, 32, osr.SCHED_AUTO, 1, 2048, 2, 64, 64),
+         ("overlap-wgs", synth.BF16, 128, osr.SCHED_AUTO, 1, 8192, 2, 128, 128),
          ("tokenloop-bf16", synth.BF16, 4, osr.SCHED_AUTO, 2, 64, 2, 32, 64),
          ("tokenloop-f32", synth.F32, 4, osr.SCHED_AUTO, 2, 64, 2, 32, 64)]
 
