@@ -124,7 +124,9 @@ extern "C" {
                                       library's side stream for the device while the next range's
                                       state passing runs on hip_stream, which waits for the side
                                       stream before the call's work ends.  Same results, bit for
-                                      bit, as _OFF */
+                                      bit, as _OFF.  A caller capturing the call into a HIP graph
+                                      may prefer _OFF (or the no-allocation entry), which keeps
+                                      all work on hip_stream */
 #define LATTICE_OSR_OVERLAP_OFF 1  /* state passing, then read-out, both on hip_stream */
 
 /* Status codes. */
