@@ -179,3 +179,142 @@ def test_planted_mistake_fails_finite_differences(name):
     exec(compile(src.replace(old, new), "osr_backward_mutant.py", "exec"), mod.__dict__)
     worst = max(_fd_check(mod, s, 4, DEC, LIN2, True, segment=4) for s in (0, 1))
     assert worst > 1e-3, (name, worst)
+
+
+# ---------------------------------------------------------------------------
+# The chunk-parallel form of the gradient, derived by hand, against autograd.
+#
+# Per chunk (eq. recurrence_linear2; the chunk-parallel form of "Parallel and
+# Hardware Efficient Form"): with Z the projected chunk-start state,
+#   H = K Z - V (decoding) or -V (similarity),  Ht = H Z^T,  nh = rowsum(H^2),
+#   a = gamma k,  w = nh - Ht^2 (used where > 0),  beta = (mu^2 + a^2 w)^(-1/2),
+#   kh = beta a,  G = beta (mu + a Ht),  A_t = prod_{u <= t} G_u (per slot),
+#   Y = (Q A) Z - tril((Q A)(kh / A)^T) H,   R_end = diag(A_C) Z - (kh A_C / A)^T H.
+# Its vector-Jacobian product is taken matrix by matrix (the products above,
+# then the gate cumulative products through the reverse recursion
+# E_t = dA_t + G_{t+1} E_{t+1}, dG_t = A_{t-1} E_t, with no division by G),
+# and the chunks are chained backwards through the projection of their start
+# states.  This is a second, independent evaluation of the gradient (matrix
+# products instead of autograd of the token loop); it is also the form a
+# chunk-parallel matrix-core backward would compute.
+
+def _chunk_form_grad(q, k, v, g, mu, S0, dy, dso, C, mode):
+    """fp64 numpy, one (b,h): q, k, g [T,m]; v, dy [T,d]; mu [T]; S0, dso [m,d]."""
+    T, m = q.shape
+    d = v.shape[1]
+    NC = T // C
+    # forward: chunk-start states (before projection)
+    starts, S = [], S0.copy()
+    for n in range(NC):
+        starts.append(S.copy())
+        sl = slice(n * C, (n + 1) * C)
+        Z = S / np.linalg.norm(S, axis=1, keepdims=True)
+        H = k[sl] @ Z - v[sl] if mode == DEC else -v[sl]
+        Ht = H @ Z.T
+        nh = np.sum(H * H, axis=1)
+        a = g[sl] * k[sl]
+        w = np.maximum(nh[:, None] - Ht * Ht, 0.0)
+        beta = 1.0 / np.sqrt(mu[sl][:, None] ** 2 + a * a * w)
+        kh = beta * a
+        G = beta * (mu[sl][:, None] + a * Ht)
+        A = np.cumprod(G, axis=0)
+        S = A[-1][:, None] * Z - (kh * A[-1] / A).T @ H
+    # the returned state is the end state projected
+    nS = np.linalg.norm(S, axis=1, keepdims=True)
+    Zo = S / nS
+    dR = (dso - Zo * np.sum(Zo * dso, axis=1, keepdims=True)) / nS
+    out = {key: np.zeros_like(x) for key, x in (("dq", q), ("dk", k), ("dv", v), ("dgamma", g), ("dmu", mu))}
+    for n in reversed(range(NC)):
+        sl = slice(n * C, (n + 1) * C)
+        S = starts[n]
+        nZ = np.linalg.norm(S, axis=1, keepdims=True)
+        Z = S / nZ
+        Q, K, V, Gm, Mu, dY = q[sl], k[sl], v[sl], g[sl], mu[sl], dy[sl]
+        H = K @ Z - V if mode == DEC else -V
+        Ht = H @ Z.T
+        nh = np.sum(H * H, axis=1)
+        a = Gm * K
+        wraw = nh[:, None] - Ht * Ht
+        Mk = wraw > 0
+        w = np.where(Mk, wraw, 0.0)
+        beta = 1.0 / np.sqrt(Mu[:, None] ** 2 + a * a * w)
+        kh = beta * a
+        G = beta * (Mu[:, None] + a * Ht)
+        A = np.cumprod(G, axis=0)
+        AC = A[-1]
+        QA, KA = Q * A, kh / A
+        P = np.tril(QA @ KA.T)
+        W = KA * AC
+        # read-out
+        dZ = QA.T @ dY
+        dQA = dY @ Z.T
+        dH = -P.T @ dY
+        dP = -np.tril(dY @ H.T)
+        dQA += dP @ KA
+        dKA = dP.T @ QA
+        # chunk-end state
+        dZ += AC[:, None] * dR
+        dAC = np.sum(Z * dR, axis=1)
+        dH += -W @ dR
+        dW = -H @ dR.T
+        dKA += dW * AC
+        dAC += np.sum(dW * KA, axis=0)
+        # Q A and kh / A
+        out["dq"][sl] = dQA * A
+        dA = dQA * Q - dKA * KA / A
+        dA[-1] += dAC
+        dkh = dKA / A
+        # cumulative product, reverse recursion
+        E = np.zeros_like(dA)
+        E[-1] = dA[-1]
+        for t in range(C - 2, -1, -1):
+            E[t] = dA[t] + G[t + 1] * E[t + 1]
+        Aprev = np.vstack([np.ones((1, m)), A[:-1]])
+        dG = Aprev * E
+        # gates
+        dbeta = dG * (Mu[:, None] + a * Ht) + dkh * a
+        dHt = dG * kh
+        da = dG * beta * Ht + dkh * beta
+        dmu = np.sum(dG * beta, axis=1)
+        tb = -0.5 * beta ** 3 * dbeta
+        dmu += np.sum(2.0 * Mu[:, None] * tb, axis=1)
+        da += 2.0 * a * w * tb
+        dw = np.where(Mk, a * a * tb, 0.0)
+        dnh = np.sum(dw, axis=1)
+        dHt += -2.0 * Ht * dw
+        out["dgamma"][sl] = da * K
+        dK = da * Gm
+        dH += dHt @ Z + 2.0 * dnh[:, None] * H
+        dZ += dHt.T @ H
+        if mode == DEC:
+            dK += dH @ Z.T
+            dZ += K.T @ dH
+        out["dk"][sl] = dK
+        out["dv"][sl] = -dH
+        out["dmu"][sl] = dmu
+        # chunk-start projection
+        dR = (dZ - Z * np.sum(Z * dZ, axis=1, keepdims=True)) / nZ
+    out["dstate_in"] = dR
+    return out
+
+
+@pytest.mark.parametrize("C,T", [(1, 6), (4, 16), (8, 24), (16, 32)])
+@pytest.mark.parametrize("mode", [DEC, SIM])
+def test_chunk_parallel_gradient_form(C, T, mode):
+    """The hand-derived chunk-parallel gradient equals the autograd gradient of
+    the chunk-wise forward to rounding (per-slot gamma, several chunks)."""
+    inp = synth.make_inputs(1, T, 2, 6, 5, seed=900 + C + T + mode, in_dtype=synth.F32, gamma_per_slot=True)
+    q, k, v, g, mu, S0 = inp.values_f64()
+    rng = np.random.default_rng(901 + C)
+    dy = rng.standard_normal(v.shape)
+    dso = rng.standard_normal(S0.shape)
+    ref = ob.osr_backward(q, k, v, g, mu, S0, dy, dso, chunk_size=C, mode=mode)
+    for h in range(2):
+        got = _chunk_form_grad(q[0, :, h], k[0, :, h], v[0, :, h], g[0, :, h], mu[0, :, h], S0[0, h],
+                               dy[0, :, h], dso[0, h], C, mode)
+        for key, ref_key in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dgamma", "dgamma"), ("dmu", "dmu")):
+            r = ref[ref_key][0, :, h]
+            scale = max(1.0, float(np.max(np.abs(r))))
+            assert np.max(np.abs(got[key] - r)) <= 1e-9 * scale, (key, C, mode)
+        r = ref["dstate_in"][0, h]
+        assert np.max(np.abs(got["dstate_in"] - r)) <= 1e-9 * max(1.0, float(np.max(np.abs(r))))
