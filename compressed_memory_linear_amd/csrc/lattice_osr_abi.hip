@@ -46,6 +46,8 @@ int check_desc(const lattice_osr_desc* d) {
     if (d->chain_wgs != LATTICE_OSR_WGS_AUTO && d->chain_wgs != LATTICE_OSR_WGS_ONE) return LATTICE_OSR_ERR_UNSUPPORTED;
     if (d->readout_overlap != LATTICE_OSR_OVERLAP_AUTO && d->readout_overlap != LATTICE_OSR_OVERLAP_OFF)
         return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->bwd_form != LATTICE_OSR_BWD_AUTO && d->bwd_form != LATTICE_OSR_BWD_WALK && d->bwd_form != LATTICE_OSR_BWD_CHUNK)
+        return LATTICE_OSR_ERR_UNSUPPORTED;
     return LATTICE_OSR_OK;
 }
 
@@ -221,12 +223,20 @@ size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
     return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, osr::bwd_split_p(d->B, d->H, d->m, d->d, C, chain, d->chain_wgs));
 }
 
+// The chunk-parallel backward where it is built and not turned off.
+bool bwd_chunk_form(const lattice_osr_desc* d, int C) {
+    return d->bwd_form != LATTICE_OSR_BWD_WALK && bwd_uses_chain(d, C) &&
+           osr::bwd_chunk_supported(d->m, d->d, C, d->in_dtype == LATTICE_OSR_BF16,
+                                    d->linearisation == LATTICE_OSR_LIN1, d->mode);
+}
+
 // Shape rules of the backward: those of the chunked forward.
 int check_bwd_desc(const lattice_osr_desc* d, int C) {
     int rc = check_desc(d);
     if (rc) return rc;
     if (C <= 0 || d->T % C != 0) return LATTICE_OSR_ERR_SHAPE;
     if (!pow2_chunk(C)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (d->bwd_form == LATTICE_OSR_BWD_CHUNK && !bwd_chunk_form(d, C)) return LATTICE_OSR_ERR_UNSUPPORTED;
     return LATTICE_OSR_OK;
 }
 
@@ -461,6 +471,7 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
         p.chain_b = p.chain_c + nch * mc;
         p.chain_hh = p.chain_b + nch * mc;
     }
+    if (bwd_chunk_form(desc, chunk_size)) return osr::launch_bwd_chunk(desc->m, desc->d, p, true, st);
     // slot rows split over workgroups: every workgroup of a sequence must be resident
     // at once (they wait for each other), so no more workgroups than compute units
     p.split_p = osr::bwd_split_p(desc->B, desc->H, desc->m, desc->d, chunk_size, chain, desc->chain_wgs);

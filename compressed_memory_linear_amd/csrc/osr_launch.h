@@ -74,6 +74,12 @@ int bwd_split_p(int B, int H, int m, int d, int C, bool chain, int chain_wgs);
 bool bwd_split_fits(int m, int d, int C, int P);
 size_t bwd_xchg_bytes(int B, int H, int d, int P);
 int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
+// The chunk-parallel backward on the fp32 matrix cores (osr_bwd_chunk.hip):
+// where it is built (m = d = C = 64, bf16 inputs, the default linearisation,
+// decoding or similarity objective), with the chunk-start states already in
+// the workspace (states_ready).  Same workspace layout as launch_bwd.
+bool bwd_chunk_supported(int m, int d, int C, bool in_bf16, bool lin1, int mode);
+int launch_bwd_chunk(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 
 // Layer glue (HBM-bound streaming kernels).  pre: q = conv4(xq), k = conv4(xk)
 // (depthwise causal, width 4, N = H*m channels per token row), gamma =

@@ -24,6 +24,7 @@ SCHED_AUTO, SCHED_SPLIT, SCHED_FUSED = 0, 1, 2
 PAIRS_AUTO, PAIRS_OFF = 0, 1
 WGS_AUTO, WGS_ONE = 0, 1
 OVERLAP_AUTO, OVERLAP_OFF = 0, 1
+BWD_AUTO, BWD_WALK, BWD_CHUNK = 0, 1, 2
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_ALIGN = -1, -2, -3, -4, -5, -6, -7
@@ -38,7 +39,7 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 class lattice_osr_desc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "T", "H", "m", "d", "gamma_per_slot", "in_dtype", "y_dtype", "mode", "linearisation",
-                 "schedule", "chain_pairs", "chain_wgs", "readout_overlap")]
+                 "schedule", "chain_pairs", "chain_wgs", "readout_overlap", "bwd_form")]
 
 
 class OSRError(RuntimeError):
@@ -99,9 +100,10 @@ lattice_osr_status_string = status_string
 
 
 def make_desc(B, T, H, m, d, gamma_per_slot=1, in_dtype=BF16, y_dtype=F32, mode=MODE_DEC, linearisation=LIN2,
-              schedule=SCHED_AUTO, chain_pairs=PAIRS_AUTO, chain_wgs=WGS_AUTO, readout_overlap=OVERLAP_AUTO):
+              schedule=SCHED_AUTO, chain_pairs=PAIRS_AUTO, chain_wgs=WGS_AUTO, readout_overlap=OVERLAP_AUTO,
+              bwd_form=BWD_AUTO):
     return lattice_osr_desc(B, T, H, m, d, gamma_per_slot, in_dtype, y_dtype, mode, linearisation, schedule,
-                            chain_pairs, chain_wgs, readout_overlap)
+                            chain_pairs, chain_wgs, readout_overlap, bwd_form)
 
 
 def lattice_osr_workspace_bytes(desc: lattice_osr_desc, chunk_size: int) -> int:
@@ -144,7 +146,8 @@ def _check_cuda(*tensors):
 
 
 def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation=0, schedule=SCHED_AUTO,
-               chain_pairs=PAIRS_AUTO, chain_wgs=WGS_AUTO, readout_overlap=OVERLAP_AUTO) -> lattice_osr_desc:
+               chain_pairs=PAIRS_AUTO, chain_wgs=WGS_AUTO, readout_overlap=OVERLAP_AUTO,
+               bwd_form=BWD_AUTO) -> lattice_osr_desc:
     """Descriptor of a forward call, after checking every input against it:
     q, k [B,T,H,m]; v [B,T,H,d]; gamma [B,T,H,m] or [B,T,H]; mu [B,T,H]
     (all one dtype, float32 or bfloat16); state_in [B,H,m,d] float32; all
@@ -165,7 +168,7 @@ def _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation=0, sch
     _check_tensor("mu", mu, (B, T, H), q.dtype, q.device)
     _check_tensor("state_in", state_in, (B, H, m, d), torch.float32, q.device)
     return make_desc(B, T, H, m, d, per_slot, _DT[q.dtype], _DT[y_dtype], mode, linearisation, schedule,
-                     chain_pairs, chain_wgs, readout_overlap)
+                     chain_pairs, chain_wgs, readout_overlap, bwd_form)
 
 
 def _check_outputs(desc, q, state_in, state_out, y, y_dtype):
@@ -325,15 +328,19 @@ def lattice_osr_bwd_workspace_bytes(desc: lattice_osr_desc, chunk_size: int) -> 
 
 def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size: int, *,
                             mode: int = MODE_DEC, grads: Optional[dict] = None, workspace=None,
-                            stream=None, linearisation: int = LIN2, chain_wgs: int = WGS_AUTO) -> dict:
+                            stream=None, linearisation: int = LIN2, chain_wgs: int = WGS_AUTO,
+                            bwd_form: int = BWD_AUTO) -> dict:
     """Backward of the chunk-wise forward: gradients of sum(dy*y) +
     sum(dstate_out*state_out) with respect to q, k, v, gamma, mu and
     state_in.  dy has y's shape (float32 or bfloat16), dstate_out the state's.
     Returns a dict of float32 tensors dq, dk, dv, dgamma, dmu, dstate_in
     (allocated unless passed in `grads`).  chain_wgs: WGS_ONE keeps each
-    sequence on one workgroup (speed only)."""
+    sequence of the token walk on one workgroup (speed only); bwd_form:
+    BWD_WALK / BWD_CHUNK pick the backward's form (BWD_AUTO: the chunk form
+    where it is built)."""
     lib = load_library()
-    desc = _desc_from(q, k, v, gamma, mu, state_in, dy.dtype, mode, linearisation, chain_wgs=chain_wgs)
+    desc = _desc_from(q, k, v, gamma, mu, state_in, dy.dtype, mode, linearisation, chain_wgs=chain_wgs,
+                      bwd_form=bwd_form)
     _check_tensor("dy", dy, tuple(v.shape), None, q.device)
     _check_tensor("dstate_out", dstate_out, tuple(state_in.shape), torch.float32, q.device)
     named = (("q", q), ("k", k), ("v", v), ("gamma", gamma), ("mu", mu), ("state_in", state_in))

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define LATTICE_OSR_ABI_VERSION 5
+#define LATTICE_OSR_ABI_VERSION 6
 
 #if defined(__GNUC__) || defined(__clang__)
 #define LATTICE_OSR_API __attribute__((visibility("default")))
@@ -129,6 +129,19 @@ extern "C" {
                                       all work on hip_stream */
 #define LATTICE_OSR_OVERLAP_OFF 1  /* state passing, then read-out, both on hip_stream */
 
+/*
+ * Form of the backward (lattice_osr_bwd_chunked; the forward ignores it).
+ * WALK: a reverse walk over the tokens, in fp32 on the vector units.
+ * CHUNK: the chunk-parallel form on the fp32 matrix cores (built for
+ * m = d = chunk_size = 64, bf16 inputs, the default linearisation, the
+ * decoding and similarity objectives; elsewhere the call returns
+ * LATTICE_OSR_ERR_UNSUPPORTED).  AUTO: CHUNK where it is built, else WALK.
+ * Both compute the same gradient up to fp32 rounding.
+ */
+#define LATTICE_OSR_BWD_AUTO 0
+#define LATTICE_OSR_BWD_WALK 1
+#define LATTICE_OSR_BWD_CHUNK 2
+
 /* Status codes. */
 #define LATTICE_OSR_OK 0
 #define LATTICE_OSR_ERR_NULL (-1)        /* a required pointer is NULL              */
@@ -154,6 +167,7 @@ typedef struct {
     int32_t chain_pairs;    /* LATTICE_OSR_PAIRS_AUTO (0) or _OFF (1)            */
     int32_t chain_wgs;      /* LATTICE_OSR_WGS_AUTO (0) or _ONE (1)              */
     int32_t readout_overlap; /* LATTICE_OSR_OVERLAP_AUTO (0) or _OFF (1)         */
+    int32_t bwd_form;       /* LATTICE_OSR_BWD_AUTO (0), _WALK (1), _CHUNK (2)   */
 } lattice_osr_desc;
 
 /*

@@ -34,7 +34,7 @@ def test_header_declarations_are_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert osr.lattice_osr_abi_version() == 5
+    assert osr.lattice_osr_abi_version() == 6
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         s = osr.status_string(code)
         assert s and s != "unknown status"
@@ -80,6 +80,7 @@ def test_null_pointers(fn):
     ("chain_pairs", 2, osr.ERR_UNSUPPORTED), ("chain_pairs", -1, osr.ERR_UNSUPPORTED),
     ("chain_wgs", 2, osr.ERR_UNSUPPORTED), ("chain_wgs", -1, osr.ERR_UNSUPPORTED),
     ("readout_overlap", 2, osr.ERR_UNSUPPORTED), ("readout_overlap", -1, osr.ERR_UNSUPPORTED),
+    ("bwd_form", 3, osr.ERR_UNSUPPORTED), ("bwd_form", -1, osr.ERR_UNSUPPORTED),
 ])
 def test_bad_descriptor(field, value, status):
     d = osr.make_desc(2, 8, 2, 32, 32)
@@ -363,6 +364,30 @@ def test_bwd_null_pointers_and_shapes():
     assert _bwd_call(d4, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED
     with pytest.raises(osr.OSRError):
         osr.lattice_osr_bwd_workspace_bytes(d4, 4)
+
+
+def test_bwd_form_choice():
+    """The chunk-parallel backward is built for m = d = C = 64 with bf16 inputs,
+    the default linearisation and the decoding or similarity objective: asking
+    for it elsewhere is ERR_UNSUPPORTED; the walk and the automatic choice take
+    every configuration, and the workspace does not depend on the form."""
+    ok = dict(B=1, T=128, H=2, m=64, d=64)
+    for form in (osr.BWD_AUTO, osr.BWD_WALK, osr.BWD_CHUNK):
+        d = osr.make_desc(**ok, bwd_form=form)
+        assert osr.lattice_osr_bwd_workspace_bytes(d, 64) == \
+            osr.lattice_osr_bwd_workspace_bytes(osr.make_desc(**ok), 64)
+    bad = [dict(C=32), dict(C=64, in_dtype=osr.F32), dict(C=64, linearisation=osr.LIN1),
+           dict(C=64, mode=osr.MODE_ENC), dict(C=64, m=32), dict(C=64, d=128)]
+    for b in bad:
+        kw = dict(ok)
+        C = b.pop("C")
+        kw.update(b)
+        chunk = osr.make_desc(**kw, bwd_form=osr.BWD_CHUNK)
+        assert _bwd_call(chunk, _bwd_ptrs(), C) == osr.ERR_UNSUPPORTED, b
+        with pytest.raises(osr.OSRError):
+            osr.lattice_osr_bwd_workspace_bytes(chunk, C)
+        for form in (osr.BWD_AUTO, osr.BWD_WALK):
+            assert osr.lattice_osr_bwd_workspace_bytes(osr.make_desc(**kw, bwd_form=form), C) > 0
 
 
 def test_bwd_workspace_too_small():

@@ -59,14 +59,14 @@ def _upstream(inp, seed, dy_bf16=False):
     return dy, dso
 
 
-def _gpu_bwd(inp, dy, dso, C, mode, dy_bf16=False, lin=osr.LIN2, chain_wgs=osr.WGS_AUTO):
+def _gpu_bwd(inp, dy, dso, C, mode, dy_bf16=False, lin=osr.LIN2, chain_wgs=osr.WGS_AUTO, bwd_form=osr.BWD_AUTO):
     t = osr.to_device(inp, "cuda")
     dyt = torch.from_numpy(dy).cuda()
     if dy_bf16:
         dyt = dyt.to(torch.bfloat16)   # exact: dy already holds bf16 values
     g = osr.lattice_osr_bwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], dyt,
                                     torch.from_numpy(dso).cuda(), C, mode=mode, linearisation=lin,
-                                    chain_wgs=chain_wgs)
+                                    chain_wgs=chain_wgs, bwd_form=bwd_form)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in g.items()}
 
@@ -202,9 +202,11 @@ def test_bwd_headline_workload_sampled():
     _say("bwd headline chunked_b4h8_t2048_m64d64_c64, sampled (b,h)")
     inp = synth.workload_inputs("chunked_b4h8_t2048_m64d64_c64")
     dy, dso = _upstream(inp, 16)
-    got = _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC)
     bh = [(0, 0), (1, 5), (2, 3), (3, 7)]
-    _check(inp, got, _oracle(inp, dy, dso, 64, osr.MODE_DEC, bh), bh=bh)
+    ref = _oracle(inp, dy, dso, 64, osr.MODE_DEC, bh)
+    for form in (osr.BWD_CHUNK, osr.BWD_WALK):
+        _say(f"  form {form}")
+        _check(inp, _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC, bwd_form=form), ref, bh=bh)
 
 
 def test_bwd_d128_workload_sampled():
@@ -288,8 +290,8 @@ def test_bwd_split_over_workgroups(B, H, m, d, C, T, mode, lin):
     _say(f"bwd slot rows split over workgroups B{B} H{H} m{m} d{d} C{C} T{T} mode{mode} lin{lin}")
     inp = synth.make_inputs(B, T, H, m, d, seed=2100 + m + d + C + mode, in_dtype=synth.BF16)
     dy, dso = _upstream(inp, 2200 + m + d)
-    split = _gpu_bwd(inp, dy, dso, C, mode, lin=lin)
-    one = _gpu_bwd(inp, dy, dso, C, mode, lin=lin, chain_wgs=osr.WGS_ONE)
+    split = _gpu_bwd(inp, dy, dso, C, mode, lin=lin, bwd_form=osr.BWD_WALK)
+    one = _gpu_bwd(inp, dy, dso, C, mode, lin=lin, chain_wgs=osr.WGS_ONE, bwd_form=osr.BWD_WALK)
     for key in split:
         assert _rel(split[key], one[key]) <= 1e-5, key
     _check(inp, split, _oracle(inp, dy, dso, C, mode, lin=ob.LIN1 if lin == osr.LIN1 else ob.LIN2))
@@ -299,7 +301,7 @@ def test_bwd_split_deterministic():
     _say("bwd split over workgroups: bit-identical reruns, B1 H4 T512 m=d=128 C64")
     inp = synth.make_inputs(1, 512, 4, 128, 128, seed=2300, in_dtype=synth.BF16)
     dy, dso = _upstream(inp, 2301)
-    a = _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC)
-    b = _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC)
+    a = _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC, bwd_form=osr.BWD_WALK)
+    b = _gpu_bwd(inp, dy, dso, 64, osr.MODE_DEC, bwd_form=osr.BWD_WALK)
     for key in a:
         assert np.array_equal(a[key], b[key]), key
