@@ -75,7 +75,7 @@ def chain_reference_ms(w: dict, chunk: int) -> float:
 # Sources of the backward kernel: not part of the forward and decode kernels
 # whose traffic counters are keyed by the hash below.
 BWD_SOURCES = ("osr_bwd.hip", "osr_bwd_kernel.h", "osr_bwd_m16.hip", "osr_bwd_m32.hip", "osr_bwd_m64.hip",
-               "osr_bwd_m128.hip")
+               "osr_bwd_m128.hip", "osr_bwd_chunk.hip")
 # Source of the layer-glue kernels: not part of either.
 GLUE_SOURCES = ("osr_glue.hip",)
 
@@ -397,6 +397,7 @@ def main() -> int:
                                                      (SMALL, "chunked", 64, 10, 2, 0),
                                                      (SMALL, "chunked", 64, 10, 0, 1),
                                                      (SMALL, "backward", 64, 2, 0, 0),
+                                                     (SMALL, "backward", 4, 1, 0, 0),
                                                      (HEADLINE, "backward", HEADLINE_CHUNK, 2, 0, 0)):
             # the small workload (51 MB) fits the 256 MB Infinity Cache: rotate 8 input copies
             c = Case(name, entry, chunk, copies=8 if name == SMALL and entry == "chunked" else 1,

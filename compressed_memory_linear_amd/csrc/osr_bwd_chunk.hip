@@ -62,7 +62,33 @@ __device__ __forceinline__ f4 mm(f4 acc, const float* a, const float* b, int lan
     return acc;
 }
 
+// Four output tiles that share the A operand: acc[j] += A B_j with B_j
+// starting at b + j * BS (independent accumulation chains, one A load per
+// step for four products).
+template <int K, int AI, int AK, int BK, int BJ, int BS>
+__device__ __forceinline__ void mm4(f4 (&acc)[4], const float* a, const float* b, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+    const float* pa = a + r * AI + kq * AK;
+    const float* pb = b + kq * BK + r * BJ;
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 4) {
+        const float av = pa[k0 * AK];
+        float bv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bv[j] = pb[k0 * BK + j * BS];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[j], acc[j], 0, 0, 0);
+    }
+}
+
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
+
+// Workgroup barrier for LDS data only: every wave's LDS accesses have
+// completed, then s_barrier.  (__syncthreads also waits for the wave's
+// global loads and stores; the kernel's global accesses are each thread's own
+// -- outputs, and the workspace elements it wrote itself -- so no other wave
+// waits for them.)
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Sum over the 16 lanes of a lane row (same lg).
 __device__ __forceinline__ float row16_sum(float x) {
@@ -140,7 +166,8 @@ __device__ __forceinline__ void affine_scan_rev(const float (&gn)[4], const floa
 // backward's second evaluation repeats the first bit for bit.
 struct TileGates {
     float a[4], wv[4], beta[4], kap[4], g[4], A[4], Ap[4], sfx[4];
-    float ar, ae;
+    float rA[4];    // 1 / A (v_rcp_f32)
+    float ar, rar, ae;  // a_ref, 1 / a_ref, A_end
 };
 __device__ __forceinline__ void tile_gates(const float (&kq)[4], const float (&gm)[4], const float (&mu)[4],
                                            const float (&hh)[4], const float (&ht)[4], int lane, TileGates& o) {
@@ -184,7 +211,9 @@ __device__ __forceinline__ void tile_gates(const float (&kq)[4], const float (&g
     for (int r = 0; r < 4; ++r) {
         o.A[r] = below * lprod[r];
         o.Ap[r] = r == 0 ? below : below * lprod[r - 1];
+        o.rA[r] = __builtin_amdgcn_rcpf(o.A[r]);
     }
+    o.rar = __builtin_amdgcn_rcpf(o.ar);
 }
 
 template <int M, int D, int C, typename TIn, bool DYB>
@@ -311,48 +340,54 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
                 gm[r] = gps ? ld<TIn>(gp, tt * M + 16 * mt + lc) : ld<TIn>(gp, tt);
             }
         };
-        __syncthreads();
+        lds_barrier();
 
         // ---- 2. H = K Z - V for this wave's tile; |h|^2 ----
         float hh[4] = {0.f, 0.f, 0.f, 0.f};
+        {
+            f4 acc[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            f4 acc;
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = -Us[(TL * w + t_lane + r) * LDX + 16 * dt + lc];
-            if (dec) acc = mm<M, LDX, 1, LDX, 1>(acc, Ws + TL * w * LDX, Zs + 16 * dt, lane);
+                for (int r = 0; r < 4; ++r) acc[dt][r] = -Us[(TL * w + t_lane + r) * LDX + 16 * dt + lc];
+            if (dec) mm4<M, LDX, 1, LDX, 1, 16>(acc, Ws + TL * w * LDX, Zs, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                Hs[(TL * w + t_lane + r) * LDX + 16 * dt + lc] = acc[r];
-                hh[r] += acc[r] * acc[r];
-            }
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    Hs[(TL * w + t_lane + r) * LDX + 16 * dt + lc] = acc[dt][r];
+                    hh[r] += acc[dt][r] * acc[dt][r];
+                }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) hh[r] = row16_sum(hh[r]);
         if (lc == 0)
 #pragma unroll
             for (int r = 0; r < 4; ++r) nh_s[TL * w + t_lane + r] = hh[r];
-        __syncthreads();  // H visible; every wave is done with K in Ws
+        lds_barrier();  // H visible; every wave is done with K in Ws
 
         // ---- 3. c = H Z^T (this tile) and the gates ----
         float ht[MT][4];
+        float kq3[MT][4], qv3[MT][4], gm3[MT][4];  // this tile's inputs, loaded before the product
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f4 acc = mm<D, LDX, 1, 1, LDX>(zero4(), Hs + TL * w * LDX, Zs + 16 * mt * LDX, lane);
+        for (int mt = 0; mt < MT; ++mt) load_in(mt, kq3[mt], qv3[mt], gm3[mt]);
+        {
+            f4 acc[MT] = {zero4(), zero4(), zero4(), zero4()};
+            mm4<D, LDX, 1, 1, LDX, 16 * LDX>(acc, Hs + TL * w * LDX, Zs, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ht[mt][r] = acc[r];
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ht[mt][r] = acc[mt][r];
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            float kq[4], qv[4], gm[4];
-            load_in(mt, kq, qv, gm);
             TileGates tg;
-            tile_gates(kq, gm, mu, hh, ht[mt], lane, tg);
+            tile_gates(kq3[mt], gm3[mt], mu, hh, ht[mt], lane, tg);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int o = (TL * w + t_lane + r) * LDX + 16 * mt + lc;
-                QAs[o] = qv[r] * tg.A[r] / tg.ar;
-                KAs[o] = tg.kap[r] * tg.ar / tg.A[r];
+                QAs[o] = qv3[mt][r] * tg.A[r] * tg.rar;
+                KAs[o] = tg.kap[r] * tg.ar * tg.rA[r];
                 Ws[o] = tg.kap[r] * tg.sfx[r];
             }
             if (lg == 0) {
@@ -360,7 +395,7 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
                 ar_s[w * M + 16 * mt + lc] = tg.ar;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 4. per tile: P, dP and the lambda-free gradients ----
         {
@@ -373,31 +408,32 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
                 dPs[w][(t_lane + r) * 17 + lc] = causal ? -pd[r] : 0.f;
             }
         }
-        __syncthreads();
+        lds_barrier();
         float dqa[MT][4], dka[MT][4];
+        {
+            // dQA' = dP KA', dKA' = dP^T QA', dH = -P^T dY (into Us: V is dead since step 2)
+            f4 x[MT] = {zero4(), zero4(), zero4(), zero4()}, y[MT] = {zero4(), zero4(), zero4(), zero4()};
+            f4 z[DT] = {zero4(), zero4(), zero4(), zero4()};
+            mm4<TL, 17, 1, LDX, 1, 16>(x, dPs[w], KAs + TL * w * LDX, lane);
+            mm4<TL, 1, 17, LDX, 1, 16>(y, dPs[w], QAs + TL * w * LDX, lane);
+            mm4<TL, 1, 17, LDX, 1, 16>(z, Ps[w], Ys + TL * w * LDX, lane);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            // dQA' = dP KA', dKA' = dP^T QA'
-            const f4 x = mm<TL, 17, 1, LDX, 1>(zero4(), dPs[w], KAs + TL * w * LDX + 16 * mt, lane);
-            const f4 y = mm<TL, 1, 17, LDX, 1>(zero4(), dPs[w], QAs + TL * w * LDX + 16 * mt, lane);
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                dqa[mt][r] = x[r];
-                dka[mt][r] = y[r];
-            }
-        }
+                for (int r = 0; r < 4; ++r) {
+                    dqa[mt][r] = x[mt][r];
+                    dka[mt][r] = y[mt][r];
+                }
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            // dH = -P^T dY, into Us (V is dead since step 2)
-            const f4 x = mm<TL, 1, 17, LDX, 1>(zero4(), Ps[w], Ys + TL * w * LDX + 16 * dt, lane);
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Us[(TL * w + t_lane + r) * LDX + 16 * dt + lc] = -x[r];
+                for (int r = 0; r < 4; ++r) Us[(TL * w + t_lane + r) * LDX + 16 * dt + lc] = -z[dt][r];
         }
 
         // ---- 5. tile-start states R_b (Ls), kept in the workspace for step 6 ----
 #pragma unroll
         for (int j = 0; j < 16; ++j) Ls[er * LDX + 16 * ec + j] = Zs[er * LDX + 16 * ec + j];
-        __syncthreads();
+        lds_barrier();
         for (int tb = 0; tb < NT; ++tb) {
             {
                 float* dst = rst + static_cast<int64_t>(tb) * M * D + er * D + 16 * ec;
@@ -415,23 +451,22 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
                     KAs[(TL * tb + t_lane + r) * LDX + 16 * w + lc] = ar_s[tb * M + 16 * w + lc] * x[r];
             }
             if (tb + 1 < NT) {
-                __syncthreads();  // every read of R_b done
+                lds_barrier();  // every read of R_b done
                 // R_{b+1} = diag(A_end) R_b - W_b^T H_b: wave w takes slots 16 w .. 16 w + 15
+                f4 x[DT] = {zero4(), zero4(), zero4(), zero4()};
+                mm4<TL, 1, LDX, LDX, 1, 16>(x, Ws + TL * tb * LDX + 16 * w, Hs + TL * tb * LDX, lane);
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const f4 x = mm<TL, 1, LDX, LDX, 1>(zero4(), Ws + TL * tb * LDX + 16 * w, Hs + TL * tb * LDX + 16 * dt,
-                                                        lane);
+                for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int sl = 16 * w + t_lane + r;
                         const int o = sl * LDX + 16 * dt + lc;
-                        Ls[o] = fmaf(ae_s[tb * M + sl], Ls[o], -x[r]);
+                        Ls[o] = fmaf(ae_s[tb * M + sl], Ls[o], -x[dt][r]);
                     }
-                }
-                __syncthreads();
+                lds_barrier();
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 6. tiles in reverse with lambda ----
         {
@@ -439,16 +474,25 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) Ls[er * LDX + 16 * ec + j] = src[j];
         }
-        __syncthreads();
+        lds_barrier();
+        // R_b as this thread stored it, one tile ahead of its use
+        float rb[16];
+        {
+            const float* src = rst + static_cast<int64_t>(NT - 1) * M * D + er * D + 16 * ec;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) rb[j] = src[j];
+        }
         for (int tb = NT - 1; tb >= 0; --tb) {
             {
-                // dA_end = rowdot(R_b, lambda) (R_b as this thread stored it)
-                const float* src = rst + static_cast<int64_t>(tb) * M * D + er * D + 16 * ec;
+                // dA_end = rowdot(R_b, lambda)
                 float s = 0.f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) s = fmaf(src[j], Ls[er * LDX + 16 * ec + j], s);
+                for (int j = 0; j < 16; ++j) s = fmaf(rb[j], Ls[er * LDX + 16 * ec + j], s);
                 s = quad_sum(s);
                 if (ec == 0) dae_s[tb * M + er] = s;
+                const float* src = rst + static_cast<int64_t>(tb > 0 ? tb - 1 : 0) * M * D + er * D + 16 * ec;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) rb[j] = src[j];
             }
             // dW = -H_b lambda^T (slot block w) and dH_b -= W_b lambda (columns 16 w ..)
             const f4 dwx = mm<D, LDX, 1, 1, LDX>(zero4(), Hs + TL * tb * LDX, Ls + 16 * w * LDX, lane);
@@ -457,32 +501,35 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Us[(TL * tb + t_lane + r) * LDX + 16 * w + lc] -= x[r];
             }
-            __syncthreads();  // every read of lambda and of W_b done
+            lds_barrier();  // every read of lambda and of W_b done
             // dW over W_b in Ws (only step 7 reads it, as dW)
 #pragma unroll
             for (int r = 0; r < 4; ++r) Ws[(TL * tb + t_lane + r) * LDX + 16 * w + lc] = -dwx[r];
             // lambda <- diag(A_end) lambda + a_ref (.) QA'^T dY_b: wave w takes slots 16 w ..
+            {
+                f4 x[DT] = {zero4(), zero4(), zero4(), zero4()};
+                mm4<TL, 1, LDX, LDX, 1, 16>(x, QAs + TL * tb * LDX + 16 * w, Ys + TL * tb * LDX, lane);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const f4 x = mm<TL, 1, LDX, LDX, 1>(zero4(), QAs + TL * tb * LDX + 16 * w, Ys + TL * tb * LDX + 16 * dt,
-                                                    lane);
+                for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int sl = 16 * w + t_lane + r;
-                    const int o = sl * LDX + 16 * dt + lc;
-                    Ls[o] = fmaf(ae_s[tb * M + sl], Ls[o], ar_s[tb * M + sl] * x[r]);
-                }
+                    for (int r = 0; r < 4; ++r) {
+                        const int sl = 16 * w + t_lane + r;
+                        const int o = sl * LDX + 16 * dt + lc;
+                        Ls[o] = fmaf(ae_s[tb * M + sl], Ls[o], ar_s[tb * M + sl] * x[dt][r]);
+                    }
             }
-            __syncthreads();
+            lds_barrier();
         }
 
         // ---- 7. per tile: gradients of A, W's suffix products, the gates ----
         float dht[MT][4], dkv[MT][4], dnh[4] = {0.f, 0.f, 0.f, 0.f}, dmu[4] = {0.f, 0.f, 0.f, 0.f};
         float dgt_tok[4] = {0.f, 0.f, 0.f, 0.f}, kqs[MT][4];
+        float kq[4], qv[4], gm[4];  // slot block mt's inputs; block mt + 1's are loaded meanwhile
+        load_in(0, kq, qv, gm);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            float kq[4], qv[4], gm[4];
-            load_in(mt, kq, qv, gm);
+            float kqn[4], qvn[4], gmn[4];
+            load_in(mt + 1 < MT ? mt + 1 : mt, kqn, qvn, gmn);
             TileGates tg;
             tile_gates(kq, gm, mu, hh, ht[mt], lane, tg);
             const float dae = dae_s[w * M + 16 * mt + lc];
@@ -495,11 +542,11 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float ka = tg.kap[r] * tg.ar / tg.A[r];
+                const float ka = tg.kap[r] * tg.ar * tg.rA[r];
                 // dq = dQA' A / a_ref
-                p.dq[bth(tc + t_lane + r) * M + 16 * mt + lc] = dqa[mt][r] * tg.A[r] / tg.ar;
-                dA[r] = dqa[mt][r] * qv[r] / tg.ar - dka[mt][r] * ka / tg.A[r];
-                dk_[r] = dka[mt][r] * tg.ar / tg.A[r] + dwt[r] * tg.sfx[r];
+                p.dq[bth(tc + t_lane + r) * M + 16 * mt + lc] = dqa[mt][r] * tg.A[r] * tg.rar;
+                dA[r] = dqa[mt][r] * qv[r] * tg.rar - dka[mt][r] * ka * tg.rA[r];
+                dk_[r] = dka[mt][r] * tg.ar * tg.rA[r] + dwt[r] * tg.sfx[r];
                 u[r] = dwt[r] * tg.kap[r];
             }
             // the tile's last token: dA_end
@@ -544,6 +591,12 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
                 dkv[mt][r] = da * gm[r];
                 kqs[mt][r] = kq[r];
             }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                kq[r] = kqn[r];
+                qv[r] = qvn[r];
+                gm[r] = gmn[r];
+            }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -569,46 +622,55 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
                 QAs[o] = dht[mt][r];
                 KAs[o] = kqs[mt][r];
             }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 8. dH += dc Z + 2 d|h|^2 H; dV = -dH ----
+        {
+            f4 acc[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            f4 acc;
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = Us[(TL * w + t_lane + r) * LDX + 16 * dt + lc];
-            acc = mm<M, LDX, 1, LDX, 1>(acc, QAs + TL * w * LDX, Zs + 16 * dt, lane);
+                for (int r = 0; r < 4; ++r) acc[dt][r] = Us[(TL * w + t_lane + r) * LDX + 16 * dt + lc];
+            mm4<M, LDX, 1, LDX, 1, 16>(acc, QAs + TL * w * LDX, Zs, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = TL * w + t_lane + r;
-                const float v = fmaf(2.f * dnh_s[t], Hs[t * LDX + 16 * dt + lc], acc[r]);
-                Us[t * LDX + 16 * dt + lc] = v;
-                p.dv[bth(n * C + t) * D + 16 * dt + lc] = -v;
-            }
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = TL * w + t_lane + r;
+                    const float v = fmaf(2.f * dnh_s[t], Hs[t * LDX + 16 * dt + lc], acc[dt][r]);
+                    Us[t * LDX + 16 * dt + lc] = v;
+                    p.dv[bth(n * C + t) * D + 16 * dt + lc] = -v;
+                }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 9. dZ = lambda + dc^T H (+ K^T dH); dK = da gamma (+ dH Z^T) ----
+        {
+            f4 acc[DT];
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-            f4 acc;
+            for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = Ls[(16 * w + t_lane + r) * LDX + 16 * dt + lc];
-            acc = mm<C, 1, LDX, LDX, 1>(acc, QAs + 16 * w, Hs + 16 * dt, lane);
-            if (dec) acc = mm<C, 1, LDX, LDX, 1>(acc, KAs + 16 * w, Us + 16 * dt, lane);
+                for (int r = 0; r < 4; ++r) acc[dt][r] = Ls[(16 * w + t_lane + r) * LDX + 16 * dt + lc];
+            mm4<C, 1, LDX, LDX, 1, 16>(acc, QAs + 16 * w, Hs, lane);
+            if (dec) mm4<C, 1, LDX, LDX, 1, 16>(acc, KAs + 16 * w, Us, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Ls[(16 * w + t_lane + r) * LDX + 16 * dt + lc] = acc[r];
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Ls[(16 * w + t_lane + r) * LDX + 16 * dt + lc] = acc[dt][r];
         }
+        {
+            f4 acc[MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            f4 acc;
+            for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[r] = dkv[mt][r];
-            if (dec) acc = mm<D, LDX, 1, 1, LDX>(acc, Us + TL * w * LDX, Zs + 16 * mt * LDX, lane);
+                for (int r = 0; r < 4; ++r) acc[mt][r] = dkv[mt][r];
+            if (dec) mm4<D, LDX, 1, 1, LDX, 16 * LDX>(acc, Us + TL * w * LDX, Zs, lane);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p.dk[bth(tc + t_lane + r) * M + 16 * mt + lc] = acc[r];
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p.dk[bth(tc + t_lane + r) * M + 16 * mt + lc] = acc[mt][r];
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- 10. back through the chunk-start projection ----
         {
@@ -625,7 +687,7 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) dst[j] = inv * fmaf(-pr, zz[j], dz[j]);
         }
-        __syncthreads();  // the next chunk overwrites every LDS array
+        lds_barrier();  // the next chunk overwrites every LDS array
     }
     {
         const float* src = rst + static_cast<int64_t>(NT) * M * D + er * D + 16 * ec;

@@ -287,7 +287,15 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * tokens' sums over slots: the workspace then ends with their hand-off
  * buffers, B*H*(2 P 8 (d + 4) * 4 + 128 P) bytes.  The result equals one
  * workgroup's (LATTICE_OSR_WGS_ONE) up to the order of those fp32 sums;
- * reruns are bit-identical.  The remaining rules (shapes,
+ * reruns are bit-identical.  Where desc->bwd_form allows it (AUTO or CHUNK;
+ * built for m = d = chunk_size = 64 on that same path), the gradient is
+ * instead taken in its chunk-parallel form on the fp32 matrix cores, one
+ * workgroup per (b,h): per chunk the vector-Jacobian products of the
+ * chunk's matrix form (16-token tiles), the gate gradients by recursions
+ * over the tile's tokens; the same workspace and the same result up to fp32
+ * rounding (the token walk's to 1e-4 of RMS; with forget gates mu near 0 the
+ * tile's gate products span many decades and the two agree to 5e-3).  The
+ * remaining rules (shapes,
  * chunk sizes, alignment of the inputs, status codes, asynchrony) are those
  * of lattice_osr_fwd_chunked.
  */
