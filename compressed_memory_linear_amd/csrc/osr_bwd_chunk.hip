@@ -57,7 +57,7 @@ __device__ __forceinline__ f4 mm(f4 acc, const float* a, const float* b, int lan
     const int r = lane & 15, kq = lane >> 4;
     const float* pa = a + r * AI + kq * AK;
     const float* pb = b + kq * BK + r * BJ;
-#pragma unroll
+#pragma unroll 8
     for (int k0 = 0; k0 < K; k0 += 4) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k0 * AK], pb[k0 * BK], acc, 0, 0, 0);
     return acc;
 }
@@ -216,33 +216,60 @@ __device__ __forceinline__ void tile_gates(const float (&kq)[4], const float (&g
     o.rar = __builtin_amdgcn_rcpf(o.ar);
 }
 
+// Two output tiles that share the A operand (acc[j] += A B_j, B_j at b + j * BS).
+template <int K, int AI, int AK, int BK, int BJ, int BS>
+__device__ __forceinline__ void mm2(f4 (&acc)[2], const float* a, const float* b, int lane) {
+    const int r = lane & 15, kq = lane >> 4;
+    const float* pa = a + r * AI + kq * AK;
+    const float* pb = b + kq * BK + r * BJ;
+#pragma unroll 8
+    for (int k0 = 0; k0 < K; k0 += 4) {
+        const float av = pa[k0 * AK];
+        const float b0 = pb[k0 * BK], b1 = pb[k0 * BK + BS];
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b0, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b1, acc[1], 0, 0, 0);
+    }
+}
+
+// Sum over the 8 consecutive lanes of an element row (the M x D passes).
+__device__ __forceinline__ float oct_sum(float x) {
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
+    x += __shfl_xor(x, 4, 64);
+    return x;
+}
+
 template <int M, int D, int C, typename TIn, bool DYB>
 struct Cfg {
     static constexpr int LDX = 68;  // row stride (floats) of the LDS matrices
     static constexpr int NT = C / TL;
-    static constexpr int NW = NT;   // wave b holds tile b
     static constexpr int MT = M / 16, DT = D / 16;
+    static constexpr int NWAVE = 8;  // waves (b, hf): tile b = w & 3, half hf = w >> 2
+    static constexpr int NTH = 64 * NWAVE;
     static_assert(M == 64 && D == 64 && C == 64, "built for m = d = C = 64");
-    static_assert(MT == NW, "the M x D products give wave w the slot block w");
+    static_assert(NT == 4 && MT == 4 && DT == 4, "4 tiles, 4 slot blocks, 4 column blocks");
 };
 
 template <int M, int D, int C, typename TIn, bool DYB>
-__global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void osr_bwd_chunk_kernel(BwdParams p) {
     using G = Cfg<M, D, C, TIn, DYB>;
-    constexpr int LDX = G::LDX, NT = G::NT, MT = G::MT, DT = G::DT;
+    constexpr int LDX = G::LDX, NT = G::NT;
     __shared__ __attribute__((aligned(16))) float Zs[M * LDX];   // Z
     __shared__ __attribute__((aligned(16))) float Hs[C * LDX];   // H
     __shared__ __attribute__((aligned(16))) float Ys[C * LDX];   // dY
     __shared__ __attribute__((aligned(16))) float Us[C * LDX];   // V, then dH
     __shared__ __attribute__((aligned(16))) float Ls[M * LDX];   // R_b, then lambda, then dZ
     __shared__ __attribute__((aligned(16))) float QAs[C * LDX];  // Q A / a_ref, then dc
-    __shared__ __attribute__((aligned(16))) float KAs[C * LDX];  // kappa a_ref / A, then K
-    __shared__ __attribute__((aligned(16))) float Ws[C * LDX];   // K, then W
+    __shared__ __attribute__((aligned(16))) float KAs[C * LDX];  // kappa a_ref / A, then dQA' parts, then K
+    __shared__ __attribute__((aligned(16))) float Ws[C * LDX];   // K, then W, then dW
     __shared__ float Ps[NT][16 * 17], dPs[NT][16 * 17];          // per tile: P, dP ([t][u])
-    __shared__ float nh_s[C], dnh_s[C], ae_s[NT * M], ar_s[NT * M], dae_s[NT * M], invn_s[M];
+    __shared__ float part_s[2][3][C];  // per-token sums of the two halves: |h|^2, d|h|^2, dmu (and dgamma)
+    __shared__ float pg_s[2][C];
+    __shared__ float ae_s[NT * M], ar_s[NT * M], dae_s[NT * M], invn_s[M];
 
     const int bh = blockIdx.x, b = bh / p.f.H, hd = bh % p.f.H;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lg = lane >> 4, lc = lane & 15;
+    const int tw = w & 3, hf = w >> 2;  // this wave's tile and half (slot / column blocks 2 hf, 2 hf + 1)
     const int T = p.f.T, NC = T / C;
     const bool dec = p.f.mode == 0;
     const bool gps = p.f.gamma_per_slot != 0;
@@ -253,84 +280,69 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
     const TIn* mp = static_cast<const TIn*>(p.f.mu);
     float* ws = p.ws + static_cast<int64_t>(bh) * bwd_floats_per_bh<M, D>(T, C);
     const float* sck = ws;                                      // [NC+1][M][D] chunk-start states
-    float* rst = ws + static_cast<int64_t>(NC + 1) * M * D;     // [NT][M][D] tile-start states
+    float* rst = ws + static_cast<int64_t>(NC + 1) * M * D;     // [NT][M][D] tile-start states, then lambda
     auto bth = [&](int t) { return (static_cast<int64_t>(b) * T + t) * p.f.H + hd; };
 
-    // M x D element passes: row er, columns 16 ec .. 16 ec + 15
-    const int er = tid >> 2, ec = tid & 3;
-    float lam[16];  // lambda (gradient of the chunk-end state) between chunks, this thread's elements
+    // M x D element passes: row er, columns 8 ec .. 8 ec + 7
+    const int er = tid >> 3, ec = tid & 7;
+    const int eo = er * LDX + 8 * ec, go = er * D + 8 * ec;
 
-    // the returned state is the end state projected: its backward
     {
-        const float* s = sck + static_cast<int64_t>(NC) * M * D + er * D + 16 * ec;
-        const float* g = p.dstate_out + static_cast<int64_t>(bh) * M * D + er * D + 16 * ec;
-        float sv[16], n2 = 0.f, pr = 0.f;
+        // the returned state is the end state projected: its backward; lambda lives in the
+        // workspace between chunks (each thread its own elements)
+        const float* s = sck + static_cast<int64_t>(NC) * M * D + go;
+        const float* g = p.dstate_out + static_cast<int64_t>(bh) * M * D + go;
+        float sv[8], lv[8], n2 = 0.f, pr = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 8; ++j) {
             sv[j] = s[j];
-            lam[j] = g[j];
+            lv[j] = g[j];
             n2 += sv[j] * sv[j];
         }
-        const float inv = rsqrtf(quad_sum(n2));
+        const float inv = rsqrtf(oct_sum(n2));
 #pragma unroll
-        for (int j = 0; j < 16; ++j) pr += sv[j] * inv * lam[j];
-        pr = quad_sum(pr);
+        for (int j = 0; j < 8; ++j) pr += sv[j] * inv * lv[j];
+        pr = oct_sum(pr);
+        float* dst = rst + static_cast<int64_t>(NT) * M * D + go;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) lam[j] = inv * (lam[j] - pr * sv[j] * inv);
-    }
-
-    {
-        // lambda lives in the workspace between chunks (each thread its own elements)
-        float* dst = rst + static_cast<int64_t>(NT) * M * D + er * D + 16 * ec;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dst[j] = lam[j];
+        for (int j = 0; j < 8; ++j) dst[j] = inv * (lv[j] - pr * sv[j] * inv);
     }
     const int t_lane = 4 * lg;  // first token (within the tile) of this lane's rows
     for (int n = NC - 1; n >= 0; --n) {
-        const int tc = n * C + TL * w;  // first token of this wave's tile
-        // ---- 1. Z, V, dY, K into LDS; this tile's inputs into registers ----
+        const int tc = n * C + TL * tw;  // first token of this wave's tile
+        // ---- 1. Z, V, dY, K into LDS; this tile's mu ----
         {
-            const float* s = sck + static_cast<int64_t>(n) * M * D + er * D + 16 * ec;
-            float sv[16], n2 = 0.f;
+            const float* s = sck + static_cast<int64_t>(n) * M * D + go;
+            float sv[8], n2 = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
+            for (int j = 0; j < 8; ++j) {
                 sv[j] = s[j];
                 n2 += sv[j] * sv[j];
             }
-            const float inv = rsqrtf(quad_sum(n2));
+            const float inv = rsqrtf(oct_sum(n2));
 #pragma unroll
-            for (int j = 0; j < 16; ++j) Zs[er * LDX + 16 * ec + j] = sv[j] * inv;
+            for (int j = 0; j < 8; ++j) Zs[eo + j] = sv[j] * inv;
             if (ec == 0) invn_s[er] = inv;
             // token rows: V and dY [C][D], K [C][M] (er is the token here)
             const int64_t tv = bth(n * C + er);
 #pragma unroll
-            for (int j = 0; j < 16; j += 4) {
-                const float4 v4 = ld4<TIn>(vp, tv * D + 16 * ec + j);
-                Us[er * LDX + 16 * ec + j + 0] = v4.x;
-                Us[er * LDX + 16 * ec + j + 1] = v4.y;
-                Us[er * LDX + 16 * ec + j + 2] = v4.z;
-                Us[er * LDX + 16 * ec + j + 3] = v4.w;
+            for (int j = 0; j < 8; j += 4) {
+                const float4 v4 = ld4<TIn>(vp, tv * D + 8 * ec + j);
                 float4 y4;
                 if constexpr (DYB)
-                    y4 = ld4<uint16_t>(static_cast<const uint16_t*>(p.dy), tv * D + 16 * ec + j);
+                    y4 = ld4<uint16_t>(static_cast<const uint16_t*>(p.dy), tv * D + 8 * ec + j);
                 else
-                    y4 = ld4<float>(static_cast<const float*>(p.dy), tv * D + 16 * ec + j);
-                Ys[er * LDX + 16 * ec + j + 0] = y4.x;
-                Ys[er * LDX + 16 * ec + j + 1] = y4.y;
-                Ys[er * LDX + 16 * ec + j + 2] = y4.z;
-                Ys[er * LDX + 16 * ec + j + 3] = y4.w;
-                const float4 k4 = ld4<TIn>(kp, tv * M + 16 * ec + j);
-                Ws[er * LDX + 16 * ec + j + 0] = k4.x;
-                Ws[er * LDX + 16 * ec + j + 1] = k4.y;
-                Ws[er * LDX + 16 * ec + j + 2] = k4.z;
-                Ws[er * LDX + 16 * ec + j + 3] = k4.w;
+                    y4 = ld4<float>(static_cast<const float*>(p.dy), tv * D + 8 * ec + j);
+                const float4 k4 = ld4<TIn>(kp, tv * M + 8 * ec + j);
+                *reinterpret_cast<float4*>(Us + eo + j) = v4;
+                *reinterpret_cast<float4*>(Ys + eo + j) = y4;
+                *reinterpret_cast<float4*>(Ws + eo + j) = k4;
             }
         }
-        // this tile's mu (token tc + t_lane + r); its q, k, gamma are loaded per
-        // slot block where they are used (slot 16 mt + lc)
         float mu[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) mu[r] = ld<TIn>(mp, bth(tc + t_lane + r));
+        // this wave's slot blocks 2 hf + j of its tile: k, q, gamma
         auto load_in = [&](int mt, float (&kq)[4], float (&qv)[4], float (&gm)[4]) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -340,213 +352,236 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
                 gm[r] = gps ? ld<TIn>(gp, tt * M + 16 * mt + lc) : ld<TIn>(gp, tt);
             }
         };
+        float kq3[2][4], qv3[2][4], gm3[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) load_in(2 * hf + j, kq3[j], qv3[j], gm3[j]);
         lds_barrier();
 
-        // ---- 2. H = K Z - V for this wave's tile; |h|^2 ----
-        float hh[4] = {0.f, 0.f, 0.f, 0.f};
+        // ---- 2. H = K Z - V: tile tw, column blocks 2 hf, 2 hf + 1; |h|^2 ----
+        float hh[4];
         {
-            f4 acc[DT];
+            f4 acc[2];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[dt][r] = -Us[(TL * w + t_lane + r) * LDX + 16 * dt + lc];
-            if (dec) mm4<M, LDX, 1, LDX, 1, 16>(acc, Ws + TL * w * LDX, Zs, lane);
+                for (int r = 0; r < 4; ++r) acc[j][r] = -Us[(TL * tw + t_lane + r) * LDX + 16 * (2 * hf + j) + lc];
+            if (dec) mm2<M, LDX, 1, LDX, 1, 16>(acc, Ws + TL * tw * LDX, Zs + 32 * hf, lane);
+            float ph[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    Hs[(TL * w + t_lane + r) * LDX + 16 * dt + lc] = acc[dt][r];
-                    hh[r] += acc[dt][r] * acc[dt][r];
+                    Hs[(TL * tw + t_lane + r) * LDX + 16 * (2 * hf + j) + lc] = acc[j][r];
+                    ph[r] += acc[j][r] * acc[j][r];
                 }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ph[r] = row16_sum(ph[r]);
+            if (lc == 0)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part_s[hf][0][TL * tw + t_lane + r] = ph[r];
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) hh[r] = row16_sum(hh[r]);
-        if (lc == 0)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) nh_s[TL * w + t_lane + r] = hh[r];
         lds_barrier();  // H visible; every wave is done with K in Ws
+#pragma unroll
+        for (int r = 0; r < 4; ++r) hh[r] = part_s[0][0][TL * tw + t_lane + r] + part_s[1][0][TL * tw + t_lane + r];
 
-        // ---- 3. c = H Z^T (this tile) and the gates ----
-        float ht[MT][4];
-        float kq3[MT][4], qv3[MT][4], gm3[MT][4];  // this tile's inputs, loaded before the product
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) load_in(mt, kq3[mt], qv3[mt], gm3[mt]);
+        // ---- 3. c = H Z^T (tile tw, slot blocks 2 hf + j) and the gates ----
+        float ht[2][4];
         {
-            f4 acc[MT] = {zero4(), zero4(), zero4(), zero4()};
-            mm4<D, LDX, 1, 1, LDX, 16 * LDX>(acc, Hs + TL * w * LDX, Zs, lane);
+            f4 acc[2] = {zero4(), zero4()};
+            mm2<D, LDX, 1, 1, LDX, 16 * LDX>(acc, Hs + TL * tw * LDX, Zs + 32 * hf * LDX, lane);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ht[mt][r] = acc[mt][r];
+                for (int r = 0; r < 4; ++r) ht[j][r] = acc[j][r];
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+        for (int j = 0; j < 2; ++j) {
+            const int mt = 2 * hf + j;
             TileGates tg;
-            tile_gates(kq3[mt], gm3[mt], mu, hh, ht[mt], lane, tg);
+            tile_gates(kq3[j], gm3[j], mu, hh, ht[j], lane, tg);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int o = (TL * w + t_lane + r) * LDX + 16 * mt + lc;
-                QAs[o] = qv3[mt][r] * tg.A[r] * tg.rar;
+                const int o = (TL * tw + t_lane + r) * LDX + 16 * mt + lc;
+                QAs[o] = qv3[j][r] * tg.A[r] * tg.rar;
                 KAs[o] = tg.kap[r] * tg.ar * tg.rA[r];
                 Ws[o] = tg.kap[r] * tg.sfx[r];
             }
             if (lg == 0) {
-                ae_s[w * M + 16 * mt + lc] = tg.ae;
-                ar_s[w * M + 16 * mt + lc] = tg.ar;
+                ae_s[tw * M + 16 * mt + lc] = tg.ae;
+                ar_s[tw * M + 16 * mt + lc] = tg.ar;
             }
         }
         lds_barrier();
 
-        // ---- 4. per tile: P, dP and the lambda-free gradients ----
+        // ---- 4. per tile: P (half 0), dP (half 1), then the lambda-free gradients ----
         {
-            const f4 pa = mm<M, LDX, 1, 1, LDX>(zero4(), QAs + TL * w * LDX, KAs + TL * w * LDX, lane);
-            const f4 pd = mm<D, LDX, 1, 1, LDX>(zero4(), Ys + TL * w * LDX, Hs + TL * w * LDX, lane);
+            f4 x = zero4();
+            if (hf == 0)
+                x = mm<M, LDX, 1, 1, LDX>(x, QAs + TL * tw * LDX, KAs + TL * tw * LDX, lane);
+            else
+                x = mm<D, LDX, 1, 1, LDX>(x, Ys + TL * tw * LDX, Hs + TL * tw * LDX, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool causal = lc <= t_lane + r;  // u <= t
-                Ps[w][(t_lane + r) * 17 + lc] = causal ? pa[r] : 0.f;
-                dPs[w][(t_lane + r) * 17 + lc] = causal ? -pd[r] : 0.f;
+                if (hf == 0)
+                    Ps[tw][(t_lane + r) * 17 + lc] = causal ? x[r] : 0.f;
+                else
+                    dPs[tw][(t_lane + r) * 17 + lc] = causal ? -x[r] : 0.f;
             }
         }
         lds_barrier();
-        float dqa[MT][4], dka[MT][4];
+        float dqa[2][4], dka[2][4];  // (dqa goes to KAs at the next barrier)
         {
-            // dQA' = dP KA', dKA' = dP^T QA', dH = -P^T dY (into Us: V is dead since step 2)
-            f4 x[MT] = {zero4(), zero4(), zero4(), zero4()}, y[MT] = {zero4(), zero4(), zero4(), zero4()};
-            f4 z[DT] = {zero4(), zero4(), zero4(), zero4()};
-            mm4<TL, 17, 1, LDX, 1, 16>(x, dPs[w], KAs + TL * w * LDX, lane);
-            mm4<TL, 1, 17, LDX, 1, 16>(y, dPs[w], QAs + TL * w * LDX, lane);
-            mm4<TL, 1, 17, LDX, 1, 16>(z, Ps[w], Ys + TL * w * LDX, lane);
+            // dQA' = dP KA', dKA' = dP^T QA' (slot blocks 2 hf + j), dH = -P^T dY (column blocks 2 hf + j,
+            // into Us: V is dead since step 2)
+            f4 x[2] = {zero4(), zero4()}, y[2] = {zero4(), zero4()}, z[2] = {zero4(), zero4()};
+            mm2<TL, 17, 1, LDX, 1, 16>(x, dPs[tw], KAs + TL * tw * LDX + 32 * hf, lane);
+            mm2<TL, 1, 17, LDX, 1, 16>(y, dPs[tw], QAs + TL * tw * LDX + 32 * hf, lane);
+            mm2<TL, 1, 17, LDX, 1, 16>(z, Ps[tw], Ys + TL * tw * LDX + 32 * hf, lane);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    dqa[mt][r] = x[mt][r];
-                    dka[mt][r] = y[mt][r];
+                    dqa[j][r] = x[j][r];
+                    dka[j][r] = y[j][r];
+                    Us[(TL * tw + t_lane + r) * LDX + 16 * (2 * hf + j) + lc] = -z[j][r];
                 }
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Us[(TL * w + t_lane + r) * LDX + 16 * dt + lc] = -z[dt][r];
         }
 
         // ---- 5. tile-start states R_b (Ls), kept in the workspace for step 6 ----
+        lds_barrier();  // every read of KAs (as kappa a_ref / A) done: dQA' so far into it
 #pragma unroll
-        for (int j = 0; j < 16; ++j) Ls[er * LDX + 16 * ec + j] = Zs[er * LDX + 16 * ec + j];
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) KAs[(TL * tw + t_lane + r) * LDX + 16 * (2 * hf + j) + lc] = dqa[j][r];
+        {
+            float* dst = rst + go;
+            const float4 z0 = *reinterpret_cast<const float4*>(Zs + eo);
+            const float4 z1 = *reinterpret_cast<const float4*>(Zs + eo + 4);
+            *reinterpret_cast<float4*>(Ls + eo) = z0;
+            *reinterpret_cast<float4*>(Ls + eo + 4) = z1;
+            *reinterpret_cast<float4*>(dst) = z0;
+            *reinterpret_cast<float4*>(dst + 4) = z1;
+        }
         lds_barrier();
         for (int tb = 0; tb < NT; ++tb) {
-            {
-                float* dst = rst + static_cast<int64_t>(tb) * M * D + er * D + 16 * ec;
+            if (hf == 0) {
+                // a_ref (.) dY_b R_b^T (the rest of dQA'), slot block tw, into KAs
+                const f4 x = mm<D, LDX, 1, 1, LDX>(zero4(), Ys + TL * tb * LDX, Ls + 16 * tw * LDX, lane);
 #pragma unroll
-                for (int j = 0; j < 16; j += 4)
-                    *reinterpret_cast<float4*>(dst + j) =
-                        make_float4(Ls[er * LDX + 16 * ec + j], Ls[er * LDX + 16 * ec + j + 1],
-                                    Ls[er * LDX + 16 * ec + j + 2], Ls[er * LDX + 16 * ec + j + 3]);
-            }
-            {
-                // a_ref (.) dY_b R_b^T (the rest of dQA'), slot block w, into KAs (free since step 4)
-                const f4 x = mm<D, LDX, 1, 1, LDX>(zero4(), Ys + TL * tb * LDX, Ls + 16 * w * LDX, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    KAs[(TL * tb + t_lane + r) * LDX + 16 * w + lc] = ar_s[tb * M + 16 * w + lc] * x[r];
+                for (int r = 0; r < 4; ++r) {
+                    // (the tile's owner wrote its part of dQA' here before the barrier above)
+                    const int o = (TL * tb + t_lane + r) * LDX + 16 * tw + lc;
+                    KAs[o] = fmaf(ar_s[tb * M + 16 * tw + lc], x[r], KAs[o]);
+                }
             }
             if (tb + 1 < NT) {
                 lds_barrier();  // every read of R_b done
-                // R_{b+1} = diag(A_end) R_b - W_b^T H_b: wave w takes slots 16 w .. 16 w + 15
-                f4 x[DT] = {zero4(), zero4(), zero4(), zero4()};
-                mm4<TL, 1, LDX, LDX, 1, 16>(x, Ws + TL * tb * LDX + 16 * w, Hs + TL * tb * LDX, lane);
+                // R_{b+1} = diag(A_end) R_b - W_b^T H_b: slot block tw, column blocks 2 hf + j
+                f4 x[2] = {zero4(), zero4()};
+                mm2<TL, 1, LDX, LDX, 1, 16>(x, Ws + TL * tb * LDX + 16 * tw, Hs + TL * tb * LDX + 32 * hf, lane);
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int sl = 16 * w + t_lane + r;
-                        const int o = sl * LDX + 16 * dt + lc;
-                        Ls[o] = fmaf(ae_s[tb * M + sl], Ls[o], -x[dt][r]);
+                        const int sl = 16 * tw + t_lane + r;
+                        const int o = sl * LDX + 16 * (2 * hf + j) + lc;
+                        Ls[o] = fmaf(ae_s[tb * M + sl], Ls[o], -x[j][r]);
                     }
                 lds_barrier();
+                float* dst = rst + static_cast<int64_t>(tb + 1) * M * D + go;
+                *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(Ls + eo);
+                *reinterpret_cast<float4*>(dst + 4) = *reinterpret_cast<const float4*>(Ls + eo + 4);
             }
         }
         lds_barrier();
 
         // ---- 6. tiles in reverse with lambda ----
         {
-            const float* src = rst + static_cast<int64_t>(NT) * M * D + er * D + 16 * ec;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) Ls[er * LDX + 16 * ec + j] = src[j];
+            const float* src = rst + static_cast<int64_t>(NT) * M * D + go;
+            *reinterpret_cast<float4*>(Ls + eo) = *reinterpret_cast<const float4*>(src);
+            *reinterpret_cast<float4*>(Ls + eo + 4) = *reinterpret_cast<const float4*>(src + 4);
         }
         lds_barrier();
-        // R_b as this thread stored it, one tile ahead of its use
-        float rb[16];
+        float rb[8];  // R_b as this thread stored it, one tile ahead of its use
         {
-            const float* src = rst + static_cast<int64_t>(NT - 1) * M * D + er * D + 16 * ec;
+            const float* src = rst + static_cast<int64_t>(NT - 1) * M * D + go;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) rb[j] = src[j];
+            for (int j = 0; j < 8; ++j) rb[j] = src[j];
         }
         for (int tb = NT - 1; tb >= 0; --tb) {
             {
                 // dA_end = rowdot(R_b, lambda)
                 float s = 0.f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) s = fmaf(rb[j], Ls[er * LDX + 16 * ec + j], s);
-                s = quad_sum(s);
+                for (int j = 0; j < 8; ++j) s = fmaf(rb[j], Ls[eo + j], s);
+                s = oct_sum(s);
                 if (ec == 0) dae_s[tb * M + er] = s;
-                const float* src = rst + static_cast<int64_t>(tb > 0 ? tb - 1 : 0) * M * D + er * D + 16 * ec;
+                const float* src = rst + static_cast<int64_t>(tb > 0 ? tb - 1 : 0) * M * D + go;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) rb[j] = src[j];
+                for (int j = 0; j < 8; ++j) rb[j] = src[j];
             }
-            // dW = -H_b lambda^T (slot block w) and dH_b -= W_b lambda (columns 16 w ..)
-            const f4 dwx = mm<D, LDX, 1, 1, LDX>(zero4(), Hs + TL * tb * LDX, Ls + 16 * w * LDX, lane);
-            {
-                const f4 x = mm<M, LDX, 1, LDX, 1>(zero4(), Ws + TL * tb * LDX, Ls + 16 * w, lane);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Us[(TL * tb + t_lane + r) * LDX + 16 * w + lc] -= x[r];
-            }
+            // half 0: dW = -H_b lambda^T (slot block tw); half 1: dH_b -= W_b lambda (column block tw)
+            f4 x;
+            if (hf == 0)
+                x = mm<D, LDX, 1, 1, LDX>(zero4(), Hs + TL * tb * LDX, Ls + 16 * tw * LDX, lane);
+            else
+                x = mm<M, LDX, 1, LDX, 1>(zero4(), Ws + TL * tb * LDX, Ls + 16 * tw, lane);
             lds_barrier();  // every read of lambda and of W_b done
-            // dW over W_b in Ws (only step 7 reads it, as dW)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) Ws[(TL * tb + t_lane + r) * LDX + 16 * w + lc] = -dwx[r];
-            // lambda <- diag(A_end) lambda + a_ref (.) QA'^T dY_b: wave w takes slots 16 w ..
+            for (int r = 0; r < 4; ++r) {
+                const int o = (TL * tb + t_lane + r) * LDX + 16 * tw + lc;
+                if (hf == 0)
+                    Ws[o] = -x[r];  // dW over W_b (only step 7 reads it, as dW)
+                else
+                    Us[o] -= x[r];
+            }
+            // lambda <- diag(A_end) lambda + a_ref (.) QA'^T dY_b: slot block tw, column blocks 2 hf + j
             {
-                f4 x[DT] = {zero4(), zero4(), zero4(), zero4()};
-                mm4<TL, 1, LDX, LDX, 1, 16>(x, QAs + TL * tb * LDX + 16 * w, Ys + TL * tb * LDX, lane);
+                f4 y[2] = {zero4(), zero4()};
+                mm2<TL, 1, LDX, LDX, 1, 16>(y, QAs + TL * tb * LDX + 16 * tw, Ys + TL * tb * LDX + 32 * hf, lane);
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int sl = 16 * w + t_lane + r;
-                        const int o = sl * LDX + 16 * dt + lc;
-                        Ls[o] = fmaf(ae_s[tb * M + sl], Ls[o], ar_s[tb * M + sl] * x[dt][r]);
+                        const int sl = 16 * tw + t_lane + r;
+                        const int o = sl * LDX + 16 * (2 * hf + j) + lc;
+                        Ls[o] = fmaf(ae_s[tb * M + sl], Ls[o], ar_s[tb * M + sl] * y[j][r]);
                     }
             }
             lds_barrier();
         }
 
-        // ---- 7. per tile: gradients of A, W's suffix products, the gates ----
-        float dht[MT][4], dkv[MT][4], dnh[4] = {0.f, 0.f, 0.f, 0.f}, dmu[4] = {0.f, 0.f, 0.f, 0.f};
-        float dgt_tok[4] = {0.f, 0.f, 0.f, 0.f}, kqs[MT][4];
-        float kq[4], qv[4], gm[4];  // slot block mt's inputs; block mt + 1's are loaded meanwhile
-        load_in(0, kq, qv, gm);
+        // ---- 7. per tile and half: gradients of A, W's suffix products, the gates ----
+        float dht[2][4], dkv[2][4], dnh[4] = {0.f, 0.f, 0.f, 0.f}, dmu[4] = {0.f, 0.f, 0.f, 0.f};
+        float dgt_tok[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            float kqn[4], qvn[4], gmn[4];
-            load_in(mt + 1 < MT ? mt + 1 : mt, kqn, qvn, gmn);
+        for (int j = 0; j < 2; ++j) load_in(2 * hf + j, kq3[j], qv3[j], gm3[j]);  // (again: not kept since step 3)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            mu[r] = ld<TIn>(mp, bth(tc + t_lane + r));
+            hh[r] = part_s[0][0][TL * tw + t_lane + r] + part_s[1][0][TL * tw + t_lane + r];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int mt = 2 * hf + j;
             TileGates tg;
-            tile_gates(kq, gm, mu, hh, ht[mt], lane, tg);
-            const float dae = dae_s[w * M + 16 * mt + lc];
+            tile_gates(kq3[j], gm3[j], mu, hh, ht[j], lane, tg);
+            const float dae = dae_s[tw * M + 16 * mt + lc];
             float dA[4], dk_[4], u[4], X[4], Xp[4], dwt[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int o = (TL * w + t_lane + r) * LDX + 16 * mt + lc;
-                dqa[mt][r] += KAs[o];
+                const int o = (TL * tw + t_lane + r) * LDX + 16 * mt + lc;
+                dqa[j][r] = KAs[o];
                 dwt[r] = Ws[o];
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float ka = tg.kap[r] * tg.ar * tg.rA[r];
                 // dq = dQA' A / a_ref
-                p.dq[bth(tc + t_lane + r) * M + 16 * mt + lc] = dqa[mt][r] * tg.A[r] * tg.rar;
-                dA[r] = dqa[mt][r] * qv[r] * tg.rar - dka[mt][r] * ka * tg.rA[r];
-                dk_[r] = dka[mt][r] * tg.ar * tg.rA[r] + dwt[r] * tg.sfx[r];
+                p.dq[bth(tc + t_lane + r) * M + 16 * mt + lc] = dqa[j][r] * tg.A[r] * tg.rar;
+                dA[r] = dqa[j][r] * qv3[j][r] * tg.rar - dka[j][r] * ka * tg.rA[r];
+                dk_[r] = dka[j][r] * tg.ar * tg.rA[r] + dwt[r] * tg.sfx[r];
                 u[r] = dwt[r] * tg.kap[r];
             }
             // the tile's last token: dA_end
@@ -572,30 +607,23 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const float a = tg.a[r], bt_ = tg.beta[r], wv = tg.wv[r];
-                const bool msk = hh[r] - ht[mt][r] * ht[mt][r] > 0.f;
-                const float dbeta = dg[r] * (mu[r] + a * ht[mt][r]) + dk_[r] * a;
+                const bool msk = hh[r] - ht[j][r] * ht[j][r] > 0.f;
+                const float dbeta = dg[r] * (mu[r] + a * ht[j][r]) + dk_[r] * a;
                 float dc = dg[r] * tg.kap[r];
-                float da = dg[r] * bt_ * ht[mt][r] + dk_[r] * bt_;
+                float da = dg[r] * bt_ * ht[j][r] + dk_[r] * bt_;
                 const float tb_ = -0.5f * bt_ * bt_ * bt_ * dbeta;
                 dmu[r] += dg[r] * bt_ + 2.f * mu[r] * tb_;
                 da = fmaf(2.f * a * wv, tb_, da);
                 const float dw = msk ? a * a * tb_ : 0.f;
                 dnh[r] += dw;
-                dc -= 2.f * ht[mt][r] * dw;
-                dht[mt][r] = dc;
-                const float dgam = da * kq[r];
+                dc -= 2.f * ht[j][r] * dw;
+                dht[j][r] = dc;
+                const float dgam = da * kq3[j][r];
                 if (gps)
                     p.dgamma[bth(tc + t_lane + r) * M + 16 * mt + lc] = dgam;
                 else
                     dgt_tok[r] += dgam;
-                dkv[mt][r] = da * gm[r];
-                kqs[mt][r] = kq[r];
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                kq[r] = kqn[r];
-                qv[r] = qvn[r];
-                gm[r] = gmn[r];
+                dkv[j][r] = da * gm3[j][r];
             }
         }
 #pragma unroll
@@ -607,93 +635,104 @@ __global__ __launch_bounds__(256) void osr_bwd_chunk_kernel(BwdParams p) {
         if (lc == 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int64_t tt = bth(tc + t_lane + r);
-                p.dmu[tt] = dmu[r];
-                if (!gps) p.dgamma[tt] = dgt_tok[r];
-                dnh_s[TL * w + t_lane + r] = dnh[r];
+                const int t = TL * tw + t_lane + r;
+                part_s[hf][1][t] = dnh[r];
+                part_s[hf][2][t] = dmu[r];
+                pg_s[hf][t] = dgt_tok[r];
             }
         }
         // dc into QAs (token-major), K into KAs (decoding objective: K^T dH)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int o = (TL * w + t_lane + r) * LDX + 16 * mt + lc;
-                QAs[o] = dht[mt][r];
-                KAs[o] = kqs[mt][r];
+                const int o = (TL * tw + t_lane + r) * LDX + 16 * (2 * hf + j) + lc;
+                QAs[o] = dht[j][r];
+                KAs[o] = kq3[j][r];
             }
         lds_barrier();
+        if (hf == 0 && lc == 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = TL * tw + t_lane + r;
+                const int64_t tt = bth(n * C + t);
+                p.dmu[tt] = part_s[0][2][t] + part_s[1][2][t];
+                if (!gps) p.dgamma[tt] = pg_s[0][t] + pg_s[1][t];
+            }
+        }
 
-        // ---- 8. dH += dc Z + 2 d|h|^2 H; dV = -dH ----
+        // ---- 8. dH += dc Z + 2 d|h|^2 H (tile tw, column blocks 2 hf + j); dV = -dH ----
         {
-            f4 acc[DT];
+            f4 acc[2];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[dt][r] = Us[(TL * w + t_lane + r) * LDX + 16 * dt + lc];
-            mm4<M, LDX, 1, LDX, 1, 16>(acc, QAs + TL * w * LDX, Zs, lane);
+                for (int r = 0; r < 4; ++r) acc[j][r] = Us[(TL * tw + t_lane + r) * LDX + 16 * (2 * hf + j) + lc];
+            mm2<M, LDX, 1, LDX, 1, 16>(acc, QAs + TL * tw * LDX, Zs + 32 * hf, lane);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = TL * w + t_lane + r;
-                    const float v = fmaf(2.f * dnh_s[t], Hs[t * LDX + 16 * dt + lc], acc[dt][r]);
-                    Us[t * LDX + 16 * dt + lc] = v;
-                    p.dv[bth(n * C + t) * D + 16 * dt + lc] = -v;
+                    const int t = TL * tw + t_lane + r, c = 16 * (2 * hf + j) + lc;
+                    const float dn = part_s[0][1][t] + part_s[1][1][t];
+                    const float v = fmaf(2.f * dn, Hs[t * LDX + c], acc[j][r]);
+                    Us[t * LDX + c] = v;
+                    p.dv[bth(n * C + t) * D + c] = -v;
                 }
         }
         lds_barrier();
 
-        // ---- 9. dZ = lambda + dc^T H (+ K^T dH); dK = da gamma (+ dH Z^T) ----
+        // ---- 9. dZ = lambda + dc^T H (+ K^T dH) (slot block tw, column blocks 2 hf + j);
+        //         dK = da gamma (+ dH Z^T) (tile tw, slot blocks 2 hf + j) ----
         {
-            f4 acc[DT];
+            f4 acc[2];
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[dt][r] = Ls[(16 * w + t_lane + r) * LDX + 16 * dt + lc];
-            mm4<C, 1, LDX, LDX, 1, 16>(acc, QAs + 16 * w, Hs, lane);
-            if (dec) mm4<C, 1, LDX, LDX, 1, 16>(acc, KAs + 16 * w, Us, lane);
+                for (int r = 0; r < 4; ++r) acc[j][r] = Ls[(16 * tw + t_lane + r) * LDX + 16 * (2 * hf + j) + lc];
+            mm2<C, 1, LDX, LDX, 1, 16>(acc, QAs + 16 * tw, Hs + 32 * hf, lane);
+            if (dec) mm2<C, 1, LDX, LDX, 1, 16>(acc, KAs + 16 * tw, Us + 32 * hf, lane);
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Ls[(16 * w + t_lane + r) * LDX + 16 * dt + lc] = acc[dt][r];
+                for (int r = 0; r < 4; ++r) Ls[(16 * tw + t_lane + r) * LDX + 16 * (2 * hf + j) + lc] = acc[j][r];
         }
         {
-            f4 acc[MT];
+            f4 acc[2];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[mt][r] = dkv[mt][r];
-            if (dec) mm4<D, LDX, 1, 1, LDX, 16 * LDX>(acc, Us + TL * w * LDX, Zs, lane);
+                for (int r = 0; r < 4; ++r) acc[j][r] = dkv[j][r];
+            if (dec) mm2<D, LDX, 1, 1, LDX, 16 * LDX>(acc, Us + TL * tw * LDX, Zs + 32 * hf * LDX, lane);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p.dk[bth(tc + t_lane + r) * M + 16 * mt + lc] = acc[mt][r];
+                for (int r = 0; r < 4; ++r) p.dk[bth(tc + t_lane + r) * M + 16 * (2 * hf + j) + lc] = acc[j][r];
         }
         lds_barrier();
 
         // ---- 10. back through the chunk-start projection ----
         {
-            float dz[16], zz[16], pr = 0.f;
+            float dz[8], zz[8], pr = 0.f;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                dz[j] = Ls[er * LDX + 16 * ec + j];
-                zz[j] = Zs[er * LDX + 16 * ec + j];
+            for (int j = 0; j < 8; ++j) {
+                dz[j] = Ls[eo + j];
+                zz[j] = Zs[eo + j];
                 pr = fmaf(zz[j], dz[j], pr);
             }
-            pr = quad_sum(pr);
+            pr = oct_sum(pr);
             const float inv = invn_s[er];
-            float* dst = rst + static_cast<int64_t>(NT) * M * D + er * D + 16 * ec;
+            float* dst = rst + static_cast<int64_t>(NT) * M * D + go;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) dst[j] = inv * fmaf(-pr, zz[j], dz[j]);
+            for (int j = 0; j < 8; ++j) dst[j] = inv * fmaf(-pr, zz[j], dz[j]);
         }
         lds_barrier();  // the next chunk overwrites every LDS array
     }
     {
-        const float* src = rst + static_cast<int64_t>(NT) * M * D + er * D + 16 * ec;
-        float* dst = p.dstate_in + static_cast<int64_t>(bh) * M * D + er * D + 16 * ec;
+        const float* src = rst + static_cast<int64_t>(NT) * M * D + go;
+        float* dst = p.dstate_in + static_cast<int64_t>(bh) * M * D + go;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) dst[j] = src[j];
+        for (int j = 0; j < 8; ++j) dst[j] = src[j];
     }
 }
 
@@ -710,9 +749,9 @@ int launch_bwd_chunk(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t
     if (!bwd_chunk_supported(m, d, p.f.chunk, in_bf16, p.f.lin1 != 0, p.f.mode) || !p.states_ready) return -3;
     const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H));
     if (p.dy_bf16)
-        hipLaunchKernelGGL((cbwd::osr_bwd_chunk_kernel<64, 64, 64, uint16_t, true>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((cbwd::osr_bwd_chunk_kernel<64, 64, 64, uint16_t, true>), grid, dim3(512), 0, st, p);
     else
-        hipLaunchKernelGGL((cbwd::osr_bwd_chunk_kernel<64, 64, 64, uint16_t, false>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((cbwd::osr_bwd_chunk_kernel<64, 64, 64, uint16_t, false>), grid, dim3(512), 0, st, p);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
