@@ -503,6 +503,11 @@ __global__ __launch_bounds__(512) void osr_bwd_chunk_kernel(BwdParams p) {
             *reinterpret_cast<float4*>(Ls + eo + 4) = *reinterpret_cast<const float4*>(src + 4);
         }
         lds_barrier();
+        // step 7's inputs again (not kept since step 3), loaded during the sweep
+#pragma unroll
+        for (int j = 0; j < 2; ++j) load_in(2 * hf + j, kq3[j], qv3[j], gm3[j]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mu[r] = ld<TIn>(mp, bth(tc + t_lane + r));
         float rb[8];  // R_b as this thread stored it, one tile ahead of its use
         {
             const float* src = rst + static_cast<int64_t>(NT - 1) * M * D + go;
@@ -556,12 +561,7 @@ __global__ __launch_bounds__(512) void osr_bwd_chunk_kernel(BwdParams p) {
         float dht[2][4], dkv[2][4], dnh[4] = {0.f, 0.f, 0.f, 0.f}, dmu[4] = {0.f, 0.f, 0.f, 0.f};
         float dgt_tok[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 2; ++j) load_in(2 * hf + j, kq3[j], qv3[j], gm3[j]);  // (again: not kept since step 3)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            mu[r] = ld<TIn>(mp, bth(tc + t_lane + r));
-            hh[r] = part_s[0][0][TL * tw + t_lane + r] + part_s[1][0][TL * tw + t_lane + r];
-        }
+        for (int r = 0; r < 4; ++r) hh[r] = part_s[0][0][TL * tw + t_lane + r] + part_s[1][0][TL * tw + t_lane + r];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int mt = 2 * hf + j;
