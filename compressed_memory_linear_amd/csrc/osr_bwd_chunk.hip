@@ -35,9 +35,10 @@
 //      dZ taken back through the chunk-start projection,
 //      (dz_i - z_i (z_i . dz_i)) / |s_i|.
 // Every product is a v_mfma_f32_16x16x4_f32 chain over LDS operands (fp32
-// throughout); the per-(token, slot) values of tile b live in wave b's
+// throughout).  Eight waves: wave w takes tile w & 3 and half w >> 2, whose
+// per-(token, slot) values (slot blocks 2 half, 2 half + 1) live in its
 // registers in the accumulator layout (lane (lg, lc) holds tokens 4lg..4lg+3
-// of slot column lc of each 16-slot block).  The chunk-start states come from
+// of slot column lc of a 16-slot block).  The chunk-start states come from
 // the state-passing kernel (the backward's workspace holds them).
 #include "osr_launch.h"
 #include "osr_bwd_kernel.h"
@@ -62,25 +63,6 @@ __device__ __forceinline__ f4 mm(f4 acc, const float* a, const float* b, int lan
     return acc;
 }
 
-// Four output tiles that share the A operand: acc[j] += A B_j with B_j
-// starting at b + j * BS (independent accumulation chains, one A load per
-// step for four products).
-template <int K, int AI, int AK, int BK, int BJ, int BS>
-__device__ __forceinline__ void mm4(f4 (&acc)[4], const float* a, const float* b, int lane) {
-    const int r = lane & 15, kq = lane >> 4;
-    const float* pa = a + r * AI + kq * AK;
-    const float* pb = b + kq * BK + r * BJ;
-#pragma unroll
-    for (int k0 = 0; k0 < K; k0 += 4) {
-        const float av = pa[k0 * AK];
-        float bv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) bv[j] = pb[k0 * BK + j * BS];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv[j], acc[j], 0, 0, 0);
-    }
-}
-
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
 
 // Workgroup barrier for LDS data only: every wave's LDS accesses have
@@ -96,13 +78,6 @@ __device__ __forceinline__ float row16_sum(float x) {
     for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
     return x;
 }
-// Sum over the 4 consecutive lanes of an element row (the M x D passes).
-__device__ __forceinline__ float quad_sum(float x) {
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    return x;
-}
-
 // Affine scans over the 16 tokens of a tile, for one slot column: token
 // 4 lg + r of the lane.  Inclusive forward scan of x_t = g_t x_{t-1} + u_t
 // (x_{-1} = 0); returns x_t and, in xprev, x_{t-1}.
