@@ -81,26 +81,30 @@ size_t chain_xchg_bytes(int B, int H, int m, int d, int P) {
     return static_cast<size_t>(B) * H * (2 * P * per * sizeof(float) + static_cast<size_t>(P) * (m / 16) * 32 * sizeof(int));
 }
 
-// Chunk ranges of an overlapped read-out (split schedule).  With at most 64
-// state-passing workgroups (three quarters of the compute units or more left
-// to the read-out; at 128, B8 H16 T4096 m64 d128 C64, it measured no faster)
-// and a multiple of 64 chunks: 4 ranges of 48, 12, 3 and 1 64ths of the
-// chunks.  A range's read-out (on the side stream, where it runs at about a
-// quarter of the state passing's time per chunk while sharing the device) then
-// takes no longer than the next range's state passing, and the read-out of
-// the last range, the only one not hidden, is 1/64 of the whole; each range
-// boundary costs one event hand-off (~6.5 us), hence no more ranges than
-// that.  Else 1 (no overlap).  Returns the ranges' chunk ends in `end`.
+// Chunk ranges of an overlapped read-out (split schedule), for a multiple of
+// 64 chunks.  With at most 64 state-passing workgroups (three quarters of the
+// compute units or more left to the read-out): 4 ranges of 48, 12, 3 and 1
+// 64ths of the chunks.  A range's read-out (on the side stream, where it runs
+// at about a quarter of the state passing's time per chunk while sharing the
+// device) then takes no longer than the next range's state passing, and the
+// read-out of the last range, the only one not hidden, is 1/64 of the whole;
+// each range boundary costs one event hand-off (~6.5 us), hence no more
+// ranges than that.  With 65 to 128 (half the device left to the read-out,
+// which then runs at about two thirds of the state passing's time per chunk):
+// 4 equal ranges (B8 H16 T4096 m64 d128 C64: 0.67 -> 0.62 ms; 2 equal 0.624,
+// 24/16/16/8 64ths 0.649, 20/20/16/8 0.636, 16/16/16/8/8 0.637).  Else 1 (no
+// overlap).  Returns the ranges' chunk ends in `end`.
 int overlap_ranges(int B, int H, int m, int d, int C, int T, int chain_wgs, int readout_overlap, int* end) {
     const int NC = T / C;
     const int64_t wgs = static_cast<int64_t>(B) * H * chain_split_p(B, H, m, d, C, chain_wgs);
-    if (readout_overlap != 0 || wgs > 64 || NC < 64 || NC % 64 != 0) return 1;
-    static constexpr int kParts[] = {48, 12, 3, 1};
-    constexpr int kN = sizeof(kParts) / sizeof(kParts[0]);
+    if (readout_overlap != 0 || wgs > 128 || NC < 64 || NC % 64 != 0) return 1;
+    static constexpr int kFew[] = {48, 12, 3, 1}, kHalf[] = {16, 16, 16, 16};
+    const int* parts = wgs > 64 ? kHalf : kFew;
+    constexpr int kN = 4;
     static_assert(kN <= kMaxRanges, "ranges");
     int n = 0;
     for (int k = 0; k < kN; ++k) {
-        n += kParts[k] * (NC / 64);
+        n += parts[k] * (NC / 64);
         if (end) end[k] = n;
     }
     return kN;

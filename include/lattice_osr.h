@@ -117,10 +117,11 @@ extern "C" {
 #define LATTICE_OSR_WGS_ONE 1  /* always one workgroup per sequence */
 
 /* Read-out of the split schedule overlapped with its state passing. */
-#define LATTICE_OSR_OVERLAP_AUTO 0 /* where the state passing takes at most 64 workgroups and
+#define LATTICE_OSR_OVERLAP_AUTO 0 /* where the state passing takes at most 128 workgroups and
                                       there are at least 64 chunks (a multiple of 64): the chunks
-                                      in 4 ranges of shrinking length (48, 12, 3 and 1 64ths of
-                                      the chunks); each range's read-out runs on the
+                                      in 4 ranges (up to 64 workgroups: of shrinking length, 48,
+                                      12, 3 and 1 64ths of the chunks; from 65: equal quarters);
+                                      each range's read-out runs on the
                                       library's side stream for the device while the next range's
                                       state passing runs on hip_stream, which waits for the side
                                       stream before the call's work ends.  Same results, bit for

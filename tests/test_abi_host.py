@@ -157,14 +157,15 @@ def test_workgroup_split_workspace():
 
 
 def test_overlapped_readout_workspace():
-    """The read-out overlapped by chunk ranges (at most 64 state-passing
+    """The read-out overlapped by chunk ranges (at most 128 state-passing
     workgroups, a multiple of 64 chunks) hands the state from range to range
     through one more array of B H m d floats; OVERLAP_OFF, too few or ragged
     chunk counts, or more workgroups add none."""
     m = d = C = 128
     per_chunk = (m * d + 2 * m * C + d * C) * 4
     for BH, P, NC, carry in ((16, 4, 64, True), (16, 4, 512, True), (33, 1, 64, True), (64, 1, 128, True),
-                             (65, 1, 64, False), (16, 4, 32, False), (16, 4, 96, False)):
+                             (65, 1, 64, True), (128, 1, 64, True), (129, 1, 64, False), (16, 4, 32, False),
+                             (16, 4, 96, False)):
         T = NC * C
         auto = osr.make_desc(1, T, BH, m, d)
         off = osr.make_desc(1, T, BH, m, d, readout_overlap=osr.OVERLAP_OFF)

@@ -517,8 +517,9 @@ def test_chain_workgroup_split_deterministic():
 # a multiple: 4 ranges, the state handed from range to range unprojected):
 # the same kernels over the same chunks, so the results equal those of the
 # serial launch bit for bit, and meet the bar against the oracle.
-OVERLAP_CASES = [  # (B, H, m, d, C, chunks): workgroups per sequence 4, 2 and 1
+OVERLAP_CASES = [  # (B, H, m, d, C, chunks): workgroups per sequence 4, 2 and 1; 96 sequences (equal ranges)
     (1, 2, 128, 128, 128, 64), (1, 3, 128, 128, 64, 128), (2, 3, 64, 64, 32, 64), (1, 2, 32, 128, 64, 64),
+    (4, 24, 32, 32, 16, 64),
 ]
 
 
