@@ -21,6 +21,8 @@
 // With C = 1, Z = S and the step is the exact projected orthogonal update.
 //
 // Thread layout and reductions: osr_valu.h.
+#include <type_traits>
+
 #include "osr_launch.h"
 #include "osr_valu.h"
 
@@ -235,6 +237,177 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
         *reinterpret_cast<float4*>(sout + (rg + L::RG * i) * D + cg * 4) = s[i];
 }
 
+// Token loop for small chunks (C = CB in {2, 4, 8}, at most one batch of
+// the y exchange).  Per chunk: the chunk's h over slots once (as chunk_h),
+// then c, |h|^2 and the gates of all CB tokens together (CB (RPT + 1)
+// independent row sums instead of RPT + 1 per token), then the CB tokens'
+// state updates and read-out partials, their sums over the wave's row groups
+// again together.  Every input of the next chunk (k, q, gamma, mu of its
+// tokens, and the v this thread subtracts from h) is loaded while the current
+// chunk computes; h alternates between two LDS buffers by chunk parity, so a
+// chunk's h is written while no thread can still read the buffer (the barrier
+// inside the exchange of the chunk before orders it).
+template <int M, int D, int NT, typename TIn, int CB>
+__global__ __launch_bounds__(NT) void osr_tokenloop_small_kernel(Params p) {
+    using L = ValuLayout<M, D, NT>;
+    constexpr int BT = TokBatch<L>::BT, W = D + 4, Q = D / 4, RPT = L::RPT;
+    static_assert(CB <= BT && BT % CB == 0, "a chunk's tokens in one exchange batch");
+    static_assert(BT * Q <= NT, "one float4 of a batch per thread");
+    extern __shared__ __attribute__((aligned(16))) float dyn[];
+    float* hbuf = dyn;                   // [2][CB][D]
+    float* redc = dyn + 2 * CB * D;      // [2][BT][NW][W] the chunk's h partials
+    __shared__ __attribute__((aligned(16))) float redy[2 * BT * L::NW * W];  // y batches
+    const int bh = blockIdx.x;
+    const int b = bh / p.H, hd = bh % p.H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % L::TPR, rg = tid / L::TPR;
+    const int T = p.T, NCH = T / CB;
+    const int mode = p.mode;
+    auto bth_of = [&](int t) { return (static_cast<int64_t>(b) * T + t) * p.H + hd; };
+    const TIn* kp = static_cast<const TIn*>(p.k);
+    const TIn* qp = static_cast<const TIn*>(p.q);
+    const TIn* gp = static_cast<const TIn*>(p.gamma);
+    const TIn* mp = static_cast<const TIn*>(p.mu);
+    const TIn* vp = static_cast<const TIn*>(p.v);
+    // this thread's output float4 of the chunk's h: token uo, columns 4 co ..
+    const int uo = tid / Q < CB ? tid / Q : CB - 1, co = tid % Q;
+
+    const float* sin = p.state_in + static_cast<int64_t>(bh) * M * D;
+    float4 s[RPT], z[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const float4*>(sin + (rg + L::RG * i) * D + cg * 4);
+
+    // a chunk's inputs
+    struct In {
+        float k[CB][RPT], q[CB][RPT], g[CB][RPT], mu[CB];
+        float4 vo, v[CB];
+    };
+    auto load_chunk = [&](In& in, int n) {
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const int64_t bt = bth_of(n * CB + u);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int row = rg + L::RG * i;
+                in.k[u][i] = ld<TIn>(kp, bt * M + row);
+                in.q[u][i] = ld<TIn>(qp, bt * M + row);
+                in.g[u][i] = ld<TIn>(gp, p.gamma_per_slot ? bt * M + row : bt);
+            }
+            in.mu[u] = ld<TIn>(mp, bt);
+            in.v[u] = ld4<TIn>(vp, bt * D + cg * 4);
+        }
+        in.vo = ld4<TIn>(vp, bth_of(n * CB + uo) * D + co * 4);
+    };
+    In cur, nxt;
+    load_chunk(cur, 0);
+    int ybatch = 0;
+
+    for (int n = 0; n < NCH; ++n) {
+        project_rows<L>(s);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) z[i] = s[i];
+        float* hb = hbuf + (n & 1) * (CB * D);
+        // ---- the chunk's h ----
+        float4 h[CB];
+        if (mode == 0) {
+            float* rb = redc + (n & 1) * (BT * L::NW * W);
+#pragma unroll
+            for (int u = 0; u < CB; ++u) {
+                float4 hp = f4(0.f);
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) hp = fma4(cur.k[u][i], z[i], hp);
+                hp.x = strided_sum<L::TPR>(hp.x);
+                hp.y = strided_sum<L::TPR>(hp.y);
+                hp.z = strided_sum<L::TPR>(hp.z);
+                hp.w = strided_sum<L::TPR>(hp.w);
+                if (lane < L::TPR) *reinterpret_cast<float4*>(rb + (u * L::NW + wave) * W + cg * 4) = hp;
+            }
+            __syncthreads();
+            if (tid < CB * Q) {
+                float4 acc = *reinterpret_cast<const float4*>(rb + (uo * L::NW) * W + co * 4);
+#pragma unroll
+                for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (uo * L::NW + w) * W + co * 4);
+                *reinterpret_cast<float4*>(hb + uo * D + co * 4) = acc - cur.vo;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int u = 0; u < CB; ++u) h[u] = *reinterpret_cast<const float4*>(hb + u * D + cg * 4);
+        } else {
+#pragma unroll
+            for (int u = 0; u < CB; ++u) h[u] = mode == 2 ? cur.v[u] : f4(0.f) - cur.v[u];
+        }
+        // the next chunk's inputs, in flight while this one computes (the last re-reads itself)
+        load_chunk(nxt, n + 1 < NCH ? n + 1 : n);
+
+        // ---- c, |h|^2 and the gates of every token of the chunk ----
+        float cc[CB][RPT + 1];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) cc[u][i] = dot4(z[i], h[u]);
+            cc[u][RPT] = dot4(h[u], h[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+#pragma unroll
+            for (int i = 0; i <= RPT; ++i) cc[u][i] = group_sum<L::TPR>(cc[u][i]);
+        // ---- the tokens in turn: state update, read-out partial ----
+        float4 yp[CB];
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            const float hh = cc[u][RPT], mu = cur.mu[u];
+            yp[u] = f4(0.f);
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const float a = cur.g[u][i] * (mode == 2 ? cc[u][i] - cur.k[u][i] : cur.k[u][i]);
+                const float w = fmaxf(fmaf(-cc[u][i], cc[u][i], hh), 0.f);
+                const float beta = rsqrtf(fmaf(mu, mu, a * a * w));
+                const float kap = -beta * a;
+                if (p.lin1) {
+                    s[i] = fma4(beta * mu, s[i], fma4(beta * a * cc[u][i], z[i], kap * h[u]));
+                } else {
+                    s[i] = fma4(beta * fmaf(a, cc[u][i], mu), s[i], kap * h[u]);
+                }
+                yp[u] = fma4(cur.q[u][i], s[i], yp[u]);
+            }
+        }
+        float* rb = redy + (ybatch & 1) * (BT * L::NW * W);
+        const int u0 = (n * CB) % BT;  // this chunk's first slot in the y batch
+#pragma unroll
+        for (int u = 0; u < CB; ++u) {
+            yp[u].x = strided_sum<L::TPR>(yp[u].x);
+            yp[u].y = strided_sum<L::TPR>(yp[u].y);
+            yp[u].z = strided_sum<L::TPR>(yp[u].z);
+            yp[u].w = strided_sum<L::TPR>(yp[u].w);
+        }
+        if (lane < L::TPR)
+#pragma unroll
+            for (int u = 0; u < CB; ++u) *reinterpret_cast<float4*>(rb + ((u0 + u) * L::NW + wave) * W + cg * 4) = yp[u];
+        const int tend = (n + 1) * CB;  // tokens done
+        if (tend % BT == 0 || n + 1 == NCH) {
+            __syncthreads();  // the batch's partials visible
+            const int nb = u0 + CB, t0 = tend - nb;
+            if (tid < nb * Q) {
+                const int uu = tid / Q, c4 = tid % Q;
+                float4 acc = *reinterpret_cast<const float4*>(rb + (uu * L::NW) * W + c4 * 4);
+#pragma unroll
+                for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (uu * L::NW + w) * W + c4 * 4);
+                if (p.gate) {
+                    const float4 g = ld4<TIn>(static_cast<const TIn*>(p.gate), bth_of(t0 + uu) * D + c4 * 4);
+                    acc = make_float4(acc.x * gelu(g.x), acc.y * gelu(g.y), acc.z * gelu(g.z), acc.w * gelu(g.w));
+                }
+                st_y4(p.y, bth_of(t0 + uu) * D + c4 * 4, acc, p.y_bf16);
+            }
+            ++ybatch;
+        }
+        cur = nxt;
+    }
+    project_rows<L>(s);
+    float* sout = p.state_out + static_cast<int64_t>(bh) * M * D;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) *reinterpret_cast<float4*>(sout + (rg + L::RG * i) * D + cg * 4) = s[i];
+}
+
 // Dynamic LDS of the token loop (floats): C > 1 only.
 template <int M, int D, int NT>
 static size_t tokenloop_dyn_lds(int C) {
@@ -258,6 +431,31 @@ static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_
         else
             hipLaunchKernelGGL((osr_decode_kernel<M, D, NT_DEC, float>), grid, dim3(NT_DEC), 0, st, p);
     } else {
+        // small chunks that fit one exchange batch: the batched loop
+        constexpr int BT = TokBatch<ValuLayout<M, D, NT_TOK>>::BT;
+        const int C = p.chunk;
+        if ((C == 2 || C == 4 || C == 8) && C <= BT) {
+            using L = ValuLayout<M, D, NT_TOK>;
+            const size_t lds = (2 * static_cast<size_t>(C) * D + 2 * BT * L::NW * (D + 4)) * sizeof(float);
+            auto go = [&](auto cb) {
+                constexpr int CBV = decltype(cb)::value;
+                if constexpr (CBV <= BT) {
+                    if (in_bf16)
+                        hipLaunchKernelGGL((osr_tokenloop_small_kernel<M, D, NT_TOK, uint16_t, CBV>), grid, dim3(NT_TOK),
+                                           lds, st, p);
+                    else
+                        hipLaunchKernelGGL((osr_tokenloop_small_kernel<M, D, NT_TOK, float, CBV>), grid, dim3(NT_TOK), lds,
+                                           st, p);
+                }
+            };
+            if (C == 2)
+                go(std::integral_constant<int, 2>{});
+            else if (C == 4)
+                go(std::integral_constant<int, 4>{});
+            else
+                go(std::integral_constant<int, 8>{});
+            return hipGetLastError() == hipSuccess ? 0 : -5;
+        }
         const size_t lds = tokenloop_dyn_lds<M, D, NT_TOK>(p.chunk) * sizeof(float);
         if (in_bf16)
             hipLaunchKernelGGL((osr_tokenloop_kernel<M, D, NT_TOK, uint16_t>), grid, dim3(NT_TOK), lds, st, p);
