@@ -318,3 +318,130 @@ def test_chunk_parallel_gradient_form(C, T, mode):
             assert np.max(np.abs(got[key] - r)) <= 1e-9 * scale, (key, C, mode)
         r = ref["dstate_in"][0, h]
         assert np.max(np.abs(got["dstate_in"] - r)) <= 1e-9 * max(1.0, float(np.max(np.abs(r))))
+
+
+# The same gradient at the tile level the matrix-core backward computes it:
+# 16-token tiles, gate products running from the tile start relative to
+# a_ref (their product over the tile's first 8 tokens, which cancels and is
+# held constant), the tile-start states R_b, lambda swept over the tiles in
+# reverse, and the gate gradients by a forward recursion (W's suffix
+# products) and a reverse one (E_t = dA_t + g_{t+1} E_{t+1}).
+
+TILE = 16
+
+
+def _tile_form_grad(q, k, v, g, mu, S0, dy, dso, C, mode):
+    """fp64 numpy, one (b,h): q, k, g [T,m]; v, dy [T,d]; mu [T]; S0, dso [m,d]."""
+    T, m = q.shape
+    NC, NT = T // C, C // TILE
+
+    def gates(Z, sl):
+        H = k[sl] @ Z - v[sl] if mode == DEC else -v[sl]
+        Ht = H @ Z.T
+        nh = np.sum(H * H, axis=1)
+        a = g[sl] * k[sl]
+        wraw = nh[:, None] - Ht * Ht
+        w = np.where(wraw > 0, wraw, 0.0)
+        beta = 1.0 / np.sqrt(mu[sl][:, None] ** 2 + a * a * w)
+        return H, Ht, a, wraw > 0, w, beta, beta * a, beta * (mu[sl][:, None] + a * Ht)
+
+    def suffix(Gt):
+        return np.vstack([np.cumprod(Gt[::-1], axis=0)[::-1][1:], np.ones((1, Gt.shape[1]))])
+
+    starts, S = [], S0.copy()
+    for n in range(NC):
+        starts.append(S.copy())
+        sl = slice(n * C, (n + 1) * C)
+        Z = S / np.linalg.norm(S, axis=1, keepdims=True)
+        H, _, _, _, _, _, kap, G = gates(Z, sl)
+        R = Z
+        for b in range(NT):
+            tb = slice(b * TILE, (b + 1) * TILE)
+            R = np.prod(G[tb], axis=0)[:, None] * R - (kap[tb] * suffix(G[tb])).T @ H[tb]
+        S = R
+    nS = np.linalg.norm(S, axis=1, keepdims=True)
+    Zo = S / nS
+    lam = (dso - Zo * np.sum(Zo * dso, axis=1, keepdims=True)) / nS
+    out = {x: np.zeros_like(y) for x, y in (("dq", q), ("dk", k), ("dv", v), ("dgamma", g), ("dmu", mu))}
+    for n in reversed(range(NC)):
+        sl = slice(n * C, (n + 1) * C)
+        nZ = np.linalg.norm(starts[n], axis=1, keepdims=True)
+        Z = starts[n] / nZ
+        Q, K, Mu, dY = q[sl], k[sl], mu[sl], dy[sl]
+        H, Ht, a, Mk, w, beta, kap, G = gates(Z, sl)
+        tiles, R = [], Z
+        for b in range(NT):
+            tb = slice(b * TILE, (b + 1) * TILE)
+            A = np.cumprod(G[tb], axis=0)
+            ar = A[TILE // 2 - 1]
+            tiles.append((tb, A, ar, R, Q[tb] * A / ar, kap[tb] * ar / A, kap[tb] * suffix(G[tb])))
+            R = A[-1][:, None] * R - tiles[-1][6].T @ H[tb]
+        dG, dkap, dH = np.zeros_like(G), np.zeros_like(kap), np.zeros_like(H)
+        for tb, A, ar, Rb, QA, KA, Wt in reversed(tiles):
+            Gt = G[tb]
+            P = np.tril(QA @ KA.T)
+            dP = -np.tril(dY[tb] @ H[tb].T)
+            dQA = dY[tb] @ (ar[:, None] * Rb).T + dP @ KA
+            dKA = dP.T @ QA
+            dH[tb] += -P.T @ dY[tb] - Wt @ lam
+            dW = -H[tb] @ lam.T
+            dAE = np.sum(Rb * lam, axis=1)
+            lam = A[-1][:, None] * lam + ar[:, None] * (QA.T @ dY[tb])
+            out["dq"][sl][tb] = dQA * A / ar
+            dA = dQA * Q[tb] / ar - dKA * KA / A
+            dA[-1] += dAE
+            sfx = suffix(Gt)
+            dkap[tb] += dKA * ar / A + dW * sfx
+            F = np.zeros_like(Gt)           # sum_{s<t} dW_s kappa_s prod_{s<l<t} g_l
+            for t in range(1, TILE):
+                F[t] = Gt[t - 1] * F[t - 1] + dW[t - 1] * kap[tb][t - 1]
+            E = np.zeros_like(Gt)           # E_t = dA_t + g_{t+1} E_{t+1}
+            E[-1] = dA[-1]
+            for t in range(TILE - 2, -1, -1):
+                E[t] = dA[t] + Gt[t + 1] * E[t + 1]
+            dG[tb] = F * sfx + np.vstack([np.ones((1, m)), A[:-1]]) * E
+        dbeta = dG * (Mu[:, None] + a * Ht) + dkap * a
+        dHt = dG * kap
+        da = dG * beta * Ht + dkap * beta
+        tbeta = -0.5 * beta ** 3 * dbeta
+        dmu = np.sum(dG * beta + 2.0 * Mu[:, None] * tbeta, axis=1)
+        da += 2.0 * a * w * tbeta
+        dw = np.where(Mk, a * a * tbeta, 0.0)
+        dHt += -2.0 * Ht * dw
+        dH += dHt @ Z + 2.0 * np.sum(dw, axis=1)[:, None] * H
+        dZ = lam + dHt.T @ H
+        dK = da * g[sl]
+        if mode == DEC:
+            dK += dH @ Z.T
+            dZ += K.T @ dH
+        out["dgamma"][sl] = da * K
+        out["dk"][sl] = dK
+        out["dv"][sl] = -dH
+        out["dmu"][sl] = dmu
+        lam = (dZ - Z * np.sum(Z * dZ, axis=1, keepdims=True)) / nZ
+    out["dstate_in"] = lam
+    return out
+
+
+@pytest.mark.parametrize("C,T", [(16, 48), (32, 64), (64, 128)])
+@pytest.mark.parametrize("mode", [DEC, SIM])
+@pytest.mark.parametrize("mu_mean", [3.0, -2.0])
+def test_tile_level_gradient_form(C, T, mode, mu_mean):
+    """The tile-level evaluation (the matrix-core backward's own formulation)
+    equals the autograd gradient of the chunk-wise forward to rounding, with
+    large and small forget gates (mu = sigmoid(N(3, 1)) and sigmoid(N(-2, 1)))."""
+    inp = synth.make_inputs(1, T, 2, 8, 6, seed=950 + C + mode, in_dtype=synth.F32, gamma_per_slot=True,
+                            mu_mean=mu_mean)
+    q, k, v, g, mu, S0 = inp.values_f64()
+    rng = np.random.default_rng(951 + C)
+    dy = rng.standard_normal(v.shape)
+    dso = rng.standard_normal(S0.shape)
+    ref = ob.osr_backward(q, k, v, g, mu, S0, dy, dso, chunk_size=C, mode=mode)
+    for h in range(2):
+        got = _tile_form_grad(q[0, :, h], k[0, :, h], v[0, :, h], g[0, :, h], mu[0, :, h], S0[0, h],
+                              dy[0, :, h], dso[0, h], C, mode)
+        for key in ("dq", "dk", "dv", "dgamma", "dmu"):
+            r = ref[key][0, :, h]
+            assert np.max(np.abs(got[key] - r)) <= 1e-9 * max(1.0, float(np.max(np.abs(r)))), (key, C, mode)
+        r = ref["dstate_in"][0, h]
+        assert np.max(np.abs(got["dstate_in"] - r)) <= 1e-9 * max(1.0, float(np.max(np.abs(r))))
