@@ -44,11 +44,14 @@ size_t bwd_workspace_bytes(int B, int H, int T, int m, int d, int C) {
 bool bwd_split_fits(int m, int d, int C, int P) {
     const int ML = m / P, TPR = d / 4, NT = ML * TPR < 512 ? ML * TPR : 512, RG = NT / TPR, RPT = ML / RG;
     const int NW = NT / 64, W = d + 4;
-    int BT = RPT <= 2 ? 8 : (RPT <= 4 ? 4 : 2);
-    if (TPR == 32 && BT > 4) BT = 4;
-    size_t lds = (2 * static_cast<size_t>(BT) * NW * W + static_cast<size_t>(BT) * W) * 4 + static_cast<size_t>(C) * d * 4;
-    if (P > 1 && RPT <= 2 && ML <= 32)
-        lds += ((5 * static_cast<size_t>(ML) + 3) * C + (d <= 64 ? static_cast<size_t>(C) * d : 0)) * 4;
+    const bool stg = P > 1 && RPT <= 2 && ML <= 32;
+    // (the kernel's WalkBatch: the chunk's h batch BTC, the walk's batch BT)
+    int BTC = RPT <= 2 ? 8 : (RPT <= 4 ? 4 : 2);
+    if (TPR == 32 && BTC > 4) BTC = 4;
+    const int BT = stg && TPR == 32 && BTC < 8 ? 8 : BTC;
+    const size_t red = static_cast<size_t>(2 * BTC > BT ? 2 * BTC : BT) * NW * W;
+    size_t lds = (red + static_cast<size_t>(BT) * W) * 4 + static_cast<size_t>(C) * d * 4;
+    if (stg) lds += ((5 * static_cast<size_t>(ML) + 3) * C + (d <= 64 ? static_cast<size_t>(C) * d : 0)) * 4;
     return lds <= 160 * 1024;
 }
 

@@ -213,12 +213,31 @@ __device__ __forceinline__ void load_rev_staged(RevIn<L::RPT>& x, const BwdParam
     for (int i = 0; i < L::RPT; ++i) x.rp[i] = *reinterpret_cast<const float4*>(rpre + el0 + i * L::RG * D);
 }
 
+// Batches of the reverse walk's exchange over slots.  The token loop's batch
+// (TokBatch, also the chunk's h here) is capped at 4 tokens at d = 128 for its
+// LDS; where the split walk stages its records (P > 1, at most 32 rows and 2
+// per thread) at d = 128 it takes 8 tokens, which halves the hand-offs between
+// its workgroups, in one exchange buffer instead of two alternating ones (the
+// barrier that publishes a batch's sums already orders every read of the
+// buffer before the next batch's writes).
+template <int M, int D, int NT, int P>
+struct WalkBatch {
+    using L = ValuLayout<M / P, D, NT>;
+    static constexpr bool STG = P > 1 && L::RPT <= 2 && M / P <= 32;
+    static constexpr int BTC = TokBatch<L>::BT;                      // chunk_h's batch
+    static constexpr int BT = (STG && L::TPR == 32 && BTC < 8) ? 8 : BTC;
+    static constexpr bool RED2 = 2 * BTC >= 2 * BT;                // two alternating buffers
+    static constexpr int RED = (2 * BTC > BT ? 2 * BTC : BT) * L::NW * (D + 4);  // red floats
+    static constexpr int TOT = BT * (D + 4);                         // tot floats
+};
+
 template <int M, int D, int NT, typename TIn, bool LIN1, bool DYB, int P = 1>
 __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     static_assert(P == 1 || (M / P >= 16 && sizeof(TIn) == 2), "split: bf16 inputs, 16 rows or more each");
     using L = ValuLayout<M / P, D, NT>;
     using TR = TokRec<M, D>;
-    constexpr int BT = TokBatch<L>::BT, W = D + 4;
+    using WB = WalkBatch<M, D, NT, P>;
+    constexpr int BT = WB::BT, W = D + 4;
     // The reverse walk loads the next token's inputs and record while it works on
     // the current one, and the state before it too, where registers allow.
     constexpr bool PF_TOKEN = L::RPT <= 4;
@@ -229,8 +248,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     extern __shared__ __attribute__((aligned(16))) float hbuf[];  // [C][D], dynamic
     float* const gst = hbuf + p.f.chunk * D;  // [2 or 3][M*C]: staged gates (stage_gk)
     float* const srec = gst + (p.stage_gk ? (LIN1 ? 3 : 2) * M * p.f.chunk : 0);  // StagedRec (STG)
-    __shared__ __attribute__((aligned(16))) float red[2 * BT * L::NW * W];
-    __shared__ __attribute__((aligned(16))) float tot[BT * W];  // a batch's sums over slots
+    __shared__ __attribute__((aligned(16))) float red[WB::RED];
+    __shared__ __attribute__((aligned(16))) float tot[WB::TOT];  // a batch's sums over slots
     static_assert(BT * (D / 4 + 1) <= NT, "one float4 of a batch's sums per thread");
     const int bh = P > 1 ? blockIdx.x / P : blockIdx.x;
     const int pidx = P > 1 ? blockIdx.x % P : 0;  // this workgroup's rows: [pidx M/P, (pidx + 1) M/P)
@@ -240,7 +259,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
     const int cg = tid % L::TPR, rgl = tid / L::TPR, rg = pidx * (M / P) + rgl;
     constexpr int ML = M / P;
     // staged records (StagedRec): at most 32 rows and 2 rows per thread (more spilled)
-    constexpr bool STG = P > 1 && L::RPT <= 2 && ML <= 32;
+    constexpr bool STG = WB::STG;
+    static_assert(STG == (P > 1 && L::RPT <= 2 && ML <= 32), "staging rule");
     const int T = p.f.T, C = p.f.chunk, NC = T / C;
     const int mode = p.f.mode;
     const bool enc = !STG && mode == 2;  // (the split path never runs the encoding layer)
@@ -566,7 +586,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_kernel(BwdParams p) {
                 lrev(rv[0], C - 1);
         }
         for (int ub = C - nb; ub >= 0; ub -= nb) {
-            float* rb = red + (nred++ & 1) * (BT * L::NW * W);
+            float* rb = WB::RED2 ? red + (nred++ & 1) * (BT * L::NW * W) : red;
             float dcv[BT][L::RPT], kv[BT][L::RPT], dkin[BT][L::RPT];
             float dqv[STG ? BT : 1][L::RPT], dgv[STG ? BT : 1][L::RPT];  // (STG: this batch's dq, dgamma)
 #pragma unroll
@@ -866,8 +886,8 @@ static int launch_bwd_mdp(const BwdParams& p, bool in_bf16, hipStream_t st) {
     constexpr int NT = ((M / P) * TPR < 512) ? (M / P) * TPR : 512;
     const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H) * P);
     using L = ValuLayout<M / P, D, NT>;
-    constexpr int BT = TokBatch<L>::BT, W = D + 4;
-    constexpr size_t static_lds = (2 * BT * L::NW * W + BT * W) * sizeof(float);  // red, tot
+    using WB = WalkBatch<M, D, NT, P>;
+    constexpr size_t static_lds = (WB::RED + WB::TOT) * sizeof(float);  // red, tot
     const size_t h_lds = static_cast<size_t>(p.f.chunk) * D * sizeof(float);      // the chunk's h
     const size_t gk_lds = static_cast<size_t>(p.f.lin1 ? 3 : 2) * M * p.f.chunk * sizeof(float);
     // the chunk's gates from the state-passing kernel, staged in LDS where it fits
