@@ -122,6 +122,7 @@ osr::Params make_params(const lattice_osr_desc* d, int C, const void* q, const v
     p.raw = nullptr;
     p.raw_stride = 0;
     p.raw_c = p.raw_b = p.raw_hh = nullptr;
+    p.hrec = nullptr;
     p.B = d->B;
     p.T = d->T;
     p.H = d->H;
@@ -212,6 +213,19 @@ size_t bwd_chain_extra_bytes(const lattice_osr_desc* d, int C) {
     return nch * (2 * static_cast<size_t>(d->m) * C + C) * sizeof(float);
 }
 
+// The small-chunk reverse walk (C <= 8) where it is built and not turned off.
+bool bwd_small_form(const lattice_osr_desc* d, int C) {
+    return d->bwd_form == LATTICE_OSR_BWD_AUTO && C <= 8 &&
+           osr::bwd_small_supported(d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1);
+}
+
+// With the small-chunk walk and the decoding objective, the backward's part is
+// followed by every token's h (fp32 [B*H][T][d]).
+size_t bwd_small_h_bytes(const lattice_osr_desc* d, int C) {
+    if (!bwd_small_form(d, C) || d->mode != LATTICE_OSR_MODE_DEC) return 0;
+    return static_cast<size_t>(d->B) * d->H * d->T * d->d * sizeof(float);
+}
+
 // ... then, where the slot rows of a sequence split over several workgroups,
 // their hand-off buffers.
 size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
@@ -220,6 +234,7 @@ size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
     if (chain)
         n += osr::mfma_chain_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1) +
              bwd_chain_extra_bytes(d, C);
+    n += bwd_small_h_bytes(d, C);
     return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, osr::bwd_split_p(d->B, d->H, d->m, d->d, C, chain, d->chain_wgs));
 }
 
@@ -472,6 +487,21 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
         p.chain_hh = p.chain_b + nch * mc;
     }
     if (bwd_chunk_form(desc, chunk_size)) return osr::launch_bwd_chunk(desc->m, desc->d, p, true, st);
+    const bool in_bf16 = desc->in_dtype == LATTICE_OSR_BF16;
+    if (bwd_small_form(desc, chunk_size)) {
+        // phase 1: the forward's small-chunk token loop, keeping every chunk-start state
+        // (before projection) in the backward's layout and, decoding objective, every h
+        const size_t bwd_bytes = osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
+        osr::Params pf = make_params(desc, chunk_size, q, k, v, gamma, mu, state_in, nullptr, nullptr, nullptr);
+        pf.raw = static_cast<float*>(workspace);
+        pf.raw_stride = static_cast<int64_t>(bwd_bytes / sizeof(float)) / (static_cast<int64_t>(desc->B) * desc->H);
+        pf.hrec = bwd_small_h_bytes(desc, chunk_size)
+                      ? reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_bytes) : nullptr;
+        rc = osr::launch_valu(false, desc->m, desc->d, pf, in_bf16, st);
+        if (rc) return rc;
+        p.f.hrec = pf.hrec;
+        return osr::launch_bwd_small(desc->m, desc->d, p, in_bf16, st);
+    }
     // slot rows split over workgroups: every workgroup of a sequence must be resident
     // at once (they wait for each other), so no more workgroups than compute units
     p.split_p = osr::bwd_split_p(desc->B, desc->H, desc->m, desc->d, chunk_size, chain, desc->chain_wgs);
@@ -489,7 +519,7 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
                                                            (desc->d + 4));
         }
     }
-    return osr::launch_bwd(desc->m, desc->d, p, desc->in_dtype == LATTICE_OSR_BF16, st);
+    return osr::launch_bwd(desc->m, desc->d, p, in_bf16, st);
 }
 
 }  // extern "C"

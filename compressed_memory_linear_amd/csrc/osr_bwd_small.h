@@ -1,0 +1,470 @@
+// osr_bwd_small.h -- reverse walk of the backward at small chunks (C = 2, 4, 8).
+//
+// Method: "Lattice: Learning to Efficiently Compress the Memory" (arXiv
+// 2504.05646), section "Parallel and Hardware Efficient Form", eq.
+// recurrence_linear2 (the default linearisation).  The vector-Jacobian product
+// is that of the general walk (osr_bwd_kernel.h states the per-token reverse);
+// this kernel is its form for chunks short enough that the state before and
+// after every token of a chunk stays in registers.
+//
+// Phase 1 is the small-chunk token loop of the forward (osr_valu.hip), which
+// leaves every chunk-start state (before projection) in the workspace, in the
+// layout of the general walk, and for the decoding objective every token's h.
+// This kernel then walks the chunks backwards, one workgroup per (b,h), in
+// the token loop's thread layout:
+//   - a chunk's inputs (h, dy, k, q, gamma, mu of its C tokens) are staged in
+//     LDS by all threads together, each thread's loads issued one chunk ahead
+//     and converted to fp32 only when written to LDS; the chunk-start state
+//     is read one chunk ahead the same way;
+//   - c and |h|^2 of the chunk's tokens depend only on the projected start
+//     state z and on h, so all C (RPT + 1) row sums run together; the forward
+//     is rerun elementwise from z;
+//   - in the reverse the adjoint of the state is only scaled by the gate and
+//     takes q dy per token, so no token's row sums (dq, dg, dkap) feed the
+//     next token's: they follow one another without waiting, and the partial
+//     sums over slots of all C tokens go through one LDS exchange;
+//   - two barriers per chunk: one publishes the partial sums, the other the
+//     sums over waves together with the next chunk's staged inputs.
+#pragma once
+
+#include <type_traits>
+
+#include "osr_bwd_kernel.h"
+#include "osr_launch.h"
+#include "osr_valu.h"
+
+namespace osr {
+
+// Whether the small-chunk walk is built for (M, D, C): at most 2 slot rows per
+// thread (the chunk's states in registers) and C within the forward token
+// loop's exchange batch (its phase 1).
+template <int M, int D>
+constexpr bool bwd_small_fits(int C) {
+    using L = ValuLayout<M, D, tokenloop_threads<M, D>()>;
+    return L::RPT <= 2 && (C == 2 || C == 4 || C == 8) && C <= TokBatch<L>::BT;
+}
+
+// Four consecutive elements loaded without conversion (the conversion, and so
+// the wait for the load, happens where the value is used).
+template <typename T>
+struct Raw4;
+template <>
+struct Raw4<float> {
+    using type = float4;
+    __device__ static type load(const float* p, int64_t i) { return *reinterpret_cast<const float4*>(p + i); }
+    __device__ static float4 cvt(type v) { return v; }
+};
+template <>
+struct Raw4<uint16_t> {
+    using type = uint2;
+    __device__ static type load(const uint16_t* p, int64_t i) { return *reinterpret_cast<const uint2*>(p + i); }
+    __device__ static float4 cvt(type u) {
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u), __uint_as_float(u.y << 16),
+                           __uint_as_float(u.y & 0xFFFF0000u));
+    }
+};
+template <typename T>
+struct Raw1;
+template <>
+struct Raw1<float> {
+    using type = float;
+    __device__ static type load(const float* p, int64_t i) { return p[i]; }
+    __device__ static float cvt(type v) { return v; }
+};
+template <>
+struct Raw1<uint16_t> {
+    using type = uint16_t;
+    __device__ static type load(const uint16_t* p, int64_t i) { return p[i]; }
+    __device__ static float cvt(type v) { return bf16_bits_to_f32(v); }
+};
+
+// A chunk's staged inputs in LDS (floats): h and dy [C][D], k, q and a
+// per-slot gamma [C][M], mu and a per-token gamma [C].
+template <int M, int D, int C>
+struct SmallStage {
+    static constexpr int H = 0, DY = C * D, K = 2 * C * D, Q = K + C * M, G = Q + C * M, MU = G + C * M, GT = MU + C;
+    static constexpr int SIZE = (GT + C + 3) / 4 * 4;
+};
+
+// DEC: decoding objective (h = sum_i k_i z_i - v, from the phase-1 records);
+// otherwise h = -v (similarity) or v (encoding layer).  DYB: dy in bf16.
+template <int M, int D, int NT, int C, typename TIn, bool DYB, bool DEC>
+__global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
+    using L = ValuLayout<M, D, NT>;
+    using SG = SmallStage<M, D, C>;
+    using DYT = typename std::conditional<DYB, uint16_t, float>::type;
+    using HT = typename std::conditional<DEC, float, TIn>::type;
+    constexpr int RPT = L::RPT, Q = D / 4, MQ = M / 4, W = D + 4, NW = L::NW;
+    static_assert(RPT <= 2, "the chunk's states in registers");
+    static_assert(C * Q <= NT && C * MQ <= NT && 2 * C <= NT, "one staged unit of each kind per thread");
+    static_assert(C * (Q + 1) <= NT, "one float4 of the chunk's sums per thread");
+    __shared__ __attribute__((aligned(16))) float stg[2 * SG::SIZE];  // staged inputs, by chunk parity
+    __shared__ __attribute__((aligned(16))) float red[C * NW * W];    // partial sums over each wave's slots
+    __shared__ __attribute__((aligned(16))) float tot[C * W];         // the chunk's sums over slots
+
+    const int bh = blockIdx.x;
+    const int b = bh / p.f.H, hd = bh % p.f.H;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % L::TPR, rg = tid / L::TPR;
+    const int T = p.f.T, NC = T / C;
+    const bool enc = p.f.mode == 2;
+    const bool gps = p.f.gamma_per_slot != 0;
+    auto bth_of = [&](int t) { return (static_cast<int64_t>(b) * T + t) * p.f.H + hd; };
+    auto el = [&](int i) { return (rg + L::RG * i) * D + cg * 4; };
+    float* const sck = p.ws + static_cast<int64_t>(bh) * bwd_floats_per_bh<M, D>(T, C);  // [NC+1][M][D]
+    const float* const hrec = DEC ? p.f.hrec + static_cast<int64_t>(bh) * T * D : nullptr;
+
+    // ---- staging: this thread's unit of each kind (indices clamped; only the
+    // threads inside a kind's range write it) ----
+    const TIn* kp = static_cast<const TIn*>(p.f.k);
+    const TIn* qp = static_cast<const TIn*>(p.f.q);
+    const TIn* gp = static_cast<const TIn*>(p.f.gamma);
+    const TIn* vp = static_cast<const TIn*>(p.f.v);
+    const TIn* mp = static_cast<const TIn*>(p.f.mu);
+    const DYT* dyp = static_cast<const DYT*>(p.dy);
+    const int jq = tid < C * Q ? tid : C * Q - 1, uq = jq / Q, cq = jq % Q;      // h, dy
+    const int jm = tid < C * MQ ? tid : C * MQ - 1, um = jm / MQ, rm = jm % MQ;  // k, q, gamma
+    const int us = tid % C;                                                     // mu, per-token gamma
+    // (per-token gamma: no per-slot array, the k unit is loaded again in its place;
+    // the scalar unit reads gamma for threads C .. 2C - 1 then)
+    const TIn* gsl = gps ? gp : kp;
+    const TIn* ssrc = (!gps && tid >= C) ? gp : mp;
+    struct Pre {
+        typename Raw4<HT>::type h;
+        typename Raw4<DYT>::type dy;
+        typename Raw4<TIn>::type k, q, g;
+        typename Raw1<TIn>::type s;
+        float4 st[RPT];
+    };
+    auto issue = [&](Pre& x, int n) __attribute__((always_inline)) {
+        const int64_t bq = bth_of(n * C + uq), bm = bth_of(n * C + um);
+        if constexpr (DEC)
+            x.h = Raw4<float>::load(hrec, static_cast<int64_t>(n * C + uq) * D + cq * 4);
+        else
+            x.h = Raw4<TIn>::load(vp, bq * D + cq * 4);
+        x.dy = Raw4<DYT>::load(dyp, bq * D + cq * 4);
+        x.k = Raw4<TIn>::load(kp, bm * M + rm * 4);
+        x.q = Raw4<TIn>::load(qp, bm * M + rm * 4);
+        x.g = Raw4<TIn>::load(gsl, bm * M + rm * 4);
+        x.s = Raw1<TIn>::load(ssrc, bth_of(n * C + us));
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) x.st[i] = *reinterpret_cast<const float4*>(sck + static_cast<int64_t>(n) * M * D + el(i));
+    };
+    const float hsgn = p.f.mode == 2 ? 1.f : -1.f;
+    auto commit = [&](const Pre& x, float* sb) __attribute__((always_inline)) {
+        if (tid < C * Q) {
+            const float4 hv = Raw4<HT>::cvt(x.h);
+            *reinterpret_cast<float4*>(sb + SG::H + uq * D + cq * 4) = DEC ? hv : hsgn * hv;
+            *reinterpret_cast<float4*>(sb + SG::DY + uq * D + cq * 4) = Raw4<DYT>::cvt(x.dy);
+        }
+        if (tid < C * MQ) {
+            *reinterpret_cast<float4*>(sb + SG::K + um * M + rm * 4) = Raw4<TIn>::cvt(x.k);
+            *reinterpret_cast<float4*>(sb + SG::Q + um * M + rm * 4) = Raw4<TIn>::cvt(x.q);
+            *reinterpret_cast<float4*>(sb + SG::G + um * M + rm * 4) = Raw4<TIn>::cvt(x.g);
+        }
+        if (tid < 2 * C) sb[SG::MU + tid] = Raw1<TIn>::cvt(x.s);  // (MU, then GT)
+    };
+
+    // ---- the returned state is the end state projected: its backward ----
+    float4 dR[RPT];
+    {
+        const float* dso = p.dstate_out + static_cast<int64_t>(bh) * M * D;
+        float4 r[RPT], o[RPT];
+        float n2[RPT], pr[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            r[i] = *reinterpret_cast<const float4*>(sck + static_cast<int64_t>(NC) * M * D + el(i));
+            dR[i] = *reinterpret_cast<const float4*>(dso + el(i));
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) n2[i] = group_sum<L::TPR>(dot4(r[i], r[i]));
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            o[i] = rsqrtf(n2[i]) * r[i];
+            pr[i] = group_sum<L::TPR>(dot4(o[i], dR[i]));
+        }
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) dR[i] = rsqrtf(n2[i]) * fma4(-pr[i], o[i], dR[i]);
+    }
+
+    Pre pre;
+    issue(pre, NC - 1);
+    commit(pre, stg + ((NC - 1) & 1) * SG::SIZE);
+    float4 scur[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) scur[i] = pre.st[i];
+    __syncthreads();  // the last chunk's inputs visible
+    issue(pre, NC > 1 ? NC - 2 : 0);
+
+    for (int n = NC - 1; n >= 0; --n) {
+        const float* sb = stg + (n & 1) * SG::SIZE;
+        // the chunk-start state projected
+        float inv[RPT];
+        float4 z[RPT];
+        {
+            float n2[RPT];
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) n2[i] = group_sum<L::TPR>(dot4(scur[i], scur[i]));
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                inv[i] = rsqrtf(n2[i]);
+                z[i] = inv[i] * scur[i];
+            }
+        }
+        float4 h[C];
+#pragma unroll
+        for (int u = 0; u < C; ++u) h[u] = *reinterpret_cast<const float4*>(sb + SG::H + u * D + cg * 4);
+        // c and |h|^2 of every token of the chunk
+        float cc[C][RPT + 1];
+#pragma unroll
+        for (int u = 0; u < C; ++u) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) cc[u][i] = dot4(z[i], h[u]);
+            cc[u][RPT] = dot4(h[u], h[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < C; ++u)
+#pragma unroll
+            for (int i = 0; i <= RPT; ++i) cc[u][i] = group_sum<L::TPR>(cc[u][i]);
+        // the forward again, elementwise: beta, and the state before every token
+        // (rs[u]) and after the last (rs[C])
+        float beta[C][RPT];
+        float4 rs[C + 1][RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) rs[0][i] = z[i];
+#pragma unroll
+        for (int u = 0; u < C; ++u) {
+            const float mu = sb[SG::MU + u], hh = cc[u][RPT];
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int row = rg + L::RG * i;
+                const float k = sb[SG::K + u * M + row];
+                const float g = sb[gps ? SG::G + u * M + row : SG::GT + u];
+                const float ci = cc[u][i];
+                const float a = g * (enc ? ci - k : k);
+                const float w = fmaxf(fmaf(-ci, ci, hh), 0.f);
+                const float bt = rsqrtf(fmaf(mu, mu, a * a * w));
+                beta[u][i] = bt;
+                rs[u + 1][i] = fma4(bt * fmaf(a, ci, mu), rs[u][i], (-bt * a) * h[u]);
+            }
+        }
+
+        // ---- the chunk's tokens in reverse ----
+        float dcv[C][RPT], dkin[C][RPT];
+#pragma unroll
+        for (int u = C - 1; u >= 0; --u) {
+            const int64_t bth = bth_of(n * C + u);
+            const float4 dy = *reinterpret_cast<const float4*>(sb + SG::DY + u * D + cg * 4);
+            const float mu = sb[SG::MU + u], hh = cc[u][RPT];
+            float qv[RPT], kv[RPT], gv[RPT];
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const int row = rg + L::RG * i;
+                qv[i] = sb[SG::Q + u * M + row];
+                kv[i] = sb[SG::K + u * M + row];
+                gv[i] = sb[gps ? SG::G + u * M + row : SG::GT + u];
+            }
+            float dq[RPT], dg[RPT], dk2[RPT];
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                dq[i] = dot4(rs[u + 1][i], dy);
+                dR[i] = fma4(qv[i], dy, dR[i]);
+                dg[i] = dot4(rs[u][i], dR[i]);
+                dk2[i] = dot4(h[u], dR[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                dq[i] = group_sum<L::TPR>(dq[i]);
+                dg[i] = group_sum<L::TPR>(dg[i]);
+                dk2[i] = group_sum<L::TPR>(dk2[i]);
+            }
+            // scalar chain rule per slot: g = beta (mu + a c), kap = -beta a,
+            // beta = (mu^2 + a^2 w)^(-1/2), w = max(|h|^2 - c^2, 0)
+            float gate[RPT], dgam[RPT];
+            float4 hp = f4(0.f);
+            float4 sc = f4(0.f);  // (d|h|^2, dmu, dgamma summed over slots, 0)
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const float ci = cc[u][i], bt = beta[u][i];
+                const float coef = enc ? ci - kv[i] : kv[i];
+                const float a = gv[i] * coef;
+                const float wraw = fmaf(-ci, ci, hh);
+                const float w = fmaxf(wraw, 0.f);
+                const float kap = -bt * a;
+                const float num = fmaf(a, ci, mu);
+                gate[i] = bt * num;
+                const float dbeta = num * dg[i] - a * dk2[i];
+                float da = bt * (ci * dg[i] - dk2[i]);
+                float dmu_i = bt * dg[i];
+                float dci = bt * a * dg[i];
+                const float tb = -0.5f * bt * bt * bt * dbeta;
+                dmu_i = fmaf(2.f * mu, tb, dmu_i);
+                da = fmaf(2.f * a * w, tb, da);
+                const float dw = a * a * tb;
+                float dhh_i = 0.f;
+                if (wraw > 0.f) {
+                    dhh_i = dw;
+                    dci = fmaf(-2.f * ci, dw, dci);
+                }
+                if (enc) {
+                    dci = fmaf(gv[i], da, dci);
+                    dkin[u][i] = -gv[i] * da;
+                } else {
+                    dkin[u][i] = gv[i] * da;
+                }
+                dgam[i] = coef * da;
+                dcv[u][i] = dci;
+                hp = fma4(kap, dR[i], fma4(dci, z[i], hp));
+                sc.x += dhh_i;
+                sc.y += dmu_i;
+                sc.z += dgam[i];
+            }
+            hp.x = strided_sum<L::TPR>(hp.x);
+            hp.y = strided_sum<L::TPR>(hp.y);
+            hp.z = strided_sum<L::TPR>(hp.z);
+            hp.w = strided_sum<L::TPR>(hp.w);
+            sc.x = strided_sum<L::TPR>(sc.x);
+            sc.y = strided_sum<L::TPR>(sc.y);
+            sc.z = strided_sum<L::TPR>(sc.z);
+            if (lane < L::TPR) *reinterpret_cast<float4*>(red + (u * NW + wave) * W + cg * 4) = hp;
+            if (lane == 0) *reinterpret_cast<float4*>(red + (u * NW + wave) * W + D) = sc;
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) dR[i] = gate[i] * dR[i];
+            if (cg == 0) {
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    const int64_t o = bth * M + rg + L::RG * i;
+                    p.dq[o] = dq[i];
+                    if (gps) p.dgamma[o] = dgam[i];
+                }
+            }
+        }
+        __syncthreads();  // the chunk's partial sums visible
+        // the sums over waves, one float4 of the chunk per thread
+        if (tid < C * (Q + 1)) {
+            const int xu = tid / (Q + 1), xc4 = tid % (Q + 1);
+            float4 acc = *reinterpret_cast<const float4*>(red + (xu * NW) * W + xc4 * 4);
+#pragma unroll
+            for (int w = 1; w < NW; ++w) acc = acc + *reinterpret_cast<const float4*>(red + (xu * NW + w) * W + xc4 * 4);
+            *reinterpret_cast<float4*>(tot + xu * W + xc4 * 4) = acc;
+        }
+        // the chunk before: its staged inputs and start state (loaded during this chunk)
+        if (n > 0) commit(pre, stg + ((n - 1) & 1) * SG::SIZE);
+        float4 snext[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) snext[i] = pre.st[i];
+        __syncthreads();  // the sums over slots and the staged inputs visible
+        // (the last chunk loads chunk 0 again: unconditional, no load under a branch)
+        issue(pre, n > 1 ? n - 2 : 0);
+
+        // ---- gradients that take the sums over slots; the gradient of Z ----
+        float4 dZ[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) dZ[i] = f4(0.f);
+#pragma unroll
+        for (int u = 0; u < C; ++u) {
+            const int64_t bth = bth_of(n * C + u);
+            const float4 hsum = *reinterpret_cast<const float4*>(tot + u * W + cg * 4);
+            const float4 ssum = *reinterpret_cast<const float4*>(tot + u * W + D);
+            const float4 dh = fma4(2.f * ssum.x, h[u], hsum);
+            float dkz[RPT] = {};
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                dZ[i] = fma4(dcv[u][i], h[u], dZ[i]);
+                if constexpr (DEC) {
+                    dZ[i] = fma4(sb[SG::K + u * M + rg + L::RG * i], dh, dZ[i]);
+                    dkz[i] = dot4(z[i], dh);
+                }
+            }
+            if constexpr (DEC) {
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) dkz[i] = group_sum<L::TPR>(dkz[i]);
+            }
+            if (cg == 0) {
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) p.dk[bth * M + rg + L::RG * i] = dkin[u][i] + dkz[i];
+            }
+            if (tid == 0) {
+                p.dmu[bth] = ssum.y;
+                if (!gps) p.dgamma[bth] = ssum.z;
+            }
+            if (rg == 0) *reinterpret_cast<float4*>(p.dv + bth * D + cg * 4) = enc ? dh : f4(0.f) - dh;
+        }
+        // the gradient of Z (running path and the chunk's uses of z) back through the projection
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const float4 dz = dR[i] + dZ[i];
+            const float pz = group_sum<L::TPR>(dot4(z[i], dz));
+            dR[i] = inv[i] * fma4(-pz, z[i], dz);
+            scur[i] = snext[i];
+        }
+    }
+
+    float* dsi = p.dstate_in + static_cast<int64_t>(bh) * M * D;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) *reinterpret_cast<float4*>(dsi + el(i)) = dR[i];
+}
+
+template <int M, int D, int C, typename TIn, bool DYB>
+static void launch_bwd_small_dec(const BwdParams& p, hipStream_t st) {
+    constexpr int NT = tokenloop_threads<M, D>();
+    const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H));
+    if (p.f.mode == 0)
+        hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, true>), grid, dim3(NT), 0, st, p);
+    else
+        hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, false>), grid, dim3(NT), 0, st, p);
+}
+
+template <int M, int D, int C>
+static int launch_bwd_small_mdc(const BwdParams& p, bool in_bf16, hipStream_t st) {
+    if constexpr (!bwd_small_fits<M, D>(C)) {
+        return -3;
+    } else {
+        if (in_bf16) {
+            if (p.dy_bf16)
+                launch_bwd_small_dec<M, D, C, uint16_t, true>(p, st);
+            else
+                launch_bwd_small_dec<M, D, C, uint16_t, false>(p, st);
+        } else {
+            if (p.dy_bf16)
+                launch_bwd_small_dec<M, D, C, float, true>(p, st);
+            else
+                launch_bwd_small_dec<M, D, C, float, false>(p, st);
+        }
+        return hipGetLastError() == hipSuccess ? 0 : -5;
+    }
+}
+
+template <int M, int D>
+static int launch_bwd_small_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
+    switch (p.f.chunk) {
+        case 2: return launch_bwd_small_mdc<M, D, 2>(p, in_bf16, st);
+        case 4: return launch_bwd_small_mdc<M, D, 4>(p, in_bf16, st);
+        case 8: return launch_bwd_small_mdc<M, D, 8>(p, in_bf16, st);
+        default: return -3;
+    }
+}
+
+template <int M>
+int launch_bwd_small_m(int d, const BwdParams& p, bool in_bf16, hipStream_t st) {
+    switch (d) {
+        case 16: return launch_bwd_small_md<M, 16>(p, in_bf16, st);
+        case 32: return launch_bwd_small_md<M, 32>(p, in_bf16, st);
+        case 64: return launch_bwd_small_md<M, 64>(p, in_bf16, st);
+        case 128: return launch_bwd_small_md<M, 128>(p, in_bf16, st);
+        default: return -3;
+    }
+}
+
+template <int M>
+bool bwd_small_fits_m(int d, int C) {
+    switch (d) {
+        case 16: return bwd_small_fits<M, 16>(C);
+        case 32: return bwd_small_fits<M, 32>(C);
+        case 64: return bwd_small_fits<M, 64>(C);
+        case 128: return bwd_small_fits<M, 128>(C);
+        default: return false;
+    }
+}
+
+}  // namespace osr

@@ -1,0 +1,6 @@
+// osr_bwd_small_m64.hip -- the small-chunk reverse walk for m = 64 (kernels: osr_bwd_small.h).
+#include "osr_bwd_small.h"
+
+namespace osr {
+template int launch_bwd_small_m<64>(int, const BwdParams&, bool, hipStream_t);
+}  // namespace osr

@@ -27,6 +27,8 @@ struct Params {
     float* raw_c;      // if set (backward): c and beta of every token and slot, [B*H*NC][m*C] in
     float* raw_b;      // the layout of the gates, and |h|^2 of every token, [B*H*NC][C]
     float* raw_hh;
+    float* hrec;       // if set (backward, small chunks, decoding objective): h of every token,
+                       // [B*H][T][d] fp32 (the small-chunk token loop only)
     int B, T, H;
     int chunk;         // C
     int gamma_per_slot;

@@ -80,6 +80,13 @@ int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 // the workspace (states_ready).  Same workspace layout as launch_bwd.
 bool bwd_chunk_supported(int m, int d, int C, bool in_bf16, bool lin1, int mode);
 int launch_bwd_chunk(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
+// The reverse walk at small chunks (osr_bwd_small.hip): C in {2, 4, 8}, at most
+// 2 slot rows per thread of the token loop's layout, the default linearisation.
+// Its phase 1 is the forward's small-chunk token loop with raw (and, decoding
+// objective, hrec) set; f.hrec then points at those records.  Same workspace
+// layout as launch_bwd, plus hrec.
+bool bwd_small_supported(int m, int d, int C, bool lin1);
+int launch_bwd_small(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 
 // Layer glue (HBM-bound streaming kernels).  pre: q = conv4(xq), k = conv4(xk)
 // (depthwise causal, width 4, N = H*m channels per token row), gamma =

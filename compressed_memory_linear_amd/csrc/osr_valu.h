@@ -85,6 +85,13 @@ __device__ __forceinline__ void project_rows(float4 (&s)[L::RPT]) {
 }
 
 
+// Threads per workgroup of the token loops at (M, D): one float4 of a state
+// row per thread, at most 512 threads.
+template <int M, int D>
+constexpr int tokenloop_threads() {
+    return (M * (D / 4) < 512) ? M * (D / 4) : 512;
+}
+
 // Tokens per batched exchange over slots (the backward's reverse walk keeps 3
 // values per slot row and token of a batch in registers).
 template <class L>

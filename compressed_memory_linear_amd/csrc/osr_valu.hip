@@ -247,6 +247,9 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
 // chunk computes; h alternates between two LDS buffers by chunk parity, so a
 // chunk's h is written while no thread can still read the buffer (the barrier
 // inside the exchange of the chunk before orders it).
+// For the backward (y and state_out null, raw set): every chunk-start state
+// before projection and the end state go to raw, and (decoding objective,
+// hrec set) every chunk's h to hrec; the read-out is skipped.
 template <int M, int D, int NT, typename TIn, int CB>
 __global__ __launch_bounds__(NT) void osr_tokenloop_small_kernel(Params p) {
     using L = ValuLayout<M, D, NT>;
@@ -302,7 +305,13 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_small_kernel(Params p) {
     load_chunk(cur, 0);
     int ybatch = 0;
 
+    float* const raw = p.raw ? p.raw + static_cast<int64_t>(bh) * p.raw_stride : nullptr;
     for (int n = 0; n < NCH; ++n) {
+        if (raw) {
+#pragma unroll
+            for (int i = 0; i < RPT; ++i)
+                *reinterpret_cast<float4*>(raw + static_cast<int64_t>(n) * M * D + (rg + L::RG * i) * D + cg * 4) = s[i];
+        }
         project_rows<L>(s);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) z[i] = s[i];
@@ -328,6 +337,9 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_small_kernel(Params p) {
 #pragma unroll
                 for (int w = 1; w < L::NW; ++w) acc = acc + *reinterpret_cast<const float4*>(rb + (uo * L::NW + w) * W + co * 4);
                 *reinterpret_cast<float4*>(hb + uo * D + co * 4) = acc - cur.vo;
+                if (p.hrec)
+                    *reinterpret_cast<float4*>(p.hrec + (static_cast<int64_t>(bh) * T + n * CB + uo) * D + co * 4) =
+                        acc - cur.vo;
             }
             __syncthreads();
 #pragma unroll
@@ -371,6 +383,10 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_small_kernel(Params p) {
                 yp[u] = fma4(cur.q[u][i], s[i], yp[u]);
             }
         }
+        if (!p.y) {
+            cur = nxt;
+            continue;
+        }
         float* rb = redy + (ybatch & 1) * (BT * L::NW * W);
         const int u0 = (n * CB) % BT;  // this chunk's first slot in the y batch
 #pragma unroll
@@ -402,6 +418,12 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_small_kernel(Params p) {
         }
         cur = nxt;
     }
+    if (raw) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            *reinterpret_cast<float4*>(raw + static_cast<int64_t>(NCH) * M * D + (rg + L::RG * i) * D + cg * 4) = s[i];
+    }
+    if (!p.state_out) return;
     project_rows<L>(s);
     float* sout = p.state_out + static_cast<int64_t>(bh) * M * D;
 #pragma unroll
@@ -423,7 +445,7 @@ static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_
     // shortens each workgroup's arithmetic between its state load and store; measured 9% faster
     // than 4 waves at m = d = 128.
     constexpr int NT_DEC = (M * TPR < 512) ? M * TPR : 512;
-    constexpr int NT_TOK = (M * TPR < 512) ? M * TPR : 512;
+    constexpr int NT_TOK = tokenloop_threads<M, D>();
     const dim3 grid(static_cast<unsigned>(p.B) * static_cast<unsigned>(p.H));
     if (decode) {
         if (in_bf16)

@@ -132,12 +132,15 @@ extern "C" {
 
 /*
  * Form of the backward (lattice_osr_bwd_chunked; the forward ignores it).
- * WALK: a reverse walk over the tokens, in fp32 on the vector units.
+ * WALK: the general reverse walk over the tokens, in fp32 on the vector units.
  * CHUNK: the chunk-parallel form on the fp32 matrix cores (built for
  * m = d = chunk_size = 64, bf16 inputs, the default linearisation, the
  * decoding and similarity objectives; elsewhere the call returns
- * LATTICE_OSR_ERR_UNSUPPORTED).  AUTO: CHUNK where it is built, else WALK.
- * Both compute the same gradient up to fp32 rounding.
+ * LATTICE_OSR_ERR_UNSUPPORTED).  AUTO: CHUNK where it is built; at
+ * chunk_size 2, 4 or 8 with the default linearisation and m d <= 4096 (and
+ * d <= 64 at chunk_size 8), a reverse walk that keeps a chunk's per-token
+ * states in registers; else WALK.  All compute the same gradient up to fp32
+ * rounding.
  */
 #define LATTICE_OSR_BWD_AUTO 0
 #define LATTICE_OSR_BWD_WALK 1

@@ -359,8 +359,11 @@ def test_bwd_null_pointers_and_shapes():
     assert _bwd_call(d, _bwd_ptrs(), 0) == osr.ERR_SHAPE
     d2 = osr.make_desc(1, 8, 1, 16, 48)
     assert _bwd_call(d2, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED
+    # (the first linearisation runs the general walk, whose workspace is that of
+    # the default linearisation on the general walk)
     d3 = osr.make_desc(1, 8, 1, 16, 16, linearisation=osr.LIN1)
-    assert osr.lattice_osr_bwd_workspace_bytes(d3, 4) == osr.lattice_osr_bwd_workspace_bytes(d, 4)
+    assert osr.lattice_osr_bwd_workspace_bytes(d3, 4) == \
+        osr.lattice_osr_bwd_workspace_bytes(osr.make_desc(1, 8, 1, 16, 16, bwd_form=osr.BWD_WALK), 4)
     d4 = osr.make_desc(1, 8, 1, 16, 16, linearisation=2)
     assert _bwd_call(d4, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED
     with pytest.raises(osr.OSRError):
@@ -389,6 +392,30 @@ def test_bwd_form_choice():
             osr.lattice_osr_bwd_workspace_bytes(chunk, C)
         for form in (osr.BWD_AUTO, osr.BWD_WALK):
             assert osr.lattice_osr_bwd_workspace_bytes(osr.make_desc(**kw, bwd_form=form), C) > 0
+
+
+def test_bwd_small_chunk_form_workspace():
+    """The small-chunk reverse walk (automatic form, C in {2, 4, 8}, the default
+    linearisation, at most 2 slot rows per thread of the token loop, C within
+    its exchange batch) adds every token's h (fp32 [B*H][T][d]) to the
+    workspace for the decoding objective; nothing for the other objectives,
+    and nothing where the general walk runs."""
+    def ws(C, form=osr.BWD_AUTO, **kw):
+        return osr.lattice_osr_bwd_workspace_bytes(osr.make_desc(**kw, bwd_form=form), C)
+
+    applies = [(2, 16, 16), (4, 64, 64), (8, 64, 64), (4, 32, 128), (8, 128, 16), (2, 128, 32)]
+    for C, m, d in applies:
+        kw = dict(B=2, T=64, H=3, m=m, d=d)
+        assert ws(C, **kw) - ws(C, osr.BWD_WALK, **kw) == 2 * 3 * 64 * d * 4, (C, m, d)
+        for mode in (osr.MODE_SIM, osr.MODE_ENC):
+            assert ws(C, mode=mode, **kw) == ws(C, osr.BWD_WALK, mode=mode, **kw), (C, m, d, mode)
+    general = [dict(C=4, m=64, d=128), dict(C=4, m=128, d=64), dict(C=8, m=32, d=128), dict(C=16, m=64, d=64),
+               dict(C=1, m=64, d=64), dict(C=4, m=64, d=64, linearisation=osr.LIN1)]
+    for g in general:
+        kw = dict(B=2, T=64, H=3)
+        kw.update(g)
+        C = kw.pop("C")
+        assert ws(C, **kw) == ws(C, osr.BWD_WALK, **kw), g
 
 
 def test_bwd_workspace_too_small():
