@@ -211,11 +211,14 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
                 z[i] = inv[i] * scur[i];
             }
         }
+        // c and |h|^2 of every token of the chunk
+        float cc[C][RPT + 1];
+        float beta[C][RPT];
+        float4 rs[C + 1][RPT];
         float4 h[C];
 #pragma unroll
         for (int u = 0; u < C; ++u) h[u] = *reinterpret_cast<const float4*>(sb + SG::H + u * D + cg * 4);
-        // c and |h|^2 of every token of the chunk
-        float cc[C][RPT + 1];
+        {
 #pragma unroll
         for (int u = 0; u < C; ++u) {
 #pragma unroll
@@ -228,8 +231,6 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
             for (int i = 0; i <= RPT; ++i) cc[u][i] = group_sum<L::TPR>(cc[u][i]);
         // the forward again, elementwise: beta, and the state before every token
         // (rs[u]) and after the last (rs[C])
-        float beta[C][RPT];
-        float4 rs[C + 1][RPT];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) rs[0][i] = z[i];
 #pragma unroll
@@ -248,6 +249,16 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
                 rs[u + 1][i] = fma4(bt * fmaf(a, ci, mu), rs[u][i], (-bt * a) * h[u]);
             }
         }
+        }
+        // At C = 8, h is read from LDS again below rather than held in registers
+        // across the reverse (that spilled); at C <= 4 it stays in registers.
+        if constexpr (C > 4) asm volatile("" ::: "memory");
+        auto hat = [&](int u) __attribute__((always_inline)) {
+            if constexpr (C > 4)
+                return *reinterpret_cast<const float4*>(sb + SG::H + u * D + cg * 4);
+            else
+                return h[u];
+        };
 
         // ---- the chunk's tokens in reverse ----
         float dcv[C][RPT], dkin[C][RPT];
@@ -255,6 +266,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
         for (int u = C - 1; u >= 0; --u) {
             const int64_t bth = bth_of(n * C + u);
             const float4 dy = *reinterpret_cast<const float4*>(sb + SG::DY + u * D + cg * 4);
+            const float4 hu = hat(u);
             const float mu = sb[SG::MU + u], hh = cc[u][RPT];
             float qv[RPT], kv[RPT], gv[RPT];
 #pragma unroll
@@ -270,7 +282,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
                 dq[i] = dot4(rs[u + 1][i], dy);
                 dR[i] = fma4(qv[i], dy, dR[i]);
                 dg[i] = dot4(rs[u][i], dR[i]);
-                dk2[i] = dot4(h[u], dR[i]);
+                dk2[i] = dot4(hu, dR[i]);
             }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
@@ -366,11 +378,12 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
             const int64_t bth = bth_of(n * C + u);
             const float4 hsum = *reinterpret_cast<const float4*>(tot + u * W + cg * 4);
             const float4 ssum = *reinterpret_cast<const float4*>(tot + u * W + D);
-            const float4 dh = fma4(2.f * ssum.x, h[u], hsum);
+            const float4 hu = hat(u);
+            const float4 dh = fma4(2.f * ssum.x, hu, hsum);
             float dkz[RPT] = {};
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                dZ[i] = fma4(dcv[u][i], h[u], dZ[i]);
+                dZ[i] = fma4(dcv[u][i], hu, dZ[i]);
                 if constexpr (DEC) {
                     dZ[i] = fma4(sb[SG::K + u * M + rg + L::RG * i], dh, dZ[i]);
                     dkz[i] = dot4(z[i], dh);
