@@ -72,10 +72,9 @@ def chain_reference_ms(w: dict, chunk: int) -> float:
     return (w["T"] / chunk) * per_chunk / (BF16_MFMA_PEAK_TFLOPS * 1e12 / 256) * 1e3
 
 
-# Sources of the backward kernel: not part of the forward and decode kernels
-# whose traffic counters are keyed by the hash below.
-BWD_SOURCES = ("osr_bwd.hip", "osr_bwd_kernel.h", "osr_bwd_m16.hip", "osr_bwd_m32.hip", "osr_bwd_m64.hip",
-               "osr_bwd_m128.hip", "osr_bwd_chunk.hip")
+# Sources of the backward kernels (every csrc/osr_bwd* file): not part of the
+# forward and decode kernels whose traffic counters are keyed by the hash below.
+BWD_PREFIX = "osr_bwd"
 # Source of the layer-glue kernels: not part of either.
 GLUE_SOURCES = ("osr_glue.hip",)
 
@@ -84,7 +83,8 @@ def source_hash() -> str:
     """Hash of the sources the forward and decode kernels are built from."""
     h = hashlib.sha256()
     for p in sorted(glob.glob(os.path.join(ROOT, "compressed_memory_linear_amd", "csrc", "*"))):
-        if os.path.basename(p) in BWD_SOURCES + GLUE_SOURCES:
+        base = os.path.basename(p)
+        if base.startswith(BWD_PREFIX) or base in GLUE_SOURCES:
             continue
         with open(p, "rb") as f:
             h.update(f.read())
