@@ -226,6 +226,13 @@ size_t bwd_small_h_bytes(const lattice_osr_desc* d, int C) {
     return static_cast<size_t>(d->B) * d->H * d->T * d->d * sizeof(float);
 }
 
+// Workgroups per sequence that the workspace provides hand-off buffers for (the
+// launch may use fewer where the device has fewer compute units).
+int bwd_parts(const lattice_osr_desc* d, int C) {
+    if (bwd_small_form(d, C)) return osr::bwd_small_split_p(d->B, d->H, d->m, C, d->chain_wgs);
+    return osr::bwd_split_p(d->B, d->H, d->m, d->d, C, bwd_uses_chain(d, C), d->chain_wgs);
+}
+
 // ... then, where the slot rows of a sequence split over several workgroups,
 // their hand-off buffers.
 size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
@@ -235,7 +242,7 @@ size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
         n += osr::mfma_chain_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1) +
              bwd_chain_extra_bytes(d, C);
     n += bwd_small_h_bytes(d, C);
-    return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, osr::bwd_split_p(d->B, d->H, d->m, d->d, C, chain, d->chain_wgs));
+    return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, bwd_parts(d, C));
 }
 
 // The chunk-parallel backward where it is built and not turned off.
@@ -500,6 +507,17 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
         rc = osr::launch_valu(false, desc->m, desc->d, pf, in_bf16, st);
         if (rc) return rc;
         p.f.hrec = pf.hrec;
+        // the rows of a sequence over two workgroups where all of them can be resident
+        p.split_p = bwd_parts(desc, chunk_size);
+        p.xbuf = nullptr;
+        p.xflags = nullptr;
+        if (p.split_p > 1 && static_cast<int64_t>(desc->B) * desc->H * p.split_p > device_cus()) p.split_p = 1;
+        if (p.split_p > 1) {
+            const size_t xoff = need - osr::bwd_xchg_bytes(desc->B, desc->H, desc->d, bwd_parts(desc, chunk_size));
+            p.xbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + xoff);
+            p.xflags = reinterpret_cast<int*>(p.xbuf + static_cast<size_t>(desc->B) * desc->H * 2 * p.split_p * 8 *
+                                                           (desc->d + 4));
+        }
         return osr::launch_bwd_small(desc->m, desc->d, p, in_bf16, st);
     }
     // slot rows split over workgroups: every workgroup of a sequence must be resident

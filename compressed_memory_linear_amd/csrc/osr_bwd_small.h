@@ -25,6 +25,13 @@
 //     sums over slots of all C tokens go through one LDS exchange;
 //   - two barriers per chunk: one publishes the partial sums, the other the
 //     sums over waves together with the next chunk's staged inputs.
+// The walk is bound by VALU issue on the B*H compute units that hold a
+// sequence.  With P = 2 the slot rows of a sequence split over two workgroups
+// (M / 2 rows each, half the instructions per chunk); every row-local step is
+// unchanged, and the chunk's sums over slots, the only step that crosses rows,
+// go through the device-coherent hand-off of the split walk (osr_bwd_kernel.h):
+// each workgroup publishes its rows' sums, waits for the other's, and adds the
+// parts in workgroup order, so both hold the same sums.
 #pragma once
 
 #include <type_traits>
@@ -42,6 +49,12 @@ template <int M, int D>
 constexpr bool bwd_small_fits(int C) {
     using L = ValuLayout<M, D, tokenloop_threads<M, D>()>;
     return L::RPT <= 2 && (C == 2 || C == 4 || C == 8) && C <= TokBatch<L>::BT;
+}
+
+// Threads per workgroup of the walk with the rows split over P workgroups.
+template <int M, int D, int P>
+constexpr int bwd_small_threads() {
+    return tokenloop_threads<M / P, D>();
 }
 
 // Four consecutive elements loaded without conversion (the conversion, and so
@@ -88,9 +101,10 @@ struct SmallStage {
 
 // DEC: decoding objective (h = sum_i k_i z_i - v, from the phase-1 records);
 // otherwise h = -v (similarity) or v (encoding layer).  DYB: dy in bf16.
-template <int M, int D, int NT, int C, typename TIn, bool DYB, bool DEC>
+template <int M, int D, int NT, int C, typename TIn, bool DYB, bool DEC, int P>
 __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
-    using L = ValuLayout<M, D, NT>;
+    static_assert(P == 1 || (P == 2 && M / P >= 16), "split: two workgroups of 16 rows or more");
+    using L = ValuLayout<M / P, D, NT>;
     using SG = SmallStage<M, D, C>;
     using DYT = typename std::conditional<DYB, uint16_t, float>::type;
     using HT = typename std::conditional<DEC, float, TIn>::type;
@@ -102,10 +116,14 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) float red[C * NW * W];    // partial sums over each wave's slots
     __shared__ __attribute__((aligned(16))) float tot[C * W];         // the chunk's sums over slots
 
-    const int bh = blockIdx.x;
+    const int bh = P > 1 ? blockIdx.x / P : blockIdx.x;
+    const int pidx = P > 1 ? blockIdx.x % P : 0;  // this workgroup's rows: [pidx M/P, (pidx + 1) M/P)
     const int b = bh / p.f.H, hd = bh % p.f.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cg = tid % L::TPR, rg = tid / L::TPR;
+    // rg: the (global) slot row of this thread's first row
+    const int cg = tid % L::TPR, rg = pidx * (M / P) + tid / L::TPR;
+    int nxch = 0;          // chunks exchanged with the other workgroup (P > 1)
+    bool xbroken = false;  // a wait for it gave up (then the results are wrong, but every wave ends)
     const int T = p.f.T, NC = T / C;
     const bool enc = p.f.mode == 2;
     const bool gps = p.f.gamma_per_slot != 0;
@@ -353,13 +371,60 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
         }
         __syncthreads();  // the chunk's partial sums visible
         // the sums over waves, one float4 of the chunk per thread
-        if (tid < C * (Q + 1)) {
-            const int xu = tid / (Q + 1), xc4 = tid % (Q + 1);
-            float4 acc = *reinterpret_cast<const float4*>(red + (xu * NW) * W + xc4 * 4);
+        const bool mine = tid < C * (Q + 1);
+        const int xu = tid / (Q + 1), xc4 = tid % (Q + 1);
+        float4 acc = f4(0.f);
+        if (mine) {
+            acc = *reinterpret_cast<const float4*>(red + (xu * NW) * W + xc4 * 4);
 #pragma unroll
             for (int w = 1; w < NW; ++w) acc = acc + *reinterpret_cast<const float4*>(red + (xu * NW + w) * W + xc4 * 4);
-            *reinterpret_cast<float4*>(tot + xu * W + xc4 * 4) = acc;
         }
+        if constexpr (P > 1) {
+            // The other workgroup's sums of this chunk (over its rows): publish this
+            // one's, wait for the other's, add both in workgroup order.  Parts
+            // alternate between two buffers by chunk parity: a buffer is rewritten two
+            // chunks later, after the other workgroup has published the chunk in
+            // between, which it does only after reading this one.
+            constexpr int XW = 8 * W;  // floats per part (at most 8 tokens)
+            static_assert(C <= 8, "hand-off part size");
+            float* xb = p.xbuf + (static_cast<int64_t>(bh) * 2 + (nxch & 1)) * P * XW;
+            const __amdgpu_buffer_rsrc_t xr = xrsrc(xb, static_cast<uint32_t>(P * XW * sizeof(float)));
+            const uint32_t off = static_cast<uint32_t>(xu * W + xc4 * 4) * 4;
+            if (mine)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(bwd_u32x4, acc), xr,
+                                                       static_cast<uint32_t>(pidx * XW) * 4 + off, 0, XCPOL_SC1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's part store has retired
+            __syncthreads();  // ... and every thread's
+            if (tid == 0)
+                __hip_atomic_store(p.xflags + (bh * P + pidx) * XFLAG_STRIDE, nxch + 1, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            if (tid < P && tid != pidx && !xbroken) {
+                const int* fl = p.xflags + (bh * P + tid) * XFLAG_STRIDE;
+                int spins = 0;
+                while (__hip_atomic_load(const_cast<int*>(fl), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= nxch) {
+                    if (++spins >= XSPIN) {
+                        xbroken = true;
+                        break;
+                    }
+                }
+            }
+            __syncthreads();  // the other part is published
+            asm volatile("" ::: "memory");  // the reads below stay after the barrier
+            if (mine) {
+                float4 part[P];
+#pragma unroll
+                for (int q = 0; q < P; ++q)
+                    part[q] = q == pidx ? acc
+                                        : __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                         xr, static_cast<uint32_t>(q * XW) * 4 + off, 0,
+                                                                         XCPOL_SC1));
+                acc = part[0];
+#pragma unroll
+                for (int q = 1; q < P; ++q) acc = acc + part[q];
+            }
+            ++nxch;
+        }
+        if (mine) *reinterpret_cast<float4*>(tot + xu * W + xc4 * 4) = acc;
         // the chunk before: its staged inputs and start state (loaded during this chunk)
         if (n > 0) commit(pre, stg + ((n - 1) & 1) * SG::SIZE);
         float4 snext[RPT];
@@ -397,7 +462,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
 #pragma unroll
                 for (int i = 0; i < RPT; ++i) p.dk[bth * M + rg + L::RG * i] = dkin[u][i] + dkz[i];
             }
-            if (tid == 0) {
+            // (every workgroup of a sequence holds the same sums: the first writes them)
+            if (tid == 0 && pidx == 0) {
                 p.dmu[bth] = ssum.y;
                 if (!gps) p.dgamma[bth] = ssum.z;
             }
@@ -418,31 +484,55 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     for (int i = 0; i < RPT; ++i) *reinterpret_cast<float4*>(dsi + el(i)) = dR[i];
 }
 
-template <int M, int D, int C, typename TIn, bool DYB>
+template <int M, int D, int C, typename TIn, bool DYB, int P>
 static void launch_bwd_small_dec(const BwdParams& p, hipStream_t st) {
-    constexpr int NT = tokenloop_threads<M, D>();
-    const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H));
+    constexpr int NT = bwd_small_threads<M, D, P>();
+    const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H) * P);
+    if constexpr (P > 1) {
+        // progress counters to zero (they count the chunks of this call)
+        const int nflags = p.f.B * p.f.H * P * XFLAG_STRIDE;
+        hipLaunchKernelGGL(osr_bwd_fill_ints<0>, dim3((nflags + 255) / 256), dim3(256), 0, st, p.xflags, nflags);
+    }
     if (p.f.mode == 0)
-        hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, true>), grid, dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, true, P>), grid, dim3(NT), 0, st, p);
     else
-        hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, false>), grid, dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, false, P>), grid, dim3(NT), 0, st, p);
 }
 
+template <int M, int D, int C, int P>
+static void launch_bwd_small_p(const BwdParams& p, bool in_bf16, hipStream_t st) {
+    if (in_bf16) {
+        if (p.dy_bf16)
+            launch_bwd_small_dec<M, D, C, uint16_t, true, P>(p, st);
+        else
+            launch_bwd_small_dec<M, D, C, uint16_t, false, P>(p, st);
+    } else {
+        if (p.dy_bf16)
+            launch_bwd_small_dec<M, D, C, float, true, P>(p, st);
+        else
+            launch_bwd_small_dec<M, D, C, float, false, P>(p, st);
+    }
+}
+
+// P (p.split_p) = 2: the rows of a sequence over two workgroups, with the
+// hand-off buffers p.xbuf / p.xflags (the host ensures B*H*2 workgroups are
+// resident at once).
 template <int M, int D, int C>
 static int launch_bwd_small_mdc(const BwdParams& p, bool in_bf16, hipStream_t st) {
     if constexpr (!bwd_small_fits<M, D>(C)) {
         return -3;
     } else {
-        if (in_bf16) {
-            if (p.dy_bf16)
-                launch_bwd_small_dec<M, D, C, uint16_t, true>(p, st);
-            else
-                launch_bwd_small_dec<M, D, C, uint16_t, false>(p, st);
+        if (p.split_p == 2) {
+            if constexpr (M / 2 >= 16) {
+                if (p.xbuf == nullptr || p.xflags == nullptr) return -3;
+                launch_bwd_small_p<M, D, C, 2>(p, in_bf16, st);
+            } else {
+                return -3;
+            }
+        } else if (p.split_p == 1) {
+            launch_bwd_small_p<M, D, C, 1>(p, in_bf16, st);
         } else {
-            if (p.dy_bf16)
-                launch_bwd_small_dec<M, D, C, float, true>(p, st);
-            else
-                launch_bwd_small_dec<M, D, C, float, false>(p, st);
+            return -3;
         }
         return hipGetLastError() == hipSuccess ? 0 : -5;
     }

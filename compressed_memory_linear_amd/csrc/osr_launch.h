@@ -85,7 +85,10 @@ int launch_bwd_chunk(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t
 // Its phase 1 is the forward's small-chunk token loop with raw (and, decoding
 // objective, hrec) set; f.hrec then points at those records.  Same workspace
 // layout as launch_bwd, plus hrec.
+// split_p = 2 splits a sequence's slot rows over two workgroups, with the
+// hand-off buffers of the split walk (bwd_xchg_bytes) in xbuf / xflags.
 bool bwd_small_supported(int m, int d, int C, bool lin1);
+int bwd_small_split_p(int B, int H, int m, int C, int chain_wgs);
 int launch_bwd_small(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 
 // Layer glue (HBM-bound streaming kernels).  pre: q = conv4(xq), k = conv4(xk)

@@ -298,8 +298,18 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * chunk's matrix form (16-token tiles), the gate gradients by recursions
  * over the tile's tokens; the same workspace and the same result up to fp32
  * rounding (the token walk's to 1e-4 of RMS; with forget gates mu near 0 the
- * tile's gate products span many decades and the two agree to 5e-3).  The
- * remaining rules (shapes,
+ * tile's gate products span many decades and the two agree to 5e-3).  At
+ * chunk_size 2, 4 or 8 with desc->bwd_form AUTO (the default linearisation,
+ * m d <= 4096, chunk_size <= 4 at d = 128) a reverse walk that keeps each
+ * chunk's states in registers runs after a forward pass that stores the
+ * chunk-start states; the decoding objective adds every token's h to the
+ * workspace, 4 T d bytes per (b,h).  There, with desc->chain_wgs =
+ * LATTICE_OSR_WGS_AUTO, chunk_size >= 4, m >= 32 and B*H*2 <= 256, the slot rows of each
+ * sequence are split over 2 workgroups that exchange each chunk's sums over
+ * slots through hand-off buffers at the end of the workspace (the same size
+ * as above with P = 2); one workgroup on devices with fewer than B*H*2
+ * compute units, or with LATTICE_OSR_WGS_ONE.  The result equals the
+ * general walk's up to fp32 rounding.  The remaining rules (shapes,
  * chunk sizes, alignment of the inputs, status codes, asynchrony) are those
  * of lattice_osr_fwd_chunked.
  */

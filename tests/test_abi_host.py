@@ -398,17 +398,27 @@ def test_bwd_small_chunk_form_workspace():
     """The small-chunk reverse walk (automatic form, C in {2, 4, 8}, the default
     linearisation, at most 2 slot rows per thread of the token loop, C within
     its exchange batch) adds every token's h (fp32 [B*H][T][d]) to the
-    workspace for the decoding objective; nothing for the other objectives,
-    and nothing where the general walk runs."""
+    workspace for the decoding objective, and, where the rows of a sequence
+    split over two workgroups, their hand-off buffers; nothing where the
+    general walk runs."""
     def ws(C, form=osr.BWD_AUTO, **kw):
         return osr.lattice_osr_bwd_workspace_bytes(osr.make_desc(**kw, bwd_form=form), C)
 
     applies = [(2, 16, 16), (4, 64, 64), (8, 64, 64), (4, 32, 128), (8, 128, 16), (2, 128, 32)]
     for C, m, d in applies:
         kw = dict(B=2, T=64, H=3, m=m, d=d)
-        assert ws(C, **kw) - ws(C, osr.BWD_WALK, **kw) == 2 * 3 * 64 * d * 4, (C, m, d)
+        # from m = 32 and C = 4 the rows of a sequence split over 2 workgroups (B*H*2 <= 256):
+        # their hand-off buffers, 2 parities x 2 parts x 8 tokens x (d + 4) floats and 2 counters
+        xchg = 2 * 3 * (2 * 2 * 8 * (d + 4) * 4 + 2 * 128) if m >= 32 and C >= 4 else 0
+        one = dict(kw, chain_wgs=osr.WGS_ONE)
+        assert ws(C, **kw) - ws(C, osr.BWD_WALK, **kw) == 2 * 3 * 64 * d * 4 + xchg, (C, m, d)
+        assert ws(C, **one) - ws(C, osr.BWD_WALK, **one) == 2 * 3 * 64 * d * 4, (C, m, d)
         for mode in (osr.MODE_SIM, osr.MODE_ENC):
-            assert ws(C, mode=mode, **kw) == ws(C, osr.BWD_WALK, mode=mode, **kw), (C, m, d, mode)
+            assert ws(C, mode=mode, **kw) - ws(C, osr.BWD_WALK, mode=mode, **kw) == xchg, (C, m, d, mode)
+            assert ws(C, mode=mode, **one) == ws(C, osr.BWD_WALK, mode=mode, **one), (C, m, d, mode)
+    # no split once B*H*2 exceeds 256 compute units
+    big = dict(B=8, T=64, H=17, m=64, d=64)
+    assert ws(4, **big) - ws(4, osr.BWD_WALK, **big) == 8 * 17 * 64 * 64 * 4
     general = [dict(C=4, m=64, d=128), dict(C=4, m=128, d=64), dict(C=8, m=32, d=128), dict(C=16, m=64, d=64),
                dict(C=1, m=64, d=64), dict(C=4, m=64, d=64, linearisation=osr.LIN1)]
     for g in general:

@@ -61,13 +61,13 @@ def _upstream(inp, seed, dy_bf16=False):
     return dy, dso
 
 
-def _gpu_bwd(inp, dy, dso, C, mode, form, dy_bf16=False):
+def _gpu_bwd(inp, dy, dso, C, mode, form, dy_bf16=False, wgs=osr.WGS_AUTO):
     t = osr.to_device(inp, "cuda")
     dyt = torch.from_numpy(dy).cuda()
     if dy_bf16:
         dyt = dyt.to(torch.bfloat16)  # exact: dy already holds bf16 values
     g = osr.lattice_osr_bwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], dyt,
-                                    torch.from_numpy(dso).cuda(), C, mode=mode, bwd_form=form)
+                                    torch.from_numpy(dso).cuda(), C, mode=mode, bwd_form=form, chain_wgs=wgs)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in g.items()}
 
@@ -124,6 +124,25 @@ def test_small_chunk_backward(B, T, H, m, d, C, dt, per_slot, mode, dyb):
     _report_and_check("vs oracle", _errs(got, ref), TOL[dt])
     walk = _gpu_bwd(inp, dy, dso, C, mode, osr.BWD_WALK, dy_bf16=dyb)
     _report_and_check("vs general walk", _errs(got, walk), AGREE)
+
+
+# (B, T, H, m, d, C, objective): from m = 32 and C = 4 the automatic choice splits
+# the slot rows of each sequence over two workgroups that exchange each chunk's sums
+@pytest.mark.parametrize("B,T,H,m,d,C,mode", [(2, 128, 3, 64, 64, 4, osr.MODE_DEC), (1, 64, 2, 32, 128, 4, osr.MODE_DEC),
+                                              (2, 64, 2, 128, 16, 8, osr.MODE_SIM), (1, 96, 4, 32, 32, 8, osr.MODE_DEC)])
+def test_small_chunk_backward_split_vs_one(B, T, H, m, d, C, mode):
+    """The split over two workgroups against one workgroup per sequence
+    (LATTICE_OSR_WGS_ONE): the same gradient up to the order of the fp32
+    sums over slots (1e-4 of RMS), bit-identical on a rerun."""
+    _say(f"bwd small-chunk split vs one B{B} T{T} H{H} m{m} d{d} C{C} mode{mode}")
+    inp = synth.make_inputs(B, T, H, m, d, seed=41, in_dtype=synth.BF16)
+    dy, dso = _upstream(inp, 41)
+    split = _gpu_bwd(inp, dy, dso, C, mode, osr.BWD_AUTO)
+    one = _gpu_bwd(inp, dy, dso, C, mode, osr.BWD_AUTO, wgs=osr.WGS_ONE)
+    _report_and_check("split vs one workgroup", _errs(split, one), AGREE)
+    again = _gpu_bwd(inp, dy, dso, C, mode, osr.BWD_AUTO)
+    for key in KEYS:
+        assert np.array_equal(split[key], again[key]), key
 
 
 def test_small_chunk_backward_deterministic():
