@@ -242,6 +242,7 @@ size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
         n += osr::mfma_chain_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1) +
              bwd_chain_extra_bytes(d, C);
     n += bwd_small_h_bytes(d, C);
+    if (bwd_small_form(d, C)) return n + osr::bwd_small_xchg_bytes(d->B, d->H, d->d, bwd_parts(d, C));
     return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, bwd_parts(d, C));
 }
 
@@ -513,10 +514,8 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
         p.xflags = nullptr;
         if (p.split_p > 1 && static_cast<int64_t>(desc->B) * desc->H * p.split_p > device_cus()) p.split_p = 1;
         if (p.split_p > 1) {
-            const size_t xoff = need - osr::bwd_xchg_bytes(desc->B, desc->H, desc->d, bwd_parts(desc, chunk_size));
+            const size_t xoff = need - osr::bwd_small_xchg_bytes(desc->B, desc->H, desc->d, p.split_p);
             p.xbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + xoff);
-            p.xflags = reinterpret_cast<int*>(p.xbuf + static_cast<size_t>(desc->B) * desc->H * 2 * p.split_p * 8 *
-                                                           (desc->d + 4));
         }
         return osr::launch_bwd_small(desc->m, desc->d, p, in_bf16, st);
     }

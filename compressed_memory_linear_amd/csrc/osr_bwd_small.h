@@ -205,87 +205,84 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
         for (int i = 0; i < RPT; ++i) dR[i] = rsqrtf(n2[i]) * fma4(-pr[i], o[i], dR[i]);
     }
 
-    Pre pre;
-    issue(pre, NC - 1);
-    commit(pre, stg + ((NC - 1) & 1) * SG::SIZE);
-    float4 scur[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) scur[i] = pre.st[i];
-    __syncthreads();  // the last chunk's inputs visible
-    issue(pre, NC > 1 ? NC - 2 : 0);
-
-    for (int n = NC - 1; n >= 0; --n) {
-        const float* sb = stg + (n & 1) * SG::SIZE;
-        // the chunk-start state projected
+    // ---- one chunk's steps ----
+    // A chunk prepared for its reverse: the projected start state, c and |h|^2 of
+    // its tokens, beta, and the state before every token and after the last
+    // (h too at C <= 4; at C = 8 it is read from LDS where used: held, it spilled).
+    constexpr int HC = C > 4 ? 1 : C;
+    struct Prep {
         float inv[RPT];
         float4 z[RPT];
-        {
-            float n2[RPT];
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) n2[i] = group_sum<L::TPR>(dot4(scur[i], scur[i]));
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                inv[i] = rsqrtf(n2[i]);
-                z[i] = inv[i] * scur[i];
-            }
-        }
-        // c and |h|^2 of every token of the chunk
         float cc[C][RPT + 1];
         float beta[C][RPT];
         float4 rs[C + 1][RPT];
+        float4 h[HC];
+    };
+    auto stage_of = [&](int n) { return stg + (n & 1) * SG::SIZE; };
+    auto hat = [&](const Prep& x, const float* sb, int u) __attribute__((always_inline)) {
+        if constexpr (C > 4)
+            return *reinterpret_cast<const float4*>(sb + SG::H + u * D + cg * 4);
+        else
+            return x.h[u];
+    };
+    // c and |h|^2 of every token depend only on z and h: all C (RPT + 1) row sums
+    // together; then the forward again, elementwise
+    auto prep = [&](Prep& x, int n, const float4 (&s)[RPT]) __attribute__((always_inline)) {
+        const float* sb = stage_of(n);
+        float n2[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) n2[i] = group_sum<L::TPR>(dot4(s[i], s[i]));
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            x.inv[i] = rsqrtf(n2[i]);
+            x.z[i] = x.inv[i] * s[i];
+        }
         float4 h[C];
 #pragma unroll
         for (int u = 0; u < C; ++u) h[u] = *reinterpret_cast<const float4*>(sb + SG::H + u * D + cg * 4);
-        {
 #pragma unroll
         for (int u = 0; u < C; ++u) {
 #pragma unroll
-            for (int i = 0; i < RPT; ++i) cc[u][i] = dot4(z[i], h[u]);
-            cc[u][RPT] = dot4(h[u], h[u]);
+            for (int i = 0; i < RPT; ++i) x.cc[u][i] = dot4(x.z[i], h[u]);
+            x.cc[u][RPT] = dot4(h[u], h[u]);
         }
 #pragma unroll
         for (int u = 0; u < C; ++u)
 #pragma unroll
-            for (int i = 0; i <= RPT; ++i) cc[u][i] = group_sum<L::TPR>(cc[u][i]);
-        // the forward again, elementwise: beta, and the state before every token
-        // (rs[u]) and after the last (rs[C])
+            for (int i = 0; i <= RPT; ++i) x.cc[u][i] = group_sum<L::TPR>(x.cc[u][i]);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) rs[0][i] = z[i];
+        for (int i = 0; i < RPT; ++i) x.rs[0][i] = x.z[i];
 #pragma unroll
         for (int u = 0; u < C; ++u) {
-            const float mu = sb[SG::MU + u], hh = cc[u][RPT];
+            const float mu = sb[SG::MU + u], hh = x.cc[u][RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int row = rg + L::RG * i;
                 const float k = sb[SG::K + u * M + row];
                 const float g = sb[gps ? SG::G + u * M + row : SG::GT + u];
-                const float ci = cc[u][i];
+                const float ci = x.cc[u][i];
                 const float a = g * (enc ? ci - k : k);
                 const float w = fmaxf(fmaf(-ci, ci, hh), 0.f);
                 const float bt = rsqrtf(fmaf(mu, mu, a * a * w));
-                beta[u][i] = bt;
-                rs[u + 1][i] = fma4(bt * fmaf(a, ci, mu), rs[u][i], (-bt * a) * h[u]);
+                x.beta[u][i] = bt;
+                x.rs[u + 1][i] = fma4(bt * fmaf(a, ci, mu), x.rs[u][i], (-bt * a) * h[u]);
             }
         }
+        if constexpr (C <= 4) {
+#pragma unroll
+            for (int u = 0; u < C; ++u) x.h[u] = h[u];
         }
-        // At C = 8, h is read from LDS again below rather than held in registers
-        // across the reverse (that spilled); at C <= 4 it stays in registers.
-        if constexpr (C > 4) asm volatile("" ::: "memory");
-        auto hat = [&](int u) __attribute__((always_inline)) {
-            if constexpr (C > 4)
-                return *reinterpret_cast<const float4*>(sb + SG::H + u * D + cg * 4);
-            else
-                return h[u];
-        };
-
-        // ---- the chunk's tokens in reverse ----
-        float dcv[C][RPT], dkin[C][RPT];
+    };
+    // the chunk's tokens in reverse: dq, per-slot dgamma; per token the partial
+    // sums over the wave's slots (dh's terms, d|h|^2, dmu, per-token dgamma) to red
+    auto reverse = [&](const Prep& x, int n, float (&dcv)[C][RPT], float (&dkin)[C][RPT]) __attribute__((always_inline)) {
+        const float* sb = stage_of(n);
 #pragma unroll
         for (int u = C - 1; u >= 0; --u) {
             const int64_t bth = bth_of(n * C + u);
             const float4 dy = *reinterpret_cast<const float4*>(sb + SG::DY + u * D + cg * 4);
-            const float4 hu = hat(u);
-            const float mu = sb[SG::MU + u], hh = cc[u][RPT];
+            const float4 hu = hat(x, sb, u);
+            const float mu = sb[SG::MU + u], hh = x.cc[u][RPT];
             float qv[RPT], kv[RPT], gv[RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
@@ -297,9 +294,9 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
             float dq[RPT], dg[RPT], dk2[RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                dq[i] = dot4(rs[u + 1][i], dy);
+                dq[i] = dot4(x.rs[u + 1][i], dy);
                 dR[i] = fma4(qv[i], dy, dR[i]);
-                dg[i] = dot4(rs[u][i], dR[i]);
+                dg[i] = dot4(x.rs[u][i], dR[i]);
                 dk2[i] = dot4(hu, dR[i]);
             }
 #pragma unroll
@@ -315,7 +312,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
             float4 sc = f4(0.f);  // (d|h|^2, dmu, dgamma summed over slots, 0)
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
-                const float ci = cc[u][i], bt = beta[u][i];
+                const float ci = x.cc[u][i], bt = x.beta[u][i];
                 const float coef = enc ? ci - kv[i] : kv[i];
                 const float a = gv[i] * coef;
                 const float wraw = fmaf(-ci, ci, hh);
@@ -344,7 +341,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
                 }
                 dgam[i] = coef * da;
                 dcv[u][i] = dci;
-                hp = fma4(kap, dR[i], fma4(dci, z[i], hp));
+                hp = fma4(kap, dR[i], fma4(dci, x.z[i], hp));
                 sc.x += dhh_i;
                 sc.y += dmu_i;
                 sc.z += dgam[i];
@@ -369,72 +366,23 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
                 }
             }
         }
-        __syncthreads();  // the chunk's partial sums visible
-        // the sums over waves, one float4 of the chunk per thread
-        const bool mine = tid < C * (Q + 1);
-        const int xu = tid / (Q + 1), xc4 = tid % (Q + 1);
+    };
+    // the sums over waves, one float4 of the chunk per thread (mine)
+    const bool mine = tid < C * (Q + 1);
+    const int xu = tid / (Q + 1), xc4 = tid % (Q + 1);
+    auto wave_sums = [&]() __attribute__((always_inline)) {
         float4 acc = f4(0.f);
         if (mine) {
             acc = *reinterpret_cast<const float4*>(red + (xu * NW) * W + xc4 * 4);
 #pragma unroll
             for (int w = 1; w < NW; ++w) acc = acc + *reinterpret_cast<const float4*>(red + (xu * NW + w) * W + xc4 * 4);
         }
-        if constexpr (P > 1) {
-            // The other workgroup's sums of this chunk (over its rows): publish this
-            // one's, wait for the other's, add both in workgroup order.  Parts
-            // alternate between two buffers by chunk parity: a buffer is rewritten two
-            // chunks later, after the other workgroup has published the chunk in
-            // between, which it does only after reading this one.
-            constexpr int XW = 8 * W;  // floats per part (at most 8 tokens)
-            static_assert(C <= 8, "hand-off part size");
-            float* xb = p.xbuf + (static_cast<int64_t>(bh) * 2 + (nxch & 1)) * P * XW;
-            const __amdgpu_buffer_rsrc_t xr = xrsrc(xb, static_cast<uint32_t>(P * XW * sizeof(float)));
-            const uint32_t off = static_cast<uint32_t>(xu * W + xc4 * 4) * 4;
-            if (mine)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(bwd_u32x4, acc), xr,
-                                                       static_cast<uint32_t>(pidx * XW) * 4 + off, 0, XCPOL_SC1);
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's part store has retired
-            __syncthreads();  // ... and every thread's
-            if (tid == 0)
-                __hip_atomic_store(p.xflags + (bh * P + pidx) * XFLAG_STRIDE, nxch + 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            if (tid < P && tid != pidx && !xbroken) {
-                const int* fl = p.xflags + (bh * P + tid) * XFLAG_STRIDE;
-                int spins = 0;
-                while (__hip_atomic_load(const_cast<int*>(fl), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= nxch) {
-                    if (++spins >= XSPIN) {
-                        xbroken = true;
-                        break;
-                    }
-                }
-            }
-            __syncthreads();  // the other part is published
-            asm volatile("" ::: "memory");  // the reads below stay after the barrier
-            if (mine) {
-                float4 part[P];
-#pragma unroll
-                for (int q = 0; q < P; ++q)
-                    part[q] = q == pidx ? acc
-                                        : __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                         xr, static_cast<uint32_t>(q * XW) * 4 + off, 0,
-                                                                         XCPOL_SC1));
-                acc = part[0];
-#pragma unroll
-                for (int q = 1; q < P; ++q) acc = acc + part[q];
-            }
-            ++nxch;
-        }
-        if (mine) *reinterpret_cast<float4*>(tot + xu * W + xc4 * 4) = acc;
-        // the chunk before: its staged inputs and start state (loaded during this chunk)
-        if (n > 0) commit(pre, stg + ((n - 1) & 1) * SG::SIZE);
-        float4 snext[RPT];
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) snext[i] = pre.st[i];
-        __syncthreads();  // the sums over slots and the staged inputs visible
-        // (the last chunk loads chunk 0 again: unconditional, no load under a branch)
-        issue(pre, n > 1 ? n - 2 : 0);
-
-        // ---- gradients that take the sums over slots; the gradient of Z ----
+        return acc;
+    };
+    // gradients that take the sums over slots (tot); the gradient of Z back through
+    // the projection, which leaves dR the gradient of the chunk before's end state
+    auto finish = [&](const Prep& x, int n, const float (&dcv)[C][RPT], const float (&dkin)[C][RPT]) __attribute__((always_inline)) {
+        const float* sb = stage_of(n);
         float4 dZ[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) dZ[i] = f4(0.f);
@@ -443,7 +391,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
             const int64_t bth = bth_of(n * C + u);
             const float4 hsum = *reinterpret_cast<const float4*>(tot + u * W + cg * 4);
             const float4 ssum = *reinterpret_cast<const float4*>(tot + u * W + D);
-            const float4 hu = hat(u);
+            const float4 hu = hat(x, sb, u);
             const float4 dh = fma4(2.f * ssum.x, hu, hsum);
             float dkz[RPT] = {};
 #pragma unroll
@@ -451,7 +399,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
                 dZ[i] = fma4(dcv[u][i], hu, dZ[i]);
                 if constexpr (DEC) {
                     dZ[i] = fma4(sb[SG::K + u * M + rg + L::RG * i], dh, dZ[i]);
-                    dkz[i] = dot4(z[i], dh);
+                    dkz[i] = dot4(x.z[i], dh);
                 }
             }
             if constexpr (DEC) {
@@ -469,13 +417,132 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
             }
             if (rg == 0) *reinterpret_cast<float4*>(p.dv + bth * D + cg * 4) = enc ? dh : f4(0.f) - dh;
         }
-        // the gradient of Z (running path and the chunk's uses of z) back through the projection
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             const float4 dz = dR[i] + dZ[i];
-            const float pz = group_sum<L::TPR>(dot4(z[i], dz));
-            dR[i] = inv[i] * fma4(-pz, z[i], dz);
-            scur[i] = snext[i];
+            const float pz = group_sum<L::TPR>(dot4(x.z[i], dz));
+            dR[i] = x.inv[i] * fma4(-pz, x.z[i], dz);
+        }
+    };
+
+    Pre pre;
+    issue(pre, NC - 1);
+    commit(pre, stage_of(NC - 1));
+    float4 scur[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) scur[i] = pre.st[i];
+    __syncthreads();  // the last chunk's inputs visible
+    issue(pre, NC > 1 ? NC - 2 : 0);
+
+    // Split rows (P > 1): the chunk's sums over slots need the other workgroup's
+    // part.  Each value goes with the chunk's tag (nxch + 1) as one 64-bit pair,
+    // written and read with agent-scope atomics, so a pair is seen whole or not at
+    // all: publish writes this workgroup's pairs, await_part polls the other's own
+    // pairs until all carry the tag (no store-retire wait, barrier or counter on
+    // the way) and adds the parts in workgroup order, so both hold the same sums.
+    // Parts alternate between two buffers by chunk parity: a buffer is rewritten
+    // two chunks later, after the other workgroup has published the chunk in
+    // between, which it does only after reading this one.  The buffers are zeroed
+    // before each call (tags start at 1).
+    constexpr int XW = 8 * W;  // pairs per part (at most 8 tokens)
+    static_assert(P == 1 || C <= 8, "hand-off part size");
+    auto xpart = [&](int q) __attribute__((always_inline)) {
+        return reinterpret_cast<uint64_t*>(p.xbuf) + ((static_cast<int64_t>(bh) * 2 + (nxch & 1)) * P + q) * XW +
+               xu * W + xc4 * 4;
+    };
+    auto publish = [&](float4 acc) __attribute__((always_inline)) {
+        if (mine) {
+            uint64_t* dst = xpart(pidx);
+            const uint64_t tag = static_cast<uint64_t>(nxch + 1) << 32;
+            __hip_atomic_store(dst + 0, tag | __float_as_uint(acc.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(dst + 1, tag | __float_as_uint(acc.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(dst + 2, tag | __float_as_uint(acc.z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(dst + 3, tag | __float_as_uint(acc.w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+    auto await_part = [&](float4 acc) __attribute__((always_inline)) {
+        if (mine) {
+            const uint32_t tag = static_cast<uint32_t>(nxch + 1);
+            float4 part[P];
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                if (q == pidx) {
+                    part[q] = acc;
+                    continue;
+                }
+                uint64_t* src = xpart(q);
+                uint64_t v0 = 0, v1 = 0, v2 = 0, v3 = 0;
+                for (int spins = 0; spins < XSPIN && !xbroken; ++spins) {
+                    v0 = __hip_atomic_load(src + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    v1 = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    v2 = __hip_atomic_load(src + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    v3 = __hip_atomic_load(src + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (static_cast<uint32_t>(v0 >> 32) == tag && static_cast<uint32_t>(v1 >> 32) == tag &&
+                        static_cast<uint32_t>(v2 >> 32) == tag && static_cast<uint32_t>(v3 >> 32) == tag)
+                        break;
+                    if (spins + 1 == XSPIN) xbroken = true;
+                }
+                part[q] = make_float4(__uint_as_float(static_cast<uint32_t>(v0)), __uint_as_float(static_cast<uint32_t>(v1)),
+                                      __uint_as_float(static_cast<uint32_t>(v2)), __uint_as_float(static_cast<uint32_t>(v3)));
+            }
+            acc = part[0];
+#pragma unroll
+            for (int q = 1; q < P; ++q) acc = acc + part[q];
+        }
+        ++nxch;
+        return acc;
+    };
+
+    // At C <= 4 with split rows, each chunk publishes its part, then prepares the
+    // chunk before (which needs no gradient) while the other's part is on its way,
+    // and only then waits for it (two prepared chunks live: at C = 8 that spilled).
+    constexpr bool PIPE = P > 1 && C <= 4;
+    if constexpr (!PIPE) {
+        // Per chunk: prepare, reverse, barrier, sums over waves (over both
+        // workgroups' rows where split) and the staged inputs of the chunk before,
+        // barrier, the rest.
+        for (int n = NC - 1; n >= 0; --n) {
+            Prep x;
+            prep(x, n, scur);
+            float dcv[C][RPT], dkin[C][RPT];
+            reverse(x, n, dcv, dkin);
+            __syncthreads();  // the chunk's partial sums visible
+            float4 acc = wave_sums();
+            if constexpr (P > 1) {
+                publish(acc);
+                acc = await_part(acc);
+            }
+            if (mine) *reinterpret_cast<float4*>(tot + xu * W + xc4 * 4) = acc;
+            // the chunk before: its staged inputs and start state (loaded during this chunk)
+            if (n > 0) commit(pre, stage_of(n - 1));
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) scur[i] = pre.st[i];
+            __syncthreads();  // the sums over slots and the staged inputs visible
+            // (the last chunk loads chunk 0 again: unconditional, no load under a branch)
+            issue(pre, n > 1 ? n - 2 : 0);
+            finish(x, n, dcv, dkin);
+        }
+    } else {
+        Prep x;
+        prep(x, NC - 1, scur);
+        for (int n = NC - 1; n >= 0; --n) {
+            float dcv[C][RPT], dkin[C][RPT];
+            reverse(x, n, dcv, dkin);
+            __syncthreads();  // the chunk's partial sums visible
+            float4 acc = wave_sums();
+            publish(acc);
+            if (n > 0) commit(pre, stage_of(n - 1));
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) scur[i] = pre.st[i];
+            __syncthreads();  // the staged inputs of the chunk before visible
+            issue(pre, n > 1 ? n - 2 : 0);
+            Prep xn;
+            if (n > 0) prep(xn, n - 1, scur);
+            acc = await_part(acc);
+            if (mine) *reinterpret_cast<float4*>(tot + xu * W + xc4 * 4) = acc;
+            __syncthreads();  // the sums over slots visible
+            finish(x, n, dcv, dkin);
+            if (n > 0) x = xn;
         }
     }
 
@@ -489,9 +556,10 @@ static void launch_bwd_small_dec(const BwdParams& p, hipStream_t st) {
     constexpr int NT = bwd_small_threads<M, D, P>();
     const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H) * P);
     if constexpr (P > 1) {
-        // progress counters to zero (they count the chunks of this call)
-        const int nflags = p.f.B * p.f.H * P * XFLAG_STRIDE;
-        hipLaunchKernelGGL(osr_bwd_fill_ints<0>, dim3((nflags + 255) / 256), dim3(256), 0, st, p.xflags, nflags);
+        // the tagged hand-off pairs to zero (tags count the chunks of this call from 1)
+        const int nints = static_cast<int>(bwd_small_xchg_bytes(p.f.B, p.f.H, D, P) / sizeof(int));
+        hipLaunchKernelGGL(osr_bwd_fill_ints<0>, dim3((nints + 255) / 256), dim3(256), 0, st,
+                           reinterpret_cast<int*>(p.xbuf), nints);
     }
     if (p.f.mode == 0)
         hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, true, P>), grid, dim3(NT), 0, st, p);
@@ -515,8 +583,8 @@ static void launch_bwd_small_p(const BwdParams& p, bool in_bf16, hipStream_t st)
 }
 
 // P (p.split_p) = 2: the rows of a sequence over two workgroups, with the
-// hand-off buffers p.xbuf / p.xflags (the host ensures B*H*2 workgroups are
-// resident at once).
+// hand-off buffers at p.xbuf (bwd_small_xchg_bytes; the host ensures B*H*2
+// workgroups are resident at once).
 template <int M, int D, int C>
 static int launch_bwd_small_mdc(const BwdParams& p, bool in_bf16, hipStream_t st) {
     if constexpr (!bwd_small_fits<M, D>(C)) {
@@ -524,7 +592,7 @@ static int launch_bwd_small_mdc(const BwdParams& p, bool in_bf16, hipStream_t st
     } else {
         if (p.split_p == 2) {
             if constexpr (M / 2 >= 16) {
-                if (p.xbuf == nullptr || p.xflags == nullptr) return -3;
+                if (p.xbuf == nullptr) return -3;
                 launch_bwd_small_p<M, D, C, 2>(p, in_bf16, st);
             } else {
                 return -3;

@@ -306,8 +306,8 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * workspace, 4 T d bytes per (b,h).  There, with desc->chain_wgs =
  * LATTICE_OSR_WGS_AUTO, chunk_size >= 4, m >= 32 and B*H*2 <= 256, the slot rows of each
  * sequence are split over 2 workgroups that exchange each chunk's sums over
- * slots through hand-off buffers at the end of the workspace (the same size
- * as above with P = 2); one workgroup on devices with fewer than B*H*2
+ * slots through hand-off buffers at the end of the workspace, B*H*256 (d + 4)
+ * bytes (value and tag pairs); one workgroup on devices with fewer than B*H*2
  * compute units, or with LATTICE_OSR_WGS_ONE.  The result equals the
  * general walk's up to fp32 rounding.  The remaining rules (shapes,
  * chunk sizes, alignment of the inputs, status codes, asynchrony) are those

@@ -408,8 +408,8 @@ def test_bwd_small_chunk_form_workspace():
     for C, m, d in applies:
         kw = dict(B=2, T=64, H=3, m=m, d=d)
         # from m = 32 and C = 4 the rows of a sequence split over 2 workgroups (B*H*2 <= 256):
-        # their hand-off buffers, 2 parities x 2 parts x 8 tokens x (d + 4) floats and 2 counters
-        xchg = 2 * 3 * (2 * 2 * 8 * (d + 4) * 4 + 2 * 128) if m >= 32 and C >= 4 else 0
+        # their hand-off buffers, 2 parities x 2 parts x 8 tokens x (d + 4) (value, tag) pairs
+        xchg = 2 * 3 * (2 * 2 * 8 * (d + 4) * 8) if m >= 32 and C >= 4 else 0
         one = dict(kw, chain_wgs=osr.WGS_ONE)
         assert ws(C, **kw) - ws(C, osr.BWD_WALK, **kw) == 2 * 3 * 64 * d * 4 + xchg, (C, m, d)
         assert ws(C, **one) - ws(C, osr.BWD_WALK, **one) == 2 * 3 * 64 * d * 4, (C, m, d)
