@@ -229,7 +229,7 @@ size_t bwd_small_h_bytes(const lattice_osr_desc* d, int C) {
 // Workgroups per sequence that the workspace provides hand-off buffers for (the
 // launch may use fewer where the device has fewer compute units).
 int bwd_parts(const lattice_osr_desc* d, int C) {
-    if (bwd_small_form(d, C)) return osr::bwd_small_split_p(d->B, d->H, d->m, C, d->chain_wgs);
+    if (bwd_small_form(d, C)) return osr::bwd_small_split_p(d->B, d->H, d->m, d->d, C, d->chain_wgs);
     return osr::bwd_split_p(d->B, d->H, d->m, d->d, C, bwd_uses_chain(d, C), d->chain_wgs);
 }
 
@@ -508,11 +508,12 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
         rc = osr::launch_valu(false, desc->m, desc->d, pf, in_bf16, st);
         if (rc) return rc;
         p.f.hrec = pf.hrec;
-        // the rows of a sequence over two workgroups where all of them can be resident
+        // the rows of a sequence over P workgroups where all of them can be resident (a
+        // smaller P fits in the buffers sized for the policy's)
         p.split_p = bwd_parts(desc, chunk_size);
         p.xbuf = nullptr;
         p.xflags = nullptr;
-        if (p.split_p > 1 && static_cast<int64_t>(desc->B) * desc->H * p.split_p > device_cus()) p.split_p = 1;
+        while (p.split_p > 1 && static_cast<int64_t>(desc->B) * desc->H * p.split_p > device_cus()) p.split_p /= 2;
         if (p.split_p > 1) {
             const size_t xoff = need - osr::bwd_small_xchg_bytes(desc->B, desc->H, desc->d, p.split_p);
             p.xbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + xoff);

@@ -57,6 +57,14 @@ constexpr int bwd_small_threads() {
     return tokenloop_threads<M / P, D>();
 }
 
+// Whether P workgroups of M / P rows (16 or more) each have the threads to stage
+// a chunk's inputs and hold its sums, one unit of each kind per thread.
+template <int M, int D, int C, int P>
+constexpr bool bwd_small_split_ok() {
+    constexpr int NT = bwd_small_threads<M, D, P>();
+    return M / P >= 16 && C * (M / 4) <= NT && C * (D / 4 + 1) <= NT;
+}
+
 // Four consecutive elements loaded without conversion (the conversion, and so
 // the wait for the load, happens where the value is used).
 template <typename T>
@@ -103,7 +111,7 @@ struct SmallStage {
 // otherwise h = -v (similarity) or v (encoding layer).  DYB: dy in bf16.
 template <int M, int D, int NT, int C, typename TIn, bool DYB, bool DEC, int P>
 __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
-    static_assert(P == 1 || (P == 2 && M / P >= 16), "split: two workgroups of 16 rows or more");
+    static_assert(P == 1 || ((P == 2 || P == 4) && M / P >= 16), "split: 2 or 4 workgroups of 16 rows or more");
     using L = ValuLayout<M / P, D, NT>;
     using SG = SmallStage<M, D, C>;
     using DYT = typename std::conditional<DYB, uint16_t, float>::type;
@@ -582,8 +590,8 @@ static void launch_bwd_small_p(const BwdParams& p, bool in_bf16, hipStream_t st)
     }
 }
 
-// P (p.split_p) = 2: the rows of a sequence over two workgroups, with the
-// hand-off buffers at p.xbuf (bwd_small_xchg_bytes; the host ensures B*H*2
+// P (p.split_p) = 2 or 4: the rows of a sequence over P workgroups, with the
+// hand-off buffers at p.xbuf (bwd_small_xchg_bytes; the host ensures B*H*P
 // workgroups are resident at once).
 template <int M, int D, int C>
 static int launch_bwd_small_mdc(const BwdParams& p, bool in_bf16, hipStream_t st) {
@@ -591,9 +599,16 @@ static int launch_bwd_small_mdc(const BwdParams& p, bool in_bf16, hipStream_t st
         return -3;
     } else {
         if (p.split_p == 2) {
-            if constexpr (M / 2 >= 16) {
+            if constexpr (bwd_small_split_ok<M, D, C, 2>()) {
                 if (p.xbuf == nullptr) return -3;
                 launch_bwd_small_p<M, D, C, 2>(p, in_bf16, st);
+            } else {
+                return -3;
+            }
+        } else if (p.split_p == 4) {
+            if constexpr (bwd_small_split_ok<M, D, C, 4>()) {
+                if (p.xbuf == nullptr) return -3;
+                launch_bwd_small_p<M, D, C, 4>(p, in_bf16, st);
             } else {
                 return -3;
             }
@@ -624,6 +639,31 @@ int launch_bwd_small_m(int d, const BwdParams& p, bool in_bf16, hipStream_t st) 
         case 64: return launch_bwd_small_md<M, 64>(p, in_bf16, st);
         case 128: return launch_bwd_small_md<M, 128>(p, in_bf16, st);
         default: return -3;
+    }
+}
+
+template <int M, int D>
+bool bwd_small_split_ok_md(int C, int P) {
+    auto ok = [&](auto c) {
+        constexpr int CV = decltype(c)::value;
+        return P == 1 || (P == 2 && bwd_small_split_ok<M, D, CV, 2>()) || (P == 4 && bwd_small_split_ok<M, D, CV, 4>());
+    };
+    switch (C) {
+        case 2: return ok(std::integral_constant<int, 2>{});
+        case 4: return ok(std::integral_constant<int, 4>{});
+        case 8: return ok(std::integral_constant<int, 8>{});
+        default: return false;
+    }
+}
+
+template <int M>
+bool bwd_small_split_ok_m(int d, int C, int P) {
+    switch (d) {
+        case 16: return bwd_small_split_ok_md<M, 16>(C, P);
+        case 32: return bwd_small_split_ok_md<M, 32>(C, P);
+        case 64: return bwd_small_split_ok_md<M, 64>(C, P);
+        case 128: return bwd_small_split_ok_md<M, 128>(C, P);
+        default: return false;
     }
 }
 

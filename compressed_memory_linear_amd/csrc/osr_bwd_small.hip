@@ -22,17 +22,31 @@ bool bwd_small_supported(int m, int d, int C, bool lin1) {
     }
 }
 
-// Workgroups per sequence of the small-chunk walk: 2 (half the slot rows each,
-// half the VALU issue per chunk, one hand-off per chunk) where each keeps at
-// least 16 rows, the chunk has at least 4 tokens and B*H*2 <= 256 (one
-// workgroup per compute unit, all resident: they wait for each other);
-// chain_wgs != 0 asks for one.  The hand-off (stores retired, counter, poll,
-// loads) costs ~6.5k cycles per chunk: B4 H8 T2048 m = d = 64 measured 5.87
-// against 5.40 ms at C = 2, 4.39 against 4.57 at C = 4, 3.69 against 4.19 at
-// C = 8.
-int bwd_small_split_p(int B, int H, int m, int C, int chain_wgs) {
-    if (chain_wgs != 0 || m / 2 < 16 || C < 4) return 1;
-    return static_cast<int64_t>(B) * H * 2 <= 256 ? 2 : 1;
+static bool split_ok(int m, int d, int C, int P) {
+    switch (m) {
+        case 16: return bwd_small_split_ok_m<16>(d, C, P);
+        case 32: return bwd_small_split_ok_m<32>(d, C, P);
+        case 64: return bwd_small_split_ok_m<64>(d, C, P);
+        case 128: return bwd_small_split_ok_m<128>(d, C, P);
+        default: return false;
+    }
+}
+
+// Workgroups per sequence of the small-chunk walk (the slot rows split between
+// them: fewer instructions per chunk each, one hand-off per chunk), where each
+// keeps at least 16 rows and the threads to stage a chunk, and B*H*P <= 256 (one
+// workgroup per compute unit, all resident: they wait for each other):
+// 4 at C = 8, 2 at C = 4 (or at C = 8 where 4 do not fit), 1 at C = 2;
+// chain_wgs != 0 asks for one.  The hand-off (~2 us per chunk) against the
+// halved compute, B4 H8 T2048 m = d = 64 (ms, P = 1 / 2 / 4): C = 2 5.27 /
+// 5.87 (an earlier form of the hand-off) / -, C = 4 4.61 / 4.17 / 4.15, C = 8
+// 4.31 / 3.56 / 3.35.
+int bwd_small_split_p(int B, int H, int m, int d, int C, int chain_wgs) {
+    if (chain_wgs != 0 || C < 4) return 1;
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    if (C >= 8 && bh * 4 <= 256 && split_ok(m, d, C, 4)) return 4;
+    if (bh * 2 <= 256 && split_ok(m, d, C, 2)) return 2;
+    return 1;
 }
 
 int launch_bwd_small(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st) {

@@ -85,7 +85,7 @@ int launch_bwd_chunk(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t
 // Its phase 1 is the forward's small-chunk token loop with raw (and, decoding
 // objective, hrec) set; f.hrec then points at those records.  Same workspace
 // layout as launch_bwd, plus hrec.
-// split_p = 2 splits a sequence's slot rows over two workgroups, with their
+// split_p = 2 or 4 splits a sequence's slot rows over that many workgroups, with their
 // hand-off buffers at xbuf: per (b,h), 2 chunk parities x P parts x 8 tokens x
 // (d + 4) (value, tag) pairs of 8 bytes.
 inline size_t bwd_small_xchg_bytes(int B, int H, int d, int P) {
@@ -93,7 +93,7 @@ inline size_t bwd_small_xchg_bytes(int B, int H, int d, int P) {
     return static_cast<size_t>(B) * H * 2 * P * 8 * (d + 4) * sizeof(uint64_t);
 }
 bool bwd_small_supported(int m, int d, int C, bool lin1);
-int bwd_small_split_p(int B, int H, int m, int C, int chain_wgs);
+int bwd_small_split_p(int B, int H, int m, int d, int C, int chain_wgs);
 int launch_bwd_small(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 
 // Layer glue (HBM-bound streaming kernels).  pre: q = conv4(xq), k = conv4(xk)

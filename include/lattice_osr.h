@@ -304,12 +304,14 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * chunk's states in registers runs after a forward pass that stores the
  * chunk-start states; the decoding objective adds every token's h to the
  * workspace, 4 T d bytes per (b,h).  There, with desc->chain_wgs =
- * LATTICE_OSR_WGS_AUTO, chunk_size >= 4, m >= 32 and B*H*2 <= 256, the slot rows of each
- * sequence are split over 2 workgroups that exchange each chunk's sums over
- * slots through hand-off buffers at the end of the workspace, B*H*256 (d + 4)
- * bytes (value and tag pairs); one workgroup on devices with fewer than B*H*2
- * compute units, or with LATTICE_OSR_WGS_ONE.  The result equals the
- * general walk's up to fp32 rounding.  The remaining rules (shapes,
+ * LATTICE_OSR_WGS_AUTO, chunk_size >= 4, m >= 32 and B*H*P <= 256, the
+ * slot rows of each sequence are split over P workgroups (4 at chunk_size 8
+ * where a quarter of the rows has the threads to stage a chunk, else 2)
+ * that exchange each chunk's sums over slots through hand-off buffers at the
+ * end of the workspace, B*H*128 P (d + 4) bytes (value and tag pairs); fewer
+ * on devices with fewer than B*H*P compute units, one with
+ * LATTICE_OSR_WGS_ONE.  The result equals the general walk's up to fp32
+ * rounding.  The remaining rules (shapes,
  * chunk sizes, alignment of the inputs, status codes, asynchrony) are those
  * of lattice_osr_fwd_chunked.
  */

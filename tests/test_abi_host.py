@@ -407,9 +407,13 @@ def test_bwd_small_chunk_form_workspace():
     applies = [(2, 16, 16), (4, 64, 64), (8, 64, 64), (4, 32, 128), (8, 128, 16), (2, 128, 32)]
     for C, m, d in applies:
         kw = dict(B=2, T=64, H=3, m=m, d=d)
-        # from m = 32 and C = 4 the rows of a sequence split over 2 workgroups (B*H*2 <= 256):
-        # their hand-off buffers, 2 parities x 2 parts x 8 tokens x (d + 4) (value, tag) pairs
-        xchg = 2 * 3 * (2 * 2 * 8 * (d + 4) * 8) if m >= 32 and C >= 4 else 0
+        # from m = 32 and C = 4 the rows of a sequence split over P workgroups (B*H*P <= 256):
+        # 4 at C = 8 where each keeps 16 rows and the threads to stage a chunk (m = d = 64
+        # here; not m128 d16, where a quarter of the rows has 128 threads for 256 staged
+        # units), else 2; their hand-off buffers, 2 parities x P parts x 8 tokens x (d + 4)
+        # (value, tag) pairs
+        P = 1 if m < 32 or C < 4 else (4 if (C, m, d) == (8, 64, 64) else 2)
+        xchg = 2 * 3 * (2 * P * 8 * (d + 4) * 8) if P > 1 else 0
         one = dict(kw, chain_wgs=osr.WGS_ONE)
         assert ws(C, **kw) - ws(C, osr.BWD_WALK, **kw) == 2 * 3 * 64 * d * 4 + xchg, (C, m, d)
         assert ws(C, **one) - ws(C, osr.BWD_WALK, **one) == 2 * 3 * 64 * d * 4, (C, m, d)

@@ -127,11 +127,14 @@ def test_small_chunk_backward(B, T, H, m, d, C, dt, per_slot, mode, dyb):
 
 
 # (B, T, H, m, d, C, objective): from m = 32 and C = 4 the automatic choice splits
-# the slot rows of each sequence over two workgroups that exchange each chunk's sums
+# the slot rows of each sequence over two workgroups (four at C = 8 where a
+# quarter of the rows can stage a chunk: m64 d64 and m128 d32 here) that exchange
+# each chunk's sums
 @pytest.mark.parametrize("B,T,H,m,d,C,mode", [(2, 128, 3, 64, 64, 4, osr.MODE_DEC), (1, 64, 2, 32, 128, 4, osr.MODE_DEC),
-                                              (2, 64, 2, 128, 16, 8, osr.MODE_SIM), (1, 96, 4, 32, 32, 8, osr.MODE_DEC)])
+                                              (2, 64, 2, 128, 16, 8, osr.MODE_SIM), (1, 96, 4, 32, 32, 8, osr.MODE_DEC),
+                                              (1, 64, 4, 64, 64, 8, osr.MODE_DEC), (2, 16, 2, 128, 32, 8, osr.MODE_ENC)])
 def test_small_chunk_backward_split_vs_one(B, T, H, m, d, C, mode):
-    """The split over two workgroups against one workgroup per sequence
+    """The split over workgroups against one workgroup per sequence
     (LATTICE_OSR_WGS_ONE): the same gradient up to the order of the fp32
     sums over slots (1e-4 of RMS), bit-identical on a rerun."""
     _say(f"bwd small-chunk split vs one B{B} T{T} H{H} m{m} d{d} C{C} mode{mode}")
