@@ -148,6 +148,23 @@ def test_small_chunk_backward_split_vs_one(B, T, H, m, d, C, mode):
         assert np.array_equal(split[key], again[key]), key
 
 
+# The policy's other branches: B*H = 160 (B*H*2 > 256: one workgroup per sequence)
+# at C = 4, and B*H = 100 at C = 8 (B*H*4 > 256: two workgroups, not four)
+@pytest.mark.parametrize("B,H,C", [(4, 40, 4), (4, 25, 8)])
+def test_small_chunk_backward_many_sequences(B, H, C):
+    _say(f"bwd small-chunk many sequences B{B} T32 H{H} m64 d64 C{C} bf16")
+    inp = synth.make_inputs(B, 32, H, 64, 64, seed=43, in_dtype=synth.BF16)
+    dy, dso = _upstream(inp, 43)
+    got = _gpu_bwd(inp, dy, dso, C, osr.MODE_DEC, osr.BWD_AUTO)
+    walk = _gpu_bwd(inp, dy, dso, C, osr.MODE_DEC, osr.BWD_WALK)
+    _report_and_check("vs general walk", _errs(got, walk), AGREE)
+    bh = [(0, 0), (B - 1, H - 1)]
+    refs = [_oracle_seq(inp, dy, dso, C, osr.MODE_DEC, b, h) for b, h in bh]
+    errs = {key: max(_rel(_pick(key, got[key], b, h), _pick(key, r[key], 0, 0)) for (b, h), r in zip(bh, refs))
+            for key in KEYS}
+    _report_and_check("vs oracle (2 sequences)", errs, TOL[synth.BF16])
+
+
 def test_small_chunk_backward_deterministic():
     _say("bwd small-chunk determinism B2 T128 H2 m64 d64 C4 bf16")
     inp = synth.make_inputs(2, 128, 2, 64, 64, seed=37, in_dtype=synth.BF16)
