@@ -246,6 +246,22 @@ size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
     return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, bwd_parts(d, C));
 }
 
+// Parameters of the small-chunk backward's phase 1 (the forward's small-chunk
+// token loop): every chunk-start state before projection, and the end state,
+// into the backward's workspace layout and, decoding objective, every token's
+// h after the backward's part; y and state_out as given (null: not written).
+osr::Params small_phase1_params(const lattice_osr_desc* desc, int C, const void* q, const void* k, const void* v,
+                                const void* gamma, const void* mu, const float* state_in, float* state_out,
+                                void* y, void* workspace) {
+    const size_t bwd_bytes = osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, C);
+    osr::Params pf = make_params(desc, C, q, k, v, gamma, mu, state_in, state_out, y, nullptr);
+    pf.raw = static_cast<float*>(workspace);
+    pf.raw_stride = static_cast<int64_t>(bwd_bytes / sizeof(float)) / (static_cast<int64_t>(desc->B) * desc->H);
+    pf.hrec = bwd_small_h_bytes(desc, C) ? reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_bytes)
+                                         : nullptr;
+    return pf;
+}
+
 // The chunk-parallel backward where it is built and not turned off.
 bool bwd_chunk_form(const lattice_osr_desc* d, int C) {
     return d->bwd_form != LATTICE_OSR_BWD_WALK && bwd_uses_chain(d, C) &&
@@ -430,13 +446,19 @@ size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* desc, int32_t chu
     return bwd_workspace_needed(desc, chunk_size);
 }
 
-int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, const void* q, const void* k,
-                            const void* v, const void* gamma, const void* mu, const float* state_in,
-                            const void* dy, const float* dstate_out, float* dq, float* dk, float* dv,
-                            float* dgamma, float* dmu, float* dstate_in, void* workspace,
-                            size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// saved: the workspace already holds what lattice_osr_fwd_chunked_save stored
+// (small-chunk form only): the forward pass of phase 1 is skipped.
+int bwd_chunked_impl(const lattice_osr_desc* desc, int32_t chunk_size, const void* q, const void* k, const void* v,
+                     const void* gamma, const void* mu, const float* state_in, const void* dy,
+                     const float* dstate_out, float* dq, float* dk, float* dv, float* dgamma, float* dmu,
+                     float* dstate_in, void* workspace, size_t workspace_bytes, void* hip_stream, bool saved) {
     int rc = check_bwd_desc(desc, chunk_size);
     if (rc) return rc;
+    if (saved && !bwd_small_form(desc, chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
     const size_t need = bwd_workspace_needed(desc, chunk_size);
     rc = check_bwd_buffers(desc, q, k, v, gamma, mu, state_in, dy, dstate_out, dq, dk, dv, dgamma, dmu,
                            dstate_in, workspace, workspace_bytes, need);
@@ -499,14 +521,13 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
     if (bwd_small_form(desc, chunk_size)) {
         // phase 1: the forward's small-chunk token loop, keeping every chunk-start state
         // (before projection) in the backward's layout and, decoding objective, every h
-        const size_t bwd_bytes = osr::bwd_workspace_bytes(desc->B, desc->H, desc->T, desc->m, desc->d, chunk_size);
-        osr::Params pf = make_params(desc, chunk_size, q, k, v, gamma, mu, state_in, nullptr, nullptr, nullptr);
-        pf.raw = static_cast<float*>(workspace);
-        pf.raw_stride = static_cast<int64_t>(bwd_bytes / sizeof(float)) / (static_cast<int64_t>(desc->B) * desc->H);
-        pf.hrec = bwd_small_h_bytes(desc, chunk_size)
-                      ? reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_bytes) : nullptr;
-        rc = osr::launch_valu(false, desc->m, desc->d, pf, in_bf16, st);
-        if (rc) return rc;
+        // (unless lattice_osr_fwd_chunked_save stored them there already)
+        const osr::Params pf =
+            small_phase1_params(desc, chunk_size, q, k, v, gamma, mu, state_in, nullptr, nullptr, workspace);
+        if (!saved) {
+            rc = osr::launch_valu(false, desc->m, desc->d, pf, in_bf16, st);
+            if (rc) return rc;
+        }
         p.f.hrec = pf.hrec;
         // the rows of a sequence over P workgroups where all of them can be resident (a
         // smaller P fits in the buffers sized for the policy's)
@@ -538,6 +559,44 @@ int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, co
         }
     }
     return osr::launch_bwd(desc->m, desc->d, p, in_bf16, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size, const void* q, const void* k,
+                            const void* v, const void* gamma, const void* mu, const float* state_in,
+                            const void* dy, const float* dstate_out, float* dq, float* dk, float* dv,
+                            float* dgamma, float* dmu, float* dstate_in, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+    return bwd_chunked_impl(desc, chunk_size, q, k, v, gamma, mu, state_in, dy, dstate_out, dq, dk, dv, dgamma, dmu,
+                            dstate_in, workspace, workspace_bytes, hip_stream, false);
+}
+
+int lattice_osr_bwd_chunked_saved(const lattice_osr_desc* desc, int32_t chunk_size, const void* q, const void* k,
+                                  const void* v, const void* gamma, const void* mu, const float* state_in,
+                                  const void* dy, const float* dstate_out, float* dq, float* dk, float* dv,
+                                  float* dgamma, float* dmu, float* dstate_in, void* workspace,
+                                  size_t workspace_bytes, void* hip_stream) {
+    return bwd_chunked_impl(desc, chunk_size, q, k, v, gamma, mu, state_in, dy, dstate_out, dq, dk, dv, dgamma, dmu,
+                            dstate_in, workspace, workspace_bytes, hip_stream, true);
+}
+
+int lattice_osr_fwd_chunked_save(const lattice_osr_desc* desc, int32_t chunk_size, const void* q, const void* k,
+                                 const void* v, const void* gamma, const void* mu, const float* state_in,
+                                 float* state_out, void* y, void* bwd_workspace, size_t bwd_workspace_bytes,
+                                 void* hip_stream) {
+    int rc = check_bwd_desc(desc, chunk_size);
+    if (rc) return rc;
+    if (!bwd_small_form(desc, chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    const size_t need = bwd_workspace_needed(desc, chunk_size);
+    rc = check_buffers(desc, q, k, v, gamma, mu, state_in, state_out, y, bwd_workspace, bwd_workspace_bytes, need);
+    if (rc) return rc;
+    const osr::Params pf =
+        small_phase1_params(desc, chunk_size, q, k, v, gamma, mu, state_in, state_out, y, bwd_workspace);
+    return osr::launch_valu(false, desc->m, desc->d, pf, desc->in_dtype == LATTICE_OSR_BF16,
+                            static_cast<hipStream_t>(hip_stream));
 }
 
 }  // extern "C"

@@ -32,7 +32,8 @@ ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH, ERR_ALIAS, ERR_
 EXPORTED = ("lattice_osr_fwd_chunked", "lattice_osr_fwd_recurrent", "lattice_osr_decode_step",
             "lattice_osr_workspace_bytes", "lattice_osr_status_string", "lattice_osr_abi_version",
             "lattice_osr_bwd_chunked", "lattice_osr_bwd_workspace_bytes", "lattice_osr_glue_pre",
-            "lattice_osr_glue_post", "lattice_osr_fwd_chunked_gated", "lattice_osr_fwd_chunked_noalloc")
+            "lattice_osr_glue_post", "lattice_osr_fwd_chunked_gated", "lattice_osr_fwd_chunked_noalloc",
+            "lattice_osr_fwd_chunked_save", "lattice_osr_bwd_chunked_saved")
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -72,6 +73,10 @@ def load_library():
             getattr(lib, f).restype = ctypes.c_int
         lib.lattice_osr_bwd_chunked.argtypes = [dp, ctypes.c_int32] + [vp] * 15 + [ctypes.c_size_t, vp]
         lib.lattice_osr_bwd_chunked.restype = ctypes.c_int
+        lib.lattice_osr_bwd_chunked_saved.argtypes = [dp, ctypes.c_int32] + [vp] * 15 + [ctypes.c_size_t, vp]
+        lib.lattice_osr_bwd_chunked_saved.restype = ctypes.c_int
+        lib.lattice_osr_fwd_chunked_save.argtypes = [dp, ctypes.c_int32] + fwd[1:]
+        lib.lattice_osr_fwd_chunked_save.restype = ctypes.c_int
         lib.lattice_osr_bwd_workspace_bytes.argtypes = [dp, ctypes.c_int32]
         lib.lattice_osr_bwd_workspace_bytes.restype = ctypes.c_size_t
         lib.lattice_osr_workspace_bytes.argtypes = [dp, ctypes.c_int32]
@@ -338,6 +343,48 @@ def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_
     sequence of the token walk on one workgroup (speed only); bwd_form:
     BWD_WALK / BWD_CHUNK pick the backward's form (BWD_AUTO: the chunk form
     where it is built)."""
+    return _bwd("lattice_osr_bwd_chunked", q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size, mode, grads,
+                workspace, stream, linearisation, chain_wgs, bwd_form)
+
+
+def lattice_osr_fwd_chunked_save(q, k, v, gamma, mu, state_in, chunk_size: int, *, mode: int = MODE_DEC,
+                                 y_dtype=torch.float32, state_out=None, y=None, saved=None, stream=None,
+                                 chain_wgs: int = WGS_AUTO):
+    """The chunk-wise forward (small-chunk backward form only: C in 2, 4, 8)
+    that also stores what lattice_osr_bwd_chunked_saved needs.  Returns (y,
+    state_out, saved); saved is a uint8 tensor of
+    lattice_osr_bwd_workspace_bytes bytes (allocated unless passed), to be
+    passed as that call's `saved`."""
+    lib = load_library()
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, chain_wgs=chain_wgs)
+    _check_outputs(desc, q, state_in, state_out, y, y_dtype)
+    st = _launch_stream(stream)
+    with torch.cuda.stream(st):
+        state_out, y = _outputs(desc, q, state_in, state_out, y, y_dtype)
+        need = lattice_osr_bwd_workspace_bytes(desc, chunk_size)
+        saved, sbytes = _workspace(saved, need, q.device)
+        rc = lib.lattice_osr_fwd_chunked_save(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
+                                              _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(state_out), _ptr(y),
+                                              _ptr(saved), sbytes, st.cuda_stream)
+    if rc != OK:
+        raise OSRError(rc, "lattice_osr_fwd_chunked_save")
+    return y, state_out, saved
+
+
+def lattice_osr_bwd_chunked_saved(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size: int, *, saved,
+                                  mode: int = MODE_DEC, grads: Optional[dict] = None, stream=None,
+                                  chain_wgs: int = WGS_AUTO) -> dict:
+    """lattice_osr_bwd_chunked's gradients, bit for bit, from the values a
+    lattice_osr_fwd_chunked_save call with the same inputs stored in `saved`
+    (its forward pass skipped)."""
+    if saved is None:
+        raise ValueError("saved: the tensor lattice_osr_fwd_chunked_save returned")
+    return _bwd("lattice_osr_bwd_chunked_saved", q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size, mode,
+                grads, saved, stream, LIN2, chain_wgs, BWD_AUTO)
+
+
+def _bwd(entry, q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size, mode, grads, workspace, stream,
+         linearisation, chain_wgs, bwd_form) -> dict:
     lib = load_library()
     desc = _desc_from(q, k, v, gamma, mu, state_in, dy.dtype, mode, linearisation, chain_wgs=chain_wgs,
                       bwd_form=bwd_form)
@@ -357,13 +404,13 @@ def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_
         need = lattice_osr_bwd_workspace_bytes(desc, chunk_size)
         workspace, wbytes = _workspace(workspace, need, q.device)
         g = grads
-        rc = lib.lattice_osr_bwd_chunked(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
-                                         _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(dy), _ptr(dstate_out),
-                                         _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dgamma"]),
-                                         _ptr(g["dmu"]), _ptr(g["dstate_in"]), _ptr(workspace), wbytes,
-                                         st.cuda_stream)
+        rc = getattr(lib, entry)(ctypes.byref(desc), int(chunk_size), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(gamma), _ptr(mu), _ptr(state_in), _ptr(dy), _ptr(dstate_out),
+                                 _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dgamma"]),
+                                 _ptr(g["dmu"]), _ptr(g["dstate_in"]), _ptr(workspace), wbytes,
+                                 st.cuda_stream)
     if rc != OK:
-        raise OSRError(rc, "lattice_osr_bwd_chunked")
+        raise OSRError(rc, entry)
     return grads
 
 

@@ -327,6 +327,40 @@ LATTICE_OSR_API int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_
 LATTICE_OSR_API size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* desc, int32_t chunk_size);
 
 /*
+ * Training at small chunks without the backward's forward pass.  Where the
+ * backward takes its small-chunk form (chunk_size 2, 4 or 8 with
+ * desc->bwd_form AUTO, the default linearisation, m d <= 4096, chunk_size <= 4
+ * at d = 128; elsewhere both calls return LATTICE_OSR_ERR_UNSUPPORTED):
+ *
+ * lattice_osr_fwd_chunked_save computes y and state_out exactly as
+ * lattice_osr_fwd_chunked does (the same kernel, bit for bit; arguments and
+ * rules as there, no workspace) and also stores, in bwd_workspace
+ * (lattice_osr_bwd_workspace_bytes(desc, chunk_size) bytes, 16-byte aligned,
+ * overlapping no argument), every chunk-start state before projection and,
+ * for the decoding objective, every token's h.
+ *
+ * lattice_osr_bwd_chunked_saved returns what lattice_osr_bwd_chunked returns,
+ * bit for bit (arguments and rules as there), taking those values from its
+ * workspace instead of recomputing them: the workspace must hold what a
+ * lattice_osr_fwd_chunked_save call with the same inputs, chunk_size and desc
+ * (y_dtype aside) stored, unchanged since (work on one stream, or ordered).
+ * The backward reads them and writes only the workspace's hand-off buffers,
+ * so the saved values serve any number of backward calls.  The forward pass
+ * this skips is about a third of the backward (B4 H8 T2048 m = d = 64 C4:
+ * ~1.5 of 4.2 ms).
+ */
+LATTICE_OSR_API int lattice_osr_fwd_chunked_save(const lattice_osr_desc* desc, int32_t chunk_size,
+                            const void* q, const void* k, const void* v, const void* gamma,
+                            const void* mu, const float* state_in, float* state_out, void* y,
+                            void* bwd_workspace, size_t bwd_workspace_bytes, void* hip_stream);
+LATTICE_OSR_API int lattice_osr_bwd_chunked_saved(const lattice_osr_desc* desc, int32_t chunk_size,
+                            const void* q, const void* k, const void* v, const void* gamma,
+                            const void* mu, const float* state_in, const void* dy,
+                            const float* dstate_out, float* dq, float* dk, float* dv, float* dgamma,
+                            float* dmu, float* dstate_in, void* workspace, size_t workspace_bytes,
+                            void* hip_stream);
+
+/*
  * Layer glue before the recurrence (section "Experiments", paragraph on the
  * Lattice block: a pair of short convolutions for q and k, which share one
  * projection, and the writing intensity gamma_t = sigmoid(W_gamma x_t); the

@@ -432,6 +432,59 @@ def test_bwd_small_chunk_form_workspace():
         assert ws(C, **kw) == ws(C, osr.BWD_WALK, **kw), g
 
 
+def _fwd_save_call(d, chunk, ptrs=None, saved=None, saved_bytes=None):
+    lib = osr.load_library()
+    if saved_bytes is None:
+        need = lib.lattice_osr_bwd_workspace_bytes(ctypes.byref(d), chunk)
+        saved_bytes = need if need != ctypes.c_size_t(-1).value else 0
+    if saved is None:
+        saved = BASE + 8 * (1 << 32)
+    return lib.lattice_osr_fwd_chunked_save(ctypes.byref(d), chunk, *(ptrs or _ptrs(d)), saved, saved_bytes, None)
+
+
+def _bwd_saved_call(d, ptrs, chunk, ws=None, ws_bytes=None):
+    lib = osr.load_library()
+    if ws_bytes is None:
+        need = lib.lattice_osr_bwd_workspace_bytes(ctypes.byref(d), chunk)
+        ws_bytes = need if need != ctypes.c_size_t(-1).value else 0
+    if ws is None:
+        ws = BASE + 14 * (1 << 32)
+    return lib.lattice_osr_bwd_chunked_saved(ctypes.byref(d), chunk, *ptrs, ws, ws_bytes, None)
+
+
+def test_saved_training_pair_rules():
+    """lattice_osr_fwd_chunked_save and lattice_osr_bwd_chunked_saved exist only
+    where the backward takes its small-chunk form (C in 2, 4, 8, BWD_AUTO, the
+    default linearisation, at most 2 slot rows per thread, C within the token
+    loop's batch): UNSUPPORTED elsewhere; null pointers, a short saved buffer and
+    misalignment are refused before anything runs."""
+    ok = dict(B=1, T=64, H=2, m=64, d=64)
+    for C, kw in ((16, {}), (1, {}), (4, dict(linearisation=osr.LIN1)), (4, dict(bwd_form=osr.BWD_WALK)),
+                  (4, dict(m=64, d=128)), (8, dict(m=32, d=128))):
+        d = osr.make_desc(**dict(ok, **{k: v for k, v in kw.items() if k in ("m", "d")}),
+                          **{k: v for k, v in kw.items() if k not in ("m", "d")})
+        assert _fwd_save_call(d, C) == osr.ERR_UNSUPPORTED, (C, kw)
+        assert _bwd_saved_call(d, _bwd_ptrs(), C) == osr.ERR_UNSUPPORTED, (C, kw)
+    d = osr.make_desc(**ok)
+    for i in range(8):
+        p = _ptrs(d)
+        p[i] = None
+        assert _fwd_save_call(d, 4, ptrs=p) == osr.ERR_NULL, i
+    lib = osr.load_library()
+    assert lib.lattice_osr_fwd_chunked_save(ctypes.byref(d), 4, *_ptrs(d), None, 1 << 20, None) == osr.ERR_NULL
+    need = lib.lattice_osr_bwd_workspace_bytes(ctypes.byref(d), 4)
+    assert _fwd_save_call(d, 4, saved_bytes=need - 1) == osr.ERR_WORKSPACE
+    assert _fwd_save_call(d, 4, saved=BASE + 8 * (1 << 32) + 4) == osr.ERR_ALIGN
+    assert _fwd_save_call(d, 3) == osr.ERR_SHAPE
+    for i in range(14):
+        p = _bwd_ptrs()
+        p[i] = None
+        assert _bwd_saved_call(d, p, 4) == osr.ERR_NULL, i
+    assert _bwd_saved_call(d, _bwd_ptrs(), 4, ws_bytes=need - 1) == osr.ERR_WORKSPACE
+    # the saved buffer is an output of the forward: it may overlap no argument
+    assert _fwd_save_call(d, 4, saved=_ptrs(d)[7]) == osr.ERR_ALIAS
+
+
 def test_bwd_workspace_too_small():
     d = osr.make_desc(2, 64, 2, 32, 32)
     need = osr.lattice_osr_bwd_workspace_bytes(d, 16)

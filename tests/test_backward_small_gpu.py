@@ -192,3 +192,39 @@ def test_small_chunk_backward_workload_sampled(C):
     errs = {key: max(_rel(_pick(key, got[key], b, h), _pick(key, r[key], 0, 0)) for (b, h), r in zip(bh, refs))
             for key in KEYS}
     _report_and_check("vs oracle (2 sequences)", errs, TOL[synth.BF16])
+
+
+# (B, T, H, m, d, C, in dtype, objective, bf16 y and dy)
+SAVED_CASES = [(2, 64, 3, 64, 64, 4, synth.BF16, osr.MODE_DEC, False), (1, 64, 2, 16, 32, 2, synth.F32, osr.MODE_DEC, False),
+               (1, 64, 4, 64, 64, 8, synth.BF16, osr.MODE_SIM, True), (2, 32, 2, 32, 128, 4, synth.BF16, osr.MODE_DEC, True),
+               (1, 16, 2, 32, 32, 4, synth.F32, osr.MODE_ENC, False)]
+
+
+@pytest.mark.parametrize("B,T,H,m,d,C,dt,mode,bf16_out", SAVED_CASES)
+def test_saved_training_pair(B, T, H, m, d, C, dt, mode, bf16_out):
+    """lattice_osr_fwd_chunked_save returns lattice_osr_fwd_chunked's y and
+    state_out bit for bit, and lattice_osr_bwd_chunked_saved, from what it
+    stored, lattice_osr_bwd_chunked's gradients bit for bit (the same kernels
+    on the same values; the second backward from the same saved values too)."""
+    _say(f"saved training pair B{B} T{T} H{H} m{m} d{d} C{C} mode{mode} bf16 y/dy {bf16_out}")
+    inp = synth.make_inputs(B, T, H, m, d, seed=47, in_dtype=dt)
+    dy, dso = _upstream(inp, 47, dy_bf16=bf16_out)
+    t = osr.to_device(inp, "cuda")
+    ydt = torch.bfloat16 if bf16_out else torch.float32
+    y0, s0 = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], C, mode=mode,
+                                         y_dtype=ydt)
+    y1, s1, saved = osr.lattice_osr_fwd_chunked_save(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], C,
+                                                     mode=mode, y_dtype=ydt)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(s0, s1)
+    ref = _gpu_bwd(inp, dy, dso, C, mode, osr.BWD_AUTO, dy_bf16=bf16_out)
+    dyt = torch.from_numpy(dy).cuda()
+    if bf16_out:
+        dyt = dyt.to(torch.bfloat16)
+    dsot = torch.from_numpy(dso).cuda()
+    for rep in range(2):
+        g = osr.lattice_osr_bwd_chunked_saved(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], dyt, dsot, C,
+                                              saved=saved, mode=mode)
+        torch.cuda.synchronize()
+        for key in KEYS:
+            assert np.array_equal(g[key].cpu().numpy(), ref[key]), (rep, key)
