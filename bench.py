@@ -106,7 +106,9 @@ def measured_traffic(kernel_key: str):
 
 
 class Case:
-    """Device-resident inputs and outputs for one entry point on one workload.
+    """Device-resident inputs and outputs for one entry point on one workload
+    (entry: chunked, chunked_gated, recurrent, decode, backward, or train: the
+    saving forward and the backward from its saved values, one training step).
     With copies > 1 the steps rotate over that many separately allocated input
     sets, so a working set larger than the 256 MB Infinity Cache is read from
     HBM rather than from the cache."""
@@ -126,7 +128,7 @@ class Case:
         self.y = torch.empty((inp.B, inp.T, inp.H, inp.d), dtype=self.y_dtype, device="cuda")
         self.state_out = torch.empty_like(self.sets[0]["state"])
         self.ws = None
-        if entry == "backward":
+        if entry in ("backward", "train"):
             desc = osr.make_desc(inp.B, inp.T, inp.H, inp.m, inp.d, 1,
                                  osr.BF16 if inp.in_dtype == "bf16" else osr.F32, osr.F32, mode, linearisation)
             self.ws = torch.empty(osr.lattice_osr_bwd_workspace_bytes(desc, chunk), dtype=torch.uint8,
@@ -165,6 +167,13 @@ class Case:
         elif self.entry == "backward":
             osr.lattice_osr_bwd_chunked(*args, self.dy, self.dso, self.chunk, mode=self.mode, grads=self.grads,
                                         workspace=self.ws)
+        elif self.entry == "train":
+            # one training step of the layer at a small chunk: the forward that saves what the
+            # backward needs, then the backward from those values
+            osr.lattice_osr_fwd_chunked_save(*args, self.chunk, mode=self.mode, y_dtype=self.y_dtype,
+                                             state_out=self.state_out, y=self.y, saved=self.ws)
+            osr.lattice_osr_bwd_chunked_saved(*args, self.dy, self.dso, self.chunk, saved=self.ws, mode=self.mode,
+                                              grads=self.grads)
         elif self.entry == "recurrent":
             osr.lattice_osr_fwd_recurrent(*args, mode=self.mode, y_dtype=self.y_dtype, state_out=self.state_out,
                                           y=self.y)
@@ -398,12 +407,14 @@ def main() -> int:
                                                      (SMALL, "chunked", 64, 10, 0, 1),
                                                      (SMALL, "backward", 64, 2, 0, 0),
                                                      (SMALL, "backward", 4, 1, 0, 0),
+                                                     (SMALL, "train", 4, 1, 0, 0),
                                                      (HEADLINE, "backward", HEADLINE_CHUNK, 2, 0, 0)):
             # the small workload (51 MB) fits the 256 MB Infinity Cache: rotate 8 input copies
             c = Case(name, entry, chunk, copies=8 if name == SMALL and entry == "chunked" else 1,
                      mode=mode, linearisation=lin)
             t_ms = time_case(c, steps, 1)
-            ab = algorithmic_bytes_bwd(c.w) if entry == "backward" else algorithmic_bytes(c.w)
+            ab = {"backward": algorithmic_bytes_bwd(c.w),
+                  "train": algorithmic_bytes(c.w) + algorithmic_bytes_bwd(c.w)}.get(entry, algorithmic_bytes(c.w))
             if entry == "chunked_gated":  # the gate is read once more (in the inputs' dtype)
                 ab += c.head_tokens * c.w["d"] * (2 if c.w["in_dtype"] == "bf16" else 4)
             sec.append({"workload": name, "entry": entry, "chunk": chunk,
@@ -412,7 +423,7 @@ def main() -> int:
                         "head_tokens_per_s": c.head_tokens / (t_ms * 1e-3),
                         "hbm_gbs_algorithmic": ab / (t_ms * 1e-3) / 1e9,
                         "hbm_frac": ab / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                        "tflops_algorithmic": None if entry == "backward"
+                        "tflops_algorithmic": None if entry in ("backward", "train")
                         else algorithmic_flops(c.w, chunk) / (t_ms * 1e-3) / 1e12,
                         "chain_reference_ms": chain_reference_ms(c.w, chunk) if entry == "chunked" and chunk >= 16
                         else None})
