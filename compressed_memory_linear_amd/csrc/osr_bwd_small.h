@@ -26,12 +26,11 @@
 //   - two barriers per chunk: one publishes the partial sums, the other the
 //     sums over waves together with the next chunk's staged inputs.
 // The walk is bound by VALU issue on the B*H compute units that hold a
-// sequence.  With P = 2 the slot rows of a sequence split over two workgroups
-// (M / 2 rows each, half the instructions per chunk); every row-local step is
-// unchanged, and the chunk's sums over slots, the only step that crosses rows,
-// go through the device-coherent hand-off of the split walk (osr_bwd_kernel.h):
-// each workgroup publishes its rows' sums, waits for the other's, and adds the
-// parts in workgroup order, so both hold the same sums.
+// sequence.  With P = 2 or 4 the slot rows of a sequence split over P
+// workgroups (M / P rows each, 1/P of the instructions per chunk); every
+// row-local step is unchanged, and the chunk's sums over slots, the only step
+// that crosses rows, go from workgroup to workgroup as tagged 64-bit pairs
+// (below); each adds all parts in workgroup order, so all hold the same sums.
 #pragma once
 
 #include <type_traits>
@@ -130,8 +129,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     // rg: the (global) slot row of this thread's first row
     const int cg = tid % L::TPR, rg = pidx * (M / P) + tid / L::TPR;
-    int nxch = 0;          // chunks exchanged with the other workgroup (P > 1)
-    bool xbroken = false;  // a wait for it gave up (then the results are wrong, but every wave ends)
+    int nxch = 0;          // chunks exchanged with the other workgroups (P > 1)
+    bool xbroken = false;  // a wait for them gave up (then the results are wrong, but every wave ends)
     const int T = p.f.T, NC = T / C;
     const bool enc = p.f.mode == 2;
     const bool gps = p.f.gamma_per_slot != 0;
@@ -442,16 +441,17 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     __syncthreads();  // the last chunk's inputs visible
     issue(pre, NC > 1 ? NC - 2 : 0);
 
-    // Split rows (P > 1): the chunk's sums over slots need the other workgroup's
-    // part.  Each value goes with the chunk's tag (nxch + 1) as one 64-bit pair,
+    // Split rows (P > 1): the chunk's sums over slots need the other workgroups'
+    // parts.  Each value goes with the chunk's tag (nxch + 1) as one 64-bit pair,
     // written and read with agent-scope atomics, so a pair is seen whole or not at
-    // all: publish writes this workgroup's pairs, await_part polls the other's own
-    // pairs until all carry the tag (no store-retire wait, barrier or counter on
-    // the way) and adds the parts in workgroup order, so both hold the same sums.
-    // Parts alternate between two buffers by chunk parity: a buffer is rewritten
-    // two chunks later, after the other workgroup has published the chunk in
-    // between, which it does only after reading this one.  The buffers are zeroed
-    // before each call (tags start at 1).
+    // all: publish writes this workgroup's pairs, await_part polls each other
+    // workgroup's pairs of the thread's own float4 until all carry the tag (no
+    // store-retire wait, barrier or counter on the way) and adds all parts in
+    // workgroup order, so every workgroup holds the same sums.  Parts alternate
+    // between two buffers by chunk parity: a workgroup rewrites a buffer two
+    // chunks later, after every other one has published the chunk in between,
+    // which each does only after reading this one.  The buffers are zeroed before
+    // each call (tags start at 1).
     constexpr int XW = 8 * W;  // pairs per part (at most 8 tokens)
     static_assert(P == 1 || C <= 8, "hand-off part size");
     auto xpart = [&](int q) __attribute__((always_inline)) {
@@ -502,12 +502,13 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     };
 
     // At C <= 4 with split rows, each chunk publishes its part, then prepares the
-    // chunk before (which needs no gradient) while the other's part is on its way,
-    // and only then waits for it (two prepared chunks live: at C = 8 that spilled).
+    // chunk before (which needs no gradient) while the other parts are on their
+    // way, and only then waits for them (two prepared chunks live: at C = 8 that
+    // spilled).
     constexpr bool PIPE = P > 1 && C <= 4;
     if constexpr (!PIPE) {
-        // Per chunk: prepare, reverse, barrier, sums over waves (over both
-        // workgroups' rows where split) and the staged inputs of the chunk before,
+        // Per chunk: prepare, reverse, barrier, sums over waves (over every
+        // workgroup's rows where split) and the staged inputs of the chunk before,
         // barrier, the rest.
         for (int n = NC - 1; n >= 0; --n) {
             Prep x;

@@ -58,9 +58,11 @@ struct BwdParams {
     // workspace layout ([B*H*NC][rows/16][C/16][64 lanes][4], rows = m or d):
     // g, kappa, h, e (first linearisation) and c, beta; |h|^2 as [B*H*NC][C].
     const float *chain_g, *chain_k, *chain_h, *chain_e, *chain_c, *chain_b, *chain_hh;
-    // Slot rows split over split_p workgroups per sequence (1: not split; needs
-    // the state-passing kernel's arrays): per (b,h), two batch parities x
-    // split_p parts of one batch's sums over slots, and split_p progress counters.
+    // Slot rows split over split_p workgroups per sequence (1: not split).  The
+    // general walk (needs the state-passing kernel's arrays): per (b,h), two
+    // batch parities x split_p parts of one batch's sums over slots at xbuf, and
+    // split_p progress counters at xflags.  The small-chunk walk: tagged pairs
+    // at xbuf only (bwd_small_xchg_bytes).
     int split_p;
     float* xbuf;
     int* xflags;
