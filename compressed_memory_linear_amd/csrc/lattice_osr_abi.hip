@@ -213,10 +213,12 @@ size_t bwd_chain_extra_bytes(const lattice_osr_desc* d, int C) {
     return nch * (2 * static_cast<size_t>(d->m) * C + C) * sizeof(float);
 }
 
-// The small-chunk reverse walk (C <= 8) where it is built and not turned off.
+// The small-chunk reverse walk (C <= 8) where it is built, not turned off, and
+// the fewest workgroups per sequence it needs fit 256 compute units.
 bool bwd_small_form(const lattice_osr_desc* d, int C) {
     return d->bwd_form == LATTICE_OSR_BWD_AUTO && C <= 8 &&
-           osr::bwd_small_supported(d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1);
+           osr::bwd_small_supported(d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1) &&
+           static_cast<int64_t>(d->B) * d->H * osr::bwd_small_min_p(d->m, d->d, C) <= 256;
 }
 
 // With the small-chunk walk and the decoding objective, the backward's part is
@@ -530,11 +532,20 @@ int bwd_chunked_impl(const lattice_osr_desc* desc, int32_t chunk_size, const voi
         }
         p.f.hrec = pf.hrec;
         // the rows of a sequence over P workgroups where all of them can be resident (a
-        // smaller P fits in the buffers sized for the policy's)
+        // smaller P fits in the buffers sized for the policy's); on a device with too
+        // few compute units for the fewest the shape needs, the general walk takes the
+        // chunk-start states from phase 1 instead
+        const int64_t bh = static_cast<int64_t>(desc->B) * desc->H, cus = device_cus();
+        const int pmin = osr::bwd_small_min_p(desc->m, desc->d, chunk_size);
         p.split_p = bwd_parts(desc, chunk_size);
         p.xbuf = nullptr;
         p.xflags = nullptr;
-        while (p.split_p > 1 && static_cast<int64_t>(desc->B) * desc->H * p.split_p > device_cus()) p.split_p /= 2;
+        while (p.split_p > pmin && bh * p.split_p > cus) p.split_p /= 2;
+        if (p.split_p > 1 && bh * p.split_p > cus) {
+            p.split_p = 1;
+            p.states_ready = 1;
+            return osr::launch_bwd(desc->m, desc->d, p, in_bf16, st);
+        }
         if (p.split_p > 1) {
             const size_t xoff = need - osr::bwd_small_xchg_bytes(desc->B, desc->H, desc->d, p.split_p);
             p.xbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + xoff);

@@ -41,27 +41,38 @@
 
 namespace osr {
 
-// Whether the small-chunk walk is built for (M, D, C): at most 2 slot rows per
-// thread (the chunk's states in registers) and C within the forward token
-// loop's exchange batch (its phase 1).
-template <int M, int D>
-constexpr bool bwd_small_fits(int C) {
-    using L = ValuLayout<M, D, tokenloop_threads<M, D>()>;
-    return L::RPT <= 2 && (C == 2 || C == 4 || C == 8) && C <= TokBatch<L>::BT;
-}
-
 // Threads per workgroup of the walk with the rows split over P workgroups.
 template <int M, int D, int P>
 constexpr int bwd_small_threads() {
     return tokenloop_threads<M / P, D>();
 }
 
-// Whether P workgroups of M / P rows (16 or more) each have the threads to stage
-// a chunk's inputs and hold its sums, one unit of each kind per thread.
+// Whether the walk runs on P workgroups of M / P rows each: 16 rows or more
+// (P > 1), at most 2 slot rows per thread (the chunk's states in registers), and
+// the threads to stage a chunk's inputs and hold its sums, one unit of each kind
+// per thread.
 template <int M, int D, int C, int P>
 constexpr bool bwd_small_split_ok() {
-    constexpr int NT = bwd_small_threads<M, D, P>();
-    return M / P >= 16 && C * (M / 4) <= NT && C * (D / 4 + 1) <= NT;
+    if constexpr (M / P < 16 && P > 1) {
+        return false;
+    } else {
+        constexpr int NT = bwd_small_threads<M, D, P>();
+        return ValuLayout<M / P, D, NT>::RPT <= 2 && C * (M / 4) <= NT && C * (D / 4 + 1) <= NT;
+    }
+}
+
+// Whether the small-chunk walk is built for (M, D, C): C within the forward
+// token loop's exchange batch (its phase 1), and some P in {1, 2, 4} that
+// bwd_small_split_ok allows.
+template <int M, int D>
+constexpr bool bwd_small_fits(int C) {
+    using L = ValuLayout<M, D, tokenloop_threads<M, D>()>;
+    if (!((C == 2 || C == 4 || C == 8) && C <= TokBatch<L>::BT)) return false;
+    switch (C) {
+        case 2: return bwd_small_split_ok<M, D, 2, 1>() || bwd_small_split_ok<M, D, 2, 2>() || bwd_small_split_ok<M, D, 2, 4>();
+        case 4: return bwd_small_split_ok<M, D, 4, 1>() || bwd_small_split_ok<M, D, 4, 2>() || bwd_small_split_ok<M, D, 4, 4>();
+        default: return bwd_small_split_ok<M, D, 8, 1>() || bwd_small_split_ok<M, D, 8, 2>() || bwd_small_split_ok<M, D, 8, 4>();
+    }
 }
 
 // Four consecutive elements loaded without conversion (the conversion, and so
@@ -110,7 +121,7 @@ struct SmallStage {
 // otherwise h = -v (similarity) or v (encoding layer).  DYB: dy in bf16.
 template <int M, int D, int NT, int C, typename TIn, bool DYB, bool DEC, int P>
 __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
-    static_assert(P == 1 || ((P == 2 || P == 4) && M / P >= 16), "split: 2 or 4 workgroups of 16 rows or more");
+    static_assert(bwd_small_split_ok<M, D, C, P>(), "rows, registers and threads of the split");
     using L = ValuLayout<M / P, D, NT>;
     using SG = SmallStage<M, D, C>;
     using DYT = typename std::conditional<DYB, uint16_t, float>::type;
@@ -501,11 +512,11 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
         return acc;
     };
 
-    // At C <= 4 with split rows, each chunk publishes its part, then prepares the
-    // chunk before (which needs no gradient) while the other parts are on their
-    // way, and only then waits for them (two prepared chunks live: at C = 8 that
-    // spilled).
-    constexpr bool PIPE = P > 1 && C <= 4;
+    // With split rows and C RPT <= 4, each chunk publishes its part, then prepares
+    // the chunk before (which needs no gradient) while the other parts are on
+    // their way, and only then waits for them (two prepared chunks live: with
+    // C RPT = 8 that spilled).
+    constexpr bool PIPE = P > 1 && C * RPT <= 4;
     if constexpr (!PIPE) {
         // Per chunk: prepare, reverse, barrier, sums over waves (over every
         // workgroup's rows where split) and the staged inputs of the chunk before,
@@ -614,7 +625,10 @@ static int launch_bwd_small_mdc(const BwdParams& p, bool in_bf16, hipStream_t st
                 return -3;
             }
         } else if (p.split_p == 1) {
-            launch_bwd_small_p<M, D, C, 1>(p, in_bf16, st);
+            if constexpr (bwd_small_split_ok<M, D, C, 1>())
+                launch_bwd_small_p<M, D, C, 1>(p, in_bf16, st);
+            else
+                return -3;
         } else {
             return -3;
         }
@@ -647,7 +661,8 @@ template <int M, int D>
 bool bwd_small_split_ok_md(int C, int P) {
     auto ok = [&](auto c) {
         constexpr int CV = decltype(c)::value;
-        return P == 1 || (P == 2 && bwd_small_split_ok<M, D, CV, 2>()) || (P == 4 && bwd_small_split_ok<M, D, CV, 4>());
+        return (P == 1 && bwd_small_split_ok<M, D, CV, 1>()) || (P == 2 && bwd_small_split_ok<M, D, CV, 2>()) ||
+               (P == 4 && bwd_small_split_ok<M, D, CV, 4>());
     };
     switch (C) {
         case 2: return ok(std::integral_constant<int, 2>{});

@@ -82,8 +82,9 @@ int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 // the workspace (states_ready).  Same workspace layout as launch_bwd.
 bool bwd_chunk_supported(int m, int d, int C, bool in_bf16, bool lin1, int mode);
 int launch_bwd_chunk(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
-// The reverse walk at small chunks (osr_bwd_small.hip): C in {2, 4, 8}, at most
-// 2 slot rows per thread of the token loop's layout, the default linearisation.
+// The reverse walk at small chunks (osr_bwd_small.hip): C in {2, 4, 8} within
+// the token loop's batch, the default linearisation, and at most 2 slot rows per
+// thread on 1, 2 or 4 workgroups per sequence (bwd_small_min_p).
 // Its phase 1 is the forward's small-chunk token loop with raw (and, decoding
 // objective, hrec) set; f.hrec then points at those records.  Same workspace
 // layout as launch_bwd, plus hrec.
@@ -95,6 +96,7 @@ inline size_t bwd_small_xchg_bytes(int B, int H, int d, int P) {
     return static_cast<size_t>(B) * H * 2 * P * 8 * (d + 4) * sizeof(uint64_t);
 }
 bool bwd_small_supported(int m, int d, int C, bool lin1);
+int bwd_small_min_p(int m, int d, int C);
 int bwd_small_split_p(int B, int H, int m, int d, int C, int chain_wgs);
 int launch_bwd_small(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 

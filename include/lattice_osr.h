@@ -299,10 +299,10 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * over the tile's tokens; the same workspace and the same result up to fp32
  * rounding (the token walk's to 1e-4 of RMS; with forget gates mu near 0 the
  * tile's gate products span many decades and the two agree to 5e-3).  At
- * chunk_size 2, 4 or 8 with desc->bwd_form AUTO (the default linearisation,
- * m d <= 4096, chunk_size <= 4 at d = 128) a reverse walk that keeps each
- * chunk's states in registers runs after a forward pass that stores the
- * chunk-start states; the decoding objective adds every token's h to the
+ * chunk_size 2, 4 or 8 with desc->bwd_form AUTO (the default linearisation;
+ * chunk_size <= 4 at d = 128 and at m d = 8192, chunk_size 2 at
+ * m = d = 128) a reverse walk that keeps each chunk's states in registers
+ * runs after a forward pass that stores the chunk-start states; the decoding objective adds every token's h to the
  * workspace, 4 T d bytes per (b,h).  There, with desc->chain_wgs =
  * LATTICE_OSR_WGS_AUTO, chunk_size >= 4, m >= 32 and B*H*P <= 256, the
  * slot rows of each sequence are split over P workgroups (4 at chunk_size 8
@@ -310,7 +310,10 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * that exchange each chunk's sums over slots through hand-off buffers at the
  * end of the workspace, B*H*128 P (d + 4) bytes (value and tag pairs); fewer
  * on devices with fewer than B*H*P compute units, one with
- * LATTICE_OSR_WGS_ONE.  The result equals the general walk's up to fp32
+ * LATTICE_OSR_WGS_ONE.  At m d = 8192 and m = d = 128 the chunk's states fit
+ * only split, over at least 2 and 4 workgroups: the form needs B*H*P <= 256
+ * there, WGS_ONE gives that fewest P, and a device with fewer compute units
+ * runs the general walk within the same workspace.  The result equals the general walk's up to fp32
  * rounding.  The remaining rules (shapes,
  * chunk sizes, alignment of the inputs, status codes, asynchrony) are those
  * of lattice_osr_fwd_chunked.
@@ -328,9 +331,8 @@ LATTICE_OSR_API size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* d
 
 /*
  * Training at small chunks without the backward's forward pass.  Where the
- * backward takes its small-chunk form (chunk_size 2, 4 or 8 with
- * desc->bwd_form AUTO, the default linearisation, m d <= 4096, chunk_size <= 4
- * at d = 128; elsewhere both calls return LATTICE_OSR_ERR_UNSUPPORTED):
+ * backward takes its small-chunk form (above; elsewhere both calls return
+ * LATTICE_OSR_ERR_UNSUPPORTED):
  *
  * lattice_osr_fwd_chunked_save computes y and state_out exactly as
  * lattice_osr_fwd_chunked does (the same kernel, bit for bit; arguments and

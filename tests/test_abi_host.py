@@ -423,7 +423,17 @@ def test_bwd_small_chunk_form_workspace():
     # no split once B*H*2 exceeds 256 compute units
     big = dict(B=8, T=64, H=17, m=64, d=64)
     assert ws(4, **big) - ws(4, osr.BWD_WALK, **big) == 8 * 17 * 64 * 64 * 4
-    general = [dict(C=4, m=64, d=128), dict(C=4, m=128, d=64), dict(C=8, m=32, d=128), dict(C=16, m=64, d=64),
+    # m d = 8192 (C <= 4) and m = d = 128 (C = 2): only with the rows over 2 or 4 workgroups, which
+    # B*H*P <= 256 must allow; WGS_ONE then gives the fewest, not one
+    for C, m, d, pmin in ((4, 64, 128, 2), (2, 128, 64, 2), (4, 128, 64, 2), (2, 128, 128, 4)):
+        kw = dict(B=2, T=64, H=3, m=m, d=d)
+        xchg = 2 * 3 * (2 * pmin * 8 * (d + 4) * 8)
+        for wgs in (osr.WGS_AUTO, osr.WGS_ONE):
+            assert ws(C, chain_wgs=wgs, **kw) - ws(C, osr.BWD_WALK, chain_wgs=wgs, **kw) == \
+                2 * 3 * 64 * d * 4 + xchg, (C, m, d, wgs)
+        many = dict(B=8, T=64, H=129 // pmin, m=m, d=d)  # B*H*pmin > 256: the general walk
+        assert ws(C, **many) == ws(C, osr.BWD_WALK, **many), (C, m, d)
+    general = [dict(C=8, m=64, d=128), dict(C=4, m=128, d=128), dict(C=8, m=32, d=128), dict(C=16, m=64, d=64),
                dict(C=1, m=64, d=64), dict(C=4, m=64, d=64, linearisation=osr.LIN1)]
     for g in general:
         kw = dict(B=2, T=64, H=3)
@@ -455,12 +465,12 @@ def _bwd_saved_call(d, ptrs, chunk, ws=None, ws_bytes=None):
 def test_saved_training_pair_rules():
     """lattice_osr_fwd_chunked_save and lattice_osr_bwd_chunked_saved exist only
     where the backward takes its small-chunk form (C in 2, 4, 8, BWD_AUTO, the
-    default linearisation, at most 2 slot rows per thread, C within the token
-    loop's batch): UNSUPPORTED elsewhere; null pointers, a short saved buffer and
-    misalignment are refused before anything runs."""
+    default linearisation, C within the token loop's batch, at most 2 slot rows
+    per thread on 1, 2 or 4 workgroups): UNSUPPORTED elsewhere; null pointers, a
+    short saved buffer and misalignment are refused before anything runs."""
     ok = dict(B=1, T=64, H=2, m=64, d=64)
     for C, kw in ((16, {}), (1, {}), (4, dict(linearisation=osr.LIN1)), (4, dict(bwd_form=osr.BWD_WALK)),
-                  (4, dict(m=64, d=128)), (8, dict(m=32, d=128))):
+                  (4, dict(m=128, d=128)), (8, dict(m=32, d=128))):
         d = osr.make_desc(**dict(ok, **{k: v for k, v in kw.items() if k in ("m", "d")}),
                           **{k: v for k, v in kw.items() if k not in ("m", "d")})
         assert _fwd_save_call(d, C) == osr.ERR_UNSUPPORTED, (C, kw)

@@ -108,6 +108,10 @@ CASES = [
     (1, 4, 2, 64, 64, 4, synth.F32, True, osr.MODE_DEC, False),    # one chunk
     (1, 8, 2, 16, 32, 4, synth.F32, True, osr.MODE_ENC, False),    # encoding layer, short
     (1, 8, 2, 32, 32, 2, synth.F32, False, osr.MODE_ENC, False),
+    # m d = 8192 and m = d = 128: the rows over at least 2 or 4 workgroups
+    (2, 64, 2, 64, 128, 4, synth.BF16, True, osr.MODE_DEC, False),
+    (1, 64, 2, 128, 64, 2, synth.F32, False, osr.MODE_SIM, True),
+    (1, 32, 2, 128, 128, 2, synth.BF16, True, osr.MODE_DEC, False),
 ]
 
 
@@ -149,11 +153,12 @@ def test_small_chunk_backward_split_vs_one(B, T, H, m, d, C, mode):
 
 
 # The policy's other branches: B*H = 160 (B*H*2 > 256: one workgroup per sequence)
-# at C = 4, and B*H = 100 at C = 8 (B*H*4 > 256: two workgroups, not four)
-@pytest.mark.parametrize("B,H,C", [(4, 40, 4), (4, 25, 8)])
-def test_small_chunk_backward_many_sequences(B, H, C):
-    _say(f"bwd small-chunk many sequences B{B} T32 H{H} m64 d64 C{C} bf16")
-    inp = synth.make_inputs(B, 32, H, 64, 64, seed=43, in_dtype=synth.BF16)
+# at C = 4, B*H = 100 at C = 8 (B*H*4 > 256: two workgroups, not four), and at
+# m64 d128 B*H = 128 (two workgroups, the fewest that shape allows, filling 256)
+@pytest.mark.parametrize("B,H,m,d,C", [(4, 40, 64, 64, 4), (4, 25, 64, 64, 8), (8, 16, 64, 128, 4)])
+def test_small_chunk_backward_many_sequences(B, H, m, d, C):
+    _say(f"bwd small-chunk many sequences B{B} T32 H{H} m{m} d{d} C{C} bf16")
+    inp = synth.make_inputs(B, 32, H, m, d, seed=43, in_dtype=synth.BF16)
     dy, dso = _upstream(inp, 43)
     got = _gpu_bwd(inp, dy, dso, C, osr.MODE_DEC, osr.BWD_AUTO)
     walk = _gpu_bwd(inp, dy, dso, C, osr.MODE_DEC, osr.BWD_WALK)
