@@ -202,7 +202,7 @@ def test_small_chunk_backward_workload_sampled(C):
 # (B, T, H, m, d, C, in dtype, objective, bf16 y and dy)
 SAVED_CASES = [(2, 64, 3, 64, 64, 4, synth.BF16, osr.MODE_DEC, False), (1, 64, 2, 16, 32, 2, synth.F32, osr.MODE_DEC, False),
                (1, 64, 4, 64, 64, 8, synth.BF16, osr.MODE_SIM, True), (2, 32, 2, 32, 128, 4, synth.BF16, osr.MODE_DEC, True),
-               (1, 16, 2, 32, 32, 4, synth.F32, osr.MODE_ENC, False)]
+               (1, 16, 2, 32, 32, 4, synth.F32, osr.MODE_ENC, False), (1, 32, 2, 128, 128, 2, synth.BF16, osr.MODE_DEC, False)]
 
 
 @pytest.mark.parametrize("B,T,H,m,d,C,dt,mode,bf16_out", SAVED_CASES)
