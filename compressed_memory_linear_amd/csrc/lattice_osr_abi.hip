@@ -213,10 +213,11 @@ size_t bwd_chain_extra_bytes(const lattice_osr_desc* d, int C) {
     return nch * (2 * static_cast<size_t>(d->m) * C + C) * sizeof(float);
 }
 
-// The small-chunk reverse walk (C <= 8) where it is built, not turned off, and
-// the fewest workgroups per sequence it needs fit 256 compute units.
+// The small-chunk reverse walk where it is built, not turned off, and the fewest
+// workgroups per sequence it needs fit 256 compute units: C <= 8 after the token
+// loop, C = 16 after the state-passing kernel (bf16 inputs, not the encoding layer).
 bool bwd_small_form(const lattice_osr_desc* d, int C) {
-    return d->bwd_form == LATTICE_OSR_BWD_AUTO && C <= 8 &&
+    return d->bwd_form == LATTICE_OSR_BWD_AUTO && (C <= 8 || (C == 16 && bwd_uses_chain(d, C))) &&
            osr::bwd_small_supported(d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1) &&
            static_cast<int64_t>(d->B) * d->H * osr::bwd_small_min_p(d->m, d->d, C) <= 256;
 }
@@ -224,7 +225,7 @@ bool bwd_small_form(const lattice_osr_desc* d, int C) {
 // With the small-chunk walk and the decoding objective, the backward's part is
 // followed by every token's h (fp32 [B*H][T][d]).
 size_t bwd_small_h_bytes(const lattice_osr_desc* d, int C) {
-    if (!bwd_small_form(d, C) || d->mode != LATTICE_OSR_MODE_DEC) return 0;
+    if (C > 8 || !bwd_small_form(d, C) || d->mode != LATTICE_OSR_MODE_DEC) return 0;
     return static_cast<size_t>(d->B) * d->H * d->T * d->d * sizeof(float);
 }
 
@@ -244,7 +245,7 @@ size_t bwd_workspace_needed(const lattice_osr_desc* d, int C) {
         n += osr::mfma_chain_workspace_bytes(d->B, d->H, d->T, d->m, d->d, C, d->linearisation == LATTICE_OSR_LIN1) +
              bwd_chain_extra_bytes(d, C);
     n += bwd_small_h_bytes(d, C);
-    if (bwd_small_form(d, C)) return n + osr::bwd_small_xchg_bytes(d->B, d->H, d->d, bwd_parts(d, C));
+    if (bwd_small_form(d, C)) return n + osr::bwd_small_xchg_bytes(d->B, d->H, d->d, bwd_parts(d, C), C);
     return n + osr::bwd_xchg_bytes(d->B, d->H, d->d, bwd_parts(d, C));
 }
 
@@ -460,7 +461,7 @@ int bwd_chunked_impl(const lattice_osr_desc* desc, int32_t chunk_size, const voi
                      float* dstate_in, void* workspace, size_t workspace_bytes, void* hip_stream, bool saved) {
     int rc = check_bwd_desc(desc, chunk_size);
     if (rc) return rc;
-    if (saved && !bwd_small_form(desc, chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (saved && (chunk_size > 8 || !bwd_small_form(desc, chunk_size))) return LATTICE_OSR_ERR_UNSUPPORTED;
     const size_t need = bwd_workspace_needed(desc, chunk_size);
     rc = check_bwd_buffers(desc, q, k, v, gamma, mu, state_in, dy, dstate_out, dq, dk, dv, dgamma, dmu,
                            dstate_in, workspace, workspace_bytes, need);
@@ -526,7 +527,7 @@ int bwd_chunked_impl(const lattice_osr_desc* desc, int32_t chunk_size, const voi
         // (unless lattice_osr_fwd_chunked_save stored them there already)
         const osr::Params pf =
             small_phase1_params(desc, chunk_size, q, k, v, gamma, mu, state_in, nullptr, nullptr, workspace);
-        if (!saved) {
+        if (!saved && !chain) {
             rc = osr::launch_valu(false, desc->m, desc->d, pf, in_bf16, st);
             if (rc) return rc;
         }
@@ -547,7 +548,7 @@ int bwd_chunked_impl(const lattice_osr_desc* desc, int32_t chunk_size, const voi
             return osr::launch_bwd(desc->m, desc->d, p, in_bf16, st);
         }
         if (p.split_p > 1) {
-            const size_t xoff = need - osr::bwd_small_xchg_bytes(desc->B, desc->H, desc->d, p.split_p);
+            const size_t xoff = need - osr::bwd_small_xchg_bytes(desc->B, desc->H, desc->d, p.split_p, chunk_size);
             p.xbuf = reinterpret_cast<float*>(static_cast<char*>(workspace) + xoff);
         }
         return osr::launch_bwd_small(desc->m, desc->d, p, in_bf16, st);
@@ -600,7 +601,7 @@ int lattice_osr_fwd_chunked_save(const lattice_osr_desc* desc, int32_t chunk_siz
                                  void* hip_stream) {
     int rc = check_bwd_desc(desc, chunk_size);
     if (rc) return rc;
-    if (!bwd_small_form(desc, chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (chunk_size > 8 || !bwd_small_form(desc, chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
     const size_t need = bwd_workspace_needed(desc, chunk_size);
     rc = check_buffers(desc, q, k, v, gamma, mu, state_in, state_out, y, bwd_workspace, bwd_workspace_bytes, need);
     if (rc) return rc;

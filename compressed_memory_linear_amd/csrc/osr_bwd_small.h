@@ -57,21 +57,24 @@ constexpr bool bwd_small_split_ok() {
         return false;
     } else {
         constexpr int NT = bwd_small_threads<M, D, P>();
-        return ValuLayout<M / P, D, NT>::RPT <= 2 && C * (M / 4) <= NT && C * (D / 4 + 1) <= NT;
+        constexpr int RPT = ValuLayout<M / P, D, NT>::RPT;
+        return RPT <= 2 && C * RPT <= 16 && C * (M / 4) <= NT && C * (D / 4 + 1) <= NT;
     }
 }
 
-// Whether the small-chunk walk is built for (M, D, C): C within the forward
-// token loop's exchange batch (its phase 1), and some P in {1, 2, 4} that
-// bwd_small_split_ok allows.
+// Whether the small-chunk walk is built for (M, D, C): at C <= 8 within the
+// forward token loop's exchange batch (its phase 1; at C = 16 the matrix-core
+// state passing is phase 1), and some P in {1, 2, 4} that bwd_small_split_ok
+// allows.
 template <int M, int D>
 constexpr bool bwd_small_fits(int C) {
     using L = ValuLayout<M, D, tokenloop_threads<M, D>()>;
-    if (!((C == 2 || C == 4 || C == 8) && C <= TokBatch<L>::BT)) return false;
+    if (!(((C == 2 || C == 4 || C == 8) && C <= TokBatch<L>::BT) || C == 16)) return false;
     switch (C) {
         case 2: return bwd_small_split_ok<M, D, 2, 1>() || bwd_small_split_ok<M, D, 2, 2>() || bwd_small_split_ok<M, D, 2, 4>();
         case 4: return bwd_small_split_ok<M, D, 4, 1>() || bwd_small_split_ok<M, D, 4, 2>() || bwd_small_split_ok<M, D, 4, 4>();
-        default: return bwd_small_split_ok<M, D, 8, 1>() || bwd_small_split_ok<M, D, 8, 2>() || bwd_small_split_ok<M, D, 8, 4>();
+        case 8: return bwd_small_split_ok<M, D, 8, 1>() || bwd_small_split_ok<M, D, 8, 2>() || bwd_small_split_ok<M, D, 8, 4>();
+        default: return bwd_small_split_ok<M, D, 16, 1>() || bwd_small_split_ok<M, D, 16, 2>() || bwd_small_split_ok<M, D, 16, 4>();
     }
 }
 
@@ -117,9 +120,11 @@ struct SmallStage {
     static constexpr int SIZE = (GT + C + 3) / 4 * 4;
 };
 
-// DEC: decoding objective (h = sum_i k_i z_i - v, from the phase-1 records);
-// otherwise h = -v (similarity) or v (encoding layer).  DYB: dy in bf16.
-template <int M, int D, int NT, int C, typename TIn, bool DYB, bool DEC, int P>
+// DEC: decoding objective (h = sum_i k_i z_i - v, from the phase-1 records:
+// the token loop's [T][D] rows, or with CH the state-passing kernel's per-chunk
+// fragments); otherwise h = -v (similarity) or v (encoding layer).  DYB: dy in
+// bf16.
+template <int M, int D, int NT, int C, typename TIn, bool DYB, bool DEC, int P, bool CH = false>
 __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     static_assert(bwd_small_split_ok<M, D, C, P>(), "rows, registers and threads of the split");
     using L = ValuLayout<M / P, D, NT>;
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     auto bth_of = [&](int t) { return (static_cast<int64_t>(b) * T + t) * p.f.H + hd; };
     auto el = [&](int i) { return (rg + L::RG * i) * D + cg * 4; };
     float* const sck = p.ws + static_cast<int64_t>(bh) * bwd_floats_per_bh<M, D>(T, C);  // [NC+1][M][D]
-    const float* const hrec = DEC ? p.f.hrec + static_cast<int64_t>(bh) * T * D : nullptr;
+    const float* const hrec = DEC && !CH ? p.f.hrec + static_cast<int64_t>(bh) * T * D : nullptr;
 
     // ---- staging: this thread's unit of each kind (indices clamped; only the
     // threads inside a kind's range write it) ----
@@ -174,7 +179,14 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     };
     auto issue = [&](Pre& x, int n) __attribute__((always_inline)) {
         const int64_t bq = bth_of(n * C + uq), bm = bth_of(n * C + um);
-        if constexpr (DEC)
+        if constexpr (DEC && CH) {
+            // lane (lg, lc) of the fragment for column block jb and token tile tb holds
+            // h[16 tb + 4 lg + r][16 jb + lc]: the 4 columns of a unit are 4 floats apart
+            const float* hs = p.chain_h + (static_cast<int64_t>(bh) * NC + n) * D * C +
+                              ((static_cast<int64_t>(cq >> 2) * (C >> 4) + (uq >> 4)) * 64 + ((uq & 15) >> 2) * 16 +
+                               (cq & 3) * 4) * 4 + (uq & 3);
+            x.h = make_float4(hs[0], hs[4], hs[8], hs[12]);
+        } else if constexpr (DEC)
             x.h = Raw4<float>::load(hrec, static_cast<int64_t>(n * C + uq) * D + cq * 4);
         else
             x.h = Raw4<TIn>::load(vp, bq * D + cq * 4);
@@ -463,8 +475,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     // chunks later, after every other one has published the chunk in between,
     // which each does only after reading this one.  The buffers are zeroed before
     // each call (tags start at 1).
-    constexpr int XW = 8 * W;  // pairs per part (at most 8 tokens)
-    static_assert(P == 1 || C <= 8, "hand-off part size");
+    constexpr int XW = (C > 8 ? C : 8) * W;  // pairs per part
     auto xpart = [&](int q) __attribute__((always_inline)) {
         return reinterpret_cast<uint64_t*>(p.xbuf) + ((static_cast<int64_t>(bh) * 2 + (nxch & 1)) * P + q) * XW +
                xu * W + xc4 * 4;
@@ -573,20 +584,23 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
 
 template <int M, int D, int C, typename TIn, bool DYB, int P>
 static void launch_bwd_small_dec(const BwdParams& p, hipStream_t st) {
+    // (C = 16: h from the state-passing kernel's fragments)
+    constexpr bool CH = C > 8;
     constexpr int NT = bwd_small_threads<M, D, P>();
     const dim3 grid(static_cast<unsigned>(p.f.B) * static_cast<unsigned>(p.f.H) * P);
     if constexpr (P > 1) {
         // the tagged hand-off pairs to zero (tags count the chunks of this call from 1)
-        const int nints = static_cast<int>(bwd_small_xchg_bytes(p.f.B, p.f.H, D, P) / sizeof(int));
+        const int nints = static_cast<int>(bwd_small_xchg_bytes(p.f.B, p.f.H, D, P, C) / sizeof(int));
         hipLaunchKernelGGL(osr_bwd_fill_ints<0>, dim3((nints + 255) / 256), dim3(256), 0, st,
                            reinterpret_cast<int*>(p.xbuf), nints);
     }
     if (p.f.mode == 0)
-        hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, true, P>), grid, dim3(NT), 0, st, p);
+        hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, true, P, CH>), grid, dim3(NT), 0, st, p);
     else
         hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, false, P>), grid, dim3(NT), 0, st, p);
 }
 
+// (C = 16 follows the state-passing kernel, which takes bf16 inputs only)
 template <int M, int D, int C, int P>
 static void launch_bwd_small_p(const BwdParams& p, bool in_bf16, hipStream_t st) {
     if (in_bf16) {
@@ -594,7 +608,7 @@ static void launch_bwd_small_p(const BwdParams& p, bool in_bf16, hipStream_t st)
             launch_bwd_small_dec<M, D, C, uint16_t, true, P>(p, st);
         else
             launch_bwd_small_dec<M, D, C, uint16_t, false, P>(p, st);
-    } else {
+    } else if constexpr (C <= 8) {
         if (p.dy_bf16)
             launch_bwd_small_dec<M, D, C, float, true, P>(p, st);
         else
@@ -642,6 +656,7 @@ static int launch_bwd_small_md(const BwdParams& p, bool in_bf16, hipStream_t st)
         case 2: return launch_bwd_small_mdc<M, D, 2>(p, in_bf16, st);
         case 4: return launch_bwd_small_mdc<M, D, 4>(p, in_bf16, st);
         case 8: return launch_bwd_small_mdc<M, D, 8>(p, in_bf16, st);
+        case 16: return launch_bwd_small_mdc<M, D, 16>(p, in_bf16, st);
         default: return -3;
     }
 }
@@ -668,6 +683,7 @@ bool bwd_small_split_ok_md(int C, int P) {
         case 2: return ok(std::integral_constant<int, 2>{});
         case 4: return ok(std::integral_constant<int, 4>{});
         case 8: return ok(std::integral_constant<int, 8>{});
+        case 16: return ok(std::integral_constant<int, 16>{});
         default: return false;
     }
 }

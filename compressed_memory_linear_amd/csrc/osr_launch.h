@@ -89,11 +89,12 @@ int launch_bwd_chunk(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t
 // objective, hrec) set; f.hrec then points at those records.  Same workspace
 // layout as launch_bwd, plus hrec.
 // split_p = 2 or 4 splits a sequence's slot rows over that many workgroups, with their
-// hand-off buffers at xbuf: per (b,h), 2 chunk parities x P parts x 8 tokens x
-// (d + 4) (value, tag) pairs of 8 bytes.
-inline size_t bwd_small_xchg_bytes(int B, int H, int d, int P) {
+// hand-off buffers at xbuf: per (b,h), 2 chunk parities x P parts x max(C, 8)
+// tokens x (d + 4) (value, tag) pairs of 8 bytes.  At C = 16 the state-passing
+// kernel is phase 1 (chunk-start states, and h in its fragment layout).
+inline size_t bwd_small_xchg_bytes(int B, int H, int d, int P, int C) {
     if (P <= 1) return 0;
-    return static_cast<size_t>(B) * H * 2 * P * 8 * (d + 4) * sizeof(uint64_t);
+    return static_cast<size_t>(B) * H * 2 * P * (C > 8 ? C : 8) * (d + 4) * sizeof(uint64_t);
 }
 bool bwd_small_supported(int m, int d, int C, bool lin1);
 int bwd_small_min_p(int m, int d, int C);

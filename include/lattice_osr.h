@@ -301,8 +301,11 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * tile's gate products span many decades and the two agree to 5e-3).  At
  * chunk_size 2, 4 or 8 with desc->bwd_form AUTO (the default linearisation;
  * chunk_size <= 4 at d = 128 and at m d = 8192, chunk_size 2 at
- * m = d = 128) a reverse walk that keeps each chunk's states in registers
- * runs after a forward pass that stores the chunk-start states; the decoding objective adds every token's h to the
+ * m = d = 128), and at chunk_size 16 where the state-passing kernel runs
+ * (bf16 inputs, decoding and similarity objectives) and a chunk fits, a
+ * reverse walk that keeps each chunk's states in registers runs after a
+ * forward pass that stores the chunk-start states (at chunk_size 16 that
+ * kernel's pass, which also supplies h); the decoding objective adds every token's h to the
  * workspace, 4 T d bytes per (b,h).  There, with desc->chain_wgs =
  * LATTICE_OSR_WGS_AUTO, chunk_size >= 4, m >= 32 and B*H*P <= 256, the
  * slot rows of each sequence are split over P workgroups (4 at chunk_size 8
@@ -331,8 +334,8 @@ LATTICE_OSR_API size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* d
 
 /*
  * Training at small chunks without the backward's forward pass.  Where the
- * backward takes its small-chunk form (above; elsewhere both calls return
- * LATTICE_OSR_ERR_UNSUPPORTED):
+ * backward takes its small-chunk form at chunk_size 2, 4 or 8 (above;
+ * elsewhere both calls return LATTICE_OSR_ERR_UNSUPPORTED):
  *
  * lattice_osr_fwd_chunked_save computes y and state_out exactly as
  * lattice_osr_fwd_chunked does (the same kernel, bit for bit; arguments and

@@ -433,7 +433,18 @@ def test_bwd_small_chunk_form_workspace():
                 2 * 3 * 64 * d * 4 + xchg, (C, m, d, wgs)
         many = dict(B=8, T=64, H=129 // pmin, m=m, d=d)  # B*H*pmin > 256: the general walk
         assert ws(C, **many) == ws(C, osr.BWD_WALK, **many), (C, m, d)
-    general = [dict(C=8, m=64, d=128), dict(C=4, m=128, d=128), dict(C=8, m=32, d=128), dict(C=16, m=64, d=64),
+    # C = 16 with bf16 inputs (not the encoding layer): after the state-passing kernel, which
+    # supplies h, on at least 2 workgroups (one slot row per thread) with parts of 16 tokens
+    # (m64 d64: two workgroups, the fewest with one row per thread; m32 d32 and m64 d16: one,
+    # as two would lack the threads to stage a chunk of 16 tokens)
+    for m, d, P in ((64, 64, 2), (32, 32, 1), (64, 16, 1)):
+        kw = dict(B=2, T=64, H=3, m=m, d=d)
+        xchg = 2 * 3 * (2 * P * 16 * (d + 4) * 8) if P > 1 else 0
+        assert ws(16, **kw) - ws(16, osr.BWD_WALK, chain_wgs=osr.WGS_ONE, **kw) == xchg, (m, d)
+    for kw16 in (dict(in_dtype=osr.F32), dict(mode=osr.MODE_ENC)):
+        kw = dict(B=2, T=64, H=3, m=64, d=64, **kw16)
+        assert ws(16, **kw) == ws(16, osr.BWD_WALK, **kw), kw16
+    general = [dict(C=8, m=64, d=128), dict(C=4, m=128, d=128), dict(C=8, m=32, d=128), dict(C=32, m=64, d=64),
                dict(C=1, m=64, d=64), dict(C=4, m=64, d=64, linearisation=osr.LIN1)]
     for g in general:
         kw = dict(B=2, T=64, H=3)

@@ -1,6 +1,7 @@
-"""GPU parity of the backward at small chunks (C = 2, 4, 8), where the
-automatic form is the small-chunk reverse walk (the chunk's per-token states
-in registers, its phase 1 the forward's small-chunk token loop), against the
+"""GPU parity of the backward at small chunks (C = 2, 4, 8, and 16 with bf16
+inputs), where the automatic form is the small-chunk reverse walk (the chunk's
+per-token states in registers; its phase 1 the forward's small-chunk token
+loop, or at C = 16 the matrix-core state passing), against the
 fp64 gradient oracle (oracle/osr_backward.py) and against the general walk
 (desc.bwd_form = LATTICE_OSR_BWD_WALK).
 
@@ -112,6 +113,10 @@ CASES = [
     (2, 64, 2, 64, 128, 4, synth.BF16, True, osr.MODE_DEC, False),
     (1, 64, 2, 128, 64, 2, synth.F32, False, osr.MODE_SIM, True),
     (1, 32, 2, 128, 128, 2, synth.BF16, True, osr.MODE_DEC, False),
+    # C = 16 (bf16 inputs): after the matrix-core state passing, h from its fragments
+    (2, 64, 2, 64, 64, 16, synth.BF16, True, osr.MODE_DEC, False),
+    (1, 64, 3, 32, 32, 16, synth.BF16, False, osr.MODE_SIM, True),
+    (1, 64, 2, 64, 32, 16, synth.BF16, True, osr.MODE_DEC, True),
 ]
 
 
@@ -180,9 +185,9 @@ def test_small_chunk_backward_deterministic():
         assert np.array_equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("C", [4, 8])
+@pytest.mark.parametrize("C", [4, 8, 16])
 def test_small_chunk_backward_workload_sampled(C):
-    """B4 H8 T2048 m64 d64 (the training workload's shape) at C = 4 and 8:
+    """B4 H8 T2048 m64 d64 (the training workload's shape) at C = 4, 8, 16:
     against the general walk in full, and two whole sequences against the
     oracle."""
     _say(f"bwd small-chunk workload B4 H8 T2048 m64 d64 C{C} bf16, sampled (b,h)")
