@@ -298,28 +298,30 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * chunk's matrix form (16-token tiles), the gate gradients by recursions
  * over the tile's tokens; the same workspace and the same result up to fp32
  * rounding (the token walk's to 1e-4 of RMS; with forget gates mu near 0 the
- * tile's gate products span many decades and the two agree to 5e-3).  At
- * chunk_size 2, 4 or 8 with desc->bwd_form AUTO (the default linearisation;
- * chunk_size <= 4 at d = 128 and at m d = 8192, chunk_size 2 at
- * m = d = 128), and at chunk_size 16 where the state-passing kernel runs
- * (bf16 inputs, decoding and similarity objectives) and a chunk fits, a
- * reverse walk that keeps each chunk's states in registers runs after a
- * forward pass that stores the chunk-start states (at chunk_size 16 that
- * kernel's pass, which also supplies h); the decoding objective adds every token's h to the
- * workspace, 4 T d bytes per (b,h).  There, with desc->chain_wgs =
- * LATTICE_OSR_WGS_AUTO, chunk_size >= 4, m >= 32 and B*H*P <= 256, the
- * slot rows of each sequence are split over P workgroups (4 at chunk_size 8
- * where a quarter of the rows has the threads to stage a chunk, else 2)
- * that exchange each chunk's sums over slots through hand-off buffers at the
- * end of the workspace, B*H*128 P (d + 4) bytes (value and tag pairs); fewer
- * on devices with fewer than B*H*P compute units, one with
- * LATTICE_OSR_WGS_ONE.  At m d = 8192 and m = d = 128 the chunk's states fit
- * only split, over at least 2 and 4 workgroups: the form needs B*H*P <= 256
- * there, WGS_ONE gives that fewest P, and a device with fewer compute units
- * runs the general walk within the same workspace.  The result equals the general walk's up to fp32
- * rounding.  The remaining rules (shapes,
- * chunk sizes, alignment of the inputs, status codes, asynchrony) are those
- * of lattice_osr_fwd_chunked.
+ * tile's gate products span many decades and the two agree to 5e-3).
+ *
+ * Small chunks: with desc->bwd_form AUTO and the default linearisation, at
+ * chunk_size 2, 4 or 8 (at most 4 at d = 128 and at m d = 8192, 2 at
+ * m = d = 128) and at chunk_size 16 on the state-passing path above, where
+ * a chunk fits, a reverse walk that keeps each chunk's per-token states in
+ * registers runs after a forward pass that stores the chunk-start states
+ * (at chunk_size 16 the state-passing kernel's pass, which also supplies h;
+ * below 16 the token loop's, and for the decoding objective every token's h
+ * goes to the workspace too, 4 T d bytes per (b,h)).  With desc->chain_wgs =
+ * LATTICE_OSR_WGS_AUTO, chunk_size >= 4, m >= 32 and B*H*P <= 256, the slot
+ * rows of each sequence are split over P workgroups (4 at chunk_size 8 where
+ * a quarter of the rows has the threads to stage a chunk, else 2) that
+ * exchange each chunk's sums over slots through hand-off buffers at the end
+ * of the workspace: B*H*16 P max(chunk_size, 8) (d + 4) bytes (value and tag
+ * pairs).  Fewer workgroups on devices with fewer than B*H*P compute units,
+ * one with LATTICE_OSR_WGS_ONE.  At m d = 8192, m = d = 128 and (chunk_size
+ * 16) m = d = 64 the chunk's states fit only split, over at least 2, 4 and 2
+ * workgroups: the form needs B*H*P <= 256 there, WGS_ONE gives that fewest
+ * P, and a device with fewer compute units runs the general walk within the
+ * same workspace.  The result equals the general walk's up to fp32 rounding.
+ *
+ * The remaining rules (shapes, chunk sizes, alignment of the inputs, status
+ * codes, asynchrony) are those of lattice_osr_fwd_chunked.
  */
 LATTICE_OSR_API int lattice_osr_bwd_chunked(const lattice_osr_desc* desc, int32_t chunk_size,
                             const void* q, const void* k, const void* v, const void* gamma,
