@@ -238,3 +238,17 @@ def test_saved_training_pair(B, T, H, m, d, C, dt, mode, bf16_out):
         torch.cuda.synchronize()
         for key in KEYS:
             assert np.array_equal(g[key].cpu().numpy(), ref[key]), (rep, key)
+
+
+def test_small_chunk_backward_long_sequence():
+    """B1 H16 T65536 m64 d64 C4 (16384 chunks: the longest workload's length,
+    its hand-off tags and buffer parities over a long run): against the
+    general walk in full at the long-sequence bar."""
+    _say("bwd small-chunk long sequence B1 T65536 H16 m64 d64 C4 bf16")
+    inp = synth.make_inputs(1, 65536, 16, 64, 64, seed=53, in_dtype=synth.BF16)
+    dy, dso = _upstream(inp, 53)
+    got = _gpu_bwd(inp, dy, dso, 4, osr.MODE_DEC, osr.BWD_AUTO)
+    for key in KEYS:
+        assert np.isfinite(got[key]).all(), key
+    walk = _gpu_bwd(inp, dy, dso, 4, osr.MODE_DEC, osr.BWD_WALK)
+    _report_and_check("vs general walk", _errs(got, walk), AGREE_LONG)
