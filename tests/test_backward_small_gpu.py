@@ -113,6 +113,9 @@ CASES = [
     (2, 64, 2, 64, 128, 4, synth.BF16, True, osr.MODE_DEC, False),
     (1, 64, 2, 128, 64, 2, synth.F32, False, osr.MODE_SIM, True),
     (1, 32, 2, 128, 128, 2, synth.BF16, True, osr.MODE_DEC, False),
+    # per-token gamma with the rows split (its gradient travels in the exchanged sums)
+    (2, 64, 2, 64, 64, 4, synth.BF16, False, osr.MODE_DEC, False),
+    (1, 64, 2, 64, 64, 8, synth.F32, False, osr.MODE_SIM, False),
     # C = 16 (bf16 inputs): after the matrix-core state passing, h from its fragments
     (2, 64, 2, 64, 64, 16, synth.BF16, True, osr.MODE_DEC, False),
     (1, 64, 3, 32, 32, 16, synth.BF16, False, osr.MODE_SIM, True),
