@@ -123,8 +123,10 @@ struct SmallStage {
 // DEC: decoding objective (h = sum_i k_i z_i - v, from the phase-1 records:
 // the token loop's [T][D] rows, or with CH the state-passing kernel's per-chunk
 // fragments); otherwise h = -v (similarity) or v (encoding layer).  DYB: dy in
-// bf16.
-template <int M, int D, int NT, int C, typename TIn, bool DYB, bool DEC, int P, bool CH = false>
+// bf16.  LIN1: the first chunk linearisation (eq. recurrence_linear1: gate
+// mu beta, and the term beta a c z on the chunk-start slot), whose reverse takes
+// one more row sum per token, de = z . D, and gives the term's share of dZ.
+template <int M, int D, int NT, int C, typename TIn, bool DYB, bool DEC, int P, bool CH = false, bool LIN1 = false>
 __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     static_assert(bwd_small_split_ok<M, D, C, P>(), "rows, registers and threads of the split");
     using L = ValuLayout<M / P, D, NT>;
@@ -295,7 +297,10 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
                 const float w = fmaxf(fmaf(-ci, ci, hh), 0.f);
                 const float bt = rsqrtf(fmaf(mu, mu, a * a * w));
                 x.beta[u][i] = bt;
-                x.rs[u + 1][i] = fma4(bt * fmaf(a, ci, mu), x.rs[u][i], (-bt * a) * h[u]);
+                if constexpr (LIN1)
+                    x.rs[u + 1][i] = fma4(bt * mu, x.rs[u][i], fma4(bt * a * ci, x.z[i], (-bt * a) * h[u]));
+                else
+                    x.rs[u + 1][i] = fma4(bt * fmaf(a, ci, mu), x.rs[u][i], (-bt * a) * h[u]);
             }
         }
         if constexpr (C <= 4) {
@@ -305,7 +310,11 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     };
     // the chunk's tokens in reverse: dq, per-slot dgamma; per token the partial
     // sums over the wave's slots (dh's terms, d|h|^2, dmu, per-token dgamma) to red
-    auto reverse = [&](const Prep& x, int n, float (&dcv)[C][RPT], float (&dkin)[C][RPT]) __attribute__((always_inline)) {
+    // (dZl: the first linearisation's share of dZ, from the state's adjoint per token)
+    auto reverse = [&](const Prep& x, int n, float (&dcv)[C][RPT], float (&dkin)[C][RPT], float4 (&dZl)[RPT])
+                       __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) dZl[i] = f4(0.f);
         const float* sb = stage_of(n);
 #pragma unroll
         for (int u = C - 1; u >= 0; --u) {
@@ -321,19 +330,21 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
                 kv[i] = sb[SG::K + u * M + row];
                 gv[i] = sb[gps ? SG::G + u * M + row : SG::GT + u];
             }
-            float dq[RPT], dg[RPT], dk2[RPT];
+            float dq[RPT], dg[RPT], dk2[RPT], de[RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 dq[i] = dot4(x.rs[u + 1][i], dy);
                 dR[i] = fma4(qv[i], dy, dR[i]);
                 dg[i] = dot4(x.rs[u][i], dR[i]);
                 dk2[i] = dot4(hu, dR[i]);
+                de[i] = LIN1 ? dot4(x.z[i], dR[i]) : 0.f;
             }
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 dq[i] = group_sum<L::TPR>(dq[i]);
                 dg[i] = group_sum<L::TPR>(dg[i]);
                 dk2[i] = group_sum<L::TPR>(dk2[i]);
+                if constexpr (LIN1) de[i] = group_sum<L::TPR>(de[i]);
             }
             // scalar chain rule per slot: g = beta (mu + a c), kap = -beta a,
             // beta = (mu^2 + a^2 w)^(-1/2), w = max(|h|^2 - c^2, 0)
@@ -348,12 +359,24 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
                 const float wraw = fmaf(-ci, ci, hh);
                 const float w = fmaxf(wraw, 0.f);
                 const float kap = -bt * a;
-                const float num = fmaf(a, ci, mu);
-                gate[i] = bt * num;
-                const float dbeta = num * dg[i] - a * dk2[i];
-                float da = bt * (ci * dg[i] - dk2[i]);
-                float dmu_i = bt * dg[i];
-                float dci = bt * a * dg[i];
+                float dbeta, da, dmu_i, dci;
+                if constexpr (LIN1) {
+                    // g = mu beta, e = beta a c (coefficient of z), kap = -beta a
+                    gate[i] = bt * mu;
+                    dbeta = fmaf(mu, dg[i], a * (ci * de[i] - dk2[i]));
+                    da = bt * (ci * de[i] - dk2[i]);
+                    dmu_i = bt * dg[i];
+                    dci = bt * a * de[i];
+                    dZl[i] = fma4(bt * a * ci, dR[i], dZl[i]);
+                } else {
+                    // g = beta (mu + a c), kap = -beta a
+                    const float num = fmaf(a, ci, mu);
+                    gate[i] = bt * num;
+                    dbeta = num * dg[i] - a * dk2[i];
+                    da = bt * (ci * dg[i] - dk2[i]);
+                    dmu_i = bt * dg[i];
+                    dci = bt * a * dg[i];
+                }
                 const float tb = -0.5f * bt * bt * bt * dbeta;
                 dmu_i = fmaf(2.f * mu, tb, dmu_i);
                 da = fmaf(2.f * a * w, tb, da);
@@ -411,11 +434,12 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
     };
     // gradients that take the sums over slots (tot); the gradient of Z back through
     // the projection, which leaves dR the gradient of the chunk before's end state
-    auto finish = [&](const Prep& x, int n, const float (&dcv)[C][RPT], const float (&dkin)[C][RPT]) __attribute__((always_inline)) {
+    auto finish = [&](const Prep& x, int n, const float (&dcv)[C][RPT], const float (&dkin)[C][RPT],
+                      const float4 (&dZl)[RPT]) __attribute__((always_inline)) {
         const float* sb = stage_of(n);
         float4 dZ[RPT];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) dZ[i] = f4(0.f);
+        for (int i = 0; i < RPT; ++i) dZ[i] = dZl[i];
 #pragma unroll
         for (int u = 0; u < C; ++u) {
             const int64_t bth = bth_of(n * C + u);
@@ -536,7 +560,8 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
             Prep x;
             prep(x, n, scur);
             float dcv[C][RPT], dkin[C][RPT];
-            reverse(x, n, dcv, dkin);
+            float4 dZl[RPT];
+            reverse(x, n, dcv, dkin, dZl);
             __syncthreads();  // the chunk's partial sums visible
             float4 acc = wave_sums();
             if constexpr (P > 1) {
@@ -551,14 +576,15 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
             __syncthreads();  // the sums over slots and the staged inputs visible
             // (the last chunk loads chunk 0 again: unconditional, no load under a branch)
             issue(pre, n > 1 ? n - 2 : 0);
-            finish(x, n, dcv, dkin);
+            finish(x, n, dcv, dkin, dZl);
         }
     } else {
         Prep x;
         prep(x, NC - 1, scur);
         for (int n = NC - 1; n >= 0; --n) {
             float dcv[C][RPT], dkin[C][RPT];
-            reverse(x, n, dcv, dkin);
+            float4 dZl[RPT];
+            reverse(x, n, dcv, dkin, dZl);
             __syncthreads();  // the chunk's partial sums visible
             float4 acc = wave_sums();
             publish(acc);
@@ -572,7 +598,7 @@ __global__ __launch_bounds__(NT) void osr_bwd_small_kernel(BwdParams p) {
             acc = await_part(acc);
             if (mine) *reinterpret_cast<float4*>(tot + xu * W + xc4 * 4) = acc;
             __syncthreads();  // the sums over slots visible
-            finish(x, n, dcv, dkin);
+            finish(x, n, dcv, dkin, dZl);
             if (n > 0) x = xn;
         }
     }
@@ -593,6 +619,18 @@ static void launch_bwd_small_dec(const BwdParams& p, hipStream_t st) {
         const int nints = static_cast<int>(bwd_small_xchg_bytes(p.f.B, p.f.H, D, P, C) / sizeof(int));
         hipLaunchKernelGGL(osr_bwd_fill_ints<0>, dim3((nints + 255) / 256), dim3(256), 0, st,
                            reinterpret_cast<int*>(p.xbuf), nints);
+    }
+    // (the first linearisation is its own instantiation, at C <= 8 only)
+    if constexpr (C <= 8) {
+        if (p.f.lin1) {
+            if (p.f.mode == 0)
+                hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, true, P, CH, true>), grid, dim3(NT), 0,
+                                   st, p);
+            else
+                hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, false, P, false, true>), grid, dim3(NT),
+                                   0, st, p);
+            return;
+        }
     }
     if (p.f.mode == 0)
         hipLaunchKernelGGL((osr_bwd_small_kernel<M, D, NT, C, TIn, DYB, true, P, CH>), grid, dim3(NT), 0, st, p);

@@ -12,7 +12,7 @@ extern template int launch_bwd_small_m<64>(int, const BwdParams&, bool, hipStrea
 extern template int launch_bwd_small_m<128>(int, const BwdParams&, bool, hipStream_t);
 
 bool bwd_small_supported(int m, int d, int C, bool lin1) {
-    if (lin1) return false;
+    if (lin1 && C > 8) return false;  // (the first linearisation after the token loop only)
     switch (m) {
         case 16: return bwd_small_fits_m<16>(d, C);
         case 32: return bwd_small_fits_m<32>(d, C);

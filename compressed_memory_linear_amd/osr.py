@@ -349,14 +349,14 @@ def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_
 
 def lattice_osr_fwd_chunked_save(q, k, v, gamma, mu, state_in, chunk_size: int, *, mode: int = MODE_DEC,
                                  y_dtype=torch.float32, state_out=None, y=None, saved=None, stream=None,
-                                 chain_wgs: int = WGS_AUTO):
+                                 chain_wgs: int = WGS_AUTO, linearisation: int = LIN2):
     """The chunk-wise forward (small-chunk backward form only: C in 2, 4, 8)
     that also stores what lattice_osr_bwd_chunked_saved needs.  Returns (y,
     state_out, saved); saved is a uint8 tensor of
     lattice_osr_bwd_workspace_bytes bytes (allocated unless passed), to be
     passed as that call's `saved`."""
     lib = load_library()
-    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, chain_wgs=chain_wgs)
+    desc = _desc_from(q, k, v, gamma, mu, state_in, y_dtype, mode, linearisation, chain_wgs=chain_wgs)
     _check_outputs(desc, q, state_in, state_out, y, y_dtype)
     st = _launch_stream(stream)
     with torch.cuda.stream(st):
@@ -373,14 +373,14 @@ def lattice_osr_fwd_chunked_save(q, k, v, gamma, mu, state_in, chunk_size: int, 
 
 def lattice_osr_bwd_chunked_saved(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size: int, *, saved,
                                   mode: int = MODE_DEC, grads: Optional[dict] = None, stream=None,
-                                  chain_wgs: int = WGS_AUTO) -> dict:
+                                  chain_wgs: int = WGS_AUTO, linearisation: int = LIN2) -> dict:
     """lattice_osr_bwd_chunked's gradients, bit for bit, from the values a
     lattice_osr_fwd_chunked_save call with the same inputs stored in `saved`
     (its forward pass skipped)."""
     if saved is None:
         raise ValueError("saved: the tensor lattice_osr_fwd_chunked_save returned")
     return _bwd("lattice_osr_bwd_chunked_saved", q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size, mode,
-                grads, saved, stream, LIN2, chain_wgs, BWD_AUTO)
+                grads, saved, stream, linearisation, chain_wgs, BWD_AUTO)
 
 
 def _bwd(entry, q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_size, mode, grads, workspace, stream,

@@ -359,11 +359,9 @@ def test_bwd_null_pointers_and_shapes():
     assert _bwd_call(d, _bwd_ptrs(), 0) == osr.ERR_SHAPE
     d2 = osr.make_desc(1, 8, 1, 16, 48)
     assert _bwd_call(d2, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED
-    # (the first linearisation runs the general walk, whose workspace is that of
-    # the default linearisation on the general walk)
+    # (the linearisation does not change the workspace)
     d3 = osr.make_desc(1, 8, 1, 16, 16, linearisation=osr.LIN1)
-    assert osr.lattice_osr_bwd_workspace_bytes(d3, 4) == \
-        osr.lattice_osr_bwd_workspace_bytes(osr.make_desc(1, 8, 1, 16, 16, bwd_form=osr.BWD_WALK), 4)
+    assert osr.lattice_osr_bwd_workspace_bytes(d3, 4) == osr.lattice_osr_bwd_workspace_bytes(d, 4)
     d4 = osr.make_desc(1, 8, 1, 16, 16, linearisation=2)
     assert _bwd_call(d4, _bwd_ptrs(), 4) == osr.ERR_UNSUPPORTED
     with pytest.raises(osr.OSRError):
@@ -395,7 +393,7 @@ def test_bwd_form_choice():
 
 
 def test_bwd_small_chunk_form_workspace():
-    """The small-chunk reverse walk (automatic form, C in {2, 4, 8}, the default
+    """The small-chunk reverse walk (automatic form, C in {2, 4, 8}, either
     linearisation, at most 2 slot rows per thread of the token loop, C within
     its exchange batch) adds every token's h (fp32 [B*H][T][d]) to the
     workspace for the decoding objective, and, where the rows of a sequence
@@ -444,8 +442,12 @@ def test_bwd_small_chunk_form_workspace():
     for kw16 in (dict(in_dtype=osr.F32), dict(mode=osr.MODE_ENC)):
         kw = dict(B=2, T=64, H=3, m=64, d=64, **kw16)
         assert ws(16, **kw) == ws(16, osr.BWD_WALK, **kw), kw16
+    # the first linearisation takes the same form below C = 16 (not at 16)
+    for C in (2, 4, 8):
+        kw = dict(B=2, T=64, H=3, m=64, d=64)
+        assert ws(C, linearisation=osr.LIN1, **kw) == ws(C, **kw), C
     general = [dict(C=8, m=64, d=128), dict(C=4, m=128, d=128), dict(C=8, m=32, d=128), dict(C=32, m=64, d=64),
-               dict(C=1, m=64, d=64), dict(C=4, m=64, d=64, linearisation=osr.LIN1)]
+               dict(C=1, m=64, d=64), dict(C=16, m=64, d=64, linearisation=osr.LIN1)]
     for g in general:
         kw = dict(B=2, T=64, H=3)
         kw.update(g)
@@ -475,12 +477,12 @@ def _bwd_saved_call(d, ptrs, chunk, ws=None, ws_bytes=None):
 
 def test_saved_training_pair_rules():
     """lattice_osr_fwd_chunked_save and lattice_osr_bwd_chunked_saved exist only
-    where the backward takes its small-chunk form (C in 2, 4, 8, BWD_AUTO, the
-    default linearisation, C within the token loop's batch, at most 2 slot rows
-    per thread on 1, 2 or 4 workgroups): UNSUPPORTED elsewhere; null pointers, a
+    where the backward takes its small-chunk form at C in 2, 4, 8 (BWD_AUTO, C
+    within the token loop's batch, at most 2 slot rows per thread on 1, 2 or 4
+    workgroups; either linearisation): UNSUPPORTED elsewhere; null pointers, a
     short saved buffer and misalignment are refused before anything runs."""
     ok = dict(B=1, T=64, H=2, m=64, d=64)
-    for C, kw in ((16, {}), (1, {}), (4, dict(linearisation=osr.LIN1)), (4, dict(bwd_form=osr.BWD_WALK)),
+    for C, kw in ((16, {}), (1, {}), (16, dict(linearisation=osr.LIN1)), (4, dict(bwd_form=osr.BWD_WALK)),
                   (4, dict(m=128, d=128)), (8, dict(m=32, d=128))):
         d = osr.make_desc(**dict(ok, **{k: v for k, v in kw.items() if k in ("m", "d")}),
                           **{k: v for k, v in kw.items() if k not in ("m", "d")})

@@ -62,13 +62,14 @@ def _upstream(inp, seed, dy_bf16=False):
     return dy, dso
 
 
-def _gpu_bwd(inp, dy, dso, C, mode, form, dy_bf16=False, wgs=osr.WGS_AUTO):
+def _gpu_bwd(inp, dy, dso, C, mode, form, dy_bf16=False, wgs=osr.WGS_AUTO, lin=osr.LIN2):
     t = osr.to_device(inp, "cuda")
     dyt = torch.from_numpy(dy).cuda()
     if dy_bf16:
         dyt = dyt.to(torch.bfloat16)  # exact: dy already holds bf16 values
     g = osr.lattice_osr_bwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], dyt,
-                                    torch.from_numpy(dso).cuda(), C, mode=mode, bwd_form=form, chain_wgs=wgs)
+                                    torch.from_numpy(dso).cuda(), C, mode=mode, bwd_form=form, chain_wgs=wgs,
+                                    linearisation=lin)
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in g.items()}
 
@@ -178,6 +179,26 @@ def test_small_chunk_backward_many_sequences(B, H, m, d, C):
     _report_and_check("vs oracle (2 sequences)", errs, TOL[synth.BF16])
 
 
+# The first chunk linearisation (eq. recurrence_linear1) in the same form:
+# (B, T, H, m, d, C, in dtype, per-slot gamma, objective) over one, two and four
+# workgroups (its encoding layer: the stated short case of test_backward_gpu.py,
+# C4 T8 seed 23, which takes this form too)
+LIN1_CASES = [(1, 64, 2, 16, 32, 4, synth.F32, True, osr.MODE_DEC), (2, 64, 2, 64, 64, 4, synth.BF16, True, osr.MODE_DEC),
+              (1, 64, 2, 64, 64, 8, synth.BF16, False, osr.MODE_SIM), (1, 64, 3, 32, 32, 2, synth.F32, False, osr.MODE_DEC)]
+
+
+@pytest.mark.parametrize("B,T,H,m,d,C,dt,per_slot,mode", LIN1_CASES)
+def test_small_chunk_backward_first_linearisation(B, T, H, m, d, C, dt, per_slot, mode):
+    _say(f"bwd small-chunk LIN1 B{B} T{T} H{H} m{m} d{d} C{C} mode{mode} per_slot{per_slot}")
+    inp = synth.make_inputs(B, T, H, m, d, seed=59, in_dtype=dt, gamma_per_slot=per_slot)
+    dy, dso = _upstream(inp, 59)
+    got = _gpu_bwd(inp, dy, dso, C, mode, osr.BWD_AUTO, lin=osr.LIN1)
+    ref = ob.osr_backward(*inp.values_f64(), dy, dso, chunk_size=C, mode=mode, linearisation=ob.LIN1)
+    _report_and_check("vs oracle", _errs(got, ref), TOL[dt])
+    walk = _gpu_bwd(inp, dy, dso, C, mode, osr.BWD_WALK, lin=osr.LIN1)
+    _report_and_check("vs general walk", _errs(got, walk), AGREE)
+
+
 def test_small_chunk_backward_deterministic():
     _say("bwd small-chunk determinism B2 T128 H2 m64 d64 C4 bf16")
     inp = synth.make_inputs(2, 128, 2, 64, 64, seed=37, in_dtype=synth.BF16)
@@ -213,8 +234,9 @@ SAVED_CASES = [(2, 64, 3, 64, 64, 4, synth.BF16, osr.MODE_DEC, False), (1, 64, 2
                (1, 16, 2, 32, 32, 4, synth.F32, osr.MODE_ENC, False), (1, 32, 2, 128, 128, 2, synth.BF16, osr.MODE_DEC, False)]
 
 
+@pytest.mark.parametrize("lin", [osr.LIN2, osr.LIN1])
 @pytest.mark.parametrize("B,T,H,m,d,C,dt,mode,bf16_out", SAVED_CASES)
-def test_saved_training_pair(B, T, H, m, d, C, dt, mode, bf16_out):
+def test_saved_training_pair(B, T, H, m, d, C, dt, mode, bf16_out, lin):
     """lattice_osr_fwd_chunked_save returns lattice_osr_fwd_chunked's y and
     state_out bit for bit, and lattice_osr_bwd_chunked_saved, from what it
     stored, lattice_osr_bwd_chunked's gradients bit for bit (the same kernels
@@ -225,19 +247,19 @@ def test_saved_training_pair(B, T, H, m, d, C, dt, mode, bf16_out):
     t = osr.to_device(inp, "cuda")
     ydt = torch.bfloat16 if bf16_out else torch.float32
     y0, s0 = osr.lattice_osr_fwd_chunked(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], C, mode=mode,
-                                         y_dtype=ydt)
+                                         y_dtype=ydt, linearisation=lin)
     y1, s1, saved = osr.lattice_osr_fwd_chunked_save(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], C,
-                                                     mode=mode, y_dtype=ydt)
+                                                     mode=mode, y_dtype=ydt, linearisation=lin)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1) and torch.equal(s0, s1)
-    ref = _gpu_bwd(inp, dy, dso, C, mode, osr.BWD_AUTO, dy_bf16=bf16_out)
+    ref = _gpu_bwd(inp, dy, dso, C, mode, osr.BWD_AUTO, dy_bf16=bf16_out, lin=lin)
     dyt = torch.from_numpy(dy).cuda()
     if bf16_out:
         dyt = dyt.to(torch.bfloat16)
     dsot = torch.from_numpy(dso).cuda()
     for rep in range(2):
         g = osr.lattice_osr_bwd_chunked_saved(t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"], dyt, dsot, C,
-                                              saved=saved, mode=mode)
+                                              saved=saved, mode=mode, linearisation=lin)
         torch.cuda.synchronize()
         for key in KEYS:
             assert np.array_equal(g[key].cpu().numpy(), ref[key]), (rep, key)
