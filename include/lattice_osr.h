@@ -300,10 +300,10 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * rounding (the token walk's to 1e-4 of RMS; with forget gates mu near 0 the
  * tile's gate products span many decades and the two agree to 5e-3).
  *
- * Small chunks: with desc->bwd_form AUTO and the default linearisation, at
- * chunk_size 2, 4 or 8 (at most 4 at d = 128 and at m d = 8192, 2 at
- * m = d = 128) and at chunk_size 16 on the state-passing path above, where
- * a chunk fits, a reverse walk that keeps each chunk's per-token states in
+ * Small chunks: with desc->bwd_form AUTO, at chunk_size 2, 4 or 8 (at most
+ * 4 at d = 128 and at m d = 8192, 2 at m = d = 128; either linearisation)
+ * and at chunk_size 16 on the state-passing path above (the default
+ * linearisation), where a chunk fits, a reverse walk that keeps each chunk's per-token states in
  * registers runs after a forward pass that stores the chunk-start states
  * (at chunk_size 16 the state-passing kernel's pass, which also supplies h;
  * below 16 the token loop's, and for the decoding objective every token's h
