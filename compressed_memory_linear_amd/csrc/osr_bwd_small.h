@@ -689,23 +689,12 @@ static int launch_bwd_small_mdc(const BwdParams& p, bool in_bf16, hipStream_t st
 }
 
 template <int M, int D>
-static int launch_bwd_small_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
+int launch_bwd_small_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
     switch (p.f.chunk) {
         case 2: return launch_bwd_small_mdc<M, D, 2>(p, in_bf16, st);
         case 4: return launch_bwd_small_mdc<M, D, 4>(p, in_bf16, st);
         case 8: return launch_bwd_small_mdc<M, D, 8>(p, in_bf16, st);
         case 16: return launch_bwd_small_mdc<M, D, 16>(p, in_bf16, st);
-        default: return -3;
-    }
-}
-
-template <int M>
-int launch_bwd_small_m(int d, const BwdParams& p, bool in_bf16, hipStream_t st) {
-    switch (d) {
-        case 16: return launch_bwd_small_md<M, 16>(p, in_bf16, st);
-        case 32: return launch_bwd_small_md<M, 32>(p, in_bf16, st);
-        case 64: return launch_bwd_small_md<M, 64>(p, in_bf16, st);
-        case 128: return launch_bwd_small_md<M, 128>(p, in_bf16, st);
         default: return -3;
     }
 }

@@ -4,12 +4,26 @@
 
 namespace osr {
 
+// (one translation unit per (m, d): osr_bwd_small_m<M>_d<D>.hip)
+#define OSR_SMALL_EXTERN(M, D) extern template int launch_bwd_small_md<M, D>(const BwdParams&, bool, hipStream_t);
+#define OSR_SMALL_EXTERN_M(M) OSR_SMALL_EXTERN(M, 16) OSR_SMALL_EXTERN(M, 32) OSR_SMALL_EXTERN(M, 64) OSR_SMALL_EXTERN(M, 128)
+OSR_SMALL_EXTERN_M(16)
+OSR_SMALL_EXTERN_M(32)
+OSR_SMALL_EXTERN_M(64)
+OSR_SMALL_EXTERN_M(128)
+#undef OSR_SMALL_EXTERN_M
+#undef OSR_SMALL_EXTERN
+
 template <int M>
-int launch_bwd_small_m(int d, const BwdParams& p, bool in_bf16, hipStream_t st);
-extern template int launch_bwd_small_m<16>(int, const BwdParams&, bool, hipStream_t);
-extern template int launch_bwd_small_m<32>(int, const BwdParams&, bool, hipStream_t);
-extern template int launch_bwd_small_m<64>(int, const BwdParams&, bool, hipStream_t);
-extern template int launch_bwd_small_m<128>(int, const BwdParams&, bool, hipStream_t);
+static int launch_bwd_small_m(int d, const BwdParams& p, bool in_bf16, hipStream_t st) {
+    switch (d) {
+        case 16: return launch_bwd_small_md<M, 16>(p, in_bf16, st);
+        case 32: return launch_bwd_small_md<M, 32>(p, in_bf16, st);
+        case 64: return launch_bwd_small_md<M, 64>(p, in_bf16, st);
+        case 128: return launch_bwd_small_md<M, 128>(p, in_bf16, st);
+        default: return -3;
+    }
+}
 
 bool bwd_small_supported(int m, int d, int C, bool lin1) {
     if (lin1 && C > 8) return false;  // (the first linearisation after the token loop only)
