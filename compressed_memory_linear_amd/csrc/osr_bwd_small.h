@@ -69,8 +69,9 @@ constexpr bool bwd_small_split_ok() {
 template <int M, int D>
 constexpr bool bwd_small_fits(int C) {
     using L = ValuLayout<M, D, tokenloop_threads<M, D>()>;
-    if (!(((C == 2 || C == 4 || C == 8) && C <= TokBatch<L>::BT) || C == 16)) return false;
+    if (!(((C == 1 || C == 2 || C == 4 || C == 8) && C <= TokBatch<L>::BT) || C == 16)) return false;
     switch (C) {
+        case 1: return bwd_small_split_ok<M, D, 1, 1>() || bwd_small_split_ok<M, D, 1, 2>() || bwd_small_split_ok<M, D, 1, 4>();
         case 2: return bwd_small_split_ok<M, D, 2, 1>() || bwd_small_split_ok<M, D, 2, 2>() || bwd_small_split_ok<M, D, 2, 4>();
         case 4: return bwd_small_split_ok<M, D, 4, 1>() || bwd_small_split_ok<M, D, 4, 2>() || bwd_small_split_ok<M, D, 4, 4>();
         case 8: return bwd_small_split_ok<M, D, 8, 1>() || bwd_small_split_ok<M, D, 8, 2>() || bwd_small_split_ok<M, D, 8, 4>();
@@ -691,6 +692,7 @@ static int launch_bwd_small_mdc(const BwdParams& p, bool in_bf16, hipStream_t st
 template <int M, int D>
 int launch_bwd_small_md(const BwdParams& p, bool in_bf16, hipStream_t st) {
     switch (p.f.chunk) {
+        case 1: return launch_bwd_small_mdc<M, D, 1>(p, in_bf16, st);
         case 2: return launch_bwd_small_mdc<M, D, 2>(p, in_bf16, st);
         case 4: return launch_bwd_small_mdc<M, D, 4>(p, in_bf16, st);
         case 8: return launch_bwd_small_mdc<M, D, 8>(p, in_bf16, st);
@@ -707,6 +709,7 @@ bool bwd_small_split_ok_md(int C, int P) {
                (P == 4 && bwd_small_split_ok<M, D, CV, 4>());
     };
     switch (C) {
+        case 1: return ok(std::integral_constant<int, 1>{});
         case 2: return ok(std::integral_constant<int, 2>{});
         case 4: return ok(std::integral_constant<int, 4>{});
         case 8: return ok(std::integral_constant<int, 8>{});

@@ -13,6 +13,9 @@ namespace osr {
 // Otherwise the token-by-token forward with chunk size p.chunk (1 = exact).
 // Returns 0, -3 (unsupported m/d) or -5 (launch error).
 int launch_valu(bool decode, int m, int d, const Params& p, bool in_bf16, hipStream_t st);
+// The small-chunk token loop alone, at C in {1, 2, 4, 8} within its read-out
+// batch (the backward's phase 1 and the saving forward); -3 elsewhere.
+int launch_tokenloop_small(int m, int d, const Params& p, bool in_bf16, hipStream_t st);
 
 // MFMA chunk path (bf16 inputs): whether (m, d, C) has a built variant, the
 // workspace it needs, and the launch of the inter-chunk state-passing kernel

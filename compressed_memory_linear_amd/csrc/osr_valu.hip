@@ -439,7 +439,9 @@ static size_t tokenloop_dyn_lds(int C) {
 
 // ----------------------------------------------------------------- launch --
 template <int M, int D>
-static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_t st) {
+// small_only: the small-chunk loop at C in {1, 2, 4, 8} (the backward's phase 1,
+// which stores the chunk-start states), or -3 where it does not apply.
+static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_t st, bool small_only = false) {
     constexpr int TPR = D / 4;
     // Decode: up to 8 waves per state (fewer rows per thread: ~100 VGPRs, 4 waves per SIMD), which
     // shortens each workgroup's arithmetic between its state load and store; measured 9% faster
@@ -456,7 +458,7 @@ static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_
         // small chunks that fit one exchange batch: the batched loop
         constexpr int BT = TokBatch<ValuLayout<M, D, NT_TOK>>::BT;
         const int C = p.chunk;
-        if ((C == 2 || C == 4 || C == 8) && C <= BT) {
+        if ((C == 2 || C == 4 || C == 8 || (small_only && C == 1)) && C <= BT) {
             using L = ValuLayout<M, D, NT_TOK>;
             const size_t lds = (2 * static_cast<size_t>(C) * D + 2 * BT * L::NW * (D + 4)) * sizeof(float);
             auto go = [&](auto cb) {
@@ -470,7 +472,9 @@ static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_
                                            st, p);
                 }
             };
-            if (C == 2)
+            if (C == 1)
+                go(std::integral_constant<int, 1>{});
+            else if (C == 2)
                 go(std::integral_constant<int, 2>{});
             else if (C == 4)
                 go(std::integral_constant<int, 4>{});
@@ -478,6 +482,7 @@ static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_
                 go(std::integral_constant<int, 8>{});
             return hipGetLastError() == hipSuccess ? 0 : -5;
         }
+        if (small_only) return -3;
         const size_t lds = tokenloop_dyn_lds<M, D, NT_TOK>(p.chunk) * sizeof(float);
         if (in_bf16)
             hipLaunchKernelGGL((osr_tokenloop_kernel<M, D, NT_TOK, uint16_t>), grid, dim3(NT_TOK), lds, st, p);
@@ -488,12 +493,12 @@ static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_
 }
 
 template <int M>
-static int launch_valu_m(bool decode, int d, const Params& p, bool in_bf16, hipStream_t st) {
+static int launch_valu_m(bool decode, int d, const Params& p, bool in_bf16, hipStream_t st, bool small_only = false) {
     switch (d) {
-        case 16: return launch_valu_md<M, 16>(decode, p, in_bf16, st);
-        case 32: return launch_valu_md<M, 32>(decode, p, in_bf16, st);
-        case 64: return launch_valu_md<M, 64>(decode, p, in_bf16, st);
-        case 128: return launch_valu_md<M, 128>(decode, p, in_bf16, st);
+        case 16: return launch_valu_md<M, 16>(decode, p, in_bf16, st, small_only);
+        case 32: return launch_valu_md<M, 32>(decode, p, in_bf16, st, small_only);
+        case 64: return launch_valu_md<M, 64>(decode, p, in_bf16, st, small_only);
+        case 128: return launch_valu_md<M, 128>(decode, p, in_bf16, st, small_only);
         default: return -3;
     }
 }
@@ -504,6 +509,16 @@ int launch_valu(bool decode, int m, int d, const Params& p, bool in_bf16, hipStr
         case 32: return launch_valu_m<32>(decode, d, p, in_bf16, st);
         case 64: return launch_valu_m<64>(decode, d, p, in_bf16, st);
         case 128: return launch_valu_m<128>(decode, d, p, in_bf16, st);
+        default: return -3;
+    }
+}
+
+int launch_tokenloop_small(int m, int d, const Params& p, bool in_bf16, hipStream_t st) {
+    switch (m) {
+        case 16: return launch_valu_m<16>(false, d, p, in_bf16, st, true);
+        case 32: return launch_valu_m<32>(false, d, p, in_bf16, st, true);
+        case 64: return launch_valu_m<64>(false, d, p, in_bf16, st, true);
+        case 128: return launch_valu_m<128>(false, d, p, in_bf16, st, true);
         default: return -3;
     }
 }

@@ -300,8 +300,8 @@ LATTICE_OSR_API size_t lattice_osr_workspace_bytes(const lattice_osr_desc* desc,
  * rounding (the token walk's to 1e-4 of RMS; with forget gates mu near 0 the
  * tile's gate products span many decades and the two agree to 5e-3).
  *
- * Small chunks: with desc->bwd_form AUTO, at chunk_size 2, 4 or 8 (at most
- * 4 at d = 128 and at m d = 8192, 2 at m = d = 128; either linearisation)
+ * Small chunks: with desc->bwd_form AUTO, at chunk_size 1, 2, 4 or 8 (at
+ * most 4 at d = 128 and at m d = 8192, 2 at m = d = 128; either linearisation)
  * and at chunk_size 16 on the state-passing path above (the default
  * linearisation), where a chunk fits, a reverse walk that keeps each chunk's per-token states in
  * registers runs after a forward pass that stores the chunk-start states
@@ -336,8 +336,9 @@ LATTICE_OSR_API size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* d
 
 /*
  * Training at small chunks without the backward's forward pass.  Where the
- * backward takes its small-chunk form at chunk_size 2, 4 or 8 (above;
- * elsewhere both calls return LATTICE_OSR_ERR_UNSUPPORTED):
+ * backward takes its small-chunk form at chunk_size 2, 4 or 8 (above; not at
+ * 1, where the forward is another kernel; elsewhere both calls return
+ * LATTICE_OSR_ERR_UNSUPPORTED):
  *
  * lattice_osr_fwd_chunked_save computes y and state_out exactly as
  * lattice_osr_fwd_chunked does (the same kernel, bit for bit; arguments and

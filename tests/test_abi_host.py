@@ -300,7 +300,8 @@ def _bwd_call(d, ptrs, chunk, ws=None, ws_bytes=None):
 
 def test_bwd_workspace_formula():
     """Per (b,h): 4 (T/C + 1 + C) m d bytes of states and 4 C (2m + 4)
-    bytes of per-token values; with bf16 inputs and C >= 16 (not the encoding
+    bytes of per-token values; at C <= 8 with the decoding objective every
+    token's h (4 T d bytes, the small-chunk form); with bf16 inputs and C >= 16 (not the encoding
     layer) also the state-passing kernel's per-chunk arrays, 4 (m d + 2 m C +
     d C) bytes per chunk (one more m C with the first linearisation), and the
     c, beta and |h|^2 it keeps for the backward, 4 (2 m C + C) per chunk."""
@@ -311,6 +312,8 @@ def test_bwd_workspace_formula():
                     d = osr.make_desc(B, T, H, m, dd, in_dtype=in_dtype, mode=mode, linearisation=lin)
                     per = 4 * ((T // C + 1 + C) * m * dd + C * (2 * m + 4))
                     want = B * H * per
+                    if C <= 8 and mode == osr.MODE_DEC:
+                        want += B * H * T * dd * 4  # every token's h (the small-chunk form)
                     if in_dtype == osr.BF16 and C >= 16 and mode != osr.MODE_ENC:
                         per_chunk = m * dd + (3 if lin == osr.LIN1 else 2) * m * C + dd * C
                         per_chunk += 2 * m * C + C  # c, beta and |h|^2 kept for the backward
@@ -402,7 +405,7 @@ def test_bwd_small_chunk_form_workspace():
     def ws(C, form=osr.BWD_AUTO, **kw):
         return osr.lattice_osr_bwd_workspace_bytes(osr.make_desc(**kw, bwd_form=form), C)
 
-    applies = [(2, 16, 16), (4, 64, 64), (8, 64, 64), (4, 32, 128), (8, 128, 16), (2, 128, 32)]
+    applies = [(2, 16, 16), (4, 64, 64), (8, 64, 64), (4, 32, 128), (8, 128, 16), (2, 128, 32), (1, 64, 64)]
     for C, m, d in applies:
         kw = dict(B=2, T=64, H=3, m=m, d=d)
         # from m = 32 and C = 4 the rows of a sequence split over P workgroups (B*H*P <= 256):
@@ -447,7 +450,7 @@ def test_bwd_small_chunk_form_workspace():
         kw = dict(B=2, T=64, H=3, m=64, d=64)
         assert ws(C, linearisation=osr.LIN1, **kw) == ws(C, **kw), C
     general = [dict(C=8, m=64, d=128), dict(C=4, m=128, d=128), dict(C=8, m=32, d=128), dict(C=32, m=64, d=64),
-               dict(C=1, m=64, d=64), dict(C=16, m=64, d=64, linearisation=osr.LIN1)]
+               dict(C=16, m=64, d=64, linearisation=osr.LIN1)]
     for g in general:
         kw = dict(B=2, T=64, H=3)
         kw.update(g)

@@ -114,6 +114,9 @@ CASES = [
     (2, 64, 2, 64, 128, 4, synth.BF16, True, osr.MODE_DEC, False),
     (1, 64, 2, 128, 64, 2, synth.F32, False, osr.MODE_SIM, True),
     (1, 32, 2, 128, 128, 2, synth.BF16, True, osr.MODE_DEC, False),
+    # C = 1: the exact recurrence (a projection after every token)
+    (1, 64, 2, 64, 64, 1, synth.BF16, True, osr.MODE_DEC, False),
+    (1, 32, 2, 16, 32, 1, synth.F32, False, osr.MODE_SIM, True),
     # per-token gamma with the rows split (its gradient travels in the exchanged sums)
     (2, 64, 2, 64, 64, 4, synth.BF16, False, osr.MODE_DEC, False),
     (1, 64, 2, 64, 64, 8, synth.F32, False, osr.MODE_SIM, False),
