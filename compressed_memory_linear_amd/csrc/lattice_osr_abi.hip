@@ -461,8 +461,7 @@ int bwd_chunked_impl(const lattice_osr_desc* desc, int32_t chunk_size, const voi
                      float* dstate_in, void* workspace, size_t workspace_bytes, void* hip_stream, bool saved) {
     int rc = check_bwd_desc(desc, chunk_size);
     if (rc) return rc;
-    if (saved && (chunk_size > 8 || chunk_size < 2 || !bwd_small_form(desc, chunk_size)))
-        return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (saved && (chunk_size > 8 || !bwd_small_form(desc, chunk_size))) return LATTICE_OSR_ERR_UNSUPPORTED;
     const size_t need = bwd_workspace_needed(desc, chunk_size);
     rc = check_bwd_buffers(desc, q, k, v, gamma, mu, state_in, dy, dstate_out, dq, dk, dv, dgamma, dmu,
                            dstate_in, workspace, workspace_bytes, need);
@@ -602,8 +601,7 @@ int lattice_osr_fwd_chunked_save(const lattice_osr_desc* desc, int32_t chunk_siz
                                  void* hip_stream) {
     int rc = check_bwd_desc(desc, chunk_size);
     if (rc) return rc;
-    // (C = 1: lattice_osr_fwd_chunked runs another kernel there, so no bit-equal saving forward)
-    if (chunk_size > 8 || chunk_size < 2 || !bwd_small_form(desc, chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
+    if (chunk_size > 8 || !bwd_small_form(desc, chunk_size)) return LATTICE_OSR_ERR_UNSUPPORTED;
     const size_t need = bwd_workspace_needed(desc, chunk_size);
     rc = check_buffers(desc, q, k, v, gamma, mu, state_in, state_out, y, bwd_workspace, bwd_workspace_bytes, need);
     if (rc) return rc;

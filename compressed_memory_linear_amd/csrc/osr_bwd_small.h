@@ -1,4 +1,5 @@
-// osr_bwd_small.h -- reverse walk of the backward at small chunks (C = 2, 4, 8).
+// osr_bwd_small.h -- reverse walk of the backward at small chunks (C = 1, 2, 4, 8
+// after the token loop, 16 after the matrix-core state passing).
 //
 // Method: "Lattice: Learning to Efficiently Compress the Memory" (arXiv
 // 2504.05646), section "Parallel and Hardware Efficient Form", eq.

@@ -85,7 +85,7 @@ int launch_bwd(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
 // the workspace (states_ready).  Same workspace layout as launch_bwd.
 bool bwd_chunk_supported(int m, int d, int C, bool in_bf16, bool lin1, int mode);
 int launch_bwd_chunk(int m, int d, const BwdParams& p, bool in_bf16, hipStream_t st);
-// The reverse walk at small chunks (osr_bwd_small.hip): C in {2, 4, 8} within
+// The reverse walk at small chunks (osr_bwd_small.hip): C in {1, 2, 4, 8} within
 // the token loop's batch, the default linearisation, and at most 2 slot rows per
 // thread on 1, 2 or 4 workgroups per sequence (bwd_small_min_p).
 // Its phase 1 is the forward's small-chunk token loop with raw (and, decoding

@@ -1,6 +1,7 @@
 // osr_valu.hip -- VALU (fp32) OSR kernels for gfx950: the fused single-token
 // decode step and the token-by-token forward (exact recurrence at C = 1, the
-// chunk-linearised recurrence at C > 1).
+// chunk-linearised recurrence at C > 1): a batched loop for chunks of 1, 2, 4
+// or 8 tokens within one read-out batch, a general loop for the other sizes.
 //
 // Method: "Lattice: Learning to Efficiently Compress the Memory" (arXiv
 // 2504.05646).  Per token, with Z the unit-projected chunk-start state
@@ -120,21 +121,19 @@ __global__ __launch_bounds__(NT) void osr_decode_kernel(Params p) {
 // BT tokens one barrier lets the threads add them up (one float4 of the batch
 // each) and store y.  With C > 1, h depends only on the chunk-start state and
 // the inputs, so the chunk's h is formed up front in LDS (chunk_h) and a token
-// needs no exchange across waves at all; with C = 1 h is summed over slots per
-// token (col_sum).
+// needs no exchange across waves at all.  This loop takes the chunk sizes the
+// small-chunk loop below does not (C > 1 always: C = 1 is a small chunk).
 template <int M, int D, int NT, typename TIn>
 __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
     using L = ValuLayout<M, D, NT>;
     constexpr int BT = TokBatch<L>::BT, W = D + 4, Q = D / 4;
     static_assert(BT * Q <= NT, "one float4 of a batch's read-outs per thread");
-    // With C > 1 the chunk's h and chunk_h's exchange buffers sit in dynamic
-    // LDS (tokenloop_dyn_lds floats); with C = 1 there is none, so several
-    // workgroups can share a CU.
+    // The chunk's h and chunk_h's exchange buffers sit in dynamic LDS
+    // (tokenloop_dyn_lds floats).
     extern __shared__ __attribute__((aligned(16))) float dyn[];
     float* hbuf = dyn;                   // [C][D]
     float* redc = dyn + p.chunk * D;     // [2][BT][NW][W]
     __shared__ __attribute__((aligned(16))) float redy[2 * BT * L::NW * W];  // y batches
-    __shared__ __attribute__((aligned(16))) float redh[2][L::NW * D];        // h at C = 1
     const int bh = blockIdx.x;
     const int b = bh / p.H, hd = bh % p.H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -159,27 +158,14 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
             project_rows<L>(s);
 #pragma unroll
             for (int i = 0; i < L::RPT; ++i) z[i] = s[i];
-            if (C > 1) {
-                __syncthreads();  // every thread is done with the previous chunk's h
-                chunk_h<L, M, D, TIn>(z, p, bth_of(t), tstride, C, p.mode, hbuf, redc, nredc, tid, lane, wave,
-                                      rg, cg);
-            }
+            __syncthreads();  // every thread is done with the previous chunk's h
+            chunk_h<L, M, D, TIn>(z, p, bth_of(t), tstride, C, p.mode, hbuf, redc, nredc, tid, lane, wave, rg, cg);
         }
         // unconditional (the last token loads itself again): a load under a branch
         // is waited for where the branch joins, which would undo the prefetch
         load_token<L, M, D, TIn>(nxt, p, bth_of(t + 1 < T ? t + 1 : t), rg, cg);
 
-        float4 h;
-        if (C > 1) {
-            h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
-        } else if (p.mode == 0) {
-            float4 hp = f4(0.f);
-#pragma unroll
-            for (int i = 0; i < L::RPT; ++i) hp = fma4(cur.k[i], z[i], hp);
-            h = col_sum<L, D>(hp, redh[t & 1], lane, wave, cg) - cur.v;
-        } else {
-            h = p.mode == 2 ? cur.v : f4(0.f) - cur.v;
-        }
+        const float4 h = *reinterpret_cast<const float4*>(hbuf + tau * D + cg * 4);
         float cc[L::RPT + 1];
 #pragma unroll
         for (int i = 0; i < L::RPT; ++i) cc[i] = dot4(z[i], h);
@@ -237,7 +223,7 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_kernel(Params p) {
         *reinterpret_cast<float4*>(sout + (rg + L::RG * i) * D + cg * 4) = s[i];
 }
 
-// Token loop for small chunks (C = CB in {2, 4, 8}, at most one batch of
+// Token loop for small chunks (C = CB in {1, 2, 4, 8}, at most one batch of
 // the y exchange).  Per chunk: the chunk's h over slots once (as chunk_h),
 // then c, |h|^2 and the gates of all CB tokens together (CB (RPT + 1)
 // independent row sums instead of RPT + 1 per token), then the CB tokens'
@@ -430,11 +416,11 @@ __global__ __launch_bounds__(NT) void osr_tokenloop_small_kernel(Params p) {
     for (int i = 0; i < RPT; ++i) *reinterpret_cast<float4*>(sout + (rg + L::RG * i) * D + cg * 4) = s[i];
 }
 
-// Dynamic LDS of the token loop (floats): C > 1 only.
+// Dynamic LDS of the general token loop (floats).
 template <int M, int D, int NT>
 static size_t tokenloop_dyn_lds(int C) {
     using L = ValuLayout<M, D, NT>;
-    return C > 1 ? static_cast<size_t>(C) * D + 2 * TokBatch<L>::BT * L::NW * (D + 4) : 0;
+    return static_cast<size_t>(C) * D + 2 * TokBatch<L>::BT * L::NW * (D + 4);
 }
 
 // ----------------------------------------------------------------- launch --
@@ -458,7 +444,7 @@ static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_
         // small chunks that fit one exchange batch: the batched loop
         constexpr int BT = TokBatch<ValuLayout<M, D, NT_TOK>>::BT;
         const int C = p.chunk;
-        if ((C == 2 || C == 4 || C == 8 || (small_only && C == 1)) && C <= BT) {
+        if ((C == 1 || C == 2 || C == 4 || C == 8) && C <= BT) {
             using L = ValuLayout<M, D, NT_TOK>;
             const size_t lds = (2 * static_cast<size_t>(C) * D + 2 * BT * L::NW * (D + 4)) * sizeof(float);
             auto go = [&](auto cb) {
@@ -482,7 +468,7 @@ static int launch_valu_md(bool decode, const Params& p, bool in_bf16, hipStream_
                 go(std::integral_constant<int, 8>{});
             return hipGetLastError() == hipSuccess ? 0 : -5;
         }
-        if (small_only) return -3;
+        if (small_only || C < 2) return -3;
         const size_t lds = tokenloop_dyn_lds<M, D, NT_TOK>(p.chunk) * sizeof(float);
         if (in_bf16)
             hipLaunchKernelGGL((osr_tokenloop_kernel<M, D, NT_TOK, uint16_t>), grid, dim3(NT_TOK), lds, st, p);

@@ -350,7 +350,7 @@ def lattice_osr_bwd_chunked(q, k, v, gamma, mu, state_in, dy, dstate_out, chunk_
 def lattice_osr_fwd_chunked_save(q, k, v, gamma, mu, state_in, chunk_size: int, *, mode: int = MODE_DEC,
                                  y_dtype=torch.float32, state_out=None, y=None, saved=None, stream=None,
                                  chain_wgs: int = WGS_AUTO, linearisation: int = LIN2):
-    """The chunk-wise forward (small-chunk backward form only: C in 2, 4, 8)
+    """The chunk-wise forward (small-chunk backward form only: C in 1, 2, 4, 8)
     that also stores what lattice_osr_bwd_chunked_saved needs.  Returns (y,
     state_out, saved); saved is a uint8 tensor of
     lattice_osr_bwd_workspace_bytes bytes (allocated unless passed), to be

@@ -336,9 +336,8 @@ LATTICE_OSR_API size_t lattice_osr_bwd_workspace_bytes(const lattice_osr_desc* d
 
 /*
  * Training at small chunks without the backward's forward pass.  Where the
- * backward takes its small-chunk form at chunk_size 2, 4 or 8 (above; not at
- * 1, where the forward is another kernel; elsewhere both calls return
- * LATTICE_OSR_ERR_UNSUPPORTED):
+ * backward takes its small-chunk form at chunk_size 1, 2, 4 or 8 (above;
+ * elsewhere both calls return LATTICE_OSR_ERR_UNSUPPORTED):
  *
  * lattice_osr_fwd_chunked_save computes y and state_out exactly as
  * lattice_osr_fwd_chunked does (the same kernel, bit for bit; arguments and

@@ -480,12 +480,12 @@ def _bwd_saved_call(d, ptrs, chunk, ws=None, ws_bytes=None):
 
 def test_saved_training_pair_rules():
     """lattice_osr_fwd_chunked_save and lattice_osr_bwd_chunked_saved exist only
-    where the backward takes its small-chunk form at C in 2, 4, 8 (BWD_AUTO, C
+    where the backward takes its small-chunk form at C in 1, 2, 4, 8 (BWD_AUTO, C
     within the token loop's batch, at most 2 slot rows per thread on 1, 2 or 4
     workgroups; either linearisation): UNSUPPORTED elsewhere; null pointers, a
     short saved buffer and misalignment are refused before anything runs."""
     ok = dict(B=1, T=64, H=2, m=64, d=64)
-    for C, kw in ((16, {}), (1, {}), (16, dict(linearisation=osr.LIN1)), (4, dict(bwd_form=osr.BWD_WALK)),
+    for C, kw in ((16, {}), (16, dict(linearisation=osr.LIN1)), (4, dict(bwd_form=osr.BWD_WALK)),
                   (4, dict(m=128, d=128)), (8, dict(m=32, d=128))):
         d = osr.make_desc(**dict(ok, **{k: v for k, v in kw.items() if k in ("m", "d")}),
                           **{k: v for k, v in kw.items() if k not in ("m", "d")})

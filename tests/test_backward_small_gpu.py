@@ -1,4 +1,4 @@
-"""GPU parity of the backward at small chunks (C = 2, 4, 8, and 16 with bf16
+"""GPU parity of the backward at small chunks (C = 1, 2, 4, 8, and 16 with bf16
 inputs), where the automatic form is the small-chunk reverse walk (the chunk's
 per-token states in registers; its phase 1 the forward's small-chunk token
 loop, or at C = 16 the matrix-core state passing), against the
@@ -234,7 +234,8 @@ def test_small_chunk_backward_workload_sampled(C):
 # (B, T, H, m, d, C, in dtype, objective, bf16 y and dy)
 SAVED_CASES = [(2, 64, 3, 64, 64, 4, synth.BF16, osr.MODE_DEC, False), (1, 64, 2, 16, 32, 2, synth.F32, osr.MODE_DEC, False),
                (1, 64, 4, 64, 64, 8, synth.BF16, osr.MODE_SIM, True), (2, 32, 2, 32, 128, 4, synth.BF16, osr.MODE_DEC, True),
-               (1, 16, 2, 32, 32, 4, synth.F32, osr.MODE_ENC, False), (1, 32, 2, 128, 128, 2, synth.BF16, osr.MODE_DEC, False)]
+               (1, 16, 2, 32, 32, 4, synth.F32, osr.MODE_ENC, False), (1, 32, 2, 128, 128, 2, synth.BF16, osr.MODE_DEC, False),
+               (2, 24, 3, 64, 32, 1, synth.BF16, osr.MODE_DEC, True), (1, 16, 2, 16, 16, 1, synth.F32, osr.MODE_SIM, False)]
 
 
 @pytest.mark.parametrize("lin", [osr.LIN2, osr.LIN1])
