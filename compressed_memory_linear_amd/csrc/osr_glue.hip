@@ -14,7 +14,7 @@
 //   post: out = y * GeLU(g), GeLU(x) = x Phi(x) = x erfc(-x / sqrt 2) / 2.
 //
 // Both are bound by HBM bandwidth: every input element is read once (plus a
-// three-token halo per 32-token tile of the convolution, which the L2 serves)
+// three-token halo per 64-token tile of the convolution, which the L2 serves)
 // and every output element written once, in 16-byte pieces.  Arithmetic is
 // fp32; bf16 inputs are widened exactly and outputs rounded to nearest even.
 #include <hip/hip_runtime.h>
@@ -26,9 +26,9 @@ namespace {
 
 constexpr int kTaps = 4;        // width of the short convolution
 constexpr int kVec = 8;         // channels per thread (16 bytes of bf16)
-constexpr int kTile = 32;       // tokens per thread in the convolution
+constexpr int kTile = 64;       // tokens per thread in the convolution
 constexpr int kPreThreads = 64; // one wave per workgroup
-constexpr int kAhead = 4;       // rows loaded ahead of their use
+constexpr int kAhead = 8;       // rows loaded ahead of their use
 
 // Eight consecutive elements as fp32, from fp32 or bf16 storage (16-byte aligned).
 __device__ __forceinline__ void load8(const float* p, int64_t i, float (&x)[kVec]) {
@@ -181,8 +181,9 @@ __global__ __launch_bounds__(kPreThreads) void osr_glue_pre_kernel(GlueParams p)
     // store would wait for that store's completion too.  The loads are
     // unconditional (past the tile's end they repeat its last row) and the
     // main loop takes whole groups of rows, so that no branch forces an early
-    // wait.  104 -> 92 us for B8 H16 T4096 m64 (bf16); 8 rows ahead measured
-    // the same at 136 VGPRs.
+    // wait.  104 -> 92 us for B8 H16 T4096 m64 (bf16) at 4 rows ahead and
+    // 32-token tiles; 8 rows ahead and 64-token tiles (half the halo re-reads)
+    // 94-97 -> 91-92 us; 128-token tiles 104 us (too few waves for the chip).
     auto xrow = [&](int t) { return (static_cast<int64_t>(b) * p.T + t) * p.N + c0; };
     auto emit = [&](const Raw8<TIn>& r, int t) {
         float cur[kVec], o[kVec];

@@ -87,7 +87,8 @@ def _check_pre(inp, out, with_bias=True, with_hist=True):
 
 
 @pytest.mark.parametrize("B,T,H,m,in_dtype,per_slot", [
-    (2, 77, 3, 16, synth.BF16, True),    # several 32-token tiles and a ragged tail
+    (2, 77, 3, 16, synth.BF16, True),    # a 64-token tile and a ragged tail of 13
+    (1, 203, 2, 16, synth.BF16, True),   # three 64-token tiles and a ragged tail of 11
     (1, 64, 2, 32, synth.F32, True),
     (2, 45, 3, 16, synth.BF16, False),   # per-token gamma, H not a multiple of 8
     (1, 33, 16, 64, synth.F32, False),   # per-token gamma, rows of 16
