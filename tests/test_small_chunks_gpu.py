@@ -1,5 +1,6 @@
-"""GPU parity of the chunked forward at small chunk sizes (C = 2, 4, 8: the
-batched token loop, osr_tokenloop_small_kernel) against the fp64 oracle.
+"""GPU parity of the chunked forward at small chunk sizes (C = 1, 2, 4, 8: the
+batched token loop, osr_tokenloop_small_kernel; at C = 1 it is the exact
+recurrence, which the recurrent entry runs too) against the fp64 oracle.
 
 The paper trains with C = 4.  Bars as for every forward: max-abs error over
 the oracle's RMS at most 1e-4 for fp32 inputs and 2e-2 for bf16 inputs.
@@ -70,7 +71,7 @@ SHAPES = [(16, 16), (32, 64), (64, 64), (64, 128), (128, 32), (128, 128)]
 
 
 @pytest.mark.parametrize("m,d", SHAPES)
-@pytest.mark.parametrize("C", [2, 4, 8])
+@pytest.mark.parametrize("C", [1, 2, 4, 8])
 @pytest.mark.parametrize("dt", [synth.F32, synth.BF16])
 def test_small_chunks_shapes(m, d, C, dt):
     _say(f"small chunks m={m} d={d} C={C} {dt}")
@@ -79,7 +80,7 @@ def test_small_chunks_shapes(m, d, C, dt):
 
 
 @pytest.mark.parametrize("mode", [osr.MODE_SIM, osr.MODE_ENC])
-@pytest.mark.parametrize("C", [2, 4, 8])
+@pytest.mark.parametrize("C", [1, 2, 4, 8])
 def test_small_chunks_objectives(mode, C):
     # the encoding layer over 32 tokens, where its conditioning keeps fp32 within the bar
     T = 32 if mode == osr.MODE_ENC else 128
@@ -88,7 +89,7 @@ def test_small_chunks_objectives(mode, C):
     _run_check(inp, C, mode=mode)
 
 
-@pytest.mark.parametrize("C", [2, 4, 8])
+@pytest.mark.parametrize("C", [1, 2, 4, 8])
 @pytest.mark.parametrize("per_slot", [True, False])
 def test_small_chunks_first_linearisation(C, per_slot):
     _say(f"small chunks, first linearisation, C={C} per_slot={per_slot}")
@@ -96,17 +97,36 @@ def test_small_chunks_first_linearisation(C, per_slot):
     _run_check(inp, C, lin=osr.LIN1)
 
 
-@pytest.mark.parametrize("T", [4, 12, 20, 36])
-def test_small_chunks_partial_read_out_batch(T):
+@pytest.mark.parametrize("C,T", [(4, 4), (4, 12), (4, 20), (4, 36), (1, 1), (1, 13)])
+def test_small_chunks_partial_read_out_batch(C, T):
     """Token counts whose last read-out batch is partial (batches of 8 tokens
-    at m = d = 64, chunks of 4)."""
-    _say(f"small chunks C=4 T={T}")
+    at m = d = 64)."""
+    _say(f"small chunks C={C} T={T}")
     inp = synth.make_inputs(2, T, 2, 64, 64, seed=4400 + T, in_dtype=synth.F32)
-    _run_check(inp, 4)
+    _run_check(inp, C)
 
 
-def test_small_chunks_gated():
-    _say("small chunks with the fused GeLU post-gate, C=4, bf16")
+@pytest.mark.parametrize("C", [1, 4])
+def test_small_chunks_gated(C):
+    _say(f"small chunks with the fused GeLU post-gate, C={C}, bf16")
     inp = synth.make_inputs(2, 64, 2, 64, 64, seed=4500, in_dtype=synth.BF16)
     gate = np.random.default_rng(4501).standard_normal((2, 64, 2, 64)).astype(np.float32)
-    _run_check(inp, 4, gate=synth.bf16_bits_to_f32(synth.bf16_round_bits(gate)))
+    _run_check(inp, C, gate=synth.bf16_bits_to_f32(synth.bf16_round_bits(gate)))
+
+
+@pytest.mark.parametrize("m,d,dt,mode", [(64, 64, synth.BF16, osr.MODE_DEC), (16, 32, synth.F32, osr.MODE_SIM),
+                                         (128, 128, synth.BF16, osr.MODE_DEC), (32, 16, synth.F32, osr.MODE_ENC)])
+def test_recurrent_equals_chunked_at_one(m, d, dt, mode):
+    """The recurrent entry and the chunked forward at C = 1 run the same
+    kernel on the same values: equal bit for bit (and within the bar of the
+    oracle's exact recurrence)."""
+    _say(f"recurrent vs chunked C=1 m={m} d={d} {dt} mode={mode}")
+    T = 16 if mode == osr.MODE_ENC else 40
+    inp = synth.make_inputs(2, T, 2, m, d, seed=4600 + m + d + mode, in_dtype=dt)
+    t = osr.to_device(inp)
+    args = (t["q"], t["k"], t["v"], t["gamma"], t["mu"], t["state"])
+    y1, S1 = osr.lattice_osr_fwd_chunked(*args, 1, mode=mode)
+    y2, S2 = osr.lattice_osr_fwd_recurrent(*args, mode=mode)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(S1, S2)
+    _run_check(inp, 1, mode=mode)
